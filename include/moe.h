@@ -1,0 +1,243 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) quantized Mixture-of-Experts grouped
+ * GEMM library (libqmoe.so).
+ *
+ * The method: M tokens with K features are routed to top_k of E experts; each
+ * (token, expert) pair multiplies the token's row by that expert's quantized
+ * weight matrix W[e] (N x K); the result is scaled by the router weight and the
+ * top_k results of each token are summed.  Problem sizes are named as in the
+ * column heads (M, K, N, E, top_k) of the FP8_W8A8 and INT8_W8A16 benchmark
+ * tables on "Tianxing/moe quantization" (ROCm Triton pull request).  Formats:
+ *   - fp8 W8A8  : e4m3 activations (one fp32 scale per tensor) x e4m3 weights
+ *                 (one fp32 scale per expert)            ("FP8_W8A8 Benchmark")
+ *   - int8 W8A16: bf16 activations x int8 weights with one fp32 scale per
+ *                 expert and output channel             ("INT8_W8A16 Benchmark";
+ *                 "INT8 quantization support", AutoAWQ issue)
+ *   - MXFP8     : e4m3 data with one e8m0 scale per 32 values along K for both
+ *                 operands, rows concatenated by expert, each expert's rowwise
+ *                 scales padded to 128 rows    ("[PyTorch] Let GroupedLinear
+ *                 accept MXFP8 input and gradient", Description and the reply
+ *                 on padding the scaling factors)
+ *
+ * Conventions shared by every entry point
+ *   - All array arguments are DEVICE pointers owned by the caller.  The library
+ *     never allocates or frees memory and keeps no state besides a
+ *     thread-local record of the last error.
+ *   - Every call only enqueues work on `stream` (0 = the null stream) and never
+ *     synchronises; results are valid once the stream has reached that point.
+ *   - Arguments are validated on the host before anything is enqueued; on an
+ *     error nothing is enqueued and no output is touched.
+ *   - Return value: MOE_OK, or a negative MOE_E* code.  moe_last_error()
+ *     describes the last failure of the calling thread; for MOE_EHIP,
+ *     moe_last_hip_error() holds the hipError_t of the failed launch.
+ *   - Pointers to arrays read or written with 16-byte vector accesses
+ *     (activations, weights, quantized data, per-slot results) must be 16-byte
+ *     aligned.
+ *   - Array shapes are row-major, last index fastest.
+ *   - Byte formats: e4m3 is OCP E4M3FN (bias 7, max 448, NaN = S.1111.111, no
+ *     infinity); e8m0 byte b means 2^(b-127); bf16 is passed as uint16 bits.
+ */
+#ifndef QMOE_MOE_H
+#define QMOE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+#define MOE_OK            0
+#define MOE_EINVAL       (-1)  /* null pointer, bad size, top_k > E, misaligned pointer */
+#define MOE_EUNSUPPORTED (-2)  /* valid but unsupported: block_m, K granularity, limits */
+#define MOE_EHIP         (-3)  /* a HIP launch failed; see moe_last_hip_error() */
+
+/* ---- quantization modes ------------------------------------------------- */
+#define MOE_Q_FP8_PER_TENSOR   0  /* e4m3 + one fp32 scale per tensor (per expert for weights) */
+#define MOE_Q_MXFP8            1  /* e4m3 + one e8m0 scale per 32 values along K */
+#define MOE_Q_INT8_PER_CHANNEL 2  /* weights only: int8 + one fp32 scale per output channel */
+
+/* ---- limits ------------------------------------------------------------- */
+#define MOE_MAX_EXPERTS   128     /* E */
+#define MOE_MAX_TOPK      8       /* top_k */
+#define MOE_MAX_SLOTS     65536   /* M * top_k handled by one align call */
+
+/* Message describing the last failure on the calling thread ("" if none). */
+const char *moe_last_error(void);
+/* hipError_t of the last MOE_EHIP failure on the calling thread (0 if none). */
+int moe_last_hip_error(void);
+
+/* ======================================================================== *
+ * Sizes
+ * ======================================================================== */
+
+/* Length of the sorted-slot buffer for moe_align_block_size:
+ * M*top_k + E*(block_m-1) rounded up to a multiple of block_m.  The expert-id
+ * buffer holds moe_align_max_padded(...)/block_m entries.  Returns a negative
+ * MOE_E* code for invalid sizes. */
+int moe_align_max_padded(int M, int E, int top_k, int block_m);
+
+/* block_m the grouped GEMMs run fastest with for this routing shape: 16 while
+ * the average expert holds few rows (the weight-streaming kernel), else 128
+ * (the tiled MFMA kernel).  Both are accepted by every routed GEMM. */
+int moe_recommended_block_m(int M, int E, int top_k);
+
+/* Bytes of device workspace moe_quantize_act / moe_quantize_weights need for
+ * `mode` on `tensors` independent tensors (1 for activations, E for weights);
+ * 0 when the mode needs none. */
+size_t moe_quantize_workspace_bytes(int mode, int tensors);
+
+/* Upper bound on the rows of the padded MXFP8 rowwise scale matrix for `rows`
+ * rows spread over E experts: rows + E*127 (each expert's block is padded to
+ * a multiple of 128 rows). */
+int moe_mx_scale_rows(int rows, int E);
+
+/* ======================================================================== *
+ * a1 + a2: routing and block alignment
+ * ======================================================================== */
+
+/* Top-k routing of every token and grouping of the routed slots by expert.
+ *
+ * Routing: for token t the top_k experts with the largest float32 logits are
+ * chosen (on equal logits the lower expert index first); router weights are
+ * exp(l_e - l_max) over the chosen experts divided by their sum (the softmax
+ * over all E logits restricted to the chosen experts and renormalised).
+ * Slot i = t*top_k + j is the j-th choice of token t.
+ *
+ * Alignment: the slots are grouped by expert (ascending expert; inside an
+ * expert ascending slot), every group is padded to a multiple of block_m with
+ * the sentinel M*top_k, and every block of block_m sorted slots is labelled
+ * with its expert.
+ *
+ *   logits                 [M, E] float32, read
+ *   topk_ids               [M, top_k] int32, written
+ *   topk_weights           [M, top_k] float32, written
+ *   sorted_token_ids       [moe_align_max_padded()] int32, written in full:
+ *                          slots, then the sentinel M*top_k in padding and tail
+ *   expert_ids             [moe_align_max_padded()/block_m] int32, written in
+ *                          full: expert of each block, -1 after the last block
+ *   num_tokens_post_padded [1] int32, written: padded length (multiple of block_m)
+ *
+ * Limits: 1 <= E <= MOE_MAX_EXPERTS, 1 <= top_k <= min(E, MOE_MAX_TOPK),
+ * 0 <= M*top_k <= MOE_MAX_SLOTS, block_m in {16, 32, 64, 128, 256}.
+ * M = 0 is valid (no slots; the buffers are still written).
+ * One workgroup does the whole call (wavefront ballots and prefix scans). */
+int moe_align_block_size(const float *logits, int M, int E, int top_k, int block_m,
+                         int *topk_ids, float *topk_weights, int *sorted_token_ids,
+                         int *expert_ids, int *num_tokens_post_padded,
+                         hipStream_t stream);
+
+/* ======================================================================== *
+ * a3: activation quantization
+ * ======================================================================== */
+
+/* Dynamic quantization of bf16 activations x [rows, K] to e4m3.
+ *
+ * mode MOE_Q_FP8_PER_TENSOR: amax = max|x| over the whole tensor,
+ *   s = fl32(amax/448) (s = 1 if amax = 0), q = e4m3(fl32(x * fl32(1/s)))
+ *   rounded to nearest even and saturated to +-448.  Writes q [rows, K] and
+ *   scale[0] = s.  `workspace` must hold moe_quantize_workspace_bytes(mode, 1)
+ *   bytes (contents on entry are ignored).  m_offsets/E/scale_e8m0 unused.
+ * mode MOE_Q_MXFP8: for each row and each block of 32 values along K,
+ *   b = clamp(exponent_field(amax_block) - 8, 0, 254) (the shared exponent
+ *   floor(log2 amax) - 8 of the OCP MX rule for e4m3), q = e4m3(x * 2^(127-b))
+ *   saturated.  m_offsets [E+1] (device, int32, non-decreasing, m_offsets[0]=0,
+ *   m_offsets[E]=rows) splits the rows by expert; the scale byte of row r of
+ *   expert e goes to row P_e + (r - m_offsets[e]) of scale_e8m0 [*, K/32],
+ *   where P_e = sum over e' < e of roundup(m_e', 128); the pad rows of every
+ *   expert's block are written with 0.  scale_e8m0 must hold
+ *   moe_mx_scale_rows(rows, E) rows; rows past the padded total are not
+ *   touched.  scale/workspace unused (may be NULL).
+ *
+ * K must be a multiple of 32 (MXFP8) or 8 (fp8).  rows = 0 is valid. */
+int moe_quantize_act(const uint16_t *x, int rows, int K, int mode,
+                     const int *m_offsets, int E, uint8_t *q, float *scale,
+                     uint8_t *scale_e8m0, void *workspace, hipStream_t stream);
+
+/* Offline quantization of float32 expert weights w [E, N, K].
+ *
+ * MOE_Q_FP8_PER_TENSOR  : per expert s_e = fl32(amax(W[e])/448) (1 if zero),
+ *                         q = e4m3(fl32(w * fl32(1/s_e))); q is uint8 [E,N,K],
+ *                         scale [E].  Needs workspace of
+ *                         moe_quantize_workspace_bytes(mode, E) bytes.
+ * MOE_Q_INT8_PER_CHANNEL: per row s = fl32(amax_row/127) (1 if zero),
+ *                         q = clamp(round_half_even(fl32(w * fl32(1/s))),
+ *                         -127, 127); q is int8 [E,N,K], scale [E,N].
+ * MOE_Q_MXFP8           : per row and block of 32 along K as in
+ *                         moe_quantize_act; q uint8 [E,N,K], scale_e8m0
+ *                         [E,N,K/32] (no padding).
+ * K must be a multiple of 32 (MXFP8) or 8. */
+int moe_quantize_weights(const float *w, int E, int N, int K, int mode,
+                         void *q, float *scale, uint8_t *scale_e8m0,
+                         void *workspace, hipStream_t stream);
+
+/* ======================================================================== *
+ * a4 + a5: grouped GEMM with the fused scale / router-weight epilogue
+ * ======================================================================== */
+
+/* Routed fp8 W8A8 grouped GEMM.  For every sorted slot i of expert e (from
+ * moe_align_block_size run with the same M, E, top_k, block_m), token
+ * t = i / top_k, and every column n < N:
+ *     y[i, n] = (sum_k a[t,k] * w[e,n,k]) * (a_scale[0] * w_scale[e]) * topk_weights[i]
+ * with e4m3 operands, fp32 accumulation, and padding slots skipped.
+ *
+ *   a_q [M, K] uint8 e4m3, a_scale [1] f32, w_q [E, N, K] uint8 e4m3,
+ *   w_scale [E] f32, topk_weights [M*top_k] f32, routing buffers as written
+ *   by moe_align_block_size, y [M*top_k, N] f32 (rows of slots that are not
+ *   routed are not written; with every slot routed, y is written in full).
+ *
+ * K must be a multiple of 128; block_m must be 16 or 128. */
+int moe_grouped_gemm_fp8w8a8(const uint8_t *a_q, const float *a_scale,
+                             const uint8_t *w_q, const float *w_scale,
+                             const int *sorted_token_ids, const int *expert_ids,
+                             const int *num_tokens_post_padded,
+                             const float *topk_weights, int M, int K, int N, int E,
+                             int top_k, int block_m, float *y, hipStream_t stream);
+
+/* Routed int8 W8A16 grouped GEMM: as moe_grouped_gemm_fp8w8a8 with
+ *     y[i, n] = (sum_k a[t,k] * w[e,n,k]) * w_scale[e, n] * topk_weights[i]
+ * for bf16 a [M, K] (uint16 bits), int8 w_q [E, N, K], w_scale [E, N] f32.
+ * The int8 weights are converted exactly to bf16 inside the kernel and the
+ * products are accumulated in fp32.  K must be a multiple of 64; block_m must
+ * be 16 or 128. */
+int moe_grouped_gemm_int8w8a16(const uint16_t *a, const int8_t *w_q,
+                               const float *w_scale,
+                               const int *sorted_token_ids, const int *expert_ids,
+                               const int *num_tokens_post_padded,
+                               const float *topk_weights, int M, int K, int N, int E,
+                               int top_k, int block_m, float *y, hipStream_t stream);
+
+/* MXFP8 grouped linear over expert-contiguous rows (no router): for row r of
+ * expert e (m_offsets[e] <= r < m_offsets[e+1]) and column n < N,
+ *     out[r, n] = bf16( sum over blocks kb of 2^(ba[r,kb] + bw[e,n,kb] - 254)
+ *                       * sum_{k in kb} a[r,k] * w[e,n,k] )
+ * accumulated in fp32 and rounded to nearest even.
+ *
+ *   a_q [rows, K] uint8 e4m3; a_sf padded rowwise scales as written by
+ *   moe_quantize_act(MOE_Q_MXFP8) with the same m_offsets; w_q [E, N, K]
+ *   uint8 e4m3; w_sf [E, N, K/32] e8m0; m_offsets [E+1] int32 (device);
+ *   out [rows, N] uint16 bf16, written in full.
+ *
+ * K must be a multiple of 128. */
+int moe_grouped_gemm_mxfp8(const uint8_t *a_q, const uint8_t *a_sf,
+                           const uint8_t *w_q, const uint8_t *w_sf,
+                           const int *m_offsets, int rows, int K, int N, int E,
+                           uint16_t *out, hipStream_t stream);
+
+/* ======================================================================== *
+ * a6: combine
+ * ======================================================================== */
+
+/* Per-token combine: out[t, n] = bf16( y[t*top_k, n] + ... + y[t*top_k+top_k-1, n] )
+ * with the adds done in float32 in slot order and the sum rounded to nearest
+ * even.  y [M*top_k, N] f32, out [M, N] uint16 bf16.  N must be a multiple
+ * of 4. */
+int moe_combine(const float *y, int M, int N, int top_k, uint16_t *out,
+                hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMOE_MOE_H */

@@ -1,0 +1,338 @@
+"""Reference computation of the quantized MoE grouped GEMM, step by step.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+The problem is stated by the column heads of the benchmark tables on
+"Tianxing/moe quantization" (FP8_W8A8 Benchmark, INT8_W8A16 Benchmark):
+M tokens with K input features, E experts with N output features each, and
+every token routed to top_k experts.  The computation follows the per-expert
+decomposition of "Enabling MOE Quantization using linear decomposition"
+(Summary): for each expert, gather the tokens routed to it and apply that
+expert's quantized linear op to them; then weight each result by its router
+weight and sum the top_k results of each token.
+
+Flat slot numbering: the j-th expert choice of token t is slot i = t*top_k + j.
+Per-slot results ``y`` have shape [M*top_k, N] in that order.
+
+Readings taken where the pages are silent (each is restated in the design doc):
+
+* routing selects the top_k experts by float32 logit, larger first, the lower
+  expert index first on equal logits; router weights are the softmax over all
+  E logits restricted to the chosen experts and renormalised to sum to one
+  (the full softmax denominator cancels);
+* block alignment keeps, inside each expert, the slots in ascending slot
+  order; each expert's count is padded up to a multiple of block_m with the
+  sentinel M*top_k; the block list names the expert of every block and -1
+  after the last one;
+* fp8 per-tensor scales are s = fl32(amax / 448), applied as
+  fl32(x * fl32(1 / s)) before rounding to e4m3; an all-zero tensor has s = 1;
+* int8 per-channel weights use s = fl32(amax_row / 127) and
+  clamp(round_half_even(fl32(w * fl32(1 / s))), -127, 127);
+* MXFP8 takes the OCP MX rule for the shared exponent of each block of 32
+  values along K: 2^(floor(log2 amax) - 8), written as the e8m0 byte
+  clamp(exponent_field(amax) - 8, 0, 254), with the elements x / 2^(b-127)
+  rounded to e4m3 with saturation;
+* the contraction itself is done in float64 (at these sizes it is exact or
+  within a few float64 ulp), the epilogue multiplies by the scales and the
+  router weight in float64 and rounds once to float32;
+* the combine adds a token's top_k float32 results in slot order in float32
+  and rounds the sum to bf16 (nearest, ties to even).
+"""
+
+import numpy as np
+
+from .formats import (bf16_decode, bf16_round, e4m3_decode, e4m3_encode,
+                      e8m0_decode, f32_exponent_field)
+
+MX_BLOCK = 32        # values per shared e8m0 scale, along K
+MX_ROW_PAD = 128     # each expert's rowwise scale block is padded to 128 rows
+E4M3_EMAX = 8        # exponent of the largest e4m3 binade (448 = 1.75 * 2^8)
+
+
+def _f32(x):
+    return np.asarray(x, dtype=np.float32)
+
+
+# ----------------------------------------------------------------------------
+# routing (top-k) and block alignment
+# ----------------------------------------------------------------------------
+def route_topk(logits, top_k):
+    """Top-k expert choice and renormalised router weights for each token.
+
+    logits: float32 [M, E].  Returns (topk_ids int32 [M, top_k],
+    topk_weights float32 [M, top_k]).  The choice is made on the float32
+    logits (larger first, lower index first on ties), so it does not depend
+    on how exp is evaluated.  Weights: p_e = exp(l_e - max_l) (float64); the
+    chosen p's divided by their own sum, rounded to float32.
+    """
+    lg = _f32(logits)
+    M, E = lg.shape
+    if not 1 <= top_k <= E:
+        raise ValueError("top_k must be in [1, E]")
+    idx = np.broadcast_to(np.arange(E), (M, E))
+    order = np.lexsort((idx, -lg), axis=-1)          # primary: -logit; then index
+    ids = order[:, :top_k].astype(np.int32)
+    l64 = lg.astype(np.float64)
+    p = np.exp(l64 - l64.max(axis=1, keepdims=True))
+    pk = np.take_along_axis(p, ids.astype(np.int64), axis=1)
+    w = pk / pk.sum(axis=1, keepdims=True)
+    return ids, w.astype(np.float32)
+
+
+def align_max_padded(M, E, top_k, block_m):
+    """Length of the sorted-slot buffer: M*top_k + E*(block_m-1), rounded up
+    to a multiple of block_m (an upper bound on the padded length)."""
+    n = M * top_k + E * (block_m - 1)
+    return (n + block_m - 1) // block_m * block_m
+
+
+def align_block_size(topk_ids, E, block_m):
+    """Group the slots by expert and pad every group to a multiple of block_m.
+
+    Returns (sorted_token_ids int32 [max_padded], expert_ids int32
+    [max_padded // block_m], num_tokens_post_padded int).  Padding slots and
+    the unused tail hold the sentinel M*top_k; blocks past the padded length
+    hold expert -1.
+    """
+    ids = np.asarray(topk_ids)
+    M, top_k = ids.shape
+    flat = ids.reshape(-1).astype(np.int64)
+    sentinel = M * top_k
+    max_padded = align_max_padded(M, E, top_k, block_m)
+    sorted_ids = np.full(max_padded, sentinel, dtype=np.int32)
+    expert_ids = np.full(max_padded // block_m, -1, dtype=np.int32)
+    off = 0
+    for e in range(E):
+        members = np.nonzero(flat == e)[0]           # ascending slot order
+        cnt = len(members)
+        padded = (cnt + block_m - 1) // block_m * block_m
+        sorted_ids[off:off + cnt] = members
+        expert_ids[off // block_m:(off + padded) // block_m] = e
+        off += padded
+    return sorted_ids, expert_ids, off
+
+
+# ----------------------------------------------------------------------------
+# quantization
+# ----------------------------------------------------------------------------
+def fp8_tensor_scale(values):
+    """Per-tensor e4m3 scale s = fl32(amax / 448); 1 for an all-zero tensor."""
+    amax = np.float32(np.max(np.abs(_f32(values)))) if np.size(values) else np.float32(0)
+    if amax == 0:
+        return np.float32(1.0)
+    return np.float32(amax / np.float32(448.0))
+
+
+def fp8_quantize_with_scale(values, s):
+    """e4m3 codes of fl32(x * fl32(1 / s))."""
+    inv = np.float32(np.float32(1.0) / np.float32(s))
+    return e4m3_encode(_f32(values) * inv)
+
+
+def quantize_act_fp8(x_bf16):
+    """Dynamic per-tensor fp8 quantization of bf16 activations [M, K].
+
+    Returns (a_q uint8 [M, K], a_scale float32)."""
+    x = bf16_decode(x_bf16).astype(np.float32)
+    s = fp8_tensor_scale(x)
+    return fp8_quantize_with_scale(x, s), s
+
+
+def quantize_weight_fp8(w):
+    """Per-expert per-tensor fp8 weights: w float32 [E, N, K] ->
+    (w_q uint8 [E, N, K], w_scale float32 [E])."""
+    w = _f32(w)
+    scales = np.array([fp8_tensor_scale(w[e]) for e in range(w.shape[0])], dtype=np.float32)
+    q = np.stack([fp8_quantize_with_scale(w[e], scales[e]) for e in range(w.shape[0])])
+    return q, scales
+
+
+def int8_channel_scale(w_rows):
+    """Per-row symmetric int8 scale fl32(amax_row / 127); 1 for a zero row."""
+    amax = np.max(np.abs(_f32(w_rows)), axis=-1)
+    s = (amax / np.float32(127.0)).astype(np.float32)
+    return np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
+
+
+def quantize_weight_int8(w):
+    """Per-output-channel symmetric int8 weights: w float32 [E, N, K] ->
+    (w_q int8 [E, N, K], w_scale float32 [E, N])."""
+    w = _f32(w)
+    s = int8_channel_scale(w)
+    inv = (np.float32(1.0) / s).astype(np.float32)
+    q = np.rint(w * inv[..., None])                  # float32 product, half to even
+    return np.clip(q, -127, 127).astype(np.int8), s
+
+
+def mx_scale_byte(amax32):
+    """e8m0 byte of the shared scale 2^(floor(log2 amax) - 8) of each block:
+    clamp(exponent_field(amax) - 8, 0, 254); an all-zero block gives 0."""
+    return np.clip(f32_exponent_field(amax32) - E4M3_EMAX, 0, 254).astype(np.uint8)
+
+
+def quantize_mxfp8_rows(values):
+    """MXFP8 along the last axis: values float32 [R, K] (K % 32 == 0) ->
+    (q uint8 [R, K], scale bytes uint8 [R, K/32]).
+
+    Each element of a block is x * 2^(127 - b) (exact: a power-of-two scale)
+    rounded to e4m3 with saturation."""
+    v = _f32(values)
+    R, K = v.shape
+    if K % MX_BLOCK:
+        raise ValueError("K must be a multiple of 32 for MXFP8")
+    blk = v.reshape(R, K // MX_BLOCK, MX_BLOCK)
+    b = mx_scale_byte(np.max(np.abs(blk), axis=-1))
+    scaled = blk.astype(np.float64) * np.ldexp(1.0, 127 - b.astype(np.int64))[..., None]
+    return e4m3_encode(scaled).reshape(R, K), b
+
+
+def mx_padded_offsets(m_offsets):
+    """Start row of each expert's scale block when every block is padded to a
+    multiple of 128 rows ("[PyTorch] Let GroupedLinear accept MXFP8 input and
+    gradient", reply on the padding: each expert's rowwise scales are padded to
+    128 rows).  Returns int64 [E+1]."""
+    m = np.diff(np.asarray(m_offsets, dtype=np.int64))
+    padded = (m + MX_ROW_PAD - 1) // MX_ROW_PAD * MX_ROW_PAD
+    return np.concatenate([[0], np.cumsum(padded)])
+
+
+def quantize_act_mxfp8(x_bf16, m_offsets):
+    """MXFP8 quantization of expert-concatenated bf16 activations.
+
+    x_bf16 uint16 [R, K]; m_offsets int [E+1] (rows of expert e are
+    m_offsets[e] .. m_offsets[e+1]-1).  Returns (q uint8 [R, K],
+    sf uint8 [sum_e roundup(m_e, 128), K/32]) where expert e's scale rows start
+    at the padded offset and the pad rows are zero."""
+    x = bf16_decode(x_bf16).astype(np.float32)
+    q, b = quantize_mxfp8_rows(x)
+    mo = np.asarray(m_offsets, dtype=np.int64)
+    po = mx_padded_offsets(mo)
+    sf = np.zeros((int(po[-1]), x.shape[1] // MX_BLOCK), dtype=np.uint8)
+    for e in range(len(mo) - 1):
+        n = mo[e + 1] - mo[e]
+        sf[po[e]:po[e] + n] = b[mo[e]:mo[e + 1]]
+    return q, sf
+
+
+def quantize_weight_mxfp8(w):
+    """MXFP8 weights: w float32 [E, N, K] -> (q uint8 [E, N, K],
+    sf uint8 [E, N, K/32]), one scale per 32 values along K of each row."""
+    w = _f32(w)
+    E, N, K = w.shape
+    q, b = quantize_mxfp8_rows(w.reshape(E * N, K))
+    return q.reshape(E, N, K), b.reshape(E, N, K // MX_BLOCK)
+
+
+# ----------------------------------------------------------------------------
+# grouped GEMM with the scale / router-weight epilogue
+# ----------------------------------------------------------------------------
+def _slots_by_expert(topk_ids, slots):
+    flat = np.asarray(topk_ids).reshape(-1)
+    sel = np.arange(flat.size) if slots is None else np.asarray(slots, dtype=np.int64)
+    return sel, flat[sel]
+
+
+def _grouped(decode_a, decode_w_rows, scale_of, topk_ids, topk_weights, N, slots, cols):
+    """Shared per-expert loop: for every selected slot i (token t = i // top_k,
+    expert e) and column n: y[i, n] = (A[t] . W[e, n]) * scale_of(e, n) * w[i],
+    with the dot product in float64."""
+    top_k = np.asarray(topk_ids).shape[1]
+    sel, experts = _slots_by_expert(topk_ids, slots)
+    cols = np.arange(N) if cols is None else np.asarray(cols, dtype=np.int64)
+    wt = np.asarray(topk_weights, dtype=np.float32).reshape(-1).astype(np.float64)
+    y = np.zeros((sel.size, cols.size), dtype=np.float64)
+    for e in np.unique(experts):
+        rows = np.nonzero(experts == e)[0]
+        tokens = sel[rows] // top_k
+        acc = decode_a(tokens) @ decode_w_rows(int(e), cols).T
+        y[rows] = acc * scale_of(int(e), cols)[None, :] * wt[sel[rows]][:, None]
+    return y.astype(np.float32)
+
+
+def grouped_gemm_fp8w8a8(a_q, a_scale, w_q, w_scale, topk_ids, topk_weights,
+                         slots=None, cols=None):
+    """fp8 W8A8: e4m3 activations (one scale) x e4m3 weights (one scale per
+    expert).  Returns float32 y for the selected slots x cols (all by default).
+    ("Tianxing/moe quantization", FP8_W8A8 Benchmark.)"""
+    a_q = np.asarray(a_q)
+    w_q = np.asarray(w_q)
+    ws = np.asarray(w_scale, dtype=np.float32).astype(np.float64)
+    sa = float(np.float32(a_scale))
+    return _grouped(lambda t: e4m3_decode(a_q[t]),
+                    lambda e, c: e4m3_decode(w_q[e][c]),
+                    lambda e, c: np.full(c.size, sa * ws[e]),
+                    topk_ids, topk_weights, w_q.shape[1], slots, cols)
+
+
+def grouped_gemm_int8w8a16(a_bf16, w_q, w_scale, topk_ids, topk_weights,
+                           slots=None, cols=None):
+    """int8 W8A16: bf16 activations x int8 weights with one scale per expert
+    and output channel ("Tianxing/moe quantization", INT8_W8A16 Benchmark;
+    "INT8 quantization support": int8 weights used with 16-bit activations)."""
+    a = np.asarray(a_bf16)
+    w_q = np.asarray(w_q)
+    ws = np.asarray(w_scale, dtype=np.float32).astype(np.float64)
+    return _grouped(lambda t: bf16_decode(a[t]),
+                    lambda e, c: w_q[e][c].astype(np.float64),
+                    lambda e, c: ws[e][c],
+                    topk_ids, topk_weights, w_q.shape[1], slots, cols)
+
+
+def _mx_decode_rows(q_rows, sf_rows):
+    """Decoded MXFP8 rows: e4m3 value * 2^(b - 127) for every block of 32."""
+    R, K = q_rows.shape
+    v = e4m3_decode(q_rows).reshape(R, K // MX_BLOCK, MX_BLOCK)
+    return (v * e8m0_decode(sf_rows)[..., None]).reshape(R, K)
+
+
+def grouped_gemm_mxfp8(a_q, a_sf, w_q, w_sf, m_offsets, rows=None, cols=None):
+    """MXFP8 grouped linear over expert-contiguous row segments ("[PyTorch] Let
+    GroupedLinear accept MXFP8 input and gradient").
+
+    a_q uint8 [R, K] with rowwise scales a_sf in per-expert blocks padded to
+    128 rows (see ``quantize_act_mxfp8``); w_q uint8 [E, N, K] with w_sf
+    [E, N, K/32].  acc[r, n] = sum over blocks of 2^(ba+bw-254) * sum(qa*qw),
+    evaluated in float64; the output is bf16(fl32(acc)) as uint16
+    [len(rows), len(cols)]."""
+    a_q = np.asarray(a_q)
+    w_q = np.asarray(w_q)
+    mo = np.asarray(m_offsets, dtype=np.int64)
+    po = mx_padded_offsets(mo)
+    R, K = a_q.shape
+    N = w_q.shape[1]
+    rows = np.arange(R) if rows is None else np.asarray(rows, dtype=np.int64)
+    cols = np.arange(N) if cols is None else np.asarray(cols, dtype=np.int64)
+    expert = np.searchsorted(mo, rows, side="right") - 1
+    out = np.zeros((rows.size, cols.size), dtype=np.float64)
+    for e in np.unique(expert):
+        sel = np.nonzero(expert == e)[0]
+        r = rows[sel]
+        a = _mx_decode_rows(a_q[r], np.asarray(a_sf)[po[e] + (r - mo[e])])
+        w = _mx_decode_rows(w_q[e][cols], np.asarray(w_sf)[e][cols])
+        out[sel] = a @ w.T
+    return bf16_round(out.astype(np.float32))
+
+
+# ----------------------------------------------------------------------------
+# combine
+# ----------------------------------------------------------------------------
+def combine(y, top_k):
+    """Per-token sum of the top_k slot results, in slot order, in float32, then
+    rounded to bf16.  y float32 [M*top_k, N] -> (out32 float32 [M, N],
+    out bf16 bits uint16 [M, N])."""
+    y = _f32(y)
+    M = y.shape[0] // top_k
+    yy = y.reshape(M, top_k, -1)
+    acc = yy[:, 0, :].copy()
+    for j in range(1, top_k):
+        acc = (acc + yy[:, j, :]).astype(np.float32)
+    return acc, bf16_round(acc)
+
+
+# ----------------------------------------------------------------------------
+# accounting used by the measurements
+# ----------------------------------------------------------------------------
+def flops(M, K, N, top_k):
+    """Useful flops of one grouped GEMM: 2 * M * top_k * K * N (the accounting
+    behind the TFLOPS column of the "Tianxing/moe quantization" tables)."""
+    return 2 * M * top_k * K * N

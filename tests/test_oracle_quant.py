@@ -1,0 +1,208 @@
+"""Pins of the oracle's quantizers.
+
+* fp8 per tensor -> exact power-of-two scaling invariance, the amax element
+                    landing on +-448, the scale equal to amax/448, the
+                    round-trip of values that already sit on the scaled grid.
+* int8 per channel -> brute force per element with Python's round-half-even
+                    on exact fractions, the amax element on +-127, symmetry.
+* MXFP8          -> the statement of "[PyTorch] Let GroupedLinear accept MXFP8
+                    input and gradient" that quantizing the concatenated tensor
+                    and quantizing each expert separately give the same data
+                    (scales differ only by the per-expert padding to 128 rows),
+                    its [64, 128] -> rowwise [128, 4] shape example, the
+                    shared-exponent rule checked with math.frexp, and exact
+                    power-of-two invariance.
+"""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import formats as F
+from oracle import moe as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _bf16(a):
+    return F.bf16_round(np.asarray(a, np.float32))
+
+
+# ------------------------------------------------------------- fp8 ----
+def test_fp8_per_tensor_scale_and_amax_code():
+    rng = np.random.default_rng(0)
+    x = _bf16(rng.standard_normal((33, 64)))
+    q, s = O.quantize_act_fp8(x)
+    xv = F.bf16_decode(x)
+    amax = np.max(np.abs(xv))
+    assert s == np.float32(amax / 448.0)          # one correctly rounded division
+    i = np.unravel_index(np.argmax(np.abs(xv)), xv.shape)
+    assert q[i] & 0x7F == 0x7E                    # the amax element maps to +-448
+    assert np.all((q & 0x7F) <= 0x7E)             # never NaN
+    # dequantized values are within half an e4m3 step (relative 2^-4) of x
+    deq = F.e4m3_decode(q) * float(s)
+    big = np.abs(xv) > 2.0 ** -6 * float(s)
+    assert np.all(np.abs(deq - xv)[big] <= np.abs(xv)[big] * 2.0 ** -4 * (1 + 1e-6))
+
+
+@pytest.mark.parametrize("p", [-7, -1, 3, 11])
+def test_fp8_per_tensor_power_of_two_invariance(p):
+    rng = np.random.default_rng(1)
+    xf = rng.standard_normal((16, 32)).astype(np.float32)
+    x = _bf16(xf)
+    x2 = _bf16(F.bf16_decode(x) * 2.0 ** p)       # exact: a power-of-two scaling
+    q1, s1 = O.quantize_act_fp8(x)
+    q2, s2 = O.quantize_act_fp8(x2)
+    np.testing.assert_array_equal(q1, q2)
+    assert float(s2) == float(s1) * 2.0 ** p
+
+
+def test_fp8_per_tensor_grid_values_round_trip():
+    # x = code_value * s with s = 1 (amax = 448): quantization returns the codes
+    codes = np.array([0x7E, 0x01, 0x30, 0x45, 0xB9, 0x80, 0x5A], np.uint8)
+    x = _bf16(F.e4m3_decode(codes))
+    q, s = O.quantize_act_fp8(x[None, :])
+    assert s == 1.0
+    np.testing.assert_array_equal(q[0], codes)
+
+
+def test_fp8_zero_tensor():
+    q, s = O.quantize_act_fp8(np.zeros((4, 16), np.uint16))
+    assert s == 1.0 and np.all(q == 0)
+
+
+def test_fp8_weight_scale_per_expert():
+    rng = np.random.default_rng(2)
+    w = (rng.standard_normal((3, 8, 32)) * np.array([1, 10, 0.01])[:, None, None]).astype(np.float32)
+    q, s = O.quantize_weight_fp8(w)
+    for e in range(3):
+        assert s[e] == np.float32(np.max(np.abs(w[e])) / np.float32(448))
+        assert np.max(q[e] & 0x7F) == 0x7E
+
+
+# ------------------------------------------------------------- int8 ----
+def _round_half_even(fr):
+    f = math.floor(fr)
+    d = fr - f
+    if d > Fraction(1, 2) or (d == Fraction(1, 2) and f % 2 == 1):
+        return f + 1
+    return f
+
+
+def test_int8_per_channel_brute_force():
+    rng = np.random.default_rng(3)
+    w = (rng.standard_normal((2, 5, 24)) / 4).astype(np.float32)
+    w[1, 3] = 0.0                                  # an all-zero channel
+    q, s = O.quantize_weight_int8(w)
+    for e in range(2):
+        for n in range(5):
+            row = w[e, n]
+            amax = float(np.max(np.abs(row)))
+            s_ref = np.float32(1.0) if amax == 0 else np.float32(Fraction(amax) / 127)
+            assert s[e, n] == s_ref
+            inv = np.float32(Fraction(1) / Fraction(float(s_ref)))
+            for k in range(24):
+                prod = np.float32(Fraction(float(row[k])) * Fraction(float(inv)))
+                ref = max(-127, min(127, _round_half_even(Fraction(float(prod)))))
+                assert int(q[e, n, k]) == ref
+            if amax:
+                assert int(np.max(np.abs(q[e, n].astype(int)))) == 127
+
+
+def test_int8_symmetry():
+    rng = np.random.default_rng(4)
+    w = rng.standard_normal((1, 4, 64)).astype(np.float32)
+    q1, s1 = O.quantize_weight_int8(w)
+    q2, s2 = O.quantize_weight_int8(-w)
+    np.testing.assert_array_equal(q1, -q2)
+    np.testing.assert_array_equal(s1, s2)
+
+
+# ------------------------------------------------------------- MXFP8 ----
+def test_mxfp8_page_example_shapes():
+    g = json.load(open(os.path.join(GOLDEN, "mxfp8_padding_example.json")))
+    rng = np.random.default_rng(5)
+    E, m, K = g["experts"], g["rows_per_expert"], g["K"]
+    x = _bf16(rng.standard_normal((E * m, K)))
+    mo = np.arange(E + 1) * m
+    q, sf = O.quantize_act_mxfp8(x, mo)
+    assert list(q.shape) == g["concat_data_shape"]
+    # per expert: data [64,128] and rowwise scales [128, 4]
+    for e in range(E):
+        qe, sfe = O.quantize_act_mxfp8(x[e * m:(e + 1) * m], [0, m])
+        assert list(qe.shape) == g["per_expert_data_shape"]
+        assert list(sfe.shape) == g["per_expert_rowwise_scale_shape"]
+    # split + pad of the whole-tensor scales: every expert gets a 128-row block
+    assert sf.shape == (E * g["per_expert_rowwise_scale_shape"][0], K // 32)
+
+
+@pytest.mark.parametrize("seg", [(64, 64), (5, 130, 0, 77), (128,), (1, 1, 1)])
+def test_mxfp8_whole_equals_per_expert(seg):
+    """Quantizing the concatenated tensor, then splitting it, equals quantizing
+    each expert's chunk on its own: identical data, identical scales once each
+    expert's scale block is padded to 128 rows."""
+    rng = np.random.default_rng(sum(seg))
+    K = 96
+    R = sum(seg)
+    x = _bf16(rng.standard_normal((R, K)) * rng.uniform(0.01, 100, size=(R, 1)))
+    mo = np.concatenate([[0], np.cumsum(seg)])
+    q, sf = O.quantize_act_mxfp8(x, mo)
+    po = O.mx_padded_offsets(mo)
+    for e, n in enumerate(seg):
+        qe, sfe = O.quantize_act_mxfp8(x[mo[e]:mo[e + 1]], [0, n])
+        np.testing.assert_array_equal(q[mo[e]:mo[e + 1]], qe)
+        np.testing.assert_array_equal(sf[po[e]:po[e + 1]], sfe)
+        assert sfe.shape[0] == -(-n // 128) * 128
+        assert np.all(sfe[n:] == 0)
+
+
+def test_mxfp8_shared_exponent_rule():
+    rng = np.random.default_rng(6)
+    v = (rng.standard_normal((40, 64)) * np.exp(rng.uniform(-20, 20, size=(40, 1)))).astype(np.float32)
+    q, b = O.quantize_mxfp8_rows(v)
+    blk = v.reshape(40, 2, 32)
+    for r in range(40):
+        for j in range(2):
+            amax = float(np.max(np.abs(blk[r, j])))
+            _, ex = math.frexp(amax)                # amax = f * 2^ex, f in [0.5, 1)
+            assert int(b[r, j]) == (ex - 1) - 8 + 127
+            codes = q[r, 32 * j:32 * j + 32]
+            # the block maximum lands in the top binade [256, 448] (codes 0x78..0x7E)
+            assert 0x78 <= int(np.max(codes & 0x7F)) <= 0x7E
+            # in scaled units y = x / 2^(b-127): unsaturated elements are within
+            # half a step (relative 2^-4, absolute 2^-10 among subnormals);
+            # elements beyond 448 are clamped to +-448
+            y = blk[r, j].astype(np.float64) * 2.0 ** (127 - int(b[r, j]))
+            deq = F.e4m3_decode(codes)
+            sat = np.abs(y) > 448
+            assert np.all(deq[sat] == np.sign(y[sat]) * 448)
+            ok = np.abs(deq - y)[~sat] <= np.maximum(np.abs(y[~sat]) * 2.0 ** -4, 2.0 ** -10)
+            assert np.all(ok)
+
+
+@pytest.mark.parametrize("p", [-5, 4])
+def test_mxfp8_power_of_two_invariance(p):
+    rng = np.random.default_rng(7)
+    v = rng.standard_normal((8, 64)).astype(np.float32)
+    q1, b1 = O.quantize_mxfp8_rows(v)
+    q2, b2 = O.quantize_mxfp8_rows((v * np.float32(2.0 ** p)).astype(np.float32))
+    np.testing.assert_array_equal(q1, q2)
+    np.testing.assert_array_equal(b2.astype(int), b1.astype(int) + p)
+
+
+def test_mxfp8_zero_block_and_weights_layout():
+    v = np.zeros((2, 64), np.float32)
+    v[1, 40] = 3.0
+    q, b = O.quantize_mxfp8_rows(v)
+    assert b.tolist() == [[0, 0], [0, 128 - 8]]     # 3.0 has exponent field 128
+    assert np.all(q[0] == 0) and np.all(q[1, :32] == 0)
+    w = np.random.default_rng(8).standard_normal((2, 3, 64)).astype(np.float32)
+    wq, wsf = O.quantize_weight_mxfp8(w)
+    assert wq.shape == (2, 3, 64) and wsf.shape == (2, 3, 2)
+    q2, b2 = O.quantize_mxfp8_rows(w[1])
+    np.testing.assert_array_equal(wq[1], q2)
+    np.testing.assert_array_equal(wsf[1], b2)

@@ -1,0 +1,206 @@
+"""Benchmark of the quantized MoE hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input
+resident in HBM: routing + block alignment, activation quantization (fp8
+formats), the grouped GEMM with its fused scale / router-weight epilogue, and
+the per-token combine (MXFP8: quantization + grouped GEMM).
+
+Default workload: int8 W8A16 decode, M=64 tokens, K=4096, N=14336, E=8,
+top_k=2 (the weight-bandwidth-bound shape).  ``--workload`` selects another
+one (names in quantized_moe_grouped_top_amd.synth.WORKLOADS).
+
+The expert weights exist in several copies that the steps rotate through, so
+that no step finds its weights in the 256 MB Infinity Cache or in L2 from the
+step before.
+
+Prints one JSON line: value = whole-step throughput in algorithmic HBM GB/s
+(the byte count of the "Tianxing/moe quantization" tables: activations +
+expert weights + scales + per-slot bf16 outputs), plus the TFLOPS of the
+step, the roofline of the dominant kernel (the grouped GEMM; its launches
+timed with HIP events on the stream they run on) and the CPU oracle timed on
+the host.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"fp8": 5033.0, "mxfp8": 5033.0, "bf16": 2516.0}
+DEFAULT_WORKLOAD = "int8w8a16_m64_k4096_n14336"
+
+
+def alg_bytes(wl, active_experts=None):
+    """Algorithmic bytes of one grouped GEMM call: every activation, weight
+    and scale byte read once, every per-slot output written once as bf16."""
+    E = wl.E if active_experts is None else active_experts
+    M, K, N = wl.M, wl.K, wl.N
+    if wl.fmt == "fp8":
+        return M * K + E * N * K + 4 * (E + 1) + M * wl.top_k * N * 2
+    if wl.fmt == "int8":
+        return 2 * M * K + E * N * K + 4 * E * N + M * wl.top_k * N * 2
+    # MXFP8: data + e8m0 scales of both operands, bf16 output rows
+    return M * K * (1 + 1 / 32) + E * N * K * (1 + 1 / 32) + 2 * M * N
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--copies", type=int, default=0,
+                   help="weight copies rotated over (0: enough for >= 1 GiB of weights)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="target CPU time of the oracle baseline")
+    return p.parse_args()
+
+
+def cpu_baseline(wl, case, target_s):
+    """The CPU oracle on the same workload, timed on the host: the whole
+    step (routing, alignment, activation quantization, grouped GEMM, combine)
+    repeated until target_s seconds have passed (at least once).  Weight
+    quantization is offline and not timed."""
+    import numpy as np
+    from oracle import formats as F
+    from oracle import moe as O
+
+    w = case["w"].cpu().numpy()
+    x = case["x"].view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+    if wl.fmt == "mxfp8":
+        wq, wsf = O.quantize_weight_mxfp8(w)
+        mo = case["m_offsets"].cpu().numpy()
+    else:
+        wq, ws = (O.quantize_weight_fp8 if wl.fmt == "fp8" else O.quantize_weight_int8)(w)
+        lg = case["logits"].cpu().numpy()
+    del w
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        if wl.fmt == "mxfp8":
+            aq, asf = O.quantize_act_mxfp8(x, mo)
+            O.grouped_gemm_mxfp8(aq, asf, wq, wsf, mo)
+        else:
+            ids, wts = O.route_topk(lg, wl.top_k)
+            O.align_block_size(ids, wl.E, 16)
+            if wl.fmt == "fp8":
+                aq, sa = O.quantize_act_fp8(x)
+                y = O.grouped_gemm_fp8w8a8(aq, sa, wq, ws, ids, wts)
+            else:
+                y = O.grouped_gemm_int8w8a16(x, wq, ws, ids, wts)
+            O.combine(y, wl.top_k)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s:
+            break
+    per = el / reps
+    return {"value": round(alg_bytes(wl) / per / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "tflops": round(wl.flops / per / 1e12, 6),
+            "sample": f"whole workload, {reps} step(s) in {el:.1f} s "
+                      f"(numpy float64; BLAS threads = OMP_NUM_THREADS or all cores)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
+              f"(this build runs the hot path on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import quantized_moe_grouped_top_amd as qm
+    from quantized_moe_grouped_top_amd import runner, synth
+
+    qm.lib()                                   # fail loudly if the library is missing
+    torch.cuda.set_device(0)
+    wl = synth.WORKLOADS[args.workload]
+    case = synth.make_case(wl, 0, device="cuda")
+    w_q, w_s = runner.quantize_weights(case["w"], wl.fmt)
+    copies = args.copies or max(2, -(-(1 << 30) // w_q.numel()))
+    weights = [(w_q, w_s)] + [(w_q.clone(), w_s.clone()) for _ in range(copies - 1)]
+    if wl.fmt == "mxfp8":
+        moe = runner.MxMoE(wl.M, wl.K, wl.N, wl.E)
+        mo = case["m_offsets"]
+
+        def step(i, ev):
+            q, s = weights[i % copies]
+            moe.quantize(case["x"], mo)
+            if ev is not None:
+                ev[0].record()
+            moe.gemm(q, s, mo)
+            if ev is not None:
+                ev[1].record()
+    else:
+        moe = runner.RoutedMoE(wl.fmt, wl.M, wl.K, wl.N, wl.E, wl.top_k)
+
+        def step(i, ev):
+            q, s = weights[i % copies]
+            moe.route(case["logits"])
+            moe.quantize(case["x"])
+            if ev is not None:
+                ev[0].record()
+            moe.gemm(case["x"], q, s)
+            if ev is not None:
+                ev[1].record()
+            moe.combine()
+
+    for i in range(args.warmup):
+        step(i, None)
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    gemm_ms = sum(a.elapsed_time(b) for a, b in events) / args.steps
+
+    active = wl.E
+    if wl.fmt != "mxfp8":
+        ids = moe.topk_ids.cpu()
+        active = int(torch.unique(ids).numel())
+    nbytes = alg_bytes(wl, active)
+    ms = elapsed * 1e3 / args.steps
+    dtype = {"fp8": "fp8", "int8": "bf16", "mxfp8": "mxfp8"}[wl.fmt]
+    bound = "hbm" if wl.flops / nbytes < 600 else "mfma"
+    if bound == "hbm":
+        achieved = nbytes / (gemm_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = wl.flops / (gemm_ms * 1e-3) / 1e12
+        peak = MFMA_PEAK_TFLOPS[dtype]
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
+    roof.update({"traffic": None, "kernel": "grouped GEMM", "kernel_us": round(gemm_ms * 1e3, 2),
+                 "alg_bytes": int(nbytes), "flops": int(wl.flops)})
+    line = {
+        "metric": "TFLOPS and HBM GB/s (% of MI355X roofline) for quantized MoE GEMM, E=8 top_k=2",
+        "value": round(nbytes / (ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "tflops": round(wl.flops / (ms * 1e-3) / 1e12, 3),
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": dtype, "data": "synthetic (seeded N(0,1) activations and logits, N(0,1/sqrt(K)) weights)",
+        "config": {"workload": wl.name, "format": wl.fmt, "M": wl.M, "K": wl.K, "N": wl.N,
+                   "E": wl.E, "top_k": wl.top_k, "weight_copies": copies,
+                   "block_m": getattr(moe, "block_m", None)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, case, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,258 @@
+// C ABI of libqmoe.so (declared in include/moe.h): argument validation on the
+// host, then the launches on the caller's stream.  No entry point allocates,
+// frees or synchronises; on a validation error nothing is enqueued.
+#include "../../include/moe.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "qmoe_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+thread_local int g_hip_err = 0;
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  g_hip_err = 0;
+  return MOE_OK;
+}
+
+int hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ok();
+  g_hip_err = (int)e;
+  return fail(MOE_EHIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool valid_block_m(int b) { return b == 16 || b == 32 || b == 64 || b == 128 || b == 256; }
+
+#define REQUIRE(cond, code, ...)                  \
+  do {                                            \
+    if (!(cond)) return fail((code), __VA_ARGS__); \
+  } while (0)
+
+int check_routing_sizes(int M, int E, int top_k, const char *fn) {
+  REQUIRE(E >= 1 && E <= MOE_MAX_EXPERTS, MOE_EINVAL, "%s: E=%d outside [1, %d]", fn, E,
+          MOE_MAX_EXPERTS);
+  REQUIRE(top_k >= 1 && top_k <= E, MOE_EINVAL, "%s: top_k=%d outside [1, E=%d]", fn, top_k, E);
+  REQUIRE(top_k <= MOE_MAX_TOPK, MOE_EUNSUPPORTED, "%s: top_k=%d above %d", fn, top_k,
+          MOE_MAX_TOPK);
+  REQUIRE(M >= 0, MOE_EINVAL, "%s: M=%d is negative", fn, M);
+  REQUIRE((long long)M * top_k <= MOE_MAX_SLOTS, MOE_EUNSUPPORTED,
+          "%s: M*top_k=%lld above %d", fn, (long long)M * top_k, MOE_MAX_SLOTS);
+  return MOE_OK;
+}
+
+long long max_padded_ll(int M, int E, int top_k, int block_m) {
+  const long long n = (long long)M * top_k + (long long)E * (block_m - 1);
+  return (n + block_m - 1) / block_m * block_m;
+}
+
+int check_routed_gemm(const void *a, const void *w, const void *w_scale, const int *sorted,
+                      const int *expert_ids, const int *num_post, const float *topk_w,
+                      const float *y, int M, int K, int N, int E, int top_k, int block_m,
+                      int k_mult, const char *fn) {
+  int rc = check_routing_sizes(M, E, top_k, fn);
+  if (rc) return rc;
+  REQUIRE(K > 0 && N > 0, MOE_EINVAL, "%s: K=%d and N=%d must be positive", fn, K, N);
+  REQUIRE(K % k_mult == 0, MOE_EUNSUPPORTED, "%s: K=%d is not a multiple of %d", fn, K, k_mult);
+  REQUIRE(block_m == 16 || block_m == 128, MOE_EUNSUPPORTED,
+          "%s: block_m=%d (supported: 16, 128)", fn, block_m);
+  if (M == 0) return MOE_OK;               // nothing to do; buffers may be empty
+  REQUIRE(a && w && w_scale && sorted && expert_ids && num_post && topk_w && y, MOE_EINVAL,
+          "%s: null pointer argument", fn);
+  REQUIRE(aligned16(a) && aligned16(w), MOE_EINVAL,
+          "%s: activation and weight pointers must be 16-byte aligned", fn);
+  REQUIRE((long long)E * N * (long long)K < (1ll << 40), MOE_EUNSUPPORTED,
+          "%s: weight tensor too large", fn);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_last_error(void) { return g_err; }
+int moe_last_hip_error(void) { return g_hip_err; }
+
+int moe_align_max_padded(int M, int E, int top_k, int block_m) {
+  int rc = check_routing_sizes(M, E, top_k, "moe_align_max_padded");
+  if (rc) return rc;
+  REQUIRE(valid_block_m(block_m), MOE_EUNSUPPORTED, "moe_align_max_padded: block_m=%d",
+          block_m);
+  ok();
+  return (int)max_padded_ll(M, E, top_k, block_m);
+}
+
+int moe_recommended_block_m(int M, int E, int top_k) {
+  int rc = check_routing_sizes(M, E, top_k, "moe_recommended_block_m");
+  if (rc) return rc;
+  ok();
+  // few rows per expert: stream the weights once with all rows in registers
+  const long long avg_rows = ((long long)M * top_k + E - 1) / E;
+  return avg_rows <= 48 ? 16 : 128;
+}
+
+size_t moe_quantize_workspace_bytes(int mode, int tensors) {
+  if (mode != MOE_Q_FP8_PER_TENSOR || tensors <= 0) return 0;
+  return (size_t)tensors * qmoe::kAmaxPartials * sizeof(float);
+}
+
+int moe_mx_scale_rows(int rows, int E) {
+  if (rows < 0 || E < 1 || E > MOE_MAX_EXPERTS)
+    return fail(MOE_EINVAL, "moe_mx_scale_rows: rows=%d E=%d", rows, E);
+  ok();
+  return rows + E * (qmoe::kMxRowPad - 1);
+}
+
+int moe_align_block_size(const float *logits, int M, int E, int top_k, int block_m,
+                         int *topk_ids, float *topk_weights, int *sorted_token_ids,
+                         int *expert_ids, int *num_tokens_post_padded, hipStream_t stream) {
+  const char *fn = "moe_align_block_size";
+  int rc = check_routing_sizes(M, E, top_k, fn);
+  if (rc) return rc;
+  REQUIRE(valid_block_m(block_m), MOE_EUNSUPPORTED, "%s: block_m=%d", fn, block_m);
+  REQUIRE(sorted_token_ids && expert_ids && num_tokens_post_padded, MOE_EINVAL,
+          "%s: null output pointer", fn);
+  REQUIRE(M == 0 || (logits && topk_ids && topk_weights), MOE_EINVAL, "%s: null pointer", fn);
+  const int max_padded = (int)max_padded_ll(M, E, top_k, block_m);
+  return hip_status(qmoe::launch_route_align(logits, M, E, top_k, block_m, max_padded, topk_ids,
+                                             topk_weights, sorted_token_ids, expert_ids,
+                                             num_tokens_post_padded, stream),
+                    fn);
+}
+
+int moe_quantize_act(const uint16_t *x, int rows, int K, int mode, const int *m_offsets, int E,
+                     uint8_t *q, float *scale, uint8_t *scale_e8m0, void *workspace,
+                     hipStream_t stream) {
+  const char *fn = "moe_quantize_act";
+  REQUIRE(rows >= 0 && K > 0, MOE_EINVAL, "%s: rows=%d K=%d", fn, rows, K);
+  if (mode == MOE_Q_FP8_PER_TENSOR) {
+    REQUIRE(K % 8 == 0, MOE_EUNSUPPORTED, "%s: K=%d is not a multiple of 8", fn, K);
+    if (rows == 0) return ok();
+    REQUIRE(x && q && scale && workspace, MOE_EINVAL, "%s: null pointer argument", fn);
+    REQUIRE(aligned16(x) && ((uintptr_t)q & 7u) == 0 && ((uintptr_t)workspace & 3u) == 0,
+            MOE_EINVAL, "%s: x must be 16-byte and q 8-byte aligned", fn);
+    return hip_status(qmoe::launch_quant_fp8_tensor_bf16(x, (long long)rows * K, q, scale,
+                                                         (float *)workspace, stream),
+                      fn);
+  }
+  if (mode == MOE_Q_MXFP8) {
+    REQUIRE(E >= 1 && E <= MOE_MAX_EXPERTS, MOE_EINVAL, "%s: E=%d", fn, E);
+    REQUIRE(K % 32 == 0, MOE_EUNSUPPORTED, "%s: K=%d is not a multiple of 32", fn, K);
+    if (rows == 0) return ok();
+    REQUIRE(x && q && scale_e8m0 && m_offsets, MOE_EINVAL, "%s: null pointer argument", fn);
+    REQUIRE(aligned16(x) && aligned16(q), MOE_EINVAL, "%s: x and q must be 16-byte aligned", fn);
+    return hip_status(
+        qmoe::launch_quant_mx_act_bf16(x, rows, K, m_offsets, E, q, scale_e8m0, stream), fn);
+  }
+  return fail(MOE_EINVAL, "%s: unknown mode %d", fn, mode);
+}
+
+int moe_quantize_weights(const float *w, int E, int N, int K, int mode, void *q, float *scale,
+                         uint8_t *scale_e8m0, void *workspace, hipStream_t stream) {
+  const char *fn = "moe_quantize_weights";
+  REQUIRE(E >= 1 && N > 0 && K > 0, MOE_EINVAL, "%s: E=%d N=%d K=%d", fn, E, N, K);
+  REQUIRE(w && q, MOE_EINVAL, "%s: null pointer argument", fn);
+  REQUIRE(aligned16(w) && ((uintptr_t)q & 7u) == 0, MOE_EINVAL,
+          "%s: w must be 16-byte and q 8-byte aligned", fn);
+  const long long per = (long long)N * K;
+  if (mode == MOE_Q_FP8_PER_TENSOR) {
+    REQUIRE(scale && workspace, MOE_EINVAL, "%s: null scale or workspace", fn);
+    REQUIRE(K % 8 == 0, MOE_EUNSUPPORTED, "%s: K=%d is not a multiple of 8", fn, K);
+    REQUIRE(E <= 65535, MOE_EUNSUPPORTED, "%s: E=%d", fn, E);
+    return hip_status(qmoe::launch_quant_fp8_experts_f32(w, E, per, (uint8_t *)q, scale,
+                                                         (float *)workspace, stream),
+                      fn);
+  }
+  if (mode == MOE_Q_INT8_PER_CHANNEL) {
+    REQUIRE(scale, MOE_EINVAL, "%s: null scale", fn);
+    REQUIRE(K % 8 == 0, MOE_EUNSUPPORTED, "%s: K=%d is not a multiple of 8", fn, K);
+    return hip_status(qmoe::launch_quant_int8_rows_f32(w, (long long)E * N, K, (int8_t *)q,
+                                                       scale, stream),
+                      fn);
+  }
+  if (mode == MOE_Q_MXFP8) {
+    REQUIRE(scale_e8m0, MOE_EINVAL, "%s: null scale_e8m0", fn);
+    REQUIRE(aligned16(q), MOE_EINVAL, "%s: q must be 16-byte aligned", fn);
+    REQUIRE(K % 32 == 0, MOE_EUNSUPPORTED, "%s: K=%d is not a multiple of 32", fn, K);
+    return hip_status(
+        qmoe::launch_quant_mx_rows_f32(w, (long long)E * N, K, (uint8_t *)q, scale_e8m0, stream),
+        fn);
+  }
+  return fail(MOE_EINVAL, "%s: unknown mode %d", fn, mode);
+}
+
+int moe_grouped_gemm_fp8w8a8(const uint8_t *a_q, const float *a_scale, const uint8_t *w_q,
+                             const float *w_scale, const int *sorted_token_ids,
+                             const int *expert_ids, const int *num_tokens_post_padded,
+                             const float *topk_weights, int M, int K, int N, int E, int top_k,
+                             int block_m, float *y, hipStream_t stream) {
+  const char *fn = "moe_grouped_gemm_fp8w8a8";
+  int rc = check_routed_gemm(a_q, w_q, w_scale, sorted_token_ids, expert_ids,
+                             num_tokens_post_padded, topk_weights, y, M, K, N, E, top_k, block_m,
+                             128, fn);
+  if (rc) return rc;
+  if (M == 0) return ok();
+  REQUIRE(a_scale, MOE_EINVAL, "%s: null a_scale", fn);
+  qmoe::RoutedArgs r{sorted_token_ids, expert_ids, num_tokens_post_padded, topk_weights, M, K, N,
+                     E, top_k, block_m, (int)(max_padded_ll(M, E, top_k, block_m) / block_m), y};
+  return hip_status(qmoe::launch_gemm_fp8(a_q, a_scale, w_q, w_scale, r, stream), fn);
+}
+
+int moe_grouped_gemm_int8w8a16(const uint16_t *a, const int8_t *w_q, const float *w_scale,
+                               const int *sorted_token_ids, const int *expert_ids,
+                               const int *num_tokens_post_padded, const float *topk_weights,
+                               int M, int K, int N, int E, int top_k, int block_m, float *y,
+                               hipStream_t stream) {
+  const char *fn = "moe_grouped_gemm_int8w8a16";
+  int rc = check_routed_gemm(a, w_q, w_scale, sorted_token_ids, expert_ids,
+                             num_tokens_post_padded, topk_weights, y, M, K, N, E, top_k, block_m,
+                             64, fn);
+  if (rc) return rc;
+  if (M == 0) return ok();
+  qmoe::RoutedArgs r{sorted_token_ids, expert_ids, num_tokens_post_padded, topk_weights, M, K, N,
+                     E, top_k, block_m, (int)(max_padded_ll(M, E, top_k, block_m) / block_m), y};
+  return hip_status(qmoe::launch_gemm_int8(a, w_q, w_scale, r, stream), fn);
+}
+
+int moe_grouped_gemm_mxfp8(const uint8_t *a_q, const uint8_t *a_sf, const uint8_t *w_q,
+                           const uint8_t *w_sf, const int *m_offsets, int rows, int K, int N,
+                           int E, uint16_t *out, hipStream_t stream) {
+  const char *fn = "moe_grouped_gemm_mxfp8";
+  REQUIRE(E >= 1 && E <= MOE_MAX_EXPERTS, MOE_EINVAL, "%s: E=%d", fn, E);
+  REQUIRE(rows >= 0 && K > 0 && N > 0, MOE_EINVAL, "%s: rows=%d K=%d N=%d", fn, rows, K, N);
+  REQUIRE(a_q && a_sf && w_q && w_sf && m_offsets && out, MOE_EINVAL, "%s: null pointer", fn);
+  REQUIRE(aligned16(a_q) && aligned16(w_q) && ((uintptr_t)a_sf & 3u) == 0 &&
+              ((uintptr_t)w_sf & 3u) == 0,
+          MOE_EINVAL, "%s: data must be 16-byte and scales 4-byte aligned", fn);
+  REQUIRE(K % 128 == 0, MOE_EUNSUPPORTED, "%s: K=%d is not a multiple of 128", fn, K);
+  if (rows == 0) return ok();
+  return hip_status(
+      qmoe::launch_gemm_mxfp8(a_q, a_sf, w_q, w_sf, m_offsets, rows, K, N, E, out, stream), fn);
+}
+
+int moe_combine(const float *y, int M, int N, int top_k, uint16_t *out, hipStream_t stream) {
+  const char *fn = "moe_combine";
+  REQUIRE(M >= 0 && N > 0 && top_k >= 1 && top_k <= MOE_MAX_TOPK, MOE_EINVAL,
+          "%s: M=%d N=%d top_k=%d", fn, M, N, top_k);
+  REQUIRE(N % 4 == 0, MOE_EUNSUPPORTED, "%s: N=%d is not a multiple of 4", fn, N);
+  if (M == 0) return ok();
+  REQUIRE(y && out, MOE_EINVAL, "%s: null pointer argument", fn);
+  REQUIRE(aligned16(y) && ((uintptr_t)out & 7u) == 0, MOE_EINVAL,
+          "%s: y must be 16-byte and out 8-byte aligned", fn);
+  return hip_status(qmoe::launch_combine(y, M, N, top_k, out, stream), fn);
+}
+
+}  // extern "C"

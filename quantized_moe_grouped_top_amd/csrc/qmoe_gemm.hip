@@ -1,0 +1,579 @@
+// Grouped GEMMs of the quantized MoE layer on CDNA4 MFMA (gfx950), with the
+// fused epilogue (dequantization scales x router weight, written per routed
+// slot).
+//
+// MFMA operand convention used throughout.  For a 16x16 output tile, lane l of
+// the wavefront owns row (l & 15) of the A operand and column (l & 15) of the
+// B operand; lane group g = l >> 4 owns a quarter of the k values of one
+// instruction, with the same k assignment for A and B:
+//   - fp8 / MXFP8 (v_mfma_f32_16x16x128_f8f6f4 and its scaled form): lane
+//     group g holds k0 + 16g .. k0 + 16g + 15 in its first 16 bytes and
+//     k0 + 64 + 16g .. k0 + 64 + 16g + 15 in its last 16 bytes.  With this
+//     placement the 32 k of scale block s (k0 + 32s .. k0 + 32s + 31) sit in
+//     lane groups 2(s%2) and 2(s%2)+1, and the scaled instruction takes the
+//     e8m0 scale of (row or column l & 15, block s) from lane group s - the
+//     hardware pairing of scale lanes and data lanes, measured on gfx950
+//     (one 16-byte half of a lane belongs to a different block than the other);
+//   - bf16 (v_mfma_f32_16x16x32_bf16): lane group g holds the 16 values
+//     k0 + 16g .. k0 + 16g + 15, split over two instructions (first 8, then
+//     last 8), for A and for B.
+// The accumulator tile has column (l & 15) and rows 4*(l >> 4) + 0..3 in lane l.
+//
+// Two kernels for the routed formats, chosen by block_m:
+//   block_m = 16  : weight streaming for few rows per expert (decode).  One
+//                   workgroup per (64-column tile, expert) keeps all of the
+//                   expert's rows (up to 32 per pass) in registers, so every
+//                   weight byte is read from HBM once.  The 4 wavefronts take
+//                   interleaved k steps (together they read 4 consecutive
+//                   k steps of each weight row) and their partial sums are
+//                   added in LDS in a fixed order.
+//   block_m = 128 : tiled MFMA kernel for many rows per expert.  A 128-row
+//                   block of gathered activations is staged through LDS
+//                   (XOR-swizzled 16-byte chunks, double buffered); each
+//                   wavefront streams its own 64 weight columns straight into
+//                   registers in MFMA layout (int8 converted to bf16 there).
+//                   Tiles are ordered expert by expert, column tile by column
+//                   tile, and split over the 8 XCDs in contiguous chunks, so
+//                   the workgroups resident on one XCD share weight and
+//                   activation tiles through its L2.
+// MXFP8 uses the tiled kernel over expert-contiguous rows, with the scaled
+// MFMA and the e8m0 scales of both operands.
+#include "qmoe_internal.h"
+
+namespace qmoe {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ f32x4 mfma_fp8(const i32x8 &a, const i32x8 &b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_mx(const i32x8 &a, const i32x8 &b, f32x4 c, int sa,
+                                         int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+__device__ __forceinline__ f32x4 mfma_bf16(const i32x4 &a, const i32x4 &b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// 4 signed bytes -> 4 bf16 packed in two dwords (exact: |v| <= 128 fits the
+// 8-bit bf16 significand)
+__device__ __forceinline__ i32x2 i8x4_to_bf16x4(uint32_t d) {
+  const float f0 = (float)(int)(int8_t)(d & 0xFFu);
+  const float f1 = (float)(int)(int8_t)((d >> 8) & 0xFFu);
+  const float f2 = (float)(int)(int8_t)((d >> 16) & 0xFFu);
+  const float f3 = (float)(int)((int32_t)d >> 24);
+  return i32x2{(int)f32x2_to_bf16x2(f0, f1), (int)f32x2_to_bf16x2(f2, f3)};
+}
+
+// 16 int8 (k0+16g .. +15) -> two bf16x8 operands (first 8 k, last 8 k)
+__device__ __forceinline__ void dequant16(const i32x4 &w, i32x4 &b0, i32x4 &b1) {
+  const i32x2 p0 = i8x4_to_bf16x4((uint32_t)w[0]);
+  const i32x2 p1 = i8x4_to_bf16x4((uint32_t)w[1]);
+  const i32x2 p2 = i8x4_to_bf16x4((uint32_t)w[2]);
+  const i32x2 p3 = i8x4_to_bf16x4((uint32_t)w[3]);
+  b0 = i32x4{p0[0], p0[1], p1[0], p1[1]};
+  b1 = i32x4{p2[0], p2[1], p3[0], p3[1]};
+}
+
+__device__ __forceinline__ i32x4 ld16(const void *p) {
+  return *reinterpret_cast<const i32x4 *>(p);
+}
+
+// First block of every expert, from the ascending block labels: s_first[e] =
+// first b in [0, nb) with expert_ids[b] >= e (nb if none), for e in [0, E].
+// All threads of the workgroup take part (one or two loads each, no serial
+// search); the caller synchronises before reading s_first.
+__device__ __forceinline__ void expert_block_starts(const int *__restrict__ expert_ids, int nb,
+                                                    int E, int *s_first) {
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) s_first[e] = nb;
+  __syncthreads();
+  for (int b = threadIdx.x; b < nb; b += blockDim.x) {
+    const int cur = expert_ids[b];
+    const int prev = b > 0 ? expert_ids[b - 1] : -1;
+    for (int e = prev + 1; e <= cur && e <= E; ++e) s_first[e] = b;
+  }
+}
+
+// =============================================================================
+// block_m = 16: weight streaming
+// =============================================================================
+constexpr int kSNT = 4;    // 16-column fragments per wavefront (64 columns)
+constexpr int kSMB = 2;    // 16-row blocks kept in registers per pass
+
+template <bool kInt8>
+struct StreamCfg {
+  static constexpr int kStepK = kInt8 ? 64 : 128;      // k per wavefront step
+  static constexpr int kBVec = kInt8 ? 1 : 2;         // 16-byte B loads per fragment
+};
+
+template <bool kInt8>
+__global__ __launch_bounds__(kThreads) void stream_kernel(
+    const uint8_t *__restrict__ a, const float *__restrict__ a_scale,
+    const uint8_t *__restrict__ w, const float *__restrict__ w_scale,
+    const int *__restrict__ sorted_ids, const int *__restrict__ expert_ids,
+    const int *__restrict__ num_post, const float *__restrict__ topk_w, int M, int K, int N,
+    int top_k, float *__restrict__ y) {
+  using C = StreamCfg<kInt8>;
+  __shared__ f32x4 s_red[4][kSMB][kSNT][64];
+  __shared__ int s_slot[kSMB][16];
+  __shared__ int s_first[kMaxExperts + 1];
+
+  const int e = blockIdx.y;
+  const int n0 = blockIdx.x * (kSNT * 16);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int S = M * top_k;
+
+  expert_block_starts(expert_ids, *num_post / 16, e + 1, s_first);
+  __syncthreads();
+  const int b_begin = s_first[e];
+  const int b_end = s_first[e + 1];
+  if (b_begin >= b_end) return;
+
+  const size_t a_row_bytes = kInt8 ? (size_t)K * 2 : (size_t)K;
+  const int nsteps = K / C::kStepK;
+  // weight rows of this lane's columns (clamped; columns >= N are not stored)
+  const uint8_t *wrow[kSNT];
+#pragma unroll
+  for (int j = 0; j < kSNT; ++j) {
+    int col = n0 + j * 16 + r16;
+    col = col < N ? col : N - 1;
+    wrow[j] = w + ((size_t)e * N + col) * K + 16 * g;
+  }
+  // bytes: bf16 rows hold 16 consecutive values (32 bytes) per lane group;
+  // fp8 rows hold two 16-byte pieces 64 bytes apart
+  const size_t a_lane_off = kInt8 ? (size_t)32 * g : (size_t)16 * g;
+  constexpr int kASecond = kInt8 ? 16 : 64;
+  constexpr int kBSecond = 64;
+  const size_t a_step_bytes = kInt8 ? (size_t)C::kStepK * 2 : (size_t)C::kStepK;
+
+  for (int bp = b_begin; bp < b_end; bp += kSMB) {
+    const int nmb = (b_end - bp) < kSMB ? (b_end - bp) : kSMB;
+    const uint8_t *arow[kSMB];
+#pragma unroll
+    for (int i = 0; i < kSMB; ++i) {
+      int slot = S;
+      if (i < nmb) slot = sorted_ids[(bp + i) * 16 + r16];
+      const int tok = slot < S ? slot / top_k : 0;
+      arow[i] = a + (size_t)tok * a_row_bytes + a_lane_off;
+      if (wave == 0 && g == 0) s_slot[i][r16] = slot;
+    }
+
+    f32x4 acc[kSMB][kSNT];
+#pragma unroll
+    for (int i = 0; i < kSMB; ++i)
+#pragma unroll
+      for (int j = 0; j < kSNT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // double-buffered registers: [buffer][fragment][16-byte vector]
+    i32x4 bb[2][kSNT][C::kBVec];
+    i32x4 ab[2][kSMB][2];
+    auto load = [&](int buf, int s) {
+      const size_t wo = (size_t)s * C::kStepK;                 // weight bytes
+      const size_t ao = (size_t)s * a_step_bytes;
+#pragma unroll
+      for (int j = 0; j < kSNT; ++j)
+#pragma unroll
+        for (int v = 0; v < C::kBVec; ++v) bb[buf][j][v] = ld16(wrow[j] + wo + kBSecond * v);
+#pragma unroll
+      for (int i = 0; i < kSMB; ++i)
+        if (i < nmb) {
+          ab[buf][i][0] = ld16(arow[i] + ao);
+          ab[buf][i][1] = ld16(arow[i] + ao + kASecond);
+        }
+    };
+    auto compute = [&](int buf) {
+#pragma unroll
+      for (int j = 0; j < kSNT; ++j) {
+        if constexpr (kInt8) {
+          i32x4 b0, b1;
+          dequant16(bb[buf][j][0], b0, b1);
+#pragma unroll
+          for (int i = 0; i < kSMB; ++i)
+            if (i < nmb) {
+              acc[i][j] = mfma_bf16(ab[buf][i][0], b0, acc[i][j]);
+              acc[i][j] = mfma_bf16(ab[buf][i][1], b1, acc[i][j]);
+            }
+        } else {
+          const i32x8 b = __builtin_shufflevector(bb[buf][j][0], bb[buf][j][1], 0, 1, 2, 3, 4,
+                                                  5, 6, 7);
+#pragma unroll
+          for (int i = 0; i < kSMB; ++i)
+            if (i < nmb) {
+              const i32x8 av = __builtin_shufflevector(ab[buf][i][0], ab[buf][i][1], 0, 1, 2,
+                                                       3, 4, 5, 6, 7);
+              acc[i][j] = mfma_fp8(av, b, acc[i][j]);
+            }
+        }
+      }
+    };
+
+    int s = wave;
+    if (s < nsteps) load(0, s);
+    while (s < nsteps) {
+      if (s + 4 < nsteps) load(1, s + 4);
+      compute(0);
+      s += 4;
+      if (s >= nsteps) break;
+      if (s + 4 < nsteps) load(0, s + 4);
+      compute(1);
+      s += 4;
+    }
+
+    // ---- fixed-order reduction of the 4 wavefronts' partial sums ----------
+#pragma unroll
+    for (int i = 0; i < kSMB; ++i)
+#pragma unroll
+      for (int j = 0; j < kSNT; ++j) s_red[wave][i][j][lane] = acc[i][j];
+    __syncthreads();
+    const float sa = kInt8 ? 1.0f : a_scale[0] * w_scale[e];
+    for (int q = tid; q < nmb * kSNT * 64; q += kThreads) {
+      const int i = q / (kSNT * 64);
+      const int j = (q / 64) % kSNT;
+      const int l = q & 63;
+      f32x4 v = s_red[0][i][j][l];
+#pragma unroll
+      for (int ww = 1; ww < 4; ++ww) {
+        const f32x4 u = s_red[ww][i][j][l];
+        v[0] += u[0];
+        v[1] += u[1];
+        v[2] += u[2];
+        v[3] += u[3];
+      }
+      const int col = n0 + j * 16 + (l & 15);
+      if (col < N) {
+        const float cs = kInt8 ? w_scale[(size_t)e * N + col] : sa;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int slot = s_slot[i][4 * (l >> 4) + rr];
+          if (slot < S) y[(size_t)slot * N + col] = v[rr] * cs * topk_w[slot];
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// =============================================================================
+// block_m = 128: tiled MFMA kernel (also MXFP8)
+// =============================================================================
+constexpr int kTBM = 128;           // rows per tile
+constexpr int kTNW = 64;            // columns per wavefront
+constexpr int kTBN = 4 * kTNW;      // columns per tile
+constexpr int kTMF = kTBM / 16;     // 16-row fragments per wavefront
+constexpr int kTNF = kTNW / 16;     // 16-column fragments per wavefront
+constexpr int kRowBytes = 128;      // A bytes per row per k step (fp8: 128 k, bf16: 64 k)
+
+// byte offset of 16-byte chunk c of row r in the swizzled LDS A tile
+__device__ __forceinline__ int a_lds_off(int r, int c) {
+  return r * kRowBytes + ((c ^ (r & 7)) << 4);
+}
+
+enum { kFmtFp8 = 0, kFmtInt8 = 1, kFmtMx = 2 };
+
+template <int kFmt>
+__global__ __launch_bounds__(kThreads) void tile_kernel(
+    const uint8_t *__restrict__ a, const float *__restrict__ a_scale,
+    const uint8_t *__restrict__ a_sf, const uint8_t *__restrict__ w,
+    const float *__restrict__ w_scale, const uint8_t *__restrict__ w_sf,
+    const int *__restrict__ sorted_ids, const int *__restrict__ expert_ids,
+    const int *__restrict__ num_post, const float *__restrict__ topk_w,
+    const int *__restrict__ m_offsets, int M, int K, int N, int E, int top_k,
+    float *__restrict__ y, uint16_t *__restrict__ out) {
+  constexpr bool kInt8 = kFmt == kFmtInt8;
+  constexpr bool kMx = kFmt == kFmtMx;
+  constexpr int kStepK = kInt8 ? 64 : 128;             // k per step
+  constexpr int kBVec = kInt8 ? 1 : 2;                 // 16-byte B loads per fragment
+
+  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][kTBM * kRowBytes];
+  __shared__ uint32_t s_asf[2][kTBM];                   // MXFP8 A scales of the step
+  __shared__ int s_row[kTBM];                           // slot (routed) or row (MXFP8)
+  __shared__ int s_blk_first[kMaxExperts + 1];          // first block of every expert
+  __shared__ int s_tile_first[kMaxExperts + 1];         // first tile of every expert
+  __shared__ int s_mo[kMaxExperts + 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int ntn = (N + kTBN - 1) / kTBN;
+
+  // ---- tile space: expert by expert, column tile by column tile, row block fastest
+  if constexpr (!kMx) {
+    expert_block_starts(expert_ids, *num_post / kTBM, E, s_blk_first);
+    __syncthreads();
+  }
+  if (tid == 0) {
+    int blk = 0, tiles = 0;
+    if constexpr (kMx) {
+      for (int e = 0; e <= E; ++e) s_mo[e] = m_offsets[e];
+      for (int e = 0; e < E; ++e) {
+        s_blk_first[e] = blk;
+        s_tile_first[e] = tiles;
+        const int m = s_mo[e + 1] - s_mo[e];
+        const int nblk = m > 0 ? (m + kTBM - 1) / kTBM : 0;
+        blk += nblk;
+        tiles += nblk * ntn;
+      }
+    } else {
+      for (int e = 0; e < E; ++e) {
+        s_tile_first[e] = tiles;
+        tiles += (s_blk_first[e + 1] - s_blk_first[e]) * ntn;
+      }
+      blk = s_blk_first[E];
+    }
+    s_blk_first[E] = blk;
+    s_tile_first[E] = tiles;
+  }
+  __syncthreads();
+  const int total = s_tile_first[E];
+  const int chunk = (total + kXcds - 1) / kXcds;
+  const int xcd = blockIdx.x % kXcds;
+  const int idx = blockIdx.x / kXcds;
+  const int L = xcd * chunk + idx;
+  if (idx >= chunk || L >= total) return;
+  int e = 0;
+  while (s_tile_first[e + 1] <= L) ++e;
+  const int nblk = s_blk_first[e + 1] - s_blk_first[e];
+  const int local = L - s_tile_first[e];
+  const int nt = local / nblk;
+  const int mb = local - nt * nblk;                     // block within the expert
+  const int n0 = nt * kTBN;
+
+  // ---- rows of the tile ----------------------------------------------------
+  const int S = M * top_k;
+  int row_end = 0;                                      // MXFP8: rows of the expert
+  if constexpr (kMx) {
+    row_end = s_mo[e + 1];
+    const int r0 = s_mo[e] + mb * kTBM;
+    for (int r = tid; r < kTBM; r += kThreads) s_row[r] = r0 + r;
+  } else {
+    const int b = s_blk_first[e] + mb;
+    for (int r = tid; r < kTBM; r += kThreads) s_row[r] = sorted_ids[b * kTBM + r];
+  }
+  __syncthreads();
+
+  // A staging: thread t moves 16-byte chunks c = t + 256 q (q < 4): row c >> 3, chunk c & 7
+  const size_t a_row_bytes = kInt8 ? (size_t)K * 2 : (size_t)K;
+  const uint8_t *asrc[4];
+  int adst[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int c = tid + kThreads * q;
+    const int r = c >> 3, ch = c & 7;
+    size_t src_row;
+    if constexpr (kMx) {
+      const int rr = s_row[r];
+      src_row = (size_t)(rr < row_end ? rr : row_end - 1);
+    } else {
+      const int slot = s_row[r];
+      src_row = (size_t)(slot < S ? slot / top_k : 0);
+    }
+    asrc[q] = a + src_row * a_row_bytes + ch * 16;
+    adst[q] = a_lds_off(r, ch);
+  }
+  // MXFP8 A scales: thread t < 128 loads the 4 scale bytes of row t for the step
+  const uint8_t *asf_src = nullptr;
+  const int kb_row = K / 32;
+  if constexpr (kMx) {
+    if (tid < kTBM) {
+      int rr = s_row[tid];
+      int lr = (rr < row_end ? rr : row_end - 1) - s_mo[e];
+      // padded scale row of this data row
+      int po = 0;
+      for (int ee = 0; ee < e; ++ee)
+        po += (s_mo[ee + 1] - s_mo[ee] + kMxRowPad - 1) / kMxRowPad * kMxRowPad;
+      asf_src = a_sf + (size_t)(po + lr) * kb_row;
+    }
+  }
+
+  // B: this wavefront's 64 columns, loaded straight into registers
+  const uint8_t *wrow[kTNF];
+  const uint8_t *wsf_row[kTNF];
+#pragma unroll
+  for (int j = 0; j < kTNF; ++j) {
+    int col = n0 + wave * kTNW + j * 16 + r16;
+    col = col < N ? col : N - 1;
+    wrow[j] = w + ((size_t)e * N + col) * K + 16 * g;
+    wsf_row[j] = kMx ? (w_sf + ((size_t)e * N + col) * kb_row) : nullptr;
+  }
+
+  f32x4 acc[kTMF][kTNF];
+#pragma unroll
+  for (int i = 0; i < kTMF; ++i)
+#pragma unroll
+    for (int j = 0; j < kTNF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nsteps = K / kStepK;
+  i32x4 areg[4];
+  uint32_t asf_reg = 0;
+  i32x4 bb[2][kTNF][kBVec];
+  uint32_t bsf[2][kTNF];
+
+  auto load_a = [&](int s) {
+    const size_t off = (size_t)s * kRowBytes;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) areg[q] = ld16(asrc[q] + off);
+    if constexpr (kMx) {
+      if (tid < kTBM) asf_reg = *reinterpret_cast<const uint32_t *>(asf_src + s * 4);
+    }
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<i32x4 *>(&s_a[buf][adst[q]]) = areg[q];
+    if constexpr (kMx) {
+      if (tid < kTBM) s_asf[buf][tid] = asf_reg;
+    }
+  };
+  auto load_b = [&](int buf, int s) {
+    const size_t off = (size_t)s * kStepK;
+#pragma unroll
+    for (int j = 0; j < kTNF; ++j) {
+#pragma unroll
+      for (int v = 0; v < kBVec; ++v) bb[buf][j][v] = ld16(wrow[j] + off + 64 * v);
+      if constexpr (kMx) bsf[buf][j] = *reinterpret_cast<const uint32_t *>(wsf_row[j] + s * 4);
+    }
+  };
+  auto compute = [&](int buf) {
+    const uint8_t *sa = s_a[buf];
+    i32x4 bdq[kTNF][2];
+    if constexpr (kInt8) {
+#pragma unroll
+      for (int j = 0; j < kTNF; ++j) dequant16(bb[buf][j][0], bdq[j][0], bdq[j][1]);
+    }
+#pragma unroll
+    for (int i = 0; i < kTMF; ++i) {
+      const int r = i * 16 + r16;
+      // bf16: chunks 2g, 2g+1 (16 consecutive values); fp8: chunks g, g+4
+      const i32x4 a0 = *reinterpret_cast<const i32x4 *>(sa + a_lds_off(r, kInt8 ? 2 * g : g));
+      const i32x4 a1 = *reinterpret_cast<const i32x4 *>(sa + a_lds_off(r, kInt8 ? 2 * g + 1 : g + 4));
+      if constexpr (kInt8) {
+#pragma unroll
+        for (int j = 0; j < kTNF; ++j) {
+          acc[i][j] = mfma_bf16(a0, bdq[j][0], acc[i][j]);
+          acc[i][j] = mfma_bf16(a1, bdq[j][1], acc[i][j]);
+        }
+      } else {
+        const i32x8 av = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+        int sa_byte = 0;
+        if constexpr (kMx) sa_byte = (int)((s_asf[buf][r] >> (8 * g)) & 0xFFu);
+#pragma unroll
+        for (int j = 0; j < kTNF; ++j) {
+          const i32x8 bv =
+              __builtin_shufflevector(bb[buf][j][0], bb[buf][j][1], 0, 1, 2, 3, 4, 5, 6, 7);
+          if constexpr (kMx)
+            acc[i][j] = mfma_mx(av, bv, acc[i][j], sa_byte, (int)((bsf[buf][j] >> (8 * g)) & 0xFFu));
+          else
+            acc[i][j] = mfma_fp8(av, bv, acc[i][j]);
+        }
+      }
+    }
+  };
+
+  load_a(0);
+  load_b(0, 0);
+  store_a(0);
+  __syncthreads();
+  for (int s = 0; s < nsteps; s += 2) {
+    // even step: compute buffer 0, prefetch into buffer 1
+    if (s + 1 < nsteps) {
+      load_a(s + 1);
+      load_b(1, s + 1);
+    }
+    compute(0);
+    if (s + 1 < nsteps) store_a(1);
+    __syncthreads();
+    if (s + 1 >= nsteps) break;
+    // odd step: compute buffer 1, prefetch into buffer 0
+    if (s + 2 < nsteps) {
+      load_a(s + 2);
+      load_b(0, s + 2);
+    }
+    compute(1);
+    if (s + 2 < nsteps) store_a(0);
+    __syncthreads();
+  }
+
+  // ---- epilogue --------------------------------------------------------------
+  float cscale = 1.0f;
+  if constexpr (kFmt == kFmtFp8) cscale = a_scale[0] * w_scale[e];
+#pragma unroll
+  for (int j = 0; j < kTNF; ++j) {
+    const int col = n0 + wave * kTNW + j * 16 + r16;
+    if (col >= N) continue;
+    float cs = cscale;
+    if constexpr (kInt8) cs = w_scale[(size_t)e * N + col];
+#pragma unroll
+    for (int i = 0; i < kTMF; ++i) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int r = i * 16 + 4 * g + rr;
+        if constexpr (kMx) {
+          const int row = s_row[r];
+          if (row < row_end)
+            out[(size_t)row * N + col] = (uint16_t)(f32x2_to_bf16x2(acc[i][j][rr], 0.0f) & 0xFFFFu);
+        } else {
+          const int slot = s_row[r];
+          if (slot < S) y[(size_t)slot * N + col] = acc[i][j][rr] * cs * topk_w[slot];
+        }
+      }
+    }
+  }
+}
+
+unsigned tile_grid(long long tiles_bound) {
+  long long per = (tiles_bound + kXcds - 1) / kXcds;
+  return (unsigned)(per * kXcds);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_fp8(const uint8_t *a_q, const float *a_scale, const uint8_t *w_q,
+                           const float *w_scale, const RoutedArgs &r, hipStream_t s) {
+  if (r.block_m == 16) {
+    dim3 grid((r.N + kSNT * 16 - 1) / (kSNT * 16), r.E);
+    hipLaunchKernelGGL(stream_kernel<false>, grid, dim3(kThreads), 0, s, a_q, a_scale, w_q,
+                       w_scale, r.sorted_ids, r.expert_ids, r.num_post, r.topk_w, r.M, r.K, r.N,
+                       r.top_k, r.y);
+  } else {
+    const long long tiles = (long long)r.max_blocks * ((r.N + kTBN - 1) / kTBN);
+    hipLaunchKernelGGL(tile_kernel<kFmtFp8>, dim3(tile_grid(tiles)), dim3(kThreads), 0, s, a_q,
+                       a_scale, nullptr, w_q, w_scale, nullptr, r.sorted_ids, r.expert_ids,
+                       r.num_post, r.topk_w, nullptr, r.M, r.K, r.N, r.E, r.top_k, r.y,
+                       nullptr);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_int8(const uint16_t *a, const int8_t *w_q, const float *w_scale,
+                            const RoutedArgs &r, hipStream_t s) {
+  const uint8_t *ab = reinterpret_cast<const uint8_t *>(a);
+  const uint8_t *wb = reinterpret_cast<const uint8_t *>(w_q);
+  if (r.block_m == 16) {
+    dim3 grid((r.N + kSNT * 16 - 1) / (kSNT * 16), r.E);
+    hipLaunchKernelGGL(stream_kernel<true>, grid, dim3(kThreads), 0, s, ab, nullptr, wb, w_scale,
+                       r.sorted_ids, r.expert_ids, r.num_post, r.topk_w, r.M, r.K, r.N, r.top_k,
+                       r.y);
+  } else {
+    const long long tiles = (long long)r.max_blocks * ((r.N + kTBN - 1) / kTBN);
+    hipLaunchKernelGGL(tile_kernel<kFmtInt8>, dim3(tile_grid(tiles)), dim3(kThreads), 0, s, ab,
+                       nullptr, nullptr, wb, w_scale, nullptr, r.sorted_ids, r.expert_ids,
+                       r.num_post, r.topk_w, nullptr, r.M, r.K, r.N, r.E, r.top_k, r.y, nullptr);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_mxfp8(const uint8_t *a_q, const uint8_t *a_sf, const uint8_t *w_q,
+                             const uint8_t *w_sf, const int *m_offsets, int rows, int K, int N,
+                             int E, uint16_t *out, hipStream_t s) {
+  const long long blocks = (rows + kTBM - 1) / kTBM + E;
+  const long long tiles = blocks * ((N + kTBN - 1) / kTBN);
+  hipLaunchKernelGGL(tile_kernel<kFmtMx>, dim3(tile_grid(tiles)), dim3(kThreads), 0, s, a_q,
+                     nullptr, a_sf, w_q, nullptr, w_sf, nullptr, nullptr, nullptr, nullptr,
+                     m_offsets, rows, K, N, E, 1, nullptr, out);
+  return hipGetLastError();
+}
+
+}  // namespace qmoe

@@ -1,0 +1,144 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/moe.h declares, computes its size helpers on the host, and rejects
+invalid arguments before enqueueing anything (every call here fails
+validation, so no HIP call is made)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_moe_grouped_top_amd as qm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:  # pragma: no cover
+        return False
+
+
+# The error-path calls below pass fake device addresses.  They must never reach
+# a launch, and on a machine with a GPU they are not run at all.
+pytestmark = [
+    pytest.mark.skipif(not os.path.exists(qm.LIB_PATH), reason="libqmoe.so not built"),
+    pytest.mark.skipif(_gpu_visible(), reason="fake-pointer error paths run only without a GPU"),
+]
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) == 13
+    h = ctypes.CDLL(qm.LIB_PATH)
+    for n in names:
+        assert hasattr(h, n), n
+    assert sorted(qm.EXPORTS) == names
+
+
+def test_size_helpers():
+    assert qm.moe_align_max_padded(64, 8, 2, 16) == 128 + 8 * 15 + 8  # rounded up to 16
+    assert qm.moe_align_max_padded(4096, 8, 2, 128) == 8192 + 8 * 127 + 8
+    assert qm.moe_align_max_padded(0, 8, 2, 16) == 8 * 15 + 8
+    for M, E, k, bm in [(1, 4, 2, 16), (37, 8, 2, 128), (4096, 8, 2, 64)]:
+        n = M * k + E * (bm - 1)
+        assert qm.moe_align_max_padded(M, E, k, bm) == -(-n // bm) * bm
+    assert qm.moe_recommended_block_m(64, 8, 2) == 16
+    assert qm.moe_recommended_block_m(4096, 8, 2) == 128
+    assert qm.moe_quantize_workspace_bytes(qm.MOE_Q_FP8_PER_TENSOR, 8) == 8 * 1024 * 4
+    assert qm.moe_quantize_workspace_bytes(qm.MOE_Q_MXFP8, 8) == 0
+    assert qm.moe_mx_scale_rows(32000, 8) == 32000 + 8 * 127
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 0, 2, 16), qm.MOE_EINVAL),            # E = 0
+    ((4, 8, 9, 16), qm.MOE_EINVAL),            # top_k > E
+    ((4, 16, 9, 16), qm.MOE_EUNSUPPORTED),     # top_k above the limit
+    ((4, 8, 2, 24), qm.MOE_EUNSUPPORTED),      # block_m not supported
+    ((-1, 8, 2, 16), qm.MOE_EINVAL),           # M < 0
+    ((40000, 8, 2, 16), qm.MOE_EUNSUPPORTED),  # too many slots
+])
+def test_align_size_errors(args, code):
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_align_max_padded(*args)
+    assert ei.value.code == code
+
+
+FAKE = 1 << 20          # aligned non-null "pointer": validation fails before any use
+MIS = FAKE + 1          # misaligned for every alignment rule
+
+
+def _gemm_fp8(**kw):
+    a = dict(a_q=FAKE, a_scale=FAKE, w_q=FAKE, w_scale=FAKE, sorted_token_ids=FAKE,
+             expert_ids=FAKE, num_tokens_post_padded=FAKE, topk_weights=FAKE, M=64, K=256,
+             N=128, E=8, top_k=2, block_m=16, y=FAKE, stream=0)
+    a.update(kw)
+    return qm.moe_grouped_gemm_fp8w8a8(**a)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=200), qm.MOE_EUNSUPPORTED),        # K not a multiple of 128
+    (dict(block_m=64), qm.MOE_EUNSUPPORTED),
+    (dict(a_q=0), qm.MOE_EINVAL),
+    (dict(w_q=MIS), qm.MOE_EINVAL),
+    (dict(N=0), qm.MOE_EINVAL),
+    (dict(top_k=9), qm.MOE_EINVAL),
+    (dict(E=200, top_k=2), qm.MOE_EINVAL),
+])
+def test_gemm_fp8_rejects(kw, code):
+    with pytest.raises(qm.MoeError) as ei:
+        _gemm_fp8(**kw)
+    assert ei.value.code == code
+    assert qm.lib().moe_last_error()
+
+
+def test_gemm_int8_and_mxfp8_reject():
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_grouped_gemm_int8w8a16(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 96, 128, 8, 2,
+                                      16, FAKE, stream=0)
+    assert ei.value.code == qm.MOE_EUNSUPPORTED                 # K % 64
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_grouped_gemm_mxfp8(FAKE, FAKE, FAKE, FAKE, FAKE, 100, 192, 64, 4, FAKE, stream=0)
+    assert ei.value.code == qm.MOE_EUNSUPPORTED                 # K % 128
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_grouped_gemm_mxfp8(FAKE, MIS, FAKE, FAKE, FAKE, 100, 256, 64, 4, FAKE, stream=0)
+    assert ei.value.code == qm.MOE_EINVAL                       # misaligned scales
+
+
+def test_quantize_and_combine_reject():
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_quantize_act(FAKE, 10, 100, qm.MOE_Q_MXFP8, FAKE, 2, FAKE, None, FAKE, None, stream=0)
+    assert ei.value.code == qm.MOE_EUNSUPPORTED                 # K % 32
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_quantize_act(FAKE, 10, 64, 7, None, 1, FAKE, FAKE, None, FAKE, stream=0)
+    assert ei.value.code == qm.MOE_EINVAL                       # unknown mode
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_quantize_act(FAKE, 10, 64, qm.MOE_Q_FP8_PER_TENSOR, None, 1, FAKE, FAKE, None, None,
+                            stream=0)
+    assert ei.value.code == qm.MOE_EINVAL                       # no workspace
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_quantize_weights(FAKE, 2, 4, 64, qm.MOE_Q_INT8_PER_CHANNEL, FAKE, None, None, None,
+                                stream=0)
+    assert ei.value.code == qm.MOE_EINVAL                       # no scale
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_combine(FAKE, 4, 6, 2, FAKE, stream=0)
+    assert ei.value.code == qm.MOE_EUNSUPPORTED                 # N % 4
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_align_block_size(0, 4, 8, 2, 16, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert ei.value.code == qm.MOE_EINVAL                       # null logits
+
+
+def test_library_missing_is_loud(monkeypatch, tmp_path):
+    monkeypatch.setattr(qm, "LIB_PATH", str(tmp_path / "nope.so"))
+    monkeypatch.setattr(qm, "_lib", None)
+    with pytest.raises(qm.MoeLibraryMissing):
+        qm.lib()

@@ -1,0 +1,337 @@
+"""GPU parity of the HIP library against the CPU oracle, through the C ABI.
+
+Bars:
+* routing choices, the sorted-slot and block-expert buffers, the padded
+  length, every quantized byte and every quantization scale: bit-exact;
+* router weights: within 8 float32 units of the oracle's (the device exp
+  differs from libm's), summing to one within 4 units;
+* grouped GEMM outputs (float32, per routed slot): max |gpu - ref| <=
+  2e-2 * rms(ref) for every case;
+* bf16 layer outputs: see _parity.assert_bf16_out;
+* the combine kernel on its own: bit-exact on seeded synthetic inputs.
+
+Small cases are compared element by element; the workloads at their full
+sizes (in the launch configuration the benchmark times) are compared on
+sampled tokens, columns and rows, which the oracle computes one by one.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import quantized_moe_grouped_top_amd as qm
+from quantized_moe_grouped_top_amd import runner, synth
+from oracle import formats as F
+from oracle import moe as O
+
+from _parity import (assert_bf16_out, assert_close_rms, bits16, oracle_weights_rows, pick)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+F32_EPS = float(np.finfo(np.float32).eps)
+
+
+def _announce(what):
+    print(f"\n[parity] {what}", flush=True)
+
+
+# ----------------------------------------------------------------------------
+# routed formats
+# ----------------------------------------------------------------------------
+def run_routed(wl, block_m=None, variant=0, full=True, n_tok=48, n_col=64, logits=None):
+    _announce(f"{wl.name} block_m={block_m} full={full}")
+    M, K, N, E, top_k = wl.M, wl.K, wl.N, wl.E, wl.top_k
+    case = synth.make_case(wl, variant, device=DEV)
+    x, w = case["x"], case["w"]
+    lg = case["logits"] if logits is None else logits.to(DEV)
+    moe = runner.RoutedMoE(wl.fmt, M, K, N, E, top_k, block_m=block_m)
+    w_q, w_scale = runner.quantize_weights(w, wl.fmt)
+    moe.y.fill_(float("nan"))
+    moe.out.fill_(0x7FC0)
+    moe.forward(x, lg, w_q, w_scale)
+    torch.cuda.synchronize()
+
+    rng = np.random.default_rng(synth.seed_of(wl.name, 99) % (1 << 32))
+    lg_np = lg.cpu().numpy()
+    x_np = bits16(x)
+
+    # ---- routing and alignment: bit-exact -----------------------------------
+    ids_ref, wts_ref = O.route_topk(lg_np, top_k)
+    np.testing.assert_array_equal(moe.topk_ids.cpu().numpy(), ids_ref)
+    wts = moe.topk_weights.cpu().numpy()
+    np.testing.assert_allclose(wts, wts_ref, rtol=8 * F32_EPS, atol=1e-44)  # denormal weights
+    assert np.max(np.abs(wts.astype(np.float64).sum(1) - 1.0)) <= 4 * F32_EPS
+    s_ref, e_ref, n_ref = O.align_block_size(ids_ref, E, moe.block_m)
+    assert int(moe.num_tokens_post_padded.item()) == n_ref
+    np.testing.assert_array_equal(moe.sorted_token_ids.cpu().numpy(), s_ref)
+    np.testing.assert_array_equal(moe.expert_ids.cpu().numpy(), e_ref)
+
+    # ---- which outputs the oracle computes ----------------------------------
+    if full:
+        toks, cols = np.arange(M), np.arange(N)
+    else:
+        toks = pick(M, n_tok, rng, must=(0, M - 1))
+        cols = pick(N, n_col, rng, must=(0, N - 1, N // 2))
+    slots = (toks[:, None] * top_k + np.arange(top_k)[None, :]).reshape(-1)
+
+    # ---- weights: bit-exact quantization of the checked rows ----------------
+    wq_rows, ws_ref = oracle_weights_rows(w, wl.fmt, cols)
+    wq_dev = w_q.index_select(1, torch.as_tensor(cols, device=DEV)).cpu().numpy()
+    np.testing.assert_array_equal(wq_dev, wq_rows)
+    if wl.fmt == "fp8":
+        np.testing.assert_array_equal(w_scale.cpu().numpy(), ws_ref)
+    else:
+        np.testing.assert_array_equal(w_scale.cpu().numpy()[:, cols], ws_ref)
+    # oracle weight tensors holding only the checked columns (other rows unused)
+    wq_full = np.zeros((E, N, K), dtype=wq_rows.dtype)
+    wq_full[:, cols] = wq_rows
+    if wl.fmt == "fp8":
+        ws_full = ws_ref
+    else:
+        ws_full = np.zeros((E, N), np.float32)
+        ws_full[:, cols] = ws_ref
+
+    # ---- activations and the GEMM --------------------------------------------
+    if wl.fmt == "fp8":
+        xv = F.bf16_decode(x_np).astype(np.float32)
+        sa = O.fp8_tensor_scale(xv)
+        assert moe.a_scale.item() == float(sa)
+        aq_rows = O.fp8_quantize_with_scale(xv[toks], sa)
+        np.testing.assert_array_equal(moe.a_q.cpu().numpy()[toks], aq_rows)
+        aq_full = np.zeros((M, K), np.uint8)
+        aq_full[toks] = aq_rows
+        y_ref = O.grouped_gemm_fp8w8a8(aq_full, sa, wq_full, ws_full, ids_ref, wts_ref, slots, cols)
+    else:
+        y_ref = O.grouped_gemm_int8w8a16(x_np, wq_full, ws_full, ids_ref, wts_ref, slots, cols)
+    y_gpu = moe.y.cpu().numpy()[np.ix_(slots, cols)]
+    assert_close_rms(y_gpu, y_ref, f"{wl.name} y")
+
+    # ---- combine ---------------------------------------------------------------
+    out32_ref, out_ref = O.combine(y_ref, top_k)
+    out_gpu = bits16(moe.out)[np.ix_(toks, cols)]
+    assert_bf16_out(out_gpu, out32_ref, out_ref, f"{wl.name} out")
+    return moe
+
+
+SMALL = [
+    synth.WORKLOADS["fp8_m64_k128_n256"],
+    synth.small("fp8", 37, 256, 200, 8, 2),
+    synth.small("fp8", 300, 384, 320, 8, 2, bias_std=1.5),
+    synth.small("int8", 50, 320, 136, 6, 3),
+    synth.small("int8", 300, 256, 272, 8, 2, bias_std=1.5),
+    synth.small("fp8", 1, 128, 64, 8, 2),
+    synth.small("int8", 40, 128, 48, 1, 1),
+    synth.small("fp8", 33, 256, 96, 4, 4),
+]
+
+
+@pytest.mark.parametrize("block_m", [16, 128])
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_routed_small(wl, block_m):
+    run_routed(wl, block_m=block_m, full=True)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+@pytest.mark.parametrize("block_m", [16, 128])
+def test_routed_all_tokens_one_expert(fmt, block_m):
+    wl = synth.small(fmt, 150, 256, 80, 8, 2)
+    lg = torch.randn(150, 8, generator=torch.Generator().manual_seed(5))
+    lg[:, 3] += 100.0                        # every token picks expert 3 first
+    run_routed(wl, block_m=block_m, full=True, logits=lg)
+
+
+def test_routed_empty_batch():
+    _announce("M = 0")
+    moe = runner.RoutedMoE("fp8", 0, 128, 64, 8, 2, block_m=16)
+    lg = torch.empty(0, 8, device=DEV)
+    moe.route(lg)
+    torch.cuda.synchronize()
+    assert int(moe.num_tokens_post_padded.item()) == 0
+    assert torch.all(moe.sorted_token_ids == 0)          # the sentinel M*top_k = 0
+    assert torch.all(moe.expert_ids == -1)
+    w_q, w_s = runner.quantize_weights(torch.randn(8, 64, 128, device=DEV), "fp8")
+    # a GEMM and a combine with M = 0 are no-ops
+    qm.moe_grouped_gemm_fp8w8a8(moe.a_q, moe.a_scale, w_q, w_s, moe.sorted_token_ids,
+                                moe.expert_ids, moe.num_tokens_post_padded, moe.topk_weights, 0,
+                                128, 64, 8, 2, 16, moe.y)
+    qm.moe_combine(moe.y, 0, 64, 2, moe.out)
+    torch.cuda.synchronize()
+
+
+def test_routed_deterministic():
+    wl = synth.small("fp8", 300, 384, 320, 8, 2, bias_std=1.5)
+    case = synth.make_case(wl, 0, device=DEV)
+    for bm in (16, 128):
+        _announce(f"determinism block_m={bm}")
+        moe = runner.RoutedMoE("fp8", wl.M, wl.K, wl.N, wl.E, wl.top_k, block_m=bm)
+        w_q, w_s = runner.quantize_weights(case["w"], "fp8")
+        moe.forward(case["x"], case["logits"], w_q, w_s)
+        y1, o1 = moe.y.clone(), moe.out.clone()
+        moe.y.fill_(float("nan"))
+        moe.forward(case["x"], case["logits"], w_q, w_s)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int32), moe.y.view(torch.int32))
+        assert torch.equal(o1, moe.out)
+
+
+FULL = [synth.WORKLOADS[n] for n in [
+    "int8w8a16_m64_k4096_n14336",
+    "fp8_bias_m128_k4096_n14336", "fp8_bias_m512_k4096_n14336",
+    "fp8_bias_m1024_k4096_n14336", "fp8_bias_m4096_k4096_n14336",
+    "mistral7b_up_fp8_m4096_k4096_n28672", "mistral7b_down_fp8_m4096_k14336_n4096",
+    "mistral7b_up_int8_m4096_k4096_n28672", "mistral7b_down_int8_m4096_k14336_n4096",
+]]
+
+
+@pytest.mark.parametrize("wl", FULL, ids=[w.name for w in FULL])
+def test_routed_full_size_sampled(wl):
+    run_routed(wl, block_m=None, full=False)
+    torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------
+# MXFP8
+# ----------------------------------------------------------------------------
+def run_mx(wl, full=True, n_row=64, n_col=64):
+    _announce(f"{wl.name} full={full}")
+    case = synth.make_case(wl, 0, device=DEV)
+    x, w, mo = case["x"], case["w"], case["m_offsets"]
+    R, K, N, E = wl.M, wl.K, wl.N, wl.E
+    moe = runner.MxMoE(R, K, N, E)
+    w_q, w_sf = runner.quantize_weights(w, "mxfp8")
+    moe.a_sf.fill_(0xAB)
+    moe.out.fill_(0x7FC0)
+    moe.forward(x, mo, w_q, w_sf)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(synth.seed_of(wl.name, 98) % (1 << 32))
+    mo_np = mo.cpu().numpy().astype(np.int64)
+    po = O.mx_padded_offsets(mo_np)
+    x_np = bits16(x)
+    rows = np.arange(R) if full else pick(R, n_row, rng, must=tuple(mo_np[:-1]) + (R - 1,))
+    cols = np.arange(N) if full else pick(N, n_col, rng, must=(0, N - 1))
+
+    # activations: bit-exact data and padded scales
+    a_sf = moe.a_sf.cpu().numpy()
+    if full:
+        q_ref, sf_ref = O.quantize_act_mxfp8(x_np, mo_np)
+        np.testing.assert_array_equal(moe.a_q.cpu().numpy(), q_ref)
+        np.testing.assert_array_equal(a_sf[:po[-1]], sf_ref)
+    q_rows, b_rows = O.quantize_mxfp8_rows(F.bf16_decode(x_np[rows]).astype(np.float32))
+    np.testing.assert_array_equal(moe.a_q.cpu().numpy()[rows], q_rows)
+    e_of = np.searchsorted(mo_np, rows, side="right") - 1
+    np.testing.assert_array_equal(a_sf[po[e_of] + rows - mo_np[e_of]], b_rows)
+    for e in range(E):                       # pad rows of every expert's block are zero
+        assert np.all(a_sf[po[e] + (mo_np[e + 1] - mo_np[e]):po[e + 1]] == 0)
+
+    # weights: bit-exact on the checked rows
+    wq_rows, wsf_rows = oracle_weights_rows(w, "mxfp8", cols)
+    ct = torch.as_tensor(cols, device=DEV)
+    np.testing.assert_array_equal(w_q.index_select(1, ct).cpu().numpy(), wq_rows)
+    np.testing.assert_array_equal(w_sf.index_select(1, ct).cpu().numpy(), wsf_rows)
+
+    # GEMM output
+    aq_full = np.zeros((R, K), np.uint8)
+    aq_full[rows] = q_rows
+    asf_full = np.zeros((int(po[-1]), K // 32), np.uint8)
+    asf_full[po[e_of] + rows - mo_np[e_of]] = b_rows
+    wq_full = np.zeros((E, N, K), np.uint8)
+    wq_full[:, cols] = wq_rows
+    wsf_full = np.zeros((E, N, K // 32), np.uint8)
+    wsf_full[:, cols] = wsf_rows
+    out_ref = O.grouped_gemm_mxfp8(aq_full, asf_full, wq_full, wsf_full, mo_np, rows, cols)
+    out_gpu = bits16(moe.out)[np.ix_(rows, cols)]
+    ref32 = F.bf16_decode(out_ref)
+    assert_close_rms(F.bf16_decode(out_gpu), ref32, f"{wl.name} out")
+    assert_bf16_out(out_gpu, ref32, out_ref, f"{wl.name} out")
+
+
+MX_SMALL = [synth.small("mxfp8", 0, 256, 136, 0, 1, seg=(5, 130, 0, 77)),
+            synth.small("mxfp8", 0, 128, 64, 0, 1, seg=(128, 128)),
+            synth.small("mxfp8", 0, 384, 16, 0, 1, seg=(1,))]
+
+
+@pytest.mark.parametrize("wl", MX_SMALL, ids=[w.name for w in MX_SMALL])
+def test_mxfp8_small(wl):
+    run_mx(wl, full=True)
+
+
+MX_FULL = [synth.WORKLOADS["mxfp8_8x4000_k4096_n4096"], synth.WORKLOADS["mxfp8_22b_8x4000_k6144_n32768"]]
+
+
+@pytest.mark.parametrize("wl", MX_FULL, ids=[w.name for w in MX_FULL])
+def test_mxfp8_full_size_sampled(wl):
+    run_mx(wl, full=False)
+    torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------
+# codecs through the library
+# ----------------------------------------------------------------------------
+def _structured_values():
+    hi = np.arange(1 << 17, dtype=np.uint64) << 15
+    lows = np.array([0, 1, 0x3FFF, 0x4000, 0x4001, 0x7FFF], dtype=np.uint64)
+    bits = (hi[:, None] | lows[None, :]).reshape(-1).astype(np.uint32)
+    v = bits.view(np.float32)
+    v = v[np.isfinite(v) & (np.abs(v) <= 448.0)]
+    rnd = np.random.default_rng(1).uniform(-448, 448, size=1 << 20).astype(np.float32)
+    return np.concatenate([v, rnd, np.array([448.0], np.float32)])
+
+
+def test_fp8_encoder_structured_values():
+    """Weights whose largest magnitude is 448 have scale 1, so the fp8 weight
+    quantizer returns e4m3(w) for every value: all rounding decisions of the
+    device conversion against the oracle's encoder."""
+    _announce("e4m3 encoder")
+    v = _structured_values()
+    K = 512
+    n = -(-v.size // K) * K
+    vals = np.zeros(n, np.float32)
+    vals[:v.size] = v
+    vals[-1] = 448.0
+    w = torch.from_numpy(vals.reshape(1, n // K, K)).to(DEV)
+    q, s = runner.quantize_weights(w, "fp8")
+    torch.cuda.synchronize()
+    assert s.item() == 1.0
+    np.testing.assert_array_equal(q.cpu().numpy().reshape(-1), F.e4m3_encode(vals))
+
+
+def test_int8_quantizer_full():
+    _announce("int8 quantizer")
+    w = torch.randn(3, 40, 256, device=DEV) * torch.tensor([1.0, 1e-3, 50.0], device=DEV)[:, None, None]
+    w[1, 7] = 0.0
+    q, s = runner.quantize_weights(w, "int8")
+    torch.cuda.synchronize()
+    q_ref, s_ref = O.quantize_weight_int8(w.cpu().numpy())
+    np.testing.assert_array_equal(q.cpu().numpy(), q_ref)
+    np.testing.assert_array_equal(s.cpu().numpy(), s_ref)
+
+
+def test_fp8_activation_quantizer_full():
+    _announce("fp8 activation quantizer")
+    for M, K, scale in [(64, 128, 1.0), (333, 1024, 3e-3), (7, 8, 1e4)]:
+        x = (torch.randn(M, K, device=DEV) * scale).to(torch.bfloat16)
+        q = torch.empty(M, K, dtype=torch.uint8, device=DEV)
+        s = torch.empty(1, dtype=torch.float32, device=DEV)
+        ws = torch.empty(qm.moe_quantize_workspace_bytes(qm.MOE_Q_FP8_PER_TENSOR, 1), dtype=torch.uint8, device=DEV)
+        qm.moe_quantize_act(x, M, K, qm.MOE_Q_FP8_PER_TENSOR, None, 1, q, s, None, ws)
+        torch.cuda.synchronize()
+        q_ref, s_ref = O.quantize_act_fp8(bits16(x))
+        assert s.item() == float(s_ref)
+        np.testing.assert_array_equal(q.cpu().numpy(), q_ref)
+
+
+def test_combine_bit_exact():
+    _announce("combine")
+    rng = np.random.default_rng(3)
+    for M, N, top_k in [(64, 256, 2), (37, 100, 3), (5, 8, 1), (128, 4096, 8)]:
+        y = rng.standard_normal((M * top_k, N)).astype(np.float32)
+        # rounding ties and binade edges of bf16
+        special = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 3.99999,
+                            65504.0, 1e-40, -0.0, 2.0 ** -126] * 8, np.float32)
+        n = min(special.size, y.size)
+        y.reshape(-1)[:n] = special[:n]
+        out = torch.empty(M, N, dtype=torch.int16, device=DEV)
+        qm.moe_combine(torch.from_numpy(y).to(DEV), M, N, top_k, out)
+        torch.cuda.synchronize()
+        _, ref = O.combine(y, top_k)
+        np.testing.assert_array_equal(bits16(out), ref)

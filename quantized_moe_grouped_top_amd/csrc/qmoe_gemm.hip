@@ -108,16 +108,18 @@ template <bool kInt8>
 struct StreamCfg {
   static constexpr int kStepK = kInt8 ? 64 : 128;      // k per wavefront step
   static constexpr int kBVec = kInt8 ? 1 : 2;         // 16-byte B loads per fragment
+  static constexpr int kRing = 3;                      // register stages (steps in flight + 1)
 };
 
 template <bool kInt8>
-__global__ __launch_bounds__(kThreads) void stream_kernel(
+__global__ __launch_bounds__(kThreads, 2) void stream_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ w, const float *__restrict__ w_scale,
     const int *__restrict__ sorted_ids, const int *__restrict__ expert_ids,
     const int *__restrict__ num_post, const float *__restrict__ topk_w, int M, int K, int N,
     int top_k, float *__restrict__ y) {
   using C = StreamCfg<kInt8>;
+  constexpr int R = C::kRing;
   __shared__ f32x4 s_red[4][kSMB][kSNT][64];
   __shared__ int s_slot[kSMB][16];
   __shared__ int s_first[kMaxExperts + 1];
@@ -134,32 +136,34 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(
   const int b_end = s_first[e + 1];
   if (b_begin >= b_end) return;
 
-  const size_t a_row_bytes = kInt8 ? (size_t)K * 2 : (size_t)K;
+  const uint32_t a_row_bytes = kInt8 ? (uint32_t)K * 2 : (uint32_t)K;
   const int nsteps = K / C::kStepK;
+  // this wavefront's steps: wave, wave + 4, ... (the 4 wavefronts together
+  // read 4 consecutive steps of every weight row)
+  const int nmy = nsteps > wave ? (nsteps - wave + 3) / 4 : 0;
   // weight rows of this lane's columns (clamped; columns >= N are not stored)
-  const uint8_t *wrow[kSNT];
+  uint32_t woff[kSNT];
 #pragma unroll
   for (int j = 0; j < kSNT; ++j) {
     int col = n0 + j * 16 + r16;
     col = col < N ? col : N - 1;
-    wrow[j] = w + ((size_t)e * N + col) * K + 16 * g;
+    woff[j] = ((uint32_t)e * (uint32_t)N + (uint32_t)col) * (uint32_t)K + 16u * g;
   }
-  // bytes: bf16 rows hold 16 consecutive values (32 bytes) per lane group;
-  // fp8 rows hold two 16-byte pieces 64 bytes apart
-  const size_t a_lane_off = kInt8 ? (size_t)32 * g : (size_t)16 * g;
+  // bf16 rows hold 16 consecutive values (32 bytes) per lane group; fp8 rows
+  // hold two 16-byte pieces 64 bytes apart
+  const uint32_t a_lane_off = kInt8 ? 32u * g : 16u * g;
   constexpr int kASecond = kInt8 ? 16 : 64;
-  constexpr int kBSecond = 64;
-  const size_t a_step_bytes = kInt8 ? (size_t)C::kStepK * 2 : (size_t)C::kStepK;
+  constexpr uint32_t kAStep = kInt8 ? C::kStepK * 2 : C::kStepK;   // A bytes per step
 
   for (int bp = b_begin; bp < b_end; bp += kSMB) {
     const int nmb = (b_end - bp) < kSMB ? (b_end - bp) : kSMB;
-    const uint8_t *arow[kSMB];
+    uint32_t aoff[kSMB];
 #pragma unroll
     for (int i = 0; i < kSMB; ++i) {
       int slot = S;
       if (i < nmb) slot = sorted_ids[(bp + i) * 16 + r16];
-      const int tok = slot < S ? slot / top_k : 0;
-      arow[i] = a + (size_t)tok * a_row_bytes + a_lane_off;
+      const int tok = slot < S ? slot / top_k : 0;    // padding rows read token 0
+      aoff[i] = (uint32_t)tok * a_row_bytes + a_lane_off;
       if (wave == 0 && g == 0) s_slot[i][r16] = slot;
     }
 
@@ -169,59 +173,67 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(
 #pragma unroll
       for (int j = 0; j < kSNT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // double-buffered registers: [buffer][fragment][16-byte vector]
-    i32x4 bb[2][kSNT][C::kBVec];
-    i32x4 ab[2][kSMB][2];
-    auto load = [&](int buf, int s) {
-      const size_t wo = (size_t)s * C::kStepK;                 // weight bytes
-      const size_t ao = (size_t)s * a_step_bytes;
+    struct Stage {
+      i32x4 b[kSNT][C::kBVec];
+      i32x4 a[kSMB][2];
+    };
+    Stage st[R];
+    // t-th step of this wavefront, clamped to its last one (repeated loads at
+    // the end keep the loop free of branches and the wait counts exact)
+    auto load = [&](Stage &x, int t) {
+      const int tt = t < nmy ? t : nmy - 1;
+      const int sidx = wave + 4 * tt;
+      const uint8_t *wb = w + (size_t)sidx * C::kStepK;
+      const uint8_t *ab = a + (size_t)sidx * kAStep;
 #pragma unroll
       for (int j = 0; j < kSNT; ++j)
 #pragma unroll
-        for (int v = 0; v < C::kBVec; ++v) bb[buf][j][v] = ld16(wrow[j] + wo + kBSecond * v);
+        for (int v = 0; v < C::kBVec; ++v) x.b[j][v] = ld16(wb + woff[j] + 64 * v);
 #pragma unroll
-      for (int i = 0; i < kSMB; ++i)
-        if (i < nmb) {
-          ab[buf][i][0] = ld16(arow[i] + ao);
-          ab[buf][i][1] = ld16(arow[i] + ao + kASecond);
-        }
+      for (int i = 0; i < kSMB; ++i) {
+        x.a[i][0] = ld16(ab + aoff[i]);
+        x.a[i][1] = ld16(ab + aoff[i] + kASecond);
+      }
     };
-    auto compute = [&](int buf) {
+    auto compute = [&](const Stage &x) {
 #pragma unroll
       for (int j = 0; j < kSNT; ++j) {
         if constexpr (kInt8) {
           i32x4 b0, b1;
-          dequant16(bb[buf][j][0], b0, b1);
+          dequant16(x.b[j][0], b0, b1);
 #pragma unroll
-          for (int i = 0; i < kSMB; ++i)
-            if (i < nmb) {
-              acc[i][j] = mfma_bf16(ab[buf][i][0], b0, acc[i][j]);
-              acc[i][j] = mfma_bf16(ab[buf][i][1], b1, acc[i][j]);
-            }
+          for (int i = 0; i < kSMB; ++i) {
+            acc[i][j] = mfma_bf16(x.a[i][0], b0, acc[i][j]);
+            acc[i][j] = mfma_bf16(x.a[i][1], b1, acc[i][j]);
+          }
         } else {
-          const i32x8 b = __builtin_shufflevector(bb[buf][j][0], bb[buf][j][1], 0, 1, 2, 3, 4,
-                                                  5, 6, 7);
+          const i32x8 bv = __builtin_shufflevector(x.b[j][0], x.b[j][1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-          for (int i = 0; i < kSMB; ++i)
-            if (i < nmb) {
-              const i32x8 av = __builtin_shufflevector(ab[buf][i][0], ab[buf][i][1], 0, 1, 2,
-                                                       3, 4, 5, 6, 7);
-              acc[i][j] = mfma_fp8(av, b, acc[i][j]);
-            }
+          for (int i = 0; i < kSMB; ++i) {
+            const i32x8 av =
+                __builtin_shufflevector(x.a[i][0], x.a[i][1], 0, 1, 2, 3, 4, 5, 6, 7);
+            acc[i][j] = mfma_fp8(av, bv, acc[i][j]);
+          }
         }
       }
     };
 
-    int s = wave;
-    if (s < nsteps) load(0, s);
-    while (s < nsteps) {
-      if (s + 4 < nsteps) load(1, s + 4);
-      compute(0);
-      s += 4;
-      if (s >= nsteps) break;
-      if (s + 4 < nsteps) load(0, s + 4);
-      compute(1);
-      s += 4;
+    if (nmy > 0) {
+#pragma unroll
+      for (int r = 0; r < R - 1; ++r) load(st[r], r);
+      int t = 0;
+      for (; t + R <= nmy; t += R) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          load(st[(r + R - 1) % R], t + r + R - 1);
+          __builtin_amdgcn_sched_barrier(0);
+          compute(st[r]);
+        }
+      }
+      // the last nmy - t (< R) steps are already in stages 0 .. R-2
+#pragma unroll
+      for (int r = 0; r < R - 1; ++r)
+        if (t + r < nmy) compute(st[r]);
     }
 
     // ---- fixed-order reduction of the 4 wavefronts' partial sums ----------
@@ -276,7 +288,7 @@ __device__ __forceinline__ int a_lds_off(int r, int c) {
 enum { kFmtFp8 = 0, kFmtInt8 = 1, kFmtMx = 2 };
 
 template <int kFmt>
-__global__ __launch_bounds__(kThreads) void tile_kernel(
+__global__ __launch_bounds__(kThreads, 2) void tile_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ a_sf, const uint8_t *__restrict__ w,
     const float *__restrict__ w_scale, const uint8_t *__restrict__ w_sf,
@@ -355,49 +367,52 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(
   }
   __syncthreads();
 
-  // A staging: thread t moves 16-byte chunks c = t + 256 q (q < 4): row c >> 3, chunk c & 7
-  const size_t a_row_bytes = kInt8 ? (size_t)K * 2 : (size_t)K;
-  const uint8_t *asrc[4];
-  int adst[4];
+  // A staging: thread t moves the 16-byte chunk (t & 7) of rows (t >> 3) + 32q,
+  // q < 4.  All four rows share the swizzle (row & 7), so the LDS targets are
+  // 4096 bytes apart.  Offsets are 32-bit: the tensors are below 4 GiB.
+  const uint32_t a_row_bytes = kInt8 ? (uint32_t)K * 2 : (uint32_t)K;
+  const int ach = tid & 7;
+  uint32_t aoff[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int c = tid + kThreads * q;
-    const int r = c >> 3, ch = c & 7;
-    size_t src_row;
+    const int r = (tid >> 3) + 32 * q;
+    uint32_t src_row;
     if constexpr (kMx) {
       const int rr = s_row[r];
-      src_row = (size_t)(rr < row_end ? rr : row_end - 1);
+      src_row = (uint32_t)(rr < row_end ? rr : row_end - 1);
     } else {
       const int slot = s_row[r];
-      src_row = (size_t)(slot < S ? slot / top_k : 0);
+      src_row = (uint32_t)(slot < S ? slot / top_k : 0);
     }
-    asrc[q] = a + src_row * a_row_bytes + ch * 16;
-    adst[q] = a_lds_off(r, ch);
+    aoff[q] = src_row * a_row_bytes + (uint32_t)ach * 16u;
   }
+  const int adst = a_lds_off(tid >> 3, ach);
   // MXFP8 A scales: thread t < 128 loads the 4 scale bytes of row t for the step
-  const uint8_t *asf_src = nullptr;
+  uint32_t asf_off = 0;
   const int kb_row = K / 32;
   if constexpr (kMx) {
     if (tid < kTBM) {
-      int rr = s_row[tid];
-      int lr = (rr < row_end ? rr : row_end - 1) - s_mo[e];
-      // padded scale row of this data row
-      int po = 0;
+      const int rr = s_row[tid];
+      const int lr = (rr < row_end ? rr : row_end - 1) - s_mo[e];
+      int po = 0;                                       // padded scale row of the expert
       for (int ee = 0; ee < e; ++ee)
         po += (s_mo[ee + 1] - s_mo[ee] + kMxRowPad - 1) / kMxRowPad * kMxRowPad;
-      asf_src = a_sf + (size_t)(po + lr) * kb_row;
+      asf_off = (uint32_t)(po + lr) * (uint32_t)kb_row;
     }
   }
+  // A fragment reads: row i*16 + r16, chunks c0/c1; same swizzle for every i
+  const int rd0 = a_lds_off(r16, kInt8 ? 2 * g : g);
+  const int rd1 = a_lds_off(r16, kInt8 ? 2 * g + 1 : g + 4);
 
   // B: this wavefront's 64 columns, loaded straight into registers
-  const uint8_t *wrow[kTNF];
-  const uint8_t *wsf_row[kTNF];
+  uint32_t woff[kTNF];
+  uint32_t wsoff[kTNF];
 #pragma unroll
   for (int j = 0; j < kTNF; ++j) {
     int col = n0 + wave * kTNW + j * 16 + r16;
     col = col < N ? col : N - 1;
-    wrow[j] = w + ((size_t)e * N + col) * K + 16 * g;
-    wsf_row[j] = kMx ? (w_sf + ((size_t)e * N + col) * kb_row) : nullptr;
+    woff[j] = ((uint32_t)e * (uint32_t)N + (uint32_t)col) * (uint32_t)K + 16u * g;
+    wsoff[j] = ((uint32_t)e * (uint32_t)N + (uint32_t)col) * (uint32_t)kb_row;
   }
 
   f32x4 acc[kTMF][kTNF];
@@ -407,48 +422,48 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(
     for (int j = 0; j < kTNF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nsteps = K / kStepK;
+  struct BRegs {
+    i32x4 v[kTNF][kBVec];
+    uint32_t sf[kTNF];
+  };
+  BRegs b0, b1;
   i32x4 areg[4];
   uint32_t asf_reg = 0;
-  i32x4 bb[2][kTNF][kBVec];
-  uint32_t bsf[2][kTNF];
 
   auto load_a = [&](int s) {
-    const size_t off = (size_t)s * kRowBytes;
+    const uint8_t *base = a + (size_t)s * kRowBytes;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) areg[q] = ld16(asrc[q] + off);
+    for (int q = 0; q < 4; ++q) areg[q] = ld16(base + aoff[q]);
     if constexpr (kMx) {
-      if (tid < kTBM) asf_reg = *reinterpret_cast<const uint32_t *>(asf_src + s * 4);
+      if (tid < kTBM) asf_reg = *reinterpret_cast<const uint32_t *>(a_sf + asf_off + 4 * s);
     }
   };
-  auto store_a = [&](int buf) {
+  auto store_a = [&](uint8_t *lds, uint32_t *lds_sf) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) *reinterpret_cast<i32x4 *>(&s_a[buf][adst[q]]) = areg[q];
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<i32x4 *>(lds + adst + 4096 * q) = areg[q];
     if constexpr (kMx) {
-      if (tid < kTBM) s_asf[buf][tid] = asf_reg;
+      if (tid < kTBM) lds_sf[tid] = asf_reg;
     }
   };
-  auto load_b = [&](int buf, int s) {
-    const size_t off = (size_t)s * kStepK;
+  auto load_b = [&](BRegs &bb, int s) {
+    const uint8_t *base = w + (size_t)s * kStepK;
 #pragma unroll
     for (int j = 0; j < kTNF; ++j) {
 #pragma unroll
-      for (int v = 0; v < kBVec; ++v) bb[buf][j][v] = ld16(wrow[j] + off + 64 * v);
-      if constexpr (kMx) bsf[buf][j] = *reinterpret_cast<const uint32_t *>(wsf_row[j] + s * 4);
+      for (int v = 0; v < kBVec; ++v) bb.v[j][v] = ld16(base + woff[j] + 64 * v);
+      if constexpr (kMx) bb.sf[j] = *reinterpret_cast<const uint32_t *>(w_sf + wsoff[j] + 4 * s);
     }
   };
-  auto compute = [&](int buf) {
-    const uint8_t *sa = s_a[buf];
+  auto compute = [&](const BRegs &bb, const uint8_t *lds, const uint32_t *lds_sf) {
     i32x4 bdq[kTNF][2];
     if constexpr (kInt8) {
 #pragma unroll
-      for (int j = 0; j < kTNF; ++j) dequant16(bb[buf][j][0], bdq[j][0], bdq[j][1]);
+      for (int j = 0; j < kTNF; ++j) dequant16(bb.v[j][0], bdq[j][0], bdq[j][1]);
     }
 #pragma unroll
     for (int i = 0; i < kTMF; ++i) {
-      const int r = i * 16 + r16;
-      // bf16: chunks 2g, 2g+1 (16 consecutive values); fp8: chunks g, g+4
-      const i32x4 a0 = *reinterpret_cast<const i32x4 *>(sa + a_lds_off(r, kInt8 ? 2 * g : g));
-      const i32x4 a1 = *reinterpret_cast<const i32x4 *>(sa + a_lds_off(r, kInt8 ? 2 * g + 1 : g + 4));
+      const i32x4 a0 = *reinterpret_cast<const i32x4 *>(lds + rd0 + i * 2048);
+      const i32x4 a1 = *reinterpret_cast<const i32x4 *>(lds + rd1 + i * 2048);
       if constexpr (kInt8) {
 #pragma unroll
         for (int j = 0; j < kTNF; ++j) {
@@ -458,13 +473,12 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(
       } else {
         const i32x8 av = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
         int sa_byte = 0;
-        if constexpr (kMx) sa_byte = (int)((s_asf[buf][r] >> (8 * g)) & 0xFFu);
+        if constexpr (kMx) sa_byte = (int)((lds_sf[i * 16 + r16] >> (8 * g)) & 0xFFu);
 #pragma unroll
         for (int j = 0; j < kTNF; ++j) {
-          const i32x8 bv =
-              __builtin_shufflevector(bb[buf][j][0], bb[buf][j][1], 0, 1, 2, 3, 4, 5, 6, 7);
+          const i32x8 bv = __builtin_shufflevector(bb.v[j][0], bb.v[j][1], 0, 1, 2, 3, 4, 5, 6, 7);
           if constexpr (kMx)
-            acc[i][j] = mfma_mx(av, bv, acc[i][j], sa_byte, (int)((bsf[buf][j] >> (8 * g)) & 0xFFu));
+            acc[i][j] = mfma_mx(av, bv, acc[i][j], sa_byte, (int)((bb.sf[j] >> (8 * g)) & 0xFFu));
           else
             acc[i][j] = mfma_fp8(av, bv, acc[i][j]);
         }
@@ -472,29 +486,35 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(
     }
   };
 
+  uint8_t *lds0 = s_a[0];
+  uint8_t *lds1 = s_a[1];
+  uint32_t *sf0 = s_asf[0];
+  uint32_t *sf1 = s_asf[1];
+
+  // Two steps per iteration; the prefetch of the step after next is clamped to
+  // the last step (a repeated load at the very end), so the body has no
+  // branches and every wait count stays exact.
   load_a(0);
-  load_b(0, 0);
-  store_a(0);
+  load_b(b0, 0);
+  store_a(lds0, sf0);
   __syncthreads();
-  for (int s = 0; s < nsteps; s += 2) {
-    // even step: compute buffer 0, prefetch into buffer 1
-    if (s + 1 < nsteps) {
-      load_a(s + 1);
-      load_b(1, s + 1);
-    }
-    compute(0);
-    if (s + 1 < nsteps) store_a(1);
+  int s = 0;
+  for (; s + 2 <= nsteps; s += 2) {
+    load_a(s + 1);
+    load_b(b1, s + 1);
+    __builtin_amdgcn_sched_barrier(0);                  // keep the prefetch ahead of the MFMAs
+    compute(b0, lds0, sf0);
+    store_a(lds1, sf1);
     __syncthreads();
-    if (s + 1 >= nsteps) break;
-    // odd step: compute buffer 1, prefetch into buffer 0
-    if (s + 2 < nsteps) {
-      load_a(s + 2);
-      load_b(0, s + 2);
-    }
-    compute(1);
-    if (s + 2 < nsteps) store_a(0);
+    const int sp = (s + 2 < nsteps) ? s + 2 : nsteps - 1;
+    load_a(sp);
+    load_b(b0, sp);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(b1, lds1, sf1);
+    store_a(lds0, sf0);
     __syncthreads();
   }
+  if (s < nsteps) compute(b0, lds0, sf0);              // odd number of steps
 
   // ---- epilogue --------------------------------------------------------------
   float cscale = 1.0f;

@@ -101,34 +101,83 @@ __device__ __forceinline__ void expert_block_starts(const int *__restrict__ expe
 // =============================================================================
 // block_m = 16: weight streaming
 // =============================================================================
-constexpr int kSNT = 4;    // 16-column fragments per wavefront (64 columns)
-constexpr int kSMB = 2;    // 16-row blocks kept in registers per pass
+// One persistent workgroup per CU.  Workgroup b handles expert e = b / groups
+// and a run of G <= 7 consecutive 64-column tiles of that expert.  Its 8
+// wavefronts split the work by (16-column fragment w & 3, tile parity w >> 2):
+// every wavefront owns whole output elements, so no partial sums meet.
+//
+// Weight bytes and activation rows flow HBM/L2 -> LDS through a two-slot ring
+// filled by global_load_lds_dwordx4 (direct-to-LDS DMA from inline assembly):
+// each instruction moves 1 KB in consecutive 16-byte lane chunks (fully
+// coalesced), and data in flight costs no registers.  One stage is one k-slice
+// (128 k) of all G tiles plus the matching slice of the (up to 32) activation
+// rows, so an activation slice is fetched once for G weight tiles.  While the
+// wavefronts compute stage T, stage T+1 is in flight; before stage T+1 is read
+// every wavefront waits for its own DMA (s_waitcnt vmcnt(0)) and the workgroup
+// synchronises.  The compiler does not see these loads; the loop body issues
+// no other vector-memory loads (scales, router weights and slot ids are staged
+// in LDS before it).
+//
+// LDS rows are XOR-swizzled by 16-byte chunk so that the 16 rows one MFMA
+// operand read touches fall on distinct banks.
+constexpr int kSNT = 4;          // 16-column fragments per tile
+constexpr int kSMB = 2;          // 16-row blocks per pass
+constexpr int kSThreads = 512;   // 8 wavefronts
+constexpr int kSWaves = kSThreads / 64;
+constexpr int kSMaxTiles = 7;    // tiles per workgroup
+constexpr int kSK = 128;         // k per stage
 
 template <bool kInt8>
-struct StreamCfg {
-  static constexpr int kStepK = kInt8 ? 64 : 128;      // k per wavefront step
-  static constexpr int kBVec = kInt8 ? 1 : 2;         // 16-byte B loads per fragment
-  static constexpr int kRing = 3;                      // register stages (steps in flight + 1)
+struct SCfg {
+  static constexpr int kSub = kInt8 ? 64 : 128;            // k per MFMA sub-step
+  static constexpr int kARow = kInt8 ? 2 * kSK : kSK;       // activation bytes per row per stage
+  static constexpr int kBTile = 64 * kSK;                   // weight bytes per tile per stage
+  static constexpr int kABytes = 16 * kSMB * kARow;
+  static constexpr int kStage = kSMaxTiles * kBTile + kABytes;
+  static constexpr int kAInstr = kABytes / 1024;            // DMA instructions for the rows
 };
 
+// global_load_lds_dwordx4: lane l copies 16 bytes from sbase + voff to LDS
+// byte address m0 + 16*l.
+__device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// 128-byte rows: 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 7);
+// 256-byte rows: at chunk c ^ (r & 15).  Either way 16 consecutive rows read
+// at one chunk index cover 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int sw128(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+__device__ __forceinline__ int sw256(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
+
 template <bool kInt8>
-__global__ __launch_bounds__(kThreads, 2) void stream_kernel(
+__global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ w, const float *__restrict__ w_scale,
     const int *__restrict__ sorted_ids, const int *__restrict__ expert_ids,
     const int *__restrict__ num_post, const float *__restrict__ topk_w, int M, int K, int N,
-    int top_k, float *__restrict__ y) {
-  using C = StreamCfg<kInt8>;
-  constexpr int R = C::kRing;
-  __shared__ f32x4 s_red[4][kSMB][kSNT][64];
-  __shared__ int s_slot[kSMB][16];
+    int top_k, int groups, int tiles_per_group, float *__restrict__ y) {
+  using C = SCfg<kInt8>;
+  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[2 * C::kStage];
   __shared__ int s_first[kMaxExperts + 1];
+  __shared__ int s_slot[kSMB * 16];
+  __shared__ float s_topk[kSMB * 16];
+  __shared__ float s_scale[kSMaxTiles * 64];
 
-  const int e = blockIdx.y;
-  const int n0 = blockIdx.x * (kSNT * 16);
+  const int e = blockIdx.x / groups;
+  const int grp = blockIdx.x - e * groups;
+  const int ntiles = (N + 63) / 64;
+  const int t_begin = grp * tiles_per_group;
+  const int G = min(t_begin + tiles_per_group, ntiles) - t_begin;   // tiles of this workgroup
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int frag = wave & 3, par = wave >> 2;
   const int g = lane >> 4, r16 = lane & 15;
   const int S = M * top_k;
+  if (G <= 0) return;
 
   expert_block_starts(expert_ids, *num_post / 16, e + 1, s_first);
   __syncthreads();
@@ -136,137 +185,161 @@ __global__ __launch_bounds__(kThreads, 2) void stream_kernel(
   const int b_end = s_first[e + 1];
   if (b_begin >= b_end) return;
 
-  const uint32_t a_row_bytes = kInt8 ? (uint32_t)K * 2 : (uint32_t)K;
-  const int nsteps = K / C::kStepK;
-  // this wavefront's steps: wave, wave + 4, ... (the 4 wavefronts together
-  // read 4 consecutive steps of every weight row)
-  const int nmy = nsteps > wave ? (nsteps - wave + 3) / 4 : 0;
-  // weight rows of this lane's columns (clamped; columns >= N are not stored)
-  uint32_t woff[kSNT];
-#pragma unroll
-  for (int j = 0; j < kSNT; ++j) {
-    int col = n0 + j * 16 + r16;
-    col = col < N ? col : N - 1;
-    woff[j] = ((uint32_t)e * (uint32_t)N + (uint32_t)col) * (uint32_t)K + 16u * g;
+  // per-column scale of this workgroup's tiles (int8) or the fused scalar (fp8)
+  for (int c = tid; c < G * 64; c += kSThreads) {
+    const int col = min(t_begin * 64 + c, N - 1);
+    s_scale[c] = kInt8 ? w_scale[(size_t)e * N + col] : a_scale[0] * w_scale[e];
   }
-  // bf16 rows hold 16 consecutive values (32 bytes) per lane group; fp8 rows
-  // hold two 16-byte pieces 64 bytes apart
-  const uint32_t a_lane_off = kInt8 ? 32u * g : 16u * g;
-  constexpr int kASecond = kInt8 ? 16 : 64;
-  constexpr uint32_t kAStep = kInt8 ? C::kStepK * 2 : C::kStepK;   // A bytes per step
+
+  const uint32_t lds_ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)s_ring;
+  const uint32_t a_row_bytes = kInt8 ? (uint32_t)K * 2 : (uint32_t)K;
+  const int nst = (K + kSK - 1) / kSK;                      // stages
+  const int nsub_last = (K - (nst - 1) * kSK) / C::kSub;    // sub-steps of the last stage
+  const int nbi = G * (C::kBTile / 1024);                   // weight DMA instructions per stage
 
   for (int bp = b_begin; bp < b_end; bp += kSMB) {
-    const int nmb = (b_end - bp) < kSMB ? (b_end - bp) : kSMB;
-    uint32_t aoff[kSMB];
-#pragma unroll
-    for (int i = 0; i < kSMB; ++i) {
-      int slot = S;
-      if (i < nmb) slot = sorted_ids[(bp + i) * 16 + r16];
-      const int tok = slot < S ? slot / top_k : 0;    // padding rows read token 0
-      aoff[i] = (uint32_t)tok * a_row_bytes + a_lane_off;
-      if (wave == 0 && g == 0) s_slot[i][r16] = slot;
+    const int nmb = min(b_end - bp, kSMB);
+    __syncthreads();                                       // s_slot / ring reuse across passes
+    if (tid < kSMB * 16) {
+      const int i = tid >> 4;
+      const int slot = i < nmb ? sorted_ids[(bp + i) * 16 + (tid & 15)] : S;
+      s_slot[tid] = slot;
+      s_topk[tid] = slot < S ? topk_w[slot] : 0.0f;
+    }
+    __syncthreads();
+
+    // activation DMA of this wavefront (one 1 KB instruction, if any): the
+    // row and the swizzled chunk each lane fetches
+    uint32_t a_row = 0, a_chk = 0;
+    const bool a_issuer = wave < C::kAInstr;
+    if (a_issuer) {
+      int r, c;
+      if constexpr (kInt8) {                               // 4 rows of 256 bytes per KB
+        r = 4 * wave + (lane >> 4);
+        c = lane & 15;
+      } else {                                             // 8 rows of 128 bytes per KB
+        r = 8 * wave + (lane >> 3);
+        c = lane & 7;
+      }
+      const int slot = s_slot[r];
+      const uint32_t tok = slot < S ? (uint32_t)(slot / top_k) : 0u;
+      a_row = tok * a_row_bytes;
+      // the lane at LDS chunk position c fetches source chunk c ^ swizzle(r)
+      a_chk = 16u * (uint32_t)(kInt8 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7)));
     }
 
-    f32x4 acc[kSMB][kSNT];
-#pragma unroll
-    for (int i = 0; i < kSMB; ++i)
-#pragma unroll
-      for (int j = 0; j < kSNT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    struct Stage {
-      i32x4 b[kSNT][C::kBVec];
-      i32x4 a[kSMB][2];
-    };
-    Stage st[R];
-    // t-th step of this wavefront, clamped to its last one (repeated loads at
-    // the end keep the loop free of branches and the wait counts exact)
-    auto load = [&](Stage &x, int t) {
-      const int tt = t < nmy ? t : nmy - 1;
-      const int sidx = wave + 4 * tt;
-      const uint8_t *wb = w + (size_t)sidx * C::kStepK;
-      const uint8_t *ab = a + (size_t)sidx * kAStep;
-#pragma unroll
-      for (int j = 0; j < kSNT; ++j)
-#pragma unroll
-        for (int v = 0; v < C::kBVec; ++v) x.b[j][v] = ld16(wb + woff[j] + 64 * v);
-#pragma unroll
-      for (int i = 0; i < kSMB; ++i) {
-        x.a[i][0] = ld16(ab + aoff[i]);
-        x.a[i][1] = ld16(ab + aoff[i] + kASecond);
+    auto issue = [&](int st) {
+      const uint32_t slot_addr = lds_ring + (uint32_t)((st & 1) * C::kStage);
+      const uint8_t *wb = w + (size_t)st * kSK;
+      const uint32_t kmax = (uint32_t)(K - st * kSK) - 16u;   // last chunk inside the row
+      for (int q = wave; q < nbi; q += kSWaves) {            // 8 rows of 128 bytes per KB
+        const int tl = q >> 3;
+        const int n = 8 * (q & 7) + (lane >> 3);
+        const int c = (lane & 7) ^ ((n >> 1) & 7);
+        const int col = min((t_begin + tl) * 64 + n, N - 1);
+        const uint32_t kb = min(16u * (uint32_t)c, kmax);
+        dma16(wb, ((uint32_t)e * (uint32_t)N + (uint32_t)col) * (uint32_t)K + kb,
+              slot_addr + (uint32_t)(tl * C::kBTile + 1024 * (q & 7)));
+      }
+      if (a_issuer) {
+        const uint32_t amax = (uint32_t)(K - st * kSK) * (kInt8 ? 2u : 1u) - 16u;
+        dma16(a + (size_t)st * C::kARow, a_row + min(a_chk, amax),
+              slot_addr + (uint32_t)(kSMaxTiles * C::kBTile + 1024 * wave));
       }
     };
-    auto compute = [&](const Stage &x) {
+
+    f32x4 acc[4][kSMB];                                    // tiles par, par+2, par+4, par+6
 #pragma unroll
-      for (int j = 0; j < kSNT; ++j) {
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < kSMB; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int st) {
+      const uint8_t *sl = s_ring + (st & 1) * C::kStage;
+      const uint8_t *sa = sl + kSMaxTiles * C::kBTile;
+      const int nsub = (st == nst - 1) ? nsub_last : kSK / C::kSub;
+      const int n = 16 * frag + r16;                       // this lane's weight row in a tile
+#pragma unroll
+      for (int ss = 0; ss < kSK / C::kSub; ++ss) {
+        if (ss >= nsub) break;
         if constexpr (kInt8) {
-          i32x4 b0, b1;
-          dequant16(x.b[j][0], b0, b1);
+          const int c0 = 8 * ss + 2 * g;
+          i32x4 av[kSMB][2];
 #pragma unroll
           for (int i = 0; i < kSMB; ++i) {
-            acc[i][j] = mfma_bf16(x.a[i][0], b0, acc[i][j]);
-            acc[i][j] = mfma_bf16(x.a[i][1], b1, acc[i][j]);
+            const int r = 16 * i + r16;
+            av[i][0] = *reinterpret_cast<const i32x4 *>(sa + sw256(r, c0));
+            av[i][1] = *reinterpret_cast<const i32x4 *>(sa + sw256(r, c0 + 1));
+          }
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int tl = par + 2 * t;
+            if (tl >= G) break;
+            const i32x4 braw =
+                *reinterpret_cast<const i32x4 *>(sl + tl * C::kBTile + sw128(n, 4 * ss + g));
+            i32x4 b0, b1;
+            dequant16(braw, b0, b1);
+#pragma unroll
+            for (int i = 0; i < kSMB; ++i) {
+              if (i >= nmb) break;
+              acc[t][i] = mfma_bf16(av[i][0], b0, acc[t][i]);
+              acc[t][i] = mfma_bf16(av[i][1], b1, acc[t][i]);
+            }
           }
         } else {
-          const i32x8 bv = __builtin_shufflevector(x.b[j][0], x.b[j][1], 0, 1, 2, 3, 4, 5, 6, 7);
+          i32x8 av[kSMB];
 #pragma unroll
           for (int i = 0; i < kSMB; ++i) {
-            const i32x8 av =
-                __builtin_shufflevector(x.a[i][0], x.a[i][1], 0, 1, 2, 3, 4, 5, 6, 7);
-            acc[i][j] = mfma_fp8(av, bv, acc[i][j]);
+            const int r = 16 * i + r16;
+            const i32x4 al = *reinterpret_cast<const i32x4 *>(sa + sw128(r, g));
+            const i32x4 ah = *reinterpret_cast<const i32x4 *>(sa + sw128(r, g + 4));
+            av[i] = __builtin_shufflevector(al, ah, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int tl = par + 2 * t;
+            if (tl >= G) break;
+            const uint8_t *bt = sl + tl * C::kBTile;
+            const i32x4 bl = *reinterpret_cast<const i32x4 *>(bt + sw128(n, g));
+            const i32x4 bh = *reinterpret_cast<const i32x4 *>(bt + sw128(n, g + 4));
+            const i32x8 bv = __builtin_shufflevector(bl, bh, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+            for (int i = 0; i < kSMB; ++i) {
+              if (i >= nmb) break;
+              acc[t][i] = mfma_fp8(av[i], bv, acc[t][i]);
+            }
           }
         }
       }
     };
 
-    if (nmy > 0) {
-#pragma unroll
-      for (int r = 0; r < R - 1; ++r) load(st[r], r);
-      int t = 0;
-      for (; t + R <= nmy; t += R) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          load(st[(r + R - 1) % R], t + r + R - 1);
-          __builtin_amdgcn_sched_barrier(0);
-          compute(st[r]);
-        }
-      }
-      // the last nmy - t (< R) steps are already in stages 0 .. R-2
-#pragma unroll
-      for (int r = 0; r < R - 1; ++r)
-        if (t + r < nmy) compute(st[r]);
+    issue(0);
+    for (int st = 0; st < nst; ++st) {
+      wait_dma_all();                                      // this wave's DMA for stage st landed
+      __syncthreads();                                     // ... and everyone's; the other slot is free
+      if (st + 1 < nst) issue(st + 1);
+      compute(st);
     }
 
-    // ---- fixed-order reduction of the 4 wavefronts' partial sums ----------
+    // ---- epilogue: scale x router weight, one store per output element ----
 #pragma unroll
-    for (int i = 0; i < kSMB; ++i)
+    for (int t = 0; t < 4; ++t) {
+      const int tl = par + 2 * t;
+      if (tl >= G) break;
+      const int col = (t_begin + tl) * 64 + 16 * frag + r16;
+      if (col >= N) continue;
+      const float cs = s_scale[tl * 64 + 16 * frag + r16];
 #pragma unroll
-      for (int j = 0; j < kSNT; ++j) s_red[wave][i][j][lane] = acc[i][j];
-    __syncthreads();
-    const float sa = kInt8 ? 1.0f : a_scale[0] * w_scale[e];
-    for (int q = tid; q < nmb * kSNT * 64; q += kThreads) {
-      const int i = q / (kSNT * 64);
-      const int j = (q / 64) % kSNT;
-      const int l = q & 63;
-      f32x4 v = s_red[0][i][j][l];
-#pragma unroll
-      for (int ww = 1; ww < 4; ++ww) {
-        const f32x4 u = s_red[ww][i][j][l];
-        v[0] += u[0];
-        v[1] += u[1];
-        v[2] += u[2];
-        v[3] += u[3];
-      }
-      const int col = n0 + j * 16 + (l & 15);
-      if (col < N) {
-        const float cs = kInt8 ? w_scale[(size_t)e * N + col] : sa;
+      for (int i = 0; i < kSMB; ++i) {
+        if (i >= nmb) break;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const int slot = s_slot[i][4 * (l >> 4) + rr];
-          if (slot < S) y[(size_t)slot * N + col] = v[rr] * cs * topk_w[slot];
+          const int k = 16 * i + 4 * g + rr;
+          const int slot = s_slot[k];
+          if (slot < S) y[(size_t)slot * N + col] = acc[t][i][rr] * cs * s_topk[k];
         }
       }
     }
-    __syncthreads();
   }
 }
 
@@ -550,13 +623,38 @@ unsigned tile_grid(long long tiles_bound) {
 
 }  // namespace
 
+namespace {
+int num_cus() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+  }
+  return n;
+}
+
+// persistent decomposition of the weight stream: E * groups workgroups, each
+// with tiles_per_group consecutive 64-column tiles of one expert
+void stream_grid(int N, int E, int &groups, int &tiles_per_group) {
+  const int ntiles = (N + 63) / 64;
+  int tpg = (E * ntiles + num_cus() - 1) / num_cus();
+  tpg = tpg < 1 ? 1 : (tpg > kSMaxTiles ? kSMaxTiles : tpg);   // LDS holds <= 7 tiles
+  tiles_per_group = tpg;
+  groups = (ntiles + tpg - 1) / tpg;
+}
+}  // namespace
+
 hipError_t launch_gemm_fp8(const uint8_t *a_q, const float *a_scale, const uint8_t *w_q,
                            const float *w_scale, const RoutedArgs &r, hipStream_t s) {
   if (r.block_m == 16) {
-    dim3 grid((r.N + kSNT * 16 - 1) / (kSNT * 16), r.E);
-    hipLaunchKernelGGL(stream_kernel<false>, grid, dim3(kThreads), 0, s, a_q, a_scale, w_q,
-                       w_scale, r.sorted_ids, r.expert_ids, r.num_post, r.topk_w, r.M, r.K, r.N,
-                       r.top_k, r.y);
+    int groups, tpg;
+    stream_grid(r.N, r.E, groups, tpg);
+    hipLaunchKernelGGL(stream_kernel<false>, dim3(r.E * groups), dim3(kSThreads), 0, s, a_q,
+                       a_scale, w_q, w_scale, r.sorted_ids, r.expert_ids, r.num_post, r.topk_w,
+                       r.M, r.K, r.N, r.top_k, groups, tpg, r.y);
   } else {
     const long long tiles = (long long)r.max_blocks * ((r.N + kTBN - 1) / kTBN);
     hipLaunchKernelGGL(tile_kernel<kFmtFp8>, dim3(tile_grid(tiles)), dim3(kThreads), 0, s, a_q,
@@ -572,10 +670,11 @@ hipError_t launch_gemm_int8(const uint16_t *a, const int8_t *w_q, const float *w
   const uint8_t *ab = reinterpret_cast<const uint8_t *>(a);
   const uint8_t *wb = reinterpret_cast<const uint8_t *>(w_q);
   if (r.block_m == 16) {
-    dim3 grid((r.N + kSNT * 16 - 1) / (kSNT * 16), r.E);
-    hipLaunchKernelGGL(stream_kernel<true>, grid, dim3(kThreads), 0, s, ab, nullptr, wb, w_scale,
-                       r.sorted_ids, r.expert_ids, r.num_post, r.topk_w, r.M, r.K, r.N, r.top_k,
-                       r.y);
+    int groups, tpg;
+    stream_grid(r.N, r.E, groups, tpg);
+    hipLaunchKernelGGL(stream_kernel<true>, dim3(r.E * groups), dim3(kSThreads), 0, s, ab,
+                       nullptr, wb, w_scale, r.sorted_ids, r.expert_ids, r.num_post, r.topk_w,
+                       r.M, r.K, r.N, r.top_k, groups, tpg, r.y);
   } else {
     const long long tiles = (long long)r.max_blocks * ((r.N + kTBN - 1) / kTBN);
     hipLaunchKernelGGL(tile_kernel<kFmtInt8>, dim3(tile_grid(tiles)), dim3(kThreads), 0, s, ab,

@@ -123,6 +123,8 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     case = synth.make_case(wl, 0, device="cuda")
     w_q, w_s = runner.quantize_weights(case["w"], wl.fmt)
+    if wl.fmt != "mxfp8":
+        w_q = runner.pack_weights(w_q)              # tiled layout: one HBM block per stage
     copies = args.copies or max(2, -(-(1 << 30) // w_q.numel()))
     weights = [(w_q, w_s)] + [(w_q.clone(), w_s.clone()) for _ in range(copies - 1)]
     if wl.fmt == "mxfp8":
@@ -138,7 +140,7 @@ def main():
             if ev is not None:
                 ev[1].record()
     else:
-        moe = runner.RoutedMoE(wl.fmt, wl.M, wl.K, wl.N, wl.E, wl.top_k)
+        moe = runner.RoutedMoE(wl.fmt, wl.M, wl.K, wl.N, wl.E, wl.top_k, w_layout=qm.MOE_W_TILED)
 
         def step(i, ev):
             q, s = weights[i % copies]
@@ -194,7 +196,8 @@ def main():
         "dtype": dtype, "data": "synthetic (seeded N(0,1) activations and logits, N(0,1/sqrt(K)) weights)",
         "config": {"workload": wl.name, "format": wl.fmt, "M": wl.M, "K": wl.K, "N": wl.N,
                    "E": wl.E, "top_k": wl.top_k, "weight_copies": copies,
-                   "block_m": getattr(moe, "block_m", None)},
+                   "block_m": getattr(moe, "block_m", None),
+                   "weight_layout": "tiled" if wl.fmt != "mxfp8" else "rowmajor"},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

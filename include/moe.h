@@ -59,6 +59,10 @@ extern "C" {
 #define MOE_Q_MXFP8            1  /* e4m3 + one e8m0 scale per 32 values along K */
 #define MOE_Q_INT8_PER_CHANNEL 2  /* weights only: int8 + one fp32 scale per output channel */
 
+/* ---- expert weight layouts (fp8 and int8 weights) ------------------------ */
+#define MOE_W_ROWMAJOR 0  /* [E, N, K] bytes, K fastest */
+#define MOE_W_TILED    1  /* as written by moe_pack_weights (see there) */
+
 /* ---- limits ------------------------------------------------------------- */
 #define MOE_MAX_EXPERTS   128     /* E */
 #define MOE_MAX_TOPK      8       /* top_k */
@@ -88,6 +92,10 @@ int moe_recommended_block_m(int M, int E, int top_k);
  * `mode` on `tensors` independent tensors (1 for activations, E for weights);
  * 0 when the mode needs none. */
 size_t moe_quantize_workspace_bytes(int mode, int tensors);
+
+/* Bytes of the MOE_W_TILED layout of E x N x K one-byte weights:
+ * E * ceil(N/64) * ceil(K/128) * 8192. */
+size_t moe_packed_weight_bytes(int E, int N, int K);
 
 /* Upper bound on the rows of the padded MXFP8 rowwise scale matrix for `rows`
  * rows spread over E experts: rows + E*127 (each expert's block is padded to
@@ -173,6 +181,22 @@ int moe_quantize_weights(const float *w, int E, int N, int K, int mode,
                          void *q, float *scale, uint8_t *scale_e8m0,
                          void *workspace, hipStream_t stream);
 
+/* Offline re-layout of one-byte expert weights (e4m3 or int8) for streaming.
+ *
+ * MOE_W_TILED: the weights of expert e are cut into 64-row tiles t = n / 64
+ * (T = ceil(N/64)) and 128-byte k slices s = k / 128 (S = ceil(K/128)); the
+ * 64 x 128-byte block (e, t, s) is stored contiguously (8192 bytes) at byte
+ * offset ((e*T + t)*S + s) * 8192, rows in order, 128 bytes per row, and the
+ * 16-byte chunk c of row r (k = 128s + 16c .. 128s + 16c + 15) at chunk
+ * position c ^ ((r >> 1) & 7) of that row.  Rows n >= N and k >= K are zero.
+ * Every block is then one contiguous HBM read of the decode GEMM, landing in
+ * LDS in the bank-conflict-free order its MFMA reads use.
+ *
+ *   w_q      [E, N, K] bytes (MOE_W_ROWMAJOR), read
+ *   w_packed moe_packed_weight_bytes(E, N, K) bytes, written in full
+ * The packed size must stay below 4 GiB. */
+int moe_pack_weights(const void *w_q, int E, int N, int K, void *w_packed, hipStream_t stream);
+
 /* ======================================================================== *
  * a4 + a5: grouped GEMM with the fused scale / router-weight epilogue
  * ======================================================================== */
@@ -183,14 +207,16 @@ int moe_quantize_weights(const float *w, int E, int N, int K, int mode,
  *     y[i, n] = (sum_k a[t,k] * w[e,n,k]) * (a_scale[0] * w_scale[e]) * topk_weights[i]
  * with e4m3 operands, fp32 accumulation, and padding slots skipped.
  *
- *   a_q [M, K] uint8 e4m3, a_scale [1] f32, w_q [E, N, K] uint8 e4m3,
- *   w_scale [E] f32, topk_weights [M*top_k] f32, routing buffers as written
- *   by moe_align_block_size, y [M*top_k, N] f32 (rows of slots that are not
+ *   a_q [M, K] uint8 e4m3, a_scale [1] f32, w_q e4m3 weights in layout
+ *   w_layout (MOE_W_ROWMAJOR [E, N, K] or MOE_W_TILED), w_scale [E] f32,
+ *   topk_weights [M*top_k] f32, routing buffers as written by
+ *   moe_align_block_size, y [M*top_k, N] f32 (rows of slots that are not
  *   routed are not written; with every slot routed, y is written in full).
  *
- * K must be a multiple of 128; block_m must be 16 or 128. */
+ * K must be a multiple of 128; block_m must be 16 or 128.  block_m 16 runs the
+ * weight-streaming kernel (fastest with MOE_W_TILED), 128 the tiled one. */
 int moe_grouped_gemm_fp8w8a8(const uint8_t *a_q, const float *a_scale,
-                             const uint8_t *w_q, const float *w_scale,
+                             const uint8_t *w_q, const float *w_scale, int w_layout,
                              const int *sorted_token_ids, const int *expert_ids,
                              const int *num_tokens_post_padded,
                              const float *topk_weights, int M, int K, int N, int E,
@@ -198,12 +224,12 @@ int moe_grouped_gemm_fp8w8a8(const uint8_t *a_q, const float *a_scale,
 
 /* Routed int8 W8A16 grouped GEMM: as moe_grouped_gemm_fp8w8a8 with
  *     y[i, n] = (sum_k a[t,k] * w[e,n,k]) * w_scale[e, n] * topk_weights[i]
- * for bf16 a [M, K] (uint16 bits), int8 w_q [E, N, K], w_scale [E, N] f32.
- * The int8 weights are converted exactly to bf16 inside the kernel and the
- * products are accumulated in fp32.  K must be a multiple of 64; block_m must
- * be 16 or 128. */
+ * for bf16 a [M, K] (uint16 bits), int8 w_q in layout w_layout, w_scale
+ * [E, N] f32.  The int8 weights are converted exactly to bf16 inside the
+ * kernel and the products are accumulated in fp32.  K must be a multiple of
+ * 64; block_m must be 16 or 128. */
 int moe_grouped_gemm_int8w8a16(const uint16_t *a, const int8_t *w_q,
-                               const float *w_scale,
+                               const float *w_scale, int w_layout,
                                const int *sorted_token_ids, const int *expert_ids,
                                const int *num_tokens_post_padded,
                                const float *topk_weights, int M, int K, int N, int E,

@@ -20,12 +20,14 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmoe.so"
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP = 0, -1, -2, -3
 MOE_Q_FP8_PER_TENSOR, MOE_Q_MXFP8, MOE_Q_INT8_PER_CHANNEL = 0, 1, 2
+MOE_W_ROWMAJOR, MOE_W_TILED = 0, 1
 MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_SLOTS = 128, 8, 65536
 
 EXPORTS = [
     "moe_last_error", "moe_last_hip_error", "moe_align_max_padded", "moe_recommended_block_m",
-    "moe_quantize_workspace_bytes", "moe_mx_scale_rows", "moe_align_block_size",
-    "moe_quantize_act", "moe_quantize_weights", "moe_grouped_gemm_fp8w8a8",
+    "moe_quantize_workspace_bytes", "moe_packed_weight_bytes", "moe_mx_scale_rows",
+    "moe_align_block_size", "moe_quantize_act", "moe_quantize_weights", "moe_pack_weights",
+    "moe_grouped_gemm_fp8w8a8",
     "moe_grouped_gemm_int8w8a16", "moe_grouped_gemm_mxfp8", "moe_combine",
 ]
 
@@ -50,12 +52,14 @@ _SIGS = {
     "moe_align_max_padded": (_I, [_I, _I, _I, _I]),
     "moe_recommended_block_m": (_I, [_I, _I, _I]),
     "moe_quantize_workspace_bytes": (ctypes.c_size_t, [_I, _I]),
+    "moe_packed_weight_bytes": (ctypes.c_size_t, [_I, _I, _I]),
+    "moe_pack_weights": (_I, [_P, _I, _I, _I, _P, _P]),
     "moe_mx_scale_rows": (_I, [_I, _I]),
     "moe_align_block_size": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "moe_quantize_act": (_I, [_P, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P]),
     "moe_quantize_weights": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
-    "moe_grouped_gemm_fp8w8a8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
-    "moe_grouped_gemm_int8w8a16": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
+    "moe_grouped_gemm_fp8w8a8": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
+    "moe_grouped_gemm_int8w8a16": (_I, [_P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
     "moe_grouped_gemm_mxfp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "moe_combine": (_I, [_P, _I, _I, _I, _P, _P]),
 }
@@ -117,6 +121,10 @@ def moe_quantize_workspace_bytes(mode, tensors):
     return int(lib().moe_quantize_workspace_bytes(mode, tensors))
 
 
+def moe_packed_weight_bytes(E, N, K):
+    return int(lib().moe_packed_weight_bytes(E, N, K))
+
+
 def moe_mx_scale_rows(rows, E):
     return _size(lib().moe_mx_scale_rows(rows, E))
 
@@ -142,20 +150,24 @@ def moe_quantize_weights(w, E, N, K, mode, q, scale, scale_e8m0, workspace, stre
         _stream(stream)))
 
 
-def moe_grouped_gemm_fp8w8a8(a_q, a_scale, w_q, w_scale, sorted_token_ids, expert_ids,
+def moe_pack_weights(w_q, E, N, K, w_packed, stream=None):
+    return _check(lib().moe_pack_weights(_ptr(w_q), E, N, K, _ptr(w_packed), _stream(stream)))
+
+
+def moe_grouped_gemm_fp8w8a8(a_q, a_scale, w_q, w_scale, w_layout, sorted_token_ids, expert_ids,
                              num_tokens_post_padded, topk_weights, M, K, N, E, top_k, block_m,
                              y, stream=None):
     return _check(lib().moe_grouped_gemm_fp8w8a8(
-        _ptr(a_q), _ptr(a_scale), _ptr(w_q), _ptr(w_scale), _ptr(sorted_token_ids),
+        _ptr(a_q), _ptr(a_scale), _ptr(w_q), _ptr(w_scale), w_layout, _ptr(sorted_token_ids),
         _ptr(expert_ids), _ptr(num_tokens_post_padded), _ptr(topk_weights), M, K, N, E, top_k,
         block_m, _ptr(y), _stream(stream)))
 
 
-def moe_grouped_gemm_int8w8a16(a, w_q, w_scale, sorted_token_ids, expert_ids,
+def moe_grouped_gemm_int8w8a16(a, w_q, w_scale, w_layout, sorted_token_ids, expert_ids,
                                num_tokens_post_padded, topk_weights, M, K, N, E, top_k, block_m,
                                y, stream=None):
     return _check(lib().moe_grouped_gemm_int8w8a16(
-        _ptr(a), _ptr(w_q), _ptr(w_scale), _ptr(sorted_token_ids), _ptr(expert_ids),
+        _ptr(a), _ptr(w_q), _ptr(w_scale), w_layout, _ptr(sorted_token_ids), _ptr(expert_ids),
         _ptr(num_tokens_post_padded), _ptr(topk_weights), M, K, N, E, top_k, block_m, _ptr(y),
         _stream(stream)))
 

@@ -59,12 +59,14 @@ long long max_padded_ll(int M, int E, int top_k, int block_m) {
   return (n + block_m - 1) / block_m * block_m;
 }
 
-int check_routed_gemm(const void *a, const void *w, const void *w_scale, const int *sorted,
-                      const int *expert_ids, const int *num_post, const float *topk_w,
-                      const float *y, int M, int K, int N, int E, int top_k, int block_m,
-                      int k_mult, const char *fn) {
+int check_routed_gemm(const void *a, const void *w, const void *w_scale, int w_layout,
+                      const int *sorted, const int *expert_ids, const int *num_post,
+                      const float *topk_w, const float *y, int M, int K, int N, int E, int top_k,
+                      int block_m, int k_mult, const char *fn) {
   int rc = check_routing_sizes(M, E, top_k, fn);
   if (rc) return rc;
+  REQUIRE(w_layout == MOE_W_ROWMAJOR || w_layout == MOE_W_TILED, MOE_EINVAL,
+          "%s: unknown weight layout %d", fn, w_layout);
   REQUIRE(K > 0 && N > 0, MOE_EINVAL, "%s: K=%d and N=%d must be positive", fn, K, N);
   REQUIRE(K % k_mult == 0, MOE_EUNSUPPORTED, "%s: K=%d is not a multiple of %d", fn, K, k_mult);
   REQUIRE(block_m == 16 || block_m == 128, MOE_EUNSUPPORTED,
@@ -74,8 +76,11 @@ int check_routed_gemm(const void *a, const void *w, const void *w_scale, const i
           "%s: null pointer argument", fn);
   REQUIRE(aligned16(a) && aligned16(w), MOE_EINVAL,
           "%s: activation and weight pointers must be 16-byte aligned", fn);
-  REQUIRE((long long)E * N * (long long)K < (1ll << 40), MOE_EUNSUPPORTED,
-          "%s: weight tensor too large", fn);
+  REQUIRE((long long)E * N * (long long)K < (1ll << 32) &&
+              moe_packed_weight_bytes(E, N, K) < (1ull << 32),
+          MOE_EUNSUPPORTED, "%s: weight tensor must stay below 4 GiB", fn);
+  REQUIRE((long long)M * (long long)K * 2 < (1ll << 32), MOE_EUNSUPPORTED,
+          "%s: activation tensor must stay below 4 GiB", fn);
   return MOE_OK;
 }
 
@@ -107,6 +112,26 @@ int moe_recommended_block_m(int M, int E, int top_k) {
 size_t moe_quantize_workspace_bytes(int mode, int tensors) {
   if (mode != MOE_Q_FP8_PER_TENSOR || tensors <= 0) return 0;
   return (size_t)tensors * qmoe::kAmaxPartials * sizeof(float);
+}
+
+size_t moe_packed_weight_bytes(int E, int N, int K) {
+  if (E < 1 || N < 1 || K < 1) return 0;
+  return (size_t)E * (size_t)((N + qmoe::kPackRows - 1) / qmoe::kPackRows) *
+         (size_t)((K + qmoe::kPackK - 1) / qmoe::kPackK) * (size_t)(qmoe::kPackRows * qmoe::kPackK);
+}
+
+int moe_pack_weights(const void *w_q, int E, int N, int K, void *w_packed, hipStream_t stream) {
+  const char *fn = "moe_pack_weights";
+  REQUIRE(E >= 1 && N > 0 && K > 0, MOE_EINVAL, "%s: E=%d N=%d K=%d", fn, E, N, K);
+  REQUIRE(w_q && w_packed, MOE_EINVAL, "%s: null pointer argument", fn);
+  REQUIRE(aligned16(w_q) && aligned16(w_packed), MOE_EINVAL, "%s: pointers must be 16-byte aligned",
+          fn);
+  REQUIRE(K % 16 == 0, MOE_EUNSUPPORTED, "%s: K=%d is not a multiple of 16", fn, K);
+  REQUIRE(moe_packed_weight_bytes(E, N, K) < (1ull << 32), MOE_EUNSUPPORTED,
+          "%s: packed weights must stay below 4 GiB", fn);
+  return hip_status(qmoe::launch_pack_weights((const uint8_t *)w_q, E, N, K, (uint8_t *)w_packed,
+                                              stream),
+                    fn);
 }
 
 int moe_mx_scale_rows(int rows, int E) {
@@ -195,35 +220,37 @@ int moe_quantize_weights(const float *w, int E, int N, int K, int mode, void *q,
 }
 
 int moe_grouped_gemm_fp8w8a8(const uint8_t *a_q, const float *a_scale, const uint8_t *w_q,
-                             const float *w_scale, const int *sorted_token_ids,
+                             const float *w_scale, int w_layout, const int *sorted_token_ids,
                              const int *expert_ids, const int *num_tokens_post_padded,
                              const float *topk_weights, int M, int K, int N, int E, int top_k,
                              int block_m, float *y, hipStream_t stream) {
   const char *fn = "moe_grouped_gemm_fp8w8a8";
-  int rc = check_routed_gemm(a_q, w_q, w_scale, sorted_token_ids, expert_ids,
+  int rc = check_routed_gemm(a_q, w_q, w_scale, w_layout, sorted_token_ids, expert_ids,
                              num_tokens_post_padded, topk_weights, y, M, K, N, E, top_k, block_m,
                              128, fn);
   if (rc) return rc;
   if (M == 0) return ok();
   REQUIRE(a_scale, MOE_EINVAL, "%s: null a_scale", fn);
   qmoe::RoutedArgs r{sorted_token_ids, expert_ids, num_tokens_post_padded, topk_weights, M, K, N,
-                     E, top_k, block_m, (int)(max_padded_ll(M, E, top_k, block_m) / block_m), y};
+                     E, top_k, block_m, (int)(max_padded_ll(M, E, top_k, block_m) / block_m),
+                     w_layout, y};
   return hip_status(qmoe::launch_gemm_fp8(a_q, a_scale, w_q, w_scale, r, stream), fn);
 }
 
 int moe_grouped_gemm_int8w8a16(const uint16_t *a, const int8_t *w_q, const float *w_scale,
-                               const int *sorted_token_ids, const int *expert_ids,
+                               int w_layout, const int *sorted_token_ids, const int *expert_ids,
                                const int *num_tokens_post_padded, const float *topk_weights,
                                int M, int K, int N, int E, int top_k, int block_m, float *y,
                                hipStream_t stream) {
   const char *fn = "moe_grouped_gemm_int8w8a16";
-  int rc = check_routed_gemm(a, w_q, w_scale, sorted_token_ids, expert_ids,
+  int rc = check_routed_gemm(a, w_q, w_scale, w_layout, sorted_token_ids, expert_ids,
                              num_tokens_post_padded, topk_weights, y, M, K, N, E, top_k, block_m,
                              64, fn);
   if (rc) return rc;
   if (M == 0) return ok();
   qmoe::RoutedArgs r{sorted_token_ids, expert_ids, num_tokens_post_padded, topk_weights, M, K, N,
-                     E, top_k, block_m, (int)(max_padded_ll(M, E, top_k, block_m) / block_m), y};
+                     E, top_k, block_m, (int)(max_padded_ll(M, E, top_k, block_m) / block_m),
+                     w_layout, y};
   return hip_status(qmoe::launch_gemm_int8(a, w_q, w_scale, r, stream), fn);
 }
 

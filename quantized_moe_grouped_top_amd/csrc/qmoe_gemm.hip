@@ -84,16 +84,21 @@ __device__ __forceinline__ i32x4 ld16(const void *p) {
 }
 
 // First block of every expert, from the ascending block labels: s_first[e] =
-// first b in [0, nb) with expert_ids[b] >= e (nb if none), for e in [0, E].
-// All threads of the workgroup take part (one or two loads each, no serial
-// search); the caller synchronises before reading s_first.
-__device__ __forceinline__ void expert_block_starts(const int *__restrict__ expert_ids, int nb,
-                                                    int E, int *s_first) {
-  for (int e = threadIdx.x; e <= E; e += blockDim.x) s_first[e] = nb;
+// first b with expert_ids[b] >= e, for e in [0, E]; s_first[E] is the number
+// of blocks in use.  The labels are scanned over the whole buffer (max_blocks
+// entries, -1 after the last block), so the padded length is not needed first.
+// All threads of the workgroup take part (a few loads each, no serial search);
+// the caller synchronises before reading s_first.
+__device__ __forceinline__ void expert_block_starts(const int *__restrict__ expert_ids,
+                                                    int max_blocks, int E, int *s_first) {
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) s_first[e] = max_blocks;
   __syncthreads();
-  for (int b = threadIdx.x; b < nb; b += blockDim.x) {
-    const int cur = expert_ids[b];
-    const int prev = b > 0 ? expert_ids[b - 1] : -1;
+  constexpr int kEnd = 1 << 30;                     // the -1 label sorts after every expert
+  for (int b = threadIdx.x; b < max_blocks; b += blockDim.x) {
+    int cur = expert_ids[b];
+    int prev = b > 0 ? expert_ids[b - 1] : -1;
+    cur = cur < 0 ? kEnd : cur;
+    prev = (b > 0 && prev < 0) ? kEnd : prev;
     for (int e = prev + 1; e <= cur && e <= E; ++e) s_first[e] = b;
   }
 }
@@ -102,7 +107,8 @@ __device__ __forceinline__ void expert_block_starts(const int *__restrict__ expe
 // block_m = 16: weight streaming
 // =============================================================================
 // One persistent workgroup per CU.  Workgroup b handles expert e = b / groups
-// and a run of G <= 7 consecutive 64-column tiles of that expert.  Its 8
+// and a run of G <= 7 consecutive 64-column tiles of that expert, with up to
+// 64 of the expert's rows per pass.  Its 8
 // wavefronts split the work by (16-column fragment w & 3, tile parity w >> 2):
 // every wavefront owns whole output elements, so no partial sums meet.
 //
@@ -110,7 +116,7 @@ __device__ __forceinline__ void expert_block_starts(const int *__restrict__ expe
 // filled by global_load_lds_dwordx4 (direct-to-LDS DMA from inline assembly):
 // each instruction moves 1 KB in consecutive 16-byte lane chunks (fully
 // coalesced), and data in flight costs no registers.  One stage is one k-slice
-// (128 k) of all G tiles plus the matching slice of the (up to 32) activation
+// (128 k) of all G tiles plus the matching slice of the (up to 64) activation
 // rows, so an activation slice is fetched once for G weight tiles.  While the
 // wavefronts compute stage T, stage T+1 is in flight; before stage T+1 is read
 // every wavefront waits for its own DMA (s_waitcnt vmcnt(0)) and the workgroup
@@ -121,7 +127,7 @@ __device__ __forceinline__ void expert_block_starts(const int *__restrict__ expe
 // LDS rows are XOR-swizzled by 16-byte chunk so that the 16 rows one MFMA
 // operand read touches fall on distinct banks.
 constexpr int kSNT = 4;          // 16-column fragments per tile
-constexpr int kSMB = 2;          // 16-row blocks per pass
+constexpr int kSMB = 4;          // 16-row blocks per pass (64 rows)
 constexpr int kSThreads = 512;   // 8 wavefronts
 constexpr int kSWaves = kSThreads / 64;
 constexpr int kSMaxTiles = 7;    // tiles per workgroup
@@ -148,22 +154,32 @@ __device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t
 
 __device__ __forceinline__ void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 15]
+__device__ __forceinline__ void wait_dma_upto(int n) {
+  switch (n) {
+#define QMOE_W(k) case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+    QMOE_W(1) QMOE_W(2) QMOE_W(3) QMOE_W(4) QMOE_W(5) QMOE_W(6) QMOE_W(7) QMOE_W(8)
+    QMOE_W(9) QMOE_W(10) QMOE_W(11) QMOE_W(12) QMOE_W(13) QMOE_W(14) QMOE_W(15)
+#undef QMOE_W
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+
 // 128-byte rows: 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 7);
 // 256-byte rows: at chunk c ^ (r & 15).  Either way 16 consecutive rows read
 // at one chunk index cover 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int sw128(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 __device__ __forceinline__ int sw256(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
 
-template <bool kInt8>
+template <bool kInt8, bool kTiled>
 __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ w, const float *__restrict__ w_scale,
     const int *__restrict__ sorted_ids, const int *__restrict__ expert_ids,
     const int *__restrict__ num_post, const float *__restrict__ topk_w, int M, int K, int N,
-    int top_k, int groups, int tiles_per_group, float *__restrict__ y) {
+    int top_k, int groups, int tiles_per_group, int max_blocks, float *__restrict__ y) {
   using C = SCfg<kInt8>;
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[2 * C::kStage];
-  __shared__ int s_first[kMaxExperts + 1];
   __shared__ int s_slot[kSMB * 16];
   __shared__ float s_topk[kSMB * 16];
   __shared__ float s_scale[kSMaxTiles * 64];
@@ -179,57 +195,25 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
   const int S = M * top_k;
   if (G <= 0) return;
 
-  expert_block_starts(expert_ids, *num_post / 16, e + 1, s_first);
-  __syncthreads();
-  const int b_begin = s_first[e];
-  const int b_end = s_first[e + 1];
-  if (b_begin >= b_end) return;
-
-  // per-column scale of this workgroup's tiles (int8) or the fused scalar (fp8)
-  for (int c = tid; c < G * 64; c += kSThreads) {
-    const int col = min(t_begin * 64 + c, N - 1);
-    s_scale[c] = kInt8 ? w_scale[(size_t)e * N + col] : a_scale[0] * w_scale[e];
-  }
-
   const uint32_t lds_ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)s_ring;
   const uint32_t a_row_bytes = kInt8 ? (uint32_t)K * 2 : (uint32_t)K;
   const int nst = (K + kSK - 1) / kSK;                      // stages
   const int nsub_last = (K - (nst - 1) * kSK) / C::kSub;    // sub-steps of the last stage
   const int nbi = G * (C::kBTile / 1024);                   // weight DMA instructions per stage
 
-  for (int bp = b_begin; bp < b_end; bp += kSMB) {
-    const int nmb = min(b_end - bp, kSMB);
-    __syncthreads();                                       // s_slot / ring reuse across passes
-    if (tid < kSMB * 16) {
-      const int i = tid >> 4;
-      const int slot = i < nmb ? sorted_ids[(bp + i) * 16 + (tid & 15)] : S;
-      s_slot[tid] = slot;
-      s_topk[tid] = slot < S ? topk_w[slot] : 0.0f;
-    }
-    __syncthreads();
-
-    // activation DMA of this wavefront (one 1 KB instruction, if any): the
-    // row and the swizzled chunk each lane fetches
-    uint32_t a_row = 0, a_chk = 0;
-    const bool a_issuer = wave < C::kAInstr;
-    if (a_issuer) {
-      int r, c;
-      if constexpr (kInt8) {                               // 4 rows of 256 bytes per KB
-        r = 4 * wave + (lane >> 4);
-        c = lane & 15;
-      } else {                                             // 8 rows of 128 bytes per KB
-        r = 8 * wave + (lane >> 3);
-        c = lane & 7;
+  // weight DMA of stage st (one k-slice of all G tiles) into ring slot st & 1
+  auto issue_b = [&](int st) {
+    const uint32_t slot_addr = lds_ring + (uint32_t)((st & 1) * C::kStage);
+    if constexpr (kTiled) {
+      // one contiguous 8 KB block per tile, already in LDS order
+      const uint32_t T = (uint32_t)ntiles, Sn = (uint32_t)nst;
+      for (int q = wave; q < nbi; q += kSWaves) {
+        const int tl = q >> 3;
+        const uint32_t blk = (((uint32_t)e * T + (uint32_t)(t_begin + tl)) * Sn + (uint32_t)st) * 8192u;
+        dma16(w, blk + 1024u * (uint32_t)(q & 7) + 16u * (uint32_t)lane,
+              slot_addr + (uint32_t)(tl * C::kBTile + 1024 * (q & 7)));
       }
-      const int slot = s_slot[r];
-      const uint32_t tok = slot < S ? (uint32_t)(slot / top_k) : 0u;
-      a_row = tok * a_row_bytes;
-      // the lane at LDS chunk position c fetches source chunk c ^ swizzle(r)
-      a_chk = 16u * (uint32_t)(kInt8 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7)));
-    }
-
-    auto issue = [&](int st) {
-      const uint32_t slot_addr = lds_ring + (uint32_t)((st & 1) * C::kStage);
+    } else {
       const uint8_t *wb = w + (size_t)st * kSK;
       const uint32_t kmax = (uint32_t)(K - st * kSK) - 16u;   // last chunk inside the row
       for (int q = wave; q < nbi; q += kSWaves) {            // 8 rows of 128 bytes per KB
@@ -241,11 +225,112 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
         dma16(wb, ((uint32_t)e * (uint32_t)N + (uint32_t)col) * (uint32_t)K + kb,
               slot_addr + (uint32_t)(tl * C::kBTile + 1024 * (q & 7)));
       }
-      if (a_issuer) {
-        const uint32_t amax = (uint32_t)(K - st * kSK) * (kInt8 ? 2u : 1u) - 16u;
-        dma16(a + (size_t)st * C::kARow, a_row + min(a_chk, amax),
-              slot_addr + (uint32_t)(kSMaxTiles * C::kBTile + 1024 * wave));
+    }
+  };
+
+  // The weights of stage 0 do not depend on the routing: start them now.  The
+  // routing buffers are then read with scalar loads (they count on lgkmcnt,
+  // not vmcnt), so reading them does not wait for this DMA.
+  issue_b(0);
+  const bool early_b = true;
+  typedef const __attribute__((address_space(4))) int *cint_ptr;
+  typedef const __attribute__((address_space(4))) float *cfloat_ptr;
+  const cint_ptr c_expert_ids = (cint_ptr)expert_ids;
+  const cint_ptr c_sorted = (cint_ptr)sorted_ids;
+  const cfloat_ptr c_topk = (cfloat_ptr)topk_w;
+
+  // this expert's blocks [b_begin, b_end) from the ascending block labels
+  // (-1 after the last block); every wavefront scans them on its scalar unit,
+  // 16 labels per load
+  typedef int int16v __attribute__((ext_vector_type(16)));
+  typedef const __attribute__((address_space(4))) int16v *cint16_ptr;
+  int b_begin = max_blocks, b_end = max_blocks;
+  {
+    auto visit = [&](int b, int v) {
+      v = v < 0 ? (1 << 30) : v;
+      if (b_begin == max_blocks && v >= e) b_begin = b;
+      if (b_end == max_blocks && v > e) b_end = b;
+    };
+    int b0 = 0;
+    for (; b0 + 16 <= max_blocks && b_end == max_blocks; b0 += 16) {
+      const int16v v = *(cint16_ptr)(c_expert_ids + b0);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) visit(b0 + u, v[u]);
+    }
+    for (; b0 < max_blocks && b_end == max_blocks; ++b0) visit(b0, c_expert_ids[b0]);
+  }
+  if (b_begin >= b_end) {
+    wait_dma_all();                                        // no DMA may outlive the workgroup
+    return;
+  }
+
+  for (int bp = b_begin, pass_ = 0; bp < b_end; bp += kSMB, ++pass_) {
+    const int nmb = min(b_end - bp, kSMB);
+    __syncthreads();                                       // s_slot / ring reuse across passes
+    if (wave == 0) {                                       // slot ids and router weights, scalar
+#pragma unroll
+      for (int i = 0; i < kSMB; ++i) {
+        int16v sl;
+        if (i < nmb) {
+          sl = *(cint16_ptr)(c_sorted + (bp + i) * 16);    // one 64-byte block of slots
+        } else {
+#pragma unroll
+          for (int u = 0; u < 16; ++u) sl[u] = S;
+        }
+        float tw[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) tw[u] = sl[u] < S ? c_topk[sl[u]] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          if (lane == u) {
+            s_slot[i * 16 + u] = sl[u];
+            s_topk[i * 16 + u] = tw[u];
+          }
       }
+    }
+    __syncthreads();
+
+    // activation DMA of this wavefront (1 KB instructions q = wave + 8j): the
+    // row and the swizzled chunk each lane fetches
+    constexpr int kAPerWave = (C::kAInstr + kSWaves - 1) / kSWaves;
+    const int a_instr = kInt8 ? 4 * nmb : 2 * nmb;        // 1 KB holds 4 (bf16) or 8 (fp8) rows
+    uint32_t a_row[kAPerWave], a_chk[kAPerWave];
+#pragma unroll
+    for (int j = 0; j < kAPerWave; ++j) {
+      const int q = wave + kSWaves * j;
+      a_row[j] = 0;
+      a_chk[j] = 0;
+      if (q < C::kAInstr) {
+        int r, c;
+        if constexpr (kInt8) {                             // 4 rows of 256 bytes per KB
+          r = 4 * q + (lane >> 4);
+          c = lane & 15;
+        } else {                                           // 8 rows of 128 bytes per KB
+          r = 8 * q + (lane >> 3);
+          c = lane & 7;
+        }
+        const int slot = s_slot[r];
+        const uint32_t tok = slot < S ? (uint32_t)(slot / top_k) : 0u;
+        a_row[j] = tok * a_row_bytes;
+        // the lane at LDS chunk position c fetches source chunk c ^ swizzle(r)
+        a_chk[j] = 16u * (uint32_t)(kInt8 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7)));
+      }
+    }
+
+    auto issue_a = [&](int st) {
+      const uint32_t slot_addr = lds_ring + (uint32_t)((st & 1) * C::kStage);
+      const uint32_t amax = (uint32_t)(K - st * kSK) * (kInt8 ? 2u : 1u) - 16u;
+#pragma unroll
+      for (int j = 0; j < kAPerWave; ++j) {
+        const int q = wave + kSWaves * j;
+        if (q < a_instr)                                   // only the rows of this pass
+          dma16(a + (size_t)st * C::kARow, a_row[j] + min(a_chk[j], amax),
+                slot_addr + (uint32_t)(kSMaxTiles * C::kBTile + 1024 * q));
+      }
+    };
+    auto issue = [&](int st) {
+      issue_b(st);
+      issue_a(st);
     };
 
     f32x4 acc[4][kSMB];                                    // tiles par, par+2, par+4, par+6
@@ -267,6 +352,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
           i32x4 av[kSMB][2];
 #pragma unroll
           for (int i = 0; i < kSMB; ++i) {
+            if (i >= nmb) break;
             const int r = 16 * i + r16;
             av[i][0] = *reinterpret_cast<const i32x4 *>(sa + sw256(r, c0));
             av[i][1] = *reinterpret_cast<const i32x4 *>(sa + sw256(r, c0 + 1));
@@ -290,6 +376,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
           i32x8 av[kSMB];
 #pragma unroll
           for (int i = 0; i < kSMB; ++i) {
+            if (i >= nmb) break;
             const int r = 16 * i + r16;
             const i32x4 al = *reinterpret_cast<const i32x4 *>(sa + sw128(r, g));
             const i32x4 ah = *reinterpret_cast<const i32x4 *>(sa + sw128(r, g + 4));
@@ -313,7 +400,11 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
       }
     };
 
-    issue(0);
+    if (pass_ == 0 && early_b) {
+      issue_a(0);                                          // stage 0's weights are already in flight
+    } else {
+      issue(0);
+    }
     for (int st = 0; st < nst; ++st) {
       wait_dma_all();                                      // this wave's DMA for stage st landed
       __syncthreads();                                     // ... and everyone's; the other slot is free
@@ -322,6 +413,14 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
     }
 
     // ---- epilogue: scale x router weight, one store per output element ----
+    if (pass_ == 0) {
+      // per-column scale of this workgroup's tiles (int8) or the fused scalar
+      for (int c = tid; c < G * 64; c += kSThreads) {
+        const int col = min(t_begin * 64 + c, N - 1);
+        s_scale[c] = kInt8 ? w_scale[(size_t)e * N + col] : a_scale[0] * w_scale[e];
+      }
+      __syncthreads();
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int tl = par + 2 * t;
@@ -360,14 +459,14 @@ __device__ __forceinline__ int a_lds_off(int r, int c) {
 
 enum { kFmtFp8 = 0, kFmtInt8 = 1, kFmtMx = 2 };
 
-template <int kFmt>
+template <int kFmt, bool kTiled>
 __global__ __launch_bounds__(kThreads, 2) void tile_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ a_sf, const uint8_t *__restrict__ w,
     const float *__restrict__ w_scale, const uint8_t *__restrict__ w_sf,
     const int *__restrict__ sorted_ids, const int *__restrict__ expert_ids,
     const int *__restrict__ num_post, const float *__restrict__ topk_w,
-    const int *__restrict__ m_offsets, int M, int K, int N, int E, int top_k,
+    const int *__restrict__ m_offsets, int M, int K, int N, int E, int top_k, int max_blocks,
     float *__restrict__ y, uint16_t *__restrict__ out) {
   constexpr bool kInt8 = kFmt == kFmtInt8;
   constexpr bool kMx = kFmt == kFmtMx;
@@ -387,7 +486,7 @@ __global__ __launch_bounds__(kThreads, 2) void tile_kernel(
 
   // ---- tile space: expert by expert, column tile by column tile, row block fastest
   if constexpr (!kMx) {
-    expert_block_starts(expert_ids, *num_post / kTBM, E, s_blk_first);
+    expert_block_starts(expert_ids, max_blocks, E, s_blk_first);
     __syncthreads();
   }
   if (tid == 0) {
@@ -477,14 +576,30 @@ __global__ __launch_bounds__(kThreads, 2) void tile_kernel(
   const int rd0 = a_lds_off(r16, kInt8 ? 2 * g : g);
   const int rd1 = a_lds_off(r16, kInt8 ? 2 * g + 1 : g + 4);
 
-  // B: this wavefront's 64 columns, loaded straight into registers
-  uint32_t woff[kTNF];
+  // B: this wavefront's 64 columns, loaded straight into registers.
+  // Row-major: offset of the lane's 16-byte piece at k = 16g in its row.
+  // Tiled (moe_pack_weights): the wavefront's 64 columns are one packed tile;
+  // woff/woff2 are the lane's chunks g and g + 4 inside a 128-k block.
+  uint32_t woff[kTNF], woff2[kTNF];
   uint32_t wsoff[kTNF];
+  uint32_t wblk = 0;
+  if constexpr (kTiled) {
+    const int T = (N + 63) / 64;
+    const int pt = min(n0 / 64 + wave, T - 1);
+    wblk = ((uint32_t)e * (uint32_t)T + (uint32_t)pt) * (uint32_t)((K + 127) / 128) * 8192u;
+  }
 #pragma unroll
   for (int j = 0; j < kTNF; ++j) {
     int col = n0 + wave * kTNW + j * 16 + r16;
     col = col < N ? col : N - 1;
-    woff[j] = ((uint32_t)e * (uint32_t)N + (uint32_t)col) * (uint32_t)K + 16u * g;
+    if constexpr (kTiled) {
+      const int r = j * 16 + r16;
+      woff[j] = (uint32_t)(r * 128 + ((g ^ ((r >> 1) & 7)) << 4));
+      woff2[j] = (uint32_t)(r * 128 + (((g + 4) ^ ((r >> 1) & 7)) << 4));
+    } else {
+      woff[j] = ((uint32_t)e * (uint32_t)N + (uint32_t)col) * (uint32_t)K + 16u * g;
+      woff2[j] = woff[j] + 64u;
+    }
     wsoff[j] = ((uint32_t)e * (uint32_t)N + (uint32_t)col) * (uint32_t)kb_row;
   }
 
@@ -519,12 +634,27 @@ __global__ __launch_bounds__(kThreads, 2) void tile_kernel(
     }
   };
   auto load_b = [&](BRegs &bb, int s) {
-    const uint8_t *base = w + (size_t)s * kStepK;
+    if constexpr (kTiled) {
+      // fp8: step s is block s (chunks g, g + 4); int8: step s is half s & 1 of
+      // block s >> 1 (chunk g, then g + 4)
+      const uint8_t *base = w + wblk + (size_t)(kInt8 ? (s >> 1) : s) * 8192u;
 #pragma unroll
-    for (int j = 0; j < kTNF; ++j) {
+      for (int j = 0; j < kTNF; ++j) {
+        if constexpr (kInt8) {
+          bb.v[j][0] = ld16(base + ((s & 1) ? woff2[j] : woff[j]));
+        } else {
+          bb.v[j][0] = ld16(base + woff[j]);
+          bb.v[j][kBVec - 1] = ld16(base + woff2[j]);
+        }
+      }
+    } else {
+      const uint8_t *base = w + (size_t)s * kStepK;
 #pragma unroll
-      for (int v = 0; v < kBVec; ++v) bb.v[j][v] = ld16(base + woff[j] + 64 * v);
-      if constexpr (kMx) bb.sf[j] = *reinterpret_cast<const uint32_t *>(w_sf + wsoff[j] + 4 * s);
+      for (int j = 0; j < kTNF; ++j) {
+#pragma unroll
+        for (int v = 0; v < kBVec; ++v) bb.v[j][v] = ld16(base + (v ? woff2[j] : woff[j]));
+        if constexpr (kMx) bb.sf[j] = *reinterpret_cast<const uint32_t *>(w_sf + wsoff[j] + 4 * s);
+      }
     }
   };
   auto compute = [&](const BRegs &bb, const uint8_t *lds, const uint32_t *lds_sf) {
@@ -652,15 +782,16 @@ hipError_t launch_gemm_fp8(const uint8_t *a_q, const float *a_scale, const uint8
   if (r.block_m == 16) {
     int groups, tpg;
     stream_grid(r.N, r.E, groups, tpg);
-    hipLaunchKernelGGL(stream_kernel<false>, dim3(r.E * groups), dim3(kSThreads), 0, s, a_q,
-                       a_scale, w_q, w_scale, r.sorted_ids, r.expert_ids, r.num_post, r.topk_w,
-                       r.M, r.K, r.N, r.top_k, groups, tpg, r.y);
+    auto k = r.w_layout ? stream_kernel<false, true> : stream_kernel<false, false>;
+    hipLaunchKernelGGL(k, dim3(r.E * groups), dim3(kSThreads), 0, s, a_q, a_scale, w_q, w_scale,
+                       r.sorted_ids, r.expert_ids, r.num_post, r.topk_w, r.M, r.K, r.N, r.top_k,
+                       groups, tpg, r.max_blocks, r.y);
   } else {
     const long long tiles = (long long)r.max_blocks * ((r.N + kTBN - 1) / kTBN);
-    hipLaunchKernelGGL(tile_kernel<kFmtFp8>, dim3(tile_grid(tiles)), dim3(kThreads), 0, s, a_q,
-                       a_scale, nullptr, w_q, w_scale, nullptr, r.sorted_ids, r.expert_ids,
-                       r.num_post, r.topk_w, nullptr, r.M, r.K, r.N, r.E, r.top_k, r.y,
-                       nullptr);
+    auto k = r.w_layout ? tile_kernel<kFmtFp8, true> : tile_kernel<kFmtFp8, false>;
+    hipLaunchKernelGGL(k, dim3(tile_grid(tiles)), dim3(kThreads), 0, s, a_q, a_scale, nullptr,
+                       w_q, w_scale, nullptr, r.sorted_ids, r.expert_ids, r.num_post, r.topk_w,
+                       nullptr, r.M, r.K, r.N, r.E, r.top_k, r.max_blocks, r.y, nullptr);
   }
   return hipGetLastError();
 }
@@ -672,14 +803,16 @@ hipError_t launch_gemm_int8(const uint16_t *a, const int8_t *w_q, const float *w
   if (r.block_m == 16) {
     int groups, tpg;
     stream_grid(r.N, r.E, groups, tpg);
-    hipLaunchKernelGGL(stream_kernel<true>, dim3(r.E * groups), dim3(kSThreads), 0, s, ab,
-                       nullptr, wb, w_scale, r.sorted_ids, r.expert_ids, r.num_post, r.topk_w,
-                       r.M, r.K, r.N, r.top_k, groups, tpg, r.y);
+    auto k = r.w_layout ? stream_kernel<true, true> : stream_kernel<true, false>;
+    hipLaunchKernelGGL(k, dim3(r.E * groups), dim3(kSThreads), 0, s, ab, nullptr, wb, w_scale,
+                       r.sorted_ids, r.expert_ids, r.num_post, r.topk_w, r.M, r.K, r.N, r.top_k,
+                       groups, tpg, r.max_blocks, r.y);
   } else {
     const long long tiles = (long long)r.max_blocks * ((r.N + kTBN - 1) / kTBN);
-    hipLaunchKernelGGL(tile_kernel<kFmtInt8>, dim3(tile_grid(tiles)), dim3(kThreads), 0, s, ab,
-                       nullptr, nullptr, wb, w_scale, nullptr, r.sorted_ids, r.expert_ids,
-                       r.num_post, r.topk_w, nullptr, r.M, r.K, r.N, r.E, r.top_k, r.y, nullptr);
+    auto k = r.w_layout ? tile_kernel<kFmtInt8, true> : tile_kernel<kFmtInt8, false>;
+    hipLaunchKernelGGL(k, dim3(tile_grid(tiles)), dim3(kThreads), 0, s, ab, nullptr, nullptr, wb,
+                       w_scale, nullptr, r.sorted_ids, r.expert_ids, r.num_post, r.topk_w, nullptr,
+                       r.M, r.K, r.N, r.E, r.top_k, r.max_blocks, r.y, nullptr);
   }
   return hipGetLastError();
 }
@@ -689,9 +822,9 @@ hipError_t launch_gemm_mxfp8(const uint8_t *a_q, const uint8_t *a_sf, const uint
                              int E, uint16_t *out, hipStream_t s) {
   const long long blocks = (rows + kTBM - 1) / kTBM + E;
   const long long tiles = blocks * ((N + kTBN - 1) / kTBN);
-  hipLaunchKernelGGL(tile_kernel<kFmtMx>, dim3(tile_grid(tiles)), dim3(kThreads), 0, s, a_q,
+  hipLaunchKernelGGL((tile_kernel<kFmtMx, false>), dim3(tile_grid(tiles)), dim3(kThreads), 0, s, a_q,
                      nullptr, a_sf, w_q, nullptr, w_sf, nullptr, nullptr, nullptr, nullptr,
-                     m_offsets, rows, K, N, E, 1, nullptr, out);
+                     m_offsets, rows, K, N, E, 1, 0, nullptr, out);
   return hipGetLastError();
 }
 

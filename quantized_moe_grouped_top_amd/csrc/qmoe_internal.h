@@ -23,6 +23,8 @@ constexpr int kMaxSlots = 65536;
 constexpr int kAmaxPartials = 1024;   // per-tensor amax partial results (floats)
 constexpr int kMxBlock = 32;
 constexpr int kMxRowPad = 128;
+constexpr int kPackRows = 64;         // tiled weight layout: rows per tile
+constexpr int kPackK = 128;           // tiled weight layout: bytes of k per slice
 
 
 // Saturate to the e4m3 range so the conversion below can never overflow.
@@ -72,6 +74,7 @@ struct RoutedArgs {
   const int *num_post;
   const float *topk_w;
   int M, K, N, E, top_k, block_m, max_blocks;
+  int w_layout;                        // 0 row-major [E,N,K], 1 tiled (moe_pack_weights)
   float *y;
 };
 
@@ -82,6 +85,9 @@ hipError_t launch_gemm_int8(const uint16_t *a, const int8_t *w_q, const float *w
 hipError_t launch_gemm_mxfp8(const uint8_t *a_q, const uint8_t *a_sf, const uint8_t *w_q,
                              const uint8_t *w_sf, const int *m_offsets, int rows, int K,
                              int N, int E, uint16_t *out, hipStream_t s);
+
+hipError_t launch_pack_weights(const uint8_t *w, int E, int N, int K, uint8_t *packed,
+                               hipStream_t s);
 
 hipError_t launch_combine(const float *y, int M, int N, int top_k, uint16_t *out,
                           hipStream_t s);

@@ -225,6 +225,32 @@ __global__ __launch_bounds__(kThreads) void quant_mx_rows_kernel(const float *__
   }
 }
 
+// ---- weight re-layout for streaming: one thread per 16-byte chunk ----------
+// Block (e, t, s) of 64 rows x 128 bytes, rows in order, chunk c of row r at
+// position c ^ ((r >> 1) & 7); rows >= N and k >= K are zero.
+__global__ __launch_bounds__(kThreads) void pack_weights_kernel(const uint8_t *__restrict__ w,
+                                                                int E, int N, int K,
+                                                                uint8_t *__restrict__ packed) {
+  const int T = (N + kPackRows - 1) / kPackRows;
+  const int S = (K + kPackK - 1) / kPackK;
+  const long long chunks = (long long)E * T * S * (kPackRows * kPackK / 16);
+  for (long long i = blockIdx.x * (long long)kThreads + threadIdx.x; i < chunks;
+       i += (long long)gridDim.x * kThreads) {
+    const long long b = i >> 9;                       // 512 chunks per 8 KB block
+    const int within = (int)(i & 511);
+    const int r = within >> 3;
+    const int c = (within & 7) ^ ((r >> 1) & 7);
+    const int s_ = (int)(b % S);
+    const int t = (int)((b / S) % T);
+    const int e = (int)(b / ((long long)S * T));
+    const int n = t * kPackRows + r;
+    const int k0 = s_ * kPackK + 16 * c;
+    i32x4 v = {0, 0, 0, 0};
+    if (n < N && k0 < K) v = *reinterpret_cast<const i32x4 *>(w + ((long long)e * N + n) * K + k0);
+    *reinterpret_cast<i32x4 *>(packed + i * 16) = v;
+  }
+}
+
 int grid_for(long long items, int cap) {
   long long g = (items + kThreads - 1) / kThreads;
   if (g < 1) g = 1;
@@ -277,6 +303,15 @@ hipError_t launch_quant_mx_rows_f32(const float *w, long long rows, int K, uint8
                                     uint8_t *sf, hipStream_t s) {
   hipLaunchKernelGGL(quant_mx_rows_kernel, dim3(grid_for(rows * (K / kMxBlock), 16384)),
                      dim3(kThreads), 0, s, w, rows, K, q, sf);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_weights(const uint8_t *w, int E, int N, int K, uint8_t *packed,
+                               hipStream_t s) {
+  const long long chunks = (long long)E * ((N + kPackRows - 1) / kPackRows) *
+                           ((K + kPackK - 1) / kPackK) * (kPackRows * kPackK / 16);
+  hipLaunchKernelGGL(pack_weights_kernel, dim3(grid_for(chunks, 16384)), dim3(kThreads), 0, s, w,
+                     E, N, K, packed);
   return hipGetLastError();
 }
 

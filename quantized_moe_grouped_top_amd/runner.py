@@ -13,11 +13,11 @@ Every step runs in the library's HIP kernels; nothing here computes.
 
 import torch
 
-from . import (MOE_Q_FP8_PER_TENSOR, MOE_Q_INT8_PER_CHANNEL, MOE_Q_MXFP8, moe_align_block_size,
-               moe_align_max_padded, moe_combine, moe_grouped_gemm_fp8w8a8,
-               moe_grouped_gemm_int8w8a16, moe_grouped_gemm_mxfp8, moe_mx_scale_rows,
-               moe_quantize_act, moe_quantize_weights, moe_quantize_workspace_bytes,
-               moe_recommended_block_m)
+from . import (MOE_Q_FP8_PER_TENSOR, MOE_Q_INT8_PER_CHANNEL, MOE_Q_MXFP8, MOE_W_ROWMAJOR,
+               MOE_W_TILED, moe_align_block_size, moe_align_max_padded, moe_combine,
+               moe_grouped_gemm_fp8w8a8, moe_grouped_gemm_int8w8a16, moe_grouped_gemm_mxfp8,
+               moe_mx_scale_rows, moe_pack_weights, moe_packed_weight_bytes, moe_quantize_act,
+               moe_quantize_weights, moe_quantize_workspace_bytes, moe_recommended_block_m)
 
 
 def _empty(shape, dtype, device):
@@ -48,11 +48,21 @@ def quantize_weights(w, fmt):
     raise ValueError(fmt)
 
 
+def pack_weights(w_q):
+    """Tiled (MOE_W_TILED) copy of one-byte weights [E, N, K] on their device."""
+    E, N, K = w_q.shape
+    out = _empty((moe_packed_weight_bytes(E, N, K),), torch.uint8, w_q.device)
+    moe_pack_weights(w_q, E, N, K, out)
+    return out
+
+
 class RoutedMoE:
     """fp8 W8A8 or int8 W8A16 MoE layer of fixed (M, K, N, E, top_k)."""
 
-    def __init__(self, fmt, M, K, N, E, top_k, device="cuda", block_m=None):
+    def __init__(self, fmt, M, K, N, E, top_k, device="cuda", block_m=None,
+                 w_layout=MOE_W_ROWMAJOR):
         assert fmt in ("fp8", "int8")
+        self.w_layout = w_layout
         self.fmt, self.M, self.K, self.N, self.E, self.top_k = fmt, M, K, N, E, top_k
         self.block_m = block_m or moe_recommended_block_m(M, E, top_k)
         self.max_padded = moe_align_max_padded(M, E, top_k, self.block_m)
@@ -83,12 +93,14 @@ class RoutedMoE:
 
     def gemm(self, x, w_q, w_scale):
         if self.fmt == "fp8":
-            moe_grouped_gemm_fp8w8a8(self.a_q, self.a_scale, w_q, w_scale, self.sorted_token_ids,
+            moe_grouped_gemm_fp8w8a8(self.a_q, self.a_scale, w_q, w_scale, self.w_layout,
+                                     self.sorted_token_ids,
                                      self.expert_ids, self.num_tokens_post_padded,
                                      self.topk_weights, self.M, self.K, self.N, self.E,
                                      self.top_k, self.block_m, self.y)
         else:
-            moe_grouped_gemm_int8w8a16(x, w_q, w_scale, self.sorted_token_ids, self.expert_ids,
+            moe_grouped_gemm_int8w8a16(x, w_q, w_scale, self.w_layout, self.sorted_token_ids,
+                                       self.expert_ids,
                                        self.num_tokens_post_padded, self.topk_weights, self.M,
                                        self.K, self.N, self.E, self.top_k, self.block_m, self.y)
 

@@ -38,7 +38,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     h = ctypes.CDLL(qm.LIB_PATH)
     for n in names:
         assert hasattr(h, n), n
@@ -78,7 +78,7 @@ MIS = FAKE + 1          # misaligned for every alignment rule
 
 
 def _gemm_fp8(**kw):
-    a = dict(a_q=FAKE, a_scale=FAKE, w_q=FAKE, w_scale=FAKE, sorted_token_ids=FAKE,
+    a = dict(a_q=FAKE, a_scale=FAKE, w_q=FAKE, w_scale=FAKE, w_layout=0, sorted_token_ids=FAKE,
              expert_ids=FAKE, num_tokens_post_padded=FAKE, topk_weights=FAKE, M=64, K=256,
              N=128, E=8, top_k=2, block_m=16, y=FAKE, stream=0)
     a.update(kw)
@@ -93,6 +93,8 @@ def _gemm_fp8(**kw):
     (dict(N=0), qm.MOE_EINVAL),
     (dict(top_k=9), qm.MOE_EINVAL),
     (dict(E=200, top_k=2), qm.MOE_EINVAL),
+    (dict(w_layout=2), qm.MOE_EINVAL),         # unknown weight layout
+    (dict(N=1 << 20, K=1 << 12), qm.MOE_EUNSUPPORTED),   # weights beyond 4 GiB
 ])
 def test_gemm_fp8_rejects(kw, code):
     with pytest.raises(qm.MoeError) as ei:
@@ -103,8 +105,8 @@ def test_gemm_fp8_rejects(kw, code):
 
 def test_gemm_int8_and_mxfp8_reject():
     with pytest.raises(qm.MoeError) as ei:
-        qm.moe_grouped_gemm_int8w8a16(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 96, 128, 8, 2,
-                                      16, FAKE, stream=0)
+        qm.moe_grouped_gemm_int8w8a16(FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, 64, 96, 128, 8,
+                                      2, 16, FAKE, stream=0)
     assert ei.value.code == qm.MOE_EUNSUPPORTED                 # K % 64
     with pytest.raises(qm.MoeError) as ei:
         qm.moe_grouped_gemm_mxfp8(FAKE, FAKE, FAKE, FAKE, FAKE, 100, 192, 64, 4, FAKE, stream=0)
@@ -135,6 +137,21 @@ def test_quantize_and_combine_reject():
     with pytest.raises(qm.MoeError) as ei:
         qm.moe_align_block_size(0, 4, 8, 2, 16, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
     assert ei.value.code == qm.MOE_EINVAL                       # null logits
+
+
+def test_pack_sizes_and_rejects():
+    assert qm.moe_packed_weight_bytes(8, 14336, 4096) == 8 * 224 * 32 * 8192
+    assert qm.moe_packed_weight_bytes(2, 100, 320) == 2 * 2 * 3 * 8192     # padded tiles/slices
+    assert qm.moe_packed_weight_bytes(0, 4, 4) == 0
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_pack_weights(FAKE, 2, 64, 100, FAKE, stream=0)
+    assert ei.value.code == qm.MOE_EUNSUPPORTED                 # K % 16
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_pack_weights(MIS, 2, 64, 128, FAKE, stream=0)
+    assert ei.value.code == qm.MOE_EINVAL                       # misaligned
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_pack_weights(FAKE, 64, 1 << 16, 1 << 12, FAKE, stream=0)
+    assert ei.value.code == qm.MOE_EUNSUPPORTED                 # 16 GiB packed
 
 
 def test_library_missing_is_loud(monkeypatch, tmp_path):

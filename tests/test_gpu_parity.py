@@ -38,17 +38,19 @@ def _announce(what):
 # ----------------------------------------------------------------------------
 # routed formats
 # ----------------------------------------------------------------------------
-def run_routed(wl, block_m=None, variant=0, full=True, n_tok=48, n_col=64, logits=None):
-    _announce(f"{wl.name} block_m={block_m} full={full}")
+def run_routed(wl, block_m=None, variant=0, full=True, n_tok=48, n_col=64, logits=None,
+               layout=qm.MOE_W_ROWMAJOR):
+    _announce(f"{wl.name} block_m={block_m} layout={layout} full={full}")
     M, K, N, E, top_k = wl.M, wl.K, wl.N, wl.E, wl.top_k
     case = synth.make_case(wl, variant, device=DEV)
     x, w = case["x"], case["w"]
     lg = case["logits"] if logits is None else logits.to(DEV)
-    moe = runner.RoutedMoE(wl.fmt, M, K, N, E, top_k, block_m=block_m)
+    moe = runner.RoutedMoE(wl.fmt, M, K, N, E, top_k, block_m=block_m, w_layout=layout)
     w_q, w_scale = runner.quantize_weights(w, wl.fmt)
+    w_gemm = runner.pack_weights(w_q) if layout == qm.MOE_W_TILED else w_q
     moe.y.fill_(float("nan"))
     moe.out.fill_(0x7FC0)
-    moe.forward(x, lg, w_q, w_scale)
+    moe.forward(x, lg, w_gemm, w_scale)
     torch.cuda.synchronize()
 
     rng = np.random.default_rng(synth.seed_of(wl.name, 99) % (1 << 32))
@@ -125,19 +127,24 @@ SMALL = [
 ]
 
 
+LAYOUTS = [qm.MOE_W_ROWMAJOR, qm.MOE_W_TILED]
+
+
+@pytest.mark.parametrize("layout", LAYOUTS, ids=["rowmajor", "tiled"])
 @pytest.mark.parametrize("block_m", [16, 128])
 @pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
-def test_routed_small(wl, block_m):
-    run_routed(wl, block_m=block_m, full=True)
+def test_routed_small(wl, block_m, layout):
+    run_routed(wl, block_m=block_m, full=True, layout=layout)
 
 
+@pytest.mark.parametrize("layout", LAYOUTS, ids=["rowmajor", "tiled"])
 @pytest.mark.parametrize("fmt", ["fp8", "int8"])
 @pytest.mark.parametrize("block_m", [16, 128])
-def test_routed_all_tokens_one_expert(fmt, block_m):
+def test_routed_all_tokens_one_expert(fmt, block_m, layout):
     wl = synth.small(fmt, 150, 256, 80, 8, 2)
     lg = torch.randn(150, 8, generator=torch.Generator().manual_seed(5))
     lg[:, 3] += 100.0                        # every token picks expert 3 first
-    run_routed(wl, block_m=block_m, full=True, logits=lg)
+    run_routed(wl, block_m=block_m, full=True, logits=lg, layout=layout)
 
 
 def test_routed_empty_batch():
@@ -151,7 +158,8 @@ def test_routed_empty_batch():
     assert torch.all(moe.expert_ids == -1)
     w_q, w_s = runner.quantize_weights(torch.randn(8, 64, 128, device=DEV), "fp8")
     # a GEMM and a combine with M = 0 are no-ops
-    qm.moe_grouped_gemm_fp8w8a8(moe.a_q, moe.a_scale, w_q, w_s, moe.sorted_token_ids,
+    qm.moe_grouped_gemm_fp8w8a8(moe.a_q, moe.a_scale, w_q, w_s, qm.MOE_W_ROWMAJOR,
+                                moe.sorted_token_ids,
                                 moe.expert_ids, moe.num_tokens_post_padded, moe.topk_weights, 0,
                                 128, 64, 8, 2, 16, moe.y)
     qm.moe_combine(moe.y, 0, 64, 2, moe.out)
@@ -185,8 +193,40 @@ FULL = [synth.WORKLOADS[n] for n in [
 
 @pytest.mark.parametrize("wl", FULL, ids=[w.name for w in FULL])
 def test_routed_full_size_sampled(wl):
-    run_routed(wl, block_m=None, full=False)
+    """The benchmark's launch configuration: recommended block_m, tiled weights."""
+    run_routed(wl, block_m=None, full=False, layout=qm.MOE_W_TILED)
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("wl", FULL[:2], ids=[w.name for w in FULL[:2]])
+def test_routed_full_size_sampled_rowmajor(wl):
+    run_routed(wl, block_m=None, full=False, layout=qm.MOE_W_ROWMAJOR)
+    torch.cuda.empty_cache()
+
+
+def _pack_reference(w, N, K):
+    """The MOE_W_TILED layout as its definition states it (numpy)."""
+    E = w.shape[0]
+    T, S = -(-N // 64), -(-K // 128)
+    pad = np.zeros((E, T * 64, S * 128), np.uint8)
+    pad[:, :N, :K] = w
+    blocks = pad.reshape(E, T, 64, S, 128).transpose(0, 1, 3, 2, 4)        # [E,T,S,64,128]
+    r = np.arange(64)[:, None]
+    pos = np.arange(8)[None, :]
+    src = pos ^ ((r >> 1) & 7)                                             # chunk stored at pos
+    chunks = blocks.reshape(E, T, S, 64, 8, 16)
+    out = np.take_along_axis(chunks, np.broadcast_to(src[None, None, None, :, :, None], chunks.shape), axis=4)
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("E,N,K", [(2, 64, 128), (3, 200, 320), (1, 17, 48), (8, 256, 4096)])
+def test_pack_weights_layout(E, N, K):
+    _announce(f"pack E={E} N={N} K={K}")
+    g = torch.Generator(device=DEV).manual_seed(E * 1000 + N + K)
+    w = torch.randint(0, 256, (E, N, K), generator=g, device=DEV, dtype=torch.int32).to(torch.uint8)
+    p = runner.pack_weights(w)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(p.cpu().numpy(), _pack_reference(w.cpu().numpy(), N, K))
 
 
 # ----------------------------------------------------------------------------

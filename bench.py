@@ -16,14 +16,17 @@ step before.
 Prints one JSON line: value = whole-step throughput in algorithmic HBM GB/s
 (the byte count of the "Tianxing/moe quantization" tables: activations +
 expert weights + scales + per-slot bf16 outputs), plus the TFLOPS of the
-step, the roofline of the dominant kernel (the grouped GEMM; its launches
-timed with HIP events on the stream they run on) and the CPU oracle timed on
-the host.
+step, the roofline of the dominant kernel (the grouped GEMM; each launch in
+the timed region is bracketed by a pair of HIP events on the stream it runs
+on, torch's current stream) and the CPU oracle timed on the host.
 """
 
 import argparse
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -60,7 +63,53 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle baseline")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device-to-device copy 10 times (the known-size "
+                        "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
+
+
+GEMM_SOURCES = ("qmoe_gemm.hip", "qmoe_internal.h")
+
+
+def kernel_source_hash():
+    """sha256 over the grouped-GEMM kernel sources: a recorded HBM traffic
+    figure is only valid for the kernel it was counted on."""
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "quantized_moe_grouped_top_amd", "csrc")
+    for name in GEMM_SOURCES:
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload):
+    """HBM bytes per grouped-GEMM launch counted by rocprofv3 (FETCH_SIZE +
+    WRITE_SIZE, scaled by the copy-kernel factor) for this workload, read from
+    the traffic summaries under profiles/; None when there is none or when the
+    kernel sources changed since the counters were taken."""
+    want = kernel_source_hash()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*traffic*.md"))):
+        text = open(path).read()
+        fields = dict(re.findall(r"^- (\w+): `([^`]*)`", text, re.M))
+        if fields.get("workload") == workload and fields.get("kernel_source_sha256") == want:
+            return int(fields["traffic_bytes_per_launch"])
+    return None
+
+
+def copy_calibration():
+    """One elementwise kernel over 1 GiB of float32 (read once, written once),
+    launched 10 times: torch's own element-wise kernel, not a DMA blit."""
+    import torch
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"kernel": "torch.neg float32", "bytes_read": 4 * n,
+                                           "bytes_written": 4 * n, "launches": 10}}), flush=True)
 
 
 def cpu_baseline(wl, case, target_s):
@@ -113,6 +162,9 @@ def main():
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
               f"(this build runs the hot path on a single MI355X).", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
 
     import quantized_moe_grouped_top_amd as qm
@@ -156,6 +208,7 @@ def main():
     for i in range(args.warmup):
         step(i, None)
     torch.cuda.synchronize()
+    # the library launches on torch's current stream, which these events mark
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -183,7 +236,7 @@ def main():
         peak = MFMA_PEAK_TFLOPS[dtype]
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
-    roof.update({"traffic": None, "kernel": "grouped GEMM", "kernel_us": round(gemm_ms * 1e3, 2),
+    roof.update({"traffic": recorded_traffic(wl.name), "kernel": "grouped GEMM", "kernel_us": round(gemm_ms * 1e3, 2),
                  "alg_bytes": int(nbytes), "flops": int(wl.flops)})
     line = {
         "metric": "TFLOPS and HBM GB/s (% of MI355X roofline) for quantized MoE GEMM, E=8 top_k=2",

@@ -154,21 +154,26 @@ __device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t
 
 __device__ __forceinline__ void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 15]
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 63] (0 for anything else)
 __device__ __forceinline__ void wait_dma_upto(int n) {
   switch (n) {
 #define QMOE_W(k) case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
-    QMOE_W(1) QMOE_W(2) QMOE_W(3) QMOE_W(4) QMOE_W(5) QMOE_W(6) QMOE_W(7) QMOE_W(8)
-    QMOE_W(9) QMOE_W(10) QMOE_W(11) QMOE_W(12) QMOE_W(13) QMOE_W(14) QMOE_W(15)
+#define QMOE_W8(b) QMOE_W(b) QMOE_W(b + 1) QMOE_W(b + 2) QMOE_W(b + 3) QMOE_W(b + 4) QMOE_W(b + 5) \
+    QMOE_W(b + 6) QMOE_W(b + 7)
+    QMOE_W(1) QMOE_W(2) QMOE_W(3) QMOE_W(4) QMOE_W(5) QMOE_W(6) QMOE_W(7)
+    QMOE_W8(8) QMOE_W8(16) QMOE_W8(24) QMOE_W8(32) QMOE_W8(40) QMOE_W8(48) QMOE_W8(56)
+#undef QMOE_W8
 #undef QMOE_W
     default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
   }
 }
 
-// 128-byte rows: 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 7);
-// 256-byte rows: at chunk c ^ (r & 15).  Either way 16 consecutive rows read
-// at one chunk index cover 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int sw128(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+// 128-byte rows: 16-byte chunk c of row r sits at chunk c ^ swz(r);
+// 256-byte rows: at chunk c ^ (r & 15).  Either way the 16 rows one fragment
+// read touches at one chunk index fall on distinct banks, whether the LDS
+// serves such a read 8 lanes (128 bytes) or 16 lanes (256 bytes) at a time.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int sw128(int r, int c) { return r * 128 + ((c ^ swz(r)) << 4); }
 __device__ __forceinline__ int sw256(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
 
 template <bool kInt8, bool kTiled>
@@ -219,7 +224,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
       for (int q = wave; q < nbi; q += kSWaves) {            // 8 rows of 128 bytes per KB
         const int tl = q >> 3;
         const int n = 8 * (q & 7) + (lane >> 3);
-        const int c = (lane & 7) ^ ((n >> 1) & 7);
+        const int c = (lane & 7) ^ swz(n);
         const int col = min((t_begin + tl) * 64 + n, N - 1);
         const uint32_t kb = min(16u * (uint32_t)c, kmax);
         dma16(wb, ((uint32_t)e * (uint32_t)N + (uint32_t)col) * (uint32_t)K + kb,
@@ -313,7 +318,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
         const uint32_t tok = slot < S ? (uint32_t)(slot / top_k) : 0u;
         a_row[j] = tok * a_row_bytes;
         // the lane at LDS chunk position c fetches source chunk c ^ swizzle(r)
-        a_chk[j] = 16u * (uint32_t)(kInt8 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7)));
+        a_chk[j] = 16u * (uint32_t)(kInt8 ? (c ^ (r & 15)) : (c ^ swz(r)));
       }
     }
 
@@ -594,8 +599,8 @@ __global__ __launch_bounds__(kThreads, 2) void tile_kernel(
     col = col < N ? col : N - 1;
     if constexpr (kTiled) {
       const int r = j * 16 + r16;
-      woff[j] = (uint32_t)(r * 128 + ((g ^ ((r >> 1) & 7)) << 4));
-      woff2[j] = (uint32_t)(r * 128 + (((g + 4) ^ ((r >> 1) & 7)) << 4));
+      woff[j] = (uint32_t)(r * 128 + ((g ^ swz(r)) << 4));
+      woff2[j] = (uint32_t)(r * 128 + (((g + 4) ^ swz(r)) << 4));
     } else {
       woff[j] = ((uint32_t)e * (uint32_t)N + (uint32_t)col) * (uint32_t)K + 16u * g;
       woff2[j] = woff[j] + 64u;
@@ -746,6 +751,257 @@ __global__ __launch_bounds__(kThreads, 2) void tile_kernel(
   }
 }
 
+// =============================================================================
+// block_m = 128, fp8 W8A8 and int8 W8A16: DMA-fed MFMA tiles
+// =============================================================================
+// One workgroup of 8 wavefronts (two per SIMD) per 128-row x 256-column
+// output tile of one expert; wavefront w owns the 64 x 64 quarter-of-a-half
+// (rows 64*(w & 1).., columns 64*(w >> 1)..) as 4 x 4 MFMA fragments.  Two
+// wavefronts per SIMD let one issue MFMAs while the other waits for its LDS
+// reads.
+//
+// Every k-stage (128 k) of the tile's activation rows and weight columns is
+// copied HBM/L2 -> LDS by global_load_lds_dwordx4 (direct-to-LDS DMA, as in
+// the streaming kernel) into a ring of kSlots stages that runs kSlots - 1
+// stages ahead of the MFMAs, so loads in flight cost no registers and their
+// latency hides behind whole stages of compute.  The wavefront pair of a
+// 64-column block DMAs that block (8 KB per stage, one half each) and every
+// wavefront an eighth of the activation rows; before a stage is read each
+// wavefront waits for its own DMA and the workgroup synchronises.
+//
+// LDS layouts (16-byte chunks, XOR-swizzled so that the 16 rows one fragment
+// read touches hit distinct banks):
+//   fp8 activations, 128-byte rows: chunk c of row r at c ^ swz(r)
+//   bf16 activations, 256-byte rows: chunk c of row r at c ^ (r & 15)
+//   weights, 64 rows of 128 bytes per column block: chunk c of row r at
+//   c ^ swz(r), the MOE_W_TILED block layout, so tiled weights are a plain
+//   8 KB copy and row-major weights are swizzled on the source side.
+constexpr int kGBM = 128;
+constexpr int kGBN = 256;
+constexpr int kGThreads = 512;
+
+template <bool kInt8>
+struct GCfg {
+  static constexpr int kARow = kInt8 ? 256 : 128;           // activation bytes per row per stage
+  static constexpr int kABytes = kGBM * kARow;
+  static constexpr int kBBytes = kGBN * 128;
+  static constexpr int kStage = kABytes + kBBytes;          // 48 KB (fp8) / 64 KB (int8)
+  static constexpr int kSlots = kInt8 ? 2 : 3;              // ring stages (LDS: 144 / 128 KB)
+  static constexpr int kAPerWave = kABytes / 1024 / 8;      // activation DMA instructions per wave
+  static constexpr int kPerStage = kAPerWave + 4;           // DMA instructions per wave per stage
+};
+
+template <bool kInt8, bool kTiled>
+__global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(
+    const uint8_t *__restrict__ a, const float *__restrict__ a_scale,
+    const uint8_t *__restrict__ w, const float *__restrict__ w_scale,
+    const int *__restrict__ sorted_ids, const int *__restrict__ expert_ids,
+    const float *__restrict__ topk_w, int M, int K, int N, int E, int top_k, int max_blocks,
+    float *__restrict__ y) {
+  using C = GCfg<kInt8>;
+  constexpr int kMF = 4, kNF = 4;                       // fragments per wavefront
+  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[C::kSlots * C::kStage];
+  __shared__ int s_row[kGBM];
+  __shared__ int s_blk_first[kMaxExperts + 1];
+  __shared__ int s_tile_first[kMaxExperts + 1];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int ntn = (N + kGBN - 1) / kGBN;
+
+  // ---- tile space: expert by expert, column tile by column tile, row block
+  // fastest; each XCD takes one contiguous chunk of it
+  expert_block_starts(expert_ids, max_blocks, E, s_blk_first);
+  __syncthreads();
+  if (tid == 0) {
+    int tiles = 0;
+    for (int ee = 0; ee < E; ++ee) {
+      s_tile_first[ee] = tiles;
+      tiles += (s_blk_first[ee + 1] - s_blk_first[ee]) * ntn;
+    }
+    s_tile_first[E] = tiles;
+  }
+  __syncthreads();
+  const int total = s_tile_first[E];
+  const int chunk = (total + kXcds - 1) / kXcds;
+  const int xcd = blockIdx.x % kXcds;
+  const int idx = blockIdx.x / kXcds;
+  const int L = xcd * chunk + idx;
+  if (idx >= chunk || L >= total) return;
+  int e = 0;
+  while (s_tile_first[e + 1] <= L) ++e;
+  const int nblk = s_blk_first[e + 1] - s_blk_first[e];
+  const int local = L - s_tile_first[e];
+  const int nt = local / nblk;
+  const int mb = local - nt * nblk;
+  const int n0 = nt * kGBN;
+  const int S = M * top_k;
+  if (tid < kGBM) s_row[tid] = sorted_ids[(s_blk_first[e] + mb) * kGBM + tid];
+  __syncthreads();
+
+  // ---- DMA sources of this lane ----------------------------------------------
+  const uint32_t lds_ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)s_ring;
+  const uint32_t a_row_bytes = kInt8 ? (uint32_t)K * 2u : (uint32_t)K;
+  const int nst = (K + 127) / 128;
+  // activations: instruction q = wave * kAPerWave + u moves 8 fp8 rows (or 4
+  // bf16 rows); the lane at LDS chunk position c fetches source chunk
+  // c ^ swizzle(row)
+  uint32_t a_row[C::kAPerWave], a_chk[C::kAPerWave];
+#pragma unroll
+  for (int u = 0; u < C::kAPerWave; ++u) {
+    const int q = wave * C::kAPerWave + u;
+    int r, c;
+    if constexpr (kInt8) {
+      r = 4 * q + (lane >> 4);
+      c = (lane & 15) ^ (r & 15);
+    } else {
+      r = 8 * q + (lane >> 3);
+      c = (lane & 7) ^ swz(r);
+    }
+    const int slot = s_row[r];
+    a_row[u] = (uint32_t)(slot < S ? slot / top_k : 0) * a_row_bytes;
+    a_chk[u] = 16u * (uint32_t)c;
+  }
+  // weights: rows 32*wm .. 32*wm + 31 of column block wn (4 instructions)
+  uint32_t wblk = 0;                                    // tiled: the packed block of stage 0
+  uint32_t b_row[4], b_chk[4];                          // row-major: 8 rows per instruction
+  if constexpr (kTiled) {
+    const int T = (N + 63) / 64;
+    const int pt = min(n0 / 64 + wn, T - 1);
+    wblk = ((uint32_t)e * (uint32_t)T + (uint32_t)pt) * (uint32_t)nst * 8192u;
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int n = 8 * (4 * wm + u) + (lane >> 3);
+      const int col = min(n0 + wn * 64 + n, N - 1);
+      b_row[u] = ((uint32_t)e * (uint32_t)N + (uint32_t)col) * (uint32_t)K;
+      b_chk[u] = 16u * (uint32_t)((lane & 7) ^ swz(n));
+    }
+  }
+
+  auto issue = [&](int st, int slot_i) {
+    const uint32_t base = lds_ring + (uint32_t)(slot_i * C::kStage);
+    // the last stage of an int8 W8A16 product with K % 128 == 64 holds 64 k:
+    // chunks past the row end are clamped (fetched but never used)
+    const uint32_t amax = (uint32_t)(K - st * 128) * (kInt8 ? 2u : 1u) - 16u;
+    const uint8_t *abase = a + (size_t)st * C::kARow;
+#pragma unroll
+    for (int u = 0; u < C::kAPerWave; ++u)
+      dma16(abase, a_row[u] + min(a_chk[u], amax),
+            base + (uint32_t)((wave * C::kAPerWave + u) * 1024));
+    const uint32_t bdst = base + (uint32_t)(C::kABytes + wn * 8192 + wm * 4096);
+    if constexpr (kTiled) {
+      const uint8_t *bbase = w + wblk + (size_t)st * 8192u + wm * 4096;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        dma16(bbase, (uint32_t)(u * 1024 + 16 * lane), bdst + (uint32_t)(u * 1024));
+    } else {
+      const uint32_t kmax = (uint32_t)(K - st * 128) - 16u;
+      const uint8_t *bbase = w + (size_t)st * 128u;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        dma16(bbase, b_row[u] + min(b_chk[u], kmax), bdst + (uint32_t)(u * 1024));
+    }
+  };
+
+  f32x4 acc[kMF][kNF];
+#pragma unroll
+  for (int i = 0; i < kMF; ++i)
+#pragma unroll
+    for (int j = 0; j < kNF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // fragment read offsets (independent of the fragment index: every swizzle
+  // depends on the row modulo 16 only)
+  const int sw = swz(r16);
+  auto compute = [&](int slot_i, int nh) {
+    const uint8_t *As = s_ring + slot_i * C::kStage + wm * 64 * C::kARow;
+    const uint8_t *Bs = s_ring + slot_i * C::kStage + C::kABytes + wn * 8192;
+    if constexpr (kInt8) {
+      for (int h = 0; h < nh; ++h) {
+        i32x4 bq[kNF][2];
+#pragma unroll
+        for (int j = 0; j < kNF; ++j)
+          dequant16(ld16(Bs + (j * 16 + r16) * 128 + (((g + 4 * h) ^ sw) << 4)), bq[j][0], bq[j][1]);
+        const int c0 = ((8 * h + 2 * g) ^ r16) << 4;
+        const int c1 = ((8 * h + 2 * g + 1) ^ r16) << 4;
+        i32x4 a0[kMF], a1[kMF];
+#pragma unroll
+        for (int i = 0; i < kMF; ++i) {
+          a0[i] = ld16(As + (i * 16 + r16) * 256 + c0);
+          a1[i] = ld16(As + (i * 16 + r16) * 256 + c1);
+        }
+#pragma unroll
+        for (int i = 0; i < kMF; ++i)
+#pragma unroll
+          for (int j = 0; j < kNF; ++j) {
+            acc[i][j] = mfma_bf16(a0[i], bq[j][0], acc[i][j]);
+            acc[i][j] = mfma_bf16(a1[i], bq[j][1], acc[i][j]);
+          }
+      }
+    } else {
+      i32x8 bv[kNF], av[kMF];
+#pragma unroll
+      for (int j = 0; j < kNF; ++j) {
+        const uint8_t *br = Bs + (j * 16 + r16) * 128;
+        bv[j] = __builtin_shufflevector(ld16(br + ((g ^ sw) << 4)), ld16(br + (((g + 4) ^ sw) << 4)),
+                                        0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+      for (int i = 0; i < kMF; ++i) {
+        const uint8_t *ar = As + (i * 16 + r16) * 128;
+        av[i] = __builtin_shufflevector(ld16(ar + ((g ^ sw) << 4)), ld16(ar + (((g + 4) ^ sw) << 4)),
+                                        0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+      for (int i = 0; i < kMF; ++i)
+#pragma unroll
+        for (int j = 0; j < kNF; ++j) acc[i][j] = mfma_fp8(av[i], bv[j], acc[i][j]);
+    }
+  };
+
+  // ---- the ring: stage st lives in slot st % kSlots --------------------------
+  constexpr int D = C::kSlots - 1;                      // stages in flight ahead of compute
+#pragma unroll
+  for (int st = 0; st < D; ++st)
+    if (st < nst) issue(st, st);
+  const int nh_last = kInt8 ? ((K - (nst - 1) * 128) >= 128 ? 2 : 1) : 1;
+  int slot_c = 0;                                       // slot of stage st
+  int slot_i = D % C::kSlots;                           // slot of stage st + D
+  for (int st = 0; st < nst; ++st) {
+    // stages st .. min(st + D - 1, nst - 1) are in flight: wait for stage st
+    // (loads complete in order, so waiting for stage st leaves the later
+    // stage's kPerStage DMAs in flight)
+    if (D == 2 && st + 1 < nst) wait_dma_upto(C::kPerStage);
+    else wait_dma_all();
+    __syncthreads();                                    // stage st complete; slot_i is free
+    if (st + D < nst) issue(st + D, slot_i);
+    compute(slot_c, (kInt8 && st == nst - 1) ? nh_last : 2);
+    slot_c = slot_c + 1 == C::kSlots ? 0 : slot_c + 1;
+    slot_i = slot_i + 1 == C::kSlots ? 0 : slot_i + 1;
+  }
+
+  // ---- epilogue ------------------------------------------------------------
+  float cscale = 1.0f;
+  if constexpr (!kInt8) cscale = a_scale[0] * w_scale[e];
+#pragma unroll
+  for (int j = 0; j < kNF; ++j) {
+    const int col = n0 + wn * 64 + j * 16 + r16;
+    if (col >= N) continue;
+    float cs = cscale;
+    if constexpr (kInt8) cs = w_scale[(size_t)e * N + col];
+#pragma unroll
+    for (int i = 0; i < kMF; ++i) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int slot = s_row[wm * 64 + i * 16 + 4 * g + rr];
+        if (slot < S) y[(size_t)slot * N + col] = acc[i][j][rr] * cs * topk_w[slot];
+      }
+    }
+  }
+}
+
 unsigned tile_grid(long long tiles_bound) {
   long long per = (tiles_bound + kXcds - 1) / kXcds;
   return (unsigned)(per * kXcds);
@@ -787,11 +1043,11 @@ hipError_t launch_gemm_fp8(const uint8_t *a_q, const float *a_scale, const uint8
                        r.sorted_ids, r.expert_ids, r.num_post, r.topk_w, r.M, r.K, r.N, r.top_k,
                        groups, tpg, r.max_blocks, r.y);
   } else {
-    const long long tiles = (long long)r.max_blocks * ((r.N + kTBN - 1) / kTBN);
-    auto k = r.w_layout ? tile_kernel<kFmtFp8, true> : tile_kernel<kFmtFp8, false>;
-    hipLaunchKernelGGL(k, dim3(tile_grid(tiles)), dim3(kThreads), 0, s, a_q, a_scale, nullptr,
-                       w_q, w_scale, nullptr, r.sorted_ids, r.expert_ids, r.num_post, r.topk_w,
-                       nullptr, r.M, r.K, r.N, r.E, r.top_k, r.max_blocks, r.y, nullptr);
+    const long long tiles = (long long)r.max_blocks * ((r.N + kGBN - 1) / kGBN);
+    auto k = r.w_layout ? gemm_kernel<false, true> : gemm_kernel<false, false>;
+    hipLaunchKernelGGL(k, dim3(tile_grid(tiles)), dim3(kGThreads), 0, s, a_q, a_scale, w_q, w_scale,
+                       r.sorted_ids, r.expert_ids, r.topk_w, r.M, r.K, r.N, r.E, r.top_k,
+                       r.max_blocks, r.y);
   }
   return hipGetLastError();
 }
@@ -808,11 +1064,11 @@ hipError_t launch_gemm_int8(const uint16_t *a, const int8_t *w_q, const float *w
                        r.sorted_ids, r.expert_ids, r.num_post, r.topk_w, r.M, r.K, r.N, r.top_k,
                        groups, tpg, r.max_blocks, r.y);
   } else {
-    const long long tiles = (long long)r.max_blocks * ((r.N + kTBN - 1) / kTBN);
-    auto k = r.w_layout ? tile_kernel<kFmtInt8, true> : tile_kernel<kFmtInt8, false>;
-    hipLaunchKernelGGL(k, dim3(tile_grid(tiles)), dim3(kThreads), 0, s, ab, nullptr, nullptr, wb,
-                       w_scale, nullptr, r.sorted_ids, r.expert_ids, r.num_post, r.topk_w, nullptr,
-                       r.M, r.K, r.N, r.E, r.top_k, r.max_blocks, r.y, nullptr);
+    const long long tiles = (long long)r.max_blocks * ((r.N + kGBN - 1) / kGBN);
+    auto k = r.w_layout ? gemm_kernel<true, true> : gemm_kernel<true, false>;
+    hipLaunchKernelGGL(k, dim3(tile_grid(tiles)), dim3(kGThreads), 0, s, ab, nullptr, wb, w_scale,
+                       r.sorted_ids, r.expert_ids, r.topk_w, r.M, r.K, r.N, r.E, r.top_k,
+                       r.max_blocks, r.y);
   }
   return hipGetLastError();
 }

@@ -152,6 +152,15 @@ __device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t
                : "memory", "m0");
 }
 
+// global_load_lds_dword: lane l copies 4 bytes from sbase + voff to LDS byte
+// address m0 + 4*l.
+__device__ __forceinline__ void dma4(const void *sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // s_waitcnt vmcnt(n) for a wave-uniform n in [0, 63] (0 for anything else)
@@ -447,318 +456,17 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
   }
 }
 
-// =============================================================================
-// block_m = 128: tiled MFMA kernel (also MXFP8)
-// =============================================================================
-constexpr int kTBM = 128;           // rows per tile
-constexpr int kTNW = 64;            // columns per wavefront
-constexpr int kTBN = 4 * kTNW;      // columns per tile
-constexpr int kTMF = kTBM / 16;     // 16-row fragments per wavefront
-constexpr int kTNF = kTNW / 16;     // 16-column fragments per wavefront
-constexpr int kRowBytes = 128;      // A bytes per row per k step (fp8: 128 k, bf16: 64 k)
-
-// byte offset of 16-byte chunk c of row r in the swizzled LDS A tile
-__device__ __forceinline__ int a_lds_off(int r, int c) {
-  return r * kRowBytes + ((c ^ (r & 7)) << 4);
-}
-
 enum { kFmtFp8 = 0, kFmtInt8 = 1, kFmtMx = 2 };
 
-template <int kFmt, bool kTiled>
-__global__ __launch_bounds__(kThreads, 2) void tile_kernel(
-    const uint8_t *__restrict__ a, const float *__restrict__ a_scale,
-    const uint8_t *__restrict__ a_sf, const uint8_t *__restrict__ w,
-    const float *__restrict__ w_scale, const uint8_t *__restrict__ w_sf,
-    const int *__restrict__ sorted_ids, const int *__restrict__ expert_ids,
-    const int *__restrict__ num_post, const float *__restrict__ topk_w,
-    const int *__restrict__ m_offsets, int M, int K, int N, int E, int top_k, int max_blocks,
-    float *__restrict__ y, uint16_t *__restrict__ out) {
-  constexpr bool kInt8 = kFmt == kFmtInt8;
-  constexpr bool kMx = kFmt == kFmtMx;
-  constexpr int kStepK = kInt8 ? 64 : 128;             // k per step
-  constexpr int kBVec = kInt8 ? 1 : 2;                 // 16-byte B loads per fragment
-
-  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][kTBM * kRowBytes];
-  __shared__ uint32_t s_asf[2][kTBM];                   // MXFP8 A scales of the step
-  __shared__ int s_row[kTBM];                           // slot (routed) or row (MXFP8)
-  __shared__ int s_blk_first[kMaxExperts + 1];          // first block of every expert
-  __shared__ int s_tile_first[kMaxExperts + 1];         // first tile of every expert
-  __shared__ int s_mo[kMaxExperts + 1];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, r16 = lane & 15;
-  const int ntn = (N + kTBN - 1) / kTBN;
-
-  // ---- tile space: expert by expert, column tile by column tile, row block fastest
-  if constexpr (!kMx) {
-    expert_block_starts(expert_ids, max_blocks, E, s_blk_first);
-    __syncthreads();
-  }
-  if (tid == 0) {
-    int blk = 0, tiles = 0;
-    if constexpr (kMx) {
-      for (int e = 0; e <= E; ++e) s_mo[e] = m_offsets[e];
-      for (int e = 0; e < E; ++e) {
-        s_blk_first[e] = blk;
-        s_tile_first[e] = tiles;
-        const int m = s_mo[e + 1] - s_mo[e];
-        const int nblk = m > 0 ? (m + kTBM - 1) / kTBM : 0;
-        blk += nblk;
-        tiles += nblk * ntn;
-      }
-    } else {
-      for (int e = 0; e < E; ++e) {
-        s_tile_first[e] = tiles;
-        tiles += (s_blk_first[e + 1] - s_blk_first[e]) * ntn;
-      }
-      blk = s_blk_first[E];
-    }
-    s_blk_first[E] = blk;
-    s_tile_first[E] = tiles;
-  }
-  __syncthreads();
-  const int total = s_tile_first[E];
-  const int chunk = (total + kXcds - 1) / kXcds;
-  const int xcd = blockIdx.x % kXcds;
-  const int idx = blockIdx.x / kXcds;
-  const int L = xcd * chunk + idx;
-  if (idx >= chunk || L >= total) return;
-  int e = 0;
-  while (s_tile_first[e + 1] <= L) ++e;
-  const int nblk = s_blk_first[e + 1] - s_blk_first[e];
-  const int local = L - s_tile_first[e];
-  const int nt = local / nblk;
-  const int mb = local - nt * nblk;                     // block within the expert
-  const int n0 = nt * kTBN;
-
-  // ---- rows of the tile ----------------------------------------------------
-  const int S = M * top_k;
-  int row_end = 0;                                      // MXFP8: rows of the expert
-  if constexpr (kMx) {
-    row_end = s_mo[e + 1];
-    const int r0 = s_mo[e] + mb * kTBM;
-    for (int r = tid; r < kTBM; r += kThreads) s_row[r] = r0 + r;
-  } else {
-    const int b = s_blk_first[e] + mb;
-    for (int r = tid; r < kTBM; r += kThreads) s_row[r] = sorted_ids[b * kTBM + r];
-  }
-  __syncthreads();
-
-  // A staging: thread t moves the 16-byte chunk (t & 7) of rows (t >> 3) + 32q,
-  // q < 4.  All four rows share the swizzle (row & 7), so the LDS targets are
-  // 4096 bytes apart.  Offsets are 32-bit: the tensors are below 4 GiB.
-  const uint32_t a_row_bytes = kInt8 ? (uint32_t)K * 2 : (uint32_t)K;
-  const int ach = tid & 7;
-  uint32_t aoff[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = (tid >> 3) + 32 * q;
-    uint32_t src_row;
-    if constexpr (kMx) {
-      const int rr = s_row[r];
-      src_row = (uint32_t)(rr < row_end ? rr : row_end - 1);
-    } else {
-      const int slot = s_row[r];
-      src_row = (uint32_t)(slot < S ? slot / top_k : 0);
-    }
-    aoff[q] = src_row * a_row_bytes + (uint32_t)ach * 16u;
-  }
-  const int adst = a_lds_off(tid >> 3, ach);
-  // MXFP8 A scales: thread t < 128 loads the 4 scale bytes of row t for the step
-  uint32_t asf_off = 0;
-  const int kb_row = K / 32;
-  if constexpr (kMx) {
-    if (tid < kTBM) {
-      const int rr = s_row[tid];
-      const int lr = (rr < row_end ? rr : row_end - 1) - s_mo[e];
-      int po = 0;                                       // padded scale row of the expert
-      for (int ee = 0; ee < e; ++ee)
-        po += (s_mo[ee + 1] - s_mo[ee] + kMxRowPad - 1) / kMxRowPad * kMxRowPad;
-      asf_off = (uint32_t)(po + lr) * (uint32_t)kb_row;
-    }
-  }
-  // A fragment reads: row i*16 + r16, chunks c0/c1; same swizzle for every i
-  const int rd0 = a_lds_off(r16, kInt8 ? 2 * g : g);
-  const int rd1 = a_lds_off(r16, kInt8 ? 2 * g + 1 : g + 4);
-
-  // B: this wavefront's 64 columns, loaded straight into registers.
-  // Row-major: offset of the lane's 16-byte piece at k = 16g in its row.
-  // Tiled (moe_pack_weights): the wavefront's 64 columns are one packed tile;
-  // woff/woff2 are the lane's chunks g and g + 4 inside a 128-k block.
-  uint32_t woff[kTNF], woff2[kTNF];
-  uint32_t wsoff[kTNF];
-  uint32_t wblk = 0;
-  if constexpr (kTiled) {
-    const int T = (N + 63) / 64;
-    const int pt = min(n0 / 64 + wave, T - 1);
-    wblk = ((uint32_t)e * (uint32_t)T + (uint32_t)pt) * (uint32_t)((K + 127) / 128) * 8192u;
-  }
-#pragma unroll
-  for (int j = 0; j < kTNF; ++j) {
-    int col = n0 + wave * kTNW + j * 16 + r16;
-    col = col < N ? col : N - 1;
-    if constexpr (kTiled) {
-      const int r = j * 16 + r16;
-      woff[j] = (uint32_t)(r * 128 + ((g ^ swz(r)) << 4));
-      woff2[j] = (uint32_t)(r * 128 + (((g + 4) ^ swz(r)) << 4));
-    } else {
-      woff[j] = ((uint32_t)e * (uint32_t)N + (uint32_t)col) * (uint32_t)K + 16u * g;
-      woff2[j] = woff[j] + 64u;
-    }
-    wsoff[j] = ((uint32_t)e * (uint32_t)N + (uint32_t)col) * (uint32_t)kb_row;
-  }
-
-  f32x4 acc[kTMF][kTNF];
-#pragma unroll
-  for (int i = 0; i < kTMF; ++i)
-#pragma unroll
-    for (int j = 0; j < kTNF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nsteps = K / kStepK;
-  struct BRegs {
-    i32x4 v[kTNF][kBVec];
-    uint32_t sf[kTNF];
-  };
-  BRegs b0, b1;
-  i32x4 areg[4];
-  uint32_t asf_reg = 0;
-
-  auto load_a = [&](int s) {
-    const uint8_t *base = a + (size_t)s * kRowBytes;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) areg[q] = ld16(base + aoff[q]);
-    if constexpr (kMx) {
-      if (tid < kTBM) asf_reg = *reinterpret_cast<const uint32_t *>(a_sf + asf_off + 4 * s);
-    }
-  };
-  auto store_a = [&](uint8_t *lds, uint32_t *lds_sf) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) *reinterpret_cast<i32x4 *>(lds + adst + 4096 * q) = areg[q];
-    if constexpr (kMx) {
-      if (tid < kTBM) lds_sf[tid] = asf_reg;
-    }
-  };
-  auto load_b = [&](BRegs &bb, int s) {
-    if constexpr (kTiled) {
-      // fp8: step s is block s (chunks g, g + 4); int8: step s is half s & 1 of
-      // block s >> 1 (chunk g, then g + 4)
-      const uint8_t *base = w + wblk + (size_t)(kInt8 ? (s >> 1) : s) * 8192u;
-#pragma unroll
-      for (int j = 0; j < kTNF; ++j) {
-        if constexpr (kInt8) {
-          bb.v[j][0] = ld16(base + ((s & 1) ? woff2[j] : woff[j]));
-        } else {
-          bb.v[j][0] = ld16(base + woff[j]);
-          bb.v[j][kBVec - 1] = ld16(base + woff2[j]);
-        }
-      }
-    } else {
-      const uint8_t *base = w + (size_t)s * kStepK;
-#pragma unroll
-      for (int j = 0; j < kTNF; ++j) {
-#pragma unroll
-        for (int v = 0; v < kBVec; ++v) bb.v[j][v] = ld16(base + (v ? woff2[j] : woff[j]));
-        if constexpr (kMx) bb.sf[j] = *reinterpret_cast<const uint32_t *>(w_sf + wsoff[j] + 4 * s);
-      }
-    }
-  };
-  auto compute = [&](const BRegs &bb, const uint8_t *lds, const uint32_t *lds_sf) {
-    i32x4 bdq[kTNF][2];
-    if constexpr (kInt8) {
-#pragma unroll
-      for (int j = 0; j < kTNF; ++j) dequant16(bb.v[j][0], bdq[j][0], bdq[j][1]);
-    }
-#pragma unroll
-    for (int i = 0; i < kTMF; ++i) {
-      const i32x4 a0 = *reinterpret_cast<const i32x4 *>(lds + rd0 + i * 2048);
-      const i32x4 a1 = *reinterpret_cast<const i32x4 *>(lds + rd1 + i * 2048);
-      if constexpr (kInt8) {
-#pragma unroll
-        for (int j = 0; j < kTNF; ++j) {
-          acc[i][j] = mfma_bf16(a0, bdq[j][0], acc[i][j]);
-          acc[i][j] = mfma_bf16(a1, bdq[j][1], acc[i][j]);
-        }
-      } else {
-        const i32x8 av = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-        int sa_byte = 0;
-        if constexpr (kMx) sa_byte = (int)((lds_sf[i * 16 + r16] >> (8 * g)) & 0xFFu);
-#pragma unroll
-        for (int j = 0; j < kTNF; ++j) {
-          const i32x8 bv = __builtin_shufflevector(bb.v[j][0], bb.v[j][1], 0, 1, 2, 3, 4, 5, 6, 7);
-          if constexpr (kMx)
-            acc[i][j] = mfma_mx(av, bv, acc[i][j], sa_byte, (int)((bb.sf[j] >> (8 * g)) & 0xFFu));
-          else
-            acc[i][j] = mfma_fp8(av, bv, acc[i][j]);
-        }
-      }
-    }
-  };
-
-  uint8_t *lds0 = s_a[0];
-  uint8_t *lds1 = s_a[1];
-  uint32_t *sf0 = s_asf[0];
-  uint32_t *sf1 = s_asf[1];
-
-  // Two steps per iteration; the prefetch of the step after next is clamped to
-  // the last step (a repeated load at the very end), so the body has no
-  // branches and every wait count stays exact.
-  load_a(0);
-  load_b(b0, 0);
-  store_a(lds0, sf0);
-  __syncthreads();
-  int s = 0;
-  for (; s + 2 <= nsteps; s += 2) {
-    load_a(s + 1);
-    load_b(b1, s + 1);
-    __builtin_amdgcn_sched_barrier(0);                  // keep the prefetch ahead of the MFMAs
-    compute(b0, lds0, sf0);
-    store_a(lds1, sf1);
-    __syncthreads();
-    const int sp = (s + 2 < nsteps) ? s + 2 : nsteps - 1;
-    load_a(sp);
-    load_b(b0, sp);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(b1, lds1, sf1);
-    store_a(lds0, sf0);
-    __syncthreads();
-  }
-  if (s < nsteps) compute(b0, lds0, sf0);              // odd number of steps
-
-  // ---- epilogue --------------------------------------------------------------
-  float cscale = 1.0f;
-  if constexpr (kFmt == kFmtFp8) cscale = a_scale[0] * w_scale[e];
-#pragma unroll
-  for (int j = 0; j < kTNF; ++j) {
-    const int col = n0 + wave * kTNW + j * 16 + r16;
-    if (col >= N) continue;
-    float cs = cscale;
-    if constexpr (kInt8) cs = w_scale[(size_t)e * N + col];
-#pragma unroll
-    for (int i = 0; i < kTMF; ++i) {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int r = i * 16 + 4 * g + rr;
-        if constexpr (kMx) {
-          const int row = s_row[r];
-          if (row < row_end)
-            out[(size_t)row * N + col] = (uint16_t)(f32x2_to_bf16x2(acc[i][j][rr], 0.0f) & 0xFFFFu);
-        } else {
-          const int slot = s_row[r];
-          if (slot < S) y[(size_t)slot * N + col] = acc[i][j][rr] * cs * topk_w[slot];
-        }
-      }
-    }
-  }
-}
-
 // =============================================================================
-// block_m = 128, fp8 W8A8 and int8 W8A16: DMA-fed MFMA tiles
+// block_m = 128 (fp8 W8A8, int8 W8A16) and MXFP8: DMA-fed MFMA tiles
 // =============================================================================
 // One workgroup of 8 wavefronts (two per SIMD) per 128-row x 256-column
-// output tile of one expert; wavefront w owns the 64 x 64 quarter-of-a-half
-// (rows 64*(w & 1).., columns 64*(w >> 1)..) as 4 x 4 MFMA fragments.  Two
+// output tile of one expert; wavefront w owns the 64 x 64 block at rows
+// 64*(w & 1).., columns 64*(w >> 1).. as 4 x 4 MFMA fragments.  Two
 // wavefronts per SIMD let one issue MFMAs while the other waits for its LDS
-// reads.
+// reads.  Routed formats take the tile's rows from the sorted slots of one
+// routing block; MXFP8 from the expert's contiguous row segment.
 //
 // Every k-stage (128 k) of the tile's activation rows and weight columns is
 // copied HBM/L2 -> LDS by global_load_lds_dwordx4 (direct-to-LDS DMA, as in
@@ -766,8 +474,9 @@ __global__ __launch_bounds__(kThreads, 2) void tile_kernel(
 // stages ahead of the MFMAs, so loads in flight cost no registers and their
 // latency hides behind whole stages of compute.  The wavefront pair of a
 // 64-column block DMAs that block (8 KB per stage, one half each) and every
-// wavefront an eighth of the activation rows; before a stage is read each
-// wavefront waits for its own DMA and the workgroup synchronises.
+// wavefront an eighth of the activation rows; MXFP8 scale bytes of the stage
+// (4 per row and column) follow by global_load_lds_dword.  Before a stage is
+// read each wavefront waits for its own DMA and the workgroup synchronises.
 //
 // LDS layouts (16-byte chunks, XOR-swizzled so that the 16 rows one fragment
 // read touches hit distinct banks):
@@ -776,6 +485,10 @@ __global__ __launch_bounds__(kThreads, 2) void tile_kernel(
 //   weights, 64 rows of 128 bytes per column block: chunk c of row r at
 //   c ^ swz(r), the MOE_W_TILED block layout, so tiled weights are a plain
 //   8 KB copy and row-major weights are swizzled on the source side.
+//
+// The epilogue goes through LDS as well: each wavefront writes its scaled
+// 64 x 64 block there, then stores whole row segments (256 bytes of fp32 per
+// routed slot, 128 bytes of bf16 per MXFP8 row) with 16-byte stores.
 constexpr int kGBM = 128;
 constexpr int kGBN = 256;
 constexpr int kGThreads = 512;
@@ -790,20 +503,26 @@ struct GCfg {
   static constexpr int kAPerWave = kABytes / 1024 / 8;      // activation DMA instructions per wave
   static constexpr int kPerStage = kAPerWave + 4;           // DMA instructions per wave per stage
 };
+constexpr int kSfStage = 4 * kGBM + 4 * kGBN;                // MXFP8 scale bytes per stage
 
-template <bool kInt8, bool kTiled>
+template <int kFmt, bool kTiled>
 __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_scale,
-    const uint8_t *__restrict__ w, const float *__restrict__ w_scale,
+    const uint8_t *__restrict__ a_sf, const uint8_t *__restrict__ w,
+    const float *__restrict__ w_scale, const uint8_t *__restrict__ w_sf,
     const int *__restrict__ sorted_ids, const int *__restrict__ expert_ids,
-    const float *__restrict__ topk_w, int M, int K, int N, int E, int top_k, int max_blocks,
-    float *__restrict__ y) {
+    const float *__restrict__ topk_w, const int *__restrict__ m_offsets, int M, int K, int N,
+    int E, int top_k, int max_blocks, float *__restrict__ y, uint16_t *__restrict__ out) {
+  constexpr bool kInt8 = kFmt == kFmtInt8;
+  constexpr bool kMx = kFmt == kFmtMx;
   using C = GCfg<kInt8>;
   constexpr int kMF = 4, kNF = 4;                       // fragments per wavefront
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[C::kSlots * C::kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s_sf[kMx ? C::kSlots * kSfStage : 16];
   __shared__ int s_row[kGBM];
   __shared__ int s_blk_first[kMaxExperts + 1];
   __shared__ int s_tile_first[kMaxExperts + 1];
+  __shared__ int s_mo[kMx ? kMaxExperts + 1 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -813,14 +532,28 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(
 
   // ---- tile space: expert by expert, column tile by column tile, row block
   // fastest; each XCD takes one contiguous chunk of it
-  expert_block_starts(expert_ids, max_blocks, E, s_blk_first);
-  __syncthreads();
+  if constexpr (!kMx) {
+    expert_block_starts(expert_ids, max_blocks, E, s_blk_first);
+    __syncthreads();
+  }
   if (tid == 0) {
-    int tiles = 0;
+    int blk = 0, tiles = 0;
     for (int ee = 0; ee < E; ++ee) {
+      int nb;
+      if constexpr (kMx) {
+        s_mo[ee] = m_offsets[ee];
+        s_mo[ee + 1] = m_offsets[ee + 1];
+        const int m = s_mo[ee + 1] - s_mo[ee];
+        nb = m > 0 ? (m + kGBM - 1) / kGBM : 0;
+        s_blk_first[ee] = blk;
+        blk += nb;
+      } else {
+        nb = s_blk_first[ee + 1] - s_blk_first[ee];
+      }
       s_tile_first[ee] = tiles;
-      tiles += (s_blk_first[ee + 1] - s_blk_first[ee]) * ntn;
+      tiles += nb * ntn;
     }
+    if constexpr (kMx) s_blk_first[E] = blk;
     s_tile_first[E] = tiles;
   }
   __syncthreads();
@@ -837,9 +570,22 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(
   const int nt = local / nblk;
   const int mb = local - nt * nblk;
   const int n0 = nt * kGBN;
-  const int S = M * top_k;
-  if (tid < kGBM) s_row[tid] = sorted_ids[(s_blk_first[e] + mb) * kGBM + tid];
+  const int S = M * top_k;                              // routed: slots; MXFP8: unused
+  int row0 = 0, row_end = 0;                            // MXFP8: the tile's rows
+  if constexpr (kMx) {
+    row0 = s_mo[e] + mb * kGBM;
+    row_end = s_mo[e + 1];
+    if (tid < kGBM) s_row[tid] = row0 + tid;
+  } else {
+    if (tid < kGBM) s_row[tid] = sorted_ids[(s_blk_first[e] + mb) * kGBM + tid];
+  }
   __syncthreads();
+  // source row of tile row r (rows past the tile's end repeat a valid one)
+  auto src_row = [&](int r) -> uint32_t {
+    const int v = s_row[r];
+    if constexpr (kMx) return (uint32_t)(v < row_end ? v : row_end - 1);
+    else return (uint32_t)(v < S ? v / top_k : 0);
+  };
 
   // ---- DMA sources of this lane ----------------------------------------------
   const uint32_t lds_ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)s_ring;
@@ -860,8 +606,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(
       r = 8 * q + (lane >> 3);
       c = (lane & 7) ^ swz(r);
     }
-    const int slot = s_row[r];
-    a_row[u] = (uint32_t)(slot < S ? slot / top_k : 0) * a_row_bytes;
+    a_row[u] = src_row(r) * a_row_bytes;
     a_chk[u] = 16u * (uint32_t)c;
   }
   // weights: rows 32*wm .. 32*wm + 31 of column block wn (4 instructions)
@@ -880,6 +625,22 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(
       b_chk[u] = 16u * (uint32_t)((lane & 7) ^ swz(n));
     }
   }
+  // MXFP8 scales: wavefronts 0-1 move the 4 scale bytes of rows 64w + lane,
+  // wavefronts 2-5 those of columns 64(w-2) + lane (one dword DMA each)
+  const uint32_t kb_row = (uint32_t)K / 32u;            // scale bytes per row
+  uint32_t sf_off = 0;
+  const int sfn = (kMx && wave < 6) ? 1 : 0;            // scale DMAs of this wave per stage
+  if constexpr (kMx) {
+    if (wave < 2) {
+      int po = 0;                                       // the expert's padded scale rows
+      for (int ee = 0; ee < e; ++ee) po += (s_mo[ee + 1] - s_mo[ee] + kMxRowPad - 1) / kMxRowPad * kMxRowPad;
+      sf_off = ((uint32_t)po + src_row(64 * wave + lane) - (uint32_t)s_mo[e]) * kb_row;
+    } else if (wave < 6) {
+      const int col = min(n0 + 64 * (wave - 2) + lane, N - 1);
+      sf_off = ((uint32_t)e * (uint32_t)N + (uint32_t)col) * kb_row;
+    }
+  }
+  const uint32_t lds_sf = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)s_sf;
 
   auto issue = [&](int st, int slot_i) {
     const uint32_t base = lds_ring + (uint32_t)(slot_i * C::kStage);
@@ -903,6 +664,11 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         dma16(bbase, b_row[u] + min(b_chk[u], kmax), bdst + (uint32_t)(u * 1024));
+    }
+    if constexpr (kMx) {
+      const uint32_t sdst = lds_sf + (uint32_t)(slot_i * kSfStage);
+      if (wave < 2) dma4(a_sf + 4 * st, sf_off, sdst + (uint32_t)(256 * wave));
+      else if (wave < 6) dma4(w_sf + 4 * st, sf_off, sdst + (uint32_t)(4 * kGBM + 256 * (wave - 2)));
     }
   };
 
@@ -954,15 +720,32 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(
         av[i] = __builtin_shufflevector(ld16(ar + ((g ^ sw) << 4)), ld16(ar + (((g + 4) ^ sw) << 4)),
                                         0, 1, 2, 3, 4, 5, 6, 7);
       }
+      if constexpr (kMx) {
+        // lane (g, r16) supplies the scale of 32-k block g of its row / column
+        const uint8_t *sfs = s_sf + slot_i * kSfStage;
+        int sa[kMF], sb[kNF];
 #pragma unroll
-      for (int i = 0; i < kMF; ++i)
+        for (int i = 0; i < kMF; ++i)
+          sa[i] = (int)((*reinterpret_cast<const uint32_t *>(sfs + 4 * (wm * 64 + i * 16 + r16)) >> (8 * g)) & 0xFFu);
 #pragma unroll
-        for (int j = 0; j < kNF; ++j) acc[i][j] = mfma_fp8(av[i], bv[j], acc[i][j]);
+        for (int j = 0; j < kNF; ++j)
+          sb[j] = (int)((*reinterpret_cast<const uint32_t *>(sfs + 4 * kGBM + 4 * (wn * 64 + j * 16 + r16)) >> (8 * g)) & 0xFFu);
+#pragma unroll
+        for (int i = 0; i < kMF; ++i)
+#pragma unroll
+          for (int j = 0; j < kNF; ++j) acc[i][j] = mfma_mx(av[i], bv[j], acc[i][j], sa[i], sb[j]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < kMF; ++i)
+#pragma unroll
+          for (int j = 0; j < kNF; ++j) acc[i][j] = mfma_fp8(av[i], bv[j], acc[i][j]);
+      }
     }
   };
 
   // ---- the ring: stage st lives in slot st % kSlots --------------------------
   constexpr int D = C::kSlots - 1;                      // stages in flight ahead of compute
+  const int per_stage = C::kPerStage + sfn;             // this wave's DMAs per stage
 #pragma unroll
   for (int st = 0; st < D; ++st)
     if (st < nst) issue(st, st);
@@ -972,8 +755,8 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(
   for (int st = 0; st < nst; ++st) {
     // stages st .. min(st + D - 1, nst - 1) are in flight: wait for stage st
     // (loads complete in order, so waiting for stage st leaves the later
-    // stage's kPerStage DMAs in flight)
-    if (D == 2 && st + 1 < nst) wait_dma_upto(C::kPerStage);
+    // stage's DMAs in flight)
+    if (D == 2 && st + 1 < nst) wait_dma_upto(per_stage);
     else wait_dma_all();
     __syncthreads();                                    // stage st complete; slot_i is free
     if (st + D < nst) issue(st + D, slot_i);
@@ -982,21 +765,72 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(
     slot_i = slot_i + 1 == C::kSlots ? 0 : slot_i + 1;
   }
 
-  // ---- epilogue ------------------------------------------------------------
+  // ---- epilogue: scaled results -> LDS (the ring is free) -> row segments ----
+  __syncthreads();                                      // every wavefront is done with the ring
   float cscale = 1.0f;
-  if constexpr (!kInt8) cscale = a_scale[0] * w_scale[e];
+  if constexpr (kFmt == kFmtFp8) cscale = a_scale[0] * w_scale[e];
+  if constexpr (kMx) {
+    // bf16 [64 rows][64 columns] per wavefront, 128 bytes per row
+    uint16_t *t = reinterpret_cast<uint16_t *>(s_ring) + wave * 64 * 64;
 #pragma unroll
-  for (int j = 0; j < kNF; ++j) {
-    const int col = n0 + wn * 64 + j * 16 + r16;
-    if (col >= N) continue;
-    float cs = cscale;
-    if constexpr (kInt8) cs = w_scale[(size_t)e * N + col];
+    for (int j = 0; j < kNF; ++j)
 #pragma unroll
-    for (int i = 0; i < kMF; ++i) {
+      for (int i = 0; i < kMF; ++i)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int slot = s_row[wm * 64 + i * 16 + 4 * g + rr];
-        if (slot < S) y[(size_t)slot * N + col] = acc[i][j][rr] * cs * topk_w[slot];
+        for (int rr = 0; rr < 4; ++rr)
+          t[(i * 16 + 4 * g + rr) * 64 + j * 16 + r16] =
+              (uint16_t)(f32x2_to_bf16x2(acc[i][j][rr], 0.0f) & 0xFFFFu);
+    __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0): the wave's LDS writes done
+    __builtin_amdgcn_wave_barrier();
+    const bool vec = (N & 7) == 0 && ((uintptr_t)out & 15u) == 0;   // 16-byte aligned row segments
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int r = q * 8 + (lane >> 3);                // row within the wavefront's block
+      const int row = row0 + wm * 64 + r;
+      const int col = n0 + wn * 64 + (lane & 7) * 8;
+      if (row >= row_end || col >= N) continue;
+      const uint16_t *src = t + r * 64 + (lane & 7) * 8;
+      uint16_t *dst = out + (size_t)row * N + col;
+      if (vec && col + 8 <= N) {
+        *reinterpret_cast<i32x4 *>(dst) = *reinterpret_cast<const i32x4 *>(src);
+      } else {
+        for (int c = 0; c < 8 && col + c < N; ++c) dst[c] = src[c];
+      }
+    }
+  } else {
+    // fp32 [64 rows][64 columns] per wavefront (scale and router weight
+    // applied), 256 bytes per row
+    float *t = reinterpret_cast<float *>(s_ring) + wave * 64 * 64;
+#pragma unroll
+    for (int j = 0; j < kNF; ++j) {
+      const int col = min(n0 + wn * 64 + j * 16 + r16, N - 1);
+      float cs = cscale;
+      if constexpr (kInt8) cs = w_scale[(size_t)e * N + col];
+#pragma unroll
+      for (int i = 0; i < kMF; ++i)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int r = i * 16 + 4 * g + rr;
+          const int slot = s_row[wm * 64 + r];
+          const float tw = slot < S ? topk_w[slot] : 0.0f;
+          t[r * 64 + j * 16 + r16] = acc[i][j][rr] * cs * tw;
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0): the wave's LDS writes done
+    __builtin_amdgcn_wave_barrier();
+    const bool vec = (N & 3) == 0 && ((uintptr_t)y & 15u) == 0;     // 16-byte aligned row segments
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int r = q * 4 + (lane >> 4);
+      const int slot = s_row[wm * 64 + r];
+      const int col = n0 + wn * 64 + (lane & 15) * 4;
+      if (slot >= S || col >= N) continue;
+      const float *src = t + r * 64 + (lane & 15) * 4;
+      float *dst = y + (size_t)slot * N + col;
+      if (vec && col + 4 <= N) {
+        *reinterpret_cast<f32x4 *>(dst) = *reinterpret_cast<const f32x4 *>(src);
+      } else {
+        for (int c = 0; c < 4 && col + c < N; ++c) dst[c] = src[c];
       }
     }
   }
@@ -1044,10 +878,10 @@ hipError_t launch_gemm_fp8(const uint8_t *a_q, const float *a_scale, const uint8
                        groups, tpg, r.max_blocks, r.y);
   } else {
     const long long tiles = (long long)r.max_blocks * ((r.N + kGBN - 1) / kGBN);
-    auto k = r.w_layout ? gemm_kernel<false, true> : gemm_kernel<false, false>;
-    hipLaunchKernelGGL(k, dim3(tile_grid(tiles)), dim3(kGThreads), 0, s, a_q, a_scale, w_q, w_scale,
-                       r.sorted_ids, r.expert_ids, r.topk_w, r.M, r.K, r.N, r.E, r.top_k,
-                       r.max_blocks, r.y);
+    auto k = r.w_layout ? gemm_kernel<kFmtFp8, true> : gemm_kernel<kFmtFp8, false>;
+    hipLaunchKernelGGL(k, dim3(tile_grid(tiles)), dim3(kGThreads), 0, s, a_q, a_scale, nullptr, w_q,
+                       w_scale, nullptr, r.sorted_ids, r.expert_ids, r.topk_w, nullptr, r.M, r.K,
+                       r.N, r.E, r.top_k, r.max_blocks, r.y, nullptr);
   }
   return hipGetLastError();
 }
@@ -1065,10 +899,10 @@ hipError_t launch_gemm_int8(const uint16_t *a, const int8_t *w_q, const float *w
                        groups, tpg, r.max_blocks, r.y);
   } else {
     const long long tiles = (long long)r.max_blocks * ((r.N + kGBN - 1) / kGBN);
-    auto k = r.w_layout ? gemm_kernel<true, true> : gemm_kernel<true, false>;
-    hipLaunchKernelGGL(k, dim3(tile_grid(tiles)), dim3(kGThreads), 0, s, ab, nullptr, wb, w_scale,
-                       r.sorted_ids, r.expert_ids, r.topk_w, r.M, r.K, r.N, r.E, r.top_k,
-                       r.max_blocks, r.y);
+    auto k = r.w_layout ? gemm_kernel<kFmtInt8, true> : gemm_kernel<kFmtInt8, false>;
+    hipLaunchKernelGGL(k, dim3(tile_grid(tiles)), dim3(kGThreads), 0, s, ab, nullptr, nullptr, wb,
+                       w_scale, nullptr, r.sorted_ids, r.expert_ids, r.topk_w, nullptr, r.M, r.K,
+                       r.N, r.E, r.top_k, r.max_blocks, r.y, nullptr);
   }
   return hipGetLastError();
 }
@@ -1076,11 +910,11 @@ hipError_t launch_gemm_int8(const uint16_t *a, const int8_t *w_q, const float *w
 hipError_t launch_gemm_mxfp8(const uint8_t *a_q, const uint8_t *a_sf, const uint8_t *w_q,
                              const uint8_t *w_sf, const int *m_offsets, int rows, int K, int N,
                              int E, uint16_t *out, hipStream_t s) {
-  const long long blocks = (rows + kTBM - 1) / kTBM + E;
-  const long long tiles = blocks * ((N + kTBN - 1) / kTBN);
-  hipLaunchKernelGGL((tile_kernel<kFmtMx, false>), dim3(tile_grid(tiles)), dim3(kThreads), 0, s, a_q,
-                     nullptr, a_sf, w_q, nullptr, w_sf, nullptr, nullptr, nullptr, nullptr,
-                     m_offsets, rows, K, N, E, 1, 0, nullptr, out);
+  const long long blocks = (rows + kGBM - 1) / kGBM + E;
+  const long long tiles = blocks * ((N + kGBN - 1) / kGBN);
+  hipLaunchKernelGGL((gemm_kernel<kFmtMx, false>), dim3(tile_grid(tiles)), dim3(kGThreads), 0, s,
+                     a_q, nullptr, a_sf, w_q, nullptr, w_sf, nullptr, nullptr, nullptr, m_offsets,
+                     rows, K, N, E, 1, 0, nullptr, out);
   return hipGetLastError();
 }
 

@@ -144,7 +144,7 @@ def cpu_baseline(wl, case, target_s):
                 y = O.grouped_gemm_fp8w8a8(aq, sa, wq, ws, ids, wts)
             else:
                 y = O.grouped_gemm_int8w8a16(x, wq, ws, ids, wts)
-            O.combine(y, wl.top_k)
+            O.combine(F.bf16_decode(O.slot_results_bf16(y)), wl.top_k)
         reps += 1
         el = time.perf_counter() - t0
         if el >= target_s:

@@ -205,36 +205,41 @@ int moe_pack_weights(const void *w_q, int E, int N, int K, void *w_packed, hipSt
 /* Routed fp8 W8A8 grouped GEMM.  For every sorted slot i of expert e (from
  * moe_align_block_size run with the same M, E, top_k, block_m), token
  * t = i / top_k, and every column n < N:
- *     y[i, n] = (sum_k a[t,k] * w[e,n,k]) * (a_scale[0] * w_scale[e]) * topk_weights[i]
- * with e4m3 operands, fp32 accumulation, and padding slots skipped.
+ *     y[i, n] = bf16( (sum_k a[t,k] * w[e,n,k]) * (a_scale[0] * w_scale[e]) * topk_weights[i] )
+ * with e4m3 operands, fp32 accumulation, rounding to nearest even, and
+ * padding slots skipped.  The per-slot results are stored as bf16, two bytes
+ * per slot and column as in the output term of the byte accounting behind the
+ * FP8_W8A8 / INT8_W8A16 benchmark tables ("Tianxing/moe quantization").
  *
  *   a_q [M, K] uint8 e4m3, a_scale [1] f32, w_q e4m3 weights in layout
  *   w_layout (MOE_W_ROWMAJOR [E, N, K] or MOE_W_TILED), w_scale [E] f32,
  *   topk_weights [M*top_k] f32, routing buffers as written by
- *   moe_align_block_size, y [M*top_k, N] f32 (rows of slots that are not
- *   routed are not written; with every slot routed, y is written in full).
+ *   moe_align_block_size, y [M*top_k, N] uint16 bf16, 16-byte aligned (rows
+ *   of slots that are not routed are not written; with every slot routed, y
+ *   is written in full).
  *
- * K must be a multiple of 128; block_m must be 16 or 128.  block_m 16 runs the
- * weight-streaming kernel (fastest with MOE_W_TILED), 128 the tiled one. */
+ * K must be a multiple of 128 and N of 8; block_m must be 16 or 128.
+ * block_m 16 runs the weight-streaming kernel (fastest with MOE_W_TILED), 128
+ * the tiled one. */
 int moe_grouped_gemm_fp8w8a8(const uint8_t *a_q, const float *a_scale,
                              const uint8_t *w_q, const float *w_scale, int w_layout,
                              const int *sorted_token_ids, const int *expert_ids,
                              const int *num_tokens_post_padded,
                              const float *topk_weights, int M, int K, int N, int E,
-                             int top_k, int block_m, float *y, hipStream_t stream);
+                             int top_k, int block_m, uint16_t *y, hipStream_t stream);
 
 /* Routed int8 W8A16 grouped GEMM: as moe_grouped_gemm_fp8w8a8 with
- *     y[i, n] = (sum_k a[t,k] * w[e,n,k]) * w_scale[e, n] * topk_weights[i]
+ *     y[i, n] = bf16( (sum_k a[t,k] * w[e,n,k]) * w_scale[e, n] * topk_weights[i] )
  * for bf16 a [M, K] (uint16 bits), int8 w_q in layout w_layout, w_scale
  * [E, N] f32.  The int8 weights are converted exactly to bf16 inside the
  * kernel and the products are accumulated in fp32.  K must be a multiple of
- * 64; block_m must be 16 or 128. */
+ * 64 and N of 8; block_m must be 16 or 128. */
 int moe_grouped_gemm_int8w8a16(const uint16_t *a, const int8_t *w_q,
                                const float *w_scale, int w_layout,
                                const int *sorted_token_ids, const int *expert_ids,
                                const int *num_tokens_post_padded,
                                const float *topk_weights, int M, int K, int N, int E,
-                               int top_k, int block_m, float *y, hipStream_t stream);
+                               int top_k, int block_m, uint16_t *y, hipStream_t stream);
 
 /* MXFP8 grouped linear over expert-contiguous rows (no router): for row r of
  * expert e (m_offsets[e] <= r < m_offsets[e+1]) and column n < N,
@@ -258,10 +263,10 @@ int moe_grouped_gemm_mxfp8(const uint8_t *a_q, const uint8_t *a_sf,
  * ======================================================================== */
 
 /* Per-token combine: out[t, n] = bf16( y[t*top_k, n] + ... + y[t*top_k+top_k-1, n] )
- * with the adds done in float32 in slot order and the sum rounded to nearest
- * even.  y [M*top_k, N] f32, out [M, N] uint16 bf16.  N must be a multiple
- * of 4. */
-int moe_combine(const float *y, int M, int N, int top_k, uint16_t *out,
+ * over the bf16 per-slot results, with the adds done in float32 in slot order
+ * and the sum rounded to nearest even.  y [M*top_k, N] uint16 bf16, out
+ * [M, N] uint16 bf16, both 16-byte aligned.  N must be a multiple of 8. */
+int moe_combine(const uint16_t *y, int M, int N, int top_k, uint16_t *out,
                 hipStream_t stream);
 
 #ifdef __cplusplus

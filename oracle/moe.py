@@ -316,6 +316,16 @@ def grouped_gemm_mxfp8(a_q, a_sf, w_q, w_sf, m_offsets, rows=None, cols=None):
 # ----------------------------------------------------------------------------
 # combine
 # ----------------------------------------------------------------------------
+def slot_results_bf16(y):
+    """The per-slot results as the hot path stores them between the grouped
+    GEMM and the combine: bf16 bits (round to nearest even) of the float32
+    values.  Two bytes per routed slot and output column is what the byte
+    accounting behind the Bandwidth column of the FP8_W8A8 and INT8_W8A16
+    benchmark tables ("Tianxing/moe quantization") charges for the output
+    (M * top_k * N * 2).  y float32 [M*top_k, N] -> uint16 [M*top_k, N]."""
+    return bf16_round(_f32(y))
+
+
 def combine(y, top_k):
     """Per-token sum of the top_k slot results, in slot order, in float32, then
     rounded to bf16.  y float32 [M*top_k, N] -> (out32 float32 [M, N],

@@ -61,7 +61,7 @@ long long max_padded_ll(int M, int E, int top_k, int block_m) {
 
 int check_routed_gemm(const void *a, const void *w, const void *w_scale, int w_layout,
                       const int *sorted, const int *expert_ids, const int *num_post,
-                      const float *topk_w, const float *y, int M, int K, int N, int E, int top_k,
+                      const float *topk_w, const uint16_t *y, int M, int K, int N, int E, int top_k,
                       int block_m, int k_mult, const char *fn) {
   int rc = check_routing_sizes(M, E, top_k, fn);
   if (rc) return rc;
@@ -69,13 +69,14 @@ int check_routed_gemm(const void *a, const void *w, const void *w_scale, int w_l
           "%s: unknown weight layout %d", fn, w_layout);
   REQUIRE(K > 0 && N > 0, MOE_EINVAL, "%s: K=%d and N=%d must be positive", fn, K, N);
   REQUIRE(K % k_mult == 0, MOE_EUNSUPPORTED, "%s: K=%d is not a multiple of %d", fn, K, k_mult);
+  REQUIRE(N % 8 == 0, MOE_EUNSUPPORTED, "%s: N=%d is not a multiple of 8", fn, N);
   REQUIRE(block_m == 16 || block_m == 128, MOE_EUNSUPPORTED,
           "%s: block_m=%d (supported: 16, 128)", fn, block_m);
   if (M == 0) return MOE_OK;               // nothing to do; buffers may be empty
   REQUIRE(a && w && w_scale && sorted && expert_ids && num_post && topk_w && y, MOE_EINVAL,
           "%s: null pointer argument", fn);
-  REQUIRE(aligned16(a) && aligned16(w), MOE_EINVAL,
-          "%s: activation and weight pointers must be 16-byte aligned", fn);
+  REQUIRE(aligned16(a) && aligned16(w) && aligned16(y), MOE_EINVAL,
+          "%s: activation, weight and output pointers must be 16-byte aligned", fn);
   REQUIRE((long long)E * N * (long long)K < (1ll << 32) &&
               moe_packed_weight_bytes(E, N, K) < (1ull << 32),
           MOE_EUNSUPPORTED, "%s: weight tensor must stay below 4 GiB", fn);
@@ -223,7 +224,7 @@ int moe_grouped_gemm_fp8w8a8(const uint8_t *a_q, const float *a_scale, const uin
                              const float *w_scale, int w_layout, const int *sorted_token_ids,
                              const int *expert_ids, const int *num_tokens_post_padded,
                              const float *topk_weights, int M, int K, int N, int E, int top_k,
-                             int block_m, float *y, hipStream_t stream) {
+                             int block_m, uint16_t *y, hipStream_t stream) {
   const char *fn = "moe_grouped_gemm_fp8w8a8";
   int rc = check_routed_gemm(a_q, w_q, w_scale, w_layout, sorted_token_ids, expert_ids,
                              num_tokens_post_padded, topk_weights, y, M, K, N, E, top_k, block_m,
@@ -240,7 +241,7 @@ int moe_grouped_gemm_fp8w8a8(const uint8_t *a_q, const float *a_scale, const uin
 int moe_grouped_gemm_int8w8a16(const uint16_t *a, const int8_t *w_q, const float *w_scale,
                                int w_layout, const int *sorted_token_ids, const int *expert_ids,
                                const int *num_tokens_post_padded, const float *topk_weights,
-                               int M, int K, int N, int E, int top_k, int block_m, float *y,
+                               int M, int K, int N, int E, int top_k, int block_m, uint16_t *y,
                                hipStream_t stream) {
   const char *fn = "moe_grouped_gemm_int8w8a16";
   int rc = check_routed_gemm(a, w_q, w_scale, w_layout, sorted_token_ids, expert_ids,
@@ -270,15 +271,14 @@ int moe_grouped_gemm_mxfp8(const uint8_t *a_q, const uint8_t *a_sf, const uint8_
       qmoe::launch_gemm_mxfp8(a_q, a_sf, w_q, w_sf, m_offsets, rows, K, N, E, out, stream), fn);
 }
 
-int moe_combine(const float *y, int M, int N, int top_k, uint16_t *out, hipStream_t stream) {
+int moe_combine(const uint16_t *y, int M, int N, int top_k, uint16_t *out, hipStream_t stream) {
   const char *fn = "moe_combine";
   REQUIRE(M >= 0 && N > 0 && top_k >= 1 && top_k <= MOE_MAX_TOPK, MOE_EINVAL,
           "%s: M=%d N=%d top_k=%d", fn, M, N, top_k);
-  REQUIRE(N % 4 == 0, MOE_EUNSUPPORTED, "%s: N=%d is not a multiple of 4", fn, N);
+  REQUIRE(N % 8 == 0, MOE_EUNSUPPORTED, "%s: N=%d is not a multiple of 8", fn, N);
   if (M == 0) return ok();
   REQUIRE(y && out, MOE_EINVAL, "%s: null pointer argument", fn);
-  REQUIRE(aligned16(y) && ((uintptr_t)out & 7u) == 0, MOE_EINVAL,
-          "%s: y must be 16-byte and out 8-byte aligned", fn);
+  REQUIRE(aligned16(y) && aligned16(out), MOE_EINVAL, "%s: y and out must be 16-byte aligned", fn);
   return hip_status(qmoe::launch_combine(y, M, N, top_k, out, stream), fn);
 }
 

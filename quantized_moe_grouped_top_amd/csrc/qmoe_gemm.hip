@@ -191,7 +191,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
     const uint8_t *__restrict__ w, const float *__restrict__ w_scale,
     const int *__restrict__ sorted_ids, const int *__restrict__ expert_ids,
     const int *__restrict__ num_post, const float *__restrict__ topk_w, int M, int K, int N,
-    int top_k, int groups, int tiles_per_group, int max_blocks, float *__restrict__ y) {
+    int top_k, int groups, int tiles_per_group, int max_blocks, uint16_t *__restrict__ y) {
   using C = SCfg<kInt8>;
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[2 * C::kStage];
   __shared__ int s_slot[kSMB * 16];
@@ -426,7 +426,8 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
       compute(st);
     }
 
-    // ---- epilogue: scale x router weight, one store per output element ----
+    // ---- epilogue: scale x router weight, rounded to bf16; lane pairs
+    // (adjacent columns) combine into one 4-byte store
     if (pass_ == 0) {
       // per-column scale of this workgroup's tiles (int8) or the fused scalar
       for (int c = tid; c < G * 64; c += kSThreads) {
@@ -438,18 +439,22 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int tl = par + 2 * t;
-      if (tl >= G) break;
+      if (tl >= G) break;                              // wave-uniform
       const int col = (t_begin + tl) * 64 + 16 * frag + r16;
-      if (col >= N) continue;
       const float cs = s_scale[tl * 64 + 16 * frag + r16];
 #pragma unroll
       for (int i = 0; i < kSMB; ++i) {
-        if (i >= nmb) break;
+        if (i >= nmb) break;                           // wave-uniform
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int k = 16 * i + 4 * g + rr;
           const int slot = s_slot[k];
-          if (slot < S) y[(size_t)slot * N + col] = acc[t][i][rr] * cs * s_topk[k];
+          const float v = acc[t][i][rr] * cs * s_topk[k];
+          const float vn = __shfl_xor(v, 1);           // the next column's value
+          // N is a multiple of 8: an even column and its neighbour are both
+          // inside the row or both past its end
+          if (slot < S && (r16 & 1) == 0 && col < N)
+            *reinterpret_cast<uint32_t *>(y + (size_t)slot * N + col) = f32x2_to_bf16x2(v, vn);
         }
       }
     }
@@ -512,7 +517,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(
     const float *__restrict__ w_scale, const uint8_t *__restrict__ w_sf,
     const int *__restrict__ sorted_ids, const int *__restrict__ expert_ids,
     const float *__restrict__ topk_w, const int *__restrict__ m_offsets, int M, int K, int N,
-    int E, int top_k, int max_blocks, float *__restrict__ y, uint16_t *__restrict__ out) {
+    int E, int top_k, int max_blocks, uint16_t *__restrict__ out) {
   constexpr bool kInt8 = kFmt == kFmtInt8;
   constexpr bool kMx = kFmt == kFmtMx;
   using C = GCfg<kInt8>;
@@ -765,73 +770,52 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(
     slot_i = slot_i + 1 == C::kSlots ? 0 : slot_i + 1;
   }
 
-  // ---- epilogue: scaled results -> LDS (the ring is free) -> row segments ----
+  // ---- epilogue: results (routed: scaled by the format's scales and the
+  // router weight) as bf16 -> LDS (the ring is free) -> 128-byte row segments
+  // of the destination rows (routed: the slots; MXFP8: the expert's rows)
   __syncthreads();                                      // every wavefront is done with the ring
   float cscale = 1.0f;
   if constexpr (kFmt == kFmtFp8) cscale = a_scale[0] * w_scale[e];
-  if constexpr (kMx) {
-    // bf16 [64 rows][64 columns] per wavefront, 128 bytes per row
-    uint16_t *t = reinterpret_cast<uint16_t *>(s_ring) + wave * 64 * 64;
+  uint16_t *t = reinterpret_cast<uint16_t *>(s_ring) + wave * 64 * 64;   // [64 rows][64 columns]
 #pragma unroll
-    for (int j = 0; j < kNF; ++j)
+  for (int j = 0; j < kNF; ++j) {
+    float cs = cscale;
+    if constexpr (kInt8) cs = w_scale[(size_t)e * N + min(n0 + wn * 64 + j * 16 + r16, N - 1)];
 #pragma unroll
-      for (int i = 0; i < kMF; ++i)
+    for (int i = 0; i < kMF; ++i)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          t[(i * 16 + 4 * g + rr) * 64 + j * 16 + r16] =
-              (uint16_t)(f32x2_to_bf16x2(acc[i][j][rr], 0.0f) & 0xFFFFu);
-    __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0): the wave's LDS writes done
-    __builtin_amdgcn_wave_barrier();
-    const bool vec = (N & 7) == 0 && ((uintptr_t)out & 15u) == 0;   // 16-byte aligned row segments
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int r = q * 8 + (lane >> 3);                // row within the wavefront's block
-      const int row = row0 + wm * 64 + r;
-      const int col = n0 + wn * 64 + (lane & 7) * 8;
-      if (row >= row_end || col >= N) continue;
-      const uint16_t *src = t + r * 64 + (lane & 7) * 8;
-      uint16_t *dst = out + (size_t)row * N + col;
-      if (vec && col + 8 <= N) {
-        *reinterpret_cast<i32x4 *>(dst) = *reinterpret_cast<const i32x4 *>(src);
-      } else {
-        for (int c = 0; c < 8 && col + c < N; ++c) dst[c] = src[c];
-      }
-    }
-  } else {
-    // fp32 [64 rows][64 columns] per wavefront (scale and router weight
-    // applied), 256 bytes per row
-    float *t = reinterpret_cast<float *>(s_ring) + wave * 64 * 64;
-#pragma unroll
-    for (int j = 0; j < kNF; ++j) {
-      const int col = min(n0 + wn * 64 + j * 16 + r16, N - 1);
-      float cs = cscale;
-      if constexpr (kInt8) cs = w_scale[(size_t)e * N + col];
-#pragma unroll
-      for (int i = 0; i < kMF; ++i)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int r = i * 16 + 4 * g + rr;
+      for (int rr = 0; rr < 4; ++rr) {
+        const int r = i * 16 + 4 * g + rr;
+        float v = acc[i][j][rr];
+        if constexpr (!kMx) {
           const int slot = s_row[wm * 64 + r];
-          const float tw = slot < S ? topk_w[slot] : 0.0f;
-          t[r * 64 + j * 16 + r16] = acc[i][j][rr] * cs * tw;
+          v = v * cs * (slot < S ? topk_w[slot] : 0.0f);
         }
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0): the wave's LDS writes done
-    __builtin_amdgcn_wave_barrier();
-    const bool vec = (N & 3) == 0 && ((uintptr_t)y & 15u) == 0;     // 16-byte aligned row segments
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int r = q * 4 + (lane >> 4);
-      const int slot = s_row[wm * 64 + r];
-      const int col = n0 + wn * 64 + (lane & 15) * 4;
-      if (slot >= S || col >= N) continue;
-      const float *src = t + r * 64 + (lane & 15) * 4;
-      float *dst = y + (size_t)slot * N + col;
-      if (vec && col + 4 <= N) {
-        *reinterpret_cast<f32x4 *>(dst) = *reinterpret_cast<const f32x4 *>(src);
-      } else {
-        for (int c = 0; c < 4 && col + c < N; ++c) dst[c] = src[c];
+        t[r * 64 + j * 16 + r16] = (uint16_t)(f32x2_to_bf16x2(v, 0.0f) & 0xFFFFu);
       }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);                   // lgkmcnt(0): the wave's LDS writes done
+  __builtin_amdgcn_wave_barrier();
+  const bool vec = (N & 7) == 0 && ((uintptr_t)out & 15u) == 0;   // 16-byte aligned segments
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int r = q * 8 + (lane >> 3);                  // row within the wavefront's block
+    const int col = n0 + wn * 64 + (lane & 7) * 8;
+    int dst_row;
+    if constexpr (kMx) {
+      dst_row = row0 + wm * 64 + r;
+      if (dst_row >= row_end) continue;
+    } else {
+      dst_row = s_row[wm * 64 + r];
+      if (dst_row >= S) continue;
+    }
+    if (col >= N) continue;
+    const uint16_t *src = t + r * 64 + (lane & 7) * 8;
+    uint16_t *dst = out + (size_t)dst_row * N + col;
+    if (vec && col + 8 <= N) {
+      *reinterpret_cast<i32x4 *>(dst) = *reinterpret_cast<const i32x4 *>(src);
+    } else {
+      for (int c = 0; c < 8 && col + c < N; ++c) dst[c] = src[c];
     }
   }
 }
@@ -881,7 +865,7 @@ hipError_t launch_gemm_fp8(const uint8_t *a_q, const float *a_scale, const uint8
     auto k = r.w_layout ? gemm_kernel<kFmtFp8, true> : gemm_kernel<kFmtFp8, false>;
     hipLaunchKernelGGL(k, dim3(tile_grid(tiles)), dim3(kGThreads), 0, s, a_q, a_scale, nullptr, w_q,
                        w_scale, nullptr, r.sorted_ids, r.expert_ids, r.topk_w, nullptr, r.M, r.K,
-                       r.N, r.E, r.top_k, r.max_blocks, r.y, nullptr);
+                       r.N, r.E, r.top_k, r.max_blocks, r.y);
   }
   return hipGetLastError();
 }
@@ -902,7 +886,7 @@ hipError_t launch_gemm_int8(const uint16_t *a, const int8_t *w_q, const float *w
     auto k = r.w_layout ? gemm_kernel<kFmtInt8, true> : gemm_kernel<kFmtInt8, false>;
     hipLaunchKernelGGL(k, dim3(tile_grid(tiles)), dim3(kGThreads), 0, s, ab, nullptr, nullptr, wb,
                        w_scale, nullptr, r.sorted_ids, r.expert_ids, r.topk_w, nullptr, r.M, r.K,
-                       r.N, r.E, r.top_k, r.max_blocks, r.y, nullptr);
+                       r.N, r.E, r.top_k, r.max_blocks, r.y);
   }
   return hipGetLastError();
 }
@@ -914,7 +898,7 @@ hipError_t launch_gemm_mxfp8(const uint8_t *a_q, const uint8_t *a_sf, const uint
   const long long tiles = blocks * ((N + kGBN - 1) / kGBN);
   hipLaunchKernelGGL((gemm_kernel<kFmtMx, false>), dim3(tile_grid(tiles)), dim3(kGThreads), 0, s,
                      a_q, nullptr, a_sf, w_q, nullptr, w_sf, nullptr, nullptr, nullptr, m_offsets,
-                     rows, K, N, E, 1, 0, nullptr, out);
+                     rows, K, N, E, 1, 0, out);
   return hipGetLastError();
 }
 

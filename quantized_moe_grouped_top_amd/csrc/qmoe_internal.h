@@ -75,7 +75,7 @@ struct RoutedArgs {
   const float *topk_w;
   int M, K, N, E, top_k, block_m, max_blocks;
   int w_layout;                        // 0 row-major [E,N,K], 1 tiled (moe_pack_weights)
-  float *y;
+  uint16_t *y;                  // bf16 per-slot results [M*top_k, N]
 };
 
 hipError_t launch_gemm_fp8(const uint8_t *a_q, const float *a_scale, const uint8_t *w_q,
@@ -89,7 +89,7 @@ hipError_t launch_gemm_mxfp8(const uint8_t *a_q, const uint8_t *a_sf, const uint
 hipError_t launch_pack_weights(const uint8_t *w, int E, int N, int K, uint8_t *packed,
                                hipStream_t s);
 
-hipError_t launch_combine(const float *y, int M, int N, int top_k, uint16_t *out,
+hipError_t launch_combine(const uint16_t *y, int M, int N, int top_k, uint16_t *out,
                           hipStream_t s);
 
 }  // namespace qmoe

@@ -78,7 +78,7 @@ class RoutedMoE:
             self.a_scale = _empty((1,), torch.float32, dev)
             self.ws = _empty((moe_quantize_workspace_bytes(MOE_Q_FP8_PER_TENSOR, 1),),
                              torch.uint8, dev)
-        self.y = _empty((S, N), torch.float32, dev)
+        self.y = _empty((S, N), torch.int16, dev)      # bf16 bits, one row per slot
         self.out = _empty((M, N), torch.int16, dev)     # bf16 bits
 
     def route(self, logits):

@@ -169,3 +169,17 @@ def test_combine_special_cases():
     y = np.array([[2.0 ** -24], [2.0 ** -24], [1.0]], np.float32)
     out32, _ = O.combine(y, 3)
     assert out32[0, 0] == np.float32(1.0) + np.float32(2.0 ** -23)
+
+
+def test_slot_results_bf16_match_torch_rounding():
+    """The per-slot bf16 storage step equals torch's float32 -> bfloat16
+    conversion (round to nearest even), including ties, binade edges,
+    subnormals and signed zero."""
+    import torch
+    rng = np.random.default_rng(23)
+    y = rng.standard_normal((16, 64)).astype(np.float32) * np.float32(3.0)
+    special = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 3.99999, 65504.0,
+                        1e-40, -0.0, 2.0 ** -126, 3.0e38], np.float32)
+    y.reshape(-1)[:special.size] = special
+    ref = torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(O.slot_results_bf16(y), ref)

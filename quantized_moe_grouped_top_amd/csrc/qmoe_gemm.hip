@@ -19,25 +19,20 @@
 //     last 8), for A and for B.
 // The accumulator tile has column (l & 15) and rows 4*(l >> 4) + 0..3 in lane l.
 //
-// Two kernels for the routed formats, chosen by block_m:
-//   block_m = 16  : weight streaming for few rows per expert (decode).  One
-//                   workgroup per (64-column tile, expert) keeps all of the
-//                   expert's rows (up to 32 per pass) in registers, so every
-//                   weight byte is read from HBM once.  The 4 wavefronts take
-//                   interleaved k steps (together they read 4 consecutive
-//                   k steps of each weight row) and their partial sums are
-//                   added in LDS in a fixed order.
-//   block_m = 128 : tiled MFMA kernel for many rows per expert.  A 128-row
-//                   block of gathered activations is staged through LDS
-//                   (XOR-swizzled 16-byte chunks, double buffered); each
-//                   wavefront streams its own 64 weight columns straight into
-//                   registers in MFMA layout (int8 converted to bf16 there).
-//                   Tiles are ordered expert by expert, column tile by column
-//                   tile, and split over the 8 XCDs in contiguous chunks, so
-//                   the workgroups resident on one XCD share weight and
-//                   activation tiles through its L2.
-// MXFP8 uses the tiled kernel over expert-contiguous rows, with the scaled
-// MFMA and the e8m0 scales of both operands.
+// Two kernels, both fed by direct-to-LDS DMA (global_load_lds_dwordx4):
+//   stream_kernel (routed, block_m = 16): weight streaming for few rows per
+//                   expert (decode).  One persistent workgroup per CU owns an
+//                   expert and up to 7 consecutive 64-column tiles; weight
+//                   bytes are read from HBM once, all of the expert's rows
+//                   (64 per pass) ride along in the same LDS stages.
+//   gemm_kernel   (routed, block_m = 128, and MXFP8): 128-row x 256-column
+//                   MFMA tiles, 8 wavefronts of 64 x 64, operands of each
+//                   128-k stage DMA'd into a ring two stages ahead.  Tiles
+//                   are ordered expert by expert, column tile by column tile,
+//                   row block fastest, and split over the 8 XCDs in
+//                   contiguous chunks, so the workgroups resident on one XCD
+//                   share each weight tile through its L2.
+// Routed results are written per slot as bf16; MXFP8 rows as bf16.
 #include "qmoe_internal.h"
 
 namespace qmoe {

@@ -190,7 +190,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
   using C = SCfg<kInt8>;
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[2 * C::kStage];
   __shared__ int s_slot[kSMB * 16];
-  __shared__ float s_topk[kSMB * 16];
+  __shared__ int s_nvalid;
   __shared__ float s_scale[kSMaxTiles * 64];
 
   const int e = blockIdx.x / groups;
@@ -237,26 +237,61 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
     }
   };
 
-  // The weights of stage 0 do not depend on the routing: start them now.  The
-  // routing buffers are then read with scalar loads (they count on lgkmcnt,
-  // not vmcnt), so reading them does not wait for this DMA.
+  // Routing first.  With few blocks (decode) the block labels and the sorted
+  // slot ids are copied into LDS by dword DMA ahead of the stage-0 weights:
+  // vector-memory requests are served in order, so these small reads are not
+  // queued behind the weight stream, and the whole routing costs one memory
+  // latency instead of a chain of dependent scalar loads.  They land in the
+  // activation areas of the two ring slots, which are free until the
+  // activation DMA of the first pass (labels: slot 0, slot ids: slot 1).
+  const int n_sorted_dma = (max_blocks * 16 + 63) / 64;   // 256-byte dword DMAs
+  const int n_label_dma = (max_blocks + 63) / 64;
+  const bool staged = n_sorted_dma * 256 <= C::kABytes && n_label_dma * 256 <= C::kABytes;
+  const uint32_t lds_sorted = lds_ring + (uint32_t)(C::kStage + kSMaxTiles * C::kBTile);
+  const uint32_t lds_labels = lds_ring + (uint32_t)(kSMaxTiles * C::kBTile);
+  if (staged) {
+    for (int q = wave; q < n_sorted_dma + n_label_dma; q += kSWaves) {
+      if (q < n_sorted_dma) {
+        const int i = min(q * 64 + lane, max_blocks * 16 - 1);          // clamped: in bounds
+        dma4(sorted_ids, 4u * (uint32_t)i, lds_sorted + (uint32_t)(256 * q));
+      } else {
+        const int qq = q - n_sorted_dma;
+        const int i = min(qq * 64 + lane, max_blocks - 1);
+        dma4(expert_ids, 4u * (uint32_t)i, lds_labels + (uint32_t)(256 * qq));
+      }
+    }
+  }
+  // The weights of stage 0 do not depend on the routing: start them now (G
+  // DMAs per wavefront).  The router weights are read only in the epilogue.
   issue_b(0);
-  const bool early_b = true;
-  typedef const __attribute__((address_space(4))) int *cint_ptr;
-  typedef const __attribute__((address_space(4))) float *cfloat_ptr;
-  const cint_ptr c_expert_ids = (cint_ptr)expert_ids;
-  const cint_ptr c_sorted = (cint_ptr)sorted_ids;
-  const cfloat_ptr c_topk = (cfloat_ptr)topk_w;
 
   // this expert's blocks [b_begin, b_end) from the ascending block labels
-  // (-1 after the last block); every wavefront scans them on its scalar unit,
-  // 16 labels per load
-  typedef int int16v __attribute__((ext_vector_type(16)));
-  typedef const __attribute__((address_space(4))) int16v *cint16_ptr;
+  // (-1 after the last block)
   int b_begin = max_blocks, b_end = max_blocks;
-  {
+  constexpr int kEndLabel = 1 << 30;                       // -1 sorts after every expert
+  if (staged) {
+    wait_dma_upto(G);                                      // this wave's routing DMAs landed
+    __syncthreads();                                       // ... and everyone's
+    const int *labels = reinterpret_cast<const int *>(s_ring + kSMaxTiles * C::kBTile);
+    for (int base = 0; base < max_blocks; base += 64) {   // a wavefront-wide search
+      int v = base + lane < max_blocks ? labels[base + lane] : kEndLabel;
+      v = v < 0 ? kEndLabel : v;
+      const unsigned long long ge = __ballot(v >= e), gt = __ballot(v > e);
+      if (b_begin == max_blocks && ge) b_begin = base + __builtin_ctzll(ge);
+      if (gt) {
+        b_end = base + __builtin_ctzll(gt);
+        break;
+      }
+    }
+  } else {
+    // every wavefront scans the labels on its scalar unit, 16 per load (the
+    // scalar loads count on lgkmcnt, so they do not wait for the weight DMA)
+    typedef const __attribute__((address_space(4))) int *cint_ptr;
+    typedef int int16v __attribute__((ext_vector_type(16)));
+    typedef const __attribute__((address_space(4))) int16v *cint16_ptr;
+    const cint_ptr c_expert_ids = (cint_ptr)expert_ids;
     auto visit = [&](int b, int v) {
-      v = v < 0 ? (1 << 30) : v;
+      v = v < 0 ? kEndLabel : v;
       if (b_begin == max_blocks && v >= e) b_begin = b;
       if (b_end == max_blocks && v > e) b_end = b;
     };
@@ -276,33 +311,48 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
   for (int bp = b_begin, pass_ = 0; bp < b_end; bp += kSMB, ++pass_) {
     const int nmb = min(b_end - bp, kSMB);
     __syncthreads();                                       // s_slot / ring reuse across passes
-    if (wave == 0) {                                       // slot ids and router weights, scalar
+    int nvalid;                                            // rows holding a routed slot
+    if (staged && pass_ == 0) {
+      // from the staged copy (the activation DMA below overwrites it)
+      const int *sorted = reinterpret_cast<const int *>(s_ring + C::kStage + kSMaxTiles * C::kBTile);
+      int slot = S;
+      if (tid < nmb * 16) slot = sorted[bp * 16 + tid];
+      if (tid < kSMB * 16) s_slot[tid] = slot;
+      nvalid = __syncthreads_count(tid < kSMB * 16 && slot < S);
+    } else {
+      if (wave == 0) {                                     // slot ids, scalar
+        typedef int int16v __attribute__((ext_vector_type(16)));
+        typedef const __attribute__((address_space(4))) int16v *cint16_ptr;
+        const cint16_ptr c_sorted16 = (cint16_ptr)sorted_ids;
+        int nv = 0;
 #pragma unroll
-      for (int i = 0; i < kSMB; ++i) {
-        int16v sl;
-        if (i < nmb) {
-          sl = *(cint16_ptr)(c_sorted + (bp + i) * 16);    // one 64-byte block of slots
-        } else {
+        for (int i = 0; i < kSMB; ++i) {
+          int16v sl;
+          if (i < nmb) {
+            sl = c_sorted16[bp + i];                       // one 64-byte block of slots
+          } else {
 #pragma unroll
-          for (int u = 0; u < 16; ++u) sl[u] = S;
-        }
-        float tw[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) tw[u] = sl[u] < S ? c_topk[sl[u]] : 0.0f;
-#pragma unroll
-        for (int u = 0; u < 16; ++u)
-          if (lane == u) {
-            s_slot[i * 16 + u] = sl[u];
-            s_topk[i * 16 + u] = tw[u];
+            for (int u = 0; u < 16; ++u) sl[u] = S;
           }
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+            if (lane == u) s_slot[i * 16 + u] = sl[u];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) nv += sl[u] < S ? 1 : 0;
+        }
+        if (lane == 0) s_nvalid = nv;
       }
+      __syncthreads();
+      nvalid = s_nvalid;
     }
-    __syncthreads();
 
     // activation DMA of this wavefront (1 KB instructions q = wave + 8j): the
     // row and the swizzled chunk each lane fetches
     constexpr int kAPerWave = (C::kAInstr + kSWaves - 1) / kSWaves;
-    const int a_instr = kInt8 ? 4 * nmb : 2 * nmb;        // 1 KB holds 4 (bf16) or 8 (fp8) rows
+    // rows that hold a routed slot (padding slots only follow the expert's
+    // last routed one, and their rows are never stored, so their LDS rows
+    // are left as they are); 1 KB holds 4 (bf16) or 8 (fp8) rows
+    const int a_instr = kInt8 ? (nvalid + 3) / 4 : (nvalid + 7) / 8;
     uint32_t a_row[kAPerWave], a_chk[kAPerWave];
 #pragma unroll
     for (int j = 0; j < kAPerWave; ++j) {
@@ -409,7 +459,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
       }
     };
 
-    if (pass_ == 0 && early_b) {
+    if (pass_ == 0) {
       issue_a(0);                                          // stage 0's weights are already in flight
     } else {
       issue(0);
@@ -444,7 +494,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
         for (int rr = 0; rr < 4; ++rr) {
           const int k = 16 * i + 4 * g + rr;
           const int slot = s_slot[k];
-          const float v = acc[t][i][rr] * cs * s_topk[k];
+          const float v = acc[t][i][rr] * cs * (slot < S ? topk_w[slot] : 0.0f);
           const float vn = __shfl_xor(v, 1);           // the next column's value
           // N is a multiple of 8: an even column and its neighbour are both
           // inside the row or both past its end

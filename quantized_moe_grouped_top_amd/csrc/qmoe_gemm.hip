@@ -865,6 +865,313 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(
   }
 }
 
+// =============================================================================
+// fp8 W8A8 (block_m = 128) and MXFP8: 256 x 256 tiles
+// =============================================================================
+// A tile covers two consecutive 128-row blocks of one expert (the second may
+// be missing: an expert with an odd number of blocks) and 256 columns.  The
+// kWaves wavefronts split it as 2 (rows) x kWaves/2 (columns): each owns 128
+// rows x 512/kWaves columns as 8 x kFN MFMA fragments.  Against 64 x 64
+// wavefront tiles this reads fewer LDS bytes per MFMA (activation fragments
+// serve kFN MFMAs each) and moves a third fewer global bytes per flop.
+// Operands of stage st + 1 come HBM/L2 -> LDS by direct-to-LDS DMA while
+// stage st computes (two 64 KB ring slots); the epilogue stages bf16 results
+// in LDS and stores whole row segments.  LDS layouts as in gemm_kernel.
+constexpr int kHBM = 256;
+constexpr int kHBN = 256;
+constexpr int kHABytes = kHBM * 128;                        // 32 KB of fp8 rows per stage
+constexpr int kHBBytes = kHBN * 128;                        // 32 KB of weight rows per stage
+constexpr int kHStage = kHABytes + kHBBytes;
+constexpr int kHSf = 4 * kHBM + 4 * kHBN;                   // MXFP8 scale bytes per stage
+constexpr int kHWaves = 8;
+
+template <int kFmt, bool kTiled, int kWaves>
+__global__ __launch_bounds__(64 * kWaves, 1) void gemm_big_kernel(
+    const uint8_t *__restrict__ a, const float *__restrict__ a_scale,
+    const uint8_t *__restrict__ a_sf, const uint8_t *__restrict__ w,
+    const float *__restrict__ w_scale, const uint8_t *__restrict__ w_sf,
+    const int *__restrict__ sorted_ids, const int *__restrict__ expert_ids,
+    const float *__restrict__ topk_w, const int *__restrict__ m_offsets, int M, int K, int N,
+    int E, int top_k, int max_blocks, uint16_t *__restrict__ out) {
+  constexpr bool kMx = kFmt == kFmtMx;
+  static_assert(kFmt != kFmtInt8, "int8 W8A16 uses gemm_kernel");
+  static_assert(kWaves == 4 || kWaves == 8, "wavefronts");
+  constexpr int kThr = 64 * kWaves;
+  constexpr int kFM = 8;                                 // row fragments per wavefront (128 rows)
+  constexpr int kCols = 512 / kWaves;                    // columns per wavefront
+  constexpr int kFN = kCols / 16;
+  constexpr int kDma = 32 / kWaves;                      // activation (and weight) DMAs per wave
+  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[2 * kHStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s_sf[kMx ? 2 * kHSf : 16];
+  __shared__ int s_row[kHBM];
+  __shared__ int s_blk_first[kMaxExperts + 1];
+  __shared__ int s_tile_first[kMaxExperts + 1];
+  __shared__ int s_mo[kMx ? kMaxExperts + 1 : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int ntn = (N + kHBN - 1) / kHBN;
+
+  // ---- tile space: expert by expert, column tile by column tile, block pair
+  // fastest; each XCD takes one contiguous chunk of it
+  if constexpr (!kMx) {
+    expert_block_starts(expert_ids, max_blocks, E, s_blk_first);
+    __syncthreads();
+  }
+  if (tid == 0) {
+    int blk = 0, tiles = 0;
+    for (int ee = 0; ee < E; ++ee) {
+      int nb;
+      if constexpr (kMx) {
+        s_mo[ee] = m_offsets[ee];
+        s_mo[ee + 1] = m_offsets[ee + 1];
+        const int m = s_mo[ee + 1] - s_mo[ee];
+        nb = m > 0 ? (m + kGBM - 1) / kGBM : 0;
+        s_blk_first[ee] = blk;
+        blk += nb;
+      } else {
+        nb = s_blk_first[ee + 1] - s_blk_first[ee];
+      }
+      s_tile_first[ee] = tiles;
+      tiles += (nb + 1) / 2 * ntn;
+    }
+    if constexpr (kMx) s_blk_first[E] = blk;
+    s_tile_first[E] = tiles;
+  }
+  __syncthreads();
+  const int total = s_tile_first[E];
+  const int chunk = (total + kXcds - 1) / kXcds;
+  const int xcd = blockIdx.x % kXcds;
+  const int idx = blockIdx.x / kXcds;
+  const int L = xcd * chunk + idx;
+  if (idx >= chunk || L >= total) return;
+  int e = 0;
+  while (s_tile_first[e + 1] <= L) ++e;
+  const int nblk = s_blk_first[e + 1] - s_blk_first[e];
+  const int npair = (nblk + 1) / 2;
+  const int local = L - s_tile_first[e];
+  const int nt = local / npair;
+  const int pr = local - nt * npair;
+  const int nb_here = min(2, nblk - 2 * pr);            // 128-row blocks in this tile
+  const int n0 = nt * kHBN;
+  const int S = M * top_k;
+  int row0 = 0, row_end = 0;                            // MXFP8: the tile's rows
+  for (int r = tid; r < kHBM; r += kThr) {
+    if constexpr (kMx) {
+      row0 = s_mo[e] + 2 * pr * kGBM;
+      s_row[r] = row0 + r;
+    } else {
+      s_row[r] = r < nb_here * kGBM ? sorted_ids[(s_blk_first[e] + 2 * pr) * kGBM + r] : S;
+    }
+  }
+  if constexpr (kMx) {
+    row0 = s_mo[e] + 2 * pr * kGBM;
+    row_end = s_mo[e + 1];
+  }
+  __syncthreads();
+  auto src_row = [&](int r) -> uint32_t {
+    const int v = s_row[r];
+    if constexpr (kMx) return (uint32_t)(v < row_end ? v : row_end - 1);
+    else return (uint32_t)(v < S ? v / top_k : 0);
+  };
+  // this wave's activation DMA rows (8 kDma rows from 8 kDma wave) exist
+  const bool a_dma = (8 * kDma * wave) / kGBM < nb_here;
+  const bool busy = wm < nb_here;                       // this wave's 128 output rows exist
+
+  // ---- DMA sources of this lane ----------------------------------------------
+  const uint32_t lds_ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)s_ring;
+  const int nst = K / 128;
+  uint32_t a_off[kDma];
+#pragma unroll
+  for (int u = 0; u < kDma; ++u) {
+    const int r = 8 * (kDma * wave + u) + (lane >> 3);
+    a_off[u] = src_row(r) * (uint32_t)K + 16u * (uint32_t)((lane & 7) ^ swz(r));
+  }
+  // weights: DMAs q = kDma wave + u, 1 KB each: 64-column block q / 8, piece q % 8
+  const int bblk = (kDma * wave) / 8;                   // the same block for all of this wave's
+  uint32_t wblk = 0;
+  uint32_t b_off[kDma];
+  if constexpr (kTiled) {
+    const int T = (N + 63) / 64;
+    const int pt = min(n0 / 64 + bblk, T - 1);
+    wblk = ((uint32_t)e * (uint32_t)T + (uint32_t)pt) * (uint32_t)nst * 8192u;
+  } else {
+#pragma unroll
+    for (int u = 0; u < kDma; ++u) {
+      const int n = 8 * ((kDma * wave + u) & 7) + (lane >> 3);
+      const int col = min(n0 + bblk * 64 + n, N - 1);
+      b_off[u] = ((uint32_t)e * (uint32_t)N + (uint32_t)col) * (uint32_t)K +
+                 16u * (uint32_t)((lane & 7) ^ swz(n));
+    }
+  }
+  // MXFP8 scales: 8 dword DMAs per stage (rows 0-255, then columns 0-255, 64
+  // per DMA), spread over the wavefronts
+  constexpr int kSfPerWave = 8 / kWaves;
+  const uint32_t kb_row = (uint32_t)K / 32u;
+  uint32_t sf_off[kSfPerWave];
+  bool sf_on[kSfPerWave];
+  if constexpr (kMx) {
+    int po = 0;
+    for (int ee = 0; ee < e; ++ee) po += (s_mo[ee + 1] - s_mo[ee] + kMxRowPad - 1) / kMxRowPad * kMxRowPad;
+#pragma unroll
+    for (int u = 0; u < kSfPerWave; ++u) {
+      const int q = kSfPerWave * wave + u;             // 0-3 rows, 4-7 columns
+      if (q < 4) {
+        sf_off[u] = ((uint32_t)po + src_row(64 * q + lane) - (uint32_t)s_mo[e]) * kb_row;
+        sf_on[u] = (64 * q) / kGBM < nb_here;
+      } else {
+        sf_off[u] = ((uint32_t)e * (uint32_t)N + (uint32_t)min(n0 + 64 * (q - 4) + lane, N - 1)) * kb_row;
+        sf_on[u] = true;
+      }
+    }
+  }
+  const uint32_t lds_sf = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)s_sf;
+
+  auto issue = [&](int st, int slot_i) {
+    const uint32_t base = lds_ring + (uint32_t)(slot_i * kHStage);
+    if (a_dma) {
+      const uint8_t *src = a + (size_t)st * 128u;
+#pragma unroll
+      for (int u = 0; u < kDma; ++u)
+        dma16(src, a_off[u], base + (uint32_t)((kDma * wave + u) * 1024));
+    }
+    const uint32_t bdst = base + (uint32_t)(kHABytes + (kDma * wave) * 1024);
+    if constexpr (kTiled) {
+      const uint8_t *src = w + wblk + (size_t)st * 8192u + ((kDma * wave) & 7) * 1024;
+#pragma unroll
+      for (int u = 0; u < kDma; ++u) dma16(src, (uint32_t)(u * 1024 + 16 * lane), bdst + (uint32_t)(u * 1024));
+    } else {
+      const uint8_t *src = w + (size_t)st * 128u;
+#pragma unroll
+      for (int u = 0; u < kDma; ++u) dma16(src, b_off[u], bdst + (uint32_t)(u * 1024));
+    }
+    if constexpr (kMx) {
+      const uint32_t sdst = lds_sf + (uint32_t)(slot_i * kHSf);
+#pragma unroll
+      for (int u = 0; u < kSfPerWave; ++u) {
+        const int q = kSfPerWave * wave + u;
+        if (sf_on[u]) dma4((q < 4 ? a_sf : w_sf) + 4 * st, sf_off[u], sdst + (uint32_t)(256 * q));
+      }
+    }
+  };
+
+  f32x4 acc[kFM][kFN];
+#pragma unroll
+  for (int i = 0; i < kFM; ++i)
+#pragma unroll
+    for (int j = 0; j < kFN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int sw = swz(r16);
+  auto compute = [&](int slot_i) {
+    const uint8_t *As = s_ring + slot_i * kHStage + wm * 128 * 128;
+    const uint8_t *Bs = s_ring + slot_i * kHStage + kHABytes + wn * kCols * 128;
+    const uint8_t *sfs = s_sf + slot_i * kHSf;
+    i32x8 bv[kFN];
+#pragma unroll
+    for (int j = 0; j < kFN; ++j) {
+      const uint8_t *br = Bs + (j * 16 + r16) * 128;
+      bv[j] = __builtin_shufflevector(ld16(br + ((g ^ sw) << 4)), ld16(br + (((g + 4) ^ sw) << 4)),
+                                      0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    int sb[kFN];
+    if constexpr (kMx) {
+#pragma unroll
+      for (int j = 0; j < kFN; ++j)
+        sb[j] = (int)((*reinterpret_cast<const uint32_t *>(sfs + 4 * kHBM + 4 * (wn * kCols + j * 16 + r16)) >> (8 * g)) & 0xFFu);
+    }
+    // activation fragment i + 1 is read while the MFMAs of fragment i run
+    auto load_a = [&](int i) {
+      const uint8_t *ar = As + (i * 16 + r16) * 128;
+      return __builtin_shufflevector(ld16(ar + ((g ^ sw) << 4)), ld16(ar + (((g + 4) ^ sw) << 4)),
+                                     0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    auto load_sa = [&](int i) {
+      if constexpr (kMx)
+        return (int)((*reinterpret_cast<const uint32_t *>(sfs + 4 * (wm * 128 + i * 16 + r16)) >> (8 * g)) & 0xFFu);
+      else
+        return 0;
+    };
+    i32x8 av = load_a(0);
+    int sa = load_sa(0);
+#pragma unroll
+    for (int i = 0; i < kFM; ++i) {
+      i32x8 av_next = av;
+      int sa_next = sa;
+      if (i + 1 < kFM) {
+        av_next = load_a(i + 1);
+        sa_next = load_sa(i + 1);
+      }
+      if constexpr (kMx) {
+#pragma unroll
+        for (int j = 0; j < kFN; ++j) acc[i][j] = mfma_mx(av, bv[j], acc[i][j], sa, sb[j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kFN; ++j) acc[i][j] = mfma_fp8(av, bv[j], acc[i][j]);
+      }
+      av = av_next;
+      sa = sa_next;
+    }
+  };
+
+  // ---- two-slot ring: stage st in slot st & 1, stage st + 1 in flight ------
+  issue(0, 0);
+  for (int st = 0; st < nst; ++st) {
+    wait_dma_all();                                     // this wave's DMA of stage st landed
+    __syncthreads();                                    // ... everyone's; slot (st + 1) & 1 is free
+    if (st + 1 < nst) issue(st + 1, (st + 1) & 1);
+    if (busy) compute(st & 1);
+  }
+
+  // ---- epilogue: bf16 results -> LDS (the ring is free) -> row segments ----
+  __syncthreads();
+  float cscale = 1.0f;
+  if constexpr (!kMx) cscale = a_scale[0] * w_scale[e];
+  if (!busy) return;
+  uint16_t *t = reinterpret_cast<uint16_t *>(s_ring) + wave * 128 * kCols;   // [128 rows][kCols]
+#pragma unroll
+  for (int i = 0; i < kFM; ++i)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int r = i * 16 + 4 * g + rr;
+      float rs = 1.0f;
+      if constexpr (!kMx) {
+        const int slot = s_row[wm * 128 + r];
+        rs = cscale * (slot < S ? topk_w[slot] : 0.0f);
+      }
+#pragma unroll
+      for (int j = 0; j < kFN; ++j)
+        t[r * kCols + j * 16 + r16] = (uint16_t)(f32x2_to_bf16x2(acc[i][j][rr] * rs, 0.0f) & 0xFFFFu);
+    }
+  __builtin_amdgcn_s_waitcnt(0xC07F);                   // lgkmcnt(0): the wave's LDS writes done
+  __builtin_amdgcn_wave_barrier();
+  const bool vec = (N & 7) == 0 && ((uintptr_t)out & 15u) == 0;
+  constexpr int kLanesPerRow = kCols / 8;               // 16 bytes per lane
+  constexpr int kRowsPerStore = 64 / kLanesPerRow;
+#pragma unroll 4
+  for (int q = 0; q < 128 / kRowsPerStore; ++q) {
+    const int r = q * kRowsPerStore + lane / kLanesPerRow;
+    const int col = n0 + wn * kCols + (lane % kLanesPerRow) * 8;
+    int dst_row;
+    if constexpr (kMx) {
+      dst_row = row0 + wm * 128 + r;
+      if (dst_row >= row_end) continue;
+    } else {
+      dst_row = s_row[wm * 128 + r];
+      if (dst_row >= S) continue;
+    }
+    if (col >= N) continue;
+    const uint16_t *src = t + r * kCols + (lane % kLanesPerRow) * 8;
+    uint16_t *dst = out + (size_t)dst_row * N + col;
+    if (vec && col + 8 <= N) {
+      *reinterpret_cast<i32x4 *>(dst) = *reinterpret_cast<const i32x4 *>(src);
+    } else {
+      for (int c = 0; c < 8 && col + c < N; ++c) dst[c] = src[c];
+    }
+  }
+}
+
 unsigned tile_grid(long long tiles_bound) {
   long long per = (tiles_bound + kXcds - 1) / kXcds;
   return (unsigned)(per * kXcds);
@@ -906,9 +1213,9 @@ hipError_t launch_gemm_fp8(const uint8_t *a_q, const float *a_scale, const uint8
                        r.sorted_ids, r.expert_ids, r.num_post, r.topk_w, r.M, r.K, r.N, r.top_k,
                        groups, tpg, r.max_blocks, r.y);
   } else {
-    const long long tiles = (long long)r.max_blocks * ((r.N + kGBN - 1) / kGBN);
-    auto k = r.w_layout ? gemm_kernel<kFmtFp8, true> : gemm_kernel<kFmtFp8, false>;
-    hipLaunchKernelGGL(k, dim3(tile_grid(tiles)), dim3(kGThreads), 0, s, a_q, a_scale, nullptr, w_q,
+    const long long tiles = (long long)(r.max_blocks / 2 + r.E) * ((r.N + kHBN - 1) / kHBN);
+    auto k = r.w_layout ? gemm_big_kernel<kFmtFp8, true, kHWaves> : gemm_big_kernel<kFmtFp8, false, kHWaves>;
+    hipLaunchKernelGGL(k, dim3(tile_grid(tiles)), dim3(64 * kHWaves), 0, s, a_q, a_scale, nullptr, w_q,
                        w_scale, nullptr, r.sorted_ids, r.expert_ids, r.topk_w, nullptr, r.M, r.K,
                        r.N, r.E, r.top_k, r.max_blocks, r.y);
   }
@@ -939,9 +1246,10 @@ hipError_t launch_gemm_int8(const uint16_t *a, const int8_t *w_q, const float *w
 hipError_t launch_gemm_mxfp8(const uint8_t *a_q, const uint8_t *a_sf, const uint8_t *w_q,
                              const uint8_t *w_sf, const int *m_offsets, int rows, int K, int N,
                              int E, uint16_t *out, hipStream_t s) {
-  const long long blocks = (rows + kGBM - 1) / kGBM + E;
-  const long long tiles = blocks * ((N + kGBN - 1) / kGBN);
-  hipLaunchKernelGGL((gemm_kernel<kFmtMx, false>), dim3(tile_grid(tiles)), dim3(kGThreads), 0, s,
+  // block pairs: at most (sum of blocks + E) / 2 + E
+  const long long pairs = ((rows + kGBM - 1) / kGBM + E) / 2 + E;
+  const long long tiles = pairs * ((N + kHBN - 1) / kHBN);
+  hipLaunchKernelGGL((gemm_big_kernel<kFmtMx, false, kHWaves>), dim3(tile_grid(tiles)), dim3(64 * kHWaves), 0, s,
                      a_q, nullptr, a_sf, w_q, nullptr, w_sf, nullptr, nullptr, nullptr, m_offsets,
                      rows, K, N, E, 1, 0, out);
   return hipGetLastError();

@@ -204,7 +204,11 @@ def test_routed_full_size_sampled(wl):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("wl", FULL[:2], ids=[w.name for w in FULL[:2]])
+ROWMAJOR_FULL = FULL[:2] + [synth.WORKLOADS["fp8_bias_m4096_k4096_n14336"],
+                            synth.WORKLOADS["mistral7b_down_int8_m4096_k14336_n4096"]]
+
+
+@pytest.mark.parametrize("wl", ROWMAJOR_FULL, ids=[w.name for w in ROWMAJOR_FULL])
 def test_routed_full_size_sampled_rowmajor(wl):
     run_routed(wl, block_m=None, full=False, layout=qm.MOE_W_ROWMAJOR)
     torch.cuda.empty_cache()

@@ -48,30 +48,41 @@ __global__ __launch_bounds__(kThreads) void route_align_kernel(
   __syncthreads();
 
   // ---- 1. top-k choice and router weights of every token -------------------
+  // One pass over the token's logits keeps the top_k best (value descending;
+  // on equal values the earlier expert stays, as a later one must be strictly
+  // larger to move in) by insertion; logits are read 8 at a time so their
+  // loads overlap.
   for (int t = tid; t < M; t += kThreads) {
     const float *lg = logits + (size_t)t * E;
-    unsigned long long taken0 = 0, taken1 = 0;    // chosen experts (E <= 128)
     int ids[kMaxTopK];
     float val[kMaxTopK];
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
       ids[j] = 0;
       val[j] = 0.0f;
-      if (j < top_k) {
-        int best = -1;
-        float bv = 0.0f;
-        for (int e = 0; e < E; ++e) {
-          const bool taken = e < 64 ? ((taken0 >> e) & 1ull) : ((taken1 >> (e - 64)) & 1ull);
-          const float v = lg[e];
-          // strictly larger wins, so on equal logits the lower index stays
-          if (!taken && (best < 0 || v > bv)) {
-            best = e;
-            bv = v;
+    }
+    int nfill = 0;
+    for (int e0 = 0; e0 < E; e0 += 8) {
+      float v8[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v8[u] = e0 + u < E ? lg[e0 + u] : 0.0f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (e0 + u >= E) break;
+        float cv = v8[u];
+        int ci = e0 + u;
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) {
+          if (j < top_k && (j >= nfill || cv > val[j])) {   // place here, carry the old one down
+            const float tv = val[j];
+            const int ti = ids[j];
+            val[j] = cv;
+            ids[j] = ci;
+            cv = tv;
+            ci = ti;
           }
         }
-        if (best < 64) taken0 |= 1ull << best; else taken1 |= 1ull << (best - 64);
-        ids[j] = best;
-        val[j] = bv;
+        nfill = min(nfill + 1, top_k);
       }
     }
     // weights: exp(l_j - l_max) / sum over the chosen experts

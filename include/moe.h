@@ -188,7 +188,7 @@ int moe_quantize_weights(const float *w, int E, int N, int K, int mode,
  * 64 x 128-byte block (e, t, s) is stored contiguously (8192 bytes) at byte
  * offset ((e*T + t)*S + s) * 8192, rows in order, 128 bytes per row, and the
  * 16-byte chunk c of row r (k = 128s + 16c .. 128s + 16c + 15) at chunk
- * position c ^ ((r & 7) ^ ((r >> 3) & 1)) of that row.  Rows n >= N and
+ * position c ^ ((r >> 1) & 7) of that row.  Rows n >= N and
  * k >= K are zero.
  * Every block is then one contiguous HBM read of the decode GEMM, landing in
  * LDS in the bank-conflict-free order its MFMA reads use.

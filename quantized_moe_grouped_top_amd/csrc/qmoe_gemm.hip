@@ -173,10 +173,12 @@ __device__ __forceinline__ void wait_dma_upto(int n) {
 }
 
 // 128-byte rows: 16-byte chunk c of row r sits at chunk c ^ swz(r);
-// 256-byte rows: at chunk c ^ (r & 15).  Either way the 16 rows one fragment
-// read touches at one chunk index fall on distinct banks, whether the LDS
-// serves such a read 8 lanes (128 bytes) or 16 lanes (256 bytes) at a time.
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// 256-byte rows: at chunk c ^ (r & 15).  With these, the MFMA fragment reads
+// (ds_read_b128, lane group g of 16 rows at one chunk index each) run free of
+// LDS bank conflicts on gfx950 (measured with SQ_LDS_BANK_CONFLICT: so does
+// c ^ (r & 7) on 128-byte rows, while e.g. c ^ ((r & 7) ^ ((r >> 3) & 1))
+// conflicts two ways).
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int sw128(int r, int c) { return r * 128 + ((c ^ swz(r)) << 4); }
 __device__ __forceinline__ int sw256(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
 

@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void quant_mx_rows_kernel(const float *__
 
 // ---- weight re-layout for streaming: one thread per 16-byte chunk ----------
 // Block (e, t, s) of 64 rows x 128 bytes, rows in order, chunk c of row r at
-// position c ^ ((r & 7) ^ ((r >> 3) & 1)); rows >= N and k >= K are zero.
+// position c ^ ((r >> 1) & 7); rows >= N and k >= K are zero.
 __global__ __launch_bounds__(kThreads) void pack_weights_kernel(const uint8_t *__restrict__ w,
                                                                 int E, int N, int K,
                                                                 uint8_t *__restrict__ packed) {
@@ -239,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void pack_weights_kernel(const uint8_t *_
     const long long b = i >> 9;                       // 512 chunks per 8 KB block
     const int within = (int)(i & 511);
     const int r = within >> 3;
-    const int c = (within & 7) ^ ((r & 7) ^ ((r >> 3) & 1));
+    const int c = (within & 7) ^ ((r >> 1) & 7);
     const int s_ = (int)(b % S);
     const int t = (int)((b / S) % T);
     const int e = (int)(b / ((long long)S * T));

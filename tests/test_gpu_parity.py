@@ -223,7 +223,7 @@ def _pack_reference(w, N, K):
     blocks = pad.reshape(E, T, 64, S, 128).transpose(0, 1, 3, 2, 4)        # [E,T,S,64,128]
     r = np.arange(64)[:, None]
     pos = np.arange(8)[None, :]
-    src = pos ^ ((r & 7) ^ ((r >> 3) & 1))                                 # chunk stored at pos
+    src = pos ^ ((r >> 1) & 7)                                             # chunk stored at pos
     chunks = blocks.reshape(E, T, S, 64, 8, 16)
     out = np.take_along_axis(chunks, np.broadcast_to(src[None, None, None, :, :, None], chunks.shape), axis=4)
     return out.reshape(-1)

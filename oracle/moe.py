@@ -214,6 +214,61 @@ def quantize_act_mxfp8(x_bf16, m_offsets):
     return q, sf
 
 
+# ----------------------------------------------------------------------------
+# fused activation + quantization (the step between the up and the down
+# projection: "[PyTorch] Let GroupedLinear accept MXFP8 input and gradient",
+# Description, SwiGLU / SReLU + MXFP8 quantization)
+# ----------------------------------------------------------------------------
+ACT_SWIGLU, ACT_SRELU = 0, 1
+
+
+def swiglu(x):
+    """SwiGLU of rows [R, 2H] in float64: silu(g) * u with the gate g the first
+    half of the row, u the second, silu(g) = g / (1 + exp(-g))."""
+    v = np.asarray(x, dtype=np.float64)
+    h = v.shape[1] // 2
+    g, u = v[:, :h], v[:, h:]
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g)) * u
+
+
+def srelu(x):
+    """Squared ReLU in float64: max(x, 0)^2."""
+    r = np.maximum(np.asarray(x, dtype=np.float64), 0.0)
+    return r * r
+
+
+def act_values(x_bf16, act):
+    """The activation of bf16 rows (uint16 bits) in float64."""
+    x = bf16_decode(x_bf16)
+    return swiglu(x) if act == ACT_SWIGLU else srelu(x)
+
+
+def act_quantize_mxfp8(x_bf16, m_offsets, act):
+    """Activation of expert-concatenated bf16 rows, rounded once to float32,
+    then MXFP8 with per-expert padded scale blocks (as quantize_act_mxfp8).
+    Exact for SReLU of bf16 inputs (the square of a bf16 value fits float32);
+    for SwiGLU the float32 value of exp differs between implementations, so a
+    comparison allows the codes of nearby values (act_code_bounds)."""
+    y = act_values(x_bf16, act).astype(np.float32)
+    q, b = quantize_mxfp8_rows(y)
+    mo = np.asarray(m_offsets, dtype=np.int64)
+    po = mx_padded_offsets(mo)
+    sf = np.zeros((int(po[-1]), y.shape[1] // MX_BLOCK), dtype=np.uint8)
+    for e in range(len(mo) - 1):
+        n = mo[e + 1] - mo[e]
+        sf[po[e]:po[e] + n] = b[mo[e]:mo[e + 1]]
+    return q, sf
+
+
+def act_quantize_fp8(x_bf16, act):
+    """Activation rounded once to float32, then per-tensor fp8 (as
+    quantize_act_fp8).  Returns (q uint8 [R, H], scale float32)."""
+    y = act_values(x_bf16, act).astype(np.float32)
+    s = fp8_tensor_scale(y)
+    return fp8_quantize_with_scale(y, s), s
+
+
 def quantize_weight_mxfp8(w):
     """MXFP8 weights: w float32 [E, N, K] -> (q uint8 [E, N, K],
     sf uint8 [E, N, K/32]), one scale per 32 values along K of each row."""

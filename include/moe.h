@@ -59,6 +59,10 @@ extern "C" {
 #define MOE_Q_MXFP8            1  /* e4m3 + one e8m0 scale per 32 values along K */
 #define MOE_Q_INT8_PER_CHANNEL 2  /* weights only: int8 + one fp32 scale per output channel */
 
+/* ---- activations fused with the quantization (moe_act_quantize) -------- */
+#define MOE_ACT_SWIGLU 0  /* y = silu(g) * u, row = [g | u] (2H inputs -> H outputs) */
+#define MOE_ACT_SRELU  1  /* y = max(x, 0)^2 (H inputs -> H outputs) */
+
 /* ---- expert weight layouts (fp8 and int8 weights) ------------------------ */
 #define MOE_W_ROWMAJOR 0  /* [E, N, K] bytes, K fastest */
 #define MOE_W_TILED    1  /* as written by moe_pack_weights (see there) */
@@ -99,7 +103,7 @@ size_t moe_packed_weight_bytes(int E, int N, int K);
 
 /* Upper bound on the rows of the padded MXFP8 rowwise scale matrix for `rows`
  * rows spread over E experts: rows + E*127 (each expert's block is padded to
- * a multiple of 128 rows). */
+ * a multiple of 128 rows).  rows > 2^30 -> MOE_EUNSUPPORTED. */
 int moe_mx_scale_rows(int rows, int E);
 
 /* ======================================================================== *
@@ -159,8 +163,35 @@ int moe_align_block_size(const float *logits, int M, int E, int top_k, int block
  *   moe_mx_scale_rows(rows, E) rows; rows past the padded total are not
  *   touched.  scale/workspace unused (may be NULL).
  *
- * K must be a multiple of 32 (MXFP8) or 8 (fp8).  rows = 0 is valid. */
+ * K must be a multiple of 32 (MXFP8) or 8 (fp8); MXFP8 takes at most 2^30
+ * rows.  rows = 0 is valid. */
 int moe_quantize_act(const uint16_t *x, int rows, int K, int mode,
+                     const int *m_offsets, int E, uint8_t *q, float *scale,
+                     uint8_t *scale_e8m0, void *workspace, hipStream_t stream);
+
+/* Activation fused with its quantization: the expert FFN's step between the
+ * up and the down projection ("[PyTorch] Let GroupedLinear accept MXFP8 input
+ * and gradient", Description: SwiGLU / SReLU + MXFP8 quantization of an
+ * expert-concatenated (8*4000, 4096) input, quantized as a whole with the
+ * scaling factors padded per expert).  For every row r and output column
+ * n < H, in float32 on the bf16 inputs:
+ *   MOE_ACT_SWIGLU: x [rows, 2H], g = x[r, n], u = x[r, H + n],
+ *                   y = (g / (1 + exp(-g))) * u
+ *   MOE_ACT_SRELU : x [rows, H], y = max(x[r, n], 0)^2 (exact)
+ * SReLU is exact in float32; SwiGLU uses the hardware exp2 (with the
+ * exponent split into a float32 sum so its rounding does not grow with |g|)
+ * and the hardware reciprocal, within about 7 float32 units of the exact
+ * value (|g| >= 128 gives g * u or a signed zero, as exp(-g) is 0 or
+ * infinite in float32 there).
+ * y [rows, H] is quantized as moe_quantize_act quantizes x with the same
+ * mode (MXFP8 with per-expert padded scale blocks and m_offsets / E, or fp8
+ * per tensor with a workspace of moe_quantize_workspace_bytes(mode, 1) bytes);
+ * y itself is never stored.  q [rows, H] e4m3; scale / scale_e8m0 /
+ * workspace as for moe_quantize_act with K = H.
+ *
+ * x must be 16-byte aligned; H must be a multiple of 32 (MXFP8) or 8 (fp8);
+ * MXFP8 takes at most 2^30 rows.  rows = 0 is valid. */
+int moe_act_quantize(const uint16_t *x, int rows, int H, int act, int mode,
                      const int *m_offsets, int E, uint8_t *q, float *scale,
                      uint8_t *scale_e8m0, void *workspace, hipStream_t stream);
 

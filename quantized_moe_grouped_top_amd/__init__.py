@@ -21,12 +21,14 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmoe.so"
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP = 0, -1, -2, -3
 MOE_Q_FP8_PER_TENSOR, MOE_Q_MXFP8, MOE_Q_INT8_PER_CHANNEL = 0, 1, 2
 MOE_W_ROWMAJOR, MOE_W_TILED = 0, 1
+MOE_ACT_SWIGLU, MOE_ACT_SRELU = 0, 1
 MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_SLOTS = 128, 8, 65536
 
 EXPORTS = [
     "moe_last_error", "moe_last_hip_error", "moe_align_max_padded", "moe_recommended_block_m",
     "moe_quantize_workspace_bytes", "moe_packed_weight_bytes", "moe_mx_scale_rows",
-    "moe_align_block_size", "moe_quantize_act", "moe_quantize_weights", "moe_pack_weights",
+    "moe_align_block_size", "moe_quantize_act", "moe_act_quantize", "moe_quantize_weights",
+    "moe_pack_weights",
     "moe_grouped_gemm_fp8w8a8",
     "moe_grouped_gemm_int8w8a16", "moe_grouped_gemm_mxfp8", "moe_combine",
 ]
@@ -57,6 +59,7 @@ _SIGS = {
     "moe_mx_scale_rows": (_I, [_I, _I]),
     "moe_align_block_size": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "moe_quantize_act": (_I, [_P, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P]),
+    "moe_act_quantize": (_I, [_P, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P]),
     "moe_quantize_weights": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "moe_grouped_gemm_fp8w8a8": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
     "moe_grouped_gemm_int8w8a16": (_I, [_P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
@@ -141,6 +144,13 @@ def moe_quantize_act(x, rows, K, mode, m_offsets, E, q, scale, scale_e8m0, works
                      stream=None):
     return _check(lib().moe_quantize_act(
         _ptr(x), rows, K, mode, _ptr(m_offsets), E, _ptr(q), _ptr(scale), _ptr(scale_e8m0),
+        _ptr(workspace), _stream(stream)))
+
+
+def moe_act_quantize(x, rows, H, act, mode, m_offsets, E, q, scale, scale_e8m0, workspace,
+                     stream=None):
+    return _check(lib().moe_act_quantize(
+        _ptr(x), rows, H, act, mode, _ptr(m_offsets), E, _ptr(q), _ptr(scale), _ptr(scale_e8m0),
         _ptr(workspace), _stream(stream)))
 
 

@@ -12,6 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libqmoe.so")
 BUILD = os.path.join(HERE, "_build")
+INCLUDE = os.path.normpath(os.path.join(HERE, "..", "include"))      # moe.h, the C ABI
 SOURCES = ["qmoe_api.cpp", "qmoe_align.hip", "qmoe_quant.hip", "qmoe_gemm.hip", "qmoe_combine.hip"]
 
 ARCH = "gfx950"
@@ -20,6 +21,7 @@ FLAGS = [
     # no packed-fp32 VALU instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    f"-I{INCLUDE}",
 ]
 
 

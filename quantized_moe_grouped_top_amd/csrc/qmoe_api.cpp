@@ -1,7 +1,7 @@
 // C ABI of libqmoe.so (declared in include/moe.h): argument validation on the
 // host, then the launches on the caller's stream.  No entry point allocates,
 // frees or synchronises; on a validation error nothing is enqueued.
-#include "../../include/moe.h"
+#include "moe.h"
 
 #include <stdarg.h>
 #include <stdio.h>
@@ -9,6 +9,9 @@
 #include "qmoe_internal.h"
 
 namespace {
+
+// MXFP8 row counts: rows plus the per-expert padding stay within int.
+constexpr int kMxMaxRows = 1 << 30;
 
 thread_local char g_err[512] = "";
 thread_local int g_hip_err = 0;
@@ -138,6 +141,8 @@ int moe_pack_weights(const void *w_q, int E, int N, int K, void *w_packed, hipSt
 int moe_mx_scale_rows(int rows, int E) {
   if (rows < 0 || E < 1 || E > MOE_MAX_EXPERTS)
     return fail(MOE_EINVAL, "moe_mx_scale_rows: rows=%d E=%d", rows, E);
+  if (rows > kMxMaxRows)
+    return fail(MOE_EUNSUPPORTED, "moe_mx_scale_rows: rows=%d exceeds %d", rows, kMxMaxRows);
   ok();
   return rows + E * (qmoe::kMxRowPad - 1);
 }
@@ -177,6 +182,7 @@ int moe_quantize_act(const uint16_t *x, int rows, int K, int mode, const int *m_
   if (mode == MOE_Q_MXFP8) {
     REQUIRE(E >= 1 && E <= MOE_MAX_EXPERTS, MOE_EINVAL, "%s: E=%d", fn, E);
     REQUIRE(K % 32 == 0, MOE_EUNSUPPORTED, "%s: K=%d is not a multiple of 32", fn, K);
+    REQUIRE(rows <= kMxMaxRows, MOE_EUNSUPPORTED, "%s: rows=%d exceeds %d", fn, rows, kMxMaxRows);
     if (rows == 0) return ok();
     REQUIRE(x && q && scale_e8m0 && m_offsets, MOE_EINVAL, "%s: null pointer argument", fn);
     REQUIRE(aligned16(x) && aligned16(q), MOE_EINVAL, "%s: x and q must be 16-byte aligned", fn);
@@ -184,6 +190,38 @@ int moe_quantize_act(const uint16_t *x, int rows, int K, int mode, const int *m_
         qmoe::launch_quant_mx_act_bf16(x, rows, K, m_offsets, E, q, scale_e8m0, stream), fn);
   }
   return fail(MOE_EINVAL, "%s: unknown mode %d", fn, mode);
+}
+
+int moe_act_quantize(const uint16_t *x, int rows, int H, int act, int mode, const int *m_offsets,
+                     int E, uint8_t *q, float *scale, uint8_t *scale_e8m0, void *workspace,
+                     hipStream_t stream) {
+  const char *fn = "moe_act_quantize";
+  REQUIRE(rows >= 0 && H > 0, MOE_EINVAL, "%s: rows=%d H=%d", fn, rows, H);
+  REQUIRE(act == MOE_ACT_SWIGLU || act == MOE_ACT_SRELU, MOE_EINVAL, "%s: unknown activation %d",
+          fn, act);
+  REQUIRE(mode == MOE_Q_FP8_PER_TENSOR || mode == MOE_Q_MXFP8, MOE_EINVAL, "%s: unknown mode %d",
+          fn, mode);
+  const int mult = mode == MOE_Q_MXFP8 ? 32 : 8;
+  REQUIRE(H % mult == 0, MOE_EUNSUPPORTED, "%s: H=%d is not a multiple of %d", fn, H, mult);
+  REQUIRE((long long)rows * H * (act == MOE_ACT_SWIGLU ? 2 : 1) * 2 < (1ll << 40), MOE_EUNSUPPORTED,
+          "%s: input too large", fn);
+  if (mode == MOE_Q_MXFP8) {
+    REQUIRE(E >= 1 && E <= MOE_MAX_EXPERTS, MOE_EINVAL, "%s: E=%d", fn, E);
+    REQUIRE(rows <= kMxMaxRows, MOE_EUNSUPPORTED, "%s: rows=%d exceeds %d", fn, rows, kMxMaxRows);
+  }
+  if (rows == 0) return ok();
+  REQUIRE(x && q, MOE_EINVAL, "%s: null pointer argument", fn);
+  if (mode == MOE_Q_MXFP8) {
+    REQUIRE(scale_e8m0 && m_offsets, MOE_EINVAL, "%s: null scale or m_offsets", fn);
+    REQUIRE(aligned16(x) && aligned16(q), MOE_EINVAL, "%s: x and q must be 16-byte aligned", fn);
+  } else {
+    REQUIRE(scale && workspace, MOE_EINVAL, "%s: null scale or workspace", fn);
+    REQUIRE(aligned16(x) && ((uintptr_t)q & 7u) == 0 && ((uintptr_t)workspace & 3u) == 0,
+            MOE_EINVAL, "%s: x must be 16-byte and q 8-byte aligned", fn);
+  }
+  return hip_status(qmoe::launch_act_quant(x, rows, H, act, mode, m_offsets, E, q, scale,
+                                           scale_e8m0, (float *)workspace, stream),
+                    fn);
 }
 
 int moe_quantize_weights(const float *w, int E, int N, int K, int mode, void *q, float *scale,

@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "moe.h"
+
 namespace qmoe {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -65,6 +67,9 @@ hipError_t launch_quant_int8_rows_f32(const float *w, long long rows, int K, int
                                       float *scale, hipStream_t s);
 hipError_t launch_quant_mx_act_bf16(const uint16_t *x, int rows, int K, const int *m_offsets,
                                     int E, uint8_t *q, uint8_t *sf, hipStream_t s);
+hipError_t launch_act_quant(const uint16_t *x, int rows, int H, int act, int mode,
+                            const int *m_offsets, int E, uint8_t *q, float *scale, uint8_t *sf,
+                            float *ws, hipStream_t s);
 hipError_t launch_quant_mx_rows_f32(const float *w, long long rows, int K, uint8_t *q,
                                     uint8_t *sf, hipStream_t s);
 

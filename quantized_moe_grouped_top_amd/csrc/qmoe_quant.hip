@@ -144,12 +144,8 @@ __global__ __launch_bounds__(kThreads) void quant_int8_rows_kernel(const float *
 }
 
 // ---- MXFP8: one thread per block of 32 values ------------------------------
-// Returns the e8m0 byte and writes the 32 e4m3 codes.
-template <typename Src>
-__device__ __forceinline__ uint32_t mx_block(const Src *src, uint8_t *dst) {
-  float v[32];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) load8(src + 8 * i, v + 8 * i);
+// mx_encode: the e8m0 byte of 32 values (returned) and their 32 e4m3 codes.
+__device__ __forceinline__ uint32_t mx_encode(const float *v, uint8_t *dst) {
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
@@ -170,11 +166,113 @@ __device__ __forceinline__ uint32_t mx_block(const Src *src, uint8_t *dst) {
   return (uint32_t)b;
 }
 
-// Activations with per-expert scale blocks padded to 128 rows.  Work item =
-// (padded scale row p, block kb); pad rows only get a zero scale byte.
-__global__ __launch_bounds__(kThreads) void quant_mx_act_kernel(
-    const uint16_t *__restrict__ x, int rows, int K, const int *__restrict__ m_offsets, int E,
-    uint8_t *__restrict__ q, uint8_t *__restrict__ sf, long long work_bound) {
+template <typename Src>
+__device__ __forceinline__ uint32_t mx_block(const Src *src, uint8_t *dst) {
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) load8(src + 8 * i, v + 8 * i);
+  return mx_encode(v, dst);
+}
+
+// ---- fused activations (float32 arithmetic on bf16 inputs) -------------------
+// SwiGLU: y = silu(g) * u with silu(g) = g / (1 + exp(-g)), the gate g in the
+// first half of the row and u in the second; SReLU: y = max(x, 0)^2 (exact).
+//
+// silu in a few instructions: exp(-g) = 2^t with t = -g * log2(e) carried as
+// an unevaluated sum t_hi + t_lo (t_lo from an fma residual and the low part
+// of log2(e)).  The hardware exp2 takes t_hi and the residual enters to first
+// order, 2^(t_hi + t_lo) = 2^t_hi * (1 + t_lo * ln 2) up to t_lo^2 < 2^-32.
+// The exponent uses g clamped to [-128, 128]: exp(-g) is already 0 or
+// infinite in float32 there, so nothing changes except that t_lo stays finite
+// (the result is then g * u or a signed zero).  With the hardware reciprocal
+// of 1 + 2^t the relative error stays within about 7 float32 units.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  constexpr float kLog2e = 1.44269502162933349609375f;     // float32 nearest log2(e)
+  constexpr float kLog2eLo = 1.9259629911266175e-8f;       // log2(e) - kLog2e
+  constexpr float kLn2 = 0.693147182464599609375f;
+  const float gc = __builtin_amdgcn_fmed3f(g, -128.0f, 128.0f);
+  const float t = -gc * kLog2e;
+  const float t_lo = fmaf(-gc, kLog2e, -t) - gc * kLog2eLo;
+  const float e = __builtin_amdgcn_exp2f(t) * (1.0f + t_lo * kLn2);
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
+template <int kAct>
+__device__ __forceinline__ void act8(const uint16_t *row, int H, int col, float *y) {
+  if constexpr (kAct == MOE_ACT_SWIGLU) {
+    float gt[8], up[8];
+    load8(row + col, gt);
+    load8(row + H + col, up);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = silu_mul(gt[i], up[i]);
+  } else {
+    float v[8];
+    load8(row + col, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float r = fmaxf(v[i], 0.0f);
+      y[i] = r * r;
+    }
+  }
+}
+
+// Sources of the padded-row MXFP8 kernel: 8 consecutive values of row r
+// starting at column col (col % 8 == 0).
+// kUnroll chunks per lane are loaded before any is encoded (64 bytes of input
+// in flight per lane).
+struct Bf16Rows {
+  static constexpr int kUnroll = 4;
+  const uint16_t *x;
+  int K;
+  __device__ __forceinline__ void operator()(long long r, int col, float *v) const {
+    load8(x + r * K + col, v);
+  }
+};
+template <int kAct>
+struct ActRows {                   // activation of rows of width 2H (SwiGLU) or H
+  static constexpr int kUnroll = kAct == MOE_ACT_SWIGLU ? 2 : 4;
+  const uint16_t *x;
+  int H;
+  __device__ __forceinline__ void operator()(long long r, int col, float *v) const {
+    act8<kAct>(x + r * (kAct == MOE_ACT_SWIGLU ? 2ll * H : (long long)H), H, col, v);
+  }
+};
+
+__device__ __forceinline__ uint32_t e8m0_of_amax(float amax) {
+  // shared exponent floor(log2 amax) - 8 as an e8m0 byte, clamped to [0, 254]
+  const int b = (int)((__builtin_bit_cast(uint32_t, amax) >> 23) & 0xFFu) - 8;
+  return (uint32_t)(b < 0 ? 0 : (b > 254 ? 254 : b));
+}
+
+// One 8-value chunk of a 32-value block whose other chunks sit in the three
+// neighbouring lanes (lanes 4a .. 4a+3): the block amax is reduced over the
+// four lanes, the codes are stored, and the block's scale byte is returned.
+__device__ __forceinline__ uint32_t mx_chunk(const float *v, uint8_t *dst) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  m = fmaxf(m, __shfl_xor(m, 1));
+  m = fmaxf(m, __shfl_xor(m, 2));
+  const uint32_t b = e8m0_of_amax(m);
+  const float f = __builtin_bit_cast(float, (254u - b) << 23);   // 2^(127 - b)
+  i32x2 o;
+  o[0] = (int)f32x4_to_e4m3x4(v[0] * f, v[1] * f, v[2] * f, v[3] * f);
+  o[1] = (int)f32x4_to_e4m3x4(v[4] * f, v[5] * f, v[6] * f, v[7] * f);
+  *reinterpret_cast<i32x2 *>(dst) = o;
+  return b;
+}
+
+// MXFP8 of expert-concatenated rows [rows, K] with the scale rows of each
+// expert padded to a multiple of 128 (pad rows get zero scale bytes).  One
+// wavefront per padded scale row p (wave-uniform, so the expert of p is found
+// by a uniform forward scan as p grows); lane l takes the 8-value chunks
+// c8 = l, l + 64, ..., so four neighbouring lanes hold one block and a
+// wavefront moves 512 contiguous values of the row per step.  K % 32 == 0
+// keeps every four-lane group inside the row together.
+template <class Src>
+__global__ __launch_bounds__(kThreads) void mx_padded_kernel(
+    Src src, int rows, int K, const int *__restrict__ m_offsets, int E,
+    uint8_t *__restrict__ q, uint8_t *__restrict__ sf, int prow_bound) {
   __shared__ int s_mo[kMaxExperts + 1];
   __shared__ int s_po[kMaxExperts + 1];
   for (int e = threadIdx.x; e <= E; e += kThreads) s_mo[e] = m_offsets[e];
@@ -188,25 +286,93 @@ __global__ __launch_bounds__(kThreads) void quant_mx_act_kernel(
     s_po[E] = acc;
   }
   __syncthreads();
-  const int nb = K / kMxBlock;
-  const long long work = (long long)s_po[E] * nb;
-  const long long lim = work < work_bound ? work : work_bound;
-  for (long long i = blockIdx.x * (long long)kThreads + threadIdx.x; i < lim;
+  const int lane = threadIdx.x & 63;
+  const int n8 = K / 8, nb = K / kMxBlock;
+  const int prows = s_po[E] < prow_bound ? s_po[E] : prow_bound;
+  const int waves = gridDim.x * (kThreads / 64);
+  int e = 0;
+  for (int p = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); p < prows; p += waves) {
+    while (e < E - 1 && s_po[e + 1] <= p) ++e;
+    const int local = p - s_po[e];
+    const long long r = (long long)s_mo[e] + local;
+    const bool live = local >= 0 && local < s_mo[e + 1] - s_mo[e] && r >= 0 && r < rows;
+    uint8_t *sf_row = sf + (long long)p * nb;
+    if (live) {
+      uint8_t *q_row = q + r * K;
+      constexpr int U = Src::kUnroll;
+      int c8 = lane;
+      for (; c8 + 64 * (U - 1) < n8; c8 += 64 * U) {
+        float v[U][8];
+#pragma unroll
+        for (int j = 0; j < U; ++j) src(r, 8 * (c8 + 64 * j), v[j]);
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+          const uint32_t b = mx_chunk(v[j], q_row + 8 * (c8 + 64 * j));
+          if ((c8 & 3) == 0) sf_row[(c8 + 64 * j) >> 2] = (uint8_t)b;
+        }
+      }
+      for (; c8 < n8; c8 += 64) {
+        float v[8];
+        src(r, 8 * c8, v);
+        const uint32_t b = mx_chunk(v, q_row + 8 * c8);
+        if ((c8 & 3) == 0) sf_row[c8 >> 2] = (uint8_t)b;
+      }
+    } else {
+      for (int kb = lane; kb < nb; kb += 64) sf_row[kb] = 0;
+    }
+  }
+}
+
+// Fused activation + fp8 per tensor, pass 1: partial amax of the activation.
+template <int kAct>
+__global__ __launch_bounds__(kThreads) void act_amax_kernel(const uint16_t *__restrict__ x,
+                                                            int rows, int H,
+                                                            float *__restrict__ ws) {
+  __shared__ float red[kThreads / 64];
+  const long long in_w = kAct == MOE_ACT_SWIGLU ? 2ll * H : (long long)H;
+  const int n8 = H / 8;
+  const long long work = (long long)rows * n8;
+  float m = 0.0f;
+  for (long long i = blockIdx.x * (long long)kThreads + threadIdx.x; i < work;
        i += (long long)gridDim.x * kThreads) {
-    const int p = (int)(i / nb);
-    const int kb = (int)(i - (long long)p * nb);
-    int lo = 0, hi = E - 1;                       // last e with s_po[e] <= p
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_po[mid] <= p) lo = mid; else hi = mid - 1;
-    }
-    const int local = p - s_po[lo];
-    uint32_t b = 0;
-    const long long r = (long long)s_mo[lo] + local;
-    if (local < s_mo[lo + 1] - s_mo[lo] && r >= 0 && r < rows) {
-      b = mx_block(x + r * K + kb * kMxBlock, q + r * K + kb * kMxBlock);
-    }
-    sf[(long long)p * nb + kb] = (uint8_t)b;
+    const long long r = i / n8;
+    const int c = (int)(i - r * n8) * 8;
+    float y[8];
+    act8<kAct>(x + r * in_w, H, c, y);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(y[j]));
+  }
+  m = block_max(m, red);
+  if (threadIdx.x == 0) ws[blockIdx.x] = m;
+}
+
+// Pass 2: reduce the partials, recompute the activation and quantize it.
+template <int kAct>
+__global__ __launch_bounds__(kThreads) void act_fp8_kernel(const uint16_t *__restrict__ x,
+                                                           int rows, int H, int parts,
+                                                           const float *__restrict__ ws,
+                                                           uint8_t *__restrict__ q,
+                                                           float *__restrict__ scale) {
+  __shared__ float red[kThreads / 64];
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < parts; i += kThreads) m = fmaxf(m, ws[i]);
+  const float amax = block_max(m, red);
+  const float s = amax > 0.0f ? (float)((double)amax / 448.0) : 1.0f;
+  const float inv = (float)(1.0 / (double)s);
+  if (blockIdx.x == 0 && threadIdx.x == 0) scale[0] = s;
+  const long long in_w = kAct == MOE_ACT_SWIGLU ? 2ll * H : (long long)H;
+  const int n8 = H / 8;
+  const long long work = (long long)rows * n8;
+  for (long long i = blockIdx.x * (long long)kThreads + threadIdx.x; i < work;
+       i += (long long)gridDim.x * kThreads) {
+    const long long r = i / n8;
+    const int c = (int)(i - r * n8) * 8;
+    float y[8];
+    act8<kAct>(x + r * in_w, H, c, y);
+    i32x2 out;
+    out[0] = (int)f32x4_to_e4m3x4(y[0] * inv, y[1] * inv, y[2] * inv, y[3] * inv);
+    out[1] = (int)f32x4_to_e4m3x4(y[4] * inv, y[5] * inv, y[6] * inv, y[7] * inv);
+    *reinterpret_cast<i32x2 *>(q + r * H + c) = out;
   }
 }
 
@@ -291,11 +457,44 @@ hipError_t launch_quant_int8_rows_f32(const float *w, long long rows, int K, int
   return hipGetLastError();
 }
 
+// One wavefront per padded scale row; a workgroup of 4 wavefronts.
+static unsigned mx_padded_grid(int prow_bound) {
+  const int per_block = kThreads / 64;
+  const int blocks = (prow_bound + per_block - 1) / per_block;
+  return (unsigned)(blocks < 4096 ? (blocks > 0 ? blocks : 1) : 4096);
+}
+
 hipError_t launch_quant_mx_act_bf16(const uint16_t *x, int rows, int K, const int *m_offsets,
                                     int E, uint8_t *q, uint8_t *sf, hipStream_t s) {
-  const long long bound = ((long long)rows + (long long)E * (kMxRowPad - 1)) * (K / kMxBlock);
-  hipLaunchKernelGGL(quant_mx_act_kernel, dim3(grid_for(bound, 16384)), dim3(kThreads), 0, s, x,
-                     rows, K, m_offsets, E, q, sf, bound);
+  const int prow_bound = rows + E * (kMxRowPad - 1);
+  hipLaunchKernelGGL(mx_padded_kernel<Bf16Rows>, dim3(mx_padded_grid(prow_bound)), dim3(kThreads),
+                     0, s, Bf16Rows{x, K}, rows, K, m_offsets, E, q, sf, prow_bound);
+  return hipGetLastError();
+}
+
+hipError_t launch_act_quant(const uint16_t *x, int rows, int H, int act, int mode,
+                            const int *m_offsets, int E, uint8_t *q, float *scale, uint8_t *sf,
+                            float *ws, hipStream_t s) {
+  if (mode == MOE_Q_MXFP8) {
+    const int prow_bound = rows + E * (kMxRowPad - 1);
+    const dim3 grid(mx_padded_grid(prow_bound));
+    if (act == MOE_ACT_SWIGLU)
+      hipLaunchKernelGGL(mx_padded_kernel<ActRows<MOE_ACT_SWIGLU>>, grid, dim3(kThreads), 0, s,
+                         ActRows<MOE_ACT_SWIGLU>{x, H}, rows, H, m_offsets, E, q, sf, prow_bound);
+    else
+      hipLaunchKernelGGL(mx_padded_kernel<ActRows<MOE_ACT_SRELU>>, grid, dim3(kThreads), 0, s,
+                         ActRows<MOE_ACT_SRELU>{x, H}, rows, H, m_offsets, E, q, sf, prow_bound);
+    return hipGetLastError();
+  }
+  const long long items = (long long)rows * (H / 8);
+  const int parts = grid_for(items, kAmaxPartials);
+  auto k1 = act == MOE_ACT_SWIGLU ? act_amax_kernel<MOE_ACT_SWIGLU> : act_amax_kernel<MOE_ACT_SRELU>;
+  hipLaunchKernelGGL(k1, dim3(parts), dim3(kThreads), 0, s, x, rows, H, ws);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  auto k2 = act == MOE_ACT_SWIGLU ? act_fp8_kernel<MOE_ACT_SWIGLU> : act_fp8_kernel<MOE_ACT_SRELU>;
+  hipLaunchKernelGGL(k2, dim3(grid_for(items, 8192)), dim3(kThreads), 0, s, x, rows, H, parts, ws,
+                     q, scale);
   return hipGetLastError();
 }
 

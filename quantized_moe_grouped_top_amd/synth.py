@@ -82,6 +82,14 @@ def make_activations(M, K, seed, device="cpu"):
     return torch.randn(M, K, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
 
 
+def make_act_input(rows, width, seed, std=1.0, device="cpu"):
+    """bf16 [rows, width], N(0, std^2): the input of the activation between
+    the up and the down projection ([rows, 2H] for SwiGLU, [rows, H] else)."""
+    g = _gen(device, seed)
+    x = torch.randn(rows, width, generator=g, device=device, dtype=torch.float32)
+    return (x * std).to(torch.bfloat16)
+
+
 def make_weights(E, N, K, seed, device="cpu"):
     """float32 [E, N, K], N(0, 1/sqrt(K)); drawn one expert at a time so the
     values do not depend on how much memory is free."""

@@ -315,6 +315,196 @@ def test_mxfp8_full_size_sampled(wl):
 
 
 # ----------------------------------------------------------------------------
+# fused activation + quantization (SwiGLU / SReLU -> MXFP8 or per-tensor fp8)
+# ----------------------------------------------------------------------------
+# SwiGLU is evaluated in float32 on the device with the device exp, so its
+# float32 value may differ from the oracle's correctly rounded one by a few
+# units: the check allows, per element, the codes of every value within a
+# relative ACT_EPS of the exact activation (and per block or tensor the scales
+# of the amax within ACT_EPS), and reports how many codes differ from the
+# oracle's.  SReLU of bf16 inputs is exact in float32 and compared bit-exactly.
+ACT_EPS = 2.0 ** -19
+ACT_NAMES = {O.ACT_SWIGLU: "swiglu", O.ACT_SRELU: "srelu"}
+
+
+def _act_run(x, rows, H, act, mode, mo=None, E=1):
+    q = torch.full((rows, H), 0x5A, dtype=torch.uint8, device=DEV)
+    s = torch.full((1,), -1.0, dtype=torch.float32, device=DEV)
+    sf = ws = None
+    if mode == qm.MOE_Q_MXFP8:
+        n_sf = qm.moe_mx_scale_rows(rows, E)
+        sf = torch.full((max(n_sf, 1), H // 32), 0xA5, dtype=torch.uint8, device=DEV)
+    else:
+        ws = torch.empty(qm.moe_quantize_workspace_bytes(mode, 1), dtype=torch.uint8, device=DEV)
+    qm.moe_act_quantize(x, rows, H, act, mode, mo, E, q, s, sf, ws)
+    torch.cuda.synchronize()
+    return q, s, sf
+
+
+def _code_bounds(scaled64):
+    """Decoded e4m3 values of the lowest and highest codes of the values within
+    a relative ACT_EPS of scaled64 (the encoder is monotone)."""
+    a = scaled64 * (1.0 - ACT_EPS)
+    b = scaled64 * (1.0 + ACT_EPS)
+    lo, hi = np.minimum(a, b), np.maximum(a, b)
+    return F.e4m3_decode(F.e4m3_encode(lo)), F.e4m3_decode(F.e4m3_encode(hi))
+
+
+def _check_codes(q, scaled64, what):
+    got = F.e4m3_decode(q)
+    lo, hi = _code_bounds(scaled64)
+    bad = (got < lo) | (got > hi)
+    assert not bad.any(), f"{what}: {int(bad.sum())} codes outside the allowed range"
+
+
+def _check_act_mx(x_bits, mo_np, act, q, sf, rows_sel, what):
+    """MXFP8 of the activation on the rows rows_sel (all rows of a small
+    case, sampled rows of a large one) and every pad row of the scales."""
+    H = q.shape[1]
+    po = O.mx_padded_offsets(mo_np)
+    e_of = np.searchsorted(mo_np, rows_sel, side="right") - 1
+    sf_rows = po[e_of] + rows_sel - mo_np[e_of]
+    q_ref, sf_ref = O.act_quantize_mxfp8(x_bits[rows_sel], np.array([0, rows_sel.size]), act)
+    sf_ref = sf_ref[:rows_sel.size]
+    q_got, sf_got = q[rows_sel], sf[sf_rows]
+    pad = np.zeros(sf.shape[0], bool)          # rows past po[-1] are not the kernel's
+    pad[:po[-1]] = True
+    for e in range(len(mo_np) - 1):
+        pad[po[e]:po[e] + mo_np[e + 1] - mo_np[e]] = False
+    assert not sf[pad].any(), f"{what}: nonzero scale bytes on pad rows"
+    if act == O.ACT_SRELU:
+        np.testing.assert_array_equal(sf_got, sf_ref, err_msg=f"{what} scales")
+        np.testing.assert_array_equal(q_got, q_ref, err_msg=f"{what} codes")
+        return
+    y = O.act_values(x_bits[rows_sel], act)
+    blk = y.reshape(rows_sel.size, H // 32, 32)
+    amax = np.max(np.abs(blk), axis=-1)
+    b_lo = O.mx_scale_byte(np.float32(amax * (1 - ACT_EPS)))
+    b_hi = O.mx_scale_byte(np.float32(amax * (1 + ACT_EPS)))
+    assert np.all((sf_got >= b_lo) & (sf_got <= b_hi)), f"{what}: scale bytes out of range"
+    scaled = blk * np.ldexp(1.0, 127 - sf_got.astype(np.int64))[..., None]
+    _check_codes(q_got.reshape(blk.shape), scaled, what)
+    print(f"  {what}: {np.mean(q_got != q_ref):.2e} of codes, {np.mean(sf_got != sf_ref):.2e} "
+          f"of scale bytes differ from the oracle's", flush=True)
+
+
+def _act_amax(x_bits, act, chunk=4096):
+    """max |activation| over every row, in float64, a chunk of rows at a time."""
+    return max((float(np.max(np.abs(O.act_values(x_bits[i:i + chunk], act))))
+                for i in range(0, len(x_bits), chunk)), default=0.0)
+
+
+def _check_act_fp8(x_bits, act, q, s, rows_sel, what):
+    """Per-tensor fp8 of the activation: the scale from the amax over every row,
+    the codes on rows_sel (every row of a small case)."""
+    s_got = np.float32(s.item())
+    if act == O.ACT_SRELU and rows_sel.size == len(x_bits):
+        q_ref, s_ref = O.act_quantize_fp8(x_bits, act)
+        assert s_got == s_ref, (what, s_got, s_ref)
+        np.testing.assert_array_equal(q, q_ref, err_msg=f"{what} codes")
+        return
+    amax = _act_amax(x_bits, act)
+    y = O.act_values(x_bits[rows_sel], act)
+    if act == O.ACT_SRELU:                       # exact: the amax is a float32 value
+        s_ref = O.fp8_tensor_scale(np.float32(amax))
+        assert s_got == s_ref, (what, s_got, s_ref)
+        np.testing.assert_array_equal(q[rows_sel], O.fp8_quantize_with_scale(y.astype(np.float32), s_ref),
+                                      err_msg=f"{what} codes")
+        return
+    s_lo = O.fp8_tensor_scale(np.float32(amax * (1 - ACT_EPS)))
+    s_hi = O.fp8_tensor_scale(np.float32(amax * (1 + ACT_EPS)))
+    assert s_lo <= s_got <= s_hi, (what, s_got, s_lo, s_hi)
+    inv = float(np.float32(np.float32(1.0) / s_got))
+    _check_codes(q[rows_sel], y * inv, what)
+    q_ref = O.fp8_quantize_with_scale(y.astype(np.float32), s_got)
+    print(f"  {what}: {np.mean(q[rows_sel] != q_ref):.2e} of codes differ from the oracle's "
+          f"(same scale)", flush=True)
+
+
+ACT_MX_SMALL = [((5, 130, 0, 77), 256, 1.0), ((128,), 64, 30.0), ((1,), 2048, 3.0),
+                ((0, 0, 3), 32, 1.0)]
+
+
+@pytest.mark.parametrize("act", [O.ACT_SWIGLU, O.ACT_SRELU], ids=["swiglu", "srelu"])
+@pytest.mark.parametrize("seg,H,std", ACT_MX_SMALL,
+                         ids=[f"s{'-'.join(map(str, c[0]))}_h{c[1]}" for c in ACT_MX_SMALL])
+def test_act_quantize_mxfp8_small(act, seg, H, std):
+    what = f"act {ACT_NAMES[act]} mxfp8 seg={seg} H={H}"
+    _announce(what)
+    rows, E = sum(seg), len(seg)
+    width = 2 * H if act == O.ACT_SWIGLU else H
+    x = synth.make_act_input(rows, width, synth.seed_of(what), std)
+    mo = synth.make_segments(seg)
+    q, _, sf = _act_run(x.to(DEV), rows, H, act, qm.MOE_Q_MXFP8, mo.to(DEV), E)
+    _check_act_mx(bits16(x), mo.numpy().astype(np.int64), act, q.cpu().numpy(),
+                  sf.cpu().numpy(), np.arange(rows), what)
+
+
+def test_act_quantize_srelu_tiny_and_huge_inputs():
+    """SReLU of inputs whose squares are float32 subnormals or near the top of
+    the range: the scale byte comes from the exponent field (0 for a
+    subnormal amax) and the codes stay exact."""
+    _announce("act srelu mxfp8 extreme magnitudes")
+    H, rows = 64, 4
+    v = np.array([1e-20, 3e-22, -1e-20, 2e-19, 1e18, -1e18, 1.5e19, 0.0], np.float32)
+    x = torch.from_numpy(np.resize(v, rows * H).reshape(rows, H).copy()).to(torch.bfloat16)
+    x[0, :32] = torch.tensor(3e-21)              # a block of subnormal squares only
+    mo = synth.make_segments((rows,))
+    q, _, sf = _act_run(x.to(DEV), rows, H, O.ACT_SRELU, qm.MOE_Q_MXFP8, mo.to(DEV), 1)
+    _check_act_mx(bits16(x), mo.numpy().astype(np.int64), O.ACT_SRELU, q.cpu().numpy(),
+                  sf.cpu().numpy(), np.arange(rows), "srelu extremes")
+
+
+ACT_FP8_SMALL = [(333, 1024, 1.0), (7, 8, 30.0), (64, 128, 1e-3)]
+
+
+@pytest.mark.parametrize("act", [O.ACT_SWIGLU, O.ACT_SRELU], ids=["swiglu", "srelu"])
+@pytest.mark.parametrize("rows,H,std", ACT_FP8_SMALL, ids=[f"r{c[0]}_h{c[1]}" for c in ACT_FP8_SMALL])
+def test_act_quantize_fp8_small(act, rows, H, std):
+    what = f"act {ACT_NAMES[act]} fp8 rows={rows} H={H}"
+    _announce(what)
+    width = 2 * H if act == O.ACT_SWIGLU else H
+    x = synth.make_act_input(rows, width, synth.seed_of(what), std)
+    q, s, _ = _act_run(x.to(DEV), rows, H, act, qm.MOE_Q_FP8_PER_TENSOR)
+    _check_act_fp8(bits16(x), act, q.cpu().numpy(), s, np.arange(rows), what)
+
+
+def test_act_quantize_empty():
+    _announce("act quantize, zero rows")
+    x = torch.zeros(1, 64, dtype=torch.bfloat16, device=DEV)
+    for mode in (qm.MOE_Q_MXFP8, qm.MOE_Q_FP8_PER_TENSOR):
+        mo = torch.zeros(3, dtype=torch.int32, device=DEV)
+        q, s, sf = _act_run(x, 0, 32, O.ACT_SWIGLU, mode, mo, 2)
+        assert s.item() == -1.0                  # nothing written
+
+
+@pytest.mark.parametrize("act", [O.ACT_SWIGLU, O.ACT_SRELU], ids=["swiglu", "srelu"])
+@pytest.mark.parametrize("mode", [qm.MOE_Q_MXFP8, qm.MOE_Q_FP8_PER_TENSOR], ids=["mxfp8", "fp8"])
+def test_act_quantize_full_size_sampled(act, mode):
+    """The activation between the up (N = 2H = 4096) and the down projection
+    of the 8 x 4000-row MXFP8 layer: 32000 rows, H = 2048; sampled rows (the
+    per-tensor scale from the amax over every row)."""
+    wl = synth.WORKLOADS["mxfp8_8x4000_k4096_n4096"]
+    H = wl.N // 2 if act == O.ACT_SWIGLU else wl.N
+    rows = wl.M
+    what = f"act {ACT_NAMES[act]} {'mxfp8' if mode == qm.MOE_Q_MXFP8 else 'fp8'} {rows}x{H}"
+    _announce(what)
+    x = synth.make_act_input(rows, wl.N, synth.seed_of(what), 1.0)
+    mo = synth.make_segments(wl.seg)
+    q, s, sf = _act_run(x.to(DEV), rows, H, act, mode, mo.to(DEV), wl.E)
+    rng = np.random.default_rng(7)
+    mo_np = mo.numpy().astype(np.int64)
+    rows_sel = pick(rows, 96, rng, must=[0, rows - 1, *mo_np[1:-1], *(mo_np[1:-1] - 1)])
+    x_bits = bits16(x)
+    if mode == qm.MOE_Q_MXFP8:
+        _check_act_mx(x_bits, mo_np, act, q.cpu().numpy(), sf.cpu().numpy(), rows_sel, what)
+    else:
+        _check_act_fp8(x_bits, act, q.cpu().numpy(), s, rows_sel, what)
+    del x, q, sf
+    torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------
 # codecs through the library
 # ----------------------------------------------------------------------------
 def _structured_values():

@@ -44,6 +44,12 @@ def alg_bytes(wl, active_experts=None):
     and scale byte read once, every per-slot output written once as bf16."""
     E = wl.E if active_experts is None else active_experts
     M, K, N = wl.M, wl.K, wl.N
+    if wl.fmt.startswith("act_"):
+        # fused activation + quantization: the bf16 input [M, K] read once, the
+        # codes [M, N] and the scales written once (MXFP8: per-expert padded
+        # scale rows of N/32 bytes; fp8: one float)
+        sf = 4 if wl.fmt == "act_fp8" else sum(-(-m // 128) * 128 for m in wl.seg) * (N // 32)
+        return 2 * M * K + M * N + sf
     if wl.fmt == "fp8":
         return M * K + E * N * K + 4 * (E + 1) + M * wl.top_k * N * 2
     if wl.fmt == "int8":
@@ -121,8 +127,28 @@ def cpu_baseline(wl, case, target_s):
     from oracle import formats as F
     from oracle import moe as O
 
-    w = case["w"].cpu().numpy()
     x = case["x"].view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    if wl.fmt.startswith("act_"):
+        act = O.ACT_SWIGLU if wl.act == "swiglu" else O.ACT_SRELU
+        mo = case["m_offsets"].cpu().numpy()
+        rows = max(1, min(wl.M, 2000))            # a bounded sample of whole rows
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            if wl.fmt == "act_mxfp8":
+                O.act_quantize_mxfp8(x[:rows], [0, rows], act)
+            else:
+                O.act_quantize_fp8(x[:rows], act)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= target_s:
+                break
+        per = el / reps * wl.M / rows
+        return {"value": round(alg_bytes(wl) / per / 1e9, 3), "unit": "GB/s", "cores": threads,
+                "kind": "oracle",
+                "sample": f"the first {rows} of {wl.M} rows, {reps} time(s) in {el:.1f} s, "
+                          f"scaled to the whole input (numpy float64)"}
+    w = case["w"].cpu().numpy()
     if wl.fmt == "mxfp8":
         wq, wsf = O.quantize_weight_mxfp8(w)
         mo = case["m_offsets"].cpu().numpy()
@@ -130,7 +156,6 @@ def cpu_baseline(wl, case, target_s):
         wq, ws = (O.quantize_weight_fp8 if wl.fmt == "fp8" else O.quantize_weight_int8)(w)
         lg = case["logits"].cpu().numpy()
     del w
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
     reps, t0 = 0, time.perf_counter()
     while True:
         if wl.fmt == "mxfp8":
@@ -174,12 +199,28 @@ def main():
     torch.cuda.set_device(0)
     wl = synth.WORKLOADS[args.workload]
     case = synth.make_case(wl, 0, device="cuda")
-    w_q, w_s = runner.quantize_weights(case["w"], wl.fmt)
-    if wl.fmt != "mxfp8":
-        w_q = runner.pack_weights(w_q)              # tiled layout: one HBM block per stage
-    copies = args.copies or max(2, -(-(1 << 30) // w_q.numel()))
-    weights = [(w_q, w_s)] + [(w_q.clone(), w_s.clone()) for _ in range(copies - 1)]
-    if wl.fmt == "mxfp8":
+    if wl.fmt.startswith("act_"):
+        # input copies rotate so that no step finds its input in a cache
+        copies = args.copies or max(2, -(-(1 << 30) // (2 * case["x"].numel())))
+        xs = [case["x"]] + [case["x"].clone() for _ in range(copies - 1)]
+        moe = runner.ActQuant(wl.M, wl.N, wl.E, wl.act, wl.fmt[4:])
+        mo = case["m_offsets"]
+
+        def step(i, ev):
+            if ev is not None:
+                ev[0].record()
+            moe(xs[i % copies], mo)
+            if ev is not None:
+                ev[1].record()
+    else:
+        w_q, w_s = runner.quantize_weights(case["w"], wl.fmt)
+        if wl.fmt != "mxfp8":
+            w_q = runner.pack_weights(w_q)          # tiled layout: one HBM block per stage
+        copies = args.copies or max(2, -(-(1 << 30) // w_q.numel()))
+        weights = [(w_q, w_s)] + [(w_q.clone(), w_s.clone()) for _ in range(copies - 1)]
+    if wl.fmt.startswith("act_"):
+        pass
+    elif wl.fmt == "mxfp8":
         moe = runner.MxMoE(wl.M, wl.K, wl.N, wl.E)
         mo = case["m_offsets"]
 
@@ -220,13 +261,15 @@ def main():
     gemm_ms = sum(a.elapsed_time(b) for a, b in events) / args.steps
 
     active = wl.E
-    if wl.fmt != "mxfp8":
+    if wl.fmt in ("fp8", "int8"):
         ids = moe.topk_ids.cpu()
         active = int(torch.unique(ids).numel())
     nbytes = alg_bytes(wl, active)
     ms = elapsed * 1e3 / args.steps
-    dtype = {"fp8": "fp8", "int8": "bf16", "mxfp8": "mxfp8"}[wl.fmt]
-    bound = "hbm" if wl.flops / nbytes < 600 else "mfma"
+    dtype = {"fp8": "fp8", "int8": "bf16", "mxfp8": "mxfp8", "act_fp8": "fp8",
+             "act_mxfp8": "mxfp8"}[wl.fmt]
+    is_act = wl.fmt.startswith("act_")
+    bound = "hbm" if is_act or wl.flops / nbytes < 600 else "mfma"
     if bound == "hbm":
         achieved = nbytes / (gemm_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -236,21 +279,25 @@ def main():
         peak = MFMA_PEAK_TFLOPS[dtype]
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
-    roof.update({"traffic": recorded_traffic(wl.name), "kernel": "grouped GEMM", "kernel_us": round(gemm_ms * 1e3, 2),
-                 "alg_bytes": int(nbytes), "flops": int(wl.flops)})
+    roof.update({"traffic": recorded_traffic(wl.name),
+                 "kernel": "fused activation + quantization" if is_act else "grouped GEMM",
+                 "kernel_us": round(gemm_ms * 1e3, 2), "alg_bytes": int(nbytes),
+                 "flops": None if is_act else int(wl.flops)})
     line = {
         "metric": "TFLOPS and HBM GB/s (% of MI355X roofline) for quantized MoE GEMM, E=8 top_k=2",
         "value": round(nbytes / (ms * 1e-3) / 1e9, 2),
         "unit": "GB/s",
-        "tflops": round(wl.flops / (ms * 1e-3) / 1e12, 3),
+        "tflops": None if is_act else round(wl.flops / (ms * 1e-3) / 1e12, 3),
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": dtype, "data": "synthetic (seeded N(0,1) activations and logits, N(0,1/sqrt(K)) weights)",
         "config": {"workload": wl.name, "format": wl.fmt, "M": wl.M, "K": wl.K, "N": wl.N,
-                   "E": wl.E, "top_k": wl.top_k, "weight_copies": copies,
+                   "E": wl.E, "top_k": wl.top_k,
+                   ("input_copies" if is_act else "weight_copies"): copies,
                    "block_m": getattr(moe, "block_m", None),
-                   "weight_layout": "tiled" if wl.fmt != "mxfp8" else "rowmajor"},
+                   "weight_layout": None if is_act else
+                   ("tiled" if wl.fmt != "mxfp8" else "rowmajor")},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

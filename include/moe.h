@@ -190,7 +190,7 @@ int moe_quantize_act(const uint16_t *x, int rows, int K, int mode,
  * workspace as for moe_quantize_act with K = H.
  *
  * x must be 16-byte aligned; H must be a multiple of 32 (MXFP8) or 8 (fp8);
- * MXFP8 takes at most 2^30 rows.  rows = 0 is valid. */
+ * at most 2^30 rows.  rows = 0 is valid. */
 int moe_act_quantize(const uint16_t *x, int rows, int H, int act, int mode,
                      const int *m_offsets, int E, uint8_t *q, float *scale,
                      uint8_t *scale_e8m0, void *workspace, hipStream_t stream);

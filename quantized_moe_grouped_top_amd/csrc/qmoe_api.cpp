@@ -205,10 +205,8 @@ int moe_act_quantize(const uint16_t *x, int rows, int H, int act, int mode, cons
   REQUIRE(H % mult == 0, MOE_EUNSUPPORTED, "%s: H=%d is not a multiple of %d", fn, H, mult);
   REQUIRE((long long)rows * H * (act == MOE_ACT_SWIGLU ? 2 : 1) * 2 < (1ll << 40), MOE_EUNSUPPORTED,
           "%s: input too large", fn);
-  if (mode == MOE_Q_MXFP8) {
-    REQUIRE(E >= 1 && E <= MOE_MAX_EXPERTS, MOE_EINVAL, "%s: E=%d", fn, E);
-    REQUIRE(rows <= kMxMaxRows, MOE_EUNSUPPORTED, "%s: rows=%d exceeds %d", fn, rows, kMxMaxRows);
-  }
+  REQUIRE(rows <= kMxMaxRows, MOE_EUNSUPPORTED, "%s: rows=%d exceeds %d", fn, rows, kMxMaxRows);
+  if (mode == MOE_Q_MXFP8) REQUIRE(E >= 1 && E <= MOE_MAX_EXPERTS, MOE_EINVAL, "%s: E=%d", fn, E);
   if (rows == 0) return ok();
   REQUIRE(x && q, MOE_EINVAL, "%s: null pointer argument", fn);
   if (mode == MOE_Q_MXFP8) {

@@ -37,14 +37,18 @@ __device__ __forceinline__ float block_max(float v, float *red) {
   return r;
 }
 
-// 8 consecutive source values as float
-__device__ __forceinline__ void load8(const uint16_t *p, float *v) {
-  const i32x4 raw = *reinterpret_cast<const i32x4 *>(p);
+// 8 bf16 values (16 bytes) as float
+__device__ __forceinline__ void unpack8(const i32x4 raw, float *v) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     v[2 * i] = __builtin_bit_cast(float, (uint32_t)raw[i] << 16);
     v[2 * i + 1] = __builtin_bit_cast(float, (uint32_t)raw[i] & 0xFFFF0000u);
   }
+}
+
+// 8 consecutive source values as float
+__device__ __forceinline__ void load8(const uint16_t *p, float *v) {
+  unpack8(*reinterpret_cast<const i32x4 *>(p), v);
 }
 __device__ __forceinline__ void load8(const float *p, float *v) {
   const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
@@ -56,8 +60,32 @@ __device__ __forceinline__ void load8(const float *p, float *v) {
   }
 }
 
+// Raw 16- or 32-byte loads of 8 consecutive values and their conversion, so
+// that several loads can be issued before the first is used.
+template <typename Src> struct Raw8;
+template <> struct Raw8<uint16_t> { i32x4 a; };
+template <> struct Raw8<float> { f32x4 a, b; };
+__device__ __forceinline__ Raw8<uint16_t> ld8(const uint16_t *p) {
+  return {*reinterpret_cast<const i32x4 *>(p)};
+}
+__device__ __forceinline__ Raw8<float> ld8(const float *p) {
+  return {*reinterpret_cast<const f32x4 *>(p), *reinterpret_cast<const f32x4 *>(p + 4)};
+}
+__device__ __forceinline__ void cvt8(const Raw8<uint16_t> &r, float *v) { unpack8(r.a, v); }
+__device__ __forceinline__ void cvt8(const Raw8<float> &r, float *v) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = r.a[i];
+    v[4 + i] = r.b[i];
+  }
+}
+
+constexpr int kFlatUnroll = 4;     // 8-value items in flight per thread
+
 // ---- fp8 per tensor: pass 1, partial amax ------------------------------------
 // grid (P, T): tensor t = blockIdx.y covers [t*per, (t+1)*per); per % 8 == 0.
+// Thread i takes the 8-value items i, i + stride, ... (stride = all threads of
+// the tensor), kFlatUnroll of them loaded before any is used.
 template <typename Src>
 __global__ __launch_bounds__(kThreads) void amax_partials_kernel(const Src *__restrict__ x,
                                                                  long long per,
@@ -65,13 +93,24 @@ __global__ __launch_bounds__(kThreads) void amax_partials_kernel(const Src *__re
   __shared__ float red[kThreads / 64];
   const Src *base = x + (long long)blockIdx.y * per;
   const long long n8 = per / 8;
+  const long long stride = (long long)gridDim.x * kThreads;
   float m = 0.0f;
-  for (long long i = blockIdx.x * (long long)kThreads + threadIdx.x; i < n8;
-       i += (long long)gridDim.x * kThreads) {
-    float v[8];
-    load8(base + i * 8, v);
+  for (long long i0 = blockIdx.x * (long long)kThreads + threadIdx.x; i0 < n8;
+       i0 += kFlatUnroll * stride) {
+    Raw8<Src> raw[kFlatUnroll];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+    for (int j = 0; j < kFlatUnroll; ++j)
+      if (i0 + j * stride < n8) raw[j] = ld8(base + (i0 + j * stride) * 8);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < kFlatUnroll; ++j) {
+      if (i0 + j * stride < n8) {
+        float v[8];
+        cvt8(raw[j], v);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
+      }
+    }
   }
   m = block_max(m, red);
   if (threadIdx.x == 0) ws[blockIdx.y * kAmaxPartials + blockIdx.x] = m;
@@ -96,14 +135,26 @@ __global__ __launch_bounds__(kThreads) void quant_fp8_kernel(const Src *__restri
   const Src *src = x + (long long)t * per;
   uint8_t *dst = q + (long long)t * per;
   const long long n8 = per / 8;
-  for (long long i = blockIdx.x * (long long)kThreads + threadIdx.x; i < n8;
-       i += (long long)gridDim.x * kThreads) {
-    float v[8];
-    load8(src + i * 8, v);
-    i32x2 out;
-    out[0] = (int)f32x4_to_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-    out[1] = (int)f32x4_to_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
-    *reinterpret_cast<i32x2 *>(dst + i * 8) = out;
+  const long long stride = (long long)gridDim.x * kThreads;
+  for (long long i0 = blockIdx.x * (long long)kThreads + threadIdx.x; i0 < n8;
+       i0 += kFlatUnroll * stride) {
+    Raw8<Src> raw[kFlatUnroll];
+#pragma unroll
+    for (int j = 0; j < kFlatUnroll; ++j)
+      if (i0 + j * stride < n8) raw[j] = ld8(src + (i0 + j * stride) * 8);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < kFlatUnroll; ++j) {
+      const long long i = i0 + j * stride;
+      if (i < n8) {
+        float v[8];
+        cvt8(raw[j], v);
+        i32x2 out;
+        out[0] = (int)f32x4_to_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+        out[1] = (int)f32x4_to_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+        *reinterpret_cast<i32x2 *>(dst + i * 8) = out;
+      }
+    }
   }
 }
 
@@ -216,27 +267,67 @@ __device__ __forceinline__ void act8(const uint16_t *row, int H, int col, float 
   }
 }
 
-// Sources of the padded-row MXFP8 kernel: 8 consecutive values of row r
-// starting at column col (col % 8 == 0).
-// kUnroll chunks per lane are loaded before any is encoded (64 bytes of input
-// in flight per lane).
+// Sources of the padded-row MXFP8 kernel.  load() fetches the raw bytes of 8
+// consecutive values of row r from column col (col % 8 == 0); values() turns
+// them into the 8 float values.  The kernel issues the loads of kUnroll
+// chunks before it converts any, so they are in flight together.
 struct Bf16Rows {
-  static constexpr int kUnroll = 4;
+  static constexpr int kUnroll = 2;
+  struct Raw { i32x4 a; };
   const uint16_t *x;
   int K;
-  __device__ __forceinline__ void operator()(long long r, int col, float *v) const {
-    load8(x + r * K + col, v);
+  __device__ __forceinline__ Raw load(long long r, int col) const {
+    return {*reinterpret_cast<const i32x4 *>(x + r * K + col)};
   }
+  __device__ __forceinline__ void values(const Raw &raw, float *v) const { unpack8(raw.a, v); }
 };
+template <int kAct> struct ActRaw { i32x4 a, b; };           // SwiGLU: gate, up
+template <> struct ActRaw<MOE_ACT_SRELU> { i32x4 a; };
+
 template <int kAct>
 struct ActRows {                   // activation of rows of width 2H (SwiGLU) or H
-  static constexpr int kUnroll = kAct == MOE_ACT_SWIGLU ? 2 : 4;
+  static constexpr int kUnroll = kAct == MOE_ACT_SWIGLU ? 1 : 2;
+  using Raw = ActRaw<kAct>;
   const uint16_t *x;
   int H;
-  __device__ __forceinline__ void operator()(long long r, int col, float *v) const {
-    act8<kAct>(x + r * (kAct == MOE_ACT_SWIGLU ? 2ll * H : (long long)H), H, col, v);
+  __device__ __forceinline__ Raw load(long long r, int col) const {
+    Raw raw;
+    if constexpr (kAct == MOE_ACT_SWIGLU) {
+      const uint16_t *row = x + r * 2ll * H;
+      raw.a = *reinterpret_cast<const i32x4 *>(row + col);
+      raw.b = *reinterpret_cast<const i32x4 *>(row + H + col);
+    } else {
+      raw.a = *reinterpret_cast<const i32x4 *>(x + r * (long long)H + col);
+    }
+    return raw;
+  }
+  __device__ __forceinline__ void values(const Raw &raw, float *v) const {
+    if constexpr (kAct == MOE_ACT_SWIGLU) {
+      float g[8], u[8];
+      unpack8(raw.a, g);
+      unpack8(raw.b, u);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = silu_mul(g[i], u[i]);
+    } else {
+      unpack8(raw.a, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float t = fmaxf(v[i], 0.0f);
+        v[i] = t * t;
+      }
+    }
   }
 };
+
+// max over the four lanes of a quad (lanes 4a .. 4a+3), by DPP quad
+// permutations (xor 1, then xor 2); every lane of the quad must be active.
+__device__ __forceinline__ float quad_max(float m) {
+  m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, m),
+                                                                  0xB1, 0xF, 0xF, false)));
+  m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, m),
+                                                                  0x4E, 0xF, 0xF, false)));
+  return m;
+}
 
 __device__ __forceinline__ uint32_t e8m0_of_amax(float amax) {
   // shared exponent floor(log2 amax) - 8 as an e8m0 byte, clamped to [0, 254]
@@ -251,8 +342,7 @@ __device__ __forceinline__ uint32_t mx_chunk(const float *v, uint8_t *dst) {
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
-  m = fmaxf(m, __shfl_xor(m, 1));
-  m = fmaxf(m, __shfl_xor(m, 2));
+  m = quad_max(m);
   const uint32_t b = e8m0_of_amax(m);
   const float f = __builtin_bit_cast(float, (254u - b) << 23);   // 2^(127 - b)
   i32x2 o;
@@ -263,12 +353,21 @@ __device__ __forceinline__ uint32_t mx_chunk(const float *v, uint8_t *dst) {
 }
 
 // MXFP8 of expert-concatenated rows [rows, K] with the scale rows of each
-// expert padded to a multiple of 128 (pad rows get zero scale bytes).  One
-// wavefront per padded scale row p (wave-uniform, so the expert of p is found
-// by a uniform forward scan as p grows); lane l takes the 8-value chunks
-// c8 = l, l + 64, ..., so four neighbouring lanes hold one block and a
-// wavefront moves 512 contiguous values of the row per step.  K % 32 == 0
-// keeps every four-lane group inside the row together.
+// expert padded to a multiple of 128 (pad rows get zero scale bytes).
+//
+// Rows per workgroup step: R = 1 when a row has at least kThreads 8-value
+// chunks, else R = kThreads / (K/8); thread t owns local row t / (K/8) and the
+// chunks c8 = t % (K/8), + kThreads, ..., so the workgroup reads one
+// contiguous span of the input per load instruction and the rows in flight
+// stay close together in memory.  A workgroup takes S consecutive steps
+// before striding on (S steps fill a 128-byte line of scale bytes, so one L2
+// writes the whole line).  Four neighbouring threads hold one 32-value block
+// (K % 32 == 0), whose amax is reduced over the quad.
+//
+// Software pipeline: the first kUnroll chunks of the next row are loaded
+// before the current row is encoded, so a thread always has loads in flight.
+// Each thread finds the expert of its rows by a forward scan (its rows only
+// grow).
 template <class Src>
 __global__ __launch_bounds__(kThreads) void mx_padded_kernel(
     Src src, int rows, int K, const int *__restrict__ m_offsets, int E,
@@ -286,70 +385,125 @@ __global__ __launch_bounds__(kThreads) void mx_padded_kernel(
     s_po[E] = acc;
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63;
   const int n8 = K / 8, nb = K / kMxBlock;
+  const int R = n8 >= kThreads ? 1 : kThreads / n8;
+  const int lr = n8 >= kThreads ? 0 : (int)threadIdx.x / n8;
+  const int c0 = (int)threadIdx.x - lr * n8;
+  if (lr >= R) return;                            // whole quads of spare threads
+  const int S = R * nb >= 128 ? 1 : 128 / (R * nb);
   const int prows = s_po[E] < prow_bound ? s_po[E] : prow_bound;
-  const int waves = gridDim.x * (kThreads / 64);
+  constexpr int U = Src::kUnroll;
+  using Raw = typename Src::Raw;
+
+  // k-th row of this thread: step k % S of unit blockIdx.x + (k / S) * gridDim.x
+  auto row_of = [&](int k) {
+    return (blockIdx.x + (k / S) * gridDim.x) * (R * S) + (k % S) * R + lr;
+  };
   int e = 0;
-  for (int p = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); p < prows; p += waves) {
+  auto source_row = [&](int p, long long &r) {    // is padded row p a real row, which
     while (e < E - 1 && s_po[e + 1] <= p) ++e;
     const int local = p - s_po[e];
-    const long long r = (long long)s_mo[e] + local;
-    const bool live = local >= 0 && local < s_mo[e + 1] - s_mo[e] && r >= 0 && r < rows;
+    r = (long long)s_mo[e] + local;
+    return local >= 0 && local < s_mo[e + 1] - s_mo[e] && r >= 0 && r < rows;
+  };
+  // The first U chunks of row r.  The loads are unconditional (chunks past the
+  // row end reload chunk c0, a dead row loads row 0, which exists as rows > 0)
+  // so that every step has the same number of loads in flight and the waits
+  // before the encode can leave the next row's loads outstanding.
+  auto load_head = [&](long long r, Raw *raw) {
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int c = c0 + kThreads * j < n8 ? c0 + kThreads * j : c0;
+      raw[j] = src.load(r, 8 * c);
+    }
+  };
+  auto encode = [&](int c8, const Raw &raw, uint8_t *q_row, uint8_t *sf_row) {
+    float v[8];
+    src.values(raw, v);
+    const uint32_t b = mx_chunk(v, q_row + 8 * c8);
+    if ((c8 & 3) == 0) sf_row[c8 >> 2] = (uint8_t)b;
+  };
+
+  // One pipeline step: issue the loads of the next row into `nxt`, then
+  // encode the current row from `cur`.  Steps alternate between two buffers
+  // so that no register copy forces a wait on the loads in flight.
+  int k = 0;
+  int p = row_of(0);
+  if (p >= prows) return;
+  long long r;
+  bool live = source_row(p, r);
+  auto step = [&](Raw *cur, Raw *nxt) {
+    const int pn = row_of(k + 1);
+    const bool has_next = pn < prows;
+    long long rn = 0;
+    const bool live_n = has_next && source_row(pn, rn);
+    load_head(live_n ? rn : 0, nxt);
+    __builtin_amdgcn_sched_barrier(0);            // next row's loads go out first
     uint8_t *sf_row = sf + (long long)p * nb;
     if (live) {
       uint8_t *q_row = q + r * K;
-      constexpr int U = Src::kUnroll;
-      int c8 = lane;
-      for (; c8 + 64 * (U - 1) < n8; c8 += 64 * U) {
-        float v[U][8];
 #pragma unroll
-        for (int j = 0; j < U; ++j) src(r, 8 * (c8 + 64 * j), v[j]);
-#pragma unroll
-        for (int j = 0; j < U; ++j) {
-          const uint32_t b = mx_chunk(v[j], q_row + 8 * (c8 + 64 * j));
-          if ((c8 & 3) == 0) sf_row[(c8 + 64 * j) >> 2] = (uint8_t)b;
-        }
-      }
-      for (; c8 < n8; c8 += 64) {
-        float v[8];
-        src(r, 8 * c8, v);
-        const uint32_t b = mx_chunk(v, q_row + 8 * c8);
-        if ((c8 & 3) == 0) sf_row[c8 >> 2] = (uint8_t)b;
-      }
+      for (int j = 0; j < U; ++j)
+        if (c0 + kThreads * j < n8) encode(c0 + kThreads * j, cur[j], q_row, sf_row);
+      for (int c8 = c0 + kThreads * U; c8 < n8; c8 += kThreads)
+        encode(c8, src.load(r, 8 * c8), q_row, sf_row);
     } else {
-      for (int kb = lane; kb < nb; kb += 64) sf_row[kb] = 0;
+      for (int c8 = c0; c8 < n8; c8 += kThreads)
+        if ((c8 & 3) == 0) sf_row[c8 >> 2] = 0;
     }
+    p = pn;
+    r = rn;
+    live = live_n;
+    ++k;
+    return has_next;
+  };
+  Raw buf_a[U], buf_b[U];
+  load_head(live ? r : 0, buf_a);
+  while (step(buf_a, buf_b) && step(buf_b, buf_a)) {
   }
 }
 
-// Fused activation + fp8 per tensor, pass 1: partial amax of the activation.
-template <int kAct>
-__global__ __launch_bounds__(kThreads) void act_amax_kernel(const uint16_t *__restrict__ x,
-                                                            int rows, int H,
+// Fused activation + fp8 per tensor.  Both passes run one wavefront per row
+// (lane l takes the 8-value chunks l, l + 64, ...) with U chunks loaded
+// before any is used.  Pass 1: partial amax of the activation, one per
+// workgroup.
+template <int kAct, int U>
+__global__ __launch_bounds__(kThreads) void act_amax_kernel(ActRows<kAct> src, int rows,
                                                             float *__restrict__ ws) {
   __shared__ float red[kThreads / 64];
-  const long long in_w = kAct == MOE_ACT_SWIGLU ? 2ll * H : (long long)H;
-  const int n8 = H / 8;
-  const long long work = (long long)rows * n8;
+  const int lane = threadIdx.x & 63;
+  const int n8 = src.H / 8;
+  const int waves = gridDim.x * (kThreads / 64);
   float m = 0.0f;
-  for (long long i = blockIdx.x * (long long)kThreads + threadIdx.x; i < work;
-       i += (long long)gridDim.x * kThreads) {
-    const long long r = i / n8;
-    const int c = (int)(i - r * n8) * 8;
-    float y[8];
-    act8<kAct>(x + r * in_w, H, c, y);
+  for (int r = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); r < rows; r += waves) {
+    int c8 = lane;
+    for (; c8 + 64 * (U - 1) < n8; c8 += 64 * U) {
+      typename ActRows<kAct>::Raw raw[U];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(y[j]));
+      for (int j = 0; j < U; ++j) raw[j] = src.load(r, 8 * (c8 + 64 * j));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        float y[8];
+        src.values(raw[j], y);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(y[k]));
+      }
+    }
+    for (; c8 < n8; c8 += 64) {
+      float y[8];
+      src.values(src.load(r, 8 * c8), y);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(y[k]));
+    }
   }
   m = block_max(m, red);
   if (threadIdx.x == 0) ws[blockIdx.x] = m;
 }
 
 // Pass 2: reduce the partials, recompute the activation and quantize it.
-template <int kAct>
-__global__ __launch_bounds__(kThreads) void act_fp8_kernel(const uint16_t *__restrict__ x,
-                                                           int rows, int H, int parts,
+template <int kAct, int U>
+__global__ __launch_bounds__(kThreads) void act_fp8_kernel(ActRows<kAct> src, int rows, int parts,
                                                            const float *__restrict__ ws,
                                                            uint8_t *__restrict__ q,
                                                            float *__restrict__ scale) {
@@ -360,19 +514,29 @@ __global__ __launch_bounds__(kThreads) void act_fp8_kernel(const uint16_t *__res
   const float s = amax > 0.0f ? (float)((double)amax / 448.0) : 1.0f;
   const float inv = (float)(1.0 / (double)s);
   if (blockIdx.x == 0 && threadIdx.x == 0) scale[0] = s;
-  const long long in_w = kAct == MOE_ACT_SWIGLU ? 2ll * H : (long long)H;
-  const int n8 = H / 8;
-  const long long work = (long long)rows * n8;
-  for (long long i = blockIdx.x * (long long)kThreads + threadIdx.x; i < work;
-       i += (long long)gridDim.x * kThreads) {
-    const long long r = i / n8;
-    const int c = (int)(i - r * n8) * 8;
+  const int lane = threadIdx.x & 63;
+  const int H = src.H, n8 = H / 8;
+  const int waves = gridDim.x * (kThreads / 64);
+  auto encode = [&](const typename ActRows<kAct>::Raw &raw, uint8_t *dst) {
     float y[8];
-    act8<kAct>(x + r * in_w, H, c, y);
+    src.values(raw, y);
     i32x2 out;
     out[0] = (int)f32x4_to_e4m3x4(y[0] * inv, y[1] * inv, y[2] * inv, y[3] * inv);
     out[1] = (int)f32x4_to_e4m3x4(y[4] * inv, y[5] * inv, y[6] * inv, y[7] * inv);
-    *reinterpret_cast<i32x2 *>(q + r * H + c) = out;
+    *reinterpret_cast<i32x2 *>(dst) = out;
+  };
+  for (int r = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); r < rows; r += waves) {
+    uint8_t *q_row = q + (long long)r * H;
+    int c8 = lane;
+    for (; c8 + 64 * (U - 1) < n8; c8 += 64 * U) {
+      typename ActRows<kAct>::Raw raw[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) raw[j] = src.load(r, 8 * (c8 + 64 * j));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < U; ++j) encode(raw[j], q_row + 8 * (c8 + 64 * j));
+    }
+    for (; c8 < n8; c8 += 64) encode(src.load(r, 8 * c8), q_row + 8 * c8);
   }
 }
 
@@ -458,16 +622,20 @@ hipError_t launch_quant_int8_rows_f32(const float *w, long long rows, int K, int
 }
 
 // One wavefront per padded scale row; a workgroup of 4 wavefronts.
-static unsigned mx_padded_grid(int prow_bound) {
-  const int per_block = kThreads / 64;
-  const int blocks = (prow_bound + per_block - 1) / per_block;
-  return (unsigned)(blocks < 4096 ? (blocks > 0 ? blocks : 1) : 4096);
+// Workgroups of the padded-row MXFP8 kernel: one per R-row step, at most
+// kMxGrid (they stride beyond that).
+constexpr int kMxGrid = 8192;
+static unsigned mx_padded_grid(int prow_bound, int K) {
+  const int n8 = K / 8;
+  const int R = n8 >= kThreads ? 1 : kThreads / n8;
+  const int blocks = (prow_bound + R - 1) / R;
+  return (unsigned)(blocks < kMxGrid ? (blocks > 0 ? blocks : 1) : kMxGrid);
 }
 
 hipError_t launch_quant_mx_act_bf16(const uint16_t *x, int rows, int K, const int *m_offsets,
                                     int E, uint8_t *q, uint8_t *sf, hipStream_t s) {
   const int prow_bound = rows + E * (kMxRowPad - 1);
-  hipLaunchKernelGGL(mx_padded_kernel<Bf16Rows>, dim3(mx_padded_grid(prow_bound)), dim3(kThreads),
+  hipLaunchKernelGGL(mx_padded_kernel<Bf16Rows>, dim3(mx_padded_grid(prow_bound, K)), dim3(kThreads),
                      0, s, Bf16Rows{x, K}, rows, K, m_offsets, E, q, sf, prow_bound);
   return hipGetLastError();
 }
@@ -477,7 +645,7 @@ hipError_t launch_act_quant(const uint16_t *x, int rows, int H, int act, int mod
                             float *ws, hipStream_t s) {
   if (mode == MOE_Q_MXFP8) {
     const int prow_bound = rows + E * (kMxRowPad - 1);
-    const dim3 grid(mx_padded_grid(prow_bound));
+    const dim3 grid(mx_padded_grid(prow_bound, H));
     if (act == MOE_ACT_SWIGLU)
       hipLaunchKernelGGL(mx_padded_kernel<ActRows<MOE_ACT_SWIGLU>>, grid, dim3(kThreads), 0, s,
                          ActRows<MOE_ACT_SWIGLU>{x, H}, rows, H, m_offsets, E, q, sf, prow_bound);
@@ -486,15 +654,28 @@ hipError_t launch_act_quant(const uint16_t *x, int rows, int H, int act, int mod
                          ActRows<MOE_ACT_SRELU>{x, H}, rows, H, m_offsets, E, q, sf, prow_bound);
     return hipGetLastError();
   }
-  const long long items = (long long)rows * (H / 8);
-  const int parts = grid_for(items, kAmaxPartials);
-  auto k1 = act == MOE_ACT_SWIGLU ? act_amax_kernel<MOE_ACT_SWIGLU> : act_amax_kernel<MOE_ACT_SRELU>;
-  hipLaunchKernelGGL(k1, dim3(parts), dim3(kThreads), 0, s, x, rows, H, ws);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  auto k2 = act == MOE_ACT_SWIGLU ? act_fp8_kernel<MOE_ACT_SWIGLU> : act_fp8_kernel<MOE_ACT_SRELU>;
-  hipLaunchKernelGGL(k2, dim3(grid_for(items, 8192)), dim3(kThreads), 0, s, x, rows, H, parts, ws,
-                     q, scale);
+  // pass 1: one workgroup per 4 rows up to kAmaxPartials workgroups; pass 2:
+  // one wavefront per row (grid-stride beyond 16384 workgroups)
+  const long long row_blocks = ((long long)rows + 3) / 4;
+  const int parts = (int)(row_blocks < kAmaxPartials ? row_blocks : kAmaxPartials);
+  const int blocks2 = (int)(row_blocks < 16384 ? row_blocks : 16384);
+  if (act == MOE_ACT_SWIGLU) {
+    const ActRows<MOE_ACT_SWIGLU> src{x, H};
+    hipLaunchKernelGGL((act_amax_kernel<MOE_ACT_SWIGLU, 4>), dim3(parts), dim3(kThreads), 0, s,
+                       src, rows, ws);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((act_fp8_kernel<MOE_ACT_SWIGLU, 2>), dim3(blocks2), dim3(kThreads), 0, s,
+                       src, rows, parts, ws, q, scale);
+  } else {
+    const ActRows<MOE_ACT_SRELU> src{x, H};
+    hipLaunchKernelGGL((act_amax_kernel<MOE_ACT_SRELU, 8>), dim3(parts), dim3(kThreads), 0, s,
+                       src, rows, ws);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((act_fp8_kernel<MOE_ACT_SRELU, 4>), dim3(blocks2), dim3(kThreads), 0, s,
+                       src, rows, parts, ws, q, scale);
+  }
   return hipGetLastError();
 }
 

@@ -7,14 +7,15 @@ current stream:
     routed formats : moe_align_block_size -> [moe_quantize_act] ->
                      moe_grouped_gemm_{fp8w8a8,int8w8a16} -> moe_combine
     MXFP8          : moe_quantize_act(MXFP8) -> moe_grouped_gemm_mxfp8
+    activation     : moe_act_quantize (SwiGLU / SReLU + MXFP8 or fp8)
 
 Every step runs in the library's HIP kernels; nothing here computes.
 """
 
 import torch
 
-from . import (MOE_Q_FP8_PER_TENSOR, MOE_Q_INT8_PER_CHANNEL, MOE_Q_MXFP8, MOE_W_ROWMAJOR,
-               MOE_W_TILED, moe_align_block_size, moe_align_max_padded, moe_combine,
+from . import (MOE_ACT_SRELU, MOE_ACT_SWIGLU, MOE_Q_FP8_PER_TENSOR, MOE_Q_INT8_PER_CHANNEL, MOE_Q_MXFP8, MOE_W_ROWMAJOR,
+               MOE_W_TILED, moe_act_quantize, moe_align_block_size, moe_align_max_padded, moe_combine,
                moe_grouped_gemm_fp8w8a8, moe_grouped_gemm_int8w8a16, moe_grouped_gemm_mxfp8,
                moe_mx_scale_rows, moe_pack_weights, moe_packed_weight_bytes, moe_quantize_act,
                moe_quantize_weights, moe_quantize_workspace_bytes, moe_recommended_block_m)
@@ -137,3 +138,27 @@ class MxMoE:
         self.quantize(x, m_offsets)
         self.gemm(w_q, w_sf, m_offsets)
         return self.out
+
+
+class ActQuant:
+    """Fused activation + quantization of expert-concatenated rows: x bf16
+    [rows, 2H] (SwiGLU) or [rows, H] (SReLU) -> q [rows, H] e4m3 with MXFP8
+    scale bytes (per-expert padded blocks) or one fp8 tensor scale."""
+
+    def __init__(self, rows, H, E, act="swiglu", mode="mxfp8", device="cuda"):
+        self.rows, self.H, self.E = rows, H, E
+        self.act = {"swiglu": MOE_ACT_SWIGLU, "srelu": MOE_ACT_SRELU}[act]
+        self.mode = {"mxfp8": MOE_Q_MXFP8, "fp8": MOE_Q_FP8_PER_TENSOR}[mode]
+        self.q = _empty((rows, H), torch.uint8, device)
+        self.scale = _empty((1,), torch.float32, device)
+        self.sf = self.ws = None
+        if self.mode == MOE_Q_MXFP8:
+            self.sf = _empty((moe_mx_scale_rows(rows, E), H // 32), torch.uint8, device)
+        else:
+            self.ws = _empty((moe_quantize_workspace_bytes(MOE_Q_FP8_PER_TENSOR, 1),), torch.uint8,
+                             device)
+
+    def __call__(self, x, m_offsets=None):
+        moe_act_quantize(x, self.rows, self.H, self.act, self.mode, m_offsets, self.E, self.q,
+                         self.scale, self.sf, self.ws)
+        return self.q

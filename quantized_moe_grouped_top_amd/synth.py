@@ -14,7 +14,10 @@ input of "[PyTorch] Let GroupedLinear accept MXFP8 input and gradient"):
   quantized by the library (offline step) or by the oracle;
 * router logits: float32 [M, E], entries N(0, 1), optionally plus a per-expert
   bias N(0, 0.5) that makes the expert loads unbalanced;
-* MXFP8 grouped linear: rows concatenated by expert, equal segments.
+* MXFP8 grouped linear: rows concatenated by expert, equal segments;
+* fused activation + quantization (the step between the up and the down
+  projection): bf16 [rows, 2H] (SwiGLU) or [rows, H] (SReLU) entries N(0, 1),
+  rows concatenated by expert as for the MXFP8 grouped linear.
 """
 
 from dataclasses import dataclass, field
@@ -25,7 +28,8 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    fmt: str               # "fp8", "int8", "mxfp8"
+    fmt: str               # "fp8", "int8", "mxfp8"; "act_mxfp8", "act_fp8" (K = input
+                           # width 2H or H, N = H)
     M: int                 # tokens (MXFP8: total rows)
     K: int
     N: int
@@ -33,6 +37,7 @@ class Workload:
     top_k: int = 2
     bias_std: float = 0.0  # std of the per-expert logit bias
     seg: tuple = field(default=())  # MXFP8 rows per expert
+    act: str = ""          # fused activation workloads: "swiglu" or "srelu"
 
     @property
     def routed_rows(self):
@@ -48,6 +53,12 @@ def _mx(name, rows_per_expert, E, K, N):
                     seg=tuple([rows_per_expert] * E))
 
 
+def _act(act, mode, rows_per_expert, E, H):
+    width = 2 * H if act == "swiglu" else H
+    return Workload(f"{act}_{mode}_{E}x{rows_per_expert}_h{H}", f"act_{mode}", rows_per_expert * E,
+                    width, H, E=E, top_k=1, seg=tuple([rows_per_expert] * E), act=act)
+
+
 WORKLOADS = {w.name: w for w in [
     Workload("fp8_m64_k128_n256", "fp8", 64, 128, 256),
     Workload("int8w8a16_m64_k4096_n14336", "int8", 64, 4096, 14336),
@@ -59,6 +70,11 @@ WORKLOADS = {w.name: w for w in [
     Workload("mistral7b_down_int8_m4096_k14336_n4096", "int8", 4096, 14336, 4096),
     _mx("mxfp8_8x4000_k4096_n4096", 4000, 8, 4096, 4096),
     _mx("mxfp8_22b_8x4000_k6144_n32768", 4000, 8, 6144, 32768),
+    # the (8*4000, 4096) activation input: SwiGLU halves it to H = 2048
+    _act("swiglu", "mxfp8", 4000, 8, 2048),
+    _act("srelu", "mxfp8", 4000, 8, 4096),
+    _act("swiglu", "fp8", 4000, 8, 2048),
+    _act("srelu", "fp8", 4000, 8, 4096),
 ]}
 
 
@@ -121,6 +137,9 @@ def make_case(wl, variant=0, device="cpu"):
     """All inputs of one workload: dict of x, w, logits (routed formats) or
     x, w, m_offsets (MXFP8)."""
     s = seed_of(wl.name, variant)
+    if wl.fmt.startswith("act_"):
+        return {"x": make_act_input(wl.M, wl.K, s + 1, 1.0, device),
+                "m_offsets": make_segments(wl.seg, device)}
     case = {
         "x": make_activations(wl.M, wl.K, s + 1, device),
         "w": make_weights(wl.E, wl.N, wl.K, s + 2, device),

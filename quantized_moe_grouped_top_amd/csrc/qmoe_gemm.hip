@@ -33,6 +33,8 @@
 //                   contiguous chunks, so the workgroups resident on one XCD
 //                   share each weight tile through its L2.
 // Routed results are written per slot as bf16; MXFP8 rows as bf16.
+#include <atomic>
+
 #include "qmoe_internal.h"
 
 namespace qmoe {
@@ -1174,6 +1176,401 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gemm_big_kernel(
   }
 }
 
+// =============================================================================
+// fp8 W8A8 (block_m = 128) and MXFP8: 256 x 256 tiles on four wavefronts
+// =============================================================================
+// Same tiles, stages, LDS layout and DMA as gemm_big_kernel, but four
+// wavefronts (one per SIMD) of 128 x 128 outputs each, computed with
+// v_mfma_f32_32x32x64_f8f6f4: a wavefront's fragments of one 64-k half-stage
+// are 4 row and 4 column fragments (32 x 64 bytes), 16 MFMAs.  Against eight
+// 128 x 64 wavefronts this reads a third fewer LDS bytes per flop.
+//
+// Operand layout of the 32x32x64 f8f6f4 MFMA (checked on the device): lane
+// l = 32 g + r holds row (column) r, k 16g..16g+15 and 32+16g..32+16g+15 of
+// the half-stage; with block scales, lane 32 b + r supplies the scale of the
+// 32-k block b.  The result lane l holds column l % 32, rows
+// 8 (v / 4) + 4 g + v % 4 for accumulator v.  Fragment reads of 128-byte
+// rows with chunks swizzled by (r >> 1) & 7 are free of bank conflicts.
+//
+// Pipeline: the fragments of the next half-stage are read into the other
+// register set while the MFMAs of the current one run; the barrier that
+// hands a ring slot back to the DMA sits between the two halves of a stage,
+// after this wave's reads of the stage have completed.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 mfma32_fp8(const i32x8 &a, const i32x8 &b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32_mx(const i32x8 &a, const i32x8 &b, f32x16 c, int sa,
+                                            int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+// Tile queues of the persistent wide kernel: per launch slot, one counter
+// per XCD (the next unclaimed tile of that XCD's chunk) and a count of
+// finished workgroups.  The last workgroup of a launch sets them back to zero.
+constexpr int kLaunchSlots = 64;
+__device__ unsigned int g_tile_next[kLaunchSlots][kXcds];
+__device__ unsigned int g_tiles_done[kLaunchSlots];
+constexpr int kHwRegXccId = (31 << 11) | 20;           // s_getreg: XCC_ID, all 32 bits
+
+template <int kFmt, bool kTiled>
+__global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
+    const uint8_t *__restrict__ a, const float *__restrict__ a_scale,
+    const uint8_t *__restrict__ a_sf, const uint8_t *__restrict__ w,
+    const float *__restrict__ w_scale, const uint8_t *__restrict__ w_sf,
+    const int *__restrict__ sorted_ids, const int *__restrict__ expert_ids,
+    const float *__restrict__ topk_w, const int *__restrict__ m_offsets, int M, int K, int N,
+    int E, int top_k, int max_blocks, uint16_t *__restrict__ out, int launch_slot) {
+  constexpr bool kMx = kFmt == kFmtMx;
+  static_assert(kFmt != kFmtInt8, "int8 W8A16 uses gemm_kernel");
+  constexpr int kWaves = 4;
+  constexpr int kThr = 64 * kWaves;
+  constexpr int kDma = 32 / kWaves;                      // activation (and weight) DMAs per wave
+  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[2 * kHStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s_sf[kMx ? 2 * kHSf : 16];
+  __shared__ int s_row[kHBM];
+  __shared__ float s_rs[kMx ? 1 : kHBM];               // fp8: per-row output scale
+  __shared__ int s_blk_first[kMaxExperts + 1];
+  __shared__ int s_tile_first[kMaxExperts + 1];
+  __shared__ int s_mo[kMx ? kMaxExperts + 1 : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int g = lane >> 5, r32 = lane & 31;
+  const int ntn = (N + kHBN - 1) / kHBN;
+
+  // ---- tile space: expert by expert, column tile by column tile, block pair
+  // fastest; each XCD takes one contiguous chunk of it
+  if constexpr (!kMx) {
+    expert_block_starts(expert_ids, max_blocks, E, s_blk_first);
+    __syncthreads();
+  }
+  if (tid == 0) {
+    int blk = 0, tiles = 0;
+    for (int ee = 0; ee < E; ++ee) {
+      int nb;
+      if constexpr (kMx) {
+        s_mo[ee] = m_offsets[ee];
+        s_mo[ee + 1] = m_offsets[ee + 1];
+        const int m = s_mo[ee + 1] - s_mo[ee];
+        nb = m > 0 ? (m + kGBM - 1) / kGBM : 0;
+        s_blk_first[ee] = blk;
+        blk += nb;
+      } else {
+        nb = s_blk_first[ee + 1] - s_blk_first[ee];
+      }
+      s_tile_first[ee] = tiles;
+      tiles += (nb + 1) / 2 * ntn;
+    }
+    if constexpr (kMx) s_blk_first[E] = blk;
+    s_tile_first[E] = tiles;
+  }
+  __syncthreads();
+  // ---- persistent workgroups: each XCD owns one contiguous chunk of the
+  // tile space; a workgroup takes the next tile of its own XCD's chunk (tiles
+  // of one chunk share weights and activations in that XCD's L2), then helps
+  // the other XCDs once its own chunk is done
+  const int total = s_tile_first[E];
+  const int chunk = (total + kXcds - 1) / kXcds;
+  const int my_xcc = (int)(__builtin_amdgcn_s_getreg(kHwRegXccId) & (kXcds - 1));
+  __shared__ int s_next;
+  const int S = M * top_k;
+  for (int qx = 0; qx < kXcds; ++qx) {
+  const int xq = (my_xcc + qx) & (kXcds - 1);
+  const int n_x = min(chunk, total - xq * chunk);
+  for (;;) {
+  if (tid == 0) s_next = n_x > 0 ? (int)atomicAdd(&g_tile_next[launch_slot][xq], 1u) : n_x;
+  __syncthreads();
+  const int tile_t = s_next;
+  __syncthreads();                                      // (s_next is rewritten next round)
+  if (tile_t >= n_x) break;
+  const int L = xq * chunk + tile_t;
+  // lane-derived values are recomputed per tile from an opaque copy of the
+  // lane index, so that the compiler does not keep them live across tiles
+  int lane_opaque = lane;
+  asm volatile("" : "+v"(lane_opaque));
+  const int lane = lane_opaque;                         // shadows the kernel-wide one
+  const int g = lane >> 5, r32 = lane & 31;
+  int e = 0;
+  while (s_tile_first[e + 1] <= L) ++e;
+  const int nblk = s_blk_first[e + 1] - s_blk_first[e];
+  const int npair = (nblk + 1) / 2;
+  const int local = L - s_tile_first[e];
+  const int nt = local / npair;
+  const int pr = local - nt * npair;
+  const int nb_here = min(2, nblk - 2 * pr);            // 128-row blocks in this tile
+  const int n0 = nt * kHBN;
+  int row0 = 0, row_end = 0;                            // MXFP8: the tile's rows
+  for (int r = tid; r < kHBM; r += kThr) {
+    if constexpr (kMx) {
+      row0 = s_mo[e] + 2 * pr * kGBM;
+      s_row[r] = row0 + r;
+    } else {
+      const int slot = r < nb_here * kGBM ? sorted_ids[(s_blk_first[e] + 2 * pr) * kGBM + r] : S;
+      s_row[r] = slot;
+      // the epilogue's row scale: activation x weight scale x router weight
+      s_rs[r] = slot < S ? a_scale[0] * w_scale[e] * topk_w[slot] : 0.0f;
+    }
+  }
+  if constexpr (kMx) {
+    row0 = s_mo[e] + 2 * pr * kGBM;
+    row_end = s_mo[e + 1];
+  }
+  __syncthreads();
+  auto src_row = [&](int r) -> uint32_t {
+    const int v = s_row[r];
+    if constexpr (kMx) return (uint32_t)(v < row_end ? v : row_end - 1);
+    else return (uint32_t)(v < S ? v / top_k : 0);
+  };
+  const bool a_dma = (8 * kDma * wave) / kGBM < nb_here;  // this wave's DMA rows exist
+  const bool busy = wm < nb_here;                       // this wave's 128 output rows exist
+
+  // ---- DMA sources of this lane (as gemm_big_kernel) -------------------------
+  const uint32_t lds_ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)s_ring;
+  const int nst = K / 128;
+  uint32_t a_off[kDma];
+#pragma unroll
+  for (int u = 0; u < kDma; ++u) {
+    const int r = 8 * (kDma * wave + u) + (lane >> 3);
+    a_off[u] = src_row(r) * (uint32_t)K + 16u * (uint32_t)((lane & 7) ^ swz(r));
+  }
+  // weights: wave w loads the 64-column block w of the tile, 8 x 1 KB
+  uint32_t wblk = 0;
+  uint32_t b_off[kDma];
+  if constexpr (kTiled) {
+    const int T = (N + 63) / 64;
+    const int pt = min(n0 / 64 + wave, T - 1);
+    wblk = ((uint32_t)e * (uint32_t)T + (uint32_t)pt) * (uint32_t)nst * 8192u;
+  } else {
+#pragma unroll
+    for (int u = 0; u < kDma; ++u) {
+      const int n = 8 * u + (lane >> 3);
+      const int col = min(n0 + wave * 64 + n, N - 1);
+      b_off[u] = ((uint32_t)e * (uint32_t)N + (uint32_t)col) * (uint32_t)K +
+                 16u * (uint32_t)((lane & 7) ^ swz(n));
+    }
+  }
+  // MXFP8 scales: 8 dword DMAs per stage (rows 0-255, then columns 0-255, 64
+  // per DMA), two per wavefront
+  constexpr int kSfPerWave = 8 / kWaves;
+  const uint32_t kb_row = (uint32_t)K / 32u;
+  uint32_t sf_off[kSfPerWave];
+  bool sf_on[kSfPerWave];
+  if constexpr (kMx) {
+    int po = 0;
+    for (int ee = 0; ee < e; ++ee) po += (s_mo[ee + 1] - s_mo[ee] + kMxRowPad - 1) / kMxRowPad * kMxRowPad;
+#pragma unroll
+    for (int u = 0; u < kSfPerWave; ++u) {
+      const int q = kSfPerWave * wave + u;             // 0-3 rows, 4-7 columns
+      if (q < 4) {
+        sf_off[u] = ((uint32_t)po + src_row(64 * q + lane) - (uint32_t)s_mo[e]) * kb_row;
+        sf_on[u] = (64 * q) / kGBM < nb_here;
+      } else {
+        sf_off[u] = ((uint32_t)e * (uint32_t)N + (uint32_t)min(n0 + 64 * (q - 4) + lane, N - 1)) * kb_row;
+        sf_on[u] = true;
+      }
+    }
+  }
+  const uint32_t lds_sf = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)s_sf;
+
+  // DMA pieces of stage st into ring slot slot_i: q = 0..7 activation rows
+  // (1 KB each), 8..15 weight rows, 16..17 MXFP8 scale dwords.  Every piece is
+  // issued (rows past the tile's last block reload clamped rows), so the
+  // main loop has no branches.
+  auto issue_piece = [&](int st, int slot_i, int q) {
+    const uint32_t base = lds_ring + (uint32_t)(slot_i * kHStage);
+    if (q < kDma) {
+      dma16(a + (size_t)st * 128u, a_off[q], base + (uint32_t)((kDma * wave + q) * 1024));
+    } else if (q < 2 * kDma) {
+      const int u = q - kDma;
+      const uint32_t bdst = base + (uint32_t)(kHABytes + (kDma * wave + u) * 1024);
+      if constexpr (kTiled) dma16(w + wblk + (size_t)st * 8192u, (uint32_t)(u * 1024 + 16 * lane), bdst);
+      else dma16(w + (size_t)st * 128u, b_off[u], bdst);
+    } else if constexpr (kMx) {
+      const int u = q - 2 * kDma;
+      const int qq = kSfPerWave * wave + u;
+      dma4((qq < 4 ? a_sf : w_sf) + 4 * st, sf_off[u],
+           lds_sf + (uint32_t)(slot_i * kHSf) + (uint32_t)(256 * qq));
+    }
+  };
+  constexpr int kPieces = 2 * kDma + (kMx ? kSfPerWave : 0);
+  auto issue = [&](int st, int slot_i) {
+#pragma unroll
+    for (int q = 0; q < kPieces; ++q) issue_piece(st, slot_i, q);
+  };
+
+  // ---- fragments of one half-stage and their MFMAs -------------------------
+  // Sixteen 16-byte LDS reads per half-stage (part q: fragment q >> 2;
+  // activation low / high half, weight low / high half), read one per MFMA.
+  struct Frags {
+    i32x4 alo[4], ahi[4], blo[4], bhi[4];
+    int sa[4], sb[4];
+  };
+  const int sw = swz(r32);
+  auto read_part = [&](int slot_i, int h, Frags &f, int q) {
+    const int i = q >> 2, part = q & 3;
+    const uint8_t *base = s_ring + slot_i * kHStage +
+                          (part < 2 ? wm * 128 * 128 : kHABytes + wn * 128 * 128) + (32 * i + r32) * 128;
+    const int c = (((4 * h + g + ((part & 1) ? 2 : 0)) ^ sw) << 4);
+    const i32x4 v = ld16(base + c);
+    if (part == 0) f.alo[i] = v;
+    else if (part == 1) f.ahi[i] = v;
+    else if (part == 2) f.blo[i] = v;
+    else f.bhi[i] = v;
+  };
+  auto read_scales = [&](int slot_i, int h, Frags &f) {
+    if constexpr (kMx) {
+      const uint8_t *sfs = s_sf + slot_i * kHSf;
+      const int sh = 8 * (2 * h + g);                   // lane group g: 32-k block 2h + g
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f.sa[i] = (int)((*reinterpret_cast<const uint32_t *>(sfs + 4 * (wm * 128 + 32 * i + r32)) >> sh) & 0xFFu);
+        f.sb[i] = (int)((*reinterpret_cast<const uint32_t *>(sfs + 4 * kHBM + 4 * (wn * 128 + 32 * i + r32)) >> sh) & 0xFFu);
+      }
+    }
+  };
+  auto read_frags = [&](int slot_i, int h, Frags &f) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) read_part(slot_i, h, f, q);
+    read_scales(slot_i, h, f);
+  };
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  auto mfma_q = [&](const Frags &f, int q) {
+    const int i = q >> 2, j = q & 3;
+    const i32x8 av = __builtin_shufflevector(f.alo[i], f.ahi[i], 0, 1, 2, 3, 4, 5, 6, 7);
+    const i32x8 bv = __builtin_shufflevector(f.blo[j], f.bhi[j], 0, 1, 2, 3, 4, 5, 6, 7);
+    if constexpr (kMx) acc[i][j] = mfma32_mx(av, bv, acc[i][j], f.sa[i], f.sb[j]);
+    else acc[i][j] = mfma32_fp8(av, bv, acc[i][j]);
+  };
+  auto pin_acc = [&]() {     // the accumulators are "used" here: no MFMA sinks past
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
+  };
+
+  // ---- two-slot ring, half-stage register pipeline ----------------------------
+  // Per stage: the 16 MFMAs of half 0 run with the 16 reads of half 1 between
+  // them; then the barrier that frees the stage's slot; then the 16 MFMAs of
+  // half 1 with the DMA pieces of stage st + 2 and the reads of the next
+  // stage's half 0 between them (one memory instruction per 64-cycle MFMA,
+  // the rate the memory pipeline takes them at).  A wavefront whose 128 rows
+  // do not exist (the tile's second block is missing) computes on stale LDS
+  // rows and drops the results, so every wavefront runs the same stream.
+  Frags fa, fb;
+  issue(0, 0);
+  if (nst > 1) {
+    issue(1, 1);
+    wait_dma_upto(kPieces);                             // leave stage 1 in flight
+  } else {
+    wait_dma_all();
+  }
+  __syncthreads();                                      // stage 0 landed everywhere
+  read_frags(0, 0, fa);
+  for (int st = 0; st + 1 < nst; ++st) {
+    const int slot = st & 1;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      mfma_q(fa, q);
+      read_part(slot, 1, fb, q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    read_scales(slot, 1, fb);
+    pin_acc();
+    // this wave's reads of slot `slot` are complete; stage st + 1 (the only
+    // DMA outstanding) has landed here; after the barrier it has landed
+    // everywhere and nobody reads slot `slot` any more
+    __builtin_amdgcn_s_waitcnt(0xC07F);               // lgkmcnt(0)
+    wait_dma_all();
+    __syncthreads();
+    const int st2 = st + 2 < nst ? st + 2 : nst - 1;    // past the end: a harmless reload
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      mfma_q(fb, q);
+      issue_piece(st2, slot, q);
+      read_part(slot ^ 1, 0, fa, q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int q = 16; q < kPieces; ++q) issue_piece(st2, slot, q);
+    read_scales(slot ^ 1, 0, fa);
+    pin_acc();
+    __builtin_amdgcn_s_waitcnt(0xC07F);               // lgkmcnt(0): fa arrived
+  }
+  {
+    const int slot = (nst - 1) & 1;                     // the last stage
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      mfma_q(fa, q);
+      read_part(slot, 1, fb, q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    read_scales(slot, 1, fb);
+    pin_acc();
+    __builtin_amdgcn_s_waitcnt(0xC07F);               // lgkmcnt(0)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) mfma_q(fb, q);
+  }
+  wait_dma_all();                                       // the reload must land before the ring is reused
+
+  // ---- epilogue: bf16 results -> LDS (the ring is free) -> row segments ----
+  __syncthreads();
+  if (busy) {
+  uint16_t *t = reinterpret_cast<uint16_t *>(s_ring) + wave * 128 * 128;   // [128 rows][128]
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = 32 * i + 8 * (v / 4) + 4 * g + (v % 4);
+      float rs = 1.0f;
+      if constexpr (!kMx) rs = s_rs[wm * 128 + r];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        t[r * 128 + 32 * j + r32] = (uint16_t)(f32x2_to_bf16x2(acc[i][j][v] * rs, 0.0f) & 0xFFFFu);
+    }
+  __builtin_amdgcn_s_waitcnt(0xC07F);                   // lgkmcnt(0): the wave's LDS writes done
+  __builtin_amdgcn_wave_barrier();
+  const bool vec = (N & 7) == 0 && ((uintptr_t)out & 15u) == 0;
+#pragma unroll 4
+  for (int q = 0; q < 32; ++q) {                        // 4 rows of 16 lanes x 8 columns
+    const int r = q * 4 + lane / 16;
+    const int col = n0 + wn * 128 + (lane % 16) * 8;
+    int dst_row;
+    if constexpr (kMx) {
+      dst_row = row0 + wm * 128 + r;
+      if (dst_row >= row_end) continue;
+    } else {
+      dst_row = s_row[wm * 128 + r];
+      if (dst_row >= S) continue;
+    }
+    if (col >= N) continue;
+    const uint16_t *src = t + r * 128 + (lane % 16) * 8;
+    uint16_t *dst = out + (size_t)dst_row * N + col;
+    if (vec && col + 8 <= N) {
+      *reinterpret_cast<i32x4 *>(dst) = *reinterpret_cast<const i32x4 *>(src);
+    } else {
+      for (int c = 0; c < 8 && col + c < N; ++c) dst[c] = src[c];
+    }
+  }
+  }  // busy
+  }  // tiles of chunk xq
+  }  // chunks
+  if (tid == 0) {
+    __threadfence();
+    if (atomicAdd(&g_tiles_done[launch_slot], 1u) == gridDim.x - 1) {
+      for (int x = 0; x < kXcds; ++x) atomicExch(&g_tile_next[launch_slot][x], 0u);
+      atomicExch(&g_tiles_done[launch_slot], 0u);
+    }
+  }
+}
+
 unsigned tile_grid(long long tiles_bound) {
   long long per = (tiles_bound + kXcds - 1) / kXcds;
   return (unsigned)(per * kXcds);
@@ -1192,6 +1589,27 @@ int num_cus() {
       n = 256;
   }
   return n;
+}
+
+// Below this many routed rows per expert (on average) most 256-row tiles
+// hold a single 128-row block; the eight-wavefront kernel then idles the
+// wavefronts of the missing block and gives their SIMD time to the others,
+// where the four-wavefront kernel (one per SIMD) would leave half the MFMA
+// units to a block that does not exist.
+constexpr long long kWideMinRowsPerExpert = 384;
+
+// persistent wide-kernel grid: one workgroup per CU (at most one fits), no
+// more than there can be tiles
+unsigned wide_grid(long long tiles_bound) {
+  const long long n = num_cus();
+  return (unsigned)(tiles_bound < n ? (tiles_bound > 0 ? tiles_bound : 1) : n);
+}
+
+// launch slot of the wide kernel's tile queues: launches that may run at
+// the same time on one device must use different slots
+int next_launch_slot() {
+  static std::atomic<unsigned> seq{0};
+  return (int)(seq.fetch_add(1u, std::memory_order_relaxed) % (unsigned)kLaunchSlots);
 }
 
 // persistent decomposition of the weight stream: E * groups workgroups, each
@@ -1216,10 +1634,18 @@ hipError_t launch_gemm_fp8(const uint8_t *a_q, const float *a_scale, const uint8
                        groups, tpg, r.max_blocks, r.y);
   } else {
     const long long tiles = (long long)(r.max_blocks / 2 + r.E) * ((r.N + kHBN - 1) / kHBN);
-    auto k = r.w_layout ? gemm_big_kernel<kFmtFp8, true, kHWaves> : gemm_big_kernel<kFmtFp8, false, kHWaves>;
-    hipLaunchKernelGGL(k, dim3(tile_grid(tiles)), dim3(64 * kHWaves), 0, s, a_q, a_scale, nullptr, w_q,
-                       w_scale, nullptr, r.sorted_ids, r.expert_ids, r.topk_w, nullptr, r.M, r.K,
-                       r.N, r.E, r.top_k, r.max_blocks, r.y);
+    if ((long long)r.M * r.top_k >= kWideMinRowsPerExpert * (long long)r.E) {
+      auto k = r.w_layout ? gemm_wide_kernel<kFmtFp8, true> : gemm_wide_kernel<kFmtFp8, false>;
+      hipLaunchKernelGGL(k, dim3(wide_grid(tiles)), dim3(256), 0, s, a_q, a_scale, nullptr, w_q,
+                         w_scale, nullptr, r.sorted_ids, r.expert_ids, r.topk_w, nullptr, r.M,
+                         r.K, r.N, r.E, r.top_k, r.max_blocks, r.y, next_launch_slot());
+    } else {
+      auto k = r.w_layout ? gemm_big_kernel<kFmtFp8, true, kHWaves>
+                          : gemm_big_kernel<kFmtFp8, false, kHWaves>;
+      hipLaunchKernelGGL(k, dim3(tile_grid(tiles)), dim3(64 * kHWaves), 0, s, a_q, a_scale,
+                         nullptr, w_q, w_scale, nullptr, r.sorted_ids, r.expert_ids, r.topk_w,
+                         nullptr, r.M, r.K, r.N, r.E, r.top_k, r.max_blocks, r.y);
+    }
   }
   return hipGetLastError();
 }
@@ -1251,9 +1677,9 @@ hipError_t launch_gemm_mxfp8(const uint8_t *a_q, const uint8_t *a_sf, const uint
   // block pairs: at most (sum of blocks + E) / 2 + E
   const long long pairs = ((rows + kGBM - 1) / kGBM + E) / 2 + E;
   const long long tiles = pairs * ((N + kHBN - 1) / kHBN);
-  hipLaunchKernelGGL((gemm_big_kernel<kFmtMx, false, kHWaves>), dim3(tile_grid(tiles)), dim3(64 * kHWaves), 0, s,
+  hipLaunchKernelGGL((gemm_wide_kernel<kFmtMx, false>), dim3(wide_grid(tiles)), dim3(256), 0, s,
                      a_q, nullptr, a_sf, w_q, nullptr, w_sf, nullptr, nullptr, nullptr, m_offsets,
-                     rows, K, N, E, 1, 0, out);
+                     rows, K, N, E, 1, 0, out, next_launch_slot());
   return hipGetLastError();
 }
 

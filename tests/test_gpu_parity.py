@@ -130,6 +130,9 @@ SMALL = [
     synth.small("fp8", 1, 128, 64, 8, 2),
     synth.small("int8", 40, 128, 48, 1, 1),
     synth.small("fp8", 33, 256, 96, 4, 4),
+    # >= 384 routed rows per expert: the four-wavefront persistent kernel
+    synth.small("fp8", 400, 256, 320, 2, 2),
+    synth.small("fp8", 800, 384, 136, 4, 2, bias_std=1.5),
 ]
 
 

@@ -1442,12 +1442,16 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  // The weight fragment is the MFMA's first operand: lane 32 g + r then
+  // holds output row r of the activation fragment and, for accumulator
+  // 4 k + c, column 8 k + 4 g + c of the weight fragment (four neighbouring
+  // columns per k), which the epilogue stores as 8-byte pieces.
   auto mfma_q = [&](const Frags &f, int q) {
     const int i = q >> 2, j = q & 3;
     const i32x8 av = __builtin_shufflevector(f.alo[i], f.ahi[i], 0, 1, 2, 3, 4, 5, 6, 7);
     const i32x8 bv = __builtin_shufflevector(f.blo[j], f.bhi[j], 0, 1, 2, 3, 4, 5, 6, 7);
-    if constexpr (kMx) acc[i][j] = mfma32_mx(av, bv, acc[i][j], f.sa[i], f.sb[j]);
-    else acc[i][j] = mfma32_fp8(av, bv, acc[i][j]);
+    if constexpr (kMx) acc[i][j] = mfma32_mx(bv, av, acc[i][j], f.sb[j], f.sa[i]);
+    else acc[i][j] = mfma32_fp8(bv, av, acc[i][j]);
   };
   auto pin_acc = [&]() {     // the accumulators are "used" here: no MFMA sinks past
 #pragma unroll
@@ -1520,44 +1524,61 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
   }
   wait_dma_all();                                       // the reload must land before the ring is reused
 
-  // ---- epilogue: bf16 results -> LDS (the ring is free) -> row segments ----
-  __syncthreads();
+  // ---- epilogue: per wavefront, in two halves of 64 rows: bf16 results ->
+  // the wavefront's 16 KB of ring slot 1 (rows of 256 bytes, 16-byte chunk c
+  // of row r at c ^ (r & 15)) -> whole 256-byte row segments in HBM.  Only
+  // the wavefront itself reads its staging area, so no workgroup barrier.
+  __syncthreads();                                      // the ring is no longer read
   if (busy) {
-  uint16_t *t = reinterpret_cast<uint16_t *>(s_ring) + wave * 128 * 128;   // [128 rows][128]
+  uint8_t *stg = s_ring + kHStage + wave * 16384;
+  const bool vec = (N & 7) == 0 && ((uintptr_t)out & 15u) == 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int h = 0; h < 2; ++h) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = 32 * i + 8 * (v / 4) + 4 * g + (v % 4);
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = 2 * h + ii;
+      const int lr = ii * 32 + r32;                     // staging row
       float rs = 1.0f;
-      if constexpr (!kMx) rs = s_rs[wm * 128 + r];
+      if constexpr (!kMx) rs = s_rs[wm * 128 + 32 * i + r32];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        t[r * 128 + 32 * j + r32] = (uint16_t)(f32x2_to_bf16x2(acc[i][j][v] * rs, 0.0f) & 0xFFFFu);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const f32x16 &c = acc[i][j];
+          i32x2 pk;
+          pk[0] = (int)f32x2_to_bf16x2(c[4 * k] * rs, c[4 * k + 1] * rs);
+          pk[1] = (int)f32x2_to_bf16x2(c[4 * k + 2] * rs, c[4 * k + 3] * rs);
+          *reinterpret_cast<i32x2 *>(stg + lr * 256 + (((4 * j + k) ^ (lr & 15)) << 4) + 8 * g) = pk;
+        }
     }
-  __builtin_amdgcn_s_waitcnt(0xC07F);                   // lgkmcnt(0): the wave's LDS writes done
-  __builtin_amdgcn_wave_barrier();
-  const bool vec = (N & 7) == 0 && ((uintptr_t)out & 15u) == 0;
+    __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0): the wave's LDS writes done
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll 4
-  for (int q = 0; q < 32; ++q) {                        // 4 rows of 16 lanes x 8 columns
-    const int r = q * 4 + lane / 16;
-    const int col = n0 + wn * 128 + (lane % 16) * 8;
-    int dst_row;
-    if constexpr (kMx) {
-      dst_row = row0 + wm * 128 + r;
-      if (dst_row >= row_end) continue;
-    } else {
-      dst_row = s_row[wm * 128 + r];
-      if (dst_row >= S) continue;
+    for (int q = 0; q < 16; ++q) {                      // 4 rows of 16 lanes x 8 columns
+      const int lr = q * 4 + lane / 16;
+      const int c = lane % 16;
+      const int r = 64 * h + lr;                        // row within the wave's 128
+      const int col = n0 + wn * 128 + c * 8;
+      int dst_row;
+      if constexpr (kMx) {
+        dst_row = row0 + wm * 128 + r;
+        if (dst_row >= row_end) continue;
+      } else {
+        dst_row = s_row[wm * 128 + r];
+        if (dst_row >= S) continue;
+      }
+      if (col >= N) continue;
+      const uint8_t *src = stg + lr * 256 + ((c ^ (lr & 15)) << 4);
+      uint16_t *dst = out + (size_t)dst_row * N + col;
+      if (vec && col + 8 <= N) {
+        *reinterpret_cast<i32x4 *>(dst) = *reinterpret_cast<const i32x4 *>(src);
+      } else {
+        const uint16_t *s16 = reinterpret_cast<const uint16_t *>(src);
+        for (int cc = 0; cc < 8 && col + cc < N; ++cc) dst[cc] = s16[cc];
+      }
     }
-    if (col >= N) continue;
-    const uint16_t *src = t + r * 128 + (lane % 16) * 8;
-    uint16_t *dst = out + (size_t)dst_row * N + col;
-    if (vec && col + 8 <= N) {
-      *reinterpret_cast<i32x4 *>(dst) = *reinterpret_cast<const i32x4 *>(src);
-    } else {
-      for (int c = 0; c < 8 && col + c < N; ++c) dst[c] = src[c];
-    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0): staging read before reuse
+    __builtin_amdgcn_wave_barrier();
   }
   }  // busy
   }  // tiles of chunk xq

@@ -76,14 +76,17 @@ def parse():
 
 
 GEMM_SOURCES = ("qmoe_gemm.hip", "qmoe_internal.h")
+ACT_SOURCES = ("qmoe_quant.hip", "qmoe_internal.h")
 
 
-def kernel_source_hash():
-    """sha256 over the grouped-GEMM kernel sources: a recorded HBM traffic
-    figure is only valid for the kernel it was counted on."""
+def kernel_source_hash(workload=None):
+    """sha256 over the sources of the workload's timed kernel (the grouped
+    GEMM, or the fused activation quantization): a recorded HBM traffic figure
+    is only valid for the kernel it was counted on."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "quantized_moe_grouped_top_amd", "csrc")
-    for name in GEMM_SOURCES:
+    act = workload is not None and workload.startswith(("swiglu_", "srelu_"))
+    for name in ACT_SOURCES if act else GEMM_SOURCES:
         with open(os.path.join(d, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -94,7 +97,7 @@ def recorded_traffic(workload):
     WRITE_SIZE, scaled by the copy-kernel factor) for this workload, read from
     the traffic summaries under profiles/; None when there is none or when the
     kernel sources changed since the counters were taken."""
-    want = kernel_source_hash()
+    want = kernel_source_hash(workload)
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*traffic*.md"))):
         text = open(path).read()
         fields = dict(re.findall(r"^- (\w+): `([^`]*)`", text, re.M))

@@ -340,7 +340,7 @@ def _mx_decode_rows(q_rows, sf_rows):
     return (v * e8m0_decode(sf_rows)[..., None]).reshape(R, K)
 
 
-def grouped_gemm_mxfp8(a_q, a_sf, w_q, w_sf, m_offsets, rows=None, cols=None):
+def grouped_gemm_mxfp8(a_q, a_sf, w_q, w_sf, m_offsets, rows=None, cols=None, as_float32=False):
     """MXFP8 grouped linear over expert-contiguous row segments ("[PyTorch] Let
     GroupedLinear accept MXFP8 input and gradient").
 
@@ -348,7 +348,7 @@ def grouped_gemm_mxfp8(a_q, a_sf, w_q, w_sf, m_offsets, rows=None, cols=None):
     128 rows (see ``quantize_act_mxfp8``); w_q uint8 [E, N, K] with w_sf
     [E, N, K/32].  acc[r, n] = sum over blocks of 2^(ba+bw-254) * sum(qa*qw),
     evaluated in float64; the output is bf16(fl32(acc)) as uint16
-    [len(rows), len(cols)]."""
+    [len(rows), len(cols)] (or fl32(acc) itself with as_float32)."""
     a_q = np.asarray(a_q)
     w_q = np.asarray(w_q)
     mo = np.asarray(m_offsets, dtype=np.int64)
@@ -365,7 +365,7 @@ def grouped_gemm_mxfp8(a_q, a_sf, w_q, w_sf, m_offsets, rows=None, cols=None):
         a = _mx_decode_rows(a_q[r], np.asarray(a_sf)[po[e] + (r - mo[e])])
         w = _mx_decode_rows(w_q[e][cols], np.asarray(w_sf)[e][cols])
         out[sel] = a @ w.T
-    return bf16_round(out.astype(np.float32))
+    return out.astype(np.float32) if as_float32 else bf16_round(out.astype(np.float32))
 
 
 # ----------------------------------------------------------------------------

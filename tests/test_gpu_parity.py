@@ -508,6 +508,114 @@ def test_act_quantize_full_size_sampled(act, mode):
 
 
 # ----------------------------------------------------------------------------
+# a whole expert FFN: up projection -> fused SwiGLU + quantization -> down
+# projection (the chaining of the up and down GEMMs through the activation)
+# ----------------------------------------------------------------------------
+def test_expert_ffn_mxfp8_chain():
+    """MXFP8 (no router): x -> MXFP8 -> up GEMM [rows, 2H] bf16 -> SwiGLU +
+    MXFP8 (per-expert padded scales) -> down GEMM [rows, N2] bf16.  Checked
+    stage by stage through the chained buffers: the up projection against the
+    oracle's, and the output against the oracle's activation + down
+    projection of the device's own up-projection rows.  (An end-to-end
+    comparison against the oracle's separate chain is only reported: a bf16
+    unit of difference in an intermediate value can move an e4m3 code or a
+    block scale of the re-quantized activation, which the down projection
+    then carries.)"""
+    seg, K, H, N2 = (100, 37, 0, 200), 256, 128, 192
+    what = f"ffn mxfp8 seg={seg} K={K} H={H} N2={N2}"
+    _announce(what)
+    rows, E = sum(seg), len(seg)
+    s0 = synth.seed_of(what)
+    x = synth.make_act_input(rows, K, s0)
+    w1 = synth.make_weights(E, 2 * H, K, s0 + 1)
+    w2 = synth.make_weights(E, N2, H, s0 + 2)
+    mo = synth.make_segments(seg)
+    # device chain
+    up = runner.MxMoE(rows, K, 2 * H, E)
+    w1q, w1s = runner.quantize_weights(w1.to(DEV), "mxfp8")
+    w2q, w2s = runner.quantize_weights(w2.to(DEV), "mxfp8")
+    mo_d = mo.to(DEV)
+    y1 = up.forward(x.to(DEV), mo_d, w1q, w1s)
+    act = runner.ActQuant(rows, H, E, "swiglu", "mxfp8")
+    q2 = act(y1, mo_d)
+    out = torch.empty(rows, N2, dtype=torch.int16, device=DEV)
+    qm.moe_grouped_gemm_mxfp8(q2, act.sf, w2q, w2s, mo_d, rows, H, N2, E, out)
+    torch.cuda.synchronize()
+    # oracle, stage by stage
+    mo_np = mo.numpy().astype(np.int64)
+    aq, asf = O.quantize_act_mxfp8(bits16(x), mo_np)
+    w1q_r, w1s_r = O.quantize_weight_mxfp8(w1.numpy())
+    y1_32 = O.grouped_gemm_mxfp8(aq, asf, w1q_r, w1s_r, mo_np, as_float32=True)
+    y1_ref = F.bf16_round(y1_32)
+    y1_gpu = bits16(y1)
+    assert_bf16_out(y1_gpu, y1_32, y1_ref, what + " up")
+    w2q_r, w2s_r = O.quantize_weight_mxfp8(w2.numpy())
+    q2_r, sf2_r = O.act_quantize_mxfp8(y1_gpu, mo_np, O.ACT_SWIGLU)
+    q2_g = q2.cpu().numpy()
+    sf2_g = act.sf.cpu().numpy()[:sf2_r.shape[0]]
+    print(f"  {what}: activation codes differing {np.mean(q2_g != q2_r):.2e}, "
+          f"scale bytes differing {np.mean(sf2_g != sf2_r):.2e}", flush=True)
+    # the oracle's float32 result: the device's output is its bf16 rounding
+    ref32 = O.grouped_gemm_mxfp8(q2_r, sf2_r, w2q_r, w2s_r, mo_np, as_float32=True)
+    assert_bf16_out(bits16(out), ref32, F.bf16_round(ref32), what + " down")
+    # end to end against the oracle's own chain: reported
+    q2_e, sf2_e = O.act_quantize_mxfp8(y1_ref, mo_np, O.ACT_SWIGLU)
+    e2e = F.bf16_decode(O.grouped_gemm_mxfp8(q2_e, sf2_e, w2q_r, w2s_r, mo_np))
+    rms = float(np.sqrt(np.mean(e2e ** 2)))
+    print(f"  {what}: end to end max|gpu-oracle chain|/rms = "
+          f"{np.max(np.abs(F.bf16_decode(bits16(out)) - e2e)) / rms:.3e}; activation codes "
+          f"differing from the oracle chain's: {np.mean(q2.cpu().numpy() != q2_e):.2e}")
+
+
+def test_expert_ffn_fp8_routed_chain():
+    """Routed fp8: route -> fp8 x -> up GEMM per slot (router weight 1) ->
+    SwiGLU + fp8 per tensor over the slots -> down GEMM per slot (M' = M *
+    top_k rows, top_k' = 1: a slot is its own row, the router weight applied
+    here) -> combine.  Checked stage by stage as the MXFP8 chain."""
+    M, K, H, N2, E, top_k = 96, 256, 128, 160, 4, 2
+    what = f"ffn fp8 routed M={M} K={K} H={H} N2={N2} E={E}"
+    _announce(what)
+    s0 = synth.seed_of(what)
+    x = synth.make_act_input(M, K, s0)
+    lg = synth.make_logits(M, E, s0 + 3)
+    w1 = synth.make_weights(E, 2 * H, K, s0 + 1)
+    w2 = synth.make_weights(E, N2, H, s0 + 2)
+    S = M * top_k
+    moe = runner.RoutedMoE("fp8", M, K, 2 * H, E, top_k, block_m=16)
+    w1q, w1s = runner.quantize_weights(w1.to(DEV), "fp8")
+    w2q, w2s = runner.quantize_weights(w2.to(DEV), "fp8")
+    moe.route(lg.to(DEV))
+    moe.quantize(x.to(DEV))
+    ones = torch.ones(M, top_k, dtype=torch.float32, device=DEV)
+    qm.moe_grouped_gemm_fp8w8a8(moe.a_q, moe.a_scale, w1q, w1s, qm.MOE_W_ROWMAJOR,
+                                moe.sorted_token_ids, moe.expert_ids, moe.num_tokens_post_padded,
+                                ones, M, K, 2 * H, E, top_k, moe.block_m, moe.y)
+    act = runner.ActQuant(S, H, 1, "swiglu", "fp8")
+    q2 = act(moe.y)
+    y2 = torch.empty(S, N2, dtype=torch.int16, device=DEV)
+    qm.moe_grouped_gemm_fp8w8a8(q2, act.scale, w2q, w2s, qm.MOE_W_ROWMAJOR,
+                                moe.sorted_token_ids, moe.expert_ids, moe.num_tokens_post_padded,
+                                moe.topk_weights, S, H, N2, E, 1, moe.block_m, y2)
+    out = torch.empty(M, N2, dtype=torch.int16, device=DEV)
+    qm.moe_combine(y2, M, N2, top_k, out)
+    torch.cuda.synchronize()
+    # oracle, stage by stage (routing choices are bit-exact, so the oracle's
+    # ids are the device's; its router weights are used on its side)
+    ids, wts = O.route_topk(lg.numpy(), top_k)
+    np.testing.assert_array_equal(moe.topk_ids.cpu().numpy(), ids)
+    aq, sa = O.quantize_act_fp8(bits16(x))
+    w1q_r, w1s_r = O.quantize_weight_fp8(w1.numpy())
+    y1_32 = O.grouped_gemm_fp8w8a8(aq, sa, w1q_r, w1s_r, ids, np.ones_like(wts))
+    y1_gpu = bits16(moe.y)
+    assert_bf16_out(y1_gpu, y1_32, O.slot_results_bf16(y1_32), what + " up")
+    q2_r, s2_r = O.act_quantize_fp8(y1_gpu, O.ACT_SWIGLU)
+    w2q_r, w2s_r = O.quantize_weight_fp8(w2.numpy())
+    y2_r = O.grouped_gemm_fp8w8a8(q2_r, s2_r, w2q_r, w2s_r, ids.reshape(-1, 1), wts.reshape(-1, 1))
+    out32, out_ref = O.combine(F.bf16_decode(O.slot_results_bf16(y2_r)), top_k)
+    assert_bf16_out(bits16(out), out32, out_ref, what + " down")
+
+
+# ----------------------------------------------------------------------------
 # codecs through the library
 # ----------------------------------------------------------------------------
 def _structured_values():

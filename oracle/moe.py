@@ -164,6 +164,21 @@ def quantize_weight_int8(w):
     return np.clip(q, -127, 127).astype(np.int8), s
 
 
+def quantize_act_int8_rows(x_bf16):
+    """Dynamic per-token (per-row) symmetric int8 quantization of bf16
+    activations [M, K] ("Enabling MOE Quantization using linear
+    decomposition", Summary: the int8 dynamic-activation family, "int8dq"):
+    the rule of the int8 weights applied to each activation row,
+    s_t = fl32(amax_t / 127) (1 for a zero row),
+    q = clamp(round_half_even(fl32(x * fl32(1 / s_t))), -127, 127).
+    Returns (q int8 [M, K], s float32 [M])."""
+    x = bf16_decode(x_bf16).astype(np.float32)
+    s = int8_channel_scale(x)
+    inv = (np.float32(1.0) / s).astype(np.float32)
+    q = np.rint(x * inv[..., None])                  # float32 product, half to even
+    return np.clip(q, -127, 127).astype(np.int8), s
+
+
 def mx_scale_byte(amax32):
     """e8m0 byte of the shared scale 2^(floor(log2 amax) - 8) of each block:
     clamp(exponent_field(amax) - 8, 0, 254); an all-zero block gives 0."""
@@ -331,6 +346,33 @@ def grouped_gemm_int8w8a16(a_bf16, w_q, w_scale, topk_ids, topk_weights,
                     lambda e, c: w_q[e][c].astype(np.float64),
                     lambda e, c: ws[e][c],
                     topk_ids, topk_weights, w_q.shape[1], slots, cols)
+
+
+def grouped_gemm_int8w8a8(a_q, a_scale, w_q, w_scale, topk_ids, topk_weights,
+                          slots=None, cols=None):
+    """int8 W8A8 with dynamic per-token activation scales ("int8dq" of
+    "Enabling MOE Quantization using linear decomposition", Summary): int8
+    activation rows (scale a_scale[t] per token) x int8 weights (scale per
+    expert and output channel).  For every selected slot i (token t = i //
+    top_k, expert e) and column n: y[i, n] = (q_a[t] . q_w[e, n]) * a_scale[t]
+    * w_scale[e, n] * w[i]; the integer dot product is exact in float64
+    (|sum| < 2^53), the product of the factors is taken in float64 and
+    rounded once to float32."""
+    a_q = np.asarray(a_q)
+    w_q = np.asarray(w_q)
+    sa = np.asarray(a_scale, dtype=np.float32).astype(np.float64)
+    ws = np.asarray(w_scale, dtype=np.float32).astype(np.float64)
+    top_k = np.asarray(topk_ids).shape[1]
+    sel, experts = _slots_by_expert(topk_ids, slots)
+    cols = np.arange(w_q.shape[1]) if cols is None else np.asarray(cols, dtype=np.int64)
+    wt = np.asarray(topk_weights, dtype=np.float32).reshape(-1).astype(np.float64)
+    y = np.zeros((sel.size, cols.size), dtype=np.float64)
+    for e in np.unique(experts):
+        rows = np.nonzero(experts == e)[0]
+        tokens = sel[rows] // top_k
+        dot = a_q[tokens].astype(np.float64) @ w_q[int(e)][cols].astype(np.float64).T
+        y[rows] = dot * sa[tokens][:, None] * ws[int(e)][cols][None, :] * wt[sel[rows]][:, None]
+    return y.astype(np.float32)
 
 
 def _mx_decode_rows(q_rows, sf_rows):

@@ -183,3 +183,38 @@ def test_slot_results_bf16_match_torch_rounding():
     y.reshape(-1)[:special.size] = special
     ref = torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     np.testing.assert_array_equal(O.slot_results_bf16(y), ref)
+
+
+# ------------------------------------------------- int8 W8A8 (dynamic) ----
+def test_int8w8a8_brute_force():
+    """Exact rational arithmetic on a tiny routed case: the integer dot
+    product times the token scale, the channel scale and the router weight,
+    rounded once to float32."""
+    rng = np.random.default_rng(13)
+    M, K, N, E, top_k = 3, 32, 5, 4, 2
+    x, w, lg = _tiny(rng, M, K, N, E)
+    ids, wts = O.route_topk(lg, top_k)
+    aq, sa = O.quantize_act_int8_rows(x)
+    wq, sw = O.quantize_weight_int8(w)
+    y = np.zeros((M * top_k, N), np.float32)
+    for t in range(M):
+        for j in range(top_k):
+            e = int(ids[t, j])
+            for n in range(N):
+                dot = sum(int(aq[t, k]) * int(wq[e, n, k]) for k in range(K))
+                y[t * top_k + j, n] = np.float32(float(Fraction(dot) * _fr(sa[t]) * _fr(sw[e, n])
+                                                       * _fr(wts[t, j])))
+    np.testing.assert_array_equal(O.grouped_gemm_int8w8a8(aq, sa, wq, sw, ids, wts), y)
+
+
+def test_int8w8a8_integer_identity():
+    """Unit scales and router weight 1: the result is the plain integer
+    product of the codes (exact in float32 below 2^24)."""
+    rng = np.random.default_rng(14)
+    M, K, N = 5, 64, 7
+    aq = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    wq = rng.integers(-127, 128, (1, N, K)).astype(np.int8)
+    ids = np.zeros((M, 1), np.int32)
+    y = O.grouped_gemm_int8w8a8(aq, np.ones(M, np.float32), wq, np.ones((1, N), np.float32),
+                                ids, np.ones((M, 1), np.float32))
+    np.testing.assert_array_equal(y, (aq.astype(np.int64) @ wq[0].astype(np.int64).T).astype(np.float32))

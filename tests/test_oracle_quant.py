@@ -206,3 +206,30 @@ def test_mxfp8_zero_block_and_weights_layout():
     q2, b2 = O.quantize_mxfp8_rows(w[1])
     np.testing.assert_array_equal(wq[1], q2)
     np.testing.assert_array_equal(wsf[1], b2)
+
+
+def test_int8_activation_rows_brute_force():
+    """Per-token int8 of bf16 rows by exact arithmetic: the scale, every
+    code, +-127 at the row's amax, a zero row."""
+    rng = np.random.default_rng(5)
+    x = F.bf16_round((rng.standard_normal((4, 40)) * np.array([[1.0], [1e-3], [50.0], [0.0]])).astype(np.float32))
+    q, s = O.quantize_act_int8_rows(x)
+    xv = F.bf16_decode(x)
+    for t in range(4):
+        amax = float(np.max(np.abs(xv[t])))
+        s_ref = np.float32(1.0) if amax == 0 else np.float32(Fraction(amax) / 127)
+        assert s[t] == s_ref
+        inv = np.float32(Fraction(1) / Fraction(float(s_ref)))
+        for k in range(40):
+            prod = np.float32(Fraction(float(xv[t, k])) * Fraction(float(inv)))
+            assert int(q[t, k]) == max(-127, min(127, _round_half_even(Fraction(float(prod)))))
+        if amax:
+            assert int(np.max(np.abs(q[t].astype(int)))) == 127
+        else:
+            assert not q[t].any()
+    # the error bound of a round-to-nearest code: |q s - x| <= s / 2 (plus the
+    # rounding of the product), and symmetry
+    assert np.all(np.abs(q.astype(np.float64) * s[:, None] - xv) <= s[:, None] * (0.5 + 1e-6))
+    q2, s2 = O.quantize_act_int8_rows(F.bf16_round(-xv.astype(np.float32)))
+    np.testing.assert_array_equal(q2, -q)
+    np.testing.assert_array_equal(s2, s)

@@ -35,7 +35,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = {"fp8": 5033.0, "mxfp8": 5033.0, "bf16": 2516.0}
+MFMA_PEAK_TFLOPS = {"fp8": 5033.0, "mxfp8": 5033.0, "bf16": 2516.0, "int8": 5033.0}
 DEFAULT_WORKLOAD = "int8w8a16_m64_k4096_n14336"
 
 
@@ -54,6 +54,8 @@ def alg_bytes(wl, active_experts=None):
         return M * K + E * N * K + 4 * (E + 1) + M * wl.top_k * N * 2
     if wl.fmt == "int8":
         return 2 * M * K + E * N * K + 4 * E * N + M * wl.top_k * N * 2
+    if wl.fmt == "int8dq":      # int8 rows + one scale per token, int8 weights + channel scales
+        return M * K + 4 * M + E * N * K + 4 * E * N + M * wl.top_k * N * 2
     # MXFP8: data + e8m0 scales of both operands, bf16 output rows
     return M * K * (1 + 1 / 32) + E * N * K * (1 + 1 / 32) + 2 * M * N
 
@@ -170,6 +172,9 @@ def cpu_baseline(wl, case, target_s):
             if wl.fmt == "fp8":
                 aq, sa = O.quantize_act_fp8(x)
                 y = O.grouped_gemm_fp8w8a8(aq, sa, wq, ws, ids, wts)
+            elif wl.fmt == "int8dq":
+                aq, sa = O.quantize_act_int8_rows(x)
+                y = O.grouped_gemm_int8w8a8(aq, sa, wq, ws, ids, wts)
             else:
                 y = O.grouped_gemm_int8w8a16(x, wq, ws, ids, wts)
             O.combine(F.bf16_decode(O.slot_results_bf16(y)), wl.top_k)
@@ -264,12 +269,12 @@ def main():
     gemm_ms = sum(a.elapsed_time(b) for a, b in events) / args.steps
 
     active = wl.E
-    if wl.fmt in ("fp8", "int8"):
+    if wl.fmt in ("fp8", "int8", "int8dq"):
         ids = moe.topk_ids.cpu()
         active = int(torch.unique(ids).numel())
     nbytes = alg_bytes(wl, active)
     ms = elapsed * 1e3 / args.steps
-    dtype = {"fp8": "fp8", "int8": "bf16", "mxfp8": "mxfp8", "act_fp8": "fp8",
+    dtype = {"fp8": "fp8", "int8": "bf16", "int8dq": "int8", "mxfp8": "mxfp8", "act_fp8": "fp8",
              "act_mxfp8": "mxfp8"}[wl.fmt]
     is_act = wl.fmt.startswith("act_")
     bound = "hbm" if is_act or wl.flops / nbytes < 600 else "mfma"

@@ -57,7 +57,8 @@ extern "C" {
 /* ---- quantization modes ------------------------------------------------- */
 #define MOE_Q_FP8_PER_TENSOR   0  /* e4m3 + one fp32 scale per tensor (per expert for weights) */
 #define MOE_Q_MXFP8            1  /* e4m3 + one e8m0 scale per 32 values along K */
-#define MOE_Q_INT8_PER_CHANNEL 2  /* weights only: int8 + one fp32 scale per output channel */
+#define MOE_Q_INT8_PER_CHANNEL 2  /* int8 + one fp32 scale per row: per output channel
+                                     (weights), per token (activations) */
 
 /* ---- activations fused with the quantization (moe_act_quantize) -------- */
 #define MOE_ACT_SWIGLU 0  /* y = silu(g) * u, row = [g | u] (2H inputs -> H outputs) */
@@ -162,9 +163,15 @@ int moe_align_block_size(const float *logits, int M, int E, int top_k, int block
  *   expert's block are written with 0.  scale_e8m0 must hold
  *   moe_mx_scale_rows(rows, E) rows; rows past the padded total are not
  *   touched.  scale/workspace unused (may be NULL).
+ * mode MOE_Q_INT8_PER_CHANNEL: dynamic per-token int8 ("Enabling MOE
+ *   Quantization using linear decomposition", Summary: the int8 dynamic
+ *   activation family), per row t s_t = fl32(amax_t/127) (1 if zero),
+ *   q = clamp(round_half_even(fl32(x * fl32(1/s_t))), -127, 127).  Writes q
+ *   [rows, K] (int8 in the uint8 buffer, 8-byte aligned) and scale [rows].
+ *   m_offsets/E/scale_e8m0/workspace unused.
  *
- * K must be a multiple of 32 (MXFP8) or 8 (fp8); MXFP8 takes at most 2^30
- * rows.  rows = 0 is valid. */
+ * K must be a multiple of 32 (MXFP8) or 8 (fp8, int8); MXFP8 takes at most
+ * 2^30 rows.  rows = 0 is valid. */
 int moe_quantize_act(const uint16_t *x, int rows, int K, int mode,
                      const int *m_offsets, int E, uint8_t *q, float *scale,
                      uint8_t *scale_e8m0, void *workspace, hipStream_t stream);
@@ -258,6 +265,22 @@ int moe_grouped_gemm_fp8w8a8(const uint8_t *a_q, const float *a_scale,
                              const int *num_tokens_post_padded,
                              const float *topk_weights, int M, int K, int N, int E,
                              int top_k, int block_m, uint16_t *y, hipStream_t stream);
+
+/* Routed int8 W8A8 grouped GEMM with dynamic per-token activation scales
+ * ("Enabling MOE Quantization using linear decomposition", Summary: int8
+ * dynamic activations x int8 weights): as moe_grouped_gemm_fp8w8a8 with
+ *     y[i, n] = bf16( (sum_k a[t,k] * w[e,n,k]) * a_scale[t] * w_scale[e, n] * topk_weights[i] )
+ * for int8 a_q [M, K] with a_scale [M] f32 (moe_quantize_act with
+ * MOE_Q_INT8_PER_CHANNEL), int8 w_q in layout w_layout with w_scale [E, N]
+ * f32 (moe_quantize_weights with MOE_Q_INT8_PER_CHANNEL).  The products are
+ * accumulated exactly in int32 on the int8 MFMA and converted to fp32 once.
+ * K must be a multiple of 128 and N of 8; block_m must be 16 or 128. */
+int moe_grouped_gemm_int8w8a8(const int8_t *a_q, const float *a_scale,
+                              const int8_t *w_q, const float *w_scale, int w_layout,
+                              const int *sorted_token_ids, const int *expert_ids,
+                              const int *num_tokens_post_padded,
+                              const float *topk_weights, int M, int K, int N, int E,
+                              int top_k, int block_m, uint16_t *y, hipStream_t stream);
 
 /* Routed int8 W8A16 grouped GEMM: as moe_grouped_gemm_fp8w8a8 with
  *     y[i, n] = bf16( (sum_k a[t,k] * w[e,n,k]) * w_scale[e, n] * topk_weights[i] )

@@ -30,6 +30,7 @@ EXPORTS = [
     "moe_align_block_size", "moe_quantize_act", "moe_act_quantize", "moe_quantize_weights",
     "moe_pack_weights",
     "moe_grouped_gemm_fp8w8a8",
+    "moe_grouped_gemm_int8w8a8",
     "moe_grouped_gemm_int8w8a16", "moe_grouped_gemm_mxfp8", "moe_combine",
 ]
 
@@ -62,6 +63,7 @@ _SIGS = {
     "moe_act_quantize": (_I, [_P, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P]),
     "moe_quantize_weights": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "moe_grouped_gemm_fp8w8a8": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
+    "moe_grouped_gemm_int8w8a8": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
     "moe_grouped_gemm_int8w8a16": (_I, [_P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
     "moe_grouped_gemm_mxfp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "moe_combine": (_I, [_P, _I, _I, _I, _P, _P]),
@@ -168,6 +170,15 @@ def moe_grouped_gemm_fp8w8a8(a_q, a_scale, w_q, w_scale, w_layout, sorted_token_
                              num_tokens_post_padded, topk_weights, M, K, N, E, top_k, block_m,
                              y, stream=None):
     return _check(lib().moe_grouped_gemm_fp8w8a8(
+        _ptr(a_q), _ptr(a_scale), _ptr(w_q), _ptr(w_scale), w_layout, _ptr(sorted_token_ids),
+        _ptr(expert_ids), _ptr(num_tokens_post_padded), _ptr(topk_weights), M, K, N, E, top_k,
+        block_m, _ptr(y), _stream(stream)))
+
+
+def moe_grouped_gemm_int8w8a8(a_q, a_scale, w_q, w_scale, w_layout, sorted_token_ids, expert_ids,
+                              num_tokens_post_padded, topk_weights, M, K, N, E, top_k, block_m,
+                              y, stream=None):
+    return _check(lib().moe_grouped_gemm_int8w8a8(
         _ptr(a_q), _ptr(a_scale), _ptr(w_q), _ptr(w_scale), w_layout, _ptr(sorted_token_ids),
         _ptr(expert_ids), _ptr(num_tokens_post_padded), _ptr(topk_weights), M, K, N, E, top_k,
         block_m, _ptr(y), _stream(stream)))

@@ -179,6 +179,15 @@ int moe_quantize_act(const uint16_t *x, int rows, int K, int mode, const int *m_
                                                          (float *)workspace, stream),
                       fn);
   }
+  if (mode == MOE_Q_INT8_PER_CHANNEL) {                  // activations: one scale per row
+    REQUIRE(K % 8 == 0, MOE_EUNSUPPORTED, "%s: K=%d is not a multiple of 8", fn, K);
+    if (rows == 0) return ok();
+    REQUIRE(x && q && scale, MOE_EINVAL, "%s: null pointer argument", fn);
+    REQUIRE(aligned16(x) && ((uintptr_t)q & 7u) == 0, MOE_EINVAL,
+            "%s: x must be 16-byte and q 8-byte aligned", fn);
+    return hip_status(qmoe::launch_quant_int8_rows_bf16(x, rows, K, (int8_t *)q, scale, stream),
+                      fn);
+  }
   if (mode == MOE_Q_MXFP8) {
     REQUIRE(E >= 1 && E <= MOE_MAX_EXPERTS, MOE_EINVAL, "%s: E=%d", fn, E);
     REQUIRE(K % 32 == 0, MOE_EUNSUPPORTED, "%s: K=%d is not a multiple of 32", fn, K);
@@ -272,6 +281,24 @@ int moe_grouped_gemm_fp8w8a8(const uint8_t *a_q, const float *a_scale, const uin
                      E, top_k, block_m, (int)(max_padded_ll(M, E, top_k, block_m) / block_m),
                      w_layout, y};
   return hip_status(qmoe::launch_gemm_fp8(a_q, a_scale, w_q, w_scale, r, stream), fn);
+}
+
+int moe_grouped_gemm_int8w8a8(const int8_t *a_q, const float *a_scale, const int8_t *w_q,
+                              const float *w_scale, int w_layout, const int *sorted_token_ids,
+                              const int *expert_ids, const int *num_tokens_post_padded,
+                              const float *topk_weights, int M, int K, int N, int E, int top_k,
+                              int block_m, uint16_t *y, hipStream_t stream) {
+  const char *fn = "moe_grouped_gemm_int8w8a8";
+  int rc = check_routed_gemm(a_q, w_q, w_scale, w_layout, sorted_token_ids, expert_ids,
+                             num_tokens_post_padded, topk_weights, y, M, K, N, E, top_k, block_m,
+                             128, fn);
+  if (rc) return rc;
+  if (M == 0) return ok();
+  REQUIRE(a_scale, MOE_EINVAL, "%s: null a_scale", fn);
+  qmoe::RoutedArgs r{sorted_token_ids, expert_ids, num_tokens_post_padded, topk_weights, M, K, N,
+                     E, top_k, block_m, (int)(max_padded_ll(M, E, top_k, block_m) / block_m),
+                     w_layout, y};
+  return hip_status(qmoe::launch_gemm_int8w8a8(a_q, a_scale, w_q, w_scale, r, stream), fn);
 }
 
 int moe_grouped_gemm_int8w8a16(const uint16_t *a, const int8_t *w_q, const float *w_scale,

@@ -51,6 +51,18 @@ __device__ __forceinline__ f32x4 mfma_mx(const i32x8 &a, const i32x8 &b, f32x4 c
                                          int sb) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
+// int8 x int8 -> int32 on two 16x16x64 MFMAs (the 32 bytes of a lane's
+// fragment as two 16-byte halves; A and B use the same k placement, and an
+// integer dot product does not depend on the order of its terms).  The
+// accumulator is carried in float registers as raw int32 bits.
+__device__ __forceinline__ f32x4 mfma_i8(const i32x8 &a, const i32x8 &b, f32x4 c) {
+  i32x4 ci = __builtin_bit_cast(i32x4, c);
+  ci = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_shufflevector(a, a, 0, 1, 2, 3),
+                                             __builtin_shufflevector(b, b, 0, 1, 2, 3), ci, 0, 0, 0);
+  ci = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_shufflevector(a, a, 4, 5, 6, 7),
+                                             __builtin_shufflevector(b, b, 4, 5, 6, 7), ci, 0, 0, 0);
+  return __builtin_bit_cast(f32x4, ci);
+}
 __device__ __forceinline__ f32x4 mfma_bf16(const i32x4 &a, const i32x4 &b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -184,13 +196,19 @@ __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int sw128(int r, int c) { return r * 128 + ((c ^ swz(r)) << 4); }
 __device__ __forceinline__ int sw256(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
 
-template <bool kInt8, bool kTiled>
+// stream kernel modes: fp8 W8A8, int8 W8A16 (bf16 activations), int8 W8A8
+// (int8 activations with one scale per token)
+enum { kSFp8 = 0, kSW8A16 = 1, kSI8 = 2 };
+
+template <int kMode, bool kTiled>
 __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ w, const float *__restrict__ w_scale,
     const int *__restrict__ sorted_ids, const int *__restrict__ expert_ids,
     const int *__restrict__ num_post, const float *__restrict__ topk_w, int M, int K, int N,
     int top_k, int groups, int tiles_per_group, int max_blocks, uint16_t *__restrict__ y) {
+  constexpr bool kInt8 = kMode == kSW8A16;               // bf16 activations, int8 weights
+  constexpr bool kI8 = kMode == kSI8;                    // int8 activations and weights
   using C = SCfg<kInt8>;
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[2 * C::kStage];
   __shared__ int s_slot[kSMB * 16];
@@ -456,7 +474,8 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
 #pragma unroll
             for (int i = 0; i < kSMB; ++i) {
               if (i >= nmb) break;
-              acc[t][i] = mfma_fp8(av[i], bv, acc[t][i]);
+              if constexpr (kI8) acc[t][i] = mfma_i8(av[i], bv, acc[t][i]);
+              else acc[t][i] = mfma_fp8(av[i], bv, acc[t][i]);
             }
           }
         }
@@ -481,7 +500,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
       // per-column scale of this workgroup's tiles (int8) or the fused scalar
       for (int c = tid; c < G * 64; c += kSThreads) {
         const int col = min(t_begin * 64 + c, N - 1);
-        s_scale[c] = kInt8 ? w_scale[(size_t)e * N + col] : a_scale[0] * w_scale[e];
+        s_scale[c] = kMode == kSFp8 ? a_scale[0] * w_scale[e] : w_scale[(size_t)e * N + col];
       }
       __syncthreads();
     }
@@ -498,7 +517,13 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
         for (int rr = 0; rr < 4; ++rr) {
           const int k = 16 * i + 4 * g + rr;
           const int slot = s_slot[k];
-          const float v = acc[t][i][rr] * cs * (slot < S ? topk_w[slot] : 0.0f);
+          float rw = slot < S ? topk_w[slot] : 0.0f;     // router weight (x token scale)
+          float acc_v = acc[t][i][rr];
+          if constexpr (kI8) {
+            acc_v = (float)__builtin_bit_cast(int, acc_v);
+            rw *= slot < S ? a_scale[slot / top_k] : 0.0f;
+          }
+          const float v = acc_v * cs * rw;
           const float vn = __shfl_xor(v, 1);           // the next column's value
           // N is a multiple of 8: an even column and its neighbour are both
           // inside the row or both past its end
@@ -510,7 +535,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
   }
 }
 
-enum { kFmtFp8 = 0, kFmtInt8 = 1, kFmtMx = 2 };
+enum { kFmtFp8 = 0, kFmtInt8 = 1, kFmtMx = 2, kFmtI8 = 3 };
 
 // =============================================================================
 // block_m = 128 (fp8 W8A8, int8 W8A16) and MXFP8: DMA-fed MFMA tiles
@@ -1197,6 +1222,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gemm_big_kernel(
 // hands a ring slot back to the DMA sits between the two halves of a stage,
 // after this wave's reads of the stage have completed.
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ f32x16 mfma32_fp8(const i32x8 &a, const i32x8 &b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
@@ -1229,7 +1255,8 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[2 * kHStage];
   __shared__ __attribute__((aligned(16))) uint8_t s_sf[kMx ? 2 * kHSf : 16];
   __shared__ int s_row[kHBM];
-  __shared__ float s_rs[kMx ? 1 : kHBM];               // fp8: per-row output scale
+  __shared__ float s_rs[kMx ? 1 : kHBM];               // per-row output scale (not MXFP8)
+  __shared__ __attribute__((aligned(16))) float s_cs[kFmt == kFmtI8 ? kHBN : 4];  // int8: per column
   __shared__ int s_blk_first[kMaxExperts + 1];
   __shared__ int s_tile_first[kMaxExperts + 1];
   __shared__ int s_mo[kMx ? kMaxExperts + 1 : 1];
@@ -1310,8 +1337,16 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
       const int slot = r < nb_here * kGBM ? sorted_ids[(s_blk_first[e] + 2 * pr) * kGBM + r] : S;
       s_row[r] = slot;
       // the epilogue's row scale: activation x weight scale x router weight
-      s_rs[r] = slot < S ? a_scale[0] * w_scale[e] * topk_w[slot] : 0.0f;
+      // (int8 W8A8: the token's scale x router weight; the weight scale is
+      // per column)
+      if constexpr (kFmt == kFmtI8)
+        s_rs[r] = slot < S ? a_scale[slot / top_k] * topk_w[slot] : 0.0f;
+      else
+        s_rs[r] = slot < S ? a_scale[0] * w_scale[e] * topk_w[slot] : 0.0f;
     }
+  }
+  if constexpr (kFmt == kFmtI8) {
+    for (int c = tid; c < kHBN; c += kThr) s_cs[c] = w_scale[(size_t)e * N + min(n0 + c, N - 1)];
   }
   if constexpr (kMx) {
     row0 = s_mo[e] + 2 * pr * kGBM;
@@ -1450,8 +1485,18 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
     const int i = q >> 2, j = q & 3;
     const i32x8 av = __builtin_shufflevector(f.alo[i], f.ahi[i], 0, 1, 2, 3, 4, 5, 6, 7);
     const i32x8 bv = __builtin_shufflevector(f.blo[j], f.bhi[j], 0, 1, 2, 3, 4, 5, 6, 7);
-    if constexpr (kMx) acc[i][j] = mfma32_mx(bv, av, acc[i][j], f.sb[j], f.sa[i]);
-    else acc[i][j] = mfma32_fp8(bv, av, acc[i][j]);
+    if constexpr (kMx) {
+      acc[i][j] = mfma32_mx(bv, av, acc[i][j], f.sb[j], f.sa[i]);
+    } else if constexpr (kFmt == kFmtI8) {
+      // two 32x32x32 int8 MFMAs over the two 16-byte halves (A and B share
+      // the k placement); int32 accumulators carried as raw bits
+      i32x16 ci = __builtin_bit_cast(i32x16, acc[i][j]);
+      ci = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.blo[j], f.alo[i], ci, 0, 0, 0);
+      ci = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.bhi[j], f.ahi[i], ci, 0, 0, 0);
+      acc[i][j] = __builtin_bit_cast(f32x16, ci);
+    } else {
+      acc[i][j] = mfma32_fp8(bv, av, acc[i][j]);
+    }
   };
   auto pin_acc = [&]() {     // the accumulators are "used" here: no MFMA sinks past
 #pragma unroll
@@ -1544,10 +1589,21 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const f32x16 &c = acc[i][j];
+          f32x4 c;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) c[u] = acc[i][j][4 * k + u];
+          if constexpr (kFmt == kFmtI8) {
+            // int32 -> float, times the four columns' weight scales
+            const f32x4 cs = *reinterpret_cast<const f32x4 *>(&s_cs[wn * 128 + 32 * j + 8 * k + 4 * g]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const float raw = c[u];                   // (bit-cast a scalar, not an element)
+              c[u] = (float)__builtin_bit_cast(int, raw) * cs[u];
+            }
+          }
           i32x2 pk;
-          pk[0] = (int)f32x2_to_bf16x2(c[4 * k] * rs, c[4 * k + 1] * rs);
-          pk[1] = (int)f32x2_to_bf16x2(c[4 * k + 2] * rs, c[4 * k + 3] * rs);
+          pk[0] = (int)f32x2_to_bf16x2(c[0] * rs, c[1] * rs);
+          pk[1] = (int)f32x2_to_bf16x2(c[2] * rs, c[3] * rs);
           *reinterpret_cast<i32x2 *>(stg + lr * 256 + (((4 * j + k) ^ (lr & 15)) << 4) + 8 * g) = pk;
         }
     }
@@ -1649,7 +1705,7 @@ hipError_t launch_gemm_fp8(const uint8_t *a_q, const float *a_scale, const uint8
   if (r.block_m == 16) {
     int groups, tpg;
     stream_grid(r.N, r.E, groups, tpg);
-    auto k = r.w_layout ? stream_kernel<false, true> : stream_kernel<false, false>;
+    auto k = r.w_layout ? stream_kernel<kSFp8, true> : stream_kernel<kSFp8, false>;
     hipLaunchKernelGGL(k, dim3(r.E * groups), dim3(kSThreads), 0, s, a_q, a_scale, w_q, w_scale,
                        r.sorted_ids, r.expert_ids, r.num_post, r.topk_w, r.M, r.K, r.N, r.top_k,
                        groups, tpg, r.max_blocks, r.y);
@@ -1671,6 +1727,27 @@ hipError_t launch_gemm_fp8(const uint8_t *a_q, const float *a_scale, const uint8
   return hipGetLastError();
 }
 
+hipError_t launch_gemm_int8w8a8(const int8_t *a_q, const float *a_scale, const int8_t *w_q,
+                               const float *w_scale, const RoutedArgs &r, hipStream_t s) {
+  const uint8_t *ab = reinterpret_cast<const uint8_t *>(a_q);
+  const uint8_t *wb = reinterpret_cast<const uint8_t *>(w_q);
+  if (r.block_m == 16) {
+    int groups, tpg;
+    stream_grid(r.N, r.E, groups, tpg);
+    auto k = r.w_layout ? stream_kernel<kSI8, true> : stream_kernel<kSI8, false>;
+    hipLaunchKernelGGL(k, dim3(r.E * groups), dim3(kSThreads), 0, s, ab, a_scale, wb, w_scale,
+                       r.sorted_ids, r.expert_ids, r.num_post, r.topk_w, r.M, r.K, r.N, r.top_k,
+                       groups, tpg, r.max_blocks, r.y);
+  } else {
+    const long long tiles = (long long)(r.max_blocks / 2 + r.E) * ((r.N + kHBN - 1) / kHBN);
+    auto k = r.w_layout ? gemm_wide_kernel<kFmtI8, true> : gemm_wide_kernel<kFmtI8, false>;
+    hipLaunchKernelGGL(k, dim3(wide_grid(tiles)), dim3(256), 0, s, ab, a_scale, nullptr, wb,
+                       w_scale, nullptr, r.sorted_ids, r.expert_ids, r.topk_w, nullptr, r.M, r.K,
+                       r.N, r.E, r.top_k, r.max_blocks, r.y, next_launch_slot());
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_int8(const uint16_t *a, const int8_t *w_q, const float *w_scale,
                             const RoutedArgs &r, hipStream_t s) {
   const uint8_t *ab = reinterpret_cast<const uint8_t *>(a);
@@ -1678,7 +1755,7 @@ hipError_t launch_gemm_int8(const uint16_t *a, const int8_t *w_q, const float *w
   if (r.block_m == 16) {
     int groups, tpg;
     stream_grid(r.N, r.E, groups, tpg);
-    auto k = r.w_layout ? stream_kernel<true, true> : stream_kernel<true, false>;
+    auto k = r.w_layout ? stream_kernel<kSW8A16, true> : stream_kernel<kSW8A16, false>;
     hipLaunchKernelGGL(k, dim3(r.E * groups), dim3(kSThreads), 0, s, ab, nullptr, wb, w_scale,
                        r.sorted_ids, r.expert_ids, r.num_post, r.topk_w, r.M, r.K, r.N, r.top_k,
                        groups, tpg, r.max_blocks, r.y);

@@ -158,15 +158,17 @@ __global__ __launch_bounds__(kThreads) void quant_fp8_kernel(const Src *__restri
   }
 }
 
-// ---- int8 per output channel: one wavefront per row --------------------------
-__global__ __launch_bounds__(kThreads) void quant_int8_rows_kernel(const float *__restrict__ w,
+// ---- int8 per row (weights: per output channel; activations: per token):
+// one wavefront per row ----------------------------------------------------------
+template <typename Src>
+__global__ __launch_bounds__(kThreads) void quant_int8_rows_kernel(const Src *__restrict__ w,
                                                                    long long rows, int K,
                                                                    int8_t *__restrict__ q,
                                                                    float *__restrict__ scale) {
   const int lane = threadIdx.x & 63;
   const long long row = (long long)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const float *src = w + row * K;
+  const Src *src = w + row * K;
   float m = 0.0f;
   for (int k = lane * 8; k < K; k += 64 * 8) {
     float v[8];
@@ -616,12 +618,19 @@ hipError_t launch_quant_fp8_experts_f32(const float *w, int E, long long per, ui
 hipError_t launch_quant_int8_rows_f32(const float *w, long long rows, int K, int8_t *q,
                                       float *scale, hipStream_t s) {
   const long long blocks = (rows + kThreads / 64 - 1) / (kThreads / 64);
-  hipLaunchKernelGGL(quant_int8_rows_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, w,
-                     rows, K, q, scale);
+  hipLaunchKernelGGL(quant_int8_rows_kernel<float>, dim3((unsigned)blocks), dim3(kThreads), 0, s,
+                     w, rows, K, q, scale);
   return hipGetLastError();
 }
 
-// One wavefront per padded scale row; a workgroup of 4 wavefronts.
+hipError_t launch_quant_int8_rows_bf16(const uint16_t *x, long long rows, int K, int8_t *q,
+                                       float *scale, hipStream_t s) {
+  const long long blocks = (rows + kThreads / 64 - 1) / (kThreads / 64);
+  hipLaunchKernelGGL(quant_int8_rows_kernel<uint16_t>, dim3((unsigned)blocks), dim3(kThreads), 0,
+                     s, x, rows, K, q, scale);
+  return hipGetLastError();
+}
+
 // Workgroups of the padded-row MXFP8 kernel: one per R-row step, at most
 // kMxGrid (they stride beyond that).
 constexpr int kMxGrid = 8192;

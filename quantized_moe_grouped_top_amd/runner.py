@@ -5,7 +5,7 @@ memory only) and runs the hot path as a sequence of library calls on the
 current stream:
 
     routed formats : moe_align_block_size -> [moe_quantize_act] ->
-                     moe_grouped_gemm_{fp8w8a8,int8w8a16} -> moe_combine
+                     moe_grouped_gemm_{fp8w8a8,int8w8a8,int8w8a16} -> moe_combine
     MXFP8          : moe_quantize_act(MXFP8) -> moe_grouped_gemm_mxfp8
     activation     : moe_act_quantize (SwiGLU / SReLU + MXFP8 or fp8)
 
@@ -16,7 +16,8 @@ import torch
 
 from . import (MOE_ACT_SRELU, MOE_ACT_SWIGLU, MOE_Q_FP8_PER_TENSOR, MOE_Q_INT8_PER_CHANNEL, MOE_Q_MXFP8, MOE_W_ROWMAJOR,
                MOE_W_TILED, moe_act_quantize, moe_align_block_size, moe_align_max_padded, moe_combine,
-               moe_grouped_gemm_fp8w8a8, moe_grouped_gemm_int8w8a16, moe_grouped_gemm_mxfp8,
+               moe_grouped_gemm_fp8w8a8, moe_grouped_gemm_int8w8a8, moe_grouped_gemm_int8w8a16,
+               moe_grouped_gemm_mxfp8,
                moe_mx_scale_rows, moe_pack_weights, moe_packed_weight_bytes, moe_quantize_act,
                moe_quantize_weights, moe_quantize_workspace_bytes, moe_recommended_block_m)
 
@@ -36,7 +37,7 @@ def quantize_weights(w, fmt):
         ws = _empty((moe_quantize_workspace_bytes(MOE_Q_FP8_PER_TENSOR, E),), torch.uint8, dev)
         moe_quantize_weights(w, E, N, K, MOE_Q_FP8_PER_TENSOR, q, s, None, ws)
         return q, s
-    if fmt == "int8":
+    if fmt in ("int8", "int8dq"):
         q = _empty((E, N, K), torch.int8, dev)
         s = _empty((E, N), torch.float32, dev)
         moe_quantize_weights(w, E, N, K, MOE_Q_INT8_PER_CHANNEL, q, s, None, None)
@@ -58,11 +59,12 @@ def pack_weights(w_q):
 
 
 class RoutedMoE:
-    """fp8 W8A8 or int8 W8A16 MoE layer of fixed (M, K, N, E, top_k)."""
+    """fp8 W8A8, int8 W8A16 ("int8") or int8 W8A8 with per-token activation
+    scales ("int8dq") MoE layer of fixed (M, K, N, E, top_k)."""
 
     def __init__(self, fmt, M, K, N, E, top_k, device="cuda", block_m=None,
                  w_layout=MOE_W_ROWMAJOR):
-        assert fmt in ("fp8", "int8")
+        assert fmt in ("fp8", "int8", "int8dq")
         self.w_layout = w_layout
         self.fmt, self.M, self.K, self.N, self.E, self.top_k = fmt, M, K, N, E, top_k
         self.block_m = block_m or moe_recommended_block_m(M, E, top_k)
@@ -79,6 +81,9 @@ class RoutedMoE:
             self.a_scale = _empty((1,), torch.float32, dev)
             self.ws = _empty((moe_quantize_workspace_bytes(MOE_Q_FP8_PER_TENSOR, 1),),
                              torch.uint8, dev)
+        if fmt == "int8dq":
+            self.a_q = _empty((M, K), torch.int8, dev)
+            self.a_scale = _empty((max(M, 1),), torch.float32, dev)
         self.y = _empty((S, N), torch.int16, dev)      # bf16 bits, one row per slot
         self.out = _empty((M, N), torch.int16, dev)     # bf16 bits
 
@@ -91,6 +96,9 @@ class RoutedMoE:
         if self.fmt == "fp8":
             moe_quantize_act(x, self.M, self.K, MOE_Q_FP8_PER_TENSOR, None, 1, self.a_q,
                              self.a_scale, None, self.ws)
+        elif self.fmt == "int8dq":
+            moe_quantize_act(x, self.M, self.K, MOE_Q_INT8_PER_CHANNEL, None, 1, self.a_q,
+                             self.a_scale, None, None)
 
     def gemm(self, x, w_q, w_scale):
         if self.fmt == "fp8":
@@ -99,6 +107,11 @@ class RoutedMoE:
                                      self.expert_ids, self.num_tokens_post_padded,
                                      self.topk_weights, self.M, self.K, self.N, self.E,
                                      self.top_k, self.block_m, self.y)
+        elif self.fmt == "int8dq":
+            moe_grouped_gemm_int8w8a8(self.a_q, self.a_scale, w_q, w_scale, self.w_layout,
+                                      self.sorted_token_ids, self.expert_ids,
+                                      self.num_tokens_post_padded, self.topk_weights, self.M,
+                                      self.K, self.N, self.E, self.top_k, self.block_m, self.y)
         else:
             moe_grouped_gemm_int8w8a16(x, w_q, w_scale, self.w_layout, self.sorted_token_ids,
                                        self.expert_ids,

@@ -84,7 +84,7 @@ def oracle_weights_rows(w_dev, fmt, cols):
         s = np.array([O.fp8_tensor_scale(w_dev[e].cpu().numpy()) for e in range(E)], np.float32)
         q = np.stack([O.fp8_quantize_with_scale(rows[e], s[e]) for e in range(E)])
         return q, s
-    if fmt == "int8":
+    if fmt in ("int8", "int8dq"):
         return O.quantize_weight_int8(rows)
     q, b = O.quantize_weight_mxfp8(rows)
     return q, b

@@ -38,7 +38,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     h = ctypes.CDLL(qm.LIB_PATH)
     for n in names:
         assert hasattr(h, n), n
@@ -114,6 +114,33 @@ def test_gemm_int8_and_mxfp8_reject():
     with pytest.raises(qm.MoeError) as ei:
         qm.moe_grouped_gemm_mxfp8(FAKE, MIS, FAKE, FAKE, FAKE, 100, 256, 64, 4, FAKE, stream=0)
     assert ei.value.code == qm.MOE_EINVAL                       # misaligned scales
+
+
+def test_gemm_int8w8a8_and_int8_activation_quantizer_reject():
+    args = [FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, 64, 192, 128, 8, 2, 16, FAKE]
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_grouped_gemm_int8w8a8(*args, stream=0)
+    assert ei.value.code == qm.MOE_EUNSUPPORTED                 # K % 128
+    args[10] = 256
+    args[1] = 0
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_grouped_gemm_int8w8a8(*args, stream=0)
+    assert ei.value.code == qm.MOE_EINVAL                       # null a_scale
+    args[1] = FAKE
+    args[14] = 32
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_grouped_gemm_int8w8a8(*args, stream=0)
+    assert ei.value.code == qm.MOE_EUNSUPPORTED                 # block_m
+    args[14], args[9] = 16, 0
+    qm.moe_grouped_gemm_int8w8a8(*args, stream=0)               # M = 0: nothing to do
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_quantize_act(FAKE, 10, 100, qm.MOE_Q_INT8_PER_CHANNEL, None, 1, FAKE, FAKE, None,
+                            None, stream=0)
+    assert ei.value.code == qm.MOE_EUNSUPPORTED                 # K % 8
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_quantize_act(FAKE, 10, 64, qm.MOE_Q_INT8_PER_CHANNEL, None, 1, FAKE, None, None,
+                            None, stream=0)
+    assert ei.value.code == qm.MOE_EINVAL                       # no scale
 
 
 def test_quantize_and_combine_reject():

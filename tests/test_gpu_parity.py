@@ -104,6 +104,16 @@ def run_routed(wl, block_m=None, variant=0, full=True, n_tok=48, n_col=64, logit
         aq_full = np.zeros((M, K), np.uint8)
         aq_full[toks] = aq_rows
         y_ref = O.grouped_gemm_fp8w8a8(aq_full, sa, wq_full, ws_full, ids_ref, wts_ref, slots, cols)
+    elif wl.fmt == "int8dq":
+        # per-token scales: the checked tokens' rows alone fix them
+        aq_rows, sa_rows = O.quantize_act_int8_rows(x_np[toks])
+        np.testing.assert_array_equal(moe.a_q.cpu().numpy()[toks], aq_rows)
+        np.testing.assert_array_equal(moe.a_scale.cpu().numpy()[toks], sa_rows)
+        aq_full = np.zeros((M, K), np.int8)
+        aq_full[toks] = aq_rows
+        sa_full = np.ones(M, np.float32)
+        sa_full[toks] = sa_rows
+        y_ref = O.grouped_gemm_int8w8a8(aq_full, sa_full, wq_full, ws_full, ids_ref, wts_ref, slots, cols)
     else:
         y_ref = O.grouped_gemm_int8w8a16(x_np, wq_full, ws_full, ids_ref, wts_ref, slots, cols)
     # the per-slot results are stored as bf16: the float32 tolerance plus half
@@ -133,6 +143,10 @@ SMALL = [
     # >= 384 routed rows per expert: the four-wavefront persistent kernel
     synth.small("fp8", 400, 256, 320, 2, 2),
     synth.small("fp8", 800, 384, 136, 4, 2, bias_std=1.5),
+    # int8 W8A8 with per-token activation scales
+    synth.small("int8dq", 37, 256, 200, 8, 2),
+    synth.small("int8dq", 300, 384, 320, 8, 2, bias_std=1.5),
+    synth.small("int8dq", 400, 256, 136, 2, 2),
 ]
 
 
@@ -192,6 +206,7 @@ def test_routed_deterministic():
 
 
 FULL = [synth.WORKLOADS[n] for n in [
+    "int8dq_m64_k4096_n14336", "int8dq_bias_m4096_k4096_n14336",
     "int8w8a16_m64_k4096_n14336",
     "fp8_bias_m128_k4096_n14336", "fp8_bias_m512_k4096_n14336",
     "fp8_bias_m1024_k4096_n14336", "fp8_bias_m4096_k4096_n14336",
@@ -207,7 +222,7 @@ def test_routed_full_size_sampled(wl):
     torch.cuda.empty_cache()
 
 
-ROWMAJOR_FULL = FULL[:2] + [synth.WORKLOADS["fp8_bias_m4096_k4096_n14336"],
+ROWMAJOR_FULL = FULL[:4] + [synth.WORKLOADS["fp8_bias_m4096_k4096_n14336"],
                             synth.WORKLOADS["mistral7b_down_int8_m4096_k14336_n4096"]]
 
 

@@ -147,6 +147,20 @@ def quantize_weight_fp8(w):
     return q, scales
 
 
+def quantize_weight_fp8_rows(w):
+    """fp8 weight-only weights ("fp8wo" of "Enabling MOE Quantization using
+    linear decomposition", Summary): one e4m3 scale per expert and output
+    channel, the per-tensor rule applied to each row: s = fl32(amax_row /
+    448) (1 for a zero row), q = e4m3(fl32(w * fl32(1 / s))).  w float32
+    [E, N, K] -> (w_q uint8 [E, N, K], w_scale float32 [E, N])."""
+    w = _f32(w)
+    amax = np.max(np.abs(w), axis=-1)
+    s = np.where(amax == 0, np.float32(1.0), (amax / np.float32(448.0)).astype(np.float32))
+    s = s.astype(np.float32)
+    inv = (np.float32(1.0) / s).astype(np.float32)
+    return e4m3_encode(w * inv[..., None]), s
+
+
 def int8_channel_scale(w_rows):
     """Per-row symmetric int8 scale fl32(amax_row / 127); 1 for a zero row."""
     amax = np.max(np.abs(_f32(w_rows)), axis=-1)
@@ -344,6 +358,21 @@ def grouped_gemm_int8w8a16(a_bf16, w_q, w_scale, topk_ids, topk_weights,
     ws = np.asarray(w_scale, dtype=np.float32).astype(np.float64)
     return _grouped(lambda t: bf16_decode(a[t]),
                     lambda e, c: w_q[e][c].astype(np.float64),
+                    lambda e, c: ws[e][c],
+                    topk_ids, topk_weights, w_q.shape[1], slots, cols)
+
+
+def grouped_gemm_fp8w8a16(a_bf16, w_q, w_scale, topk_ids, topk_weights,
+                          slots=None, cols=None):
+    """fp8 weight-only: bf16 activations x e4m3 weights with one scale per
+    expert and output channel ("fp8wo" of "Enabling MOE Quantization using
+    linear decomposition", Summary); the weights are used at their exact
+    decoded values."""
+    a = np.asarray(a_bf16)
+    w_q = np.asarray(w_q)
+    ws = np.asarray(w_scale, dtype=np.float32).astype(np.float64)
+    return _grouped(lambda t: bf16_decode(a[t]),
+                    lambda e, c: e4m3_decode(w_q[e][c]),
                     lambda e, c: ws[e][c],
                     topk_ids, topk_weights, w_q.shape[1], slots, cols)
 

@@ -218,3 +218,17 @@ def test_int8w8a8_integer_identity():
     y = O.grouped_gemm_int8w8a8(aq, np.ones(M, np.float32), wq, np.ones((1, N), np.float32),
                                 ids, np.ones((M, 1), np.float32))
     np.testing.assert_array_equal(y, (aq.astype(np.int64) @ wq[0].astype(np.int64).T).astype(np.float32))
+
+
+def test_fp8w8a16_brute_force():
+    """fp8 weight-only by exact rational arithmetic on a tiny routed case."""
+    rng = np.random.default_rng(15)
+    M, K, N, E, top_k = 3, 32, 5, 4, 2
+    x, w, lg = _tiny(rng, M, K, N, E)
+    ids, wts = O.route_topk(lg, top_k)
+    wq, sw = O.quantize_weight_fp8_rows(w)
+    xv = F.bf16_decode(x)
+    dec = {int(c): _fr(v) for c, v in zip(range(256), F.e4m3_decode(np.arange(256, dtype=np.uint8))) if np.isfinite(v)}
+    ref = _exact_routed(lambda t, k: _fr(xv[t, k]), lambda e, n, k: dec[int(wq[e, n, k])],
+                        lambda e, n: _fr(sw[e, n]), ids, wts, M, K, N, top_k)
+    np.testing.assert_array_equal(O.grouped_gemm_fp8w8a16(x, wq, sw, ids, wts), ref)

@@ -233,3 +233,23 @@ def test_int8_activation_rows_brute_force():
     q2, s2 = O.quantize_act_int8_rows(F.bf16_round(-xv.astype(np.float32)))
     np.testing.assert_array_equal(q2, -q)
     np.testing.assert_array_equal(s2, s)
+
+
+def test_fp8_weight_rows_equal_per_tensor_rule_per_row():
+    """Per-channel fp8 weights are the per-tensor rule applied to every row:
+    the same codes and scales as the per-expert (per-tensor) quantizer run
+    with one row per expert; a zero row gets scale 1 and zero codes, and each
+    row's largest magnitude maps to +-448."""
+    rng = np.random.default_rng(6)
+    w = (rng.standard_normal((2, 5, 48)) * np.array([1.0, 1e-3])[:, None, None]).astype(np.float32)
+    w[1, 2] = 0.0
+    q, s = O.quantize_weight_fp8_rows(w)
+    q_t, s_t = O.quantize_weight_fp8(w.reshape(10, 1, 48))
+    np.testing.assert_array_equal(q.reshape(10, 1, 48), q_t)
+    np.testing.assert_array_equal(s.reshape(10), s_t)
+    assert s[1, 2] == 1.0 and not q[1, 2].any()
+    for e in range(2):
+        for n in range(5):
+            if (e, n) != (1, 2):
+                k = int(np.argmax(np.abs(w[e, n])))
+                assert abs(float(F.e4m3_decode(q[e, n, k]))) == 448.0

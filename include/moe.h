@@ -59,6 +59,7 @@ extern "C" {
 #define MOE_Q_MXFP8            1  /* e4m3 + one e8m0 scale per 32 values along K */
 #define MOE_Q_INT8_PER_CHANNEL 2  /* int8 + one fp32 scale per row: per output channel
                                      (weights), per token (activations) */
+#define MOE_Q_FP8_PER_CHANNEL  3  /* e4m3 + one fp32 scale per output channel (weights only) */
 
 /* ---- activations fused with the quantization (moe_act_quantize) -------- */
 #define MOE_ACT_SWIGLU 0  /* y = silu(g) * u, row = [g | u] (2H inputs -> H outputs) */
@@ -208,6 +209,11 @@ int moe_act_quantize(const uint16_t *x, int rows, int H, int act, int mode,
  *                         q = e4m3(fl32(w * fl32(1/s_e))); q is uint8 [E,N,K],
  *                         scale [E].  Needs workspace of
  *                         moe_quantize_workspace_bytes(mode, E) bytes.
+ * MOE_Q_FP8_PER_CHANNEL : per row (output channel) s = fl32(amax_row/448)
+ *                         (1 if zero), q = e4m3(fl32(w * fl32(1/s))) with
+ *                         saturation to +-448; q is uint8 [E,N,K], scale
+ *                         [E,N] ("Enabling MOE Quantization using linear
+ *                         decomposition", Summary: fp8 weight-only).
  * MOE_Q_INT8_PER_CHANNEL: per row s = fl32(amax_row/127) (1 if zero),
  *                         q = clamp(round_half_even(fl32(w * fl32(1/s))),
  *                         -127, 127); q is int8 [E,N,K], scale [E,N].
@@ -294,6 +300,22 @@ int moe_grouped_gemm_int8w8a16(const uint16_t *a, const int8_t *w_q,
                                const int *num_tokens_post_padded,
                                const float *topk_weights, int M, int K, int N, int E,
                                int top_k, int block_m, uint16_t *y, hipStream_t stream);
+
+/* Routed fp8 weight-only grouped GEMM ("Enabling MOE Quantization using
+ * linear decomposition", Summary: bf16 activations x fp8 weights with a scale
+ * per output channel): as moe_grouped_gemm_int8w8a16 with e4m3 w_q in layout
+ * w_layout and w_scale [E, N] f32 (moe_quantize_weights with
+ * MOE_Q_FP8_PER_CHANNEL).  Every e4m3 value is exactly a bf16 value, so the
+ * weights are converted exactly to bf16 inside the kernel and the products
+ * are accumulated in fp32:
+ *     y[i, n] = bf16( (sum_k a[t,k] * w[e,n,k]) * w_scale[e, n] * topk_weights[i] )
+ * K must be a multiple of 64 and N of 8; block_m must be 16 or 128. */
+int moe_grouped_gemm_fp8w8a16(const uint16_t *a, const uint8_t *w_q,
+                              const float *w_scale, int w_layout,
+                              const int *sorted_token_ids, const int *expert_ids,
+                              const int *num_tokens_post_padded,
+                              const float *topk_weights, int M, int K, int N, int E,
+                              int top_k, int block_m, uint16_t *y, hipStream_t stream);
 
 /* MXFP8 grouped linear over expert-contiguous rows (no router): for row r of
  * expert e (m_offsets[e] <= r < m_offsets[e+1]) and column n < N,

@@ -88,6 +88,26 @@ __device__ __forceinline__ void dequant16(const i32x4 &w, i32x4 &b0, i32x4 &b1) 
   b1 = i32x4{p2[0], p2[1], p3[0], p3[1]};
 }
 
+// 16 e4m3 weights -> 16 bf16 values (exact: e4m3 has 3 mantissa bits), in
+// the same order as dequant16.
+__device__ __forceinline__ void dequant16_fp8(const i32x4 &w, i32x4 &b0, i32x4 &b1) {
+  int p[8];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[d], false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[d], true);
+    p[2 * d] = (int)f32x2_to_bf16x2(lo[0], lo[1]);
+    p[2 * d + 1] = (int)f32x2_to_bf16x2(hi[0], hi[1]);
+  }
+  b0 = i32x4{p[0], p[1], p[2], p[3]};
+  b1 = i32x4{p[4], p[5], p[6], p[7]};
+}
+template <bool kFp8W>
+__device__ __forceinline__ void dequant16w(const i32x4 &w, i32x4 &b0, i32x4 &b1) {
+  if constexpr (kFp8W) dequant16_fp8(w, b0, b1);
+  else dequant16(w, b0, b1);
+}
+
 __device__ __forceinline__ i32x4 ld16(const void *p) {
   return *reinterpret_cast<const i32x4 *>(p);
 }
@@ -197,8 +217,9 @@ __device__ __forceinline__ int sw128(int r, int c) { return r * 128 + ((c ^ swz(
 __device__ __forceinline__ int sw256(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
 
 // stream kernel modes: fp8 W8A8, int8 W8A16 (bf16 activations), int8 W8A8
-// (int8 activations with one scale per token)
-enum { kSFp8 = 0, kSW8A16 = 1, kSI8 = 2 };
+// (int8 activations with one scale per token), fp8 weight-only (bf16
+// activations, e4m3 weights with one scale per channel)
+enum { kSFp8 = 0, kSW8A16 = 1, kSI8 = 2, kSF8W16 = 3 };
 
 template <int kMode, bool kTiled>
 __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
@@ -207,7 +228,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
     const int *__restrict__ sorted_ids, const int *__restrict__ expert_ids,
     const int *__restrict__ num_post, const float *__restrict__ topk_w, int M, int K, int N,
     int top_k, int groups, int tiles_per_group, int max_blocks, uint16_t *__restrict__ y) {
-  constexpr bool kInt8 = kMode == kSW8A16;               // bf16 activations, int8 weights
+  constexpr bool kInt8 = kMode == kSW8A16 || kMode == kSF8W16;   // bf16 activations
   constexpr bool kI8 = kMode == kSI8;                    // int8 activations and weights
   using C = SCfg<kInt8>;
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[2 * C::kStage];
@@ -445,7 +466,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
             const i32x4 braw =
                 *reinterpret_cast<const i32x4 *>(sl + tl * C::kBTile + sw128(n, 4 * ss + g));
             i32x4 b0, b1;
-            dequant16(braw, b0, b1);
+            dequant16w<kMode == kSF8W16>(braw, b0, b1);
 #pragma unroll
             for (int i = 0; i < kSMB; ++i) {
               if (i >= nmb) break;
@@ -535,7 +556,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
   }
 }
 
-enum { kFmtFp8 = 0, kFmtInt8 = 1, kFmtMx = 2, kFmtI8 = 3 };
+enum { kFmtFp8 = 0, kFmtInt8 = 1, kFmtMx = 2, kFmtI8 = 3, kFmtF8W16 = 4 };
 
 // =============================================================================
 // block_m = 128 (fp8 W8A8, int8 W8A16) and MXFP8: DMA-fed MFMA tiles
@@ -592,7 +613,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(
     const int *__restrict__ sorted_ids, const int *__restrict__ expert_ids,
     const float *__restrict__ topk_w, const int *__restrict__ m_offsets, int M, int K, int N,
     int E, int top_k, int max_blocks, uint16_t *__restrict__ out) {
-  constexpr bool kInt8 = kFmt == kFmtInt8;
+  constexpr bool kInt8 = kFmt == kFmtInt8 || kFmt == kFmtF8W16;   // bf16 activations
   constexpr bool kMx = kFmt == kFmtMx;
   using C = GCfg<kInt8>;
   constexpr int kMF = 4, kNF = 4;                       // fragments per wavefront
@@ -768,7 +789,8 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(
         i32x4 bq[kNF][2];
 #pragma unroll
         for (int j = 0; j < kNF; ++j)
-          dequant16(ld16(Bs + (j * 16 + r16) * 128 + (((g + 4 * h) ^ sw) << 4)), bq[j][0], bq[j][1]);
+          dequant16w<kFmt == kFmtF8W16>(ld16(Bs + (j * 16 + r16) * 128 + (((g + 4 * h) ^ sw) << 4)),
+                                        bq[j][0], bq[j][1]);
         const int c0 = ((8 * h + 2 * g) ^ r16) << 4;
         const int c1 = ((8 * h + 2 * g + 1) ^ r16) << 4;
         i32x4 a0[kMF], a1[kMF];
@@ -1744,6 +1766,26 @@ hipError_t launch_gemm_int8w8a8(const int8_t *a_q, const float *a_scale, const i
     hipLaunchKernelGGL(k, dim3(wide_grid(tiles)), dim3(256), 0, s, ab, a_scale, nullptr, wb,
                        w_scale, nullptr, r.sorted_ids, r.expert_ids, r.topk_w, nullptr, r.M, r.K,
                        r.N, r.E, r.top_k, r.max_blocks, r.y, next_launch_slot());
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp8w8a16(const uint16_t *a, const uint8_t *w_q, const float *w_scale,
+                                const RoutedArgs &r, hipStream_t s) {
+  const uint8_t *ab = reinterpret_cast<const uint8_t *>(a);
+  if (r.block_m == 16) {
+    int groups, tpg;
+    stream_grid(r.N, r.E, groups, tpg);
+    auto k = r.w_layout ? stream_kernel<kSF8W16, true> : stream_kernel<kSF8W16, false>;
+    hipLaunchKernelGGL(k, dim3(r.E * groups), dim3(kSThreads), 0, s, ab, nullptr, w_q, w_scale,
+                       r.sorted_ids, r.expert_ids, r.num_post, r.topk_w, r.M, r.K, r.N, r.top_k,
+                       groups, tpg, r.max_blocks, r.y);
+  } else {
+    const long long tiles = (long long)r.max_blocks * ((r.N + kGBN - 1) / kGBN);
+    auto k = r.w_layout ? gemm_kernel<kFmtF8W16, true> : gemm_kernel<kFmtF8W16, false>;
+    hipLaunchKernelGGL(k, dim3(tile_grid(tiles)), dim3(kGThreads), 0, s, ab, nullptr, nullptr, w_q,
+                       w_scale, nullptr, r.sorted_ids, r.expert_ids, r.topk_w, nullptr, r.M, r.K,
+                       r.N, r.E, r.top_k, r.max_blocks, r.y);
   }
   return hipGetLastError();
 }

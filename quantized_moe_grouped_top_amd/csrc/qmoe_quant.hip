@@ -196,6 +196,37 @@ __global__ __launch_bounds__(kThreads) void quant_int8_rows_kernel(const Src *__
   }
 }
 
+// ---- fp8 per output channel (fp8 weight-only): one wavefront per row -------
+__global__ __launch_bounds__(kThreads) void quant_fp8_rows_kernel(const float *__restrict__ w,
+                                                                  long long rows, int K,
+                                                                  uint8_t *__restrict__ q,
+                                                                  float *__restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float *src = w + row * K;
+  float m = 0.0f;
+  for (int k = lane * 8; k < K; k += 64 * 8) {
+    float v[8];
+    load8(src + k, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+  }
+  const float amax = wave_max(m);
+  const float s = amax > 0.0f ? (float)((double)amax / 448.0) : 1.0f;
+  const float inv = (float)(1.0 / (double)s);
+  if (lane == 0) scale[row] = s;
+  uint8_t *dst = q + row * K;
+  for (int k = lane * 8; k < K; k += 64 * 8) {
+    float v[8];
+    load8(src + k, v);
+    i32x2 out;
+    out[0] = (int)f32x4_to_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    out[1] = (int)f32x4_to_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+    *reinterpret_cast<i32x2 *>(dst + k) = out;
+  }
+}
+
 // ---- MXFP8: one thread per block of 32 values ------------------------------
 // mx_encode: the e8m0 byte of 32 values (returned) and their 32 e4m3 codes.
 __device__ __forceinline__ uint32_t mx_encode(const float *v, uint8_t *dst) {
@@ -620,6 +651,14 @@ hipError_t launch_quant_int8_rows_f32(const float *w, long long rows, int K, int
   const long long blocks = (rows + kThreads / 64 - 1) / (kThreads / 64);
   hipLaunchKernelGGL(quant_int8_rows_kernel<float>, dim3((unsigned)blocks), dim3(kThreads), 0, s,
                      w, rows, K, q, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_fp8_rows_f32(const float *w, long long rows, int K, uint8_t *q,
+                                     float *scale, hipStream_t s) {
+  const long long blocks = (rows + kThreads / 64 - 1) / (kThreads / 64);
+  hipLaunchKernelGGL(quant_fp8_rows_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, w, rows,
+                     K, q, scale);
   return hipGetLastError();
 }
 

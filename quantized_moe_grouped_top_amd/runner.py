@@ -5,7 +5,8 @@ memory only) and runs the hot path as a sequence of library calls on the
 current stream:
 
     routed formats : moe_align_block_size -> [moe_quantize_act] ->
-                     moe_grouped_gemm_{fp8w8a8,int8w8a8,int8w8a16} -> moe_combine
+                     moe_grouped_gemm_{fp8w8a8,int8w8a8,int8w8a16,fp8w8a16} ->
+                     moe_combine
     MXFP8          : moe_quantize_act(MXFP8) -> moe_grouped_gemm_mxfp8
     activation     : moe_act_quantize (SwiGLU / SReLU + MXFP8 or fp8)
 
@@ -14,9 +15,11 @@ Every step runs in the library's HIP kernels; nothing here computes.
 
 import torch
 
-from . import (MOE_ACT_SRELU, MOE_ACT_SWIGLU, MOE_Q_FP8_PER_TENSOR, MOE_Q_INT8_PER_CHANNEL, MOE_Q_MXFP8, MOE_W_ROWMAJOR,
+from . import (MOE_ACT_SRELU, MOE_ACT_SWIGLU, MOE_Q_FP8_PER_CHANNEL, MOE_Q_FP8_PER_TENSOR,
+               MOE_Q_INT8_PER_CHANNEL, MOE_Q_MXFP8, MOE_W_ROWMAJOR,
                MOE_W_TILED, moe_act_quantize, moe_align_block_size, moe_align_max_padded, moe_combine,
-               moe_grouped_gemm_fp8w8a8, moe_grouped_gemm_int8w8a8, moe_grouped_gemm_int8w8a16,
+               moe_grouped_gemm_fp8w8a8, moe_grouped_gemm_fp8w8a16, moe_grouped_gemm_int8w8a8,
+               moe_grouped_gemm_int8w8a16,
                moe_grouped_gemm_mxfp8,
                moe_mx_scale_rows, moe_pack_weights, moe_packed_weight_bytes, moe_quantize_act,
                moe_quantize_weights, moe_quantize_workspace_bytes, moe_recommended_block_m)
@@ -28,7 +31,7 @@ def _empty(shape, dtype, device):
 
 def quantize_weights(w, fmt):
     """Offline weight quantization of float32 w [E, N, K] on its device.
-    Returns (w_q, w_scale) for fp8/int8 or (w_q, w_sf) for MXFP8."""
+    Returns (w_q, w_scale) for fp8/int8/fp8wo or (w_q, w_sf) for MXFP8."""
     E, N, K = w.shape
     dev = w.device
     if fmt == "fp8":
@@ -36,6 +39,11 @@ def quantize_weights(w, fmt):
         s = _empty((E,), torch.float32, dev)
         ws = _empty((moe_quantize_workspace_bytes(MOE_Q_FP8_PER_TENSOR, E),), torch.uint8, dev)
         moe_quantize_weights(w, E, N, K, MOE_Q_FP8_PER_TENSOR, q, s, None, ws)
+        return q, s
+    if fmt == "fp8wo":
+        q = _empty((E, N, K), torch.uint8, dev)
+        s = _empty((E, N), torch.float32, dev)
+        moe_quantize_weights(w, E, N, K, MOE_Q_FP8_PER_CHANNEL, q, s, None, None)
         return q, s
     if fmt in ("int8", "int8dq"):
         q = _empty((E, N, K), torch.int8, dev)
@@ -59,12 +67,13 @@ def pack_weights(w_q):
 
 
 class RoutedMoE:
-    """fp8 W8A8, int8 W8A16 ("int8") or int8 W8A8 with per-token activation
-    scales ("int8dq") MoE layer of fixed (M, K, N, E, top_k)."""
+    """fp8 W8A8, int8 W8A16 ("int8"), int8 W8A8 with per-token activation
+    scales ("int8dq") or bf16 x fp8 weight-only ("fp8wo") MoE layer of fixed
+    (M, K, N, E, top_k)."""
 
     def __init__(self, fmt, M, K, N, E, top_k, device="cuda", block_m=None,
                  w_layout=MOE_W_ROWMAJOR):
-        assert fmt in ("fp8", "int8", "int8dq")
+        assert fmt in ("fp8", "int8", "int8dq", "fp8wo")
         self.w_layout = w_layout
         self.fmt, self.M, self.K, self.N, self.E, self.top_k = fmt, M, K, N, E, top_k
         self.block_m = block_m or moe_recommended_block_m(M, E, top_k)
@@ -112,6 +121,11 @@ class RoutedMoE:
                                       self.sorted_token_ids, self.expert_ids,
                                       self.num_tokens_post_padded, self.topk_weights, self.M,
                                       self.K, self.N, self.E, self.top_k, self.block_m, self.y)
+        elif self.fmt == "fp8wo":
+            moe_grouped_gemm_fp8w8a16(x, w_q, w_scale, self.w_layout, self.sorted_token_ids,
+                                      self.expert_ids, self.num_tokens_post_padded,
+                                      self.topk_weights, self.M, self.K, self.N, self.E,
+                                      self.top_k, self.block_m, self.y)
         else:
             moe_grouped_gemm_int8w8a16(x, w_q, w_scale, self.w_layout, self.sorted_token_ids,
                                        self.expert_ids,

@@ -75,7 +75,7 @@ def oracle_weights_rows(w_dev, fmt, cols):
     """Oracle quantization of the weight rows `cols` of every expert.
 
     Returns (q [E, len(cols), K], scale) where scale is [E] (fp8, from the
-    amax of the whole expert matrix), [E, len(cols)] (int8) or the e8m0 bytes
+    amax of the whole expert matrix), [E, len(cols)] (int8, fp8wo) or the e8m0 bytes
     [E, len(cols), K/32] (MXFP8)."""
     E = w_dev.shape[0]
     cols_t = torch.as_tensor(cols, device=w_dev.device)
@@ -86,5 +86,7 @@ def oracle_weights_rows(w_dev, fmt, cols):
         return q, s
     if fmt in ("int8", "int8dq"):
         return O.quantize_weight_int8(rows)
+    if fmt == "fp8wo":
+        return O.quantize_weight_fp8_rows(rows)
     q, b = O.quantize_weight_mxfp8(rows)
     return q, b

@@ -38,7 +38,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     h = ctypes.CDLL(qm.LIB_PATH)
     for n in names:
         assert hasattr(h, n), n
@@ -141,6 +141,37 @@ def test_gemm_int8w8a8_and_int8_activation_quantizer_reject():
         qm.moe_quantize_act(FAKE, 10, 64, qm.MOE_Q_INT8_PER_CHANNEL, None, 1, FAKE, None, None,
                             None, stream=0)
     assert ei.value.code == qm.MOE_EINVAL                       # no scale
+
+
+def test_gemm_fp8w8a16_and_fp8_channel_quantizer_reject():
+    args = [FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, 64, 96, 128, 8, 2, 16, FAKE]
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_grouped_gemm_fp8w8a16(*args, stream=0)
+    assert ei.value.code == qm.MOE_EUNSUPPORTED                 # K % 64
+    args[9] = 128
+    args[2] = 0
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_grouped_gemm_fp8w8a16(*args, stream=0)
+    assert ei.value.code == qm.MOE_EINVAL                       # null w_scale
+    args[2] = FAKE
+    args[13] = 64
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_grouped_gemm_fp8w8a16(*args, stream=0)
+    assert ei.value.code == qm.MOE_EUNSUPPORTED                 # block_m
+    args[13], args[8] = 16, 0
+    qm.moe_grouped_gemm_fp8w8a16(*args, stream=0)               # M = 0: nothing to do
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_quantize_weights(FAKE, 2, 4, 60, qm.MOE_Q_FP8_PER_CHANNEL, FAKE, FAKE, None, None,
+                                stream=0)
+    assert ei.value.code == qm.MOE_EUNSUPPORTED                 # K % 8
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_quantize_weights(FAKE, 2, 4, 64, qm.MOE_Q_FP8_PER_CHANNEL, FAKE, None, None, None,
+                                stream=0)
+    assert ei.value.code == qm.MOE_EINVAL                       # no scale
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_quantize_act(FAKE, 10, 64, qm.MOE_Q_FP8_PER_CHANNEL, None, 1, FAKE, FAKE, None,
+                            None, stream=0)
+    assert ei.value.code == qm.MOE_EINVAL                       # weights only
 
 
 def test_quantize_and_combine_reject():

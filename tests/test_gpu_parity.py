@@ -114,6 +114,8 @@ def run_routed(wl, block_m=None, variant=0, full=True, n_tok=48, n_col=64, logit
         sa_full = np.ones(M, np.float32)
         sa_full[toks] = sa_rows
         y_ref = O.grouped_gemm_int8w8a8(aq_full, sa_full, wq_full, ws_full, ids_ref, wts_ref, slots, cols)
+    elif wl.fmt == "fp8wo":
+        y_ref = O.grouped_gemm_fp8w8a16(x_np, wq_full, ws_full, ids_ref, wts_ref, slots, cols)
     else:
         y_ref = O.grouped_gemm_int8w8a16(x_np, wq_full, ws_full, ids_ref, wts_ref, slots, cols)
     # the per-slot results are stored as bf16: the float32 tolerance plus half
@@ -147,6 +149,10 @@ SMALL = [
     synth.small("int8dq", 37, 256, 200, 8, 2),
     synth.small("int8dq", 300, 384, 320, 8, 2, bias_std=1.5),
     synth.small("int8dq", 400, 256, 136, 2, 2),
+    # bf16 activations x fp8 weights with per-channel scales
+    synth.small("fp8wo", 50, 320, 136, 6, 3),
+    synth.small("fp8wo", 300, 256, 272, 8, 2, bias_std=1.5),
+    synth.small("fp8wo", 40, 128, 48, 1, 1),
 ]
 
 
@@ -208,6 +214,7 @@ def test_routed_deterministic():
 FULL = [synth.WORKLOADS[n] for n in [
     "int8dq_m64_k4096_n14336", "int8dq_bias_m4096_k4096_n14336",
     "int8w8a16_m64_k4096_n14336",
+    "fp8wo_m64_k4096_n14336", "fp8wo_bias_m4096_k4096_n14336",
     "fp8_bias_m128_k4096_n14336", "fp8_bias_m512_k4096_n14336",
     "fp8_bias_m1024_k4096_n14336", "fp8_bias_m4096_k4096_n14336",
     "mistral7b_up_fp8_m4096_k4096_n28672", "mistral7b_down_fp8_m4096_k14336_n4096",
@@ -222,8 +229,11 @@ def test_routed_full_size_sampled(wl):
     torch.cuda.empty_cache()
 
 
-ROWMAJOR_FULL = FULL[:4] + [synth.WORKLOADS["fp8_bias_m4096_k4096_n14336"],
-                            synth.WORKLOADS["mistral7b_down_int8_m4096_k14336_n4096"]]
+ROWMAJOR_FULL = [synth.WORKLOADS[n] for n in [
+    "int8dq_m64_k4096_n14336", "int8dq_bias_m4096_k4096_n14336", "int8w8a16_m64_k4096_n14336",
+    "fp8wo_m64_k4096_n14336", "fp8_bias_m128_k4096_n14336", "fp8_bias_m4096_k4096_n14336",
+    "mistral7b_down_int8_m4096_k14336_n4096",
+]]
 
 
 @pytest.mark.parametrize("wl", ROWMAJOR_FULL, ids=[w.name for w in ROWMAJOR_FULL])

@@ -226,7 +226,11 @@ def main():
     else:
         w_q, w_s = runner.quantize_weights(case["w"], wl.fmt)
         if wl.fmt != "mxfp8":
-            w_q = runner.pack_weights(w_q)          # tiled layout: one HBM block per stage
+            # decode (block_m 16): fragment-ordered weights, one contiguous 1 KB
+            # read per MFMA operand; otherwise tiles of one 8 KB block per stage
+            layout = (qm.MOE_W_FRAG if qm.moe_recommended_block_m(wl.M, wl.E, wl.top_k) == 16
+                      else qm.MOE_W_TILED)
+            w_q = runner.pack_weights(w_q, layout)
         copies = args.copies or max(2, -(-(1 << 30) // w_q.numel()))
         weights = [(w_q, w_s)] + [(w_q.clone(), w_s.clone()) for _ in range(copies - 1)]
     if wl.fmt.startswith("act_"):
@@ -244,7 +248,7 @@ def main():
             if ev is not None:
                 ev[1].record()
     else:
-        moe = runner.RoutedMoE(wl.fmt, wl.M, wl.K, wl.N, wl.E, wl.top_k, w_layout=qm.MOE_W_TILED)
+        moe = runner.RoutedMoE(wl.fmt, wl.M, wl.K, wl.N, wl.E, wl.top_k, w_layout=layout)
 
         def step(i, ev):
             q, s = weights[i % copies]
@@ -308,7 +312,8 @@ def main():
                    ("input_copies" if is_act else "weight_copies"): copies,
                    "block_m": getattr(moe, "block_m", None),
                    "weight_layout": None if is_act else
-                   ("tiled" if wl.fmt != "mxfp8" else "rowmajor")},
+                   {qm.MOE_W_TILED: "tiled", qm.MOE_W_FRAG: "frag"}.get(
+                       getattr(moe, "w_layout", None), "rowmajor")},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

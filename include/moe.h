@@ -68,6 +68,7 @@ extern "C" {
 /* ---- expert weight layouts (fp8 and int8 weights) ------------------------ */
 #define MOE_W_ROWMAJOR 0  /* [E, N, K] bytes, K fastest */
 #define MOE_W_TILED    1  /* as written by moe_pack_weights (see there) */
+#define MOE_W_FRAG     2  /* as written by moe_pack_weights (see there); block_m 16 only */
 
 /* ---- limits ------------------------------------------------------------- */
 #define MOE_MAX_EXPERTS   128     /* E */
@@ -99,9 +100,11 @@ int moe_recommended_block_m(int M, int E, int top_k);
  * 0 when the mode needs none. */
 size_t moe_quantize_workspace_bytes(int mode, int tensors);
 
-/* Bytes of the MOE_W_TILED layout of E x N x K one-byte weights:
- * E * ceil(N/64) * ceil(K/128) * 8192. */
-size_t moe_packed_weight_bytes(int E, int N, int K);
+/* Bytes of E x N x K one-byte weights in `layout`: MOE_W_TILED
+ * E * ceil(N/64) * ceil(K/128) * 8192, MOE_W_FRAG E * ceil(N/16) *
+ * ceil(K/64) * 1024, MOE_W_ROWMAJOR E * N * K; 0 for an unknown layout or a
+ * size below 1. */
+size_t moe_packed_weight_bytes(int E, int N, int K, int layout);
 
 /* Upper bound on the rows of the padded MXFP8 rowwise scale matrix for `rows`
  * rows spread over E experts: rows + E*127 (each expert's block is padded to
@@ -227,6 +230,15 @@ int moe_quantize_weights(const float *w, int E, int N, int K, int mode,
 
 /* Offline re-layout of one-byte expert weights (e4m3 or int8) for streaming.
  *
+ * MOE_W_FRAG (for block_m 16): the weights of expert e are cut into 16-row
+ * groups j = n / 16 (J = ceil(N/16)) and 64-byte k blocks b = k / 64
+ * (B = ceil(K/64)); the 1024-byte block (e, j, b) is stored at byte offset
+ * ((e*J + j)*B + b) * 1024, and its 16-byte piece p = 16*q + r (q = 0..3,
+ * r = 0..15) holds row n = 16j + r, k = 64b + 16q .. 64b + 16q + 15.  This is
+ * the order in which the 64 lanes of a wavefront take one MFMA operand
+ * fragment (lane p: row r, k group q), so each fragment is one contiguous
+ * 1 KB read straight into registers.  Rows n >= N and k >= K are zero.
+ *
  * MOE_W_TILED: the weights of expert e are cut into 64-row tiles t = n / 64
  * (T = ceil(N/64)) and 128-byte k slices s = k / 128 (S = ceil(K/128)); the
  * 64 x 128-byte block (e, t, s) is stored contiguously (8192 bytes) at byte
@@ -238,9 +250,11 @@ int moe_quantize_weights(const float *w, int E, int N, int K, int mode,
  * LDS in the bank-conflict-free order its MFMA reads use.
  *
  *   w_q      [E, N, K] bytes (MOE_W_ROWMAJOR), read
- *   w_packed moe_packed_weight_bytes(E, N, K) bytes, written in full
- * The packed size must stay below 4 GiB. */
-int moe_pack_weights(const void *w_q, int E, int N, int K, void *w_packed, hipStream_t stream);
+ *   layout   MOE_W_TILED or MOE_W_FRAG
+ *   w_packed moe_packed_weight_bytes(E, N, K, layout) bytes, written in full
+ * K must be a multiple of 16; the packed size must stay below 4 GiB. */
+int moe_pack_weights(const void *w_q, int E, int N, int K, int layout, void *w_packed,
+                     hipStream_t stream);
 
 /* ======================================================================== *
  * a4 + a5: grouped GEMM with the fused scale / router-weight epilogue
@@ -256,15 +270,17 @@ int moe_pack_weights(const void *w_q, int E, int N, int K, void *w_packed, hipSt
  * FP8_W8A8 / INT8_W8A16 benchmark tables ("Tianxing/moe quantization").
  *
  *   a_q [M, K] uint8 e4m3, a_scale [1] f32, w_q e4m3 weights in layout
- *   w_layout (MOE_W_ROWMAJOR [E, N, K] or MOE_W_TILED), w_scale [E] f32,
+ *   w_layout (MOE_W_ROWMAJOR [E, N, K], MOE_W_TILED or, with block_m 16 only,
+ *   MOE_W_FRAG), w_scale [E] f32,
  *   topk_weights [M*top_k] f32, routing buffers as written by
  *   moe_align_block_size, y [M*top_k, N] uint16 bf16, 16-byte aligned (rows
  *   of slots that are not routed are not written; with every slot routed, y
  *   is written in full).
  *
  * K must be a multiple of 128 and N of 8; block_m must be 16 or 128.
- * block_m 16 runs the weight-streaming kernel (fastest with MOE_W_TILED), 128
- * the tiled one. */
+ * block_m 16 runs the weight-streaming kernel (fastest with MOE_W_FRAG), 128
+ * the tiled one (MOE_W_FRAG is rejected there with MOE_EUNSUPPORTED).  The
+ * other routed GEMMs below take the same layouts under the same rule. */
 int moe_grouped_gemm_fp8w8a8(const uint8_t *a_q, const float *a_scale,
                              const uint8_t *w_q, const float *w_scale, int w_layout,
                              const int *sorted_token_ids, const int *expert_ids,

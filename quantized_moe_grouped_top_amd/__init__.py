@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmoe.so"
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP = 0, -1, -2, -3
 MOE_Q_FP8_PER_TENSOR, MOE_Q_MXFP8, MOE_Q_INT8_PER_CHANNEL, MOE_Q_FP8_PER_CHANNEL = 0, 1, 2, 3
-MOE_W_ROWMAJOR, MOE_W_TILED = 0, 1
+MOE_W_ROWMAJOR, MOE_W_TILED, MOE_W_FRAG = 0, 1, 2
 MOE_ACT_SWIGLU, MOE_ACT_SRELU = 0, 1
 MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_SLOTS = 128, 8, 65536
 
@@ -55,8 +55,8 @@ _SIGS = {
     "moe_align_max_padded": (_I, [_I, _I, _I, _I]),
     "moe_recommended_block_m": (_I, [_I, _I, _I]),
     "moe_quantize_workspace_bytes": (ctypes.c_size_t, [_I, _I]),
-    "moe_packed_weight_bytes": (ctypes.c_size_t, [_I, _I, _I]),
-    "moe_pack_weights": (_I, [_P, _I, _I, _I, _P, _P]),
+    "moe_packed_weight_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "moe_pack_weights": (_I, [_P, _I, _I, _I, _I, _P, _P]),
     "moe_mx_scale_rows": (_I, [_I, _I]),
     "moe_align_block_size": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "moe_quantize_act": (_I, [_P, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P]),
@@ -127,8 +127,8 @@ def moe_quantize_workspace_bytes(mode, tensors):
     return int(lib().moe_quantize_workspace_bytes(mode, tensors))
 
 
-def moe_packed_weight_bytes(E, N, K):
-    return int(lib().moe_packed_weight_bytes(E, N, K))
+def moe_packed_weight_bytes(E, N, K, layout):
+    return int(lib().moe_packed_weight_bytes(E, N, K, layout))
 
 
 def moe_mx_scale_rows(rows, E):
@@ -163,8 +163,9 @@ def moe_quantize_weights(w, E, N, K, mode, q, scale, scale_e8m0, workspace, stre
         _stream(stream)))
 
 
-def moe_pack_weights(w_q, E, N, K, w_packed, stream=None):
-    return _check(lib().moe_pack_weights(_ptr(w_q), E, N, K, _ptr(w_packed), _stream(stream)))
+def moe_pack_weights(w_q, E, N, K, layout, w_packed, stream=None):
+    return _check(lib().moe_pack_weights(_ptr(w_q), E, N, K, layout, _ptr(w_packed),
+                                         _stream(stream)))
 
 
 def moe_grouped_gemm_fp8w8a8(a_q, a_scale, w_q, w_scale, w_layout, sorted_token_ids, expert_ids,

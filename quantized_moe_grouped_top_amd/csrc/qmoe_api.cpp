@@ -68,20 +68,23 @@ int check_routed_gemm(const void *a, const void *w, const void *w_scale, int w_l
                       int block_m, int k_mult, const char *fn) {
   int rc = check_routing_sizes(M, E, top_k, fn);
   if (rc) return rc;
-  REQUIRE(w_layout == MOE_W_ROWMAJOR || w_layout == MOE_W_TILED, MOE_EINVAL,
-          "%s: unknown weight layout %d", fn, w_layout);
+  REQUIRE(w_layout == MOE_W_ROWMAJOR || w_layout == MOE_W_TILED || w_layout == MOE_W_FRAG,
+          MOE_EINVAL, "%s: unknown weight layout %d", fn, w_layout);
   REQUIRE(K > 0 && N > 0, MOE_EINVAL, "%s: K=%d and N=%d must be positive", fn, K, N);
   REQUIRE(K % k_mult == 0, MOE_EUNSUPPORTED, "%s: K=%d is not a multiple of %d", fn, K, k_mult);
   REQUIRE(N % 8 == 0, MOE_EUNSUPPORTED, "%s: N=%d is not a multiple of 8", fn, N);
   REQUIRE(block_m == 16 || block_m == 128, MOE_EUNSUPPORTED,
           "%s: block_m=%d (supported: 16, 128)", fn, block_m);
+  REQUIRE(w_layout != MOE_W_FRAG || block_m == 16, MOE_EUNSUPPORTED,
+          "%s: MOE_W_FRAG weights need block_m 16", fn);
   if (M == 0) return MOE_OK;               // nothing to do; buffers may be empty
   REQUIRE(a && w && w_scale && sorted && expert_ids && num_post && topk_w && y, MOE_EINVAL,
           "%s: null pointer argument", fn);
   REQUIRE(aligned16(a) && aligned16(w) && aligned16(y), MOE_EINVAL,
           "%s: activation, weight and output pointers must be 16-byte aligned", fn);
   REQUIRE((long long)E * N * (long long)K < (1ll << 32) &&
-              moe_packed_weight_bytes(E, N, K) < (1ull << 32),
+              moe_packed_weight_bytes(E, N, K, MOE_W_TILED) < (1ull << 32) &&
+              moe_packed_weight_bytes(E, N, K, MOE_W_FRAG) < (1ull << 32),
           MOE_EUNSUPPORTED, "%s: weight tensor must stay below 4 GiB", fn);
   REQUIRE((long long)M * (long long)K * 2 < (1ll << 32), MOE_EUNSUPPORTED,
           "%s: activation tensor must stay below 4 GiB", fn);
@@ -118,23 +121,31 @@ size_t moe_quantize_workspace_bytes(int mode, int tensors) {
   return (size_t)tensors * qmoe::kAmaxPartials * sizeof(float);
 }
 
-size_t moe_packed_weight_bytes(int E, int N, int K) {
+size_t moe_packed_weight_bytes(int E, int N, int K, int layout) {
   if (E < 1 || N < 1 || K < 1) return 0;
-  return (size_t)E * (size_t)((N + qmoe::kPackRows - 1) / qmoe::kPackRows) *
-         (size_t)((K + qmoe::kPackK - 1) / qmoe::kPackK) * (size_t)(qmoe::kPackRows * qmoe::kPackK);
+  if (layout == MOE_W_TILED)
+    return (size_t)E * (size_t)((N + qmoe::kPackRows - 1) / qmoe::kPackRows) *
+           (size_t)((K + qmoe::kPackK - 1) / qmoe::kPackK) *
+           (size_t)(qmoe::kPackRows * qmoe::kPackK);
+  if (layout == MOE_W_FRAG)
+    return (size_t)E * (size_t)((N + 15) / 16) * (size_t)((K + 63) / 64) * 1024u;
+  if (layout == MOE_W_ROWMAJOR) return (size_t)E * (size_t)N * (size_t)K;
+  return 0;
 }
 
-int moe_pack_weights(const void *w_q, int E, int N, int K, void *w_packed, hipStream_t stream) {
+int moe_pack_weights(const void *w_q, int E, int N, int K, int layout, void *w_packed,
+                     hipStream_t stream) {
   const char *fn = "moe_pack_weights";
   REQUIRE(E >= 1 && N > 0 && K > 0, MOE_EINVAL, "%s: E=%d N=%d K=%d", fn, E, N, K);
+  REQUIRE(layout == MOE_W_TILED || layout == MOE_W_FRAG, MOE_EINVAL, "%s: layout %d", fn, layout);
   REQUIRE(w_q && w_packed, MOE_EINVAL, "%s: null pointer argument", fn);
   REQUIRE(aligned16(w_q) && aligned16(w_packed), MOE_EINVAL, "%s: pointers must be 16-byte aligned",
           fn);
   REQUIRE(K % 16 == 0, MOE_EUNSUPPORTED, "%s: K=%d is not a multiple of 16", fn, K);
-  REQUIRE(moe_packed_weight_bytes(E, N, K) < (1ull << 32), MOE_EUNSUPPORTED,
+  REQUIRE(moe_packed_weight_bytes(E, N, K, layout) < (1ull << 32), MOE_EUNSUPPORTED,
           "%s: packed weights must stay below 4 GiB", fn);
-  return hip_status(qmoe::launch_pack_weights((const uint8_t *)w_q, E, N, K, (uint8_t *)w_packed,
-                                              stream),
+  return hip_status(qmoe::launch_pack_weights((const uint8_t *)w_q, E, N, K, layout,
+                                              (uint8_t *)w_packed, stream),
                     fn);
 }
 

@@ -136,39 +136,43 @@ __device__ __forceinline__ void expert_block_starts(const int *__restrict__ expe
 // block_m = 16: weight streaming
 // =============================================================================
 // One persistent workgroup per CU.  Workgroup b handles expert e = b / groups
-// and a run of G <= 7 consecutive 64-column tiles of that expert, with up to
-// 64 of the expert's rows per pass.  Its 8
-// wavefronts split the work by (16-column fragment w & 3, tile parity w >> 2):
-// every wavefront owns whole output elements, so no partial sums meet.
+// and a run of G <= 7 consecutive 64-column tiles of that expert (4G groups of
+// 16 weight rows), with up to 64 of the expert's rows per pass.  Wavefront w
+// owns the row groups w, w + 8, w + 16 and w + 24 (those below 4G): every
+// wavefront owns whole output elements, so no partial sums meet.
 //
-// Weight bytes and activation rows flow HBM/L2 -> LDS through a two-slot ring
-// filled by global_load_lds_dwordx4 (direct-to-LDS DMA from inline assembly):
-// each instruction moves 1 KB in consecutive 16-byte lane chunks (fully
-// coalesced), and data in flight costs no registers.  One stage is one k-slice
-// (128 k) of all G tiles plus the matching slice of the (up to 64) activation
-// rows, so an activation slice is fetched once for G weight tiles.  While the
-// wavefronts compute stage T, stage T+1 is in flight; before stage T+1 is read
-// every wavefront waits for its own DMA (s_waitcnt vmcnt(0)) and the workgroup
-// synchronises.  The compiler does not see these loads; the loop body issues
-// no other vector-memory loads (scales, router weights and slot ids are staged
-// in LDS before it).
+// No wavefront reads another's weights, so the weights go straight from HBM
+// into the registers that feed the MFMAs, SCfg::kD stages (128 k each) ahead of
+// their use: for each of its row groups a lane loads the two 16-byte pieces
+// that the MFMA operand placement assigns to it (weight row 16j + (l & 15),
+// k = 16g .. 16g + 15 and 64 + 16g .. 64 + 16g + 15 of the stage).  A
+// wavefront thus keeps up to kD x 8 KB of weights in flight without any LDS,
+// and the HBM stream never drains at a stage boundary.  With the MOE_W_FRAG
+// layout every such load is one contiguous 1 KB block.  The activation rows,
+// which all wavefronts share, flow into a ring of kD + 1 LDS slots by
+// global_load_lds_dwordx4 (direct-to-LDS DMA), also kD stages ahead.  Before
+// a stage is read each wavefront waits until its own loads of that stage have
+// landed (s_waitcnt vmcnt with the number of loads it has issued since) and
+// the workgroup synchronises.
 //
-// LDS rows are XOR-swizzled by 16-byte chunk so that the 16 rows one MFMA
-// operand read touches fall on distinct banks.
-constexpr int kSNT = 4;          // 16-column fragments per tile
+// LDS activation rows are XOR-swizzled by 16-byte chunk so that the 16 rows
+// one MFMA operand read touches fall on distinct banks.
 constexpr int kSMB = 4;          // 16-row blocks per pass (64 rows)
 constexpr int kSThreads = 512;   // 8 wavefronts
 constexpr int kSWaves = kSThreads / 64;
 constexpr int kSMaxTiles = 7;    // tiles per workgroup
 constexpr int kSK = 128;         // k per stage
+constexpr int kSGroups = 4;      // 16-row weight groups per wavefront
 
 template <bool kInt8>
 struct SCfg {
+  // weight stages held in registers per wavefront (loads run up to kD stages
+  // ahead of the MFMAs); the bf16 path needs more registers for its operands
+  static constexpr int kD = kInt8 ? 2 : 3;
+  static constexpr int kAS = kD + 1;                        // activation ring slots
   static constexpr int kSub = kInt8 ? 64 : 128;            // k per MFMA sub-step
   static constexpr int kARow = kInt8 ? 2 * kSK : kSK;       // activation bytes per row per stage
-  static constexpr int kBTile = 64 * kSK;                   // weight bytes per tile per stage
-  static constexpr int kABytes = 16 * kSMB * kARow;
-  static constexpr int kStage = kSMaxTiles * kBTile + kABytes;
+  static constexpr int kABytes = 16 * kSMB * kARow;         // one ring slot
   static constexpr int kAInstr = kABytes / 1024;            // DMA instructions for the rows
 };
 
@@ -221,28 +225,34 @@ __device__ __forceinline__ int sw256(int r, int c) { return r * 256 + ((c ^ (r &
 // activations, e4m3 weights with one scale per channel)
 enum { kSFp8 = 0, kSW8A16 = 1, kSI8 = 2, kSF8W16 = 3 };
 
-template <int kMode, bool kTiled>
+template <int kMode, int kLayout>
 __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ w, const float *__restrict__ w_scale,
     const int *__restrict__ sorted_ids, const int *__restrict__ expert_ids,
     const int *__restrict__ num_post, const float *__restrict__ topk_w, int M, int K, int N,
-    int top_k, int groups, int tiles_per_group, int max_blocks, uint16_t *__restrict__ y) {
+    int top_k, int groups, int tiles_per_group, int max_blocks, uint16_t *__restrict__ y,
+    uint32_t w_bytes) {
   constexpr bool kInt8 = kMode == kSW8A16 || kMode == kSF8W16;   // bf16 activations
   constexpr bool kI8 = kMode == kSI8;                    // int8 activations and weights
   using C = SCfg<kInt8>;
-  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[2 * C::kStage];
+  constexpr int kSD = C::kD, kSAS = C::kAS;
+  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kSAS * C::kABytes];
   __shared__ int s_slot[kSMB * 16];
   __shared__ int s_nvalid;
   __shared__ float s_scale[kSMaxTiles * 64];
+  __shared__ float s_rw[kSMB * 16];
 
   const int e = blockIdx.x / groups;
   const int grp = blockIdx.x - e * groups;
   const int ntiles = (N + 63) / 64;
   const int t_begin = grp * tiles_per_group;
   const int G = min(t_begin + tiles_per_group, ntiles) - t_begin;   // tiles of this workgroup
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int frag = wave & 3, par = wave >> 2;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wavefront index, in a scalar register (the compiler cannot tell that
+  // tid >> 6 is the same in every lane), so that the per-wavefront group
+  // loops below branch on the scalar unit
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r16 = lane & 15;
   const int S = M * top_k;
   if (G <= 0) return;
@@ -251,47 +261,80 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
   const uint32_t a_row_bytes = kInt8 ? (uint32_t)K * 2 : (uint32_t)K;
   const int nst = (K + kSK - 1) / kSK;                      // stages
   const int nsub_last = (K - (nst - 1) * kSK) / C::kSub;    // sub-steps of the last stage
-  const int nbi = G * (C::kBTile / 1024);                   // weight DMA instructions per stage
+  const int ngr = 4 * G;                                    // row groups of the workgroup
 
-  // weight DMA of stage st (one k-slice of all G tiles) into ring slot st & 1
-  auto issue_b = [&](int st) {
-    const uint32_t slot_addr = lds_ring + (uint32_t)((st & 1) * C::kStage);
-    if constexpr (kTiled) {
-      // one contiguous 8 KB block per tile, already in LDS order
-      const uint32_t T = (uint32_t)ntiles, Sn = (uint32_t)nst;
-      for (int q = wave; q < nbi; q += kSWaves) {
-        const int tl = q >> 3;
-        const uint32_t blk = (((uint32_t)e * T + (uint32_t)(t_begin + tl)) * Sn + (uint32_t)st) * 8192u;
-        dma16(w, blk + 1024u * (uint32_t)(q & 7) + 16u * (uint32_t)lane,
-              slot_addr + (uint32_t)(tl * C::kBTile + 1024 * (q & 7)));
-      }
+  // ---- this lane's weight pieces.  Group u of this wavefront is row group
+  // jg = wave + 8u of the workgroup: weight rows 64 (t_begin + jg / 4) +
+  // 16 (jg % 4) + 0..15, this lane's row r16 of them.  A wavefront with fewer
+  // than four groups repeats the last group's loads (L2 hits) so that every
+  // wavefront issues the same number of loads per stage.
+  // The loads are buffer loads: a per-lane offset that stays fixed over the
+  // stages (the lane's row and k group) plus a wavefront-uniform stage offset
+  // in a scalar register, checked against the size of the weight tensor (a
+  // piece past its end reads as zero; pieces past the last k of a row are
+  // never used).
+  const int KB = (K + 63) / 64;                             // MOE_W_FRAG: 64-k blocks per row group
+  const int N16 = (N + 15) / 16;
+  const __amdgpu_buffer_rsrc_t wrsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void *)w, (short)0, (int)w_bytes, 0x00020000);
+  uint32_t voff[kSGroups][2];
+#pragma unroll
+  for (int u = 0; u < kSGroups; ++u) {
+    const int jg = min(wave + kSWaves * u, ngr - 1);
+    const int tile = t_begin + (jg >> 2);
+    const int n = tile * 64 + 16 * (jg & 3) + r16;          // may be >= N in the last tile
+    if constexpr (kLayout == MOE_W_ROWMAJOR) {
+      const uint32_t row = ((uint32_t)e * (uint32_t)N + (uint32_t)min(n, N - 1)) * (uint32_t)K;
+      voff[u][0] = row + 16u * (uint32_t)g;
+      voff[u][1] = row + 64u + 16u * (uint32_t)g;
+    } else if constexpr (kLayout == MOE_W_TILED) {
+      const uint32_t row = ((uint32_t)e * (uint32_t)ntiles + (uint32_t)tile) * (uint32_t)nst * 8192u +
+                           (uint32_t)(16 * (jg & 3) + r16) * 128u;
+      voff[u][0] = row + (uint32_t)((g ^ swz(r16)) << 4);         // (swz(16q + r) = swz(r))
+      voff[u][1] = row + (uint32_t)(((g + 4) ^ swz(r16)) << 4);
     } else {
-      const uint8_t *wb = w + (size_t)st * kSK;
-      const uint32_t kmax = (uint32_t)(K - st * kSK) - 16u;   // last chunk inside the row
-      for (int q = wave; q < nbi; q += kSWaves) {            // 8 rows of 128 bytes per KB
-        const int tl = q >> 3;
-        const int n = 8 * (q & 7) + (lane >> 3);
-        const int c = (lane & 7) ^ swz(n);
-        const int col = min((t_begin + tl) * 64 + n, N - 1);
-        const uint32_t kb = min(16u * (uint32_t)c, kmax);
-        dma16(wb, ((uint32_t)e * (uint32_t)N + (uint32_t)col) * (uint32_t)K + kb,
-              slot_addr + (uint32_t)(tl * C::kBTile + 1024 * (q & 7)));
-      }
+      const uint32_t blk = ((uint32_t)e * (uint32_t)N16 + (uint32_t)min(n >> 4, N16 - 1)) *
+                           (uint32_t)KB * 1024u + 16u * (uint32_t)lane;
+      voff[u][0] = blk;
+      voff[u][1] = blk + 1024u;
     }
+  }
+  // byte offset of stage st, the same for every lane
+  auto st_off = [&](int st) -> int {
+    if constexpr (kLayout == MOE_W_ROWMAJOR) return kSK * st;
+    else if constexpr (kLayout == MOE_W_TILED) return 8192 * st;
+    else return 2048 * st;
   };
+  i32x4 wb[kSD][kSGroups][2];
+  auto load_w = [&](int st, i32x4 (&buf)[kSGroups][2]) {
+    const int so = st_off(st);
+#pragma unroll
+    for (int u = 0; u < kSGroups; ++u)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        buf[u][h] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, voff[u][h], so, 0);
+  };
+  constexpr int kLw = 2 * kSGroups;                         // weight loads per stage
 
   // Routing first.  With few blocks (decode) the block labels and the sorted
   // slot ids are copied into LDS by dword DMA ahead of the stage-0 weights:
   // vector-memory requests are served in order, so these small reads are not
   // queued behind the weight stream, and the whole routing costs one memory
-  // latency instead of a chain of dependent scalar loads.  They land in the
-  // activation areas of the two ring slots, which are free until the
-  // activation DMA of the first pass (labels: slot 0, slot ids: slot 1).
+  // latency instead of a chain of dependent scalar loads.  They land in ring
+  // slots 0 (labels) and 1 (slot ids), which are free until the activation
+  // DMA of the first pass.
+  // The epilogue's column scales are fetched first (one per thread), so that
+  // the epilogue reads only LDS.
+  float cs_pre = 0.0f;
+  if (tid < G * 64) {
+    const int col = min(t_begin * 64 + tid, N - 1);
+    cs_pre = kMode == kSFp8 ? a_scale[0] * w_scale[e] : w_scale[(size_t)e * N + col];
+  }
   const int n_sorted_dma = (max_blocks * 16 + 63) / 64;   // 256-byte dword DMAs
   const int n_label_dma = (max_blocks + 63) / 64;
   const bool staged = n_sorted_dma * 256 <= C::kABytes && n_label_dma * 256 <= C::kABytes;
-  const uint32_t lds_sorted = lds_ring + (uint32_t)(C::kStage + kSMaxTiles * C::kBTile);
-  const uint32_t lds_labels = lds_ring + (uint32_t)(kSMaxTiles * C::kBTile);
+  const uint32_t lds_labels = lds_ring;
+  const uint32_t lds_sorted = lds_ring + (uint32_t)C::kABytes;
   if (staged) {
     for (int q = wave; q < n_sorted_dma + n_label_dma; q += kSWaves) {
       if (q < n_sorted_dma) {
@@ -304,18 +347,18 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
       }
     }
   }
-  // The weights of stage 0 do not depend on the routing: start them now (G
-  // DMAs per wavefront).  The router weights are read only in the epilogue.
-  issue_b(0);
+  // The weights of stage 0 do not depend on the routing: start them now.  The
+  // router weights are read only in the epilogue.
+  load_w(0, wb[0]);
 
   // this expert's blocks [b_begin, b_end) from the ascending block labels
   // (-1 after the last block)
   int b_begin = max_blocks, b_end = max_blocks;
   constexpr int kEndLabel = 1 << 30;                       // -1 sorts after every expert
   if (staged) {
-    wait_dma_upto(G);                                      // this wave's routing DMAs landed
+    wait_dma_upto(kLw);                                    // this wave's routing DMAs landed
     __syncthreads();                                       // ... and everyone's
-    const int *labels = reinterpret_cast<const int *>(s_ring + kSMaxTiles * C::kBTile);
+    const int *labels = reinterpret_cast<const int *>(s_ring);
     for (int base = 0; base < max_blocks; base += 64) {   // a wavefront-wide search
       int v = base + lane < max_blocks ? labels[base + lane] : kEndLabel;
       v = v < 0 ? kEndLabel : v;
@@ -328,7 +371,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
     }
   } else {
     // every wavefront scans the labels on its scalar unit, 16 per load (the
-    // scalar loads count on lgkmcnt, so they do not wait for the weight DMA)
+    // scalar loads count on lgkmcnt, so they do not wait for the weights)
     typedef const __attribute__((address_space(4))) int *cint_ptr;
     typedef int int16v __attribute__((ext_vector_type(16)));
     typedef const __attribute__((address_space(4))) int16v *cint16_ptr;
@@ -347,7 +390,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
     for (; b0 < max_blocks && b_end == max_blocks; ++b0) visit(b0, c_expert_ids[b0]);
   }
   if (b_begin >= b_end) {
-    wait_dma_all();                                        // no DMA may outlive the workgroup
+    wait_dma_all();                                        // no load may outlive the workgroup
     return;
   }
 
@@ -357,7 +400,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
     int nvalid;                                            // rows holding a routed slot
     if (staged && pass_ == 0) {
       // from the staged copy (the activation DMA below overwrites it)
-      const int *sorted = reinterpret_cast<const int *>(s_ring + C::kStage + kSMaxTiles * C::kBTile);
+      const int *sorted = reinterpret_cast<const int *>(s_ring + C::kABytes);
       int slot = S;
       if (tid < nmb * 16) slot = sorted[bp * 16 + tid];
       if (tid < kSMB * 16) s_slot[tid] = slot;
@@ -388,20 +431,31 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
       __syncthreads();
       nvalid = s_nvalid;
     }
+    // router weight (x token scale) of each row, fetched now for the epilogue
+    float rw_pre = 0.0f;
+    if (tid < kSMB * 16) {
+      const int slot = s_slot[tid];
+      if (slot < S) {
+        rw_pre = topk_w[slot];
+        if constexpr (kI8) rw_pre *= a_scale[slot / top_k];
+      }
+    }
 
     // activation DMA of this wavefront (1 KB instructions q = wave + 8j): the
     // row and the swizzled chunk each lane fetches
     constexpr int kAPerWave = (C::kAInstr + kSWaves - 1) / kSWaves;
     // rows that hold a routed slot (padding slots only follow the expert's
     // last routed one, and their rows are never stored, so their LDS rows
-    // are left as they are); 1 KB holds 4 (bf16) or 8 (fp8) rows
+    // are left as they are); 1 KB holds 4 (bf16) or 8 (one-byte) rows
     const int a_instr = kInt8 ? (nvalid + 3) / 4 : (nvalid + 7) / 8;
+    int n_a = 0;                                           // this wave's DMAs per stage
     uint32_t a_row[kAPerWave], a_chk[kAPerWave];
 #pragma unroll
     for (int j = 0; j < kAPerWave; ++j) {
       const int q = wave + kSWaves * j;
       a_row[j] = 0;
       a_chk[j] = 0;
+      if (q < a_instr) ++n_a;
       if (q < C::kAInstr) {
         int r, c;
         if constexpr (kInt8) {                             // 4 rows of 256 bytes per KB
@@ -419,33 +473,27 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
       }
     }
 
-    auto issue_a = [&](int st) {
-      const uint32_t slot_addr = lds_ring + (uint32_t)((st & 1) * C::kStage);
+    // activation DMA of stage st into ring slot `ring`
+    auto issue_a = [&](int st, int ring) {
       const uint32_t amax = (uint32_t)(K - st * kSK) * (kInt8 ? 2u : 1u) - 16u;
 #pragma unroll
       for (int j = 0; j < kAPerWave; ++j) {
         const int q = wave + kSWaves * j;
         if (q < a_instr)                                   // only the rows of this pass
           dma16(a + (size_t)st * C::kARow, a_row[j] + min(a_chk[j], amax),
-                slot_addr + (uint32_t)(kSMaxTiles * C::kBTile + 1024 * q));
+                lds_ring + (uint32_t)(ring * C::kABytes + 1024 * q));
       }
     };
-    auto issue = [&](int st) {
-      issue_b(st);
-      issue_a(st);
-    };
 
-    f32x4 acc[4][kSMB];                                    // tiles par, par+2, par+4, par+6
+    f32x4 acc[kSGroups][kSMB];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int u = 0; u < kSGroups; ++u)
 #pragma unroll
-      for (int i = 0; i < kSMB; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < kSMB; ++i) acc[u][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int st) {
-      const uint8_t *sl = s_ring + (st & 1) * C::kStage;
-      const uint8_t *sa = sl + kSMaxTiles * C::kBTile;
+    auto compute = [&](int st, int ring, const i32x4 (&buf)[kSGroups][2]) {
+      const uint8_t *sa = s_ring + ring * C::kABytes;
       const int nsub = (st == nst - 1) ? nsub_last : kSK / C::kSub;
-      const int n = 16 * frag + r16;                       // this lane's weight row in a tile
 #pragma unroll
       for (int ss = 0; ss < kSK / C::kSub; ++ss) {
         if (ss >= nsub) break;
@@ -460,18 +508,15 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
             av[i][1] = *reinterpret_cast<const i32x4 *>(sa + sw256(r, c0 + 1));
           }
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int tl = par + 2 * t;
-            if (tl >= G) break;
-            const i32x4 braw =
-                *reinterpret_cast<const i32x4 *>(sl + tl * C::kBTile + sw128(n, 4 * ss + g));
+          for (int u = 0; u < kSGroups; ++u) {
+            if (wave + kSWaves * u >= ngr) break;          // wave-uniform
             i32x4 b0, b1;
-            dequant16w<kMode == kSF8W16>(braw, b0, b1);
+            dequant16w<kMode == kSF8W16>(buf[u][ss], b0, b1);
 #pragma unroll
             for (int i = 0; i < kSMB; ++i) {
               if (i >= nmb) break;
-              acc[t][i] = mfma_bf16(av[i][0], b0, acc[t][i]);
-              acc[t][i] = mfma_bf16(av[i][1], b1, acc[t][i]);
+              acc[u][i] = mfma_bf16(av[i][0], b0, acc[u][i]);
+              acc[u][i] = mfma_bf16(av[i][1], b1, acc[u][i]);
             }
           }
         } else {
@@ -485,52 +530,69 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
             av[i] = __builtin_shufflevector(al, ah, 0, 1, 2, 3, 4, 5, 6, 7);
           }
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int tl = par + 2 * t;
-            if (tl >= G) break;
-            const uint8_t *bt = sl + tl * C::kBTile;
-            const i32x4 bl = *reinterpret_cast<const i32x4 *>(bt + sw128(n, g));
-            const i32x4 bh = *reinterpret_cast<const i32x4 *>(bt + sw128(n, g + 4));
-            const i32x8 bv = __builtin_shufflevector(bl, bh, 0, 1, 2, 3, 4, 5, 6, 7);
+          for (int u = 0; u < kSGroups; ++u) {
+            if (wave + kSWaves * u >= ngr) break;          // wave-uniform
+            const i32x8 bv = __builtin_shufflevector(buf[u][0], buf[u][1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
             for (int i = 0; i < kSMB; ++i) {
               if (i >= nmb) break;
-              if constexpr (kI8) acc[t][i] = mfma_i8(av[i], bv, acc[t][i]);
-              else acc[t][i] = mfma_fp8(av[i], bv, acc[t][i]);
+              if constexpr (kI8) acc[u][i] = mfma_i8(av[i], bv, acc[u][i]);
+              else acc[u][i] = mfma_fp8(av[i], bv, acc[u][i]);
             }
           }
         }
       }
     };
 
-    if (pass_ == 0) {
-      issue_a(0);                                          // stage 0's weights are already in flight
-    } else {
-      issue(0);
+    // prologue: weights of stages 0..kSD-1 (stage 0 of the first pass is
+    // already in flight), then their activations; past the last stage the
+    // last one is loaded again (L2 hits), so every iteration below issues the
+    // same loads and the wait counts stay exact
+    if (pass_ > 0) load_w(0, wb[0]);
+#pragma unroll
+    for (int j = 1; j < kSD; ++j) load_w(min(j, nst - 1), wb[j]);
+#pragma unroll
+    for (int j = 0; j < kSD; ++j) issue_a(min(j, nst - 1), j);
+
+    // one stage: wait for it, free the previous slot, start stage st + kSD
+    // (its activations now, its weights once `buf` has been read)
+    auto step = [&](int st, i32x4 (&buf)[kSGroups][2]) {
+      // loads issued after this wave's loads of stage st (weights, then
+      // activations in the prologue; activations, then weights after it)
+      const int younger = st < kSD ? (kSD - 1 - st) * n_a + st * (n_a + kLw)
+                                   : (kSD - 1) * (n_a + kLw);
+      wait_dma_upto(younger);                              // stage st landed here
+      __syncthreads();                                     // ... and everywhere; slot st-1 is free
+      const int ahead = min(st + kSD, nst - 1);
+      issue_a(ahead, (st + kSD) % kSAS);
+      compute(st, st % kSAS, buf);
+      load_w(ahead, buf);
+    };
+    // whole rounds of kSD stages with no exit inside, so that the compiler's
+    // own wait before each MFMA counts the loads of the later stages as
+    // still in flight; then the last nst % kSD stages
+    int st0 = 0;
+    for (; st0 + kSD <= nst; st0 += kSD) {
+#pragma unroll
+      for (int j = 0; j < kSD; ++j) step(st0 + j, wb[j]);
     }
-    for (int st = 0; st < nst; ++st) {
-      wait_dma_all();                                      // this wave's DMA for stage st landed
-      __syncthreads();                                     // ... and everyone's; the other slot is free
-      if (st + 1 < nst) issue(st + 1);
-      compute(st);
-    }
+#pragma unroll
+    for (int j = 0; j + 1 < kSD; ++j)
+      if (st0 + j < nst) step(st0 + j, wb[j]);
+    wait_dma_all();                                        // the reloads land before ring reuse
 
     // ---- epilogue: scale x router weight, rounded to bf16; lane pairs
     // (adjacent columns) combine into one 4-byte store
-    if (pass_ == 0) {
-      // per-column scale of this workgroup's tiles (int8) or the fused scalar
-      for (int c = tid; c < G * 64; c += kSThreads) {
-        const int col = min(t_begin * 64 + c, N - 1);
-        s_scale[c] = kMode == kSFp8 ? a_scale[0] * w_scale[e] : w_scale[(size_t)e * N + col];
-      }
-      __syncthreads();
-    }
+    if (pass_ == 0 && tid < G * 64) s_scale[tid] = cs_pre;   // per-column (or fused) scale
+    if (tid < kSMB * 16) s_rw[tid] = rw_pre;
+    __syncthreads();
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int tl = par + 2 * t;
-      if (tl >= G) break;                              // wave-uniform
-      const int col = (t_begin + tl) * 64 + 16 * frag + r16;
-      const float cs = s_scale[tl * 64 + 16 * frag + r16];
+    for (int u = 0; u < kSGroups; ++u) {
+      const int jg = wave + kSWaves * u;
+      if (jg >= ngr) break;                                // wave-uniform
+      const int cl = 64 * (jg >> 2) + 16 * (jg & 3) + r16; // column within the workgroup
+      const int col = t_begin * 64 + cl;
+      const float cs = s_scale[cl];
 #pragma unroll
       for (int i = 0; i < kSMB; ++i) {
         if (i >= nmb) break;                           // wave-uniform
@@ -538,12 +600,9 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
         for (int rr = 0; rr < 4; ++rr) {
           const int k = 16 * i + 4 * g + rr;
           const int slot = s_slot[k];
-          float rw = slot < S ? topk_w[slot] : 0.0f;     // router weight (x token scale)
-          float acc_v = acc[t][i][rr];
-          if constexpr (kI8) {
-            acc_v = (float)__builtin_bit_cast(int, acc_v);
-            rw *= slot < S ? a_scale[slot / top_k] : 0.0f;
-          }
+          const float rw = s_rw[k];                      // router weight (x token scale)
+          float acc_v = acc[u][i][rr];
+          if constexpr (kI8) acc_v = (float)__builtin_bit_cast(int, acc_v);
           const float v = acc_v * cs * rw;
           const float vn = __shfl_xor(v, 1);           // the next column's value
           // N is a multiple of 8: an even column and its neighbour are both
@@ -1713,6 +1772,22 @@ int next_launch_slot() {
 
 // persistent decomposition of the weight stream: E * groups workgroups, each
 // with tiles_per_group consecutive 64-column tiles of one expert
+// bytes of the weight tensor in the layout the call passes (below 4 GiB)
+uint32_t stream_weight_bytes(const RoutedArgs &r) {
+  if (r.w_layout == MOE_W_TILED)
+    return (uint32_t)r.E * (uint32_t)((r.N + 63) / 64) * (uint32_t)((r.K + 127) / 128) * 8192u;
+  if (r.w_layout == MOE_W_FRAG)
+    return (uint32_t)r.E * (uint32_t)((r.N + 15) / 16) * (uint32_t)((r.K + 63) / 64) * 1024u;
+  return (uint32_t)r.E * (uint32_t)r.N * (uint32_t)r.K;
+}
+
+template <int kMode>
+decltype(&stream_kernel<kMode, MOE_W_ROWMAJOR>) stream_kernel_for(int layout) {
+  if (layout == MOE_W_FRAG) return stream_kernel<kMode, MOE_W_FRAG>;
+  if (layout == MOE_W_TILED) return stream_kernel<kMode, MOE_W_TILED>;
+  return stream_kernel<kMode, MOE_W_ROWMAJOR>;
+}
+
 void stream_grid(int N, int E, int &groups, int &tiles_per_group) {
   const int ntiles = (N + 63) / 64;
   int tpg = (E * ntiles + num_cus() - 1) / num_cus();
@@ -1727,10 +1802,10 @@ hipError_t launch_gemm_fp8(const uint8_t *a_q, const float *a_scale, const uint8
   if (r.block_m == 16) {
     int groups, tpg;
     stream_grid(r.N, r.E, groups, tpg);
-    auto k = r.w_layout ? stream_kernel<kSFp8, true> : stream_kernel<kSFp8, false>;
+    auto k = stream_kernel_for<kSFp8>(r.w_layout);
     hipLaunchKernelGGL(k, dim3(r.E * groups), dim3(kSThreads), 0, s, a_q, a_scale, w_q, w_scale,
                        r.sorted_ids, r.expert_ids, r.num_post, r.topk_w, r.M, r.K, r.N, r.top_k,
-                       groups, tpg, r.max_blocks, r.y);
+                       groups, tpg, r.max_blocks, r.y, stream_weight_bytes(r));
   } else {
     const long long tiles = (long long)(r.max_blocks / 2 + r.E) * ((r.N + kHBN - 1) / kHBN);
     if ((long long)r.M * r.top_k >= kWideMinRowsPerExpert * (long long)r.E) {
@@ -1756,10 +1831,10 @@ hipError_t launch_gemm_int8w8a8(const int8_t *a_q, const float *a_scale, const i
   if (r.block_m == 16) {
     int groups, tpg;
     stream_grid(r.N, r.E, groups, tpg);
-    auto k = r.w_layout ? stream_kernel<kSI8, true> : stream_kernel<kSI8, false>;
+    auto k = stream_kernel_for<kSI8>(r.w_layout);
     hipLaunchKernelGGL(k, dim3(r.E * groups), dim3(kSThreads), 0, s, ab, a_scale, wb, w_scale,
                        r.sorted_ids, r.expert_ids, r.num_post, r.topk_w, r.M, r.K, r.N, r.top_k,
-                       groups, tpg, r.max_blocks, r.y);
+                       groups, tpg, r.max_blocks, r.y, stream_weight_bytes(r));
   } else {
     const long long tiles = (long long)(r.max_blocks / 2 + r.E) * ((r.N + kHBN - 1) / kHBN);
     auto k = r.w_layout ? gemm_wide_kernel<kFmtI8, true> : gemm_wide_kernel<kFmtI8, false>;
@@ -1776,10 +1851,10 @@ hipError_t launch_gemm_fp8w8a16(const uint16_t *a, const uint8_t *w_q, const flo
   if (r.block_m == 16) {
     int groups, tpg;
     stream_grid(r.N, r.E, groups, tpg);
-    auto k = r.w_layout ? stream_kernel<kSF8W16, true> : stream_kernel<kSF8W16, false>;
+    auto k = stream_kernel_for<kSF8W16>(r.w_layout);
     hipLaunchKernelGGL(k, dim3(r.E * groups), dim3(kSThreads), 0, s, ab, nullptr, w_q, w_scale,
                        r.sorted_ids, r.expert_ids, r.num_post, r.topk_w, r.M, r.K, r.N, r.top_k,
-                       groups, tpg, r.max_blocks, r.y);
+                       groups, tpg, r.max_blocks, r.y, stream_weight_bytes(r));
   } else {
     const long long tiles = (long long)r.max_blocks * ((r.N + kGBN - 1) / kGBN);
     auto k = r.w_layout ? gemm_kernel<kFmtF8W16, true> : gemm_kernel<kFmtF8W16, false>;
@@ -1797,10 +1872,10 @@ hipError_t launch_gemm_int8(const uint16_t *a, const int8_t *w_q, const float *w
   if (r.block_m == 16) {
     int groups, tpg;
     stream_grid(r.N, r.E, groups, tpg);
-    auto k = r.w_layout ? stream_kernel<kSW8A16, true> : stream_kernel<kSW8A16, false>;
+    auto k = stream_kernel_for<kSW8A16>(r.w_layout);
     hipLaunchKernelGGL(k, dim3(r.E * groups), dim3(kSThreads), 0, s, ab, nullptr, wb, w_scale,
                        r.sorted_ids, r.expert_ids, r.num_post, r.topk_w, r.M, r.K, r.N, r.top_k,
-                       groups, tpg, r.max_blocks, r.y);
+                       groups, tpg, r.max_blocks, r.y, stream_weight_bytes(r));
   } else {
     const long long tiles = (long long)r.max_blocks * ((r.N + kGBN - 1) / kGBN);
     auto k = r.w_layout ? gemm_kernel<kFmtInt8, true> : gemm_kernel<kFmtInt8, false>;

@@ -83,7 +83,7 @@ struct RoutedArgs {
   const int *num_post;
   const float *topk_w;
   int M, K, N, E, top_k, block_m, max_blocks;
-  int w_layout;                        // 0 row-major [E,N,K], 1 tiled (moe_pack_weights)
+  int w_layout;                        // MOE_W_ROWMAJOR, MOE_W_TILED or MOE_W_FRAG
   uint16_t *y;                  // bf16 per-slot results [M*top_k, N]
 };
 
@@ -99,7 +99,7 @@ hipError_t launch_gemm_mxfp8(const uint8_t *a_q, const uint8_t *a_sf, const uint
                              const uint8_t *w_sf, const int *m_offsets, int rows, int K,
                              int N, int E, uint16_t *out, hipStream_t s);
 
-hipError_t launch_pack_weights(const uint8_t *w, int E, int N, int K, uint8_t *packed,
+hipError_t launch_pack_weights(const uint8_t *w, int E, int N, int K, int layout, uint8_t *packed,
                                hipStream_t s);
 
 hipError_t launch_combine(const uint16_t *y, int M, int N, int top_k, uint16_t *out,

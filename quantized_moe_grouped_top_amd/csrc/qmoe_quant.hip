@@ -614,6 +614,29 @@ __global__ __launch_bounds__(kThreads) void pack_weights_kernel(const uint8_t *_
   }
 }
 
+// ---- MOE_W_FRAG: one thread per 16-byte piece ----------------------------
+// Block (e, j, b) of 1 KB, piece p = 16q + r holding row 16j + r, k = 64b +
+// 16q .. +15; rows >= N and k >= K are zero.
+__global__ __launch_bounds__(kThreads) void pack_frag_kernel(const uint8_t *__restrict__ w, int E,
+                                                             int N, int K,
+                                                             uint8_t *__restrict__ packed) {
+  const int J = (N + 15) / 16, B = (K + 63) / 64;
+  const long long pieces = (long long)E * J * B * 64;
+  for (long long i = blockIdx.x * (long long)kThreads + threadIdx.x; i < pieces;
+       i += (long long)gridDim.x * kThreads) {
+    const long long blk = i >> 6;
+    const int p = (int)(i & 63);
+    const int b = (int)(blk % B);
+    const int j = (int)((blk / B) % J);
+    const int e = (int)(blk / ((long long)B * J));
+    const int n = 16 * j + (p & 15);
+    const int k0 = 64 * b + 16 * (p >> 4);
+    i32x4 v = {0, 0, 0, 0};
+    if (n < N && k0 < K) v = *reinterpret_cast<const i32x4 *>(w + ((long long)e * N + n) * K + k0);
+    *reinterpret_cast<i32x4 *>(packed + i * 16) = v;
+  }
+}
+
 int grid_for(long long items, int cap) {
   long long g = (items + kThreads - 1) / kThreads;
   if (g < 1) g = 1;
@@ -734,8 +757,14 @@ hipError_t launch_quant_mx_rows_f32(const float *w, long long rows, int K, uint8
   return hipGetLastError();
 }
 
-hipError_t launch_pack_weights(const uint8_t *w, int E, int N, int K, uint8_t *packed,
-                               hipStream_t s) {
+hipError_t launch_pack_weights(const uint8_t *w, int E, int N, int K, int layout,
+                               uint8_t *packed, hipStream_t s) {
+  if (layout == MOE_W_FRAG) {
+    const long long pieces = (long long)E * ((N + 15) / 16) * ((K + 63) / 64) * 64;
+    hipLaunchKernelGGL(pack_frag_kernel, dim3(grid_for(pieces, 16384)), dim3(kThreads), 0, s, w, E,
+                       N, K, packed);
+    return hipGetLastError();
+  }
   const long long chunks = (long long)E * ((N + kPackRows - 1) / kPackRows) *
                            ((K + kPackK - 1) / kPackK) * (kPackRows * kPackK / 16);
   hipLaunchKernelGGL(pack_weights_kernel, dim3(grid_for(chunks, 16384)), dim3(kThreads), 0, s, w,

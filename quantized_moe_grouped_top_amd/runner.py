@@ -58,11 +58,12 @@ def quantize_weights(w, fmt):
     raise ValueError(fmt)
 
 
-def pack_weights(w_q):
-    """Tiled (MOE_W_TILED) copy of one-byte weights [E, N, K] on their device."""
+def pack_weights(w_q, layout=MOE_W_TILED):
+    """Packed copy (MOE_W_TILED or MOE_W_FRAG) of one-byte weights [E, N, K]
+    on their device."""
     E, N, K = w_q.shape
-    out = _empty((moe_packed_weight_bytes(E, N, K),), torch.uint8, w_q.device)
-    moe_pack_weights(w_q, E, N, K, out)
+    out = _empty((moe_packed_weight_bytes(E, N, K, layout),), torch.uint8, w_q.device)
+    moe_pack_weights(w_q, E, N, K, layout, out)
     return out
 
 

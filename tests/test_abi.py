@@ -93,7 +93,8 @@ def _gemm_fp8(**kw):
     (dict(N=0), qm.MOE_EINVAL),
     (dict(top_k=9), qm.MOE_EINVAL),
     (dict(E=200, top_k=2), qm.MOE_EINVAL),
-    (dict(w_layout=2), qm.MOE_EINVAL),         # unknown weight layout
+    (dict(w_layout=3), qm.MOE_EINVAL),         # unknown weight layout
+    (dict(w_layout=2, block_m=128), qm.MOE_EUNSUPPORTED),   # MOE_W_FRAG needs block_m 16
     (dict(N=1 << 20, K=1 << 12), qm.MOE_EUNSUPPORTED),   # weights beyond 4 GiB
 ])
 def test_gemm_fp8_rejects(kw, code):
@@ -198,18 +199,28 @@ def test_quantize_and_combine_reject():
 
 
 def test_pack_sizes_and_rejects():
-    assert qm.moe_packed_weight_bytes(8, 14336, 4096) == 8 * 224 * 32 * 8192
-    assert qm.moe_packed_weight_bytes(2, 100, 320) == 2 * 2 * 3 * 8192     # padded tiles/slices
-    assert qm.moe_packed_weight_bytes(0, 4, 4) == 0
+    T = qm.MOE_W_TILED
+    assert qm.moe_packed_weight_bytes(8, 14336, 4096, T) == 8 * 224 * 32 * 8192
+    assert qm.moe_packed_weight_bytes(2, 100, 320, T) == 2 * 2 * 3 * 8192  # padded tiles/slices
+    assert qm.moe_packed_weight_bytes(0, 4, 4, T) == 0
+    F = qm.MOE_W_FRAG
+    assert qm.moe_packed_weight_bytes(8, 14336, 4096, F) == 8 * 14336 * 4096
+    assert qm.moe_packed_weight_bytes(2, 100, 320, F) == 2 * 7 * 5 * 1024  # padded groups/blocks
+    assert qm.moe_packed_weight_bytes(2, 100, 320, qm.MOE_W_ROWMAJOR) == 2 * 100 * 320
+    assert qm.moe_packed_weight_bytes(2, 100, 320, 7) == 0
+    for layout in (T, F):
+        with pytest.raises(qm.MoeError) as ei:
+            qm.moe_pack_weights(FAKE, 2, 64, 100, layout, FAKE, stream=0)
+        assert ei.value.code == qm.MOE_EUNSUPPORTED             # K % 16
+        with pytest.raises(qm.MoeError) as ei:
+            qm.moe_pack_weights(MIS, 2, 64, 128, layout, FAKE, stream=0)
+        assert ei.value.code == qm.MOE_EINVAL                   # misaligned
+        with pytest.raises(qm.MoeError) as ei:
+            qm.moe_pack_weights(FAKE, 64, 1 << 16, 1 << 12, layout, FAKE, stream=0)
+        assert ei.value.code == qm.MOE_EUNSUPPORTED             # 16 GiB packed
     with pytest.raises(qm.MoeError) as ei:
-        qm.moe_pack_weights(FAKE, 2, 64, 100, FAKE, stream=0)
-    assert ei.value.code == qm.MOE_EUNSUPPORTED                 # K % 16
-    with pytest.raises(qm.MoeError) as ei:
-        qm.moe_pack_weights(MIS, 2, 64, 128, FAKE, stream=0)
-    assert ei.value.code == qm.MOE_EINVAL                       # misaligned
-    with pytest.raises(qm.MoeError) as ei:
-        qm.moe_pack_weights(FAKE, 64, 1 << 16, 1 << 12, FAKE, stream=0)
-    assert ei.value.code == qm.MOE_EUNSUPPORTED                 # 16 GiB packed
+        qm.moe_pack_weights(FAKE, 2, 64, 128, qm.MOE_W_ROWMAJOR, FAKE, stream=0)
+    assert ei.value.code == qm.MOE_EINVAL                       # nothing to pack into
 
 
 def test_library_missing_is_loud(monkeypatch, tmp_path):

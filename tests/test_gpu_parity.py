@@ -48,7 +48,7 @@ def run_routed(wl, block_m=None, variant=0, full=True, n_tok=48, n_col=64, logit
     lg = case["logits"] if logits is None else logits.to(DEV)
     moe = runner.RoutedMoE(wl.fmt, M, K, N, E, top_k, block_m=block_m, w_layout=layout)
     w_q, w_scale = runner.quantize_weights(w, wl.fmt)
-    w_gemm = runner.pack_weights(w_q) if layout == qm.MOE_W_TILED else w_q
+    w_gemm = runner.pack_weights(w_q, layout) if layout != qm.MOE_W_ROWMAJOR else w_q
     moe.y.fill_(0x7FC0)                      # bf16 NaN: unwritten slots show up
     moe.out.fill_(0x7FC0)
     moe.forward(x, lg, w_gemm, w_scale)
@@ -156,19 +156,26 @@ SMALL = [
 ]
 
 
-LAYOUTS = [qm.MOE_W_ROWMAJOR, qm.MOE_W_TILED]
+# (block_m, weight layout): MOE_W_FRAG is for the streaming kernel only
+KERNEL_LAYOUTS = [(16, qm.MOE_W_ROWMAJOR), (16, qm.MOE_W_TILED), (16, qm.MOE_W_FRAG),
+                  (128, qm.MOE_W_ROWMAJOR), (128, qm.MOE_W_TILED)]
+KL_IDS = ["16-rowmajor", "16-tiled", "16-frag", "128-rowmajor", "128-tiled"]
 
 
-@pytest.mark.parametrize("layout", LAYOUTS, ids=["rowmajor", "tiled"])
-@pytest.mark.parametrize("block_m", [16, 128])
+def bench_layout(wl):
+    """The weight layout the benchmark uses for a workload's recommended block_m."""
+    return (qm.MOE_W_FRAG if qm.moe_recommended_block_m(wl.M, wl.E, wl.top_k) == 16
+            else qm.MOE_W_TILED)
+
+
+@pytest.mark.parametrize("block_m,layout", KERNEL_LAYOUTS, ids=KL_IDS)
 @pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
 def test_routed_small(wl, block_m, layout):
     run_routed(wl, block_m=block_m, full=True, layout=layout)
 
 
-@pytest.mark.parametrize("layout", LAYOUTS, ids=["rowmajor", "tiled"])
+@pytest.mark.parametrize("block_m,layout", KERNEL_LAYOUTS, ids=KL_IDS)
 @pytest.mark.parametrize("fmt", ["fp8", "int8"])
-@pytest.mark.parametrize("block_m", [16, 128])
 def test_routed_all_tokens_one_expert(fmt, block_m, layout):
     wl = synth.small(fmt, 150, 256, 80, 8, 2)
     lg = torch.randn(150, 8, generator=torch.Generator().manual_seed(5))
@@ -224,8 +231,8 @@ FULL = [synth.WORKLOADS[n] for n in [
 
 @pytest.mark.parametrize("wl", FULL, ids=[w.name for w in FULL])
 def test_routed_full_size_sampled(wl):
-    """The benchmark's launch configuration: recommended block_m, tiled weights."""
-    run_routed(wl, block_m=None, full=False, layout=qm.MOE_W_TILED)
+    """The benchmark's launch configuration: recommended block_m, packed weights."""
+    run_routed(wl, block_m=None, full=False, layout=bench_layout(wl))
     torch.cuda.empty_cache()
 
 
@@ -240,6 +247,16 @@ ROWMAJOR_FULL = [synth.WORKLOADS[n] for n in [
 def test_routed_full_size_sampled_rowmajor(wl):
     run_routed(wl, block_m=None, full=False, layout=qm.MOE_W_ROWMAJOR)
     torch.cuda.empty_cache()
+
+
+def _pack_frag_reference(w, N, K):
+    """The MOE_W_FRAG layout as its definition states it (numpy)."""
+    E = w.shape[0]
+    J, B = -(-N // 16), -(-K // 64)
+    pad = np.zeros((E, J * 16, B * 64), np.uint8)
+    pad[:, :N, :K] = w
+    # [e, j, r, b, q, i] (n = 16j + r, k = 64b + 16q + i) -> [e, j, b, q, r, i]
+    return pad.reshape(E, J, 16, B, 4, 16).transpose(0, 1, 3, 4, 2, 5).reshape(-1)
 
 
 def _pack_reference(w, N, K):
@@ -262,9 +279,11 @@ def test_pack_weights_layout(E, N, K):
     _announce(f"pack E={E} N={N} K={K}")
     g = torch.Generator(device=DEV).manual_seed(E * 1000 + N + K)
     w = torch.randint(0, 256, (E, N, K), generator=g, device=DEV, dtype=torch.int32).to(torch.uint8)
-    p = runner.pack_weights(w)
+    p = runner.pack_weights(w, qm.MOE_W_TILED)
+    f = runner.pack_weights(w, qm.MOE_W_FRAG)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(p.cpu().numpy(), _pack_reference(w.cpu().numpy(), N, K))
+    np.testing.assert_array_equal(f.cpu().numpy(), _pack_frag_reference(w.cpu().numpy(), N, K))
 
 
 # ----------------------------------------------------------------------------

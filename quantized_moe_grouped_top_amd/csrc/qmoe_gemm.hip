@@ -168,6 +168,7 @@ template <bool kInt8>
 struct SCfg {
   // weight stages held in registers per wavefront (loads run up to kD stages
   // ahead of the MFMAs); the bf16 path needs more registers for its operands
+  // (with three stages there it runs slower, measured)
   static constexpr int kD = kInt8 ? 2 : 3;
   static constexpr int kAS = kD + 1;                        // activation ring slots
   static constexpr int kSub = kInt8 ? 64 : 128;            // k per MFMA sub-step
@@ -581,36 +582,45 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
       if (st0 + j < nst) step(st0 + j, wb[j]);
     wait_dma_all();                                        // the reloads land before ring reuse
 
-    // ---- epilogue: scale x router weight, rounded to bf16; lane pairs
-    // (adjacent columns) combine into one 4-byte store
+    // ---- epilogue: scale x router weight, rounded to bf16, staged one
+    // 16-row block at a time in the (now idle) activation ring as [16][64 G]
+    // bf16 rows, then written out as whole 16-byte pieces of each routed
+    // slot's row
     if (pass_ == 0 && tid < G * 64) s_scale[tid] = cs_pre;   // per-column (or fused) scale
     if (tid < kSMB * 16) s_rw[tid] = rw_pre;
     __syncthreads();
+    uint16_t *stg = reinterpret_cast<uint16_t *>(s_ring);
+    const int wcols = 64 * G;                              // columns of this workgroup
+    const int pieces = wcols / 8;                          // 16-byte pieces per staged row
 #pragma unroll
-    for (int u = 0; u < kSGroups; ++u) {
-      const int jg = wave + kSWaves * u;
-      if (jg >= ngr) break;                                // wave-uniform
-      const int cl = 64 * (jg >> 2) + 16 * (jg & 3) + r16; // column within the workgroup
-      const int col = t_begin * 64 + cl;
-      const float cs = s_scale[cl];
+    for (int i = 0; i < kSMB; ++i) {
+      if (i >= nmb) break;                                 // wave-uniform
 #pragma unroll
-      for (int i = 0; i < kSMB; ++i) {
-        if (i >= nmb) break;                           // wave-uniform
+      for (int u = 0; u < kSGroups; ++u) {
+        const int jg = wave + kSWaves * u;
+        if (jg >= ngr) break;                              // wave-uniform
+        const int cl = 64 * (jg >> 2) + 16 * (jg & 3) + r16;   // column within the workgroup
+        const float cs = s_scale[cl];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const int k = 16 * i + 4 * g + rr;
-          const int slot = s_slot[k];
-          const float rw = s_rw[k];                      // router weight (x token scale)
+          const int k = 4 * g + rr;                        // row within the block
           float acc_v = acc[u][i][rr];
           if constexpr (kI8) acc_v = (float)__builtin_bit_cast(int, acc_v);
-          const float v = acc_v * cs * rw;
-          const float vn = __shfl_xor(v, 1);           // the next column's value
-          // N is a multiple of 8: an even column and its neighbour are both
-          // inside the row or both past its end
-          if (slot < S && (r16 & 1) == 0 && col < N)
-            *reinterpret_cast<uint32_t *>(y + (size_t)slot * N + col) = f32x2_to_bf16x2(v, vn);
+          const float v = acc_v * cs * s_rw[16 * i + k];   // x router weight (x token scale)
+          stg[k * wcols + cl] = (uint16_t)f32x2_to_bf16x2(v, 0.0f);
         }
       }
+      __syncthreads();
+      // N is a multiple of 8, so a piece is inside the row or past its end
+      for (int q = tid; q < 16 * pieces; q += kSThreads) {
+        const int k = q / pieces, c8 = q - k * pieces;
+        const int slot = s_slot[16 * i + k];
+        const int col = t_begin * 64 + 8 * c8;
+        if (slot < S && col < N)
+          *reinterpret_cast<i32x4 *>(y + (size_t)slot * N + col) =
+              *reinterpret_cast<const i32x4 *>(stg + k * wcols + 8 * c8);
+      }
+      __syncthreads();                                     // the staging area is reused
     }
   }
 }

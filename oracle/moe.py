@@ -28,6 +28,8 @@ Readings taken where the pages are silent (each is restated in the design doc):
   fl32(x * fl32(1 / s)) before rounding to e4m3; an all-zero tensor has s = 1;
 * int8 per-channel weights use s = fl32(amax_row / 127) and
   clamp(round_half_even(fl32(w * fl32(1 / s))), -127, 127);
+* int4 weight-only weights take the same rule with 7 in place of 127 (codes
+  -7..7, one scale per output channel);
 * MXFP8 takes the OCP MX rule for the shared exponent of each block of 32
   values along K: 2^(floor(log2 amax) - 8), written as the e8m0 byte
   clamp(exponent_field(amax) - 8, 0, 254), with the elements x / 2^(b-127)
@@ -176,6 +178,22 @@ def quantize_weight_int8(w):
     inv = (np.float32(1.0) / s).astype(np.float32)
     q = np.rint(w * inv[..., None])                  # float32 product, half to even
     return np.clip(q, -127, 127).astype(np.int8), s
+
+
+def quantize_weight_int4(w):
+    """int4 weight-only weights ("int4wo" of "Enabling MOE Quantization using
+    linear decomposition", Summary; the page gives no granularity): the int8
+    per-output-channel rule with 7 in place of 127, s = fl32(amax_row / 7)
+    (1 for a zero row), q = clamp(round_half_even(fl32(w * fl32(1 / s))),
+    -7, 7).  w float32 [E, N, K] -> (w_q int8 [E, N, K] holding the codes,
+    w_scale float32 [E, N])."""
+    w = _f32(w)
+    amax = np.max(np.abs(w), axis=-1)
+    s = np.where(amax == 0, np.float32(1.0), (amax / np.float32(7.0)).astype(np.float32))
+    s = s.astype(np.float32)
+    inv = (np.float32(1.0) / s).astype(np.float32)
+    q = np.rint(w * inv[..., None])                  # float32 product, half to even
+    return np.clip(q, -7, 7).astype(np.int8), s
 
 
 def quantize_act_int8_rows(x_bf16):
@@ -353,6 +371,21 @@ def grouped_gemm_int8w8a16(a_bf16, w_q, w_scale, topk_ids, topk_weights,
     """int8 W8A16: bf16 activations x int8 weights with one scale per expert
     and output channel ("Tianxing/moe quantization", INT8_W8A16 Benchmark;
     "INT8 quantization support": int8 weights used with 16-bit activations)."""
+    a = np.asarray(a_bf16)
+    w_q = np.asarray(w_q)
+    ws = np.asarray(w_scale, dtype=np.float32).astype(np.float64)
+    return _grouped(lambda t: bf16_decode(a[t]),
+                    lambda e, c: w_q[e][c].astype(np.float64),
+                    lambda e, c: ws[e][c],
+                    topk_ids, topk_weights, w_q.shape[1], slots, cols)
+
+
+def grouped_gemm_int4w16(a_bf16, w_q, w_scale, topk_ids, topk_weights,
+                         slots=None, cols=None):
+    """int4 weight-only: bf16 activations x int4 codes (-7..7) with one scale
+    per expert and output channel ("int4wo" of "Enabling MOE Quantization
+    using linear decomposition", Summary); the codes are used as the exact
+    integers they stand for."""
     a = np.asarray(a_bf16)
     w_q = np.asarray(w_q)
     ws = np.asarray(w_scale, dtype=np.float32).astype(np.float64)

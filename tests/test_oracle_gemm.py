@@ -232,3 +232,32 @@ def test_fp8w8a16_brute_force():
     ref = _exact_routed(lambda t, k: _fr(xv[t, k]), lambda e, n, k: dec[int(wq[e, n, k])],
                         lambda e, n: _fr(sw[e, n]), ids, wts, M, K, N, top_k)
     np.testing.assert_array_equal(O.grouped_gemm_fp8w8a16(x, wq, sw, ids, wts), ref)
+
+
+def test_int4w16_brute_force():
+    """int4 weight-only by exact rational arithmetic on a tiny routed case:
+    bf16 activations times the integer codes, the channel scale and the
+    router weight, rounded once to float32."""
+    rng = np.random.default_rng(16)
+    M, K, N, E, top_k = 3, 32, 5, 4, 2
+    x, w, lg = _tiny(rng, M, K, N, E)
+    ids, wts = O.route_topk(lg, top_k)
+    wq, sw = O.quantize_weight_int4(w)
+    assert wq.min() >= -7 and wq.max() <= 7
+    xv = F.bf16_decode(x)
+    ref = _exact_routed(lambda t, k: _fr(xv[t, k]), lambda e, n, k: Fraction(int(wq[e, n, k])),
+                        lambda e, n: _fr(sw[e, n]), ids, wts, M, K, N, top_k)
+    np.testing.assert_array_equal(O.grouped_gemm_int4w16(x, wq, sw, ids, wts), ref)
+
+
+def test_int4w16_integer_identity():
+    """Small-integer activations, unit scales, one expert and router weight 1:
+    the plain integer product of the codes."""
+    rng = np.random.default_rng(17)
+    M, K, N = 4, 64, 6
+    xi = rng.integers(-20, 21, (M, K))
+    x = _bf16(xi.astype(np.float32))
+    wq = rng.integers(-7, 8, (1, N, K)).astype(np.int8)
+    ids = np.zeros((M, 1), np.int32)
+    y = O.grouped_gemm_int4w16(x, wq, np.ones((1, N), np.float32), ids, np.ones((M, 1), np.float32))
+    np.testing.assert_array_equal(y, (xi @ wq[0].astype(np.int64).T).astype(np.float32))

@@ -253,3 +253,48 @@ def test_fp8_weight_rows_equal_per_tensor_rule_per_row():
             if (e, n) != (1, 2):
                 k = int(np.argmax(np.abs(w[e, n])))
                 assert abs(float(F.e4m3_decode(q[e, n, k]))) == 448.0
+
+
+# ------------------------------------------------------------- int4 -----
+def test_int4_per_channel_brute_force():
+    """int4 weight-only codes and scales by exact rational arithmetic: the
+    scale is amax/7 rounded once to float32, every code the float32 product
+    w * fl32(1/s) rounded half to even and clamped to -7..7; each nonzero row
+    reaches |q| = 7 at its largest element."""
+    rng = np.random.default_rng(21)
+    w = (rng.standard_normal((2, 6, 40)) / 5).astype(np.float32)
+    w[0, 2] = 0.0                                  # an all-zero channel
+    w[1, 4, :8] = [0.5, -0.5, 1.5, 2.5, -3.5, 3.5, 0.25, 0.0]   # half-way codes at s = 0.5
+    w[1, 4, 8:] = 0.0
+    q, s = O.quantize_weight_int4(w)
+    assert q.dtype == np.int8 and s.dtype == np.float32
+    for e in range(2):
+        for n in range(6):
+            row = w[e, n]
+            amax = float(np.max(np.abs(row)))
+            s_ref = np.float32(1.0) if amax == 0 else np.float32(Fraction(amax) / 7)
+            assert s[e, n] == s_ref
+            inv = np.float32(Fraction(1) / Fraction(float(s_ref)))
+            for k in range(40):
+                prod = np.float32(Fraction(float(row[k])) * Fraction(float(inv)))
+                ref = max(-7, min(7, _round_half_even(Fraction(float(prod)))))
+                assert int(q[e, n, k]) == ref
+            if amax:
+                assert int(np.max(np.abs(q[e, n].astype(int)))) == 7
+            else:
+                assert not q[e, n].any()
+    # the hand-made row: amax 3.5 -> s = 0.5, codes of w / 0.5 half to even
+    assert s[1, 4] == np.float32(0.5)
+    np.testing.assert_array_equal(q[1, 4, :8], [1, -1, 3, 5, -7, 7, 0, 0])
+
+
+def test_int4_symmetry_and_error_bound():
+    rng = np.random.default_rng(22)
+    w = rng.standard_normal((2, 3, 64)).astype(np.float32)
+    q1, s1 = O.quantize_weight_int4(w)
+    q2, s2 = O.quantize_weight_int4(-w)
+    np.testing.assert_array_equal(q1, -q2)
+    np.testing.assert_array_equal(s1, s2)
+    # every code is within half a step of w / s (no clamping below amax)
+    err = np.abs(w.astype(np.float64) - q1 * s1[..., None].astype(np.float64))
+    assert np.all(err <= 0.5 * s1[..., None] * (1 + 1e-6))

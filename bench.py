@@ -54,6 +54,8 @@ def alg_bytes(wl, active_experts=None):
         return M * K + E * N * K + 4 * (E + 1) + M * wl.top_k * N * 2
     if wl.fmt in ("int8", "fp8wo"):   # bf16 rows, one-byte weights + channel scales
         return 2 * M * K + E * N * K + 4 * E * N + M * wl.top_k * N * 2
+    if wl.fmt == "int4wo":            # bf16 rows, half-byte weights + channel scales
+        return 2 * M * K + E * N * K // 2 + 4 * E * N + M * wl.top_k * N * 2
     if wl.fmt == "int8dq":      # int8 rows + one scale per token, int8 weights + channel scales
         return M * K + 4 * M + E * N * K + 4 * E * N + M * wl.top_k * N * 2
     # MXFP8: data + e8m0 scales of both operands, bf16 output rows
@@ -158,8 +160,8 @@ def cpu_baseline(wl, case, target_s):
         wq, wsf = O.quantize_weight_mxfp8(w)
         mo = case["m_offsets"].cpu().numpy()
     else:
-        wq, ws = {"fp8": O.quantize_weight_fp8, "fp8wo": O.quantize_weight_fp8_rows}.get(
-            wl.fmt, O.quantize_weight_int8)(w)
+        wq, ws = {"fp8": O.quantize_weight_fp8, "fp8wo": O.quantize_weight_fp8_rows,
+                  "int4wo": O.quantize_weight_int4}.get(wl.fmt, O.quantize_weight_int8)(w)
         lg = case["logits"].cpu().numpy()
     del w
     reps, t0 = 0, time.perf_counter()
@@ -178,6 +180,8 @@ def cpu_baseline(wl, case, target_s):
                 y = O.grouped_gemm_int8w8a8(aq, sa, wq, ws, ids, wts)
             elif wl.fmt == "fp8wo":
                 y = O.grouped_gemm_fp8w8a16(x, wq, ws, ids, wts)
+            elif wl.fmt == "int4wo":
+                y = O.grouped_gemm_int4w16(x, wq, ws, ids, wts)
             else:
                 y = O.grouped_gemm_int8w8a16(x, wq, ws, ids, wts)
             O.combine(F.bf16_decode(O.slot_results_bf16(y)), wl.top_k)
@@ -276,12 +280,12 @@ def main():
     gemm_ms = sum(a.elapsed_time(b) for a, b in events) / args.steps
 
     active = wl.E
-    if wl.fmt in ("fp8", "int8", "int8dq", "fp8wo"):
+    if wl.fmt in ("fp8", "int8", "int8dq", "fp8wo", "int4wo"):
         ids = moe.topk_ids.cpu()
         active = int(torch.unique(ids).numel())
     nbytes = alg_bytes(wl, active)
     ms = elapsed * 1e3 / args.steps
-    dtype = {"fp8": "fp8", "int8": "bf16", "int8dq": "int8", "fp8wo": "bf16", "mxfp8": "mxfp8", "act_fp8": "fp8",
+    dtype = {"fp8": "fp8", "int8": "bf16", "int8dq": "int8", "fp8wo": "bf16", "int4wo": "bf16", "mxfp8": "mxfp8", "act_fp8": "fp8",
              "act_mxfp8": "mxfp8"}[wl.fmt]
     is_act = wl.fmt.startswith("act_")
     bound = "hbm" if is_act or wl.flops / nbytes < 600 else "mfma"

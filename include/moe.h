@@ -60,6 +60,8 @@ extern "C" {
 #define MOE_Q_INT8_PER_CHANNEL 2  /* int8 + one fp32 scale per row: per output channel
                                      (weights), per token (activations) */
 #define MOE_Q_FP8_PER_CHANNEL  3  /* e4m3 + one fp32 scale per output channel (weights only) */
+#define MOE_Q_INT4_PER_CHANNEL 4  /* int4 (two per byte) + one fp32 scale per output channel
+                                     (weights only) */
 
 /* ---- activations fused with the quantization (moe_act_quantize) -------- */
 #define MOE_ACT_SWIGLU 0  /* y = silu(g) * u, row = [g | u] (2H inputs -> H outputs) */
@@ -217,6 +219,15 @@ int moe_act_quantize(const uint16_t *x, int rows, int H, int act, int mode,
  *                         saturation to +-448; q is uint8 [E,N,K], scale
  *                         [E,N] ("Enabling MOE Quantization using linear
  *                         decomposition", Summary: fp8 weight-only).
+ * MOE_Q_INT4_PER_CHANNEL: per row s = fl32(amax_row/7) (1 if zero),
+ *                         q = clamp(round_half_even(fl32(w * fl32(1/s))), -7, 7)
+ *                         ("Enabling MOE Quantization using linear
+ *                         decomposition", Summary: int4 weight-only); q is
+ *                         uint8 [E, N, K/2] (4-byte aligned): the 8 codes of
+ *                         k = 8c .. 8c+7 of a row form the little-endian dword
+ *                         c of that row (bytes 4c .. 4c+3), code k = 8c + j
+ *                         stored as the 4-bit number q + 8 (1 .. 15) in bits
+ *                         4f .. 4f+3 with f = (j >> 1) + 4 (j & 1); scale [E,N].
  * MOE_Q_INT8_PER_CHANNEL: per row s = fl32(amax_row/127) (1 if zero),
  *                         q = clamp(round_half_even(fl32(w * fl32(1/s))),
  *                         -127, 127); q is int8 [E,N,K], scale [E,N].
@@ -332,6 +343,25 @@ int moe_grouped_gemm_fp8w8a16(const uint16_t *a, const uint8_t *w_q,
                               const int *num_tokens_post_padded,
                               const float *topk_weights, int M, int K, int N, int E,
                               int top_k, int block_m, uint16_t *y, hipStream_t stream);
+
+/* Routed int4 weight-only grouped GEMM ("Enabling MOE Quantization using
+ * linear decomposition", Summary: bf16 activations x int4 weights with one
+ * scale per output channel): as moe_grouped_gemm_int8w8a16 with
+ *     y[i, n] = bf16( (sum_k a[t,k] * q[e,n,k]) * w_scale[e, n] * topk_weights[i] )
+ * for the codes q of w_q (moe_quantize_weights with MOE_Q_INT4_PER_CHANNEL),
+ * given as that [E, N, K/2] byte matrix (MOE_W_ROWMAJOR) or as its
+ * MOE_W_FRAG packing (moe_pack_weights of the byte matrix with K/2 in place
+ * of K); w_scale [E, N] f32.  The kernel turns each code into the bf16 value
+ * 136 + q exactly, accumulates in fp32 on the bf16 MFMA and subtracts 136
+ * times the row sum of the activations (accumulated the same way) before the
+ * epilogue.  K must be a multiple of 128 and N of 8; block_m must be 16
+ * (other block_m and MOE_W_TILED give MOE_EUNSUPPORTED). */
+int moe_grouped_gemm_int4w4a16(const uint16_t *a, const uint8_t *w_q,
+                               const float *w_scale, int w_layout,
+                               const int *sorted_token_ids, const int *expert_ids,
+                               const int *num_tokens_post_padded,
+                               const float *topk_weights, int M, int K, int N, int E,
+                               int top_k, int block_m, uint16_t *y, hipStream_t stream);
 
 /* MXFP8 grouped linear over expert-contiguous rows (no router): for row r of
  * expert e (m_offsets[e] <= r < m_offsets[e+1]) and column n < N,

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmoe.so"
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP = 0, -1, -2, -3
 MOE_Q_FP8_PER_TENSOR, MOE_Q_MXFP8, MOE_Q_INT8_PER_CHANNEL, MOE_Q_FP8_PER_CHANNEL = 0, 1, 2, 3
+MOE_Q_INT4_PER_CHANNEL = 4
 MOE_W_ROWMAJOR, MOE_W_TILED, MOE_W_FRAG = 0, 1, 2
 MOE_ACT_SWIGLU, MOE_ACT_SRELU = 0, 1
 MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_SLOTS = 128, 8, 65536
@@ -30,7 +31,7 @@ EXPORTS = [
     "moe_align_block_size", "moe_quantize_act", "moe_act_quantize", "moe_quantize_weights",
     "moe_pack_weights",
     "moe_grouped_gemm_fp8w8a8",
-    "moe_grouped_gemm_int8w8a8", "moe_grouped_gemm_fp8w8a16",
+    "moe_grouped_gemm_int8w8a8", "moe_grouped_gemm_fp8w8a16", "moe_grouped_gemm_int4w4a16",
     "moe_grouped_gemm_int8w8a16", "moe_grouped_gemm_mxfp8", "moe_combine",
 ]
 
@@ -66,6 +67,7 @@ _SIGS = {
     "moe_grouped_gemm_int8w8a8": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
     "moe_grouped_gemm_int8w8a16": (_I, [_P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
     "moe_grouped_gemm_fp8w8a16": (_I, [_P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
+    "moe_grouped_gemm_int4w4a16": (_I, [_P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
     "moe_grouped_gemm_mxfp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "moe_combine": (_I, [_P, _I, _I, _I, _P, _P]),
 }
@@ -199,6 +201,15 @@ def moe_grouped_gemm_fp8w8a16(a, w_q, w_scale, w_layout, sorted_token_ids, exper
                               num_tokens_post_padded, topk_weights, M, K, N, E, top_k, block_m,
                               y, stream=None):
     return _check(lib().moe_grouped_gemm_fp8w8a16(
+        _ptr(a), _ptr(w_q), _ptr(w_scale), w_layout, _ptr(sorted_token_ids), _ptr(expert_ids),
+        _ptr(num_tokens_post_padded), _ptr(topk_weights), M, K, N, E, top_k, block_m, _ptr(y),
+        _stream(stream)))
+
+
+def moe_grouped_gemm_int4w4a16(a, w_q, w_scale, w_layout, sorted_token_ids, expert_ids,
+                               num_tokens_post_padded, topk_weights, M, K, N, E, top_k, block_m,
+                               y, stream=None):
+    return _check(lib().moe_grouped_gemm_int4w4a16(
         _ptr(a), _ptr(w_q), _ptr(w_scale), w_layout, _ptr(sorted_token_ids), _ptr(expert_ids),
         _ptr(num_tokens_post_padded), _ptr(topk_weights), M, K, N, E, top_k, block_m, _ptr(y),
         _stream(stream)))

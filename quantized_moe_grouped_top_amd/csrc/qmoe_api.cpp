@@ -258,6 +258,14 @@ int moe_quantize_weights(const float *w, int E, int N, int K, int mode, void *q,
                                                          (float *)workspace, stream),
                       fn);
   }
+  if (mode == MOE_Q_INT4_PER_CHANNEL) {
+    REQUIRE(scale, MOE_EINVAL, "%s: null scale", fn);
+    REQUIRE(((uintptr_t)q & 3u) == 0, MOE_EINVAL, "%s: q must be 4-byte aligned", fn);
+    REQUIRE(K % 8 == 0, MOE_EUNSUPPORTED, "%s: K=%d is not a multiple of 8", fn, K);
+    return hip_status(qmoe::launch_quant_int4_rows_f32(w, (long long)E * N, K, (uint8_t *)q, scale,
+                                                       stream),
+                      fn);
+  }
   if (mode == MOE_Q_FP8_PER_CHANNEL) {
     REQUIRE(scale, MOE_EINVAL, "%s: null scale", fn);
     REQUIRE(K % 8 == 0, MOE_EUNSUPPORTED, "%s: K=%d is not a multiple of 8", fn, K);
@@ -316,6 +324,26 @@ int moe_grouped_gemm_fp8w8a16(const uint16_t *a, const uint8_t *w_q, const float
                      E, top_k, block_m, (int)(max_padded_ll(M, E, top_k, block_m) / block_m),
                      w_layout, y};
   return hip_status(qmoe::launch_gemm_fp8w8a16(a, w_q, w_scale, r, stream), fn);
+}
+
+int moe_grouped_gemm_int4w4a16(const uint16_t *a, const uint8_t *w_q, const float *w_scale,
+                               int w_layout, const int *sorted_token_ids, const int *expert_ids,
+                               const int *num_tokens_post_padded, const float *topk_weights,
+                               int M, int K, int N, int E, int top_k, int block_m, uint16_t *y,
+                               hipStream_t stream) {
+  const char *fn = "moe_grouped_gemm_int4w4a16";
+  int rc = check_routed_gemm(a, w_q, w_scale, w_layout, sorted_token_ids, expert_ids,
+                             num_tokens_post_padded, topk_weights, y, M, K, N, E, top_k, block_m,
+                             128, fn);
+  if (rc) return rc;
+  REQUIRE(block_m == 16, MOE_EUNSUPPORTED, "%s: block_m=%d (int4 weights: 16 only)", fn, block_m);
+  REQUIRE(w_layout != MOE_W_TILED, MOE_EUNSUPPORTED, "%s: MOE_W_TILED is not offered for int4",
+          fn);
+  if (M == 0) return ok();
+  qmoe::RoutedArgs r{sorted_token_ids, expert_ids, num_tokens_post_padded, topk_weights, M, K, N,
+                     E, top_k, block_m, (int)(max_padded_ll(M, E, top_k, block_m) / block_m),
+                     w_layout, y};
+  return hip_status(qmoe::launch_gemm_int4w16(a, w_q, w_scale, r, stream), fn);
 }
 
 int moe_grouped_gemm_int8w8a8(const int8_t *a_q, const float *a_scale, const int8_t *w_q,

@@ -224,7 +224,21 @@ __device__ __forceinline__ int sw256(int r, int c) { return r * 256 + ((c ^ (r &
 // stream kernel modes: fp8 W8A8, int8 W8A16 (bf16 activations), int8 W8A8
 // (int8 activations with one scale per token), fp8 weight-only (bf16
 // activations, e4m3 weights with one scale per channel)
-enum { kSFp8 = 0, kSW8A16 = 1, kSI8 = 2, kSF8W16 = 3 };
+enum { kSFp8 = 0, kSW8A16 = 1, kSI8 = 2, kSF8W16 = 3, kSW4A16 = 4 };
+
+// int4 weights (two per byte, stored as q + 8 in 4-bit fields; each group of
+// 8 consecutive k forms one little-endian dword with value j in field
+// (j >> 1) + 4 (j & 1)): one dword -> the 8 bf16 values 136 + q of an MFMA
+// operand.  OR-ing a field into the bf16 pattern of 128 gives 128 + (q + 8)
+// exactly (the significand holds 7 bits), two values per instruction pair;
+// the constant 136 times the row sum of the activations is taken off after
+// the contraction.
+__device__ __forceinline__ i32x4 int4x8_to_bf16x8(uint32_t d) {
+  constexpr uint32_t kMask = 0x000F000Fu, kBase = 0x43004300u;   // bf16 128.0 in both halves
+  return i32x4{(int)((d & kMask) | kBase), (int)(((d >> 4) & kMask) | kBase),
+               (int)(((d >> 8) & kMask) | kBase), (int)(((d >> 12) & kMask) | kBase)};
+}
+constexpr float kInt4Offset = 136.0f;
 
 template <int kMode, int kLayout>
 __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
@@ -234,15 +248,18 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
     const int *__restrict__ num_post, const float *__restrict__ topk_w, int M, int K, int N,
     int top_k, int groups, int tiles_per_group, int max_blocks, uint16_t *__restrict__ y,
     uint32_t w_bytes) {
-  constexpr bool kInt8 = kMode == kSW8A16 || kMode == kSF8W16;   // bf16 activations
+  constexpr bool kInt8 = kMode == kSW8A16 || kMode == kSF8W16 || kMode == kSW4A16;   // bf16 acts
   constexpr bool kI8 = kMode == kSI8;                    // int8 activations and weights
+  constexpr bool kW4 = kMode == kSW4A16;                 // int4 weights: 64 bytes per row per stage
+  constexpr int kP = kW4 ? 1 : 2;                        // 16-byte weight pieces per group and stage
   using C = SCfg<kInt8>;
-  constexpr int kSD = C::kD, kSAS = C::kAS;
+  constexpr int kSD = kW4 ? 3 : C::kD, kSAS = kSD + 1;
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kSAS * C::kABytes];
   __shared__ int s_slot[kSMB * 16];
   __shared__ int s_nvalid;
   __shared__ float s_scale[kSMaxTiles * 64];
   __shared__ float s_rw[kSMB * 16];
+  __shared__ float s_A[kSMB * 16];                       // int4: activation row sums
 
   const int e = blockIdx.x / groups;
   const int grp = blockIdx.x - e * groups;
@@ -274,7 +291,11 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
   // in a scalar register, checked against the size of the weight tensor (a
   // piece past its end reads as zero; pieces past the last k of a row are
   // never used).
-  const int KB = (K + 63) / 64;                             // MOE_W_FRAG: 64-k blocks per row group
+  // int4 weights are a byte matrix [E, N, K/2] (MOE_W_ROWMAJOR) or its
+  // MOE_W_FRAG packing; one stage (128 k) is 64 bytes of a row, one 16-byte
+  // piece per lane (k 32g .. 32g + 31).
+  const int row_bytes = kW4 ? K / 2 : K;
+  const int KB = (row_bytes + 63) / 64;                     // MOE_W_FRAG: 64-byte blocks per row group
   const int N16 = (N + 15) / 16;
   const __amdgpu_buffer_rsrc_t wrsrc =
       __builtin_amdgcn_make_buffer_rsrc((void *)w, (short)0, (int)w_bytes, 0x00020000);
@@ -285,7 +306,8 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
     const int tile = t_begin + (jg >> 2);
     const int n = tile * 64 + 16 * (jg & 3) + r16;          // may be >= N in the last tile
     if constexpr (kLayout == MOE_W_ROWMAJOR) {
-      const uint32_t row = ((uint32_t)e * (uint32_t)N + (uint32_t)min(n, N - 1)) * (uint32_t)K;
+      const uint32_t row =
+          ((uint32_t)e * (uint32_t)N + (uint32_t)min(n, N - 1)) * (uint32_t)row_bytes;
       voff[u][0] = row + 16u * (uint32_t)g;
       voff[u][1] = row + 64u + 16u * (uint32_t)g;
     } else if constexpr (kLayout == MOE_W_TILED) {
@@ -302,20 +324,20 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
   }
   // byte offset of stage st, the same for every lane
   auto st_off = [&](int st) -> int {
-    if constexpr (kLayout == MOE_W_ROWMAJOR) return kSK * st;
+    if constexpr (kLayout == MOE_W_ROWMAJOR) return (kW4 ? kSK / 2 : kSK) * st;
     else if constexpr (kLayout == MOE_W_TILED) return 8192 * st;
-    else return 2048 * st;
+    else return (kW4 ? 1024 : 2048) * st;
   };
-  i32x4 wb[kSD][kSGroups][2];
-  auto load_w = [&](int st, i32x4 (&buf)[kSGroups][2]) {
+  i32x4 wb[kSD][kSGroups][kP];
+  auto load_w = [&](int st, i32x4 (&buf)[kSGroups][kP]) {
     const int so = st_off(st);
 #pragma unroll
     for (int u = 0; u < kSGroups; ++u)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < kP; ++h)
         buf[u][h] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, voff[u][h], so, 0);
   };
-  constexpr int kLw = 2 * kSGroups;                         // weight loads per stage
+  constexpr int kLw = kP * kSGroups;                        // weight loads per stage
 
   // Routing first.  With few blocks (decode) the block labels and the sorted
   // slot ids are copied into LDS by dword DMA ahead of the stage-0 weights:
@@ -492,8 +514,36 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
 #pragma unroll
       for (int i = 0; i < kSMB; ++i) acc[u][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int st, int ring, const i32x4 (&buf)[kSGroups][2]) {
+    f32x4 accA = f32x4{0.f, 0.f, 0.f, 0.f};               // int4: row sums of block `wave`
+    auto compute = [&](int st, int ring, const i32x4 (&buf)[kSGroups][kP]) {
       const uint8_t *sa = s_ring + ring * C::kABytes;
+      if constexpr (kW4) {
+        // four MFMA sub-steps of 32 k: lane group g takes k 32g + 8m .. + 7
+        // (activation chunk 4g + m, weight dword m); wavefront i < nmb also
+        // sums the rows of block i (an MFMA against ones)
+        const i32x4 ones = {0x3F803F80, 0x3F803F80, 0x3F803F80, 0x3F803F80};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          i32x4 av[kSMB];
+#pragma unroll
+          for (int i = 0; i < kSMB; ++i) {
+            if (i >= nmb) break;
+            av[i] = *reinterpret_cast<const i32x4 *>(sa + sw256(16 * i + r16, 4 * g + m));
+            if (i == wave) accA = mfma_bf16(av[i], ones, accA);
+          }
+#pragma unroll
+          for (int u = 0; u < kSGroups; ++u) {
+            if (wave + kSWaves * u >= ngr) break;          // wave-uniform
+            const i32x4 b = int4x8_to_bf16x8((uint32_t)buf[u][0][m]);
+#pragma unroll
+            for (int i = 0; i < kSMB; ++i) {
+              if (i >= nmb) break;
+              acc[u][i] = mfma_bf16(av[i], b, acc[u][i]);
+            }
+          }
+        }
+        return;
+      }
       const int nsub = (st == nst - 1) ? nsub_last : kSK / C::kSub;
 #pragma unroll
       for (int ss = 0; ss < kSK / C::kSub; ++ss) {
@@ -557,7 +607,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
 
     // one stage: wait for it, free the previous slot, start stage st + kSD
     // (its activations now, its weights once `buf` has been read)
-    auto step = [&](int st, i32x4 (&buf)[kSGroups][2]) {
+    auto step = [&](int st, i32x4 (&buf)[kSGroups][kP]) {
       // loads issued after this wave's loads of stage st (weights, then
       // activations in the prologue; activations, then weights after it)
       const int younger = st < kSD ? (kSD - 1 - st) * n_a + st * (n_a + kLw)
@@ -588,6 +638,12 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
     // slot's row
     if (pass_ == 0 && tid < G * 64) s_scale[tid] = cs_pre;   // per-column (or fused) scale
     if (tid < kSMB * 16) s_rw[tid] = rw_pre;
+    if constexpr (kW4) {
+      if (wave < nmb && r16 == 0) {                        // every column holds the row sum
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) s_A[16 * wave + 4 * g + rr] = accA[rr];
+      }
+    }
     __syncthreads();
     uint16_t *stg = reinterpret_cast<uint16_t *>(s_ring);
     const int wcols = 64 * G;                              // columns of this workgroup
@@ -606,6 +662,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
           const int k = 4 * g + rr;                        // row within the block
           float acc_v = acc[u][i][rr];
           if constexpr (kI8) acc_v = (float)__builtin_bit_cast(int, acc_v);
+          if constexpr (kW4) acc_v = fmaf(-kInt4Offset, s_A[16 * i + k], acc_v);
           const float v = acc_v * cs * s_rw[16 * i + k];   // x router weight (x token scale)
           stg[k * wcols + cl] = (uint16_t)f32x2_to_bf16x2(v, 0.0f);
         }
@@ -1893,6 +1950,25 @@ hipError_t launch_gemm_int8(const uint16_t *a, const int8_t *w_q, const float *w
                        w_scale, nullptr, r.sorted_ids, r.expert_ids, r.topk_w, nullptr, r.M, r.K,
                        r.N, r.E, r.top_k, r.max_blocks, r.y);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_int4w16(const uint16_t *a, const uint8_t *w_q, const float *w_scale,
+                               const RoutedArgs &r, hipStream_t s) {
+  // block_m 16 only (checked by the caller); w_q is the [E, N, K/2] byte matrix
+  // or its MOE_W_FRAG packing
+  int groups, tpg;
+  stream_grid(r.N, r.E, groups, tpg);
+  const uint32_t half = (uint32_t)(r.K / 2);
+  const uint32_t w_bytes = r.w_layout == MOE_W_FRAG
+                               ? (uint32_t)r.E * (uint32_t)((r.N + 15) / 16) * ((half + 63u) / 64u) * 1024u
+                               : (uint32_t)r.E * (uint32_t)r.N * half;
+  auto k = r.w_layout == MOE_W_FRAG ? stream_kernel<kSW4A16, MOE_W_FRAG>
+                                    : stream_kernel<kSW4A16, MOE_W_ROWMAJOR>;
+  hipLaunchKernelGGL(k, dim3(r.E * groups), dim3(kSThreads), 0, s,
+                     reinterpret_cast<const uint8_t *>(a), nullptr, w_q, w_scale, r.sorted_ids,
+                     r.expert_ids, r.num_post, r.topk_w, r.M, r.K, r.N, r.top_k, groups, tpg,
+                     r.max_blocks, r.y, w_bytes);
   return hipGetLastError();
 }
 

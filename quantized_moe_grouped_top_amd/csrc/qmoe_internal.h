@@ -65,6 +65,8 @@ hipError_t launch_quant_fp8_experts_f32(const float *w, int E, long long per_exp
                                         uint8_t *q, float *scale, float *ws, hipStream_t s);
 hipError_t launch_quant_int8_rows_f32(const float *w, long long rows, int K, int8_t *q,
                                       float *scale, hipStream_t s);
+hipError_t launch_quant_int4_rows_f32(const float *w, long long rows, int K, uint8_t *q,
+                                      float *scale, hipStream_t s);
 hipError_t launch_quant_fp8_rows_f32(const float *w, long long rows, int K, uint8_t *q,
                                      float *scale, hipStream_t s);
 hipError_t launch_quant_int8_rows_bf16(const uint16_t *x, long long rows, int K, int8_t *q,
@@ -91,6 +93,8 @@ hipError_t launch_gemm_fp8(const uint8_t *a_q, const float *a_scale, const uint8
                            const float *w_scale, const RoutedArgs &r, hipStream_t s);
 hipError_t launch_gemm_int8(const uint16_t *a, const int8_t *w_q, const float *w_scale,
                             const RoutedArgs &r, hipStream_t s);
+hipError_t launch_gemm_int4w16(const uint16_t *a, const uint8_t *w_q, const float *w_scale,
+                               const RoutedArgs &r, hipStream_t s);
 hipError_t launch_gemm_fp8w8a16(const uint16_t *a, const uint8_t *w_q, const float *w_scale,
                                 const RoutedArgs &r, hipStream_t s);
 hipError_t launch_gemm_int8w8a8(const int8_t *a_q, const float *a_scale, const int8_t *w_q,

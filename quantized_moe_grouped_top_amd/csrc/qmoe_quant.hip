@@ -196,6 +196,45 @@ __global__ __launch_bounds__(kThreads) void quant_int8_rows_kernel(const Src *__
   }
 }
 
+// ---- int4 per output channel (int4 weight-only): one wavefront per row -----
+// Codes q = clamp(rne(w * fl32(1/s)), -7, 7) with s = fl32(amax/7), stored as
+// q + 8 in 4-bit fields: the 8 codes of k = 8c .. 8c+7 form dword c of the
+// row, value j in field (j >> 1) + 4 (j & 1).
+__global__ __launch_bounds__(kThreads) void quant_int4_rows_kernel(const float *__restrict__ w,
+                                                                   long long rows, int K,
+                                                                   uint8_t *__restrict__ q,
+                                                                   float *__restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float *src = w + row * K;
+  float m = 0.0f;
+  for (int k = lane * 8; k < K; k += 64 * 8) {
+    float v[8];
+    load8(src + k, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+  }
+  const float amax = wave_max(m);
+  const float s = amax > 0.0f ? (float)((double)amax / 7.0) : 1.0f;
+  const float inv = (float)(1.0 / (double)s);
+  if (lane == 0) scale[row] = s;
+  uint32_t *dst = reinterpret_cast<uint32_t *>(q + row * (K / 2));
+  for (int k = lane * 8; k < K; k += 64 * 8) {
+    float v[8];
+    load8(src + k, v);
+    uint32_t word = 0u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float r = __builtin_rintf(v[j] * inv);              // round half to even
+      r = __builtin_amdgcn_fmed3f(r, -7.0f, 7.0f);
+      const uint32_t field = (uint32_t)((j >> 1) + 4 * (j & 1));
+      word |= ((uint32_t)((int)r + 8) & 0xFu) << (4u * field);
+    }
+    dst[k / 8] = word;
+  }
+}
+
 // ---- fp8 per output channel (fp8 weight-only): one wavefront per row -------
 __global__ __launch_bounds__(kThreads) void quant_fp8_rows_kernel(const float *__restrict__ w,
                                                                   long long rows, int K,
@@ -674,6 +713,14 @@ hipError_t launch_quant_int8_rows_f32(const float *w, long long rows, int K, int
   const long long blocks = (rows + kThreads / 64 - 1) / (kThreads / 64);
   hipLaunchKernelGGL(quant_int8_rows_kernel<float>, dim3((unsigned)blocks), dim3(kThreads), 0, s,
                      w, rows, K, q, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_int4_rows_f32(const float *w, long long rows, int K, uint8_t *q,
+                                      float *scale, hipStream_t s) {
+  const long long blocks = (rows + kThreads / 64 - 1) / (kThreads / 64);
+  hipLaunchKernelGGL(quant_int4_rows_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, w, rows,
+                     K, q, scale);
   return hipGetLastError();
 }
 

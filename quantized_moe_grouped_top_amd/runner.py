@@ -5,7 +5,7 @@ memory only) and runs the hot path as a sequence of library calls on the
 current stream:
 
     routed formats : moe_align_block_size -> [moe_quantize_act] ->
-                     moe_grouped_gemm_{fp8w8a8,int8w8a8,int8w8a16,fp8w8a16} ->
+                     moe_grouped_gemm_{fp8w8a8,int8w8a8,int8w8a16,fp8w8a16,int4w4a16} ->
                      moe_combine
     MXFP8          : moe_quantize_act(MXFP8) -> moe_grouped_gemm_mxfp8
     activation     : moe_act_quantize (SwiGLU / SReLU + MXFP8 or fp8)
@@ -16,9 +16,11 @@ Every step runs in the library's HIP kernels; nothing here computes.
 import torch
 
 from . import (MOE_ACT_SRELU, MOE_ACT_SWIGLU, MOE_Q_FP8_PER_CHANNEL, MOE_Q_FP8_PER_TENSOR,
-               MOE_Q_INT8_PER_CHANNEL, MOE_Q_MXFP8, MOE_W_ROWMAJOR,
+               MOE_Q_INT4_PER_CHANNEL, MOE_Q_INT8_PER_CHANNEL, MOE_Q_MXFP8, MOE_W_FRAG,
+               MOE_W_ROWMAJOR,
                MOE_W_TILED, moe_act_quantize, moe_align_block_size, moe_align_max_padded, moe_combine,
-               moe_grouped_gemm_fp8w8a8, moe_grouped_gemm_fp8w8a16, moe_grouped_gemm_int8w8a8,
+               moe_grouped_gemm_fp8w8a8, moe_grouped_gemm_fp8w8a16, moe_grouped_gemm_int4w4a16,
+               moe_grouped_gemm_int8w8a8,
                moe_grouped_gemm_int8w8a16,
                moe_grouped_gemm_mxfp8,
                moe_mx_scale_rows, moe_pack_weights, moe_packed_weight_bytes, moe_quantize_act,
@@ -39,6 +41,11 @@ def quantize_weights(w, fmt):
         s = _empty((E,), torch.float32, dev)
         ws = _empty((moe_quantize_workspace_bytes(MOE_Q_FP8_PER_TENSOR, E),), torch.uint8, dev)
         moe_quantize_weights(w, E, N, K, MOE_Q_FP8_PER_TENSOR, q, s, None, ws)
+        return q, s
+    if fmt == "int4wo":                  # packed codes [E, N, K/2]
+        q = _empty((E, N, K // 2), torch.uint8, dev)
+        s = _empty((E, N), torch.float32, dev)
+        moe_quantize_weights(w, E, N, K, MOE_Q_INT4_PER_CHANNEL, q, s, None, None)
         return q, s
     if fmt == "fp8wo":
         q = _empty((E, N, K), torch.uint8, dev)
@@ -69,12 +76,12 @@ def pack_weights(w_q, layout=MOE_W_TILED):
 
 class RoutedMoE:
     """fp8 W8A8, int8 W8A16 ("int8"), int8 W8A8 with per-token activation
-    scales ("int8dq") or bf16 x fp8 weight-only ("fp8wo") MoE layer of fixed
-    (M, K, N, E, top_k)."""
+    scales ("int8dq"), bf16 x fp8 weight-only ("fp8wo") or bf16 x int4
+    weight-only ("int4wo", block_m 16) MoE layer of fixed (M, K, N, E, top_k)."""
 
     def __init__(self, fmt, M, K, N, E, top_k, device="cuda", block_m=None,
                  w_layout=MOE_W_ROWMAJOR):
-        assert fmt in ("fp8", "int8", "int8dq", "fp8wo")
+        assert fmt in ("fp8", "int8", "int8dq", "fp8wo", "int4wo")
         self.w_layout = w_layout
         self.fmt, self.M, self.K, self.N, self.E, self.top_k = fmt, M, K, N, E, top_k
         self.block_m = block_m or moe_recommended_block_m(M, E, top_k)
@@ -122,6 +129,11 @@ class RoutedMoE:
                                       self.sorted_token_ids, self.expert_ids,
                                       self.num_tokens_post_padded, self.topk_weights, self.M,
                                       self.K, self.N, self.E, self.top_k, self.block_m, self.y)
+        elif self.fmt == "int4wo":
+            moe_grouped_gemm_int4w4a16(x, w_q, w_scale, self.w_layout, self.sorted_token_ids,
+                                       self.expert_ids, self.num_tokens_post_padded,
+                                       self.topk_weights, self.M, self.K, self.N, self.E,
+                                       self.top_k, self.block_m, self.y)
         elif self.fmt == "fp8wo":
             moe_grouped_gemm_fp8w8a16(x, w_q, w_scale, self.w_layout, self.sorted_token_ids,
                                       self.expert_ids, self.num_tokens_post_padded,

@@ -30,6 +30,7 @@ class Workload:
     name: str
     fmt: str               # "fp8", "int8" (W8A16), "int8dq" (W8A8, per-token activation
                            # scales), "fp8wo" (bf16 x fp8 per-channel weights),
+                           # "int4wo" (bf16 x int4 per-channel weights),
                            # "mxfp8"; "act_mxfp8", "act_fp8" (K = input
                            # width 2H or H, N = H)
     M: int                 # tokens (MXFP8: total rows)
@@ -77,6 +78,8 @@ WORKLOADS = {w.name: w for w in [
     # bf16 activations x fp8 weights with per-channel scales, same shapes
     Workload("fp8wo_m64_k4096_n14336", "fp8wo", 64, 4096, 14336),
     Workload("fp8wo_bias_m4096_k4096_n14336", "fp8wo", 4096, 4096, 14336, bias_std=0.5),
+    # bf16 activations x int4 weights with per-channel scales, decode shape
+    Workload("int4wo_m64_k4096_n14336", "int4wo", 64, 4096, 14336),
     _mx("mxfp8_8x4000_k4096_n4096", 4000, 8, 4096, 4096),
     _mx("mxfp8_22b_8x4000_k6144_n32768", 4000, 8, 6144, 32768),
     # the (8*4000, 4096) activation input: SwiGLU halves it to H = 2048

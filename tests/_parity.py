@@ -88,5 +88,21 @@ def oracle_weights_rows(w_dev, fmt, cols):
         return O.quantize_weight_int8(rows)
     if fmt == "fp8wo":
         return O.quantize_weight_fp8_rows(rows)
+    if fmt == "int4wo":
+        return O.quantize_weight_int4(rows)
     q, b = O.quantize_weight_mxfp8(rows)
     return q, b
+
+
+def unpack_int4(packed):
+    """Codes of MOE_Q_INT4_PER_CHANNEL bytes [..., K/2] -> int8 [..., K], as
+    the layout is defined: the 8 codes of k = 8c .. 8c+7 form little-endian
+    dword c, code 8c + j stored as q + 8 in bits 4f .. 4f+3, f = (j >> 1) +
+    4 (j & 1)."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    words = packed.view("<u4").astype(np.int64)                     # [..., K/8]
+    out = np.empty(words.shape + (8,), np.int8)
+    for j in range(8):
+        f = (j >> 1) + 4 * (j & 1)
+        out[..., j] = ((words >> (4 * f)) & 0xF) - 8
+    return out.reshape(packed.shape[:-1] + (packed.shape[-1] * 2,))

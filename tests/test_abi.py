@@ -38,7 +38,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     h = ctypes.CDLL(qm.LIB_PATH)
     for n in names:
         assert hasattr(h, n), n
@@ -171,6 +171,40 @@ def test_gemm_fp8w8a16_and_fp8_channel_quantizer_reject():
     assert ei.value.code == qm.MOE_EINVAL                       # no scale
     with pytest.raises(qm.MoeError) as ei:
         qm.moe_quantize_act(FAKE, 10, 64, qm.MOE_Q_FP8_PER_CHANNEL, None, 1, FAKE, FAKE, None,
+                            None, stream=0)
+    assert ei.value.code == qm.MOE_EINVAL                       # weights only
+
+
+def test_gemm_int4_and_int4_quantizer_reject():
+    args = [FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, 64, 192, 128, 8, 2, 16, FAKE]
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_grouped_gemm_int4w4a16(*args, stream=0)
+    assert ei.value.code == qm.MOE_EUNSUPPORTED                 # K % 128
+    args[9] = 256
+    args[13] = 128
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_grouped_gemm_int4w4a16(*args, stream=0)
+    assert ei.value.code == qm.MOE_EUNSUPPORTED                 # block_m 16 only
+    args[13], args[3] = 16, qm.MOE_W_TILED
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_grouped_gemm_int4w4a16(*args, stream=0)
+    assert ei.value.code == qm.MOE_EUNSUPPORTED                 # no tiled int4 layout
+    args[3], args[1] = qm.MOE_W_FRAG, 0
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_grouped_gemm_int4w4a16(*args, stream=0)
+    assert ei.value.code == qm.MOE_EINVAL                       # null weights
+    args[1], args[8] = FAKE, 0
+    qm.moe_grouped_gemm_int4w4a16(*args, stream=0)              # M = 0: nothing to do
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_quantize_weights(FAKE, 2, 4, 60, qm.MOE_Q_INT4_PER_CHANNEL, FAKE, FAKE, None, None,
+                                stream=0)
+    assert ei.value.code == qm.MOE_EUNSUPPORTED                 # K % 8
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_quantize_weights(FAKE, 2, 4, 64, qm.MOE_Q_INT4_PER_CHANNEL, FAKE + 2, FAKE, None,
+                                None, stream=0)
+    assert ei.value.code == qm.MOE_EINVAL                       # misaligned codes
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_quantize_act(FAKE, 10, 64, qm.MOE_Q_INT4_PER_CHANNEL, None, 1, FAKE, FAKE, None,
                             None, stream=0)
     assert ei.value.code == qm.MOE_EINVAL                       # weights only
 

@@ -25,7 +25,8 @@ from quantized_moe_grouped_top_amd import runner, synth
 from oracle import formats as F
 from oracle import moe as O
 
-from _parity import (assert_bf16_out, assert_close_rms, bits16, oracle_weights_rows, pick)
+from _parity import (assert_bf16_out, assert_close_rms, bits16, oracle_weights_rows, pick,
+                     unpack_int4)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -80,6 +81,8 @@ def run_routed(wl, block_m=None, variant=0, full=True, n_tok=48, n_col=64, logit
     # ---- weights: bit-exact quantization of the checked rows ----------------
     wq_rows, ws_ref = oracle_weights_rows(w, wl.fmt, cols)
     wq_dev = w_q.index_select(1, torch.as_tensor(cols, device=DEV)).cpu().numpy()
+    if wl.fmt == "int4wo":
+        wq_dev = unpack_int4(wq_dev)
     np.testing.assert_array_equal(wq_dev, wq_rows)
     if wl.fmt == "fp8":
         np.testing.assert_array_equal(w_scale.cpu().numpy(), ws_ref)
@@ -116,6 +119,8 @@ def run_routed(wl, block_m=None, variant=0, full=True, n_tok=48, n_col=64, logit
         y_ref = O.grouped_gemm_int8w8a8(aq_full, sa_full, wq_full, ws_full, ids_ref, wts_ref, slots, cols)
     elif wl.fmt == "fp8wo":
         y_ref = O.grouped_gemm_fp8w8a16(x_np, wq_full, ws_full, ids_ref, wts_ref, slots, cols)
+    elif wl.fmt == "int4wo":
+        y_ref = O.grouped_gemm_int4w16(x_np, wq_full, ws_full, ids_ref, wts_ref, slots, cols)
     else:
         y_ref = O.grouped_gemm_int8w8a16(x_np, wq_full, ws_full, ids_ref, wts_ref, slots, cols)
     # the per-slot results are stored as bf16: the float32 tolerance plus half
@@ -174,6 +179,21 @@ def test_routed_small(wl, block_m, layout):
     run_routed(wl, block_m=block_m, full=True, layout=layout)
 
 
+# int4 weight-only: the streaming kernel only (block_m 16), plain or packed
+INT4_SMALL = [
+    synth.small("int4wo", 50, 384, 136, 6, 3),
+    synth.small("int4wo", 300, 256, 272, 8, 2, bias_std=1.5),   # several passes per expert
+    synth.small("int4wo", 40, 128, 48, 1, 1),
+    synth.small("int4wo", 1, 128, 64, 8, 2),
+]
+
+
+@pytest.mark.parametrize("layout", [qm.MOE_W_ROWMAJOR, qm.MOE_W_FRAG], ids=["rowmajor", "frag"])
+@pytest.mark.parametrize("wl", INT4_SMALL, ids=[w.name for w in INT4_SMALL])
+def test_routed_int4(wl, layout):
+    run_routed(wl, block_m=16, full=True, layout=layout)
+
+
 @pytest.mark.parametrize("block_m,layout", KERNEL_LAYOUTS, ids=KL_IDS)
 @pytest.mark.parametrize("fmt", ["fp8", "int8"])
 def test_routed_all_tokens_one_expert(fmt, block_m, layout):
@@ -221,7 +241,7 @@ def test_routed_deterministic():
 FULL = [synth.WORKLOADS[n] for n in [
     "int8dq_m64_k4096_n14336", "int8dq_bias_m4096_k4096_n14336",
     "int8w8a16_m64_k4096_n14336",
-    "fp8wo_m64_k4096_n14336", "fp8wo_bias_m4096_k4096_n14336",
+    "fp8wo_m64_k4096_n14336", "fp8wo_bias_m4096_k4096_n14336", "int4wo_m64_k4096_n14336",
     "fp8_bias_m128_k4096_n14336", "fp8_bias_m512_k4096_n14336",
     "fp8_bias_m1024_k4096_n14336", "fp8_bias_m4096_k4096_n14336",
     "mistral7b_up_fp8_m4096_k4096_n28672", "mistral7b_down_fp8_m4096_k14336_n4096",
@@ -238,7 +258,8 @@ def test_routed_full_size_sampled(wl):
 
 ROWMAJOR_FULL = [synth.WORKLOADS[n] for n in [
     "int8dq_m64_k4096_n14336", "int8dq_bias_m4096_k4096_n14336", "int8w8a16_m64_k4096_n14336",
-    "fp8wo_m64_k4096_n14336", "fp8_bias_m128_k4096_n14336", "fp8_bias_m4096_k4096_n14336",
+    "fp8wo_m64_k4096_n14336", "int4wo_m64_k4096_n14336", "fp8_bias_m128_k4096_n14336",
+    "fp8_bias_m4096_k4096_n14336",
     "mistral7b_down_int8_m4096_k14336_n4096",
 ]]
 

@@ -325,6 +325,101 @@ def quantize_weight_mxfp8(w):
     return q.reshape(E, N, K), b.reshape(E, N, K // MX_BLOCK)
 
 
+def mx_colwise_offsets(m_offsets):
+    """Start row of each expert's block in the columnwise layout: the expert's
+    rows padded to a multiple of 128 (the padding of the rowwise scales, which
+    also gives the [4, 128] columnwise scale shape of a [64, 128] expert in
+    "[PyTorch] Let GroupedLinear accept MXFP8 input and gradient").  Returns
+    int64 [E+1]; the padded totals are the same as ``mx_padded_offsets``."""
+    return mx_padded_offsets(m_offsets)
+
+
+def quantize_mxfp8_colwise(values, m_offsets):
+    """Columnwise MXFP8 of expert-concatenated rows (the scaling factors along
+    the rows that the gradient GEMMs contract over, "[PyTorch] Let
+    GroupedLinear accept MXFP8 input and gradient": colwise scales, one per 32
+    rows of a column).
+
+    values float32-convertible [R, C]; for expert e (rows m_offsets[e] ..
+    m_offsets[e+1]-1) the rows are padded with zeros to Rp_e = roundup(m_e,
+    128) and every column is cut into blocks of 32 consecutive rows of the
+    expert, each with one e8m0 scale by the rule of ``quantize_mxfp8_rows``.
+    The result is stored transposed, expert by expert: expert e's codes are a
+    [C, Rp_e] block (element (c, j) is the code of row m_offsets[e] + j,
+    column c) and its scales a [C, Rp_e / 32] block.  Returns the flat
+    concatenations (qT uint8 [C * sum Rp_e], sfT uint8 [C * sum Rp_e / 32])."""
+    v = _f32(values)
+    mo = np.asarray(m_offsets, dtype=np.int64)
+    po = mx_colwise_offsets(mo)
+    C = v.shape[1]
+    qs, bs = [], []
+    for e in range(len(mo) - 1):
+        rp = int(po[e + 1] - po[e])
+        seg = np.zeros((rp, C), np.float32)
+        seg[: mo[e + 1] - mo[e]] = v[mo[e]:mo[e + 1]]
+        q, b = quantize_mxfp8_rows(seg.T)                 # blocks along the rows
+        qs.append(q.reshape(-1))
+        bs.append(b.reshape(-1))
+    if not qs:
+        return np.zeros(0, np.uint8), np.zeros(0, np.uint8)
+    return np.concatenate(qs), np.concatenate(bs)
+
+
+def quantize_act_mxfp8_colwise(x_bf16, m_offsets):
+    """Columnwise MXFP8 of bf16 rows (activations or output gradients), see
+    ``quantize_mxfp8_colwise``."""
+    return quantize_mxfp8_colwise(bf16_decode(x_bf16).astype(np.float32), m_offsets)
+
+
+def quantize_weight_mxfp8_colwise(w):
+    """MXFP8 weights quantized along N (the dimension the input gradient
+    contracts over): w float32 [E, N, K] with N % 128 == 0 ->
+    (qT uint8 [E, K, N], sfT uint8 [E, K, N / 32]), expert e's [K, N] block
+    being the columnwise quantization of w[e]."""
+    w = _f32(w)
+    E, N, K = w.shape
+    if N % MX_ROW_PAD:
+        raise ValueError("N must be a multiple of 128")
+    q, b = quantize_mxfp8_colwise(w.reshape(E * N, K), np.arange(E + 1) * N)
+    return q.reshape(E, K, N), b.reshape(E, K, N // MX_BLOCK)
+
+
+def grouped_linear_dgrad_mxfp8(dy_q, dy_sf, wT_q, wT_sf, m_offsets, rows=None, cols=None,
+                               as_float32=False):
+    """Input gradient of the MXFP8 grouped linear y = x W_e^T: for row r of
+    expert e, dx[r, k] = sum_n dy[r, n] W_e[n, k], with the output gradient
+    quantized rowwise (blocks along N, per-expert padded scales as for
+    activations) and the weights columnwise (``quantize_weight_mxfp8_colwise``,
+    blocks along N).  The same contraction as the forward grouped linear with
+    W_e^T in place of the weights, so that routine is the step; output
+    bf16 [rows, K]."""
+    return grouped_gemm_mxfp8(dy_q, dy_sf, wT_q, wT_sf, m_offsets, rows, cols, as_float32)
+
+
+def grouped_linear_wgrad_mxfp8(dyT_q, dyT_sf, xT_q, xT_sf, m_offsets, N, K, as_float32=False):
+    """Weight gradient of the MXFP8 grouped linear: dW_e[n, k] = sum over the
+    rows r of expert e of dy[r, n] x[r, k], both operands quantized columnwise
+    (blocks of 32 rows, ``quantize_act_mxfp8_colwise`` layout).  Each expert's
+    contraction runs over its padded rows (the padding is zero).  Returns
+    bf16 [E, N, K] as uint16 (or float32 with as_float32)."""
+    mo = np.asarray(m_offsets, dtype=np.int64)
+    po = mx_colwise_offsets(mo)
+    E = len(mo) - 1
+    out = np.zeros((E, N, K), np.float64)
+    for e in range(E):
+        rp = int(po[e + 1] - po[e])
+        if rp == 0:
+            continue
+        nb = rp // MX_BLOCK
+        dy = _mx_decode_rows(np.asarray(dyT_q)[N * po[e]: N * po[e + 1]].reshape(N, rp),
+                             np.asarray(dyT_sf)[N * po[e] // MX_BLOCK: N * po[e + 1] // MX_BLOCK].reshape(N, nb))
+        xx = _mx_decode_rows(np.asarray(xT_q)[K * po[e]: K * po[e + 1]].reshape(K, rp),
+                             np.asarray(xT_sf)[K * po[e] // MX_BLOCK: K * po[e + 1] // MX_BLOCK].reshape(K, nb))
+        out[e] = dy @ xx.T
+    out32 = out.astype(np.float32)
+    return out32 if as_float32 else bf16_round(out32)
+
+
 # ----------------------------------------------------------------------------
 # grouped GEMM with the scale / router-weight epilogue
 # ----------------------------------------------------------------------------

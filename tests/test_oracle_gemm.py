@@ -261,3 +261,65 @@ def test_int4w16_integer_identity():
     ids = np.zeros((M, 1), np.int32)
     y = O.grouped_gemm_int4w16(x, wq, np.ones((1, N), np.float32), ids, np.ones((M, 1), np.float32))
     np.testing.assert_array_equal(y, (xi @ wq[0].astype(np.int64).T).astype(np.float32))
+
+
+# ------------------------------------------------- MXFP8 gradients -----
+def _int_rows(rng, R, C):
+    """Small integers: every 32-block quantizes to MXFP8 without loss (|v| <= 7
+    has at most three significant bits, scaled by a power of two)."""
+    return rng.integers(-7, 8, (R, C)).astype(np.float32)
+
+
+@pytest.mark.parametrize("seg", [(40, 0, 100), (128, 128), (1,)])
+def test_mxfp8_dgrad_wgrad_closed_form(seg):
+    """On losslessly quantized integers the gradients are the plain products:
+    dx = dy W_e per row of expert e, dW_e = dy_e^T x_e, rounded to bf16."""
+    rng = np.random.default_rng(41)
+    E, N, K = len(seg), 128, 64
+    R = sum(seg)
+    mo = np.concatenate([[0], np.cumsum(seg)])
+    x = _bf16(_int_rows(rng, R, K))
+    dy = _bf16(_int_rows(rng, R, N))
+    w = rng.integers(-7, 8, (E, N, K)).astype(np.float32)
+    dy_q, dy_sf = O.quantize_act_mxfp8(dy, mo)
+    wT_q, wT_sf = O.quantize_weight_mxfp8_colwise(w)
+    dx = O.grouped_linear_dgrad_mxfp8(dy_q, dy_sf, wT_q, wT_sf, mo)
+    dyv, xv = F.bf16_decode(dy).astype(np.float64), F.bf16_decode(x).astype(np.float64)
+    ref = np.zeros((R, K))
+    for e in range(E):
+        ref[mo[e]:mo[e + 1]] = dyv[mo[e]:mo[e + 1]] @ w[e].astype(np.float64)
+    np.testing.assert_array_equal(dx, F.bf16_round(ref.astype(np.float32)))
+    dyT_q, dyT_sf = O.quantize_act_mxfp8_colwise(dy, mo)
+    xT_q, xT_sf = O.quantize_act_mxfp8_colwise(x, mo)
+    dw = O.grouped_linear_wgrad_mxfp8(dyT_q, dyT_sf, xT_q, xT_sf, mo, N, K)
+    refw = np.stack([dyv[mo[e]:mo[e + 1]].T @ xv[mo[e]:mo[e + 1]] for e in range(E)])
+    np.testing.assert_array_equal(dw, F.bf16_round(refw.astype(np.float32)))
+
+
+def test_mxfp8_wgrad_brute_force():
+    """Weight gradient by exact rational arithmetic on decoded codes: the sum
+    over an expert's rows of 2^(b-127) e4m3 products, rounded once to float32."""
+    rng = np.random.default_rng(42)
+    seg = [45, 3]
+    N, K = 4, 3
+    R = sum(seg)
+    mo = np.concatenate([[0], np.cumsum(seg)])
+    dy = _bf16(rng.standard_normal((R, N)) * 2)
+    x = _bf16(rng.standard_normal((R, K)))
+    dyT_q, dyT_sf = O.quantize_act_mxfp8_colwise(dy, mo)
+    xT_q, xT_sf = O.quantize_act_mxfp8_colwise(x, mo)
+    got = O.grouped_linear_wgrad_mxfp8(dyT_q, dyT_sf, xT_q, xT_sf, mo, N, K, as_float32=True)
+    dec = F.e4m3_decode(np.arange(256, dtype=np.uint8))
+    po = O.mx_colwise_offsets(mo)
+    for e in range(len(seg)):
+        rp = int(po[e + 1] - po[e])
+        for n in range(N):
+            for k in range(K):
+                acc = Fraction(0)
+                for j in range(rp):
+                    qa = int(dyT_q[N * po[e] + n * rp + j])
+                    qb = int(xT_q[K * po[e] + k * rp + j])
+                    ba = int(dyT_sf[N * po[e] // 32 + n * (rp // 32) + j // 32])
+                    bb = int(xT_sf[K * po[e] // 32 + k * (rp // 32) + j // 32])
+                    acc += _fr(dec[qa]) * _fr(dec[qb]) * Fraction(2) ** (ba + bb - 254)
+                assert got[e, n, k] == np.float32(float(acc))

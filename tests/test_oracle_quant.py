@@ -298,3 +298,81 @@ def test_int4_symmetry_and_error_bound():
     # every code is within half a step of w / s (no clamping below amax)
     err = np.abs(w.astype(np.float64) - q1 * s1[..., None].astype(np.float64))
     assert np.all(err <= 0.5 * s1[..., None] * (1 + 1e-6))
+
+
+# ------------------------------------------------------ MXFP8 colwise ----
+def test_mxfp8_colwise_page_shapes():
+    """The worked example of the MXFP8 page: two [64, 128] experts have
+    columnwise scales [4, 128] each (two 32-row blocks padded to four); the
+    whole [128, 128] tensor has [4, 128], whose blocks are those of the
+    experts (64 rows are whole blocks), and the codes agree."""
+    g = json.load(open(os.path.join(GOLDEN, "mxfp8_padding_example.json")))
+    rng = np.random.default_rng(31)
+    E, m, K = g["experts"], g["rows_per_expert"], g["K"]
+    x = _bf16(rng.standard_normal((E * m, K)))
+    mo = np.arange(E + 1) * m
+    qT, sfT = O.quantize_act_mxfp8_colwise(x, mo)
+    rp = 128                                        # each expert padded to 128 rows
+    assert qT.size == K * E * rp and sfT.size == K * E * rp // 32
+    whole_q, whole_sf = O.quantize_act_mxfp8_colwise(x, [0, E * m])
+    whole_sf = whole_sf.reshape(K, E * m // 32)
+    assert list(whole_sf.T.shape) == g["concat_colwise_scale_shape"]
+    whole_q = whole_q.reshape(K, E * m)
+    for e in range(E):
+        sfe = sfT[K * rp // 32 * e: K * rp // 32 * (e + 1)].reshape(K, rp // 32)
+        assert list(sfe.T.shape) == g["per_expert_colwise_scale_shape"]
+        np.testing.assert_array_equal(sfe[:, : m // 32], whole_sf[:, e * m // 32: (e + 1) * m // 32])
+        assert not sfe[:, m // 32:].any()           # blocks of padding rows: scale byte 0
+        qe = qT[K * rp * e: K * rp * (e + 1)].reshape(K, rp)
+        np.testing.assert_array_equal(qe[:, :m], whole_q[:, e * m: (e + 1) * m])
+        assert not qe[:, m:].any()
+
+
+def test_mxfp8_colwise_is_rowwise_of_transpose():
+    """One expert whose rows fill whole 128-row blocks: the columnwise codes
+    and scales are the rowwise activation quantization of the transposed
+    tensor (its single 128-multiple block needs no padding)."""
+    rng = np.random.default_rng(32)
+    R, C = 256, 96
+    x = _bf16(rng.standard_normal((R, C)) * 3)
+    qT, sfT = O.quantize_act_mxfp8_colwise(x, [0, R])
+    qr, sfr = O.quantize_act_mxfp8(np.ascontiguousarray(x.T), [0, C])
+    np.testing.assert_array_equal(qT.reshape(C, R), qr)
+    np.testing.assert_array_equal(sfT.reshape(C, R // 32), sfr[:C])
+
+
+def test_mxfp8_colwise_ragged_blocks():
+    """Ragged experts: every scale byte is clamp(floor(log2 amax) + 127 - 8,
+    0, 254) over the 32 rows of its block that belong to the expert (0 when
+    they are all padding), and every code decodes to the value (saturated at
+    448 times the block scale) within half an e4m3 step."""
+    rng = np.random.default_rng(33)
+    seg = [37, 0, 70, 5]
+    C = 40
+    x = (rng.standard_normal((sum(seg), C)) * np.exp(rng.standard_normal((sum(seg), 1)))).astype(np.float32)
+    mo = np.concatenate([[0], np.cumsum(seg)])
+    qT, sfT = O.quantize_mxfp8_colwise(x, mo)
+    po = O.mx_colwise_offsets(mo)
+    dec = F.e4m3_decode(np.arange(256, dtype=np.uint8))
+    for e in range(len(seg)):
+        rp = int(po[e + 1] - po[e])
+        qe = qT[C * po[e]: C * po[e + 1]].reshape(C, rp)
+        be = sfT[C * po[e] // 32: C * po[e + 1] // 32].reshape(C, rp // 32)
+        for c in range(C):
+            for blk in range(rp // 32):
+                r0 = mo[e] + 32 * blk
+                vals = x[r0: min(r0 + 32, mo[e + 1]), c] if r0 < mo[e + 1] else np.zeros(0, np.float32)
+                amax = float(np.max(np.abs(vals))) if vals.size else 0.0
+                want = 0 if amax == 0 else max(0, min(254, math.frexp(amax)[1] - 1 + 127 - 8))
+                assert int(be[c, blk]) == want
+                codes = qe[c, 32 * blk: 32 * blk + 32]
+                got = dec[codes].astype(np.float64) * 2.0 ** (int(be[c, blk]) - 127)
+                ref = np.zeros(32)
+                ref[: vals.size] = vals
+                # the OCP rule lets amax * 2^(127-b) reach up to 512: values past
+                # e4m3's 448 saturate
+                top = 448.0 * 2.0 ** (int(be[c, blk]) - 127)
+                ref = np.sign(ref) * np.minimum(np.abs(ref), top)
+                step = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-300))) - 3)
+                step = np.maximum(step, 2.0 ** (int(be[c, blk]) - 127 - 9))   # e4m3 subnormal step
+                assert np.all(np.abs(got - ref) <= 0.5 * step + 1e-300)

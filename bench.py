@@ -58,6 +58,11 @@ def alg_bytes(wl, active_experts=None):
         return 2 * M * K + E * N * K // 2 + 4 * E * N + M * wl.top_k * N * 2
     if wl.fmt == "int8dq":      # int8 rows + one scale per token, int8 weights + channel scales
         return M * K + 4 * M + E * N * K + 4 * E * N + M * wl.top_k * N * 2
+    if wl.fmt == "mxfp8_dgrad":       # dy codes + scales, weights along N, bf16 dx [M, K]
+        return M * N * (1 + 1 / 32) + E * N * K * (1 + 1 / 32) + 2 * M * K
+    if wl.fmt == "mxfp8_wgrad":       # columnwise dy and x (padded rows), bf16 dw [E, N, K]
+        P = sum(-(-m // 128) * 128 for m in wl.seg)
+        return (N + K) * P * (1 + 1 / 32) + 2 * E * N * K
     # MXFP8: data + e8m0 scales of both operands, bf16 output rows
     return M * K * (1 + 1 / 32) + E * N * K * (1 + 1 / 32) + 2 * M * N
 
@@ -156,6 +161,29 @@ def cpu_baseline(wl, case, target_s):
                 "sample": f"the first {rows} of {wl.M} rows, {reps} time(s) in {el:.1f} s, "
                           f"scaled to the whole input (numpy float64)"}
     w = case["w"].cpu().numpy()
+    if wl.fmt in ("mxfp8_dgrad", "mxfp8_wgrad"):
+        mo = case["m_offsets"].cpu().numpy()
+        dy = case["dy"].view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+        wq, wsf = O.quantize_weight_mxfp8_colwise(w) if wl.fmt == "mxfp8_dgrad" else (None, None)
+        del w
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            if wl.fmt == "mxfp8_dgrad":
+                dq, dsf = O.quantize_act_mxfp8(dy, mo)
+                O.grouped_linear_dgrad_mxfp8(dq, dsf, wq, wsf, mo)
+            else:
+                dT, dTsf = O.quantize_act_mxfp8_colwise(dy, mo)
+                xT, xTsf = O.quantize_act_mxfp8_colwise(x, mo)
+                O.grouped_linear_wgrad_mxfp8(dT, dTsf, xT, xTsf, mo, wl.N, wl.K)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= target_s:
+                break
+        per = el / reps
+        return {"value": round(alg_bytes(wl) / per / 1e9, 3), "unit": "GB/s", "cores": threads,
+                "kind": "oracle", "tflops": round(wl.flops / per / 1e12, 6),
+                "sample": f"whole workload, {reps} step(s) in {el:.1f} s "
+                          f"(numpy float64; BLAS threads = OMP_NUM_THREADS or all cores)"}
     if wl.fmt == "mxfp8":
         wq, wsf = O.quantize_weight_mxfp8(w)
         mo = case["m_offsets"].cpu().numpy()
@@ -227,9 +255,22 @@ def main():
             moe(xs[i % copies], mo)
             if ev is not None:
                 ev[1].record()
+    elif wl.fmt == "mxfp8_wgrad":
+        copies = 1                             # operands are made from x and dy every step
+        moe = runner.MxWgrad(wl.M, wl.K, wl.N, wl.E, wl.seg)
+        mo = case["m_offsets"]
+
+        def step(i, ev):
+            moe.quantize(case["dy"], case["x"], mo)
+            if ev is not None:
+                ev[0].record()
+            moe.gemm()
+            if ev is not None:
+                ev[1].record()
     else:
-        w_q, w_s = runner.quantize_weights(case["w"], wl.fmt)
-        if wl.fmt != "mxfp8":
+        w_q, w_s = runner.quantize_weights(
+            case["w"], "mxfp8_colwise" if wl.fmt == "mxfp8_dgrad" else wl.fmt)
+        if not wl.fmt.startswith("mxfp8"):
             # decode (block_m 16): fragment-ordered weights, one contiguous 1 KB
             # read per MFMA operand; otherwise tiles of one 8 KB block per stage
             layout = (qm.MOE_W_FRAG if qm.moe_recommended_block_m(wl.M, wl.E, wl.top_k) == 16
@@ -237,8 +278,21 @@ def main():
             w_q = runner.pack_weights(w_q, layout)
         copies = args.copies or max(2, -(-(1 << 30) // w_q.numel()))
         weights = [(w_q, w_s)] + [(w_q.clone(), w_s.clone()) for _ in range(copies - 1)]
-    if wl.fmt.startswith("act_"):
+    if wl.fmt.startswith("act_") or wl.fmt == "mxfp8_wgrad":
         pass
+    elif wl.fmt == "mxfp8_dgrad":
+        # the output gradient [M, N] against the weights along N: dx [M, K]
+        moe = runner.MxMoE(wl.M, wl.N, wl.K, wl.E)
+        mo = case["m_offsets"]
+
+        def step(i, ev):
+            q, s = weights[i % copies]
+            moe.quantize(case["dy"], mo)
+            if ev is not None:
+                ev[0].record()
+            moe.gemm(q, s, mo)
+            if ev is not None:
+                ev[1].record()
     elif wl.fmt == "mxfp8":
         moe = runner.MxMoE(wl.M, wl.K, wl.N, wl.E)
         mo = case["m_offsets"]
@@ -285,7 +339,8 @@ def main():
         active = int(torch.unique(ids).numel())
     nbytes = alg_bytes(wl, active)
     ms = elapsed * 1e3 / args.steps
-    dtype = {"fp8": "fp8", "int8": "bf16", "int8dq": "int8", "fp8wo": "bf16", "int4wo": "bf16", "mxfp8": "mxfp8", "act_fp8": "fp8",
+    dtype = {"fp8": "fp8", "int8": "bf16", "int8dq": "int8", "fp8wo": "bf16", "int4wo": "bf16",
+             "mxfp8": "mxfp8", "mxfp8_dgrad": "mxfp8", "mxfp8_wgrad": "mxfp8", "act_fp8": "fp8",
              "act_mxfp8": "mxfp8"}[wl.fmt]
     is_act = wl.fmt.startswith("act_")
     bound = "hbm" if is_act or wl.flops / nbytes < 600 else "mfma"
@@ -315,7 +370,7 @@ def main():
                    "E": wl.E, "top_k": wl.top_k,
                    ("input_copies" if is_act else "weight_copies"): copies,
                    "block_m": getattr(moe, "block_m", None),
-                   "weight_layout": None if is_act else
+                   "weight_layout": None if is_act or wl.fmt == "mxfp8_wgrad" else
                    {qm.MOE_W_TILED: "tiled", qm.MOE_W_FRAG: "frag"}.get(
                        getattr(moe, "w_layout", None), "rowmajor")},
         "roofline": roof,

@@ -62,6 +62,8 @@ extern "C" {
 #define MOE_Q_FP8_PER_CHANNEL  3  /* e4m3 + one fp32 scale per output channel (weights only) */
 #define MOE_Q_INT4_PER_CHANNEL 4  /* int4 (two per byte) + one fp32 scale per output channel
                                      (weights only) */
+#define MOE_Q_MXFP8_COLWISE    5  /* e4m3 + one e8m0 scale per 32 values along N, stored
+                                     transposed (weights only: the input gradient) */
 
 /* ---- activations fused with the quantization (moe_act_quantize) -------- */
 #define MOE_ACT_SWIGLU 0  /* y = silu(g) * u, row = [g | u] (2H inputs -> H outputs) */
@@ -231,6 +233,12 @@ int moe_act_quantize(const uint16_t *x, int rows, int H, int act, int mode,
  * MOE_Q_INT8_PER_CHANNEL: per row s = fl32(amax_row/127) (1 if zero),
  *                         q = clamp(round_half_even(fl32(w * fl32(1/s))),
  *                         -127, 127); q is int8 [E,N,K], scale [E,N].
+ * MOE_Q_MXFP8_COLWISE   : blocks of 32 along N (per k and expert) by the MXFP8
+ *                         rule, stored transposed: q uint8 [E, K, N] (q[e,k,n]
+ *                         the code of w[e,n,k]), scale_e8m0 [E, K, N/32]; the
+ *                         weights of the input gradient ("[PyTorch] Let
+ *                         GroupedLinear accept MXFP8 input and gradient").
+ *                         N must be a multiple of 128 and K of 64.
  * MOE_Q_MXFP8           : per row and block of 32 along K as in
  *                         moe_quantize_act; q uint8 [E,N,K], scale_e8m0
  *                         [E,N,K/32] (no padding).
@@ -374,11 +382,51 @@ int moe_grouped_gemm_int4w4a16(const uint16_t *a, const uint8_t *w_q,
  *   uint8 e4m3; w_sf [E, N, K/32] e8m0; m_offsets [E+1] int32 (device);
  *   out [rows, N] uint16 bf16, written in full.
  *
+ * With the output gradient dy as a (moe_quantize_act(MOE_Q_MXFP8), K = the
+ * layer's N) and the weights quantized with MOE_Q_MXFP8_COLWISE as w ([E, K,
+ * N], N = the layer's K) the same call computes the input gradient
+ * dx[r, k] = sum_n dy[r, n] w[e, n, k] of the grouped linear.
+ *
  * K must be a multiple of 128. */
 int moe_grouped_gemm_mxfp8(const uint8_t *a_q, const uint8_t *a_sf,
                            const uint8_t *w_q, const uint8_t *w_sf,
                            const int *m_offsets, int rows, int K, int N, int E,
                            uint16_t *out, hipStream_t stream);
+
+/* ======================================================================== *
+ * MXFP8 backward of the grouped linear ("[PyTorch] Let GroupedLinear accept
+ * MXFP8 input and gradient": colwise scaling factors for the gradient)
+ * ======================================================================== */
+
+/* Columnwise MXFP8 of expert-concatenated bf16 rows (activations x or output
+ * gradients dy) for the weight gradient: for expert e (rows m_offsets[e] ..
+ * m_offsets[e+1]-1, m_e of them) the rows are padded with zeros to
+ * Rp_e = roundup(m_e, 128); column c, padded rows 32j .. 32j+31 form one
+ * block with one e8m0 scale by the MXFP8 rule (moe_quantize_act).  Stored
+ * transposed, expert by expert, with P_e = Rp_0 + .. + Rp_{e-1}:
+ *   qT  code of row m_offsets[e] + i, column c at byte C*P_e + c*Rp_e + i
+ *       (zero for the padding rows)
+ *   sfT scale of block j of column c at byte C*P_e/32 + c*Rp_e/32 + j
+ * x [rows, C] bf16 (2-byte aligned), m_offsets [E+1] int32 (device), qT at
+ * least C * moe_mx_scale_rows(rows, E) bytes (16-byte aligned), sfT at least
+ * C * moe_mx_scale_rows(rows, E) / 32 bytes.  C must be a multiple of 64;
+ * rows + 127 E at most 65535 * 128. */
+int moe_quantize_act_colwise(const uint16_t *x, int rows, int C, const int *m_offsets, int E,
+                             uint8_t *qT, uint8_t *sfT, hipStream_t stream);
+
+/* Weight gradient of the MXFP8 grouped linear y = x W_e^T: for every expert
+ *     dw[e, n, k] = bf16( sum over the padded rows i of expert e, in blocks of
+ *                   32, of 2^(b_dy + b_x - 254) * dyT[n, i] * xT[k, i] )
+ * accumulated in fp32 (an expert without rows gets zeros).  dyT_q / dyT_sf
+ * and xT_q / xT_sf are moe_quantize_act_colwise of dy [rows, N] and
+ * x [rows, K] with the same expert segments; m_splits [E] are the rows per
+ * expert in HOST memory (the caller knows the split; no device read or
+ * synchronisation is needed to size the launches).  dw [E, N, K] uint16 bf16,
+ * 16-byte aligned, written in full.  N must be a multiple of 128 and K of
+ * 64.  One MXFP8 grouped-linear launch per expert is enqueued on `stream`. */
+int moe_grouped_gemm_mxfp8_wgrad(const uint8_t *dyT_q, const uint8_t *dyT_sf,
+                                 const uint8_t *xT_q, const uint8_t *xT_sf, const int *m_splits,
+                                 int E, int N, int K, uint16_t *dw, hipStream_t stream);
 
 /* ======================================================================== *
  * a6: combine

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmoe.so"
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP = 0, -1, -2, -3
 MOE_Q_FP8_PER_TENSOR, MOE_Q_MXFP8, MOE_Q_INT8_PER_CHANNEL, MOE_Q_FP8_PER_CHANNEL = 0, 1, 2, 3
-MOE_Q_INT4_PER_CHANNEL = 4
+MOE_Q_INT4_PER_CHANNEL, MOE_Q_MXFP8_COLWISE = 4, 5
 MOE_W_ROWMAJOR, MOE_W_TILED, MOE_W_FRAG = 0, 1, 2
 MOE_ACT_SWIGLU, MOE_ACT_SRELU = 0, 1
 MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_SLOTS = 128, 8, 65536
@@ -33,6 +33,7 @@ EXPORTS = [
     "moe_grouped_gemm_fp8w8a8",
     "moe_grouped_gemm_int8w8a8", "moe_grouped_gemm_fp8w8a16", "moe_grouped_gemm_int4w4a16",
     "moe_grouped_gemm_int8w8a16", "moe_grouped_gemm_mxfp8", "moe_combine",
+    "moe_quantize_act_colwise", "moe_grouped_gemm_mxfp8_wgrad",
 ]
 
 
@@ -68,6 +69,8 @@ _SIGS = {
     "moe_grouped_gemm_int8w8a16": (_I, [_P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
     "moe_grouped_gemm_fp8w8a16": (_I, [_P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
     "moe_grouped_gemm_int4w4a16": (_I, [_P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
+    "moe_quantize_act_colwise": (_I, [_P, _I, _I, _P, _I, _P, _P, _P]),
+    "moe_grouped_gemm_mxfp8_wgrad": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P, _P]),
     "moe_grouped_gemm_mxfp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "moe_combine": (_I, [_P, _I, _I, _I, _P, _P]),
 }
@@ -213,6 +216,19 @@ def moe_grouped_gemm_int4w4a16(a, w_q, w_scale, w_layout, sorted_token_ids, expe
         _ptr(a), _ptr(w_q), _ptr(w_scale), w_layout, _ptr(sorted_token_ids), _ptr(expert_ids),
         _ptr(num_tokens_post_padded), _ptr(topk_weights), M, K, N, E, top_k, block_m, _ptr(y),
         _stream(stream)))
+
+
+def moe_quantize_act_colwise(x, rows, C, m_offsets, E, qT, sfT, stream=None):
+    return _check(lib().moe_quantize_act_colwise(_ptr(x), rows, C, _ptr(m_offsets), E, _ptr(qT),
+                                                 _ptr(sfT), _stream(stream)))
+
+
+def moe_grouped_gemm_mxfp8_wgrad(dyT_q, dyT_sf, xT_q, xT_sf, m_splits, E, N, K, dw, stream=None):
+    """m_splits: rows per expert, a host sequence of E ints."""
+    splits = (ctypes.c_int * E)(*[int(v) for v in m_splits])
+    return _check(lib().moe_grouped_gemm_mxfp8_wgrad(
+        _ptr(dyT_q), _ptr(dyT_sf), _ptr(xT_q), _ptr(xT_sf), ctypes.cast(splits, ctypes.c_void_p),
+        E, N, K, _ptr(dw), _stream(stream)))
 
 
 def moe_grouped_gemm_mxfp8(a_q, a_sf, w_q, w_sf, m_offsets, rows, K, N, E, out, stream=None):

@@ -280,6 +280,15 @@ int moe_quantize_weights(const float *w, int E, int N, int K, int mode, void *q,
                                                        scale, stream),
                       fn);
   }
+  if (mode == MOE_Q_MXFP8_COLWISE) {
+    REQUIRE(scale_e8m0, MOE_EINVAL, "%s: null scale_e8m0", fn);
+    REQUIRE(aligned16(q), MOE_EINVAL, "%s: q must be 16-byte aligned", fn);
+    REQUIRE(N % 128 == 0 && K % 64 == 0, MOE_EUNSUPPORTED,
+            "%s: N=%d must be a multiple of 128 and K=%d of 64", fn, N, K);
+    REQUIRE((long long)E * N / 128 <= 65535, MOE_EUNSUPPORTED, "%s: E*N too large", fn);
+    return hip_status(
+        qmoe::launch_mx_colwise_weights(w, E, N, K, (uint8_t *)q, scale_e8m0, stream), fn);
+  }
   if (mode == MOE_Q_MXFP8) {
     REQUIRE(scale_e8m0, MOE_EINVAL, "%s: null scale_e8m0", fn);
     REQUIRE(aligned16(q), MOE_EINVAL, "%s: q must be 16-byte aligned", fn);
@@ -395,6 +404,62 @@ int moe_grouped_gemm_mxfp8(const uint8_t *a_q, const uint8_t *a_sf, const uint8_
   if (rows == 0) return ok();
   return hip_status(
       qmoe::launch_gemm_mxfp8(a_q, a_sf, w_q, w_sf, m_offsets, rows, K, N, E, out, stream), fn);
+}
+
+int moe_quantize_act_colwise(const uint16_t *x, int rows, int C, const int *m_offsets, int E,
+                             uint8_t *qT, uint8_t *sfT, hipStream_t stream) {
+  const char *fn = "moe_quantize_act_colwise";
+  REQUIRE(E >= 1 && E <= MOE_MAX_EXPERTS, MOE_EINVAL, "%s: E=%d", fn, E);
+  REQUIRE(rows >= 0 && C > 0, MOE_EINVAL, "%s: rows=%d C=%d", fn, rows, C);
+  REQUIRE(C % 64 == 0, MOE_EUNSUPPORTED, "%s: C=%d is not a multiple of 64", fn, C);
+  REQUIRE((long long)rows + (long long)E * 127 <= 65535ll * 128, MOE_EUNSUPPORTED,
+          "%s: rows=%d beyond the supported %d", fn, rows, 65535 * 128 - E * 127);
+  REQUIRE(((long long)rows + (long long)E * 127) * C < (1ll << 32), MOE_EUNSUPPORTED,
+          "%s: the transposed codes must stay below 4 GiB", fn);
+  if (rows == 0) return ok();
+  REQUIRE(x && m_offsets && qT && sfT, MOE_EINVAL, "%s: null pointer argument", fn);
+  REQUIRE(((uintptr_t)x & 1u) == 0 && aligned16(qT), MOE_EINVAL,
+          "%s: x must be 2-byte and qT 16-byte aligned", fn);
+  return hip_status(qmoe::launch_mx_colwise_bf16(x, rows, C, m_offsets, E, qT, sfT, stream), fn);
+}
+
+int moe_grouped_gemm_mxfp8_wgrad(const uint8_t *dyT_q, const uint8_t *dyT_sf,
+                                 const uint8_t *xT_q, const uint8_t *xT_sf, const int *m_splits,
+                                 int E, int N, int K, uint16_t *dw, hipStream_t stream) {
+  const char *fn = "moe_grouped_gemm_mxfp8_wgrad";
+  REQUIRE(E >= 1 && E <= MOE_MAX_EXPERTS, MOE_EINVAL, "%s: E=%d", fn, E);
+  REQUIRE(N > 0 && K > 0, MOE_EINVAL, "%s: N=%d K=%d", fn, N, K);
+  REQUIRE(N % 128 == 0 && K % 64 == 0, MOE_EUNSUPPORTED,
+          "%s: N=%d must be a multiple of 128 and K=%d of 64", fn, N, K);
+  REQUIRE(m_splits && dyT_q && dyT_sf && xT_q && xT_sf && dw, MOE_EINVAL,
+          "%s: null pointer argument", fn);
+  REQUIRE(aligned16(dyT_q) && aligned16(xT_q) && aligned16(dw) && ((uintptr_t)dyT_sf & 3u) == 0 &&
+              ((uintptr_t)xT_sf & 3u) == 0,
+          MOE_EINVAL, "%s: codes and output must be 16-byte and scales 4-byte aligned", fn);
+  REQUIRE((long long)E * N * (long long)K * 2 < (1ll << 40), MOE_EUNSUPPORTED, "%s: sizes", fn);
+  long long total = 0;
+  for (int e = 0; e < E; ++e) {
+    REQUIRE(m_splits[e] >= 0, MOE_EINVAL, "%s: m_splits[%d]=%d", fn, e, m_splits[e]);
+    total += (m_splits[e] + 127) / 128 * 128;
+  }
+  REQUIRE(total * (long long)(N > K ? N : K) < (1ll << 32), MOE_EUNSUPPORTED,
+          "%s: the transposed operands must stay below 4 GiB", fn);
+  long long off = 0;                                      // padded rows of the experts before e
+  for (int e = 0; e < E; ++e) {
+    const long long rp = (m_splits[e] + 127) / 128 * 128;
+    uint16_t *out = dw + (size_t)e * (size_t)N * (size_t)K;
+    hipError_t err;
+    if (rp == 0) {                                        // no rows: the gradient is zero
+      err = qmoe::launch_fill_u16(out, (long long)N * K, 0, stream);
+    } else {
+      err = qmoe::launch_gemm_mxfp8(dyT_q + (size_t)N * off, dyT_sf + (size_t)N * off / 32,
+                                    xT_q + (size_t)K * off, xT_sf + (size_t)K * off / 32, nullptr,
+                                    N, (int)rp, K, 1, out, stream);
+    }
+    if (err != hipSuccess) return hip_status(err, fn);
+    off += rp;
+  }
+  return ok();
 }
 
 int moe_combine(const uint16_t *y, int M, int N, int top_k, uint16_t *out, hipStream_t stream) {

@@ -1426,8 +1426,9 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
     for (int ee = 0; ee < E; ++ee) {
       int nb;
       if constexpr (kMx) {
-        s_mo[ee] = m_offsets[ee];
-        s_mo[ee + 1] = m_offsets[ee + 1];
+        // no m_offsets: one segment of all M rows (a single expert)
+        s_mo[ee] = m_offsets ? m_offsets[ee] : 0;
+        s_mo[ee + 1] = m_offsets ? m_offsets[ee + 1] : M;
         const int m = s_mo[ee + 1] - s_mo[ee];
         nb = m > 0 ? (m + kGBM - 1) / kGBM : 0;
         s_blk_first[ee] = blk;

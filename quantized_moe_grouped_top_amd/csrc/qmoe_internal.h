@@ -103,6 +103,11 @@ hipError_t launch_gemm_mxfp8(const uint8_t *a_q, const uint8_t *a_sf, const uint
                              const uint8_t *w_sf, const int *m_offsets, int rows, int K,
                              int N, int E, uint16_t *out, hipStream_t s);
 
+hipError_t launch_mx_colwise_bf16(const uint16_t *x, int rows, int C, const int *m_offsets,
+                                  int E, uint8_t *qT, uint8_t *sfT, hipStream_t s);
+hipError_t launch_mx_colwise_weights(const float *w, int E, int N, int K, uint8_t *qT,
+                                     uint8_t *sfT, hipStream_t s);
+hipError_t launch_fill_u16(uint16_t *p, long long n, uint16_t v, hipStream_t s);
 hipError_t launch_pack_weights(const uint8_t *w, int E, int N, int K, int layout, uint8_t *packed,
                                hipStream_t s);
 

@@ -289,6 +289,58 @@ __device__ __forceinline__ uint32_t mx_encode(const float *v, uint8_t *dst) {
   return (uint32_t)b;
 }
 
+// ---- MXFP8 along the rows (columnwise scales), stored transposed ----------
+// For expert e its rows are padded with zeros to Rp_e = roundup(m_e, 128);
+// column c, rows 32j .. 32j+31 of the padded segment form one block.  Output,
+// expert by expert (P_e = sum of Rp of the experts before e): codes at
+// C * P_e + c * Rp_e + row, scale bytes at C * P_e / 32 + c * Rp_e / 32 + j.
+// A workgroup takes 64 columns x 128 padded rows (one padded chunk of one
+// expert); thread (sb, c) reads the 32 values of its block column by column
+// (a row of 64 columns per load across the wavefront) and writes the block's
+// 32 codes as two 16-byte stores.
+__device__ __forceinline__ float ld1(const uint16_t *p) {
+  return __builtin_bit_cast(float, (uint32_t)*p << 16);
+}
+__device__ __forceinline__ float ld1(const float *p) { return *p; }
+
+template <typename Src>
+__global__ __launch_bounds__(kThreads) void mx_colwise_kernel(const Src *__restrict__ x, int C,
+                                                              const int *__restrict__ m_offsets,
+                                                              int E, int uniform_rows,
+                                                              uint8_t *__restrict__ qT,
+                                                              uint8_t *__restrict__ sfT) {
+  __shared__ long long s_po[kMaxExperts + 1];               // padded start of each expert
+  __shared__ int s_mo[kMaxExperts + 1];
+  if (threadIdx.x == 0) {
+    long long acc = 0;
+    for (int e = 0; e <= E; ++e) {
+      // uniform_rows > 0: E segments of uniform_rows rows (weights), no m_offsets
+      s_mo[e] = uniform_rows > 0 ? e * uniform_rows : m_offsets[e];
+      s_po[e] = acc;
+      if (e < E) {
+        const int m = uniform_rows > 0 ? uniform_rows : m_offsets[e + 1] - m_offsets[e];
+        acc += (long long)(m + kMxRowPad - 1) / kMxRowPad * kMxRowPad;
+      }
+    }
+  }
+  __syncthreads();
+  const long long pr = (long long)kMxRowPad * blockIdx.y;   // padded row of this chunk
+  if (pr >= s_po[E]) return;
+  int e = 0;
+  while (s_po[e + 1] <= pr) ++e;
+  const long long rp = s_po[e + 1] - s_po[e];
+  const int c = blockIdx.x * 64 + (threadIdx.x & 63);
+  const long long j0 = pr - s_po[e] + kMxBlock * (threadIdx.x >> 6);   // row in the padded segment
+  const long long r0 = s_mo[e] + j0;
+  const long long rend = s_mo[e + 1];
+  float v[kMxBlock];
+#pragma unroll
+  for (int i = 0; i < kMxBlock; ++i) v[i] = r0 + i < rend ? ld1(x + (r0 + i) * C + c) : 0.0f;
+  const size_t base = (size_t)C * (size_t)s_po[e];
+  const uint32_t b = mx_encode(v, qT + base + (size_t)c * (size_t)rp + (size_t)j0);
+  sfT[base / kMxBlock + (size_t)c * (size_t)(rp / kMxBlock) + (size_t)(j0 / kMxBlock)] = (uint8_t)b;
+}
+
 template <typename Src>
 __device__ __forceinline__ uint32_t mx_block(const Src *src, uint8_t *dst) {
   float v[32];
@@ -801,6 +853,37 @@ hipError_t launch_quant_mx_rows_f32(const float *w, long long rows, int K, uint8
                                     uint8_t *sf, hipStream_t s) {
   hipLaunchKernelGGL(quant_mx_rows_kernel, dim3(grid_for(rows * (K / kMxBlock), 16384)),
                      dim3(kThreads), 0, s, w, rows, K, q, sf);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_colwise_bf16(const uint16_t *x, int rows, int C, const int *m_offsets,
+                                  int E, uint8_t *qT, uint8_t *sfT, hipStream_t s) {
+  // chunks of 128 padded rows: at most (rows + E * 127) / 128 of them
+  const long long chunks = ((long long)rows + (long long)E * (kMxRowPad - 1)) / kMxRowPad;
+  if (chunks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(mx_colwise_kernel<uint16_t>, dim3((unsigned)(C / 64), (unsigned)chunks),
+                     dim3(kThreads), 0, s, x, C, m_offsets, E, 0, qT, sfT);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_colwise_weights(const float *w, int E, int N, int K, uint8_t *qT,
+                                     uint8_t *sfT, hipStream_t s) {
+  // w [E, N, K] as E segments of N rows (N % 128 == 0) and K columns
+  const long long chunks = (long long)E * N / kMxRowPad;
+  hipLaunchKernelGGL(mx_colwise_kernel<float>, dim3((unsigned)(K / 64), (unsigned)chunks),
+                     dim3(kThreads), 0, s, w, K, nullptr, E, N, qT, sfT);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(kThreads) void fill_u16_kernel(uint16_t *__restrict__ p, long long n,
+                                                            uint16_t v) {
+  for (long long i = blockIdx.x * (long long)kThreads + threadIdx.x; i < n;
+       i += (long long)gridDim.x * kThreads)
+    p[i] = v;
+}
+
+hipError_t launch_fill_u16(uint16_t *p, long long n, uint16_t v, hipStream_t s) {
+  hipLaunchKernelGGL(fill_u16_kernel, dim3(grid_for(n, 16384)), dim3(kThreads), 0, s, p, n, v);
   return hipGetLastError();
 }
 

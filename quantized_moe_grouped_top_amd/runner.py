@@ -8,6 +8,9 @@ current stream:
                      moe_grouped_gemm_{fp8w8a8,int8w8a8,int8w8a16,fp8w8a16,int4w4a16} ->
                      moe_combine
     MXFP8          : moe_quantize_act(MXFP8) -> moe_grouped_gemm_mxfp8
+    MXFP8 backward : input gradient = the MXFP8 call with the output gradient
+                     and MOE_Q_MXFP8_COLWISE weights; weight gradient =
+                     moe_quantize_act_colwise (dy, x) -> moe_grouped_gemm_mxfp8_wgrad
     activation     : moe_act_quantize (SwiGLU / SReLU + MXFP8 or fp8)
 
 Every step runs in the library's HIP kernels; nothing here computes.
@@ -16,13 +19,14 @@ Every step runs in the library's HIP kernels; nothing here computes.
 import torch
 
 from . import (MOE_ACT_SRELU, MOE_ACT_SWIGLU, MOE_Q_FP8_PER_CHANNEL, MOE_Q_FP8_PER_TENSOR,
-               MOE_Q_INT4_PER_CHANNEL, MOE_Q_INT8_PER_CHANNEL, MOE_Q_MXFP8, MOE_W_FRAG,
+               MOE_Q_INT4_PER_CHANNEL, MOE_Q_INT8_PER_CHANNEL, MOE_Q_MXFP8, MOE_Q_MXFP8_COLWISE,
+               MOE_W_FRAG,
                MOE_W_ROWMAJOR,
                MOE_W_TILED, moe_act_quantize, moe_align_block_size, moe_align_max_padded, moe_combine,
                moe_grouped_gemm_fp8w8a8, moe_grouped_gemm_fp8w8a16, moe_grouped_gemm_int4w4a16,
                moe_grouped_gemm_int8w8a8,
                moe_grouped_gemm_int8w8a16,
-               moe_grouped_gemm_mxfp8,
+               moe_grouped_gemm_mxfp8, moe_grouped_gemm_mxfp8_wgrad, moe_quantize_act_colwise,
                moe_mx_scale_rows, moe_pack_weights, moe_packed_weight_bytes, moe_quantize_act,
                moe_quantize_weights, moe_quantize_workspace_bytes, moe_recommended_block_m)
 
@@ -61,6 +65,11 @@ def quantize_weights(w, fmt):
         q = _empty((E, N, K), torch.uint8, dev)
         sf = _empty((E, N, K // 32), torch.uint8, dev)
         moe_quantize_weights(w, E, N, K, MOE_Q_MXFP8, q, None, sf, None)
+        return q, sf
+    if fmt == "mxfp8_colwise":           # along N, transposed: [E, K, N]
+        q = _empty((E, K, N), torch.uint8, dev)
+        sf = _empty((E, K, N // 32), torch.uint8, dev)
+        moe_quantize_weights(w, E, N, K, MOE_Q_MXFP8_COLWISE, q, None, sf, None)
         return q, sf
     raise ValueError(fmt)
 
@@ -178,6 +187,30 @@ class MxMoE:
         self.quantize(x, m_offsets)
         self.gemm(w_q, w_sf, m_offsets)
         return self.out
+
+
+class MxWgrad:
+    """Weight gradient of the MXFP8 grouped linear: columnwise quantization
+    of the output gradient dy [rows, N] and the input x [rows, K], then one
+    grouped-linear launch per expert into dw [E, N, K] (bf16 bits)."""
+
+    def __init__(self, rows, K, N, E, m_splits, device="cuda"):
+        self.rows, self.K, self.N, self.E = rows, K, N, E
+        self.m_splits = [int(v) for v in m_splits]
+        P = moe_mx_scale_rows(rows, E)
+        self.dyT_q = _empty((N * P,), torch.uint8, device)
+        self.dyT_sf = _empty((N * P // 32 + 1,), torch.uint8, device)
+        self.xT_q = _empty((K * P,), torch.uint8, device)
+        self.xT_sf = _empty((K * P // 32 + 1,), torch.uint8, device)
+        self.dw = _empty((E, N, K), torch.int16, device)
+
+    def quantize(self, dy, x, m_offsets):
+        moe_quantize_act_colwise(dy, self.rows, self.N, m_offsets, self.E, self.dyT_q, self.dyT_sf)
+        moe_quantize_act_colwise(x, self.rows, self.K, m_offsets, self.E, self.xT_q, self.xT_sf)
+
+    def gemm(self):
+        moe_grouped_gemm_mxfp8_wgrad(self.dyT_q, self.dyT_sf, self.xT_q, self.xT_sf, self.m_splits,
+                                     self.E, self.N, self.K, self.dw)
 
 
 class ActQuant:

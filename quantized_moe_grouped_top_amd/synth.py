@@ -31,7 +31,8 @@ class Workload:
     fmt: str               # "fp8", "int8" (W8A16), "int8dq" (W8A8, per-token activation
                            # scales), "fp8wo" (bf16 x fp8 per-channel weights),
                            # "int4wo" (bf16 x int4 per-channel weights),
-                           # "mxfp8"; "act_mxfp8", "act_fp8" (K = input
+                           # "mxfp8", "mxfp8_dgrad", "mxfp8_wgrad" (its
+                           # backward); "act_mxfp8", "act_fp8" (K = input
                            # width 2H or H, N = H)
     M: int                 # tokens (MXFP8: total rows)
     K: int
@@ -44,7 +45,7 @@ class Workload:
 
     @property
     def routed_rows(self):
-        return self.M if self.fmt == "mxfp8" else self.M * self.top_k
+        return self.M if self.fmt.startswith("mxfp8") else self.M * self.top_k
 
     @property
     def flops(self):
@@ -82,6 +83,12 @@ WORKLOADS = {w.name: w for w in [
     Workload("int4wo_m64_k4096_n14336", "int4wo", 64, 4096, 14336),
     _mx("mxfp8_8x4000_k4096_n4096", 4000, 8, 4096, 4096),
     _mx("mxfp8_22b_8x4000_k6144_n32768", 4000, 8, 6144, 32768),
+    # the backward of the (8*4000, 4096) grouped linear: input gradient
+    # (dy [rows, N] x W) and weight gradient (dy^T x per expert), K = N = 4096
+    Workload("mxfp8_dgrad_8x4000_k4096_n4096", "mxfp8_dgrad", 32000, 4096, 4096, E=8, top_k=1,
+             seg=tuple([4000] * 8)),
+    Workload("mxfp8_wgrad_8x4000_k4096_n4096", "mxfp8_wgrad", 32000, 4096, 4096, E=8, top_k=1,
+             seg=tuple([4000] * 8)),
     # the (8*4000, 4096) activation input: SwiGLU halves it to H = 2048
     _act("swiglu", "mxfp8", 4000, 8, 2048),
     _act("srelu", "mxfp8", 4000, 8, 4096),
@@ -156,8 +163,10 @@ def make_case(wl, variant=0, device="cpu"):
         "x": make_activations(wl.M, wl.K, s + 1, device),
         "w": make_weights(wl.E, wl.N, wl.K, s + 2, device),
     }
-    if wl.fmt == "mxfp8":
+    if wl.fmt.startswith("mxfp8"):
         case["m_offsets"] = make_segments(wl.seg, device)
+        if wl.fmt != "mxfp8":            # backward: the output gradient [M, N]
+            case["dy"] = make_act_input(wl.M, wl.N, s + 4, 0.5, device)
     else:
         case["logits"] = make_logits(wl.M, wl.E, s + 3, wl.bias_std, device)
     return case

@@ -38,7 +38,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 21
     h = ctypes.CDLL(qm.LIB_PATH)
     for n in names:
         assert hasattr(h, n), n
@@ -207,6 +207,31 @@ def test_gemm_int4_and_int4_quantizer_reject():
         qm.moe_quantize_act(FAKE, 10, 64, qm.MOE_Q_INT4_PER_CHANNEL, None, 1, FAKE, FAKE, None,
                             None, stream=0)
     assert ei.value.code == qm.MOE_EINVAL                       # weights only
+
+
+def test_mx_backward_rejects():
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_quantize_act_colwise(FAKE, 100, 96, FAKE, 2, FAKE, FAKE, stream=0)
+    assert ei.value.code == qm.MOE_EUNSUPPORTED                 # C % 64
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_quantize_act_colwise(FAKE, 100, 128, FAKE, 0, FAKE, FAKE, stream=0)
+    assert ei.value.code == qm.MOE_EINVAL                       # E = 0
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_quantize_act_colwise(FAKE, 100, 128, FAKE, 2, MIS, FAKE, stream=0)
+    assert ei.value.code == qm.MOE_EINVAL                       # misaligned codes
+    qm.moe_quantize_act_colwise(FAKE, 0, 128, FAKE, 2, FAKE, FAKE, stream=0)   # no rows
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_grouped_gemm_mxfp8_wgrad(FAKE, FAKE, FAKE, FAKE, [10, 20], 2, 100, 128, FAKE,
+                                        stream=0)
+    assert ei.value.code == qm.MOE_EUNSUPPORTED                 # N % 128
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_grouped_gemm_mxfp8_wgrad(FAKE, FAKE, FAKE, FAKE, [10, -1], 2, 128, 128, FAKE,
+                                        stream=0)
+    assert ei.value.code == qm.MOE_EINVAL                       # negative split
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_quantize_weights(FAKE, 2, 100, 128, qm.MOE_Q_MXFP8_COLWISE, FAKE, None, FAKE,
+                                None, stream=0)
+    assert ei.value.code == qm.MOE_EUNSUPPORTED                 # N % 128
 
 
 def test_quantize_and_combine_reject():

@@ -294,14 +294,27 @@ __device__ __forceinline__ uint32_t mx_encode(const float *v, uint8_t *dst) {
 // column c, rows 32j .. 32j+31 of the padded segment form one block.  Output,
 // expert by expert (P_e = sum of Rp of the experts before e): codes at
 // C * P_e + c * Rp_e + row, scale bytes at C * P_e / 32 + c * Rp_e / 32 + j.
-// A workgroup takes 64 columns x 128 padded rows (one padded chunk of one
-// expert); thread (sb, c) reads the 32 values of its block column by column
-// (a row of 64 columns per load across the wavefront) and writes the block's
-// 32 codes as two 16-byte stores.
-__device__ __forceinline__ float ld1(const uint16_t *p) {
-  return __builtin_bit_cast(float, (uint32_t)*p << 16);
+// A workgroup takes 256 columns x 128 padded rows (one padded chunk of one
+// expert); thread (sb, cg) reads the 32 rows of its block for 4 neighbouring
+// columns (one 8- or 16-byte load per row, a row of the wavefront's 256
+// columns per load instruction), then encodes and writes the 4 columns'
+// blocks (32 contiguous codes each).
+constexpr int kColwiseCols = 4;                     // columns per thread
+
+__device__ __forceinline__ void ld4col(const uint16_t *p, float *v) {
+  const i32x2 r = *reinterpret_cast<const i32x2 *>(p);
+  v[0] = __builtin_bit_cast(float, (uint32_t)r[0] << 16);
+  v[1] = __builtin_bit_cast(float, (uint32_t)r[0] & 0xFFFF0000u);
+  v[2] = __builtin_bit_cast(float, (uint32_t)r[1] << 16);
+  v[3] = __builtin_bit_cast(float, (uint32_t)r[1] & 0xFFFF0000u);
 }
-__device__ __forceinline__ float ld1(const float *p) { return *p; }
+__device__ __forceinline__ void ld4col(const float *p, float *v) {
+  const f32x4 r = *reinterpret_cast<const f32x4 *>(p);
+  v[0] = r[0];
+  v[1] = r[1];
+  v[2] = r[2];
+  v[3] = r[3];
+}
 
 template <typename Src>
 __global__ __launch_bounds__(kThreads) void mx_colwise_kernel(const Src *__restrict__ x, int C,
@@ -329,16 +342,26 @@ __global__ __launch_bounds__(kThreads) void mx_colwise_kernel(const Src *__restr
   int e = 0;
   while (s_po[e + 1] <= pr) ++e;
   const long long rp = s_po[e + 1] - s_po[e];
-  const int c = blockIdx.x * 64 + (threadIdx.x & 63);
+  const int c0 = (blockIdx.x * 64 + (threadIdx.x & 63)) * kColwiseCols;
+  if (c0 >= C) return;                                      // (C % 64: whole groups only)
   const long long j0 = pr - s_po[e] + kMxBlock * (threadIdx.x >> 6);   // row in the padded segment
   const long long r0 = s_mo[e] + j0;
   const long long rend = s_mo[e + 1];
-  float v[kMxBlock];
+  float v[kColwiseCols][kMxBlock];
 #pragma unroll
-  for (int i = 0; i < kMxBlock; ++i) v[i] = r0 + i < rend ? ld1(x + (r0 + i) * C + c) : 0.0f;
+  for (int i = 0; i < kMxBlock; ++i) {
+    float t[kColwiseCols] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (r0 + i < rend) ld4col(x + (r0 + i) * C + c0, t);
+#pragma unroll
+    for (int j = 0; j < kColwiseCols; ++j) v[j][i] = t[j];
+  }
   const size_t base = (size_t)C * (size_t)s_po[e];
-  const uint32_t b = mx_encode(v, qT + base + (size_t)c * (size_t)rp + (size_t)j0);
-  sfT[base / kMxBlock + (size_t)c * (size_t)(rp / kMxBlock) + (size_t)(j0 / kMxBlock)] = (uint8_t)b;
+#pragma unroll
+  for (int j = 0; j < kColwiseCols; ++j) {
+    const size_t c = (size_t)(c0 + j);
+    const uint32_t b = mx_encode(v[j], qT + base + c * (size_t)rp + (size_t)j0);
+    sfT[base / kMxBlock + c * (size_t)(rp / kMxBlock) + (size_t)(j0 / kMxBlock)] = (uint8_t)b;
+  }
 }
 
 template <typename Src>
@@ -861,7 +884,8 @@ hipError_t launch_mx_colwise_bf16(const uint16_t *x, int rows, int C, const int 
   // chunks of 128 padded rows: at most (rows + E * 127) / 128 of them
   const long long chunks = ((long long)rows + (long long)E * (kMxRowPad - 1)) / kMxRowPad;
   if (chunks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(mx_colwise_kernel<uint16_t>, dim3((unsigned)(C / 64), (unsigned)chunks),
+  hipLaunchKernelGGL(mx_colwise_kernel<uint16_t>,
+                     dim3((unsigned)((C / kColwiseCols + 63) / 64), (unsigned)chunks),
                      dim3(kThreads), 0, s, x, C, m_offsets, E, 0, qT, sfT);
   return hipGetLastError();
 }
@@ -870,7 +894,8 @@ hipError_t launch_mx_colwise_weights(const float *w, int E, int N, int K, uint8_
                                      uint8_t *sfT, hipStream_t s) {
   // w [E, N, K] as E segments of N rows (N % 128 == 0) and K columns
   const long long chunks = (long long)E * N / kMxRowPad;
-  hipLaunchKernelGGL(mx_colwise_kernel<float>, dim3((unsigned)(K / 64), (unsigned)chunks),
+  hipLaunchKernelGGL(mx_colwise_kernel<float>,
+                     dim3((unsigned)((K / kColwiseCols + 63) / 64), (unsigned)chunks),
                      dim3(kThreads), 0, s, w, K, nullptr, E, N, qT, sfT);
   return hipGetLastError();
 }

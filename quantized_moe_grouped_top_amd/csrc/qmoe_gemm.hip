@@ -1452,11 +1452,18 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
   const int my_xcc = (int)(__builtin_amdgcn_s_getreg(kHwRegXccId) & (kXcds - 1));
   __shared__ int s_next;
   const int S = M * top_k;
+  // thread 0 claims a tile's successor (from the same queue) just before the
+  // tile's epilogue, so that the atomic's latency passes while the epilogue
+  // runs; -1: nothing claimed ahead
+  int ahead = -1;
   for (int qx = 0; qx < kXcds; ++qx) {
   const int xq = (my_xcc + qx) & (kXcds - 1);
   const int n_x = min(chunk, total - xq * chunk);
   for (;;) {
-  if (tid == 0) s_next = n_x > 0 ? (int)atomicAdd(&g_tile_next[launch_slot][xq], 1u) : n_x;
+  if (tid == 0) {
+    s_next = ahead >= 0 ? ahead : (n_x > 0 ? (int)atomicAdd(&g_tile_next[launch_slot][xq], 1u) : n_x);
+    ahead = -1;
+  }
   __syncthreads();
   const int tile_t = s_next;
   __syncthreads();                                      // (s_next is rewritten next round)
@@ -1723,6 +1730,7 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
   // of row r at c ^ (r & 15)) -> whole 256-byte row segments in HBM.  Only
   // the wavefront itself reads its staging area, so no workgroup barrier.
   __syncthreads();                                      // the ring is no longer read
+  if (tid == 0) ahead = (int)atomicAdd(&g_tile_next[launch_slot][xq], 1u);
   if (busy) {
   uint8_t *stg = s_ring + kHStage + wave * 16384;
   const bool vec = (N & 7) == 0 && ((uintptr_t)out & 15u) == 0;

@@ -203,6 +203,44 @@ def test_routed_all_tokens_one_expert(fmt, block_m, layout):
     run_routed(wl, block_m=block_m, full=True, logits=lg, layout=layout)
 
 
+# the routing limits: the most experts and the largest top_k the library takes
+LIMITS = [synth.small("fp8", 300, 128, 64, qm.MOE_MAX_EXPERTS, qm.MOE_MAX_TOPK),
+          synth.small("int8", 70, 128, 64, qm.MOE_MAX_EXPERTS, qm.MOE_MAX_TOPK)]
+
+
+@pytest.mark.parametrize("block_m", [16, 128])
+@pytest.mark.parametrize("wl", LIMITS, ids=[w.name for w in LIMITS])
+def test_routed_limits(wl, block_m):
+    run_routed(wl, block_m=block_m, full=True, layout=qm.MOE_W_ROWMAJOR)
+
+
+@pytest.mark.parametrize("block_m", [16, 128])
+def test_routed_tied_logits(block_m):
+    """All logits equal: the lower expert index wins every tie, router
+    weights are 1/top_k."""
+    wl = synth.small("fp8", 90, 128, 64, 8, 3)
+    run_routed(wl, block_m=block_m, full=True, logits=torch.zeros(90, 8))
+
+
+@pytest.mark.parametrize("block_m", [16, 128])
+def test_align_most_slots(block_m):
+    """The largest slot count (M * top_k = MOE_MAX_SLOTS): routing and block
+    alignment bit-exact against the oracle."""
+    _announce(f"align M*top_k = {qm.MOE_MAX_SLOTS} block_m={block_m}")
+    E, top_k = 8, 2
+    M = qm.MOE_MAX_SLOTS // top_k
+    lg = synth.make_logits(M, E, synth.seed_of("most slots"), 0.5, DEV)
+    moe = runner.RoutedMoE("fp8", M, 128, 64, E, top_k, block_m=block_m)
+    moe.route(lg)
+    torch.cuda.synchronize()
+    ids_ref, _ = O.route_topk(lg.cpu().numpy(), top_k)
+    np.testing.assert_array_equal(moe.topk_ids.cpu().numpy(), ids_ref)
+    s_ref, e_ref, n_ref = O.align_block_size(ids_ref, E, block_m)
+    assert int(moe.num_tokens_post_padded.item()) == n_ref
+    np.testing.assert_array_equal(moe.sorted_token_ids.cpu().numpy(), s_ref)
+    np.testing.assert_array_equal(moe.expert_ids.cpu().numpy(), e_ref)
+
+
 def test_routed_empty_batch():
     _announce("M = 0")
     moe = runner.RoutedMoE("fp8", 0, 128, 64, 8, 2, block_m=16)

@@ -164,16 +164,17 @@ constexpr int kSMaxTiles = 7;    // tiles per workgroup
 constexpr int kSK = 128;         // k per stage
 constexpr int kSGroups = 4;      // 16-row weight groups per wavefront
 
-template <bool kInt8>
+template <bool kInt8, int kMB>
 struct SCfg {
   // weight stages held in registers per wavefront (loads run up to kD stages
-  // ahead of the MFMAs); the bf16 path needs more registers for its operands
-  // (with three stages there it runs slower, measured)
-  static constexpr int kD = kInt8 ? 2 : 3;
+  // ahead of the MFMAs); the bf16 path with 64 rows per pass needs the
+  // registers of the third stage for its operands (with three stages and
+  // those operands it runs slower, measured)
+  static constexpr int kD = (kInt8 && kMB > 2) ? 2 : 3;
   static constexpr int kAS = kD + 1;                        // activation ring slots
   static constexpr int kSub = kInt8 ? 64 : 128;            // k per MFMA sub-step
   static constexpr int kARow = kInt8 ? 2 * kSK : kSK;       // activation bytes per row per stage
-  static constexpr int kABytes = 16 * kSMB * kARow;         // one ring slot
+  static constexpr int kABytes = 16 * kMB * kARow;          // one ring slot
   static constexpr int kAInstr = kABytes / 1024;            // DMA instructions for the rows
 };
 
@@ -240,7 +241,7 @@ __device__ __forceinline__ i32x4 int4x8_to_bf16x8(uint32_t d) {
 }
 constexpr float kInt4Offset = 136.0f;
 
-template <int kMode, int kLayout>
+template <int kMode, int kLayout, int kMB>
 __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
     const uint8_t *__restrict__ a, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ w, const float *__restrict__ w_scale,
@@ -252,14 +253,14 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
   constexpr bool kI8 = kMode == kSI8;                    // int8 activations and weights
   constexpr bool kW4 = kMode == kSW4A16;                 // int4 weights: 64 bytes per row per stage
   constexpr int kP = kW4 ? 1 : 2;                        // 16-byte weight pieces per group and stage
-  using C = SCfg<kInt8>;
+  using C = SCfg<kInt8, kMB>;
   constexpr int kSD = kW4 ? 3 : C::kD, kSAS = kSD + 1;
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kSAS * C::kABytes];
-  __shared__ int s_slot[kSMB * 16];
+  __shared__ int s_slot[kMB * 16];
   __shared__ int s_nvalid;
   __shared__ float s_scale[kSMaxTiles * 64];
-  __shared__ float s_rw[kSMB * 16];
-  __shared__ float s_A[kSMB * 16];                       // int4: activation row sums
+  __shared__ float s_rw[kMB * 16];
+  __shared__ float s_A[kMB * 16];                       // int4: activation row sums
 
   const int e = blockIdx.x / groups;
   const int grp = blockIdx.x - e * groups;
@@ -417,8 +418,8 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
     return;
   }
 
-  for (int bp = b_begin, pass_ = 0; bp < b_end; bp += kSMB, ++pass_) {
-    const int nmb = min(b_end - bp, kSMB);
+  for (int bp = b_begin, pass_ = 0; bp < b_end; bp += kMB, ++pass_) {
+    const int nmb = min(b_end - bp, kMB);
     __syncthreads();                                       // s_slot / ring reuse across passes
     int nvalid;                                            // rows holding a routed slot
     if (staged && pass_ == 0) {
@@ -426,8 +427,8 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
       const int *sorted = reinterpret_cast<const int *>(s_ring + C::kABytes);
       int slot = S;
       if (tid < nmb * 16) slot = sorted[bp * 16 + tid];
-      if (tid < kSMB * 16) s_slot[tid] = slot;
-      nvalid = __syncthreads_count(tid < kSMB * 16 && slot < S);
+      if (tid < kMB * 16) s_slot[tid] = slot;
+      nvalid = __syncthreads_count(tid < kMB * 16 && slot < S);
     } else {
       if (wave == 0) {                                     // slot ids, scalar
         typedef int int16v __attribute__((ext_vector_type(16)));
@@ -435,7 +436,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
         const cint16_ptr c_sorted16 = (cint16_ptr)sorted_ids;
         int nv = 0;
 #pragma unroll
-        for (int i = 0; i < kSMB; ++i) {
+        for (int i = 0; i < kMB; ++i) {
           int16v sl;
           if (i < nmb) {
             sl = c_sorted16[bp + i];                       // one 64-byte block of slots
@@ -456,7 +457,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
     }
     // router weight (x token scale) of each row, fetched now for the epilogue
     float rw_pre = 0.0f;
-    if (tid < kSMB * 16) {
+    if (tid < kMB * 16) {
       const int slot = s_slot[tid];
       if (slot < S) {
         rw_pre = topk_w[slot];
@@ -508,11 +509,11 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
       }
     };
 
-    f32x4 acc[kSGroups][kSMB];
+    f32x4 acc[kSGroups][kMB];
 #pragma unroll
     for (int u = 0; u < kSGroups; ++u)
 #pragma unroll
-      for (int i = 0; i < kSMB; ++i) acc[u][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < kMB; ++i) acc[u][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     f32x4 accA = f32x4{0.f, 0.f, 0.f, 0.f};               // int4: row sums of block `wave`
     auto compute = [&](int st, int ring, const i32x4 (&buf)[kSGroups][kP]) {
@@ -524,9 +525,9 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
         const i32x4 ones = {0x3F803F80, 0x3F803F80, 0x3F803F80, 0x3F803F80};
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          i32x4 av[kSMB];
+          i32x4 av[kMB];
 #pragma unroll
-          for (int i = 0; i < kSMB; ++i) {
+          for (int i = 0; i < kMB; ++i) {
             if (i >= nmb) break;
             av[i] = *reinterpret_cast<const i32x4 *>(sa + sw256(16 * i + r16, 4 * g + m));
             if (i == wave) accA = mfma_bf16(av[i], ones, accA);
@@ -536,7 +537,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
             if (wave + kSWaves * u >= ngr) break;          // wave-uniform
             const i32x4 b = int4x8_to_bf16x8((uint32_t)buf[u][0][m]);
 #pragma unroll
-            for (int i = 0; i < kSMB; ++i) {
+            for (int i = 0; i < kMB; ++i) {
               if (i >= nmb) break;
               acc[u][i] = mfma_bf16(av[i], b, acc[u][i]);
             }
@@ -550,9 +551,9 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
         if (ss >= nsub) break;
         if constexpr (kInt8) {
           const int c0 = 8 * ss + 2 * g;
-          i32x4 av[kSMB][2];
+          i32x4 av[kMB][2];
 #pragma unroll
-          for (int i = 0; i < kSMB; ++i) {
+          for (int i = 0; i < kMB; ++i) {
             if (i >= nmb) break;
             const int r = 16 * i + r16;
             av[i][0] = *reinterpret_cast<const i32x4 *>(sa + sw256(r, c0));
@@ -564,16 +565,16 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
             i32x4 b0, b1;
             dequant16w<kMode == kSF8W16>(buf[u][ss], b0, b1);
 #pragma unroll
-            for (int i = 0; i < kSMB; ++i) {
+            for (int i = 0; i < kMB; ++i) {
               if (i >= nmb) break;
               acc[u][i] = mfma_bf16(av[i][0], b0, acc[u][i]);
               acc[u][i] = mfma_bf16(av[i][1], b1, acc[u][i]);
             }
           }
         } else {
-          i32x8 av[kSMB];
+          i32x8 av[kMB];
 #pragma unroll
-          for (int i = 0; i < kSMB; ++i) {
+          for (int i = 0; i < kMB; ++i) {
             if (i >= nmb) break;
             const int r = 16 * i + r16;
             const i32x4 al = *reinterpret_cast<const i32x4 *>(sa + sw128(r, g));
@@ -585,7 +586,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
             if (wave + kSWaves * u >= ngr) break;          // wave-uniform
             const i32x8 bv = __builtin_shufflevector(buf[u][0], buf[u][1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-            for (int i = 0; i < kSMB; ++i) {
+            for (int i = 0; i < kMB; ++i) {
               if (i >= nmb) break;
               if constexpr (kI8) acc[u][i] = mfma_i8(av[i], bv, acc[u][i]);
               else acc[u][i] = mfma_fp8(av[i], bv, acc[u][i]);
@@ -637,7 +638,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
     // bf16 rows, then written out as whole 16-byte pieces of each routed
     // slot's row
     if (pass_ == 0 && tid < G * 64) s_scale[tid] = cs_pre;   // per-column (or fused) scale
-    if (tid < kSMB * 16) s_rw[tid] = rw_pre;
+    if (tid < kMB * 16) s_rw[tid] = rw_pre;
     if constexpr (kW4) {
       if (wave < nmb && r16 == 0) {                        // every column holds the row sum
 #pragma unroll
@@ -649,7 +650,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
     const int wcols = 64 * G;                              // columns of this workgroup
     const int pieces = wcols / 8;                          // 16-byte pieces per staged row
 #pragma unroll
-    for (int i = 0; i < kSMB; ++i) {
+    for (int i = 0; i < kMB; ++i) {
       if (i >= nmb) break;                                 // wave-uniform
 #pragma unroll
       for (int u = 0; u < kSGroups; ++u) {
@@ -1857,11 +1858,21 @@ uint32_t stream_weight_bytes(const RoutedArgs &r) {
   return (uint32_t)r.E * (uint32_t)r.N * (uint32_t)r.K;
 }
 
+template <int kMode, int kMB>
+decltype(&stream_kernel<kMode, MOE_W_ROWMAJOR, kMB>) stream_kernel_l(int layout) {
+  if (layout == MOE_W_FRAG) return stream_kernel<kMode, MOE_W_FRAG, kMB>;
+  if (layout == MOE_W_TILED) return stream_kernel<kMode, MOE_W_TILED, kMB>;
+  return stream_kernel<kMode, MOE_W_ROWMAJOR, kMB>;
+}
+// The bf16-activation paths take 32 rows per pass when the experts average
+// at most 16 routed rows (decode): the registers saved go to a third weight
+// stage in flight; an expert with more rows takes further passes.
+bool stream_two_blocks(const RoutedArgs &r) {
+  return (long long)r.M * r.top_k <= 16ll * r.E;
+}
 template <int kMode>
-decltype(&stream_kernel<kMode, MOE_W_ROWMAJOR>) stream_kernel_for(int layout) {
-  if (layout == MOE_W_FRAG) return stream_kernel<kMode, MOE_W_FRAG>;
-  if (layout == MOE_W_TILED) return stream_kernel<kMode, MOE_W_TILED>;
-  return stream_kernel<kMode, MOE_W_ROWMAJOR>;
+decltype(&stream_kernel<kMode, MOE_W_ROWMAJOR, kSMB>) stream_kernel_for(int layout, bool two) {
+  return two ? stream_kernel_l<kMode, 2>(layout) : stream_kernel_l<kMode, kSMB>(layout);
 }
 
 void stream_grid(int N, int E, int &groups, int &tiles_per_group) {
@@ -1878,7 +1889,7 @@ hipError_t launch_gemm_fp8(const uint8_t *a_q, const float *a_scale, const uint8
   if (r.block_m == 16) {
     int groups, tpg;
     stream_grid(r.N, r.E, groups, tpg);
-    auto k = stream_kernel_for<kSFp8>(r.w_layout);
+    auto k = stream_kernel_for<kSFp8>(r.w_layout, false);
     hipLaunchKernelGGL(k, dim3(r.E * groups), dim3(kSThreads), 0, s, a_q, a_scale, w_q, w_scale,
                        r.sorted_ids, r.expert_ids, r.num_post, r.topk_w, r.M, r.K, r.N, r.top_k,
                        groups, tpg, r.max_blocks, r.y, stream_weight_bytes(r));
@@ -1907,7 +1918,7 @@ hipError_t launch_gemm_int8w8a8(const int8_t *a_q, const float *a_scale, const i
   if (r.block_m == 16) {
     int groups, tpg;
     stream_grid(r.N, r.E, groups, tpg);
-    auto k = stream_kernel_for<kSI8>(r.w_layout);
+    auto k = stream_kernel_for<kSI8>(r.w_layout, false);
     hipLaunchKernelGGL(k, dim3(r.E * groups), dim3(kSThreads), 0, s, ab, a_scale, wb, w_scale,
                        r.sorted_ids, r.expert_ids, r.num_post, r.topk_w, r.M, r.K, r.N, r.top_k,
                        groups, tpg, r.max_blocks, r.y, stream_weight_bytes(r));
@@ -1927,7 +1938,7 @@ hipError_t launch_gemm_fp8w8a16(const uint16_t *a, const uint8_t *w_q, const flo
   if (r.block_m == 16) {
     int groups, tpg;
     stream_grid(r.N, r.E, groups, tpg);
-    auto k = stream_kernel_for<kSF8W16>(r.w_layout);
+    auto k = stream_kernel_for<kSF8W16>(r.w_layout, stream_two_blocks(r));
     hipLaunchKernelGGL(k, dim3(r.E * groups), dim3(kSThreads), 0, s, ab, nullptr, w_q, w_scale,
                        r.sorted_ids, r.expert_ids, r.num_post, r.topk_w, r.M, r.K, r.N, r.top_k,
                        groups, tpg, r.max_blocks, r.y, stream_weight_bytes(r));
@@ -1948,7 +1959,7 @@ hipError_t launch_gemm_int8(const uint16_t *a, const int8_t *w_q, const float *w
   if (r.block_m == 16) {
     int groups, tpg;
     stream_grid(r.N, r.E, groups, tpg);
-    auto k = stream_kernel_for<kSW8A16>(r.w_layout);
+    auto k = stream_kernel_for<kSW8A16>(r.w_layout, stream_two_blocks(r));
     hipLaunchKernelGGL(k, dim3(r.E * groups), dim3(kSThreads), 0, s, ab, nullptr, wb, w_scale,
                        r.sorted_ids, r.expert_ids, r.num_post, r.topk_w, r.M, r.K, r.N, r.top_k,
                        groups, tpg, r.max_blocks, r.y, stream_weight_bytes(r));
@@ -1972,8 +1983,7 @@ hipError_t launch_gemm_int4w16(const uint16_t *a, const uint8_t *w_q, const floa
   const uint32_t w_bytes = r.w_layout == MOE_W_FRAG
                                ? (uint32_t)r.E * (uint32_t)((r.N + 15) / 16) * ((half + 63u) / 64u) * 1024u
                                : (uint32_t)r.E * (uint32_t)r.N * half;
-  auto k = r.w_layout == MOE_W_FRAG ? stream_kernel<kSW4A16, MOE_W_FRAG>
-                                    : stream_kernel<kSW4A16, MOE_W_ROWMAJOR>;
+  auto k = stream_kernel_for<kSW4A16>(r.w_layout, stream_two_blocks(r));
   hipLaunchKernelGGL(k, dim3(r.E * groups), dim3(kSThreads), 0, s,
                      reinterpret_cast<const uint8_t *>(a), nullptr, w_q, w_scale, r.sorted_ids,
                      r.expert_ids, r.num_post, r.topk_w, r.M, r.K, r.N, r.top_k, groups, tpg,

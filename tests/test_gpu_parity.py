@@ -154,6 +154,10 @@ SMALL = [
     synth.small("int8dq", 37, 256, 200, 8, 2),
     synth.small("int8dq", 300, 384, 320, 8, 2, bias_std=1.5),
     synth.small("int8dq", 400, 256, 136, 2, 2),
+    # few rows per expert on average (32 rows per pass for bf16 activations)
+    # with a biased router, so that some experts need several passes
+    synth.small("int8", 60, 256, 136, 8, 2, bias_std=1.5),
+    synth.small("fp8wo", 60, 256, 136, 8, 2, bias_std=1.5),
     # bf16 activations x fp8 weights with per-channel scales
     synth.small("fp8wo", 50, 320, 136, 6, 3),
     synth.small("fp8wo", 300, 256, 272, 8, 2, bias_std=1.5),
@@ -185,6 +189,7 @@ INT4_SMALL = [
     synth.small("int4wo", 300, 256, 272, 8, 2, bias_std=1.5),   # several passes per expert
     synth.small("int4wo", 40, 128, 48, 1, 1),
     synth.small("int4wo", 1, 128, 64, 8, 2),
+    synth.small("int4wo", 60, 256, 136, 8, 2, bias_std=1.5),   # 32 rows per pass, several
 ]
 
 

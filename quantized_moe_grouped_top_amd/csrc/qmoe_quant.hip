@@ -294,26 +294,49 @@ __device__ __forceinline__ uint32_t mx_encode(const float *v, uint8_t *dst) {
 // column c, rows 32j .. 32j+31 of the padded segment form one block.  Output,
 // expert by expert (P_e = sum of Rp of the experts before e): codes at
 // C * P_e + c * Rp_e + row, scale bytes at C * P_e / 32 + c * Rp_e / 32 + j.
-// A workgroup takes 256 columns x 128 padded rows (one padded chunk of one
-// expert); thread (sb, cg) reads the 32 rows of its block for 4 neighbouring
-// columns (one 8- or 16-byte load per row, a row of the wavefront's 256
-// columns per load instruction), then encodes and writes the 4 columns'
-// blocks (32 contiguous codes each).
-constexpr int kColwiseCols = 4;                     // columns per thread
+// A workgroup takes one padded 128-row chunk of one expert x 64 columns: the
+// tile is read row by row (16 lanes x 8 or 16 bytes per row, coalesced) into
+// LDS transposed (a row of LDS per column), then thread (c, j) encodes block
+// j of column c from LDS and four neighbouring threads write the column's
+// 128 codes as one contiguous 128-byte run.
+constexpr int kColwiseCols = 64;                    // columns per workgroup
 
-__device__ __forceinline__ void ld4col(const uint16_t *p, float *v) {
-  const i32x2 r = *reinterpret_cast<const i32x2 *>(p);
-  v[0] = __builtin_bit_cast(float, (uint32_t)r[0] << 16);
-  v[1] = __builtin_bit_cast(float, (uint32_t)r[0] & 0xFFFF0000u);
-  v[2] = __builtin_bit_cast(float, (uint32_t)r[1] << 16);
-  v[3] = __builtin_bit_cast(float, (uint32_t)r[1] & 0xFFFF0000u);
+template <typename Src> struct ColwiseRaw;
+template <> struct ColwiseRaw<uint16_t> {
+  using Vec = i32x2;                                // 4 bf16 of one row
+  static constexpr int kPad = 8;                    // row stride 272 bytes (16-byte aligned)
+};
+template <> struct ColwiseRaw<float> {
+  using Vec = f32x4;                                // 4 floats of one row
+  static constexpr int kPad = 4;                    // row stride 528 bytes
+};
+__device__ __forceinline__ void put4(uint16_t (*t)[kMxRowPad + ColwiseRaw<uint16_t>::kPad], int c,
+                                     int r, const i32x2 &v) {
+  t[c][r] = (uint16_t)((uint32_t)v[0] & 0xFFFFu);
+  t[c + 1][r] = (uint16_t)((uint32_t)v[0] >> 16);
+  t[c + 2][r] = (uint16_t)((uint32_t)v[1] & 0xFFFFu);
+  t[c + 3][r] = (uint16_t)((uint32_t)v[1] >> 16);
 }
-__device__ __forceinline__ void ld4col(const float *p, float *v) {
-  const f32x4 r = *reinterpret_cast<const f32x4 *>(p);
-  v[0] = r[0];
-  v[1] = r[1];
-  v[2] = r[2];
-  v[3] = r[3];
+__device__ __forceinline__ void put4(float (*t)[kMxRowPad + ColwiseRaw<float>::kPad], int c, int r,
+                                     const f32x4 &v) {
+  t[c][r] = v[0];
+  t[c + 1][r] = v[1];
+  t[c + 2][r] = v[2];
+  t[c + 3][r] = v[3];
+}
+__device__ __forceinline__ void get32(const uint16_t *p, float *v) {   // 32 bf16, 16-byte aligned
+#pragma unroll
+  for (int i = 0; i < 4; ++i) unpack8(*reinterpret_cast<const i32x4 *>(p + 8 * i), v + 8 * i);
+}
+__device__ __forceinline__ void get32(const float *p, float *v) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const f32x4 q = *reinterpret_cast<const f32x4 *>(p + 4 * i);
+    v[4 * i] = q[0];
+    v[4 * i + 1] = q[1];
+    v[4 * i + 2] = q[2];
+    v[4 * i + 3] = q[3];
+  }
 }
 
 template <typename Src>
@@ -322,8 +345,11 @@ __global__ __launch_bounds__(kThreads) void mx_colwise_kernel(const Src *__restr
                                                               int E, int uniform_rows,
                                                               uint8_t *__restrict__ qT,
                                                               uint8_t *__restrict__ sfT) {
+  using R = ColwiseRaw<Src>;
+  static_assert(kThreads == 256, "64 columns x 4 blocks: one thread each");
   __shared__ long long s_po[kMaxExperts + 1];               // padded start of each expert
   __shared__ int s_mo[kMaxExperts + 1];
+  __shared__ __attribute__((aligned(16))) Src s_t[kColwiseCols][kMxRowPad + R::kPad];
   if (threadIdx.x == 0) {
     long long acc = 0;
     for (int e = 0; e <= E; ++e) {
@@ -338,30 +364,33 @@ __global__ __launch_bounds__(kThreads) void mx_colwise_kernel(const Src *__restr
   }
   __syncthreads();
   const long long pr = (long long)kMxRowPad * blockIdx.y;   // padded row of this chunk
-  if (pr >= s_po[E]) return;
+  if (pr >= s_po[E]) return;                                // (uniform over the workgroup)
   int e = 0;
   while (s_po[e + 1] <= pr) ++e;
   const long long rp = s_po[e + 1] - s_po[e];
-  const int c0 = (blockIdx.x * 64 + (threadIdx.x & 63)) * kColwiseCols;
-  if (c0 >= C) return;                                      // (C % 64: whole groups only)
-  const long long j0 = pr - s_po[e] + kMxBlock * (threadIdx.x >> 6);   // row in the padded segment
-  const long long r0 = s_mo[e] + j0;
+  const int c0 = blockIdx.x * kColwiseCols;
+  const long long row0 = s_mo[e] + (pr - s_po[e]);          // first data row of the chunk
   const long long rend = s_mo[e + 1];
-  float v[kColwiseCols][kMxBlock];
+  // load: row r = tid / 16 + 16 i, columns c0 + 4 (tid % 16) .. + 3
+  {
+    const int cg = 4 * (threadIdx.x & 15);
 #pragma unroll
-  for (int i = 0; i < kMxBlock; ++i) {
-    float t[kColwiseCols] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (r0 + i < rend) ld4col(x + (r0 + i) * C + c0, t);
-#pragma unroll
-    for (int j = 0; j < kColwiseCols; ++j) v[j][i] = t[j];
+    for (int i = 0; i < kMxRowPad / 16; ++i) {
+      const int r = (int)(threadIdx.x >> 4) + 16 * i;
+      typename R::Vec v{};
+      if (row0 + r < rend) v = *reinterpret_cast<const typename R::Vec *>(x + (row0 + r) * C + c0 + cg);
+      put4(s_t, cg, r, v);
+    }
   }
+  __syncthreads();
+  const int c = (int)(threadIdx.x >> 2), j = (int)(threadIdx.x & 3);
+  float v[kMxBlock];
+  get32(&s_t[c][kMxBlock * j], v);
   const size_t base = (size_t)C * (size_t)s_po[e];
-#pragma unroll
-  for (int j = 0; j < kColwiseCols; ++j) {
-    const size_t c = (size_t)(c0 + j);
-    const uint32_t b = mx_encode(v[j], qT + base + c * (size_t)rp + (size_t)j0);
-    sfT[base / kMxBlock + c * (size_t)(rp / kMxBlock) + (size_t)(j0 / kMxBlock)] = (uint8_t)b;
-  }
+  const size_t col = (size_t)(c0 + c);
+  const long long j0 = pr - s_po[e] + kMxBlock * j;          // row in the padded segment
+  const uint32_t b = mx_encode(v, qT + base + col * (size_t)rp + (size_t)j0);
+  sfT[base / kMxBlock + col * (size_t)(rp / kMxBlock) + (size_t)(j0 / kMxBlock)] = (uint8_t)b;
 }
 
 template <typename Src>
@@ -884,8 +913,7 @@ hipError_t launch_mx_colwise_bf16(const uint16_t *x, int rows, int C, const int 
   // chunks of 128 padded rows: at most (rows + E * 127) / 128 of them
   const long long chunks = ((long long)rows + (long long)E * (kMxRowPad - 1)) / kMxRowPad;
   if (chunks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(mx_colwise_kernel<uint16_t>,
-                     dim3((unsigned)((C / kColwiseCols + 63) / 64), (unsigned)chunks),
+  hipLaunchKernelGGL(mx_colwise_kernel<uint16_t>, dim3((unsigned)(C / kColwiseCols), (unsigned)chunks),
                      dim3(kThreads), 0, s, x, C, m_offsets, E, 0, qT, sfT);
   return hipGetLastError();
 }
@@ -894,8 +922,7 @@ hipError_t launch_mx_colwise_weights(const float *w, int E, int N, int K, uint8_
                                      uint8_t *sfT, hipStream_t s) {
   // w [E, N, K] as E segments of N rows (N % 128 == 0) and K columns
   const long long chunks = (long long)E * N / kMxRowPad;
-  hipLaunchKernelGGL(mx_colwise_kernel<float>,
-                     dim3((unsigned)((K / kColwiseCols + 63) / 64), (unsigned)chunks),
+  hipLaunchKernelGGL(mx_colwise_kernel<float>, dim3((unsigned)(K / kColwiseCols), (unsigned)chunks),
                      dim3(kThreads), 0, s, w, K, nullptr, E, N, qT, sfT);
   return hipGetLastError();
 }

@@ -423,7 +423,7 @@ int moe_quantize_act_colwise(const uint16_t *x, int rows, int C, const int *m_of
  * expert in HOST memory (the caller knows the split; no device read or
  * synchronisation is needed to size the launches).  dw [E, N, K] uint16 bf16,
  * 16-byte aligned, written in full.  N must be a multiple of 128 and K of
- * 64.  One MXFP8 grouped-linear launch per expert is enqueued on `stream`. */
+ * 64.  One launch covers every expert. */
 int moe_grouped_gemm_mxfp8_wgrad(const uint8_t *dyT_q, const uint8_t *dyT_sf,
                                  const uint8_t *xT_q, const uint8_t *xT_sf, const int *m_splits,
                                  int E, int N, int K, uint16_t *dw, hipStream_t stream);

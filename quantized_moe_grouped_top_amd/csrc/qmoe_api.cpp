@@ -444,21 +444,12 @@ int moe_grouped_gemm_mxfp8_wgrad(const uint8_t *dyT_q, const uint8_t *dyT_sf,
   }
   REQUIRE(total * (long long)(N > K ? N : K) < (1ll << 32), MOE_EUNSUPPORTED,
           "%s: the transposed operands must stay below 4 GiB", fn);
-  long long off = 0;                                      // padded rows of the experts before e
-  for (int e = 0; e < E; ++e) {
-    const long long rp = (m_splits[e] + 127) / 128 * 128;
-    uint16_t *out = dw + (size_t)e * (size_t)N * (size_t)K;
-    hipError_t err;
-    if (rp == 0) {                                        // no rows: the gradient is zero
-      err = qmoe::launch_fill_u16(out, (long long)N * K, 0, stream);
-    } else {
-      err = qmoe::launch_gemm_mxfp8(dyT_q + (size_t)N * off, dyT_sf + (size_t)N * off / 32,
-                                    xT_q + (size_t)K * off, xT_sf + (size_t)K * off / 32, nullptr,
-                                    N, (int)rp, K, 1, out, stream);
-    }
-    if (err != hipSuccess) return hip_status(err, fn);
-    off += rp;
-  }
+  int po[MOE_MAX_EXPERTS + 1];                            // padded row offsets (host)
+  po[0] = 0;
+  for (int e = 0; e < E; ++e) po[e + 1] = po[e] + (m_splits[e] + 127) / 128 * 128;
+  const hipError_t err =
+      qmoe::launch_gemm_mxfp8_wgrad(dyT_q, dyT_sf, xT_q, xT_sf, po, E, N, K, dw, stream);
+  if (err != hipSuccess) return hip_status(err, fn);
   return ok();
 }
 

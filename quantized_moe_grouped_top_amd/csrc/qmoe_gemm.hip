@@ -683,7 +683,13 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
   }
 }
 
-enum { kFmtFp8 = 0, kFmtInt8 = 1, kFmtMx = 2, kFmtI8 = 3, kFmtF8W16 = 4 };
+enum { kFmtFp8 = 0, kFmtInt8 = 1, kFmtMx = 2, kFmtI8 = 3, kFmtF8W16 = 4, kFmtMxW = 5 };
+
+// MXFP8 weight gradient: the padded row offset of every expert's columnwise
+// operands (P_e; P_E is the total), passed by value
+struct WgradSeg {
+  int po[kMaxExperts + 1];
+};
 
 // =============================================================================
 // block_m = 128 (fp8 W8A8, int8 W8A16) and MXFP8: DMA-fed MFMA tiles
@@ -1395,8 +1401,14 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
     const float *__restrict__ w_scale, const uint8_t *__restrict__ w_sf,
     const int *__restrict__ sorted_ids, const int *__restrict__ expert_ids,
     const float *__restrict__ topk_w, const int *__restrict__ m_offsets, int M, int K, int N,
-    int E, int top_k, int max_blocks, uint16_t *__restrict__ out, int launch_slot) {
-  constexpr bool kMx = kFmt == kFmtMx;
+    int E, int top_k, int max_blocks, uint16_t *__restrict__ out, int launch_slot,
+    WgradSeg seg) {
+  // kFmtMxW, the weight gradient of the MXFP8 grouped linear: expert e's
+  // output rows are e*M .. e*M + M - 1 (dW_e [M, N]), its contraction runs
+  // over its Ke = seg.po[e+1] - seg.po[e] padded rows; operand rows are Ke
+  // bytes long, expert e's A block at M * P_e, its B block at N * P_e
+  constexpr bool kW = kFmt == kFmtMxW;
+  constexpr bool kMx = kFmt == kFmtMx || kW;
   static_assert(kFmt != kFmtInt8, "int8 W8A16 uses gemm_kernel");
   constexpr int kWaves = 4;
   constexpr int kThr = 64 * kWaves;
@@ -1427,9 +1439,15 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
     for (int ee = 0; ee < E; ++ee) {
       int nb;
       if constexpr (kMx) {
-        // no m_offsets: one segment of all M rows (a single expert)
-        s_mo[ee] = m_offsets ? m_offsets[ee] : 0;
-        s_mo[ee + 1] = m_offsets ? m_offsets[ee + 1] : M;
+        // no m_offsets: one segment of all M rows (a single expert); the
+        // weight gradient: M rows per expert
+        if constexpr (kW) {
+          s_mo[ee] = ee * M;
+          s_mo[ee + 1] = (ee + 1) * M;
+        } else {
+          s_mo[ee] = m_offsets ? m_offsets[ee] : 0;
+          s_mo[ee + 1] = m_offsets ? m_offsets[ee + 1] : M;
+        }
         const int m = s_mo[ee + 1] - s_mo[ee];
         nb = m > 0 ? (m + kGBM - 1) / kGBM : 0;
         s_blk_first[ee] = blk;
@@ -1520,12 +1538,17 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
 
   // ---- DMA sources of this lane (as gemm_big_kernel) -------------------------
   const uint32_t lds_ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)s_ring;
-  const int nst = K / 128;
+  // the contraction of this tile: K, or the expert's padded rows (weight gradient)
+  const int Ke = kW ? seg.po[e + 1] - seg.po[e] : K;
+  const int nst = Ke / 128;
+  const uint32_t pe = kW ? (uint32_t)seg.po[e] : 0u;
   uint32_t a_off[kDma];
 #pragma unroll
   for (int u = 0; u < kDma; ++u) {
     const int r = 8 * (kDma * wave + u) + (lane >> 3);
-    a_off[u] = src_row(r) * (uint32_t)K + 16u * (uint32_t)((lane & 7) ^ swz(r));
+    const uint32_t chunk = 16u * (uint32_t)((lane & 7) ^ swz(r));
+    if constexpr (kW) a_off[u] = (uint32_t)M * pe + (src_row(r) - (uint32_t)s_mo[e]) * (uint32_t)Ke + chunk;
+    else a_off[u] = src_row(r) * (uint32_t)K + chunk;
   }
   // weights: wave w loads the 64-column block w of the tile, 8 x 1 KB
   uint32_t wblk = 0;
@@ -1539,14 +1562,15 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
     for (int u = 0; u < kDma; ++u) {
       const int n = 8 * u + (lane >> 3);
       const int col = min(n0 + wave * 64 + n, N - 1);
-      b_off[u] = ((uint32_t)e * (uint32_t)N + (uint32_t)col) * (uint32_t)K +
-                 16u * (uint32_t)((lane & 7) ^ swz(n));
+      const uint32_t chunk = 16u * (uint32_t)((lane & 7) ^ swz(n));
+      if constexpr (kW) b_off[u] = (uint32_t)N * pe + (uint32_t)col * (uint32_t)Ke + chunk;
+      else b_off[u] = ((uint32_t)e * (uint32_t)N + (uint32_t)col) * (uint32_t)K + chunk;
     }
   }
   // MXFP8 scales: 8 dword DMAs per stage (rows 0-255, then columns 0-255, 64
   // per DMA), two per wavefront
   constexpr int kSfPerWave = 8 / kWaves;
-  const uint32_t kb_row = (uint32_t)K / 32u;
+  const uint32_t kb_row = (uint32_t)Ke / 32u;
   uint32_t sf_off[kSfPerWave];
   bool sf_on[kSfPerWave];
   if constexpr (kMx) {
@@ -1556,10 +1580,14 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
     for (int u = 0; u < kSfPerWave; ++u) {
       const int q = kSfPerWave * wave + u;             // 0-3 rows, 4-7 columns
       if (q < 4) {
-        sf_off[u] = ((uint32_t)po + src_row(64 * q + lane) - (uint32_t)s_mo[e]) * kb_row;
+        const uint32_t rr = src_row(64 * q + lane) - (uint32_t)s_mo[e];
+        if constexpr (kW) sf_off[u] = (uint32_t)M * pe / 32u + rr * kb_row;
+        else sf_off[u] = ((uint32_t)po + rr) * kb_row;
         sf_on[u] = (64 * q) / kGBM < nb_here;
       } else {
-        sf_off[u] = ((uint32_t)e * (uint32_t)N + (uint32_t)min(n0 + 64 * (q - 4) + lane, N - 1)) * kb_row;
+        const uint32_t cc = (uint32_t)min(n0 + 64 * (q - 4) + lane, N - 1);
+        if constexpr (kW) sf_off[u] = (uint32_t)N * pe / 32u + cc * kb_row;
+        else sf_off[u] = ((uint32_t)e * (uint32_t)N + cc) * kb_row;
         sf_on[u] = true;
       }
     }
@@ -1670,6 +1698,7 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
   // the rate the memory pipeline takes them at).  A wavefront whose 128 rows
   // do not exist (the tile's second block is missing) computes on stale LDS
   // rows and drops the results, so every wavefront runs the same stream.
+  if (!kW || nst > 0) {                                 // (an expert without rows: zeros)
   Frags fa, fb;
   issue(0, 0);
   if (nst > 1) {
@@ -1724,6 +1753,7 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
 #pragma unroll
     for (int q = 0; q < 16; ++q) mfma_q(fb, q);
   }
+  }  // stages
   wait_dma_all();                                       // the reload must land before the ring is reused
 
   // ---- epilogue: per wavefront, in two halves of 64 rows: bf16 results ->
@@ -1899,7 +1929,7 @@ hipError_t launch_gemm_fp8(const uint8_t *a_q, const float *a_scale, const uint8
       auto k = r.w_layout ? gemm_wide_kernel<kFmtFp8, true> : gemm_wide_kernel<kFmtFp8, false>;
       hipLaunchKernelGGL(k, dim3(wide_grid(tiles)), dim3(256), 0, s, a_q, a_scale, nullptr, w_q,
                          w_scale, nullptr, r.sorted_ids, r.expert_ids, r.topk_w, nullptr, r.M,
-                         r.K, r.N, r.E, r.top_k, r.max_blocks, r.y, next_launch_slot());
+                         r.K, r.N, r.E, r.top_k, r.max_blocks, r.y, next_launch_slot(), WgradSeg{});
     } else {
       auto k = r.w_layout ? gemm_big_kernel<kFmtFp8, true, kHWaves>
                           : gemm_big_kernel<kFmtFp8, false, kHWaves>;
@@ -1927,7 +1957,7 @@ hipError_t launch_gemm_int8w8a8(const int8_t *a_q, const float *a_scale, const i
     auto k = r.w_layout ? gemm_wide_kernel<kFmtI8, true> : gemm_wide_kernel<kFmtI8, false>;
     hipLaunchKernelGGL(k, dim3(wide_grid(tiles)), dim3(256), 0, s, ab, a_scale, nullptr, wb,
                        w_scale, nullptr, r.sorted_ids, r.expert_ids, r.topk_w, nullptr, r.M, r.K,
-                       r.N, r.E, r.top_k, r.max_blocks, r.y, next_launch_slot());
+                       r.N, r.E, r.top_k, r.max_blocks, r.y, next_launch_slot(), WgradSeg{});
   }
   return hipGetLastError();
 }
@@ -1991,6 +2021,20 @@ hipError_t launch_gemm_int4w16(const uint16_t *a, const uint8_t *w_q, const floa
   return hipGetLastError();
 }
 
+hipError_t launch_gemm_mxfp8_wgrad(const uint8_t *dyT_q, const uint8_t *dyT_sf, const uint8_t *xT_q,
+                                   const uint8_t *xT_sf, const int *padded_offsets, int E, int N,
+                                   int K, uint16_t *dw, hipStream_t s) {
+  WgradSeg seg{};
+  for (int e = 0; e <= E; ++e) seg.po[e] = padded_offsets[e];
+  // per expert ceil(N / 128) row blocks, in pairs, times ceil(K / 256) column tiles
+  const long long pairs = (long long)E * (((N + kGBM - 1) / kGBM + 1) / 2);
+  const long long tiles = pairs * ((K + kHBN - 1) / kHBN);
+  hipLaunchKernelGGL((gemm_wide_kernel<kFmtMxW, false>), dim3(wide_grid(tiles)), dim3(256), 0, s,
+                     dyT_q, nullptr, dyT_sf, xT_q, nullptr, xT_sf, nullptr, nullptr, nullptr, nullptr,
+                     N, 0, K, E, 1, 0, dw, next_launch_slot(), seg);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_mxfp8(const uint8_t *a_q, const uint8_t *a_sf, const uint8_t *w_q,
                              const uint8_t *w_sf, const int *m_offsets, int rows, int K, int N,
                              int E, uint16_t *out, hipStream_t s) {
@@ -1999,7 +2043,7 @@ hipError_t launch_gemm_mxfp8(const uint8_t *a_q, const uint8_t *a_sf, const uint
   const long long tiles = pairs * ((N + kHBN - 1) / kHBN);
   hipLaunchKernelGGL((gemm_wide_kernel<kFmtMx, false>), dim3(wide_grid(tiles)), dim3(256), 0, s,
                      a_q, nullptr, a_sf, w_q, nullptr, w_sf, nullptr, nullptr, nullptr, m_offsets,
-                     rows, K, N, E, 1, 0, out, next_launch_slot());
+                     rows, K, N, E, 1, 0, out, next_launch_slot(), WgradSeg{});
   return hipGetLastError();
 }
 

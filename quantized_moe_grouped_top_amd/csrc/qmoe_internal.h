@@ -93,6 +93,9 @@ hipError_t launch_gemm_fp8(const uint8_t *a_q, const float *a_scale, const uint8
                            const float *w_scale, const RoutedArgs &r, hipStream_t s);
 hipError_t launch_gemm_int8(const uint16_t *a, const int8_t *w_q, const float *w_scale,
                             const RoutedArgs &r, hipStream_t s);
+hipError_t launch_gemm_mxfp8_wgrad(const uint8_t *dyT_q, const uint8_t *dyT_sf, const uint8_t *xT_q,
+                                   const uint8_t *xT_sf, const int *padded_offsets, int E, int N,
+                                   int K, uint16_t *dw, hipStream_t s);
 hipError_t launch_gemm_int4w16(const uint16_t *a, const uint8_t *w_q, const float *w_scale,
                                const RoutedArgs &r, hipStream_t s);
 hipError_t launch_gemm_fp8w8a16(const uint16_t *a, const uint8_t *w_q, const float *w_scale,
@@ -107,7 +110,6 @@ hipError_t launch_mx_colwise_bf16(const uint16_t *x, int rows, int C, const int 
                                   int E, uint8_t *qT, uint8_t *sfT, hipStream_t s);
 hipError_t launch_mx_colwise_weights(const float *w, int E, int N, int K, uint8_t *qT,
                                      uint8_t *sfT, hipStream_t s);
-hipError_t launch_fill_u16(uint16_t *p, long long n, uint16_t v, hipStream_t s);
 hipError_t launch_pack_weights(const uint8_t *w, int E, int N, int K, int layout, uint8_t *packed,
                                hipStream_t s);
 

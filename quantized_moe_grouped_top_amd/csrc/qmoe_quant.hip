@@ -927,18 +927,6 @@ hipError_t launch_mx_colwise_weights(const float *w, int E, int N, int K, uint8_
   return hipGetLastError();
 }
 
-__global__ __launch_bounds__(kThreads) void fill_u16_kernel(uint16_t *__restrict__ p, long long n,
-                                                            uint16_t v) {
-  for (long long i = blockIdx.x * (long long)kThreads + threadIdx.x; i < n;
-       i += (long long)gridDim.x * kThreads)
-    p[i] = v;
-}
-
-hipError_t launch_fill_u16(uint16_t *p, long long n, uint16_t v, hipStream_t s) {
-  hipLaunchKernelGGL(fill_u16_kernel, dim3(grid_for(n, 16384)), dim3(kThreads), 0, s, p, n, v);
-  return hipGetLastError();
-}
-
 hipError_t launch_pack_weights(const uint8_t *w, int E, int N, int K, int layout,
                                uint8_t *packed, hipStream_t s) {
   if (layout == MOE_W_FRAG) {

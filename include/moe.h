@@ -252,7 +252,10 @@ int moe_quantize_weights(const float *w, int E, int N, int K, int mode,
  * MOE_W_FRAG (for block_m 16): the weights of expert e are cut into 16-row
  * groups j = n / 16 (J = ceil(N/16)) and 64-byte k blocks b = k / 64
  * (B = ceil(K/64)); the 1024-byte block (e, j, b) is stored at byte offset
- * ((e*J + j)*B + b) * 1024, and its 16-byte piece p = 16*q + r (q = 0..3,
+ * ((e*B + b)*J + j) * 1024 (k block outside row group: at any moment the
+ * workgroups streaming one expert read one contiguous stretch of it, which
+ * spreads the reads evenly over the HBM channels), and its 16-byte piece
+ * p = 16*q + r (q = 0..3,
  * r = 0..15) holds row n = 16j + r, k = 64b + 16q .. 64b + 16q + 15.  This is
  * the order in which the 64 lanes of a wavefront take one MFMA operand
  * fragment (lane p: row r, k group q), so each fragment is one contiguous

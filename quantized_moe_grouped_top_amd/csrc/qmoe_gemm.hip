@@ -317,17 +317,17 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
       voff[u][0] = row + (uint32_t)((g ^ swz(r16)) << 4);         // (swz(16q + r) = swz(r))
       voff[u][1] = row + (uint32_t)(((g + 4) ^ swz(r16)) << 4);
     } else {
-      const uint32_t blk = ((uint32_t)e * (uint32_t)N16 + (uint32_t)min(n >> 4, N16 - 1)) *
-                           (uint32_t)KB * 1024u + 16u * (uint32_t)lane;
+      const uint32_t blk = ((uint32_t)e * (uint32_t)KB * (uint32_t)N16 +
+                            (uint32_t)min(n >> 4, N16 - 1)) * 1024u + 16u * (uint32_t)lane;
       voff[u][0] = blk;
-      voff[u][1] = blk + 1024u;
+      voff[u][1] = blk + (uint32_t)N16 * 1024u;
     }
   }
   // byte offset of stage st, the same for every lane
   auto st_off = [&](int st) -> int {
     if constexpr (kLayout == MOE_W_ROWMAJOR) return (kW4 ? kSK / 2 : kSK) * st;
     else if constexpr (kLayout == MOE_W_TILED) return 8192 * st;
-    else return (kW4 ? 1024 : 2048) * st;
+    else return (kW4 ? 1024 : 2048) * N16 * st;
   };
   i32x4 wb[kSD][kSGroups][kP];
   auto load_w = [&](int st, i32x4 (&buf)[kSGroups][kP]) {

@@ -758,8 +758,8 @@ __global__ __launch_bounds__(kThreads) void pack_weights_kernel(const uint8_t *_
 }
 
 // ---- MOE_W_FRAG: one thread per 16-byte piece ----------------------------
-// Block (e, j, b) of 1 KB, piece p = 16q + r holding row 16j + r, k = 64b +
-// 16q .. +15; rows >= N and k >= K are zero.
+// Block (e, j, b) of 1 KB at ((e B + b) J + j) KB, piece p = 16q + r holding
+// row 16j + r, k = 64b + 16q .. +15; rows >= N and k >= K are zero.
 __global__ __launch_bounds__(kThreads) void pack_frag_kernel(const uint8_t *__restrict__ w, int E,
                                                              int N, int K,
                                                              uint8_t *__restrict__ packed) {
@@ -769,8 +769,8 @@ __global__ __launch_bounds__(kThreads) void pack_frag_kernel(const uint8_t *__re
        i += (long long)gridDim.x * kThreads) {
     const long long blk = i >> 6;
     const int p = (int)(i & 63);
-    const int b = (int)(blk % B);
-    const int j = (int)((blk / B) % J);
+    const int j = (int)(blk % J);
+    const int b = (int)((blk / J) % B);
     const int e = (int)(blk / ((long long)B * J));
     const int n = 16 * j + (p & 15);
     const int k0 = 64 * b + 16 * (p >> 4);

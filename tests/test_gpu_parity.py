@@ -319,8 +319,8 @@ def _pack_frag_reference(w, N, K):
     J, B = -(-N // 16), -(-K // 64)
     pad = np.zeros((E, J * 16, B * 64), np.uint8)
     pad[:, :N, :K] = w
-    # [e, j, r, b, q, i] (n = 16j + r, k = 64b + 16q + i) -> [e, j, b, q, r, i]
-    return pad.reshape(E, J, 16, B, 4, 16).transpose(0, 1, 3, 4, 2, 5).reshape(-1)
+    # [e, j, r, b, q, i] (n = 16j + r, k = 64b + 16q + i) -> [e, b, j, q, r, i]
+    return pad.reshape(E, J, 16, B, 4, 16).transpose(0, 3, 1, 4, 2, 5).reshape(-1)
 
 
 def _pack_reference(w, N, K):

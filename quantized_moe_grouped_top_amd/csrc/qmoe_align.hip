@@ -4,12 +4,16 @@
 // The alignment produces the layout the grouped GEMMs consume: the slots
 // i = t*top_k + j grouped by expert, each group padded to a multiple of
 // block_m, and the expert of every block of block_m sorted slots.  The sort is
-// a stable counting sort: per chunk of 1024 slots, one wavefront ballot per
-// expert gives each slot its rank among the slots of its expert inside its
-// wavefront (mbcnt over the ballot mask), a prefix scan over the 16 wavefront
-// counts gives the wavefront offsets, and a running count per expert carries
-// the offsets across chunks.  Slot order inside an expert is therefore the
-// ascending slot order.
+// a stable counting sort with no workgroup barrier inside its loops: each
+// wavefront owns a contiguous range of slots.  For 64 slots at a time, one
+// ballot per bit of the expert index gives every lane the mask of the lanes
+// holding the same expert (its peers); mbcnt over that mask is the lane's rank
+// among them, and the lowest peer alone updates the expert's entry in LDS
+// (the leaders of one instruction hold distinct experts, so their updates do
+// not collide).  A first walk counts each wavefront's slots per expert, a scan
+// turns the counts into every wavefront's first position per expert, and a
+// second walk hands out the positions.  Slot order inside an expert is
+// therefore the ascending slot order.
 #include "qmoe_internal.h"
 
 namespace qmoe {
@@ -25,6 +29,92 @@ __device__ __forceinline__ int lane_rank(unsigned long long mask) {
                                    __builtin_amdgcn_mbcnt_lo((unsigned)mask, 0u));
 }
 
+// Top-k choice and router weights of the tokens t = tid, tid + kThreads, ...
+// with top_k = kK known at compile time.
+template <int kK>
+__device__ __forceinline__ void route_tokens(const float *__restrict__ logits, int M, int E,
+                                             int tid, int *__restrict__ topk_ids,
+                                             float *__restrict__ topk_w, uint8_t *s_eid) {
+  // four tokens per thread and round, the first eight logits of all four
+  // loaded before any is used (a lone workgroup waits out every load latency
+  // it does not overlap)
+  constexpr int kTok = 4;
+  for (int t0 = tid; t0 < M; t0 += kTok * kThreads) {
+    float first[kTok][8];
+#pragma unroll
+    for (int q = 0; q < kTok; ++q) {
+      const int t = t0 + q * kThreads;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) first[q][u] = (t < M && u < E) ? logits[(size_t)t * E + u] : 0.0f;
+    }
+#pragma unroll
+    for (int q = 0; q < kTok; ++q) {
+      const int t = t0 + q * kThreads;
+      if (t >= M) break;
+      const float *lg = logits + (size_t)t * E;
+      int ids[kK];
+      float val[kK];
+#pragma unroll
+      for (int j = 0; j < kK; ++j) {
+        ids[j] = 0;
+        val[j] = 0.0f;
+      }
+      int nfill = 0;
+      for (int e0 = 0; e0 < E; e0 += 8) {
+        float v8[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v8[u] = e0 == 0 ? first[q][u] : (e0 + u < E ? lg[e0 + u] : 0.0f);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (e0 + u >= E) break;
+          float cv = v8[u];
+          int ci = e0 + u;
+#pragma unroll
+          for (int j = 0; j < kK; ++j) {
+            if (j >= nfill || cv > val[j]) {   // place here, carry the old one down
+              const float tv = val[j];
+              const int ti = ids[j];
+              val[j] = cv;
+              ids[j] = ci;
+              cv = tv;
+              ci = ti;
+            }
+          }
+          nfill = min(nfill + 1, kK);
+        }
+      }
+      // weights: exp(l_j - l_max) / sum over the chosen experts
+      float ex[kK];
+      float sum = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kK; ++j) {
+        ex[j] = expf(val[j] - val[0]);
+        sum += ex[j];
+      }
+#pragma unroll
+      for (int j = 0; j < kK; ++j) {
+        const int i = t * kK + j;
+        topk_ids[i] = ids[j];
+        topk_w[i] = ex[j] / sum;
+        s_eid[i] = (uint8_t)ids[j];
+      }
+    }
+  }
+}
+
+// mask of the lanes whose `e` equals this lane's, among the lanes of `valid`
+// (one ballot per bit of an index below 2^nbits)
+__device__ __forceinline__ unsigned long long peer_mask(int e, int nbits,
+                                                        unsigned long long valid) {
+  unsigned long long peers = valid;
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const unsigned long long mb = __ballot(bit);
+    peers &= bit ? mb : ~mb;
+  }
+  return peers;
+}
+
 __global__ __launch_bounds__(kThreads) void route_align_kernel(
     const float *__restrict__ logits, int M, int E, int top_k, int block_m, int max_padded,
     int *__restrict__ topk_ids, float *__restrict__ topk_w, int *__restrict__ sorted_ids,
@@ -32,146 +122,125 @@ __global__ __launch_bounds__(kThreads) void route_align_kernel(
   __shared__ uint8_t s_eid[kMaxSlots];            // expert of every slot
   __shared__ int s_cnt[kMaxExperts];              // slots per expert
   __shared__ int s_off[kMaxExperts + 1];          // padded start of every expert
-  __shared__ int s_run[kMaxExperts];              // slots of each expert already placed
-  __shared__ int s_chunk[kMaxExperts];            // slots of each expert in this chunk
-  __shared__ int s_wcnt[kWaves][kMaxExperts];     // per-wavefront counts of a chunk
+  __shared__ int s_wcnt[kWaves][kMaxExperts];     // slots per wavefront range and expert
+  __shared__ int s_wpos[kWaves][kMaxExperts];     // next position per wavefront and expert
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int S = M * top_k;
 
-  for (int e = tid; e < E; e += kThreads) {
-    s_cnt[e] = 0;
-    s_run[e] = 0;
-  }
-  __syncthreads();
+  for (int x = tid; x < kWaves * kMaxExperts; x += kThreads) (&s_wcnt[0][0])[x] = 0;
 
   // ---- 1. top-k choice and router weights of every token -------------------
   // One pass over the token's logits keeps the top_k best (value descending;
   // on equal values the earlier expert stays, as a later one must be strictly
   // larger to move in) by insertion; logits are read 8 at a time so their
   // loads overlap.
-  for (int t = tid; t < M; t += kThreads) {
-    const float *lg = logits + (size_t)t * E;
-    int ids[kMaxTopK];
-    float val[kMaxTopK];
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      ids[j] = 0;
-      val[j] = 0.0f;
-    }
-    int nfill = 0;
-    for (int e0 = 0; e0 < E; e0 += 8) {
-      float v8[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v8[u] = e0 + u < E ? lg[e0 + u] : 0.0f;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (e0 + u >= E) break;
-        float cv = v8[u];
-        int ci = e0 + u;
-#pragma unroll
-        for (int j = 0; j < kMaxTopK; ++j) {
-          if (j < top_k && (j >= nfill || cv > val[j])) {   // place here, carry the old one down
-            const float tv = val[j];
-            const int ti = ids[j];
-            val[j] = cv;
-            ids[j] = ci;
-            cv = tv;
-            ci = ti;
-          }
-        }
-        nfill = min(nfill + 1, top_k);
-      }
-    }
-    // weights: exp(l_j - l_max) / sum over the chosen experts
-    float ex[kMaxTopK];
-    float sum = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      ex[j] = (j < top_k) ? expf(val[j] - val[0]) : 0.0f;
-      sum += ex[j];
-    }
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      if (j < top_k) {
-        const int i = t * top_k + j;
-        topk_ids[i] = ids[j];
-        topk_w[i] = ex[j] / sum;
-        s_eid[i] = (uint8_t)ids[j];
-        atomicAdd(&s_cnt[ids[j]], 1);
-      }
-    }
+  switch (top_k) {
+    case 1: route_tokens<1>(logits, M, E, tid, topk_ids, topk_w, s_eid); break;
+    case 2: route_tokens<2>(logits, M, E, tid, topk_ids, topk_w, s_eid); break;
+    case 3: route_tokens<3>(logits, M, E, tid, topk_ids, topk_w, s_eid); break;
+    case 4: route_tokens<4>(logits, M, E, tid, topk_ids, topk_w, s_eid); break;
+    case 5: route_tokens<5>(logits, M, E, tid, topk_ids, topk_w, s_eid); break;
+    case 6: route_tokens<6>(logits, M, E, tid, topk_ids, topk_w, s_eid); break;
+    case 7: route_tokens<7>(logits, M, E, tid, topk_ids, topk_w, s_eid); break;
+    default: route_tokens<kMaxTopK>(logits, M, E, tid, topk_ids, topk_w, s_eid); break;
   }
   __syncthreads();
 
-  // ---- 2. padded offsets of every expert --------------------------------------
-  if (tid == 0) {
-    int acc = 0;
-    for (int e = 0; e < E; ++e) {
-      s_off[e] = acc;
-      acc += (s_cnt[e] + block_m - 1) / block_m * block_m;
+  // ---- 2. slots per wavefront range and expert ---------------------------------
+  // Wavefront w owns slots [lo, hi).
+  const int per = ((S + kWaves - 1) / kWaves + 63) & ~63;
+  const int lo = min(wave * per, S), hi = min(lo + per, S);
+  const int nbits = E > 1 ? 32 - __builtin_clz((unsigned)(E - 1)) : 0;
+  for (int base = lo; base < hi; base += 64) {
+    const int i = base + lane;
+    const bool valid = i < hi;
+    const int my_e = valid ? (int)s_eid[i] : 0;
+    const unsigned long long peers = peer_mask(my_e, nbits, __ballot(valid));
+    if (valid && lane_rank(peers) == 0) atomicAdd(&s_wcnt[wave][my_e], __popcll(peers));
+  }
+  __syncthreads();
+
+  // ---- 3. padded offsets of every expert and every wavefront's first
+  // positions: wavefront 0, lane l holding experts l and l + 64 -------------
+  if (wave == 0) {
+    int w0[kWaves], w1[kWaves];
+    int n0 = 0, n1 = 0;                            // slots of experts lane, lane + 64
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      w0[w] = s_wcnt[w][lane];
+      w1[w] = s_wcnt[w][lane + 64];
+      n0 += w0[w];
+      n1 += w1[w];
     }
-    s_off[E] = acc;
-    *num_post = acc;
+    if (lane < E) s_cnt[lane] = n0;
+    if (lane + 64 < E) s_cnt[lane + 64] = n1;
+    const int c0 = (n0 + block_m - 1) / block_m * block_m;   // zero past the last expert
+    const int c1 = (n1 + block_m - 1) / block_m * block_m;
+    int x0 = c0, x1 = c1;                          // inclusive scans over the lanes
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y0 = __shfl_up(x0, d), y1 = __shfl_up(x1, d);
+      if (lane >= d) {
+        x0 += y0;
+        x1 += y1;
+      }
+    }
+    const int tot0 = __shfl(x0, 63);
+    int r0 = x0 - c0, r1 = tot0 + x1 - c1;         // padded starts
+    if (lane < E) s_off[lane] = r0;
+    if (lane + 64 < E) s_off[lane + 64] = r1;
+    const int total = tot0 + __shfl(x1, 63);
+    if (lane == 0) {
+      s_off[E] = total;
+      *num_post = total;
+    }
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      s_wpos[w][lane] = r0;
+      s_wpos[w][lane + 64] = r1;
+      r0 += w0[w];
+      r1 += w1[w];
+    }
   }
   __syncthreads();
   const int total = s_off[E];
 
-  // ---- 3. block labels, padding and tail ---------------------------------------
+  // ---- 4. block labels, padding and tail ---------------------------------------
   const int nblocks = max_padded / block_m;
   for (int b = tid; b < nblocks; b += kThreads) {
     const int p = b * block_m;
     int label = -1;
     if (p < total) {
-      int lo = 0, hi = E - 1;                    // last e with s_off[e] <= p
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_off[mid] <= p) lo = mid; else hi = mid - 1;
+      int e_lo = 0, e_hi = E - 1;                // last e with s_off[e] <= p
+      while (e_lo < e_hi) {
+        const int mid = (e_lo + e_hi + 1) >> 1;
+        if (s_off[mid] <= p) e_lo = mid; else e_hi = mid - 1;
       }
-      label = lo;
+      label = e_lo;
     }
     expert_ids[b] = label;
   }
-  for (int p = tid; p < max_padded; p += kThreads) {
-    bool pad = p >= total;
-    if (!pad) {
-      int lo = 0, hi = E - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_off[mid] <= p) lo = mid; else hi = mid - 1;
-      }
-      pad = p >= s_off[lo] + s_cnt[lo];
-    }
-    if (pad) sorted_ids[p] = S;                   // the sentinel
+  for (int e = wave; e < E; e += kWaves) {      // each expert's padding, one wavefront
+    const int p1 = s_off[e + 1];
+    for (int p = s_off[e] + s_cnt[e] + lane; p < p1; p += 64) sorted_ids[p] = S;
   }
+  for (int p = total + tid; p < max_padded; p += kThreads) sorted_ids[p] = S;   // the tail
 
-  // ---- 4. stable scatter of the slots -----------------------------------------
-  for (int base = 0; base < S; base += kThreads) {
-    const int i = base + tid;
-    const int my_e = (i < S) ? (int)s_eid[i] : -1;
-    int my_rank = 0;
-    for (int e = 0; e < E; ++e) {
-      const unsigned long long m = __ballot(my_e == e);
-      if (lane == 0) s_wcnt[wave][e] = __popcll(m);
-      if (my_e == e) my_rank = lane_rank(m);
+  // ---- 5. stable scatter of the slots -----------------------------------------
+  for (int base = lo; base < hi; base += 64) {
+    const int i = base + lane;
+    const bool valid = i < hi;
+    const int my_e = valid ? (int)s_eid[i] : 0;
+    const unsigned long long peers = peer_mask(my_e, nbits, __ballot(valid));
+    const int rank = lane_rank(peers);
+    if (valid) {
+      const int pos = s_wpos[wave][my_e];        // read by every lane first ...
+      sorted_ids[pos + rank] = i;
+      if (rank == 0) s_wpos[wave][my_e] = pos + __popcll(peers);   // ... then one per expert
     }
-    __syncthreads();
-    for (int e = tid; e < E; e += kThreads) {     // exclusive scan over wavefronts
-      int acc = 0;
-      for (int w = 0; w < kWaves; ++w) {
-        const int c = s_wcnt[w][e];
-        s_wcnt[w][e] = acc;
-        acc += c;
-      }
-      s_chunk[e] = acc;
-    }
-    __syncthreads();
-    if (my_e >= 0) sorted_ids[s_off[my_e] + s_run[my_e] + s_wcnt[wave][my_e] + my_rank] = i;
-    __syncthreads();
-    for (int e = tid; e < E; e += kThreads) s_run[e] += s_chunk[e];
-    __syncthreads();
   }
 }
 

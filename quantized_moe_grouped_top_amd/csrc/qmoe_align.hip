@@ -33,73 +33,87 @@ __device__ __forceinline__ int lane_rank(unsigned long long mask) {
 // with top_k = kK known at compile time.
 template <int kK>
 __device__ __forceinline__ void route_tokens(const float *__restrict__ logits, int M, int E,
-                                             int tid, int *__restrict__ topk_ids,
+                                             int t_first, int t_step, int *__restrict__ topk_ids,
                                              float *__restrict__ topk_w, uint8_t *s_eid) {
-  // four tokens per thread and round, the first eight logits of all four
-  // loaded before any is used (a lone workgroup waits out every load latency
-  // it does not overlap)
-  constexpr int kTok = 4;
-  for (int t0 = tid; t0 < M; t0 += kTok * kThreads) {
-    float first[kTok][8];
+  for (int t = t_first; t < M; t += t_step) {
+    const float *lg = logits + (size_t)t * E;
+    int ids[kK];
+    float val[kK];
 #pragma unroll
-    for (int q = 0; q < kTok; ++q) {
-      const int t = t0 + q * kThreads;
+    for (int j = 0; j < kK; ++j) {
+      ids[j] = 0;
+      val[j] = 0.0f;
+    }
+    int nfill = 0;
+    for (int e0 = 0; e0 < E; e0 += 8) {
+      float v8[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) first[q][u] = (t < M && u < E) ? logits[(size_t)t * E + u] : 0.0f;
+      for (int u = 0; u < 8; ++u) v8[u] = e0 + u < E ? lg[e0 + u] : 0.0f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (e0 + u >= E) break;
+        float cv = v8[u];
+        int ci = e0 + u;
+#pragma unroll
+        for (int j = 0; j < kK; ++j) {
+          if (j >= nfill || cv > val[j]) {   // place here, carry the old one down
+            const float tv = val[j];
+            const int ti = ids[j];
+            val[j] = cv;
+            ids[j] = ci;
+            cv = tv;
+            ci = ti;
+          }
+        }
+        nfill = min(nfill + 1, kK);
+      }
+    }
+    // weights: exp(l_j - l_max) / sum over the chosen experts
+    float ex[kK];
+    float sum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kK; ++j) {
+      ex[j] = expf(val[j] - val[0]);
+      sum += ex[j];
     }
 #pragma unroll
-    for (int q = 0; q < kTok; ++q) {
-      const int t = t0 + q * kThreads;
-      if (t >= M) break;
-      const float *lg = logits + (size_t)t * E;
-      int ids[kK];
-      float val[kK];
-#pragma unroll
-      for (int j = 0; j < kK; ++j) {
-        ids[j] = 0;
-        val[j] = 0.0f;
-      }
-      int nfill = 0;
-      for (int e0 = 0; e0 < E; e0 += 8) {
-        float v8[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v8[u] = e0 == 0 ? first[q][u] : (e0 + u < E ? lg[e0 + u] : 0.0f);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          if (e0 + u >= E) break;
-          float cv = v8[u];
-          int ci = e0 + u;
-#pragma unroll
-          for (int j = 0; j < kK; ++j) {
-            if (j >= nfill || cv > val[j]) {   // place here, carry the old one down
-              const float tv = val[j];
-              const int ti = ids[j];
-              val[j] = cv;
-              ids[j] = ci;
-              cv = tv;
-              ci = ti;
-            }
-          }
-          nfill = min(nfill + 1, kK);
-        }
-      }
-      // weights: exp(l_j - l_max) / sum over the chosen experts
-      float ex[kK];
-      float sum = 0.0f;
-#pragma unroll
-      for (int j = 0; j < kK; ++j) {
-        ex[j] = expf(val[j] - val[0]);
-        sum += ex[j];
-      }
-#pragma unroll
-      for (int j = 0; j < kK; ++j) {
-        const int i = t * kK + j;
-        topk_ids[i] = ids[j];
-        topk_w[i] = ex[j] / sum;
-        s_eid[i] = (uint8_t)ids[j];
-      }
+    for (int j = 0; j < kK; ++j) {
+      const int i = t * kK + j;
+      topk_ids[i] = ids[j];
+      topk_w[i] = ex[j] / sum;
+      if (s_eid) s_eid[i] = (uint8_t)ids[j];
     }
   }
+}
+
+__device__ __forceinline__ void route_tokens_k(const float *__restrict__ logits, int M, int E,
+                                               int top_k, int t_first, int t_step,
+                                               int *__restrict__ topk_ids,
+                                               float *__restrict__ topk_w, uint8_t *s_eid) {
+  switch (top_k) {
+    case 1: route_tokens<1>(logits, M, E, t_first, t_step, topk_ids, topk_w, s_eid); break;
+    case 2: route_tokens<2>(logits, M, E, t_first, t_step, topk_ids, topk_w, s_eid); break;
+    case 3: route_tokens<3>(logits, M, E, t_first, t_step, topk_ids, topk_w, s_eid); break;
+    case 4: route_tokens<4>(logits, M, E, t_first, t_step, topk_ids, topk_w, s_eid); break;
+    case 5: route_tokens<5>(logits, M, E, t_first, t_step, topk_ids, topk_w, s_eid); break;
+    case 6: route_tokens<6>(logits, M, E, t_first, t_step, topk_ids, topk_w, s_eid); break;
+    case 7: route_tokens<7>(logits, M, E, t_first, t_step, topk_ids, topk_w, s_eid); break;
+    default: route_tokens<kMaxTopK>(logits, M, E, t_first, t_step, topk_ids, topk_w, s_eid); break;
+  }
+}
+
+// Many tokens: the top-k choice runs on its own grid, one token per thread,
+// before the one-workgroup alignment (one lone workgroup would take it at a
+// few microseconds per 1024 tokens).
+constexpr int kRouteThreads = 256;
+constexpr int kSplitTokens = 1024;
+
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(const float *__restrict__ logits,
+                                                              int M, int E, int top_k,
+                                                              int *__restrict__ topk_ids,
+                                                              float *__restrict__ topk_w) {
+  route_tokens_k(logits, M, E, top_k, blockIdx.x * kRouteThreads + threadIdx.x, M, topk_ids,
+                 topk_w, nullptr);
 }
 
 // mask of the lanes whose `e` equals this lane's, among the lanes of `valid`
@@ -117,8 +131,8 @@ __device__ __forceinline__ unsigned long long peer_mask(int e, int nbits,
 
 __global__ __launch_bounds__(kThreads) void route_align_kernel(
     const float *__restrict__ logits, int M, int E, int top_k, int block_m, int max_padded,
-    int *__restrict__ topk_ids, float *__restrict__ topk_w, int *__restrict__ sorted_ids,
-    int *__restrict__ expert_ids, int *__restrict__ num_post) {
+    int routed, int *__restrict__ topk_ids, float *__restrict__ topk_w,
+    int *__restrict__ sorted_ids, int *__restrict__ expert_ids, int *__restrict__ num_post) {
   __shared__ uint8_t s_eid[kMaxSlots];            // expert of every slot
   __shared__ int s_cnt[kMaxExperts];              // slots per expert
   __shared__ int s_off[kMaxExperts + 1];          // padded start of every expert
@@ -137,15 +151,10 @@ __global__ __launch_bounds__(kThreads) void route_align_kernel(
   // on equal values the earlier expert stays, as a later one must be strictly
   // larger to move in) by insertion; logits are read 8 at a time so their
   // loads overlap.
-  switch (top_k) {
-    case 1: route_tokens<1>(logits, M, E, tid, topk_ids, topk_w, s_eid); break;
-    case 2: route_tokens<2>(logits, M, E, tid, topk_ids, topk_w, s_eid); break;
-    case 3: route_tokens<3>(logits, M, E, tid, topk_ids, topk_w, s_eid); break;
-    case 4: route_tokens<4>(logits, M, E, tid, topk_ids, topk_w, s_eid); break;
-    case 5: route_tokens<5>(logits, M, E, tid, topk_ids, topk_w, s_eid); break;
-    case 6: route_tokens<6>(logits, M, E, tid, topk_ids, topk_w, s_eid); break;
-    case 7: route_tokens<7>(logits, M, E, tid, topk_ids, topk_w, s_eid); break;
-    default: route_tokens<kMaxTopK>(logits, M, E, tid, topk_ids, topk_w, s_eid); break;
+  if (routed) {                                  // top-k already chosen by route_kernel
+    for (int i = tid; i < S; i += kThreads) s_eid[i] = (uint8_t)topk_ids[i];
+  } else {
+    route_tokens_k(logits, M, E, top_k, tid, kThreads, topk_ids, topk_w, s_eid);
   }
   __syncthreads();
 
@@ -249,8 +258,16 @@ __global__ __launch_bounds__(kThreads) void route_align_kernel(
 hipError_t launch_route_align(const float *logits, int M, int E, int top_k, int block_m,
                               int max_padded, int *topk_ids, float *topk_w, int *sorted_ids,
                               int *expert_ids, int *num_post, hipStream_t s) {
+  const int routed = M > kSplitTokens;
+  if (routed) {
+    hipLaunchKernelGGL(route_kernel, dim3((M + kRouteThreads - 1) / kRouteThreads),
+                       dim3(kRouteThreads), 0, s, logits, M, E, top_k, topk_ids, topk_w);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   hipLaunchKernelGGL(route_align_kernel, dim3(1), dim3(kThreads), 0, s, logits, M, E, top_k,
-                     block_m, max_padded, topk_ids, topk_w, sorted_ids, expert_ids, num_post);
+                     block_m, max_padded, routed, topk_ids, topk_w, sorted_ids, expert_ids,
+                     num_post);
   return hipGetLastError();
 }
 

@@ -246,6 +246,26 @@ def test_align_most_slots(block_m):
     np.testing.assert_array_equal(moe.expert_ids.cpu().numpy(), e_ref)
 
 
+@pytest.mark.parametrize("M,E,top_k", [(1025, 8, 2), (3000, qm.MOE_MAX_EXPERTS, qm.MOE_MAX_TOPK),
+                                         (5000, 4, 1), (2048, 16, 5)])
+def test_route_many_tokens(M, E, top_k):
+    """Above 1024 tokens the top-k choice runs on its own grid before the
+    alignment: expert ids and block layout bit-exact, router weights within
+    a few float32 units, for several top_k specialisations."""
+    _announce(f"route M={M} E={E} top_k={top_k}")
+    lg = synth.make_logits(M, E, synth.seed_of(f"route {M} {E} {top_k}"), 0.5, DEV)
+    moe = runner.RoutedMoE("fp8", M, 128, 64, E, top_k, block_m=128)
+    moe.route(lg)
+    torch.cuda.synchronize()
+    ids_ref, w_ref = O.route_topk(lg.cpu().numpy(), top_k)
+    np.testing.assert_array_equal(moe.topk_ids.cpu().numpy(), ids_ref)
+    np.testing.assert_allclose(moe.topk_weights.cpu().numpy(), w_ref, rtol=1e-6, atol=1e-7)
+    s_ref, e_ref, n_ref = O.align_block_size(ids_ref, E, 128)
+    assert int(moe.num_tokens_post_padded.item()) == n_ref
+    np.testing.assert_array_equal(moe.sorted_token_ids.cpu().numpy(), s_ref)
+    np.testing.assert_array_equal(moe.expert_ids.cpu().numpy(), e_ref)
+
+
 def test_routed_empty_batch():
     _announce("M = 0")
     moe = runner.RoutedMoE("fp8", 0, 128, 64, 8, 2, block_m=16)

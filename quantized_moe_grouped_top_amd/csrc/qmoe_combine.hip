@@ -23,21 +23,25 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t *__res
     const long long t = i / n8;
     const int c = (int)(i - t * n8) * 8;
     const uint16_t *src = y + (t * top_k) * (long long)N + c;
+    // every slot's load is issued before the first is used (one memory
+    // latency per token instead of top_k)
+    i32x4 v[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (j < top_k) v[j] = *reinterpret_cast<const i32x4 *>(src + (long long)j * N);
     float acc[8];
-    {
-      const i32x4 v = *reinterpret_cast<const i32x4 *>(src);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q] = bf16_lo(v[q]);
-        acc[2 * q + 1] = bf16_hi(v[q]);
-      }
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] = bf16_lo(v[0][q]);
+      acc[2 * q + 1] = bf16_hi(v[0][q]);
     }
-    for (int j = 1; j < top_k; ++j) {
-      const i32x4 v = *reinterpret_cast<const i32x4 *>(src + (long long)j * N);
+#pragma unroll
+    for (int j = 1; j < kMaxTopK; ++j) {
+      if (j >= top_k) break;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        acc[2 * q] = acc[2 * q] + bf16_lo(v[q]);
-        acc[2 * q + 1] = acc[2 * q + 1] + bf16_hi(v[q]);
+        acc[2 * q] = acc[2 * q] + bf16_lo(v[j][q]);
+        acc[2 * q + 1] = acc[2 * q + 1] + bf16_hi(v[j][q]);
       }
     }
     i32x4 o;

@@ -125,6 +125,20 @@ __global__ __launch_bounds__(kThreads) void quant_fp8_kernel(const Src *__restri
                                                              float *__restrict__ scale) {
   __shared__ float red[kThreads / 64];
   const int t = blockIdx.y;
+  const Src *src = x + (long long)t * per;
+  uint8_t *dst = q + (long long)t * per;
+  const long long n8 = per / 8;
+  const long long stride = (long long)gridDim.x * kThreads;
+  auto load_round = [&](long long r0, Raw8<Src> (&raw)[kFlatUnroll]) {
+#pragma unroll
+    for (int j = 0; j < kFlatUnroll; ++j)
+      if (r0 + j * stride < n8) raw[j] = ld8(src + (r0 + j * stride) * 8);
+  };
+  // the first round's loads do not depend on the scale: they are in flight
+  // while the partial maxima are reduced
+  long long i0 = blockIdx.x * (long long)kThreads + threadIdx.x;
+  Raw8<Src> raw[kFlatUnroll];
+  load_round(i0, raw);
   float m = 0.0f;
   for (int i = threadIdx.x; i < parts; i += kThreads) m = fmaxf(m, ws[t * kAmaxPartials + i]);
   const float amax = block_max(m, red);
@@ -132,17 +146,7 @@ __global__ __launch_bounds__(kThreads) void quant_fp8_kernel(const Src *__restri
   const float inv = (float)(1.0 / (double)s);
   if (blockIdx.x == 0 && threadIdx.x == 0) scale[t] = s;
 
-  const Src *src = x + (long long)t * per;
-  uint8_t *dst = q + (long long)t * per;
-  const long long n8 = per / 8;
-  const long long stride = (long long)gridDim.x * kThreads;
-  for (long long i0 = blockIdx.x * (long long)kThreads + threadIdx.x; i0 < n8;
-       i0 += kFlatUnroll * stride) {
-    Raw8<Src> raw[kFlatUnroll];
-#pragma unroll
-    for (int j = 0; j < kFlatUnroll; ++j)
-      if (i0 + j * stride < n8) raw[j] = ld8(src + (i0 + j * stride) * 8);
-    __builtin_amdgcn_sched_barrier(0);
+  for (; i0 < n8; i0 += kFlatUnroll * stride) {
 #pragma unroll
     for (int j = 0; j < kFlatUnroll; ++j) {
       const long long i = i0 + j * stride;
@@ -155,6 +159,7 @@ __global__ __launch_bounds__(kThreads) void quant_fp8_kernel(const Src *__restri
         *reinterpret_cast<i32x2 *>(dst + i * 8) = out;
       }
     }
+    load_round(i0 + kFlatUnroll * stride, raw);
   }
 }
 
@@ -795,8 +800,9 @@ hipError_t launch_quant_fp8_tensor_bf16(const uint16_t *x, long long numel, uint
                      numel, ws);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(quant_fp8_kernel<uint16_t>, dim3(grid_for(numel / 8, 8192), 1),
-                     dim3(kThreads), 0, s, x, numel, parts, ws, q, scale);
+  const int grid = grid_for(numel / 8 / kFlatUnroll, 2048);   // one round of loads per thread
+  hipLaunchKernelGGL(quant_fp8_kernel<uint16_t>, dim3(grid, 1), dim3(kThreads), 0, s, x, numel,
+                     parts, ws, q, scale);
   return hipGetLastError();
 }
 

@@ -144,7 +144,9 @@ int moe_mx_scale_rows(int rows, int E);
  * Limits: 1 <= E <= MOE_MAX_EXPERTS, 1 <= top_k <= min(E, MOE_MAX_TOPK),
  * 0 <= M*top_k <= MOE_MAX_SLOTS, block_m in {16, 32, 64, 128, 256}.
  * M = 0 is valid (no slots; the buffers are still written).
- * One workgroup does the whole call (wavefront ballots and prefix scans). */
+ * Up to 1024 tokens one workgroup does the whole call; above that the top-k
+ * choice runs on a grid of its own first.  Either way the call enqueues
+ * its kernels on `s` and never synchronizes. */
 int moe_align_block_size(const float *logits, int M, int E, int top_k, int block_m,
                          int *topk_ids, float *topk_weights, int *sorted_token_ids,
                          int *expert_ids, int *num_tokens_post_padded,

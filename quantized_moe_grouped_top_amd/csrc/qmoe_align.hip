@@ -1,5 +1,6 @@
 // Routing (top-k over the router logits) and block alignment of the routed
-// slots, in one workgroup.
+// slots: one workgroup for both up to 1024 tokens; above that the top-k runs
+// on a grid of its own (one token per thread) and the workgroup aligns.
 //
 // The alignment produces the layout the grouped GEMMs consume: the slots
 // i = t*top_k + j grouped by expert, each group padded to a multiple of

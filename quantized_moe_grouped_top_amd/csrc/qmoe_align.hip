@@ -55,15 +55,23 @@ __device__ __forceinline__ void route_tokens(const float *__restrict__ logits, i
         if (e0 + u >= E) break;
         float cv = v8[u];
         int ci = e0 + u;
+        // The list is ordered by (value descending, expert ascending).  The
+        // new expert has the largest index so far, so it moves in only past
+        // strictly smaller values; once it is placed, every entry below moves
+        // down one position without another comparison (an entry that is
+        // carried down must stay ahead of an equal value below it, which has
+        // a larger index).
+        bool carry = false;
 #pragma unroll
         for (int j = 0; j < kK; ++j) {
-          if (j >= nfill || cv > val[j]) {   // place here, carry the old one down
+          if (carry || j >= nfill || cv > val[j]) {
             const float tv = val[j];
             const int ti = ids[j];
             val[j] = cv;
             ids[j] = ci;
             cv = tv;
             ci = ti;
+            carry = true;
           }
         }
         nfill = min(nfill + 1, kK);
@@ -149,9 +157,8 @@ __global__ __launch_bounds__(kThreads) void route_align_kernel(
 
   // ---- 1. top-k choice and router weights of every token -------------------
   // One pass over the token's logits keeps the top_k best (value descending;
-  // on equal values the earlier expert stays, as a later one must be strictly
-  // larger to move in) by insertion; logits are read 8 at a time so their
-  // loads overlap.
+  // on equal values the lower expert index first) by insertion; logits are
+  // read 8 at a time so their loads overlap.
   if (routed) {                                  // top-k already chosen by route_kernel
     for (int i = tid; i < S; i += kThreads) s_eid[i] = (uint8_t)topk_ids[i];
   } else {

@@ -227,6 +227,59 @@ def test_routed_tied_logits(block_m):
     run_routed(wl, block_m=block_m, full=True, logits=torch.zeros(90, 8))
 
 
+def _tied_logits(M, E, seed):
+    """Small-integer logits (many exact ties, and ties that a larger value
+    displaces down the top-k list), plus the rows [5, 3, 3, 4, ...] and
+    [1, 1, 2, ...] that need a tied entry carried past a larger one."""
+    g = torch.Generator().manual_seed(seed)
+    lg = torch.randint(0, 4, (M, E), generator=g).to(torch.float32)
+    lg[0, :] = 0.0
+    lg[0, :4] = torch.tensor([5.0, 3.0, 3.0, 4.0])
+    if M > 1:
+        lg[1, :] = 0.0
+        lg[1, :3] = torch.tensor([1.0, 1.0, 2.0])
+    if M > 2:
+        lg[2, :] = -1.0                      # one row of equal values
+    return lg.contiguous()
+
+
+# token counts on both sides of the split between the one-workgroup routing
+# and the routing grid (above 1024 tokens)
+TIE_CASES = [(M, E, k) for M in (300, 2500) for E in (8, 16, 128)
+             for k in range(1, 9) if k <= E]
+
+
+@pytest.mark.parametrize("block_m", [16, 128])
+@pytest.mark.parametrize("M,E,top_k", TIE_CASES, ids=[f"m{M}_e{E}_k{k}" for M, E, k in TIE_CASES])
+def test_route_tied_integer_logits(M, E, top_k, block_m):
+    """Integer-valued router logits: the expert choice follows (value
+    descending, expert ascending) bit-exactly, with the sorted slots, block
+    labels and padded length bit-exact as well."""
+    _announce(f"tied logits M={M} E={E} top_k={top_k} block_m={block_m}")
+    lg = _tied_logits(M, E, synth.seed_of(f"ties {M} {E} {top_k}") % (1 << 31))
+    moe = runner.RoutedMoE("fp8", M, 128, 64, E, top_k, block_m=block_m)
+    moe.route(lg.to(DEV))
+    torch.cuda.synchronize()
+    ids_ref, w_ref = O.route_topk(lg.numpy(), top_k)
+    np.testing.assert_array_equal(moe.topk_ids.cpu().numpy(), ids_ref)
+    wts = moe.topk_weights.cpu().numpy()
+    np.testing.assert_allclose(wts, w_ref, rtol=8 * F32_EPS, atol=1e-44)
+    assert np.max(np.abs(wts.astype(np.float64).sum(1) - 1.0)) <= 4 * F32_EPS
+    s_ref, e_ref, n_ref = O.align_block_size(ids_ref, E, block_m)
+    assert int(moe.num_tokens_post_padded.item()) == n_ref
+    np.testing.assert_array_equal(moe.sorted_token_ids.cpu().numpy(), s_ref)
+    np.testing.assert_array_equal(moe.expert_ids.cpu().numpy(), e_ref)
+
+
+@pytest.mark.parametrize("block_m", [16, 128])
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+def test_routed_integer_logits_end_to_end(fmt, block_m):
+    """The whole layer with tied integer logits (top_k 3): routing, GEMM and
+    combine against the oracle."""
+    wl = synth.small(fmt, 200, 256, 96, 8, 3)
+    run_routed(wl, block_m=block_m, full=True, logits=_tied_logits(200, 8, 77))
+
+
 @pytest.mark.parametrize("block_m", [16, 128])
 def test_align_most_slots(block_m):
     """The largest slot count (M * top_k = MOE_MAX_SLOTS): routing and block

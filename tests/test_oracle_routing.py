@@ -45,6 +45,23 @@ def test_topk_ties_take_lower_index():
     assert w[0, 0] == w[0, 1] == np.float32(0.5)
 
 
+@pytest.mark.parametrize("E,top_k", [(4, 3), (8, 2), (8, 5), (16, 8)])
+def test_topk_ties_match_sorted_rows(E, top_k):
+    """Small-integer logits (ties everywhere, tied values displaced down the
+    list by larger ones): each row's choice equals Python's sorted() by
+    (logit descending, expert ascending), cut at top_k."""
+    rng = np.random.default_rng(100 + E + top_k)
+    lg = rng.integers(0, 4, size=(400, E)).astype(np.float32)
+    lg[0, :] = 0.0
+    lg[0, :4] = [5, 3, 3, 4]
+    ids, _ = O.route_topk(lg, top_k)
+    for t in range(lg.shape[0]):
+        want = sorted(range(E), key=lambda e: (-float(lg[t, e]), e))[:top_k]
+        assert ids[t].tolist() == want
+    if top_k == 3 and E == 4:
+        assert ids[0].tolist() == [0, 3, 1]
+
+
 def test_router_weights_sum_to_one_and_ratios():
     rng = np.random.default_rng(3)
     lg = rng.standard_normal((500, 8)).astype(np.float32)

@@ -5,9 +5,13 @@ resident in HBM: routing + block alignment, activation quantization (fp8
 formats), the grouped GEMM with its fused scale / router-weight epilogue, and
 the per-token combine (MXFP8: quantization + grouped GEMM).
 
-Default workload: int8 W8A16 decode, M=64 tokens, K=4096, N=14336, E=8,
-top_k=2 (the weight-bandwidth-bound shape).  ``--workload`` selects another
-one (names in quantized_moe_grouped_top_amd.synth.WORKLOADS).
+Default workload: the mistral-7B-shaped up projection in fp8 W8A8, M=4096
+tokens, K=4096, N=28672, E=8, top_k=2 (the first row of the FP8_W8A8 "Model
+Results" on "Tianxing/moe quantization"; the largest E=8, top_k=2
+configuration on one GPU, bound by the fp8 MFMA peak).  The same run also
+times the int8 W8A16 decode shape (M=64, K=4096, N=14336, bound by HBM) and
+reports it under "decode".  ``--workload`` selects one other workload (names
+in quantized_moe_grouped_top_amd.synth.WORKLOADS) and times only that.
 
 The expert weights exist in several copies that the steps rotate through, so
 that no step finds its weights in the 256 MB Infinity Cache or in L2 from the
@@ -36,7 +40,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"fp8": 5033.0, "mxfp8": 5033.0, "bf16": 2516.0, "int8": 5033.0}
-DEFAULT_WORKLOAD = "int8w8a16_m64_k4096_n14336"
+DEFAULT_WORKLOAD = "mistral7b_up_fp8_m4096_k4096_n28672"
+DECODE_WORKLOAD = "int8w8a16_m64_k4096_n14336"
 
 
 def alg_bytes(wl, active_experts=None):
@@ -72,7 +77,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--workload", default=None,
+                   help=f"one workload to time (default: {DEFAULT_WORKLOAD}, plus "
+                        f"{DECODE_WORKLOAD} reported under 'decode')")
     p.add_argument("--copies", type=int, default=0,
                    help="weight copies rotated over (0: enough for >= 1 GiB of weights)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -130,11 +137,27 @@ def copy_calibration():
                                            "bytes_written": 4 * n, "launches": 10}}), flush=True)
 
 
+def _sample_weights(O, w, fmt, cols):
+    """Oracle weight quantization of the output channels `cols` of every
+    expert (an expert's per-tensor fp8 scale still comes from its whole
+    matrix): offline, outside the timed region."""
+    import numpy as np
+    rows = w[:, cols]
+    if fmt == "fp8":
+        s = np.array([O.fp8_tensor_scale(w[e]) for e in range(w.shape[0])], np.float32)
+        q = np.stack([O.fp8_quantize_with_scale(rows[e], s[e]) for e in range(w.shape[0])])
+        return q, s
+    return {"fp8wo": O.quantize_weight_fp8_rows, "int4wo": O.quantize_weight_int4}.get(
+        fmt, O.quantize_weight_int8)(rows)
+
+
 def cpu_baseline(wl, case, target_s):
-    """The CPU oracle on the same workload, timed on the host: the whole
-    step (routing, alignment, activation quantization, grouped GEMM, combine)
-    repeated until target_s seconds have passed (at least once).  Weight
-    quantization is offline and not timed."""
+    """The CPU oracle on the same workload, timed on the host, on a bounded
+    sample: the whole step (routing, alignment, activation quantization,
+    grouped GEMM, combine) repeated until target_s seconds have passed (at
+    least once).  Weight quantization is offline and not timed.  Routed
+    workloads above 0.25 TFLOP run the step over every token
+    but only the first n_s output columns, and the time is scaled by N / n_s."""
     import numpy as np
     from oracle import formats as F
     from oracle import moe as O
@@ -143,7 +166,6 @@ def cpu_baseline(wl, case, target_s):
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
     if wl.fmt.startswith("act_"):
         act = O.ACT_SWIGLU if wl.act == "swiglu" else O.ACT_SRELU
-        mo = case["m_offsets"].cpu().numpy()
         rows = max(1, min(wl.M, 2000))            # a bounded sample of whole rows
         reps, t0 = 0, time.perf_counter()
         while True:
@@ -184,12 +206,15 @@ def cpu_baseline(wl, case, target_s):
                 "kind": "oracle", "tflops": round(wl.flops / per / 1e12, 6),
                 "sample": f"whole workload, {reps} step(s) in {el:.1f} s "
                           f"(numpy float64; BLAS threads = OMP_NUM_THREADS or all cores)"}
+    n_s = wl.N
     if wl.fmt == "mxfp8":
         wq, wsf = O.quantize_weight_mxfp8(w)
         mo = case["m_offsets"].cpu().numpy()
     else:
-        wq, ws = {"fp8": O.quantize_weight_fp8, "fp8wo": O.quantize_weight_fp8_rows,
-                  "int4wo": O.quantize_weight_int4}.get(wl.fmt, O.quantize_weight_int8)(w)
+        budget = 2.5e11                             # flops of the sampled step
+        if wl.flops > budget:
+            n_s = max(256, min(wl.N, int(wl.N * budget / wl.flops) // 256 * 256))
+        wq, ws = _sample_weights(O, w, wl.fmt, np.arange(n_s))
         lg = case["logits"].cpu().numpy()
     del w
     reps, t0 = 0, time.perf_counter()
@@ -217,31 +242,25 @@ def cpu_baseline(wl, case, target_s):
         el = time.perf_counter() - t0
         if el >= target_s:
             break
-    per = el / reps
+    per = el / reps * wl.N / n_s
+    what = ("whole workload" if n_s == wl.N else
+            f"every token, output columns 0..{n_s - 1} of {wl.N}, time scaled by N / {n_s}")
     return {"value": round(alg_bytes(wl) / per / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "tflops": round(wl.flops / per / 1e12, 6),
-            "sample": f"whole workload, {reps} step(s) in {el:.1f} s "
+            "sample": f"{what}; {reps} step(s) in {el:.1f} s "
                       f"(numpy float64; BLAS threads = OMP_NUM_THREADS or all cores)"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
-              f"(this build runs the hot path on a single MI355X).", file=sys.stderr)
-        sys.exit(2)
-    if args.copy_calibration:
-        copy_calibration()
-        return
+def measure(wl, args):
+    """Time `args.steps` steps of one workload after `args.warmup` untimed
+    ones.  Returns (fields of the JSON line, the inputs, the layer object)."""
     import torch
 
     import quantized_moe_grouped_top_amd as qm
     from quantized_moe_grouped_top_amd import runner, synth
 
-    qm.lib()                                   # fail loudly if the library is missing
-    torch.cuda.set_device(0)
-    wl = synth.WORKLOADS[args.workload]
     case = synth.make_case(wl, 0, device="cuda")
+    layout = None
     if wl.fmt.startswith("act_"):
         # input copies rotate so that no step finds its input in a cache
         copies = args.copies or max(2, -(-(1 << 30) // (2 * case["x"].numel())))
@@ -278,46 +297,44 @@ def main():
             w_q = runner.pack_weights(w_q, layout)
         copies = args.copies or max(2, -(-(1 << 30) // w_q.numel()))
         weights = [(w_q, w_s)] + [(w_q.clone(), w_s.clone()) for _ in range(copies - 1)]
-    if wl.fmt.startswith("act_") or wl.fmt == "mxfp8_wgrad":
-        pass
-    elif wl.fmt == "mxfp8_dgrad":
-        # the output gradient [M, N] against the weights along N: dx [M, K]
-        moe = runner.MxMoE(wl.M, wl.N, wl.K, wl.E)
-        mo = case["m_offsets"]
+        if wl.fmt == "mxfp8_dgrad":
+            # the output gradient [M, N] against the weights along N: dx [M, K]
+            moe = runner.MxMoE(wl.M, wl.N, wl.K, wl.E)
+            mo = case["m_offsets"]
 
-        def step(i, ev):
-            q, s = weights[i % copies]
-            moe.quantize(case["dy"], mo)
-            if ev is not None:
-                ev[0].record()
-            moe.gemm(q, s, mo)
-            if ev is not None:
-                ev[1].record()
-    elif wl.fmt == "mxfp8":
-        moe = runner.MxMoE(wl.M, wl.K, wl.N, wl.E)
-        mo = case["m_offsets"]
+            def step(i, ev):
+                q, s = weights[i % copies]
+                moe.quantize(case["dy"], mo)
+                if ev is not None:
+                    ev[0].record()
+                moe.gemm(q, s, mo)
+                if ev is not None:
+                    ev[1].record()
+        elif wl.fmt == "mxfp8":
+            moe = runner.MxMoE(wl.M, wl.K, wl.N, wl.E)
+            mo = case["m_offsets"]
 
-        def step(i, ev):
-            q, s = weights[i % copies]
-            moe.quantize(case["x"], mo)
-            if ev is not None:
-                ev[0].record()
-            moe.gemm(q, s, mo)
-            if ev is not None:
-                ev[1].record()
-    else:
-        moe = runner.RoutedMoE(wl.fmt, wl.M, wl.K, wl.N, wl.E, wl.top_k, w_layout=layout)
+            def step(i, ev):
+                q, s = weights[i % copies]
+                moe.quantize(case["x"], mo)
+                if ev is not None:
+                    ev[0].record()
+                moe.gemm(q, s, mo)
+                if ev is not None:
+                    ev[1].record()
+        else:
+            moe = runner.RoutedMoE(wl.fmt, wl.M, wl.K, wl.N, wl.E, wl.top_k, w_layout=layout)
 
-        def step(i, ev):
-            q, s = weights[i % copies]
-            moe.route(case["logits"])
-            moe.quantize(case["x"])
-            if ev is not None:
-                ev[0].record()
-            moe.gemm(case["x"], q, s)
-            if ev is not None:
-                ev[1].record()
-            moe.combine()
+            def step(i, ev):
+                q, s = weights[i % copies]
+                moe.route(case["logits"])
+                moe.quantize(case["x"])
+                if ev is not None:
+                    ev[0].record()
+                moe.gemm(case["x"], q, s)
+                if ev is not None:
+                    ev[1].record()
+                moe.combine()
 
     for i in range(args.warmup):
         step(i, None)
@@ -357,26 +374,65 @@ def main():
                  "kernel": "fused activation + quantization" if is_act else "grouped GEMM",
                  "kernel_us": round(gemm_ms * 1e3, 2), "alg_bytes": int(nbytes),
                  "flops": None if is_act else int(wl.flops)})
-    line = {
-        "metric": "TFLOPS and HBM GB/s (% of MI355X roofline) for quantized MoE GEMM, E=8 top_k=2",
+    fields = {
         "value": round(nbytes / (ms * 1e-3) / 1e9, 2),
-        "unit": "GB/s",
         "tflops": None if is_act else round(wl.flops / (ms * 1e-3) / 1e12, 3),
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": dtype, "data": "synthetic (seeded N(0,1) activations and logits, N(0,1/sqrt(K)) weights)",
+        "dtype": dtype,
         "config": {"workload": wl.name, "format": wl.fmt, "M": wl.M, "K": wl.K, "N": wl.N,
                    "E": wl.E, "top_k": wl.top_k,
                    ("input_copies" if is_act else "weight_copies"): copies,
                    "block_m": getattr(moe, "block_m", None),
-                   "weight_layout": None if is_act or wl.fmt == "mxfp8_wgrad" else
-                   {qm.MOE_W_TILED: "tiled", qm.MOE_W_FRAG: "frag"}.get(
-                       getattr(moe, "w_layout", None), "rowmajor")},
+                   "weight_layout": None if layout is None else
+                   {qm.MOE_W_TILED: "tiled", qm.MOE_W_FRAG: "frag"}.get(layout, "rowmajor")},
         "roofline": roof,
+    }
+    return fields, case, moe
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
+              f"(this build runs the hot path on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    import torch
+
+    import quantized_moe_grouped_top_amd as qm
+    from quantized_moe_grouped_top_amd import synth
+
+    qm.lib()                                   # fail loudly if the library is missing
+    torch.cuda.set_device(0)
+    wl = synth.WORKLOADS[args.workload or DEFAULT_WORKLOAD]
+    fields, case, moe = measure(wl, args)
+    del moe
+    line = {
+        "metric": "TFLOPS and HBM GB/s (% of MI355X roofline) for quantized MoE GEMM, E=8 top_k=2",
+        "value": fields["value"],
+        "unit": "GB/s",
+        "tflops": fields["tflops"],
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": fields["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": fields["dtype"],
+        "data": "synthetic (seeded N(0,1) activations and logits, N(0,1/sqrt(K)) weights)",
+        "config": fields["config"],
+        "roofline": fields["roofline"],
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, case, args.cpu_seconds)
+    del case
+    if args.workload is None:
+        # the HBM-bound decode shape, timed in the same run (no CPU baseline)
+        torch.cuda.empty_cache()
+        dfields, _, _ = measure(synth.WORKLOADS[DECODE_WORKLOAD], args)
+        line["decode"] = {"workload": DECODE_WORKLOAD, "ms_per_step": dfields["ms_per_step"],
+                          "value": dfields["value"], "unit": "GB/s",
+                          "gemm_us": dfields["roofline"]["kernel_us"],
+                          "roofline": dfields["roofline"]}
     print(json.dumps(line), flush=True)
 
 

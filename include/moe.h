@@ -21,8 +21,11 @@
  *
  * Conventions shared by every entry point
  *   - All array arguments are DEVICE pointers owned by the caller.  The library
- *     never allocates or frees memory and keeps no state besides a
- *     thread-local record of the last error.
+ *     never allocates or frees memory and keeps no device state: every launch
+ *     depends only on its arguments, so calls may run concurrently on
+ *     different streams.  On the host it keeps a thread-local record of the
+ *     last error and the compute-unit count of the device (which sizes the
+ *     persistent grids).
  *   - Every call only enqueues work on `stream` (0 = the null stream) and never
  *     synchronises; results are valid once the stream has reached that point.
  *   - Arguments are validated on the host before anything is enqueued; on an

@@ -13,7 +13,8 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libqmoe.so")
 BUILD = os.path.join(HERE, "_build")
 INCLUDE = os.path.normpath(os.path.join(HERE, "..", "include"))      # moe.h, the C ABI
-SOURCES = ["qmoe_api.cpp", "qmoe_align.hip", "qmoe_quant.hip", "qmoe_gemm.hip", "qmoe_combine.hip"]
+SOURCES = ["qmoe_api.cpp", "qmoe_align.hip", "qmoe_quant.hip", "qmoe_gemm.hip", "qmoe_gemm_tile.hip",
+           "qmoe_combine.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

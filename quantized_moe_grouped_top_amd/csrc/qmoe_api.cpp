@@ -62,6 +62,10 @@ long long max_padded_ll(int M, int E, int top_k, int block_m) {
   return (n + block_m - 1) / block_m * block_m;
 }
 
+// Outputs written by 32-bit buffer offsets (the out-of-range offset of the
+// tile GEMM's dropped stores lies above this)
+constexpr long long kMaxOutBytes = 0xFFFFFF00ll;
+
 int check_routed_gemm(const void *a, const void *w, const void *w_scale, int w_layout,
                       const int *sorted, const int *expert_ids, const int *num_post,
                       const float *topk_w, const uint16_t *y, int M, int K, int N, int E, int top_k,
@@ -88,6 +92,8 @@ int check_routed_gemm(const void *a, const void *w, const void *w_scale, int w_l
           MOE_EUNSUPPORTED, "%s: weight tensor must stay below 4 GiB", fn);
   REQUIRE((long long)M * (long long)K * 2 < (1ll << 32), MOE_EUNSUPPORTED,
           "%s: activation tensor must stay below 4 GiB", fn);
+  REQUIRE((long long)M * top_k * (long long)N * 2 < kMaxOutBytes, MOE_EUNSUPPORTED,
+          "%s: per-slot results must stay below 4 GiB", fn);
   return MOE_OK;
 }
 
@@ -401,6 +407,14 @@ int moe_grouped_gemm_mxfp8(const uint8_t *a_q, const uint8_t *a_sf, const uint8_
               ((uintptr_t)w_sf & 3u) == 0,
           MOE_EINVAL, "%s: data must be 16-byte and scales 4-byte aligned", fn);
   REQUIRE(K % 128 == 0, MOE_EUNSUPPORTED, "%s: K=%d is not a multiple of 128", fn, K);
+  REQUIRE(N % 8 == 0, MOE_EUNSUPPORTED, "%s: N=%d is not a multiple of 8", fn, N);
+  REQUIRE(aligned16(out), MOE_EINVAL, "%s: out must be 16-byte aligned", fn);
+  // every offset inside the kernels is 32-bit: activation codes (with the
+  // scale rows padded to 128 per expert), weight codes and the output
+  REQUIRE(((long long)rows + (long long)E * 127) * K < (1ll << 32) &&
+              (long long)E * N * (long long)K < (1ll << 32) &&
+              (long long)rows * N * 2 < kMaxOutBytes,
+          MOE_EUNSUPPORTED, "%s: operands and output must stay below 4 GiB", fn);
   if (rows == 0) return ok();
   return hip_status(
       qmoe::launch_gemm_mxfp8(a_q, a_sf, w_q, w_sf, m_offsets, rows, K, N, E, out, stream), fn);
@@ -436,7 +450,8 @@ int moe_grouped_gemm_mxfp8_wgrad(const uint8_t *dyT_q, const uint8_t *dyT_sf,
   REQUIRE(aligned16(dyT_q) && aligned16(xT_q) && aligned16(dw) && ((uintptr_t)dyT_sf & 3u) == 0 &&
               ((uintptr_t)xT_sf & 3u) == 0,
           MOE_EINVAL, "%s: codes and output must be 16-byte and scales 4-byte aligned", fn);
-  REQUIRE((long long)E * N * (long long)K * 2 < (1ll << 40), MOE_EUNSUPPORTED, "%s: sizes", fn);
+  REQUIRE((long long)E * N * (long long)K * 2 < kMaxOutBytes, MOE_EUNSUPPORTED,
+          "%s: the weight gradient must stay below 4 GiB", fn);
   long long total = 0;
   for (int e = 0; e < E; ++e) {
     REQUIRE(m_splits[e] >= 0, MOE_EINVAL, "%s: m_splits[%d]=%d", fn, e, m_splits[e]);

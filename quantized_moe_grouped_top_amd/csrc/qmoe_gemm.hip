@@ -19,30 +19,33 @@
 //     last 8), for A and for B.
 // The accumulator tile has column (l & 15) and rows 4*(l >> 4) + 0..3 in lane l.
 //
-// Two kernels, both fed by direct-to-LDS DMA (global_load_lds_dwordx4):
+// Kernels in this file:
 //   stream_kernel (routed, block_m = 16): weight streaming for few rows per
 //                   expert (decode).  One persistent workgroup per CU owns an
-//                   expert and up to 7 consecutive 64-column tiles; weight
-//                   bytes are read from HBM once, all of the expert's rows
-//                   (64 per pass) ride along in the same LDS stages.
-//   gemm_kernel   (routed, block_m = 128, and MXFP8): 128-row x 256-column
-//                   MFMA tiles, 8 wavefronts of 64 x 64, operands of each
-//                   128-k stage DMA'd into a ring two stages ahead.  Tiles
-//                   are ordered expert by expert, column tile by column tile,
-//                   row block fastest, and split over the 8 XCDs in
-//                   contiguous chunks, so the workgroups resident on one XCD
-//                   share each weight tile through its L2.
+//                   expert and up to 7 consecutive 64-column tiles; each lane
+//                   loads exactly the weight pieces of its MFMA operands from
+//                   HBM into registers (buffer loads, up to three 128-k
+//                   stages ahead), so weight bytes are read once and never
+//                   pass through LDS; the expert's rows arrive in LDS by
+//                   direct-to-LDS DMA.
+//   gemm_big_kernel (routed fp8, block_m = 128, fewer than 384 rows per
+//                   expert): 256 x 256 tiles on eight wavefronts of 128 x 64,
+//                   operands DMA'd into an LDS ring.
+//   gemm_kernel   (routed int8 W8A16 and fp8 weight-only, block_m = 128):
+//                   128 x 256 tiles on eight wavefronts, weights converted to
+//                   bf16 in registers for the bf16 MFMA.
+// The fp8 W8A8 and int8 W8A8 GEMMs with at least 384 routed rows per expert
+// and the MXFP8 grouped linear (forward and weight gradient) run the 256 x
+// 256 tile kernel of qmoe_gemm_tile.hip.
 // Routed results are written per slot as bf16; MXFP8 rows as bf16.
-#include <atomic>
 
-#include "qmoe_internal.h"
+#include "qmoe_device.h"
 
 namespace qmoe {
 
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kXcds = 8;
 
 __device__ __forceinline__ f32x4 mfma_fp8(const i32x8 &a, const i32x8 &b, f32x4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
@@ -112,25 +115,6 @@ __device__ __forceinline__ i32x4 ld16(const void *p) {
   return *reinterpret_cast<const i32x4 *>(p);
 }
 
-// First block of every expert, from the ascending block labels: s_first[e] =
-// first b with expert_ids[b] >= e, for e in [0, E]; s_first[E] is the number
-// of blocks in use.  The labels are scanned over the whole buffer (max_blocks
-// entries, -1 after the last block), so the padded length is not needed first.
-// All threads of the workgroup take part (a few loads each, no serial search);
-// the caller synchronises before reading s_first.
-__device__ __forceinline__ void expert_block_starts(const int *__restrict__ expert_ids,
-                                                    int max_blocks, int E, int *s_first) {
-  for (int e = threadIdx.x; e <= E; e += blockDim.x) s_first[e] = max_blocks;
-  __syncthreads();
-  constexpr int kEnd = 1 << 30;                     // the -1 label sorts after every expert
-  for (int b = threadIdx.x; b < max_blocks; b += blockDim.x) {
-    int cur = expert_ids[b];
-    int prev = b > 0 ? expert_ids[b - 1] : -1;
-    cur = cur < 0 ? kEnd : cur;
-    prev = (b > 0 && prev < 0) ? kEnd : prev;
-    for (int e = prev + 1; e <= cur && e <= E; ++e) s_first[e] = b;
-  }
-}
 
 // =============================================================================
 // block_m = 16: weight streaming
@@ -178,39 +162,6 @@ struct SCfg {
   static constexpr int kAInstr = kABytes / 1024;            // DMA instructions for the rows
 };
 
-// global_load_lds_dwordx4: lane l copies 16 bytes from sbase + voff to LDS
-// byte address m0 + 16*l.
-__device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
-               : "memory", "m0");
-}
-
-// global_load_lds_dword: lane l copies 4 bytes from sbase + voff to LDS byte
-// address m0 + 4*l.
-__device__ __forceinline__ void dma4(const void *sbase, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 63] (0 for anything else)
-__device__ __forceinline__ void wait_dma_upto(int n) {
-  switch (n) {
-#define QMOE_W(k) case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
-#define QMOE_W8(b) QMOE_W(b) QMOE_W(b + 1) QMOE_W(b + 2) QMOE_W(b + 3) QMOE_W(b + 4) QMOE_W(b + 5) \
-    QMOE_W(b + 6) QMOE_W(b + 7)
-    QMOE_W(1) QMOE_W(2) QMOE_W(3) QMOE_W(4) QMOE_W(5) QMOE_W(6) QMOE_W(7)
-    QMOE_W8(8) QMOE_W8(16) QMOE_W8(24) QMOE_W8(32) QMOE_W8(40) QMOE_W8(48) QMOE_W8(56)
-#undef QMOE_W8
-#undef QMOE_W
-    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-  }
-}
 
 // 128-byte rows: 16-byte chunk c of row r sits at chunk c ^ swz(r);
 // 256-byte rows: at chunk c ^ (r & 15).  With these, the MFMA fragment reads
@@ -683,13 +634,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
   }
 }
 
-enum { kFmtFp8 = 0, kFmtInt8 = 1, kFmtMx = 2, kFmtI8 = 3, kFmtF8W16 = 4, kFmtMxW = 5 };
 
-// MXFP8 weight gradient: the padded row offset of every expert's columnwise
-// operands (P_e; P_E is the total), passed by value
-struct WgradSeg {
-  int po[kMaxExperts + 1];
-};
 
 // =============================================================================
 // block_m = 128 (fp8 W8A8, int8 W8A16) and MXFP8: DMA-fed MFMA tiles
@@ -1356,486 +1301,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gemm_big_kernel(
   }
 }
 
-// =============================================================================
-// fp8 W8A8 (block_m = 128) and MXFP8: 256 x 256 tiles on four wavefronts
-// =============================================================================
-// Same tiles, stages, LDS layout and DMA as gemm_big_kernel, but four
-// wavefronts (one per SIMD) of 128 x 128 outputs each, computed with
-// v_mfma_f32_32x32x64_f8f6f4: a wavefront's fragments of one 64-k half-stage
-// are 4 row and 4 column fragments (32 x 64 bytes), 16 MFMAs.  Against eight
-// 128 x 64 wavefronts this reads a third fewer LDS bytes per flop.
-//
-// Operand layout of the 32x32x64 f8f6f4 MFMA (checked on the device): lane
-// l = 32 g + r holds row (column) r, k 16g..16g+15 and 32+16g..32+16g+15 of
-// the half-stage; with block scales, lane 32 b + r supplies the scale of the
-// 32-k block b.  The result lane l holds column l % 32, rows
-// 8 (v / 4) + 4 g + v % 4 for accumulator v.  Fragment reads of 128-byte
-// rows with chunks swizzled by (r >> 1) & 7 are free of bank conflicts.
-//
-// Pipeline: the fragments of the next half-stage are read into the other
-// register set while the MFMAs of the current one run; the barrier that
-// hands a ring slot back to the DMA sits between the two halves of a stage,
-// after this wave's reads of the stage have completed.
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef int i32x16 __attribute__((ext_vector_type(16)));
-__device__ __forceinline__ f32x16 mfma32_fp8(const i32x8 &a, const i32x8 &b, f32x16 c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
-__device__ __forceinline__ f32x16 mfma32_mx(const i32x8 &a, const i32x8 &b, f32x16 c, int sa,
-                                            int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
-}
-
-// Tile queues of the persistent wide kernel: per launch slot, one counter
-// per XCD (the next unclaimed tile of that XCD's chunk) and a count of
-// finished workgroups.  The last workgroup of a launch sets them back to zero.
-constexpr int kLaunchSlots = 64;
-__device__ unsigned int g_tile_next[kLaunchSlots][kXcds];
-__device__ unsigned int g_tiles_done[kLaunchSlots];
-constexpr int kHwRegXccId = (31 << 11) | 20;           // s_getreg: XCC_ID, all 32 bits
-
-template <int kFmt, bool kTiled>
-__global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
-    const uint8_t *__restrict__ a, const float *__restrict__ a_scale,
-    const uint8_t *__restrict__ a_sf, const uint8_t *__restrict__ w,
-    const float *__restrict__ w_scale, const uint8_t *__restrict__ w_sf,
-    const int *__restrict__ sorted_ids, const int *__restrict__ expert_ids,
-    const float *__restrict__ topk_w, const int *__restrict__ m_offsets, int M, int K, int N,
-    int E, int top_k, int max_blocks, uint16_t *__restrict__ out, int launch_slot,
-    WgradSeg seg) {
-  // kFmtMxW, the weight gradient of the MXFP8 grouped linear: expert e's
-  // output rows are e*M .. e*M + M - 1 (dW_e [M, N]), its contraction runs
-  // over its Ke = seg.po[e+1] - seg.po[e] padded rows; operand rows are Ke
-  // bytes long, expert e's A block at M * P_e, its B block at N * P_e
-  constexpr bool kW = kFmt == kFmtMxW;
-  constexpr bool kMx = kFmt == kFmtMx || kW;
-  static_assert(kFmt != kFmtInt8, "int8 W8A16 uses gemm_kernel");
-  constexpr int kWaves = 4;
-  constexpr int kThr = 64 * kWaves;
-  constexpr int kDma = 32 / kWaves;                      // activation (and weight) DMAs per wave
-  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[2 * kHStage];
-  __shared__ __attribute__((aligned(16))) uint8_t s_sf[kMx ? 2 * kHSf : 16];
-  __shared__ int s_row[kHBM];
-  __shared__ float s_rs[kMx ? 1 : kHBM];               // per-row output scale (not MXFP8)
-  __shared__ __attribute__((aligned(16))) float s_cs[kFmt == kFmtI8 ? kHBN : 4];  // int8: per column
-  __shared__ int s_blk_first[kMaxExperts + 1];
-  __shared__ int s_tile_first[kMaxExperts + 1];
-  __shared__ int s_mo[kMx ? kMaxExperts + 1 : 1];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
-  const int g = lane >> 5, r32 = lane & 31;
-  const int ntn = (N + kHBN - 1) / kHBN;
-
-  // ---- tile space: expert by expert, column tile by column tile, block pair
-  // fastest; each XCD takes one contiguous chunk of it
-  if constexpr (!kMx) {
-    expert_block_starts(expert_ids, max_blocks, E, s_blk_first);
-    __syncthreads();
-  }
-  if (tid == 0) {
-    int blk = 0, tiles = 0;
-    for (int ee = 0; ee < E; ++ee) {
-      int nb;
-      if constexpr (kMx) {
-        // no m_offsets: one segment of all M rows (a single expert); the
-        // weight gradient: M rows per expert
-        if constexpr (kW) {
-          s_mo[ee] = ee * M;
-          s_mo[ee + 1] = (ee + 1) * M;
-        } else {
-          s_mo[ee] = m_offsets ? m_offsets[ee] : 0;
-          s_mo[ee + 1] = m_offsets ? m_offsets[ee + 1] : M;
-        }
-        const int m = s_mo[ee + 1] - s_mo[ee];
-        nb = m > 0 ? (m + kGBM - 1) / kGBM : 0;
-        s_blk_first[ee] = blk;
-        blk += nb;
-      } else {
-        nb = s_blk_first[ee + 1] - s_blk_first[ee];
-      }
-      s_tile_first[ee] = tiles;
-      tiles += (nb + 1) / 2 * ntn;
-    }
-    if constexpr (kMx) s_blk_first[E] = blk;
-    s_tile_first[E] = tiles;
-  }
-  __syncthreads();
-  // ---- persistent workgroups: each XCD owns one contiguous chunk of the
-  // tile space; a workgroup takes the next tile of its own XCD's chunk (tiles
-  // of one chunk share weights and activations in that XCD's L2), then helps
-  // the other XCDs once its own chunk is done
-  const int total = s_tile_first[E];
-  const int chunk = (total + kXcds - 1) / kXcds;
-  const int my_xcc = (int)(__builtin_amdgcn_s_getreg(kHwRegXccId) & (kXcds - 1));
-  __shared__ int s_next;
-  const int S = M * top_k;
-  // thread 0 claims a tile's successor (from the same queue) just before the
-  // tile's epilogue, so that the atomic's latency passes while the epilogue
-  // runs; -1: nothing claimed ahead
-  int ahead = -1;
-  for (int qx = 0; qx < kXcds; ++qx) {
-  const int xq = (my_xcc + qx) & (kXcds - 1);
-  const int n_x = min(chunk, total - xq * chunk);
-  for (;;) {
-  if (tid == 0) {
-    s_next = ahead >= 0 ? ahead : (n_x > 0 ? (int)atomicAdd(&g_tile_next[launch_slot][xq], 1u) : n_x);
-    ahead = -1;
-  }
-  __syncthreads();
-  const int tile_t = s_next;
-  __syncthreads();                                      // (s_next is rewritten next round)
-  if (tile_t >= n_x) break;
-  const int L = xq * chunk + tile_t;
-  // lane-derived values are recomputed per tile from an opaque copy of the
-  // lane index, so that the compiler does not keep them live across tiles
-  int lane_opaque = lane;
-  asm volatile("" : "+v"(lane_opaque));
-  const int lane = lane_opaque;                         // shadows the kernel-wide one
-  const int g = lane >> 5, r32 = lane & 31;
-  int e = 0;
-  while (s_tile_first[e + 1] <= L) ++e;
-  const int nblk = s_blk_first[e + 1] - s_blk_first[e];
-  const int npair = (nblk + 1) / 2;
-  const int local = L - s_tile_first[e];
-  const int nt = local / npair;
-  const int pr = local - nt * npair;
-  const int nb_here = min(2, nblk - 2 * pr);            // 128-row blocks in this tile
-  const int n0 = nt * kHBN;
-  int row0 = 0, row_end = 0;                            // MXFP8: the tile's rows
-  for (int r = tid; r < kHBM; r += kThr) {
-    if constexpr (kMx) {
-      row0 = s_mo[e] + 2 * pr * kGBM;
-      s_row[r] = row0 + r;
-    } else {
-      const int slot = r < nb_here * kGBM ? sorted_ids[(s_blk_first[e] + 2 * pr) * kGBM + r] : S;
-      s_row[r] = slot;
-      // the epilogue's row scale: activation x weight scale x router weight
-      // (int8 W8A8: the token's scale x router weight; the weight scale is
-      // per column)
-      if constexpr (kFmt == kFmtI8)
-        s_rs[r] = slot < S ? a_scale[slot / top_k] * topk_w[slot] : 0.0f;
-      else
-        s_rs[r] = slot < S ? a_scale[0] * w_scale[e] * topk_w[slot] : 0.0f;
-    }
-  }
-  if constexpr (kFmt == kFmtI8) {
-    for (int c = tid; c < kHBN; c += kThr) s_cs[c] = w_scale[(size_t)e * N + min(n0 + c, N - 1)];
-  }
-  if constexpr (kMx) {
-    row0 = s_mo[e] + 2 * pr * kGBM;
-    row_end = s_mo[e + 1];
-  }
-  __syncthreads();
-  auto src_row = [&](int r) -> uint32_t {
-    const int v = s_row[r];
-    if constexpr (kMx) return (uint32_t)(v < row_end ? v : row_end - 1);
-    else return (uint32_t)(v < S ? v / top_k : 0);
-  };
-  const bool a_dma = (8 * kDma * wave) / kGBM < nb_here;  // this wave's DMA rows exist
-  const bool busy = wm < nb_here;                       // this wave's 128 output rows exist
-
-  // ---- DMA sources of this lane (as gemm_big_kernel) -------------------------
-  const uint32_t lds_ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)s_ring;
-  // the contraction of this tile: K, or the expert's padded rows (weight gradient)
-  const int Ke = kW ? seg.po[e + 1] - seg.po[e] : K;
-  const int nst = Ke / 128;
-  const uint32_t pe = kW ? (uint32_t)seg.po[e] : 0u;
-  uint32_t a_off[kDma];
-#pragma unroll
-  for (int u = 0; u < kDma; ++u) {
-    const int r = 8 * (kDma * wave + u) + (lane >> 3);
-    const uint32_t chunk = 16u * (uint32_t)((lane & 7) ^ swz(r));
-    if constexpr (kW) a_off[u] = (uint32_t)M * pe + (src_row(r) - (uint32_t)s_mo[e]) * (uint32_t)Ke + chunk;
-    else a_off[u] = src_row(r) * (uint32_t)K + chunk;
-  }
-  // weights: wave w loads the 64-column block w of the tile, 8 x 1 KB
-  uint32_t wblk = 0;
-  uint32_t b_off[kDma];
-  if constexpr (kTiled) {
-    const int T = (N + 63) / 64;
-    const int pt = min(n0 / 64 + wave, T - 1);
-    wblk = ((uint32_t)e * (uint32_t)T + (uint32_t)pt) * (uint32_t)nst * 8192u;
-  } else {
-#pragma unroll
-    for (int u = 0; u < kDma; ++u) {
-      const int n = 8 * u + (lane >> 3);
-      const int col = min(n0 + wave * 64 + n, N - 1);
-      const uint32_t chunk = 16u * (uint32_t)((lane & 7) ^ swz(n));
-      if constexpr (kW) b_off[u] = (uint32_t)N * pe + (uint32_t)col * (uint32_t)Ke + chunk;
-      else b_off[u] = ((uint32_t)e * (uint32_t)N + (uint32_t)col) * (uint32_t)K + chunk;
-    }
-  }
-  // MXFP8 scales: 8 dword DMAs per stage (rows 0-255, then columns 0-255, 64
-  // per DMA), two per wavefront
-  constexpr int kSfPerWave = 8 / kWaves;
-  const uint32_t kb_row = (uint32_t)Ke / 32u;
-  uint32_t sf_off[kSfPerWave];
-  bool sf_on[kSfPerWave];
-  if constexpr (kMx) {
-    int po = 0;
-    for (int ee = 0; ee < e; ++ee) po += (s_mo[ee + 1] - s_mo[ee] + kMxRowPad - 1) / kMxRowPad * kMxRowPad;
-#pragma unroll
-    for (int u = 0; u < kSfPerWave; ++u) {
-      const int q = kSfPerWave * wave + u;             // 0-3 rows, 4-7 columns
-      if (q < 4) {
-        const uint32_t rr = src_row(64 * q + lane) - (uint32_t)s_mo[e];
-        if constexpr (kW) sf_off[u] = (uint32_t)M * pe / 32u + rr * kb_row;
-        else sf_off[u] = ((uint32_t)po + rr) * kb_row;
-        sf_on[u] = (64 * q) / kGBM < nb_here;
-      } else {
-        const uint32_t cc = (uint32_t)min(n0 + 64 * (q - 4) + lane, N - 1);
-        if constexpr (kW) sf_off[u] = (uint32_t)N * pe / 32u + cc * kb_row;
-        else sf_off[u] = ((uint32_t)e * (uint32_t)N + cc) * kb_row;
-        sf_on[u] = true;
-      }
-    }
-  }
-  const uint32_t lds_sf = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)s_sf;
-
-  // DMA pieces of stage st into ring slot slot_i: q = 0..7 activation rows
-  // (1 KB each), 8..15 weight rows, 16..17 MXFP8 scale dwords.  Every piece is
-  // issued (rows past the tile's last block reload clamped rows), so the
-  // main loop has no branches.
-  auto issue_piece = [&](int st, int slot_i, int q) {
-    const uint32_t base = lds_ring + (uint32_t)(slot_i * kHStage);
-    if (q < kDma) {
-      dma16(a + (size_t)st * 128u, a_off[q], base + (uint32_t)((kDma * wave + q) * 1024));
-    } else if (q < 2 * kDma) {
-      const int u = q - kDma;
-      const uint32_t bdst = base + (uint32_t)(kHABytes + (kDma * wave + u) * 1024);
-      if constexpr (kTiled) dma16(w + wblk + (size_t)st * 8192u, (uint32_t)(u * 1024 + 16 * lane), bdst);
-      else dma16(w + (size_t)st * 128u, b_off[u], bdst);
-    } else if constexpr (kMx) {
-      const int u = q - 2 * kDma;
-      const int qq = kSfPerWave * wave + u;
-      dma4((qq < 4 ? a_sf : w_sf) + 4 * st, sf_off[u],
-           lds_sf + (uint32_t)(slot_i * kHSf) + (uint32_t)(256 * qq));
-    }
-  };
-  constexpr int kPieces = 2 * kDma + (kMx ? kSfPerWave : 0);
-  auto issue = [&](int st, int slot_i) {
-#pragma unroll
-    for (int q = 0; q < kPieces; ++q) issue_piece(st, slot_i, q);
-  };
-
-  // ---- fragments of one half-stage and their MFMAs -------------------------
-  // Sixteen 16-byte LDS reads per half-stage (part q: fragment q >> 2;
-  // activation low / high half, weight low / high half), read one per MFMA.
-  struct Frags {
-    i32x4 alo[4], ahi[4], blo[4], bhi[4];
-    int sa[4], sb[4];
-  };
-  const int sw = swz(r32);
-  auto read_part = [&](int slot_i, int h, Frags &f, int q) {
-    const int i = q >> 2, part = q & 3;
-    const uint8_t *base = s_ring + slot_i * kHStage +
-                          (part < 2 ? wm * 128 * 128 : kHABytes + wn * 128 * 128) + (32 * i + r32) * 128;
-    const int c = (((4 * h + g + ((part & 1) ? 2 : 0)) ^ sw) << 4);
-    const i32x4 v = ld16(base + c);
-    if (part == 0) f.alo[i] = v;
-    else if (part == 1) f.ahi[i] = v;
-    else if (part == 2) f.blo[i] = v;
-    else f.bhi[i] = v;
-  };
-  auto read_scales = [&](int slot_i, int h, Frags &f) {
-    if constexpr (kMx) {
-      const uint8_t *sfs = s_sf + slot_i * kHSf;
-      const int sh = 8 * (2 * h + g);                   // lane group g: 32-k block 2h + g
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f.sa[i] = (int)((*reinterpret_cast<const uint32_t *>(sfs + 4 * (wm * 128 + 32 * i + r32)) >> sh) & 0xFFu);
-        f.sb[i] = (int)((*reinterpret_cast<const uint32_t *>(sfs + 4 * kHBM + 4 * (wn * 128 + 32 * i + r32)) >> sh) & 0xFFu);
-      }
-    }
-  };
-  auto read_frags = [&](int slot_i, int h, Frags &f) {
-#pragma unroll
-    for (int q = 0; q < 16; ++q) read_part(slot_i, h, f, q);
-    read_scales(slot_i, h, f);
-  };
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-  // The weight fragment is the MFMA's first operand: lane 32 g + r then
-  // holds output row r of the activation fragment and, for accumulator
-  // 4 k + c, column 8 k + 4 g + c of the weight fragment (four neighbouring
-  // columns per k), which the epilogue stores as 8-byte pieces.
-  auto mfma_q = [&](const Frags &f, int q) {
-    const int i = q >> 2, j = q & 3;
-    const i32x8 av = __builtin_shufflevector(f.alo[i], f.ahi[i], 0, 1, 2, 3, 4, 5, 6, 7);
-    const i32x8 bv = __builtin_shufflevector(f.blo[j], f.bhi[j], 0, 1, 2, 3, 4, 5, 6, 7);
-    if constexpr (kMx) {
-      acc[i][j] = mfma32_mx(bv, av, acc[i][j], f.sb[j], f.sa[i]);
-    } else if constexpr (kFmt == kFmtI8) {
-      // two 32x32x32 int8 MFMAs over the two 16-byte halves (A and B share
-      // the k placement); int32 accumulators carried as raw bits
-      i32x16 ci = __builtin_bit_cast(i32x16, acc[i][j]);
-      ci = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.blo[j], f.alo[i], ci, 0, 0, 0);
-      ci = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.bhi[j], f.ahi[i], ci, 0, 0, 0);
-      acc[i][j] = __builtin_bit_cast(f32x16, ci);
-    } else {
-      acc[i][j] = mfma32_fp8(bv, av, acc[i][j]);
-    }
-  };
-  auto pin_acc = [&]() {     // the accumulators are "used" here: no MFMA sinks past
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
-  };
-
-  // ---- two-slot ring, half-stage register pipeline ----------------------------
-  // Per stage: the 16 MFMAs of half 0 run with the 16 reads of half 1 between
-  // them; then the barrier that frees the stage's slot; then the 16 MFMAs of
-  // half 1 with the DMA pieces of stage st + 2 and the reads of the next
-  // stage's half 0 between them (one memory instruction per 64-cycle MFMA,
-  // the rate the memory pipeline takes them at).  A wavefront whose 128 rows
-  // do not exist (the tile's second block is missing) computes on stale LDS
-  // rows and drops the results, so every wavefront runs the same stream.
-  if (!kW || nst > 0) {                                 // (an expert without rows: zeros)
-  Frags fa, fb;
-  issue(0, 0);
-  if (nst > 1) {
-    issue(1, 1);
-    wait_dma_upto(kPieces);                             // leave stage 1 in flight
-  } else {
-    wait_dma_all();
-  }
-  __syncthreads();                                      // stage 0 landed everywhere
-  read_frags(0, 0, fa);
-  for (int st = 0; st + 1 < nst; ++st) {
-    const int slot = st & 1;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      mfma_q(fa, q);
-      read_part(slot, 1, fb, q);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    read_scales(slot, 1, fb);
-    pin_acc();
-    // this wave's reads of slot `slot` are complete; stage st + 1 (the only
-    // DMA outstanding) has landed here; after the barrier it has landed
-    // everywhere and nobody reads slot `slot` any more
-    __builtin_amdgcn_s_waitcnt(0xC07F);               // lgkmcnt(0)
-    wait_dma_all();
-    __syncthreads();
-    const int st2 = st + 2 < nst ? st + 2 : nst - 1;    // past the end: a harmless reload
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      mfma_q(fb, q);
-      issue_piece(st2, slot, q);
-      read_part(slot ^ 1, 0, fa, q);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int q = 16; q < kPieces; ++q) issue_piece(st2, slot, q);
-    read_scales(slot ^ 1, 0, fa);
-    pin_acc();
-    __builtin_amdgcn_s_waitcnt(0xC07F);               // lgkmcnt(0): fa arrived
-  }
-  {
-    const int slot = (nst - 1) & 1;                     // the last stage
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      mfma_q(fa, q);
-      read_part(slot, 1, fb, q);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    read_scales(slot, 1, fb);
-    pin_acc();
-    __builtin_amdgcn_s_waitcnt(0xC07F);               // lgkmcnt(0)
-#pragma unroll
-    for (int q = 0; q < 16; ++q) mfma_q(fb, q);
-  }
-  }  // stages
-  wait_dma_all();                                       // the reload must land before the ring is reused
-
-  // ---- epilogue: per wavefront, in two halves of 64 rows: bf16 results ->
-  // the wavefront's 16 KB of ring slot 1 (rows of 256 bytes, 16-byte chunk c
-  // of row r at c ^ (r & 15)) -> whole 256-byte row segments in HBM.  Only
-  // the wavefront itself reads its staging area, so no workgroup barrier.
-  __syncthreads();                                      // the ring is no longer read
-  if (tid == 0) ahead = (int)atomicAdd(&g_tile_next[launch_slot][xq], 1u);
-  if (busy) {
-  uint8_t *stg = s_ring + kHStage + wave * 16384;
-  const bool vec = (N & 7) == 0 && ((uintptr_t)out & 15u) == 0;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-      const int i = 2 * h + ii;
-      const int lr = ii * 32 + r32;                     // staging row
-      float rs = 1.0f;
-      if constexpr (!kMx) rs = s_rs[wm * 128 + 32 * i + r32];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          f32x4 c;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) c[u] = acc[i][j][4 * k + u];
-          if constexpr (kFmt == kFmtI8) {
-            // int32 -> float, times the four columns' weight scales
-            const f32x4 cs = *reinterpret_cast<const f32x4 *>(&s_cs[wn * 128 + 32 * j + 8 * k + 4 * g]);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const float raw = c[u];                   // (bit-cast a scalar, not an element)
-              c[u] = (float)__builtin_bit_cast(int, raw) * cs[u];
-            }
-          }
-          i32x2 pk;
-          pk[0] = (int)f32x2_to_bf16x2(c[0] * rs, c[1] * rs);
-          pk[1] = (int)f32x2_to_bf16x2(c[2] * rs, c[3] * rs);
-          *reinterpret_cast<i32x2 *>(stg + lr * 256 + (((4 * j + k) ^ (lr & 15)) << 4) + 8 * g) = pk;
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0): the wave's LDS writes done
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll 4
-    for (int q = 0; q < 16; ++q) {                      // 4 rows of 16 lanes x 8 columns
-      const int lr = q * 4 + lane / 16;
-      const int c = lane % 16;
-      const int r = 64 * h + lr;                        // row within the wave's 128
-      const int col = n0 + wn * 128 + c * 8;
-      int dst_row;
-      if constexpr (kMx) {
-        dst_row = row0 + wm * 128 + r;
-        if (dst_row >= row_end) continue;
-      } else {
-        dst_row = s_row[wm * 128 + r];
-        if (dst_row >= S) continue;
-      }
-      if (col >= N) continue;
-      const uint8_t *src = stg + lr * 256 + ((c ^ (lr & 15)) << 4);
-      uint16_t *dst = out + (size_t)dst_row * N + col;
-      if (vec && col + 8 <= N) {
-        *reinterpret_cast<i32x4 *>(dst) = *reinterpret_cast<const i32x4 *>(src);
-      } else {
-        const uint16_t *s16 = reinterpret_cast<const uint16_t *>(src);
-        for (int cc = 0; cc < 8 && col + cc < N; ++cc) dst[cc] = s16[cc];
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0): staging read before reuse
-    __builtin_amdgcn_wave_barrier();
-  }
-  }  // busy
-  }  // tiles of chunk xq
-  }  // chunks
-  if (tid == 0) {
-    __threadfence();
-    if (atomicAdd(&g_tiles_done[launch_slot], 1u) == gridDim.x - 1) {
-      for (int x = 0; x < kXcds; ++x) atomicExch(&g_tile_next[launch_slot][x], 0u);
-      atomicExch(&g_tiles_done[launch_slot], 0u);
-    }
-  }
-}
-
 unsigned tile_grid(long long tiles_bound) {
   long long per = (tiles_bound + kXcds - 1) / kXcds;
   return (unsigned)(per * kXcds);
@@ -1862,20 +1327,6 @@ int num_cus() {
 // where the four-wavefront kernel (one per SIMD) would leave half the MFMA
 // units to a block that does not exist.
 constexpr long long kWideMinRowsPerExpert = 384;
-
-// persistent wide-kernel grid: one workgroup per CU (at most one fits), no
-// more than there can be tiles
-unsigned wide_grid(long long tiles_bound) {
-  const long long n = num_cus();
-  return (unsigned)(tiles_bound < n ? (tiles_bound > 0 ? tiles_bound : 1) : n);
-}
-
-// launch slot of the wide kernel's tile queues: launches that may run at
-// the same time on one device must use different slots
-int next_launch_slot() {
-  static std::atomic<unsigned> seq{0};
-  return (int)(seq.fetch_add(1u, std::memory_order_relaxed) % (unsigned)kLaunchSlots);
-}
 
 // persistent decomposition of the weight stream: E * groups workgroups, each
 // with tiles_per_group consecutive 64-column tiles of one expert
@@ -1914,6 +1365,29 @@ void stream_grid(int N, int E, int &groups, int &tiles_per_group) {
 }
 }  // namespace
 
+namespace {
+TileArgs routed_tile_args(const uint8_t *a, const float *a_scale, const uint8_t *w,
+                          const float *w_scale, const RoutedArgs &r) {
+  TileArgs t{};
+  t.a = a;
+  t.a_scale = a_scale;
+  t.w = w;
+  t.w_scale = w_scale;
+  t.sorted_ids = r.sorted_ids;
+  t.expert_ids = r.expert_ids;
+  t.topk_w = r.topk_w;
+  t.out = r.y;
+  t.out_bytes = (uint32_t)((unsigned long long)r.M * r.top_k * r.N * 2ull);
+  t.M = r.M;
+  t.K = r.K;
+  t.N = r.N;
+  t.E = r.E;
+  t.top_k = r.top_k;
+  t.max_blocks = r.max_blocks;
+  return t;
+}
+}  // namespace
+
 hipError_t launch_gemm_fp8(const uint8_t *a_q, const float *a_scale, const uint8_t *w_q,
                            const float *w_scale, const RoutedArgs &r, hipStream_t s) {
   if (r.block_m == 16) {
@@ -1926,10 +1400,8 @@ hipError_t launch_gemm_fp8(const uint8_t *a_q, const float *a_scale, const uint8
   } else {
     const long long tiles = (long long)(r.max_blocks / 2 + r.E) * ((r.N + kHBN - 1) / kHBN);
     if ((long long)r.M * r.top_k >= kWideMinRowsPerExpert * (long long)r.E) {
-      auto k = r.w_layout ? gemm_wide_kernel<kFmtFp8, true> : gemm_wide_kernel<kFmtFp8, false>;
-      hipLaunchKernelGGL(k, dim3(wide_grid(tiles)), dim3(256), 0, s, a_q, a_scale, nullptr, w_q,
-                         w_scale, nullptr, r.sorted_ids, r.expert_ids, r.topk_w, nullptr, r.M,
-                         r.K, r.N, r.E, r.top_k, r.max_blocks, r.y, next_launch_slot(), WgradSeg{});
+      return launch_tile_gemm(kFmtFp8, r.w_layout == MOE_W_TILED,
+                              routed_tile_args(a_q, a_scale, w_q, w_scale, r), nullptr, tiles, s);
     } else {
       auto k = r.w_layout ? gemm_big_kernel<kFmtFp8, true, kHWaves>
                           : gemm_big_kernel<kFmtFp8, false, kHWaves>;
@@ -1954,10 +1426,8 @@ hipError_t launch_gemm_int8w8a8(const int8_t *a_q, const float *a_scale, const i
                        groups, tpg, r.max_blocks, r.y, stream_weight_bytes(r));
   } else {
     const long long tiles = (long long)(r.max_blocks / 2 + r.E) * ((r.N + kHBN - 1) / kHBN);
-    auto k = r.w_layout ? gemm_wide_kernel<kFmtI8, true> : gemm_wide_kernel<kFmtI8, false>;
-    hipLaunchKernelGGL(k, dim3(wide_grid(tiles)), dim3(256), 0, s, ab, a_scale, nullptr, wb,
-                       w_scale, nullptr, r.sorted_ids, r.expert_ids, r.topk_w, nullptr, r.M, r.K,
-                       r.N, r.E, r.top_k, r.max_blocks, r.y, next_launch_slot(), WgradSeg{});
+    return launch_tile_gemm(kFmtI8, r.w_layout == MOE_W_TILED,
+                            routed_tile_args(ab, a_scale, wb, w_scale, r), nullptr, tiles, s);
   }
   return hipGetLastError();
 }
@@ -2029,10 +1499,19 @@ hipError_t launch_gemm_mxfp8_wgrad(const uint8_t *dyT_q, const uint8_t *dyT_sf, 
   // per expert ceil(N / 128) row blocks, in pairs, times ceil(K / 256) column tiles
   const long long pairs = (long long)E * (((N + kGBM - 1) / kGBM + 1) / 2);
   const long long tiles = pairs * ((K + kHBN - 1) / kHBN);
-  hipLaunchKernelGGL((gemm_wide_kernel<kFmtMxW, false>), dim3(wide_grid(tiles)), dim3(256), 0, s,
-                     dyT_q, nullptr, dyT_sf, xT_q, nullptr, xT_sf, nullptr, nullptr, nullptr, nullptr,
-                     N, 0, K, E, 1, 0, dw, next_launch_slot(), seg);
-  return hipGetLastError();
+  TileArgs a{};
+  a.a = dyT_q;
+  a.a_sf = dyT_sf;
+  a.w = xT_q;
+  a.w_sf = xT_sf;
+  a.out = dw;
+  a.out_bytes = (uint32_t)((unsigned long long)E * N * K * 2ull);
+  a.M = N;          // output rows per expert (dW_e is [N, K])
+  a.K = 0;          // per expert: the padded row count of its segment
+  a.N = K;
+  a.E = E;
+  a.top_k = 1;
+  return launch_tile_gemm(kFmtMxW, false, a, &seg, tiles, s);
 }
 
 hipError_t launch_gemm_mxfp8(const uint8_t *a_q, const uint8_t *a_sf, const uint8_t *w_q,
@@ -2041,10 +1520,20 @@ hipError_t launch_gemm_mxfp8(const uint8_t *a_q, const uint8_t *a_sf, const uint
   // block pairs: at most (sum of blocks + E) / 2 + E
   const long long pairs = ((rows + kGBM - 1) / kGBM + E) / 2 + E;
   const long long tiles = pairs * ((N + kHBN - 1) / kHBN);
-  hipLaunchKernelGGL((gemm_wide_kernel<kFmtMx, false>), dim3(wide_grid(tiles)), dim3(256), 0, s,
-                     a_q, nullptr, a_sf, w_q, nullptr, w_sf, nullptr, nullptr, nullptr, m_offsets,
-                     rows, K, N, E, 1, 0, out, next_launch_slot(), WgradSeg{});
-  return hipGetLastError();
+  TileArgs a{};
+  a.a = a_q;
+  a.a_sf = a_sf;
+  a.w = w_q;
+  a.w_sf = w_sf;
+  a.m_offsets = m_offsets;
+  a.out = out;
+  a.out_bytes = (uint32_t)((unsigned long long)rows * N * 2ull);
+  a.M = rows;
+  a.K = K;
+  a.N = N;
+  a.E = E;
+  a.top_k = 1;
+  return launch_tile_gemm(kFmtMx, false, a, nullptr, tiles, s);
 }
 
 }  // namespace qmoe

@@ -115,6 +115,23 @@ def test_gemm_int8_and_mxfp8_reject():
     with pytest.raises(qm.MoeError) as ei:
         qm.moe_grouped_gemm_mxfp8(FAKE, MIS, FAKE, FAKE, FAKE, 100, 256, 64, 4, FAKE, stream=0)
     assert ei.value.code == qm.MOE_EINVAL                       # misaligned scales
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_grouped_gemm_mxfp8(FAKE, FAKE, FAKE, FAKE, FAKE, 100, 256, 68, 4, FAKE, stream=0)
+    assert ei.value.code == qm.MOE_EUNSUPPORTED                 # N % 8
+    # 32-bit offsets: weight codes E*N*K, activation codes with padded scale
+    # rows, and the output must each stay below 4 GiB
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_grouped_gemm_mxfp8(FAKE, FAKE, FAKE, FAKE, FAKE, 1000, 16384, 32768, 8, FAKE,
+                                  stream=0)
+    assert ei.value.code == qm.MOE_EUNSUPPORTED                 # 8 * 32768 * 16384 bytes
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_grouped_gemm_mxfp8(FAKE, FAKE, FAKE, FAKE, FAKE, 300000, 16384, 64, 1, FAKE,
+                                  stream=0)
+    assert ei.value.code == qm.MOE_EUNSUPPORTED                 # activation codes past 4 GiB
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_grouped_gemm_mxfp8(FAKE, FAKE, FAKE, FAKE, FAKE, 70000, 128, 32768, 1, FAKE,
+                                  stream=0)
+    assert ei.value.code == qm.MOE_EUNSUPPORTED                 # bf16 output past 4 GiB
 
 
 def test_gemm_int8w8a8_and_int8_activation_quantizer_reject():

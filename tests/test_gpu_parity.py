@@ -697,11 +697,11 @@ def test_expert_ffn_mxfp8_chain():
     MXFP8 (per-expert padded scales) -> down GEMM [rows, N2] bf16.  Checked
     stage by stage through the chained buffers: the up projection against the
     oracle's, and the output against the oracle's activation + down
-    projection of the device's own up-projection rows.  (An end-to-end
-    comparison against the oracle's separate chain is only reported: a bf16
-    unit of difference in an intermediate value can move an e4m3 code or a
-    block scale of the re-quantized activation, which the down projection
-    then carries.)"""
+    projection of the device's own up-projection rows.  No end-to-end bar
+    against the oracle's separate chain: a bf16 unit of difference in an
+    intermediate value can move an e4m3 code or a block scale of the
+    re-quantized activation, so the two chains may legitimately differ by
+    more than the per-stage bound."""
     seg, K, H, N2 = (100, 37, 0, 200), 256, 128, 192
     what = f"ffn mxfp8 seg={seg} K={K} H={H} N2={N2}"
     _announce(what)
@@ -739,13 +739,6 @@ def test_expert_ffn_mxfp8_chain():
     # the oracle's float32 result: the device's output is its bf16 rounding
     ref32 = O.grouped_gemm_mxfp8(q2_r, sf2_r, w2q_r, w2s_r, mo_np, as_float32=True)
     assert_bf16_out(bits16(out), ref32, F.bf16_round(ref32), what + " down")
-    # end to end against the oracle's own chain: reported
-    q2_e, sf2_e = O.act_quantize_mxfp8(y1_ref, mo_np, O.ACT_SWIGLU)
-    e2e = F.bf16_decode(O.grouped_gemm_mxfp8(q2_e, sf2_e, w2q_r, w2s_r, mo_np))
-    rms = float(np.sqrt(np.mean(e2e ** 2)))
-    print(f"  {what}: end to end max|gpu-oracle chain|/rms = "
-          f"{np.max(np.abs(F.bf16_decode(bits16(out)) - e2e)) / rms:.3e}; activation codes "
-          f"differing from the oracle chain's: {np.mean(q2.cpu().numpy() != q2_e):.2e}")
 
 
 def test_expert_ffn_fp8_routed_chain():

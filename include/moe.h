@@ -189,6 +189,21 @@ int moe_quantize_act(const uint16_t *x, int rows, int K, int mode,
                      const int *m_offsets, int E, uint8_t *q, float *scale,
                      uint8_t *scale_e8m0, void *workspace, hipStream_t stream);
 
+/* Allocation-free variant of moe_quantize_act, for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments,
+ * results and errors as moe_quantize_act without `workspace`: the partial
+ * maxima of MOE_Q_FP8_PER_TENSOR go to a static device array of the library
+ * (4 KiB per device, kept until the process ends; its address is looked up on
+ * the first call on each device, which is not graph-capturable), whose
+ * capacity covers any tensor size (MOE_EUNSUPPORTED if a mode needed more).
+ * The other modes use no scratch.  Nothing is allocated and nothing needs to
+ * start at zero.  Calls that overlap on one device share the array and race:
+ * serialize them (one stream, or events between streams). */
+int moe_quantize_act_noalloc(const uint16_t *x, int rows, int K, int mode,
+                             const int *m_offsets, int E, uint8_t *q, float *scale_fp32,
+                             uint8_t *scale_e8m0, hipStream_t stream);
+
 /* Activation fused with its quantization: the expert FFN's step between the
  * up and the down projection ("[PyTorch] Let GroupedLinear accept MXFP8 input
  * and gradient", Description: SwiGLU / SReLU + MXFP8 quantization of an

@@ -28,7 +28,8 @@ MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_SLOTS = 128, 8, 65536
 EXPORTS = [
     "moe_last_error", "moe_last_hip_error", "moe_align_max_padded", "moe_recommended_block_m",
     "moe_quantize_workspace_bytes", "moe_packed_weight_bytes", "moe_mx_scale_rows",
-    "moe_align_block_size", "moe_quantize_act", "moe_act_quantize", "moe_quantize_weights",
+    "moe_align_block_size", "moe_quantize_act", "moe_quantize_act_noalloc", "moe_act_quantize",
+    "moe_quantize_weights",
     "moe_pack_weights",
     "moe_grouped_gemm_fp8w8a8",
     "moe_grouped_gemm_int8w8a8", "moe_grouped_gemm_fp8w8a16", "moe_grouped_gemm_int4w4a16",
@@ -62,6 +63,7 @@ _SIGS = {
     "moe_mx_scale_rows": (_I, [_I, _I]),
     "moe_align_block_size": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "moe_quantize_act": (_I, [_P, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P]),
+    "moe_quantize_act_noalloc": (_I, [_P, _I, _I, _I, _P, _I, _P, _P, _P, _P]),
     "moe_act_quantize": (_I, [_P, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P]),
     "moe_quantize_weights": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "moe_grouped_gemm_fp8w8a8": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
@@ -153,6 +155,12 @@ def moe_quantize_act(x, rows, K, mode, m_offsets, E, q, scale, scale_e8m0, works
     return _check(lib().moe_quantize_act(
         _ptr(x), rows, K, mode, _ptr(m_offsets), E, _ptr(q), _ptr(scale), _ptr(scale_e8m0),
         _ptr(workspace), _stream(stream)))
+
+
+def moe_quantize_act_noalloc(x, rows, K, mode, m_offsets, E, q, scale, scale_e8m0, stream=None):
+    return _check(lib().moe_quantize_act_noalloc(
+        _ptr(x), rows, K, mode, _ptr(m_offsets), E, _ptr(q), _ptr(scale), _ptr(scale_e8m0),
+        _stream(stream)))
 
 
 def moe_act_quantize(x, rows, H, act, mode, m_offsets, E, q, scale, scale_e8m0, workspace,

@@ -6,6 +6,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "qmoe_internal.h"
 
 namespace {
@@ -94,6 +96,35 @@ int check_routed_gemm(const void *a, const void *w, const void *w_scale, int w_l
           "%s: activation tensor must stay below 4 GiB", fn);
   REQUIRE((long long)M * top_k * (long long)N * 2 < kMaxOutBytes, MOE_EUNSUPPORTED,
           "%s: per-slot results must stay below 4 GiB", fn);
+  return MOE_OK;
+}
+
+// ---- scratch of moe_quantize_act_noalloc ------------------------------------
+// The per-tensor fp8 quantizer's partial maxima live in this device array
+// instead of a caller workspace.  Host code never uses the array's name as a
+// device address: the address comes from hipGetSymbolAddress, once per
+// device, with that device current.
+constexpr int kScratchFloats = qmoe::kAmaxPartials;     // 4 KiB
+__device__ __align__(256) float scratch[kScratchFloats];
+constexpr int kMaxDevices = 64;
+float *g_scratch_dev[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+// this device's copy of `scratch` (resolved on the first call on the device)
+int scratch_for_current_device(float **out, const char *fn) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  REQUIRE(dev >= 0 && dev < kMaxDevices, MOE_EUNSUPPORTED, "%s: device %d beyond %d", fn, dev,
+          kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void *ptr = nullptr;
+    const hipError_t es = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (es != hipSuccess || !ptr) return hip_status(es != hipSuccess ? es : hipErrorInvalidSymbol, fn);
+    g_scratch_dev[dev] = static_cast<float *>(ptr);
+  }
+  *out = g_scratch_dev[dev];
   return MOE_OK;
 }
 
@@ -216,6 +247,29 @@ int moe_quantize_act(const uint16_t *x, int rows, int K, int mode, const int *m_
         qmoe::launch_quant_mx_act_bf16(x, rows, K, m_offsets, E, q, scale_e8m0, stream), fn);
   }
   return fail(MOE_EINVAL, "%s: unknown mode %d", fn, mode);
+}
+
+int moe_quantize_act_noalloc(const uint16_t *x, int rows, int K, int mode, const int *m_offsets,
+                             int E, uint8_t *q, float *scale, uint8_t *scale_e8m0,
+                             hipStream_t stream) {
+  const char *fn = "moe_quantize_act_noalloc";
+  if (mode != MOE_Q_FP8_PER_TENSOR)       // the other modes use no scratch
+    return moe_quantize_act(x, rows, K, mode, m_offsets, E, q, scale, scale_e8m0, nullptr, stream);
+  REQUIRE(rows >= 0 && K > 0, MOE_EINVAL, "%s: rows=%d K=%d", fn, rows, K);
+  REQUIRE(K % 8 == 0, MOE_EUNSUPPORTED, "%s: K=%d is not a multiple of 8", fn, K);
+  const size_t need = moe_quantize_workspace_bytes(mode, 1);
+  REQUIRE(need <= sizeof(float) * kScratchFloats, MOE_EUNSUPPORTED,
+          "%s: %zu bytes of scratch needed, the static scratch holds %zu", fn, need,
+          sizeof(float) * kScratchFloats);
+  if (rows == 0) return ok();
+  REQUIRE(x && q && scale, MOE_EINVAL, "%s: null pointer argument", fn);
+  REQUIRE(aligned16(x) && ((uintptr_t)q & 7u) == 0, MOE_EINVAL,
+          "%s: x must be 16-byte and q 8-byte aligned", fn);
+  float *ws = nullptr;
+  const int rc = scratch_for_current_device(&ws, fn);
+  if (rc != MOE_OK) return rc;
+  return hip_status(qmoe::launch_quant_fp8_tensor_bf16(x, (long long)rows * K, q, scale, ws, stream),
+                    fn);
 }
 
 int moe_act_quantize(const uint16_t *x, int rows, int H, int act, int mode, const int *m_offsets,

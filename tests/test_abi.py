@@ -38,7 +38,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     h = ctypes.CDLL(qm.LIB_PATH)
     for n in names:
         assert hasattr(h, n), n
@@ -304,3 +304,21 @@ def test_library_missing_is_loud(monkeypatch, tmp_path):
     monkeypatch.setattr(qm, "_lib", None)
     with pytest.raises(qm.MoeLibraryMissing):
         qm.lib()
+
+
+def test_quantize_act_noalloc_rejects_before_any_device_call():
+    """The allocation-free activation quantizer validates like moe_quantize_act
+    (no GPU is touched on these paths)."""
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_quantize_act_noalloc(FAKE, 10, 100, qm.MOE_Q_FP8_PER_TENSOR, None, 1, FAKE, FAKE,
+                                    None, stream=0)
+    assert ei.value.code == qm.MOE_EUNSUPPORTED                 # K % 8
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_quantize_act_noalloc(None, 10, 128, qm.MOE_Q_FP8_PER_TENSOR, None, 1, FAKE, FAKE,
+                                    None, stream=0)
+    assert ei.value.code == qm.MOE_EINVAL                       # null input
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_quantize_act_noalloc(FAKE, 10, 128, 17, None, 1, FAKE, FAKE, None, stream=0)
+    assert ei.value.code == qm.MOE_EINVAL                       # unknown mode
+    assert qm.moe_quantize_act_noalloc(FAKE, 0, 128, qm.MOE_Q_FP8_PER_TENSOR, None, 1, FAKE,
+                                       FAKE, None, stream=0) == qm.MOE_OK

@@ -91,7 +91,7 @@ def parse():
     return p.parse_args()
 
 
-GEMM_SOURCES = ("qmoe_gemm.hip", "qmoe_internal.h")
+GEMM_SOURCES = ("qmoe_gemm.hip", "qmoe_gemm_tile.hip", "qmoe_device.h", "qmoe_internal.h")
 ACT_SOURCES = ("qmoe_quant.hip", "qmoe_internal.h")
 
 

@@ -72,6 +72,48 @@ static __device__ __forceinline__ void expert_block_starts(const int *__restrict
   }
 }
 
+// Byte weights -> bf16 MFMA operands, exactly (int8: |v| <= 128 fits the
+// 8-bit bf16 significand; e4m3: 3 mantissa bits, exponents -9..8).
+// 4 signed bytes -> 4 bf16 packed in two dwords (exact: |v| <= 128 fits the
+// 8-bit bf16 significand)
+static __device__ __forceinline__ i32x2 i8x4_to_bf16x4(uint32_t d) {
+  const float f0 = (float)(int)(int8_t)(d & 0xFFu);
+  const float f1 = (float)(int)(int8_t)((d >> 8) & 0xFFu);
+  const float f2 = (float)(int)(int8_t)((d >> 16) & 0xFFu);
+  const float f3 = (float)(int)((int32_t)d >> 24);
+  return i32x2{(int)f32x2_to_bf16x2(f0, f1), (int)f32x2_to_bf16x2(f2, f3)};
+}
+
+// 16 int8 (k0+16g .. +15) -> two bf16x8 operands (first 8 k, last 8 k)
+static __device__ __forceinline__ void dequant16(const i32x4 &w, i32x4 &b0, i32x4 &b1) {
+  const i32x2 p0 = i8x4_to_bf16x4((uint32_t)w[0]);
+  const i32x2 p1 = i8x4_to_bf16x4((uint32_t)w[1]);
+  const i32x2 p2 = i8x4_to_bf16x4((uint32_t)w[2]);
+  const i32x2 p3 = i8x4_to_bf16x4((uint32_t)w[3]);
+  b0 = i32x4{p0[0], p0[1], p1[0], p1[1]};
+  b1 = i32x4{p2[0], p2[1], p3[0], p3[1]};
+}
+
+// 16 e4m3 weights -> 16 bf16 values (exact: e4m3 has 3 mantissa bits), in
+// the same order as dequant16.
+static __device__ __forceinline__ void dequant16_fp8(const i32x4 &w, i32x4 &b0, i32x4 &b1) {
+  int p[8];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[d], false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[d], true);
+    p[2 * d] = (int)f32x2_to_bf16x2(lo[0], lo[1]);
+    p[2 * d + 1] = (int)f32x2_to_bf16x2(hi[0], hi[1]);
+  }
+  b0 = i32x4{p[0], p[1], p[2], p[3]};
+  b1 = i32x4{p[4], p[5], p[6], p[7]};
+}
+template <bool kFp8W>
+static __device__ __forceinline__ void dequant16w(const i32x4 &w, i32x4 &b0, i32x4 &b1) {
+  if constexpr (kFp8W) dequant16_fp8(w, b0, b1);
+  else dequant16(w, b0, b1);
+}
+
 // grouped-GEMM formats of the tiled kernels
 enum { kFmtFp8 = 0, kFmtInt8 = 1, kFmtMx = 2, kFmtI8 = 3, kFmtF8W16 = 4, kFmtMxW = 5 };
 

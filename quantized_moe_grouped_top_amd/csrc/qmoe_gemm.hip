@@ -71,46 +71,6 @@ __device__ __forceinline__ f32x4 mfma_bf16(const i32x4 &a, const i32x4 &b, f32x4
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// 4 signed bytes -> 4 bf16 packed in two dwords (exact: |v| <= 128 fits the
-// 8-bit bf16 significand)
-__device__ __forceinline__ i32x2 i8x4_to_bf16x4(uint32_t d) {
-  const float f0 = (float)(int)(int8_t)(d & 0xFFu);
-  const float f1 = (float)(int)(int8_t)((d >> 8) & 0xFFu);
-  const float f2 = (float)(int)(int8_t)((d >> 16) & 0xFFu);
-  const float f3 = (float)(int)((int32_t)d >> 24);
-  return i32x2{(int)f32x2_to_bf16x2(f0, f1), (int)f32x2_to_bf16x2(f2, f3)};
-}
-
-// 16 int8 (k0+16g .. +15) -> two bf16x8 operands (first 8 k, last 8 k)
-__device__ __forceinline__ void dequant16(const i32x4 &w, i32x4 &b0, i32x4 &b1) {
-  const i32x2 p0 = i8x4_to_bf16x4((uint32_t)w[0]);
-  const i32x2 p1 = i8x4_to_bf16x4((uint32_t)w[1]);
-  const i32x2 p2 = i8x4_to_bf16x4((uint32_t)w[2]);
-  const i32x2 p3 = i8x4_to_bf16x4((uint32_t)w[3]);
-  b0 = i32x4{p0[0], p0[1], p1[0], p1[1]};
-  b1 = i32x4{p2[0], p2[1], p3[0], p3[1]};
-}
-
-// 16 e4m3 weights -> 16 bf16 values (exact: e4m3 has 3 mantissa bits), in
-// the same order as dequant16.
-__device__ __forceinline__ void dequant16_fp8(const i32x4 &w, i32x4 &b0, i32x4 &b1) {
-  int p[8];
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[d], false);
-    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[d], true);
-    p[2 * d] = (int)f32x2_to_bf16x2(lo[0], lo[1]);
-    p[2 * d + 1] = (int)f32x2_to_bf16x2(hi[0], hi[1]);
-  }
-  b0 = i32x4{p[0], p[1], p[2], p[3]};
-  b1 = i32x4{p[4], p[5], p[6], p[7]};
-}
-template <bool kFp8W>
-__device__ __forceinline__ void dequant16w(const i32x4 &w, i32x4 &b0, i32x4 &b1) {
-  if constexpr (kFp8W) dequant16_fp8(w, b0, b1);
-  else dequant16(w, b0, b1);
-}
-
 __device__ __forceinline__ i32x4 ld16(const void *p) {
   return *reinterpret_cast<const i32x4 *>(p);
 }
@@ -1443,6 +1403,11 @@ hipError_t launch_gemm_fp8w8a16(const uint16_t *a, const uint8_t *w_q, const flo
                        r.sorted_ids, r.expert_ids, r.num_post, r.topk_w, r.M, r.K, r.N, r.top_k,
                        groups, tpg, r.max_blocks, r.y, stream_weight_bytes(r));
   } else {
+    if ((long long)r.M * r.top_k >= kWideMinRowsPerExpert * (long long)r.E) {
+      const long long tt = (long long)(r.max_blocks / 2 + r.E) * ((r.N + kHBN - 1) / kHBN);
+      return launch_tile_gemm(kFmtF8W16, r.w_layout == MOE_W_TILED,
+                              routed_tile_args(ab, nullptr, w_q, w_scale, r), nullptr, tt, s);
+    }
     const long long tiles = (long long)r.max_blocks * ((r.N + kGBN - 1) / kGBN);
     auto k = r.w_layout ? gemm_kernel<kFmtF8W16, true> : gemm_kernel<kFmtF8W16, false>;
     hipLaunchKernelGGL(k, dim3(tile_grid(tiles)), dim3(kGThreads), 0, s, ab, nullptr, nullptr, w_q,
@@ -1464,6 +1429,11 @@ hipError_t launch_gemm_int8(const uint16_t *a, const int8_t *w_q, const float *w
                        r.sorted_ids, r.expert_ids, r.num_post, r.topk_w, r.M, r.K, r.N, r.top_k,
                        groups, tpg, r.max_blocks, r.y, stream_weight_bytes(r));
   } else {
+    if ((long long)r.M * r.top_k >= kWideMinRowsPerExpert * (long long)r.E) {
+      const long long tt = (long long)(r.max_blocks / 2 + r.E) * ((r.N + kHBN - 1) / kHBN);
+      return launch_tile_gemm(kFmtInt8, r.w_layout == MOE_W_TILED,
+                              routed_tile_args(ab, nullptr, wb, w_scale, r), nullptr, tt, s);
+    }
     const long long tiles = (long long)r.max_blocks * ((r.N + kGBN - 1) / kGBN);
     auto k = r.w_layout ? gemm_kernel<kFmtInt8, true> : gemm_kernel<kFmtInt8, false>;
     hipLaunchKernelGGL(k, dim3(tile_grid(tiles)), dim3(kGThreads), 0, s, ab, nullptr, nullptr, wb,

@@ -1,16 +1,20 @@
 // The large-M grouped GEMM: 256 x 256 output tiles on four wavefronts (one
 // per SIMD, 128 x 128 outputs each in 256 accumulation registers), for fp8
-// W8A8 and int8 W8A8 over routed rows (block_m 128) and for MXFP8 (the
-// forward grouped linear and its weight gradient).
+// W8A8, int8 W8A8, int8 W8A16 and fp8 weight-only over routed rows (block_m
+// 128) and for MXFP8 (the forward grouped linear and its weight gradient).
 //
 // Operands.  A tile's rows are two 128-row routing blocks of one expert (the
 // sorted slots) or 256 consecutive rows of an expert's segment (MXFP8); its
 // columns are 256 output channels of that expert.  Each k-stage is 128 bytes
-// of every row and column (64 KB), copied HBM/L2 -> LDS by
-// global_load_lds_dwordx4 (direct-to-LDS DMA, whole 128-byte lines) into a
-// ring of two stage slots.  The contraction is v_mfma_*_32x32x64_f8f6f4
-// (scaled for MXFP8) or two v_mfma_i32_32x32x32_i8, with the weight fragment
-// as the first operand.
+// of every activation row (128 k of one-byte codes, 64 k of bf16) and the
+// same k of every weight column, copied HBM/L2 -> LDS by
+// global_load_lds_dwordx4 (direct-to-LDS DMA, whole 128-byte lines, or 64-byte
+// halves for the weights of bf16 stages) into a ring of stage slots (two of
+// 64 KB; three of 48 KB for bf16 activations).  The contraction is
+// v_mfma_*_32x32x64_f8f6f4 (scaled for MXFP8), two v_mfma_i32_32x32x32_i8, or,
+// for bf16 activations, two v_mfma_f32_32x32x16_bf16 on weights widened to
+// bf16 in registers (exact for int8 and e4m3 values), always with the weight
+// fragment as the first operand.
 //
 // Persistent schedule.  One workgroup per CU.  The tiles are ordered expert
 // by expert, column tile by column tile, block pair fastest, and cut into
@@ -20,12 +24,12 @@
 // share activation rows and weight columns in that XCD's L2.  The schedule is
 // static: no device state, no atomics, every launch independent.
 //
-// Pipeline.  A stage is computed as two 64-k halves of 16 MFMAs each; the
-// fragment reads of the next half are spread over the MFMAs of the current
-// one.  Between the halves a wavefront waits for the next stage's copy and
-// meets the others at the one barrier of the stage, which also frees the
-// stage's slot; the second half then issues the DMA of the stage after next
-// into that slot, one 1 KB piece per MFMA.  The DMA runs across tile
+// Pipeline.  A stage is computed as two halves; the fragment reads of the
+// next half are spread over the MFMAs of the current one.  Between the halves
+// a wavefront waits for the next stage's copy and meets the others at the one
+// barrier of the stage, which also frees the stage's slot; the second half
+// then issues the DMA of the stage a ring's length ahead into that slot, one
+// 1 KB piece per MFMA (per other MFMA for bf16).  The DMA runs across tile
 // boundaries: the first stages of a workgroup's next tile (and, for routed
 // rows, its sorted slots and router weights, fetched into LDS by dword DMA one
 // tile ahead) are loaded while the current tile's last stages are computed,
@@ -38,8 +42,9 @@
 // complete while the next tile's first half-stage computes.
 //
 // LDS rows are 128 bytes with 16-byte chunk c of row r at c ^ ((r >> 1) & 7)
-// (the MOE_W_TILED block layout, so tiled weights are a plain copy): the
-// fragment reads (32 rows at one chunk per lane group) hit distinct banks.
+// (the MOE_W_TILED block layout, so tiled weights are a plain copy), or 64
+// bytes (bf16-stage weights) with chunk c at c ^ (((r >> 1) ^ (r >> 3)) & 3):
+// the fragment reads (32 rows at one chunk per lane group) hit distinct banks.
 #include "qmoe_device.h"
 
 namespace qmoe {
@@ -49,16 +54,20 @@ namespace {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 
+// every helper lambda of the kernel is inlined (an outlined one would move
+// its captured state through scratch memory)
+#define QMOE_INLINE __attribute__((always_inline))
+
 constexpr int kTM = 256;                        // tile rows
 constexpr int kTN = 256;                        // tile columns
-constexpr int kTK = 128;                        // k bytes per stage
-constexpr int kRing = 2;                        // stage slots
-constexpr int kASlot = kTM * kTK;               // 32 KB of activation rows per stage
-constexpr int kSlot = kASlot + kTN * kTK;       // 64 KB per stage
+constexpr int kARow = 128;                      // activation bytes per row and stage
+constexpr int kASlot = kTM * kARow;             // 32 KB of activation rows per stage
 constexpr int kSfSlot = 4 * (kTM + kTN);        // MXFP8: the scale dword of every row and column
 constexpr int kInfo = 4;                        // routing-info buffers (tiles)
 
+// chunk swizzles: 128-byte rows (8 chunks), 64-byte rows (4 chunks)
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swz64(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
@@ -70,24 +79,38 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 __device__ __forceinline__ f32x16 mfma32_fp8(const i32x8 &a, const i32x8 &b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
+__device__ __forceinline__ f32x16 mfma32_bf16(const i32x4 &a, const i32x4 &b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
 __device__ __forceinline__ f32x16 mfma32_mx(const i32x8 &a, const i32x8 &b, f32x16 c, int sa,
                                             int sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
 
-// Fragments of one half-stage (64 k): for row (column) fragment i, lane
-// 32 g + r holds row r, k 16g..16g+15 (lo) and 32+16g..32+16g+15 (hi) of the
-// half; MXFP8: the e8m0 scale of 32-k block g of the half for row (column) r.
+// Fragments of one half-stage.  One-byte formats (64 k per half): for row
+// (column) fragment i, lane 32 g + r holds row r, k 16g..16g+15 (lo) and
+// 32+16g..32+16g+15 (hi) of the half; MXFP8: the e8m0 scale of 32-k block g
+// of the half for row (column) r.  bf16 activations (32 k per half, two
+// 32x32x16 MFMAs): lane 32 g + r holds k 16g..16g+7 (lo) and 16g+8..16g+15
+// (hi) of activation row r, and the 16 weight bytes k 16g..16g+15 of column r
+// in blo (bhi unused); the two MFMAs take the first and the last 8 k of each
+// lane, a fixed assignment of k to the MFMA inputs that both operands share.
 struct Frags {
   i32x4 alo[4], ahi[4], blo[4], bhi[4];
   int sa[4], sb[4];
 };
 
-// Order in which a half-stage's 16 fragment parts are read: by first use in
-// the MFMA order (i, j) = (q >> 2, q & 3).  Part p: kind (0 A lo, 1 A hi,
-// 2 B lo, 3 B hi) and fragment index.
+// Order in which a half-stage's fragment parts are read: by first use in
+// the MFMA order.  Part p: kind (0 A lo, 1 A hi, 2 B lo, 3 B hi) and fragment
+// index.  One-byte formats, MFMA order (i, j) = (q >> 2, q & 3): 16 parts.
 constexpr int kPartKind[16] = {0, 1, 2, 3, 2, 3, 2, 3, 2, 3, 0, 1, 0, 1, 0, 1};
 constexpr int kPartFrag[16] = {0, 0, 0, 0, 1, 1, 2, 2, 3, 3, 1, 1, 2, 2, 3, 3};
+// bf16 activations, 32 MFMAs per half in the order (j, step, i) = (q >> 3,
+// (q >> 2) & 1, q & 3) (four independent accumulators between the two steps
+// of one): 12 parts, one read after every other MFMA.
+constexpr int kPart16Kind[12] = {2, 0, 0, 0, 0, 1, 1, 1, 1, 2, 2, 2};
+constexpr int kPart16Frag[12] = {0, 0, 1, 2, 3, 0, 1, 2, 3, 1, 2, 3};
 
 template <int kFmt, bool kTiled>
 __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const WgradSeg seg) {
@@ -95,7 +118,17 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
   constexpr bool kMx = kFmt == kFmtMx || kW;
   constexpr bool kRouted = !kMx;
   constexpr bool kI8 = kFmt == kFmtI8;
-  constexpr int kPieces = 16 + (kMx ? 2 : 0);       // DMA instructions per wavefront and stage
+  // bf16 activations x byte weights (int8 W8A16, fp8 weight-only): weights
+  // converted to bf16 in registers, bf16 MFMAs, 64 k per stage (the same 128
+  // activation bytes per row), three stage slots
+  constexpr bool kB16 = kFmt == kFmtInt8 || kFmt == kFmtF8W16;
+  constexpr bool kCS = kI8 || kB16;                  // one weight scale per output column
+  constexpr int kTK = kB16 ? 64 : 128;               // k per stage
+  constexpr int kBRow = kB16 ? 64 : 128;             // weight bytes per row and stage
+  constexpr int kRing = kB16 ? 3 : 2;                // stage slots
+  constexpr int kSlot = kASlot + kTN * kBRow;        // 48 / 64 KB per stage
+  constexpr int kBP = kB16 ? 4 : 8;                  // weight DMA pieces per wavefront and stage
+  constexpr int kPieces = 8 + kBP + (kMx ? 2 : 0);   // DMA instructions per wavefront and stage
   static_assert(!(kTiled && kMx), "MXFP8 weights are row-major");
 
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kRing * kSlot];
@@ -103,7 +136,7 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
   __shared__ __attribute__((aligned(16))) int s_row[kRouted ? kInfo : 1][kTM];    // sorted slots
   __shared__ __attribute__((aligned(16))) float s_tw[kRouted ? kInfo : 1][kTM];   // router weights
   __shared__ __attribute__((aligned(16))) float s_ts[kI8 ? kInfo : 1][kTM];       // token scales
-  __shared__ __attribute__((aligned(16))) float s_cs[kI8 ? kInfo : 1][kTN];       // column scales
+  __shared__ __attribute__((aligned(16))) float s_cs[kCS ? kInfo : 1][kTN];       // column scales
   __shared__ int s_blk_first[kMaxExperts + 1];
   __shared__ int s_tile_first[kMaxExperts + 1];
   __shared__ int s_mo[kMx ? kMaxExperts + 1 : 1];     // first row of every segment
@@ -169,12 +202,12 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
   const int c0 = xq * chunk, c1 = min(c0 + chunk, total);
   const int n_my = c0 + wl < c1 ? (c1 - c0 - wl + Gx - 1) / Gx : 0;
   if (n_my == 0) return;
-  auto tile_of = [&](int k) { return c0 + wl + k * Gx; };
+  auto tile_of = [&](int k) QMOE_INLINE { return c0 + wl + k * Gx; };
 
   struct Tile {
     int e, nt, pr, nb, nst;
   };
-  auto decode = [&](int k) -> Tile {
+  auto decode = [&](int k) QMOE_INLINE -> Tile {
     const int L = tile_of(k);
     int e = 0;
     while (s_tile_first[e + 1] <= L) ++e;
@@ -203,7 +236,7 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
 
   // routing info of tile k (its 256 sorted slots) into buffer k % kInfo; wave w
   // loads rows 64w .. 64w + 63 (rows of a missing second block repeat the first)
-  auto issue_info = [&](int k) {
+  auto issue_info = [&](int k) QMOE_INLINE {
     int lane_opaque = lane;
     asm volatile("" : "+v"(lane_opaque));
     const int lane = lane_opaque;
@@ -217,7 +250,7 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
 
   // Enter tile k: its DMA offsets (and, for routed rows, the routing info of
   // tile k + 1 and the gathers of tile k's router weights and scales).
-  auto enter = [&](int k) {
+  auto enter = [&](int k) QMOE_INLINE {
     // lane-derived values are recomputed here from an opaque copy of the lane
     // index, so that the compiler does not keep them live through the stages
     int lane_opaque = lane;
@@ -231,7 +264,9 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
     const int n0 = t.nt * kTN;
     if constexpr (kRouted) {
       const int buf = k % kInfo;
-      if (k > 0) wait_dma_upto(issued - info_mark);  // this tile's sorted slots have landed
+      // this tile's sorted slots have landed (once 64 or more loads follow
+      // them they have: at most 63 are outstanding and loads return in order)
+      if (k > 0 && issued - info_mark < 64) wait_dma_upto(issued - info_mark);
       if (k + 1 < n_my) issue_info(k + 1);
       const int nvalid = t.nb * 128;
 #pragma unroll
@@ -239,7 +274,7 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
         const int R = 64 * wave + 8 * u + (lane >> 3);
         const int slot = s_row[buf][R];
         const uint32_t tok = (R < nvalid && slot < S) ? (uint32_t)(slot / top_k) : 0u;
-        a_off[u] = tok * (uint32_t)K + 16u * (uint32_t)((lane & 7) ^ swz(R));
+        a_off[u] = tok * (uint32_t)(kB16 ? 2 * K : K) + 16u * (uint32_t)((lane & 7) ^ swz(R));
       }
       {
         const int R = 64 * wave + lane;
@@ -249,9 +284,12 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
         ++issued;
         if constexpr (kI8) {
           dma4(p.a_scale, (uint32_t)(sl / top_k) * 4u, lds_addr(&s_ts[buf][64 * wave]));
+          ++issued;
+        }
+        if constexpr (kCS) {
           const int col = min(n0 + 64 * wave + lane, N - 1);
           dma4(p.w_scale + (size_t)t.e * N, (uint32_t)col * 4u, lds_addr(&s_cs[buf][64 * wave]));
-          issued += 2;
+          ++issued;
         }
       }
     } else {
@@ -282,12 +320,33 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
     }
     // weight columns: wave w loads columns 64w .. 64w + 63 of the tile
     if constexpr (kTiled) {
-      // MOE_W_TILED: one 8 KB block of 64 rows x 128 k bytes per stage, in
-      // the LDS row order and swizzle already
+      // MOE_W_TILED: 8 KB blocks of 64 rows x 128 k bytes, chunk c of row r
+      // at c ^ ((r >> 1) & 7).  One-byte formats: one block per stage, in the
+      // LDS row order and swizzle already.  bf16 activations: a 64-k stage is
+      // chunks 4h .. 4h + 3 of the rows (h = stage parity), which for row r
+      // sit at bit 6 of the offset flipped by h
       const int T = (N + 63) / 64;
-      const int S128 = K / 128;
+      const int S128 = (K + 127) / 128;
       const int tb = min(n0 / 64 + wave, T - 1);
       b_src = p.w + (size_t)((t.e * T + tb) * S128) * 8192u;
+      if constexpr (kB16) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = 16 * u + (lane >> 2);
+          const int x = (r >> 1) & 7;
+          const int c = (lane & 3) ^ swz64(r);
+          b_off[u] = (uint32_t)(r * 128 + 16 * ((c ^ x) & 3) + 64 * ((x >> 2) & 1));
+        }
+      }
+    } else if constexpr (kB16) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int R = 64 * wave + 16 * u + (lane >> 2);
+        const uint32_t col = (uint32_t)min(n0 + R, N - 1);
+        b_off[u] = ((uint32_t)t.e * (uint32_t)N + col) * (uint32_t)K +
+                   16u * (uint32_t)((lane & 3) ^ swz64(R));
+      }
+      b_src = p.w;
     } else {
       const uint32_t Ke = kW ? (uint32_t)(seg.po[t.e + 1] - seg.po[t.e]) : (uint32_t)K;
       const uint32_t pe = kW ? (uint32_t)seg.po[t.e] : 0u;
@@ -305,7 +364,7 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
 
   // Make (cur_k, cur_st) a stage that exists, entering the next tiles as
   // needed; cur_live turns false once every stage has been loaded.
-  auto advance = [&]() {
+  auto advance = [&]() QMOE_INLINE {
     while (cur_live && cur_st >= cur_nst) {
       if (cur_k + 1 < n_my) enter(cur_k + 1);
       else cur_live = false;
@@ -313,32 +372,53 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
   };
 
   // DMA piece q of stage st of the cursor's tile into ring slot `slot`:
-  // 0-7 activation rows, 8-15 weight rows (1 KB each), 16-17 MXFP8 scale dwords
-  auto issue_piece = [&](int q, int slot, uint32_t st) {
+  // 0-7 activation rows, 8.. weight rows (1 KB each), then the two MXFP8
+  // scale dwords
+  auto issue_piece = [&](int q, int slot, uint32_t st) QMOE_INLINE {
     const uint32_t base = lds_ring + (uint32_t)(slot * kSlot);
     if (q < 8) {
-      dma16(p.a + st * kTK, a_off[q], base + (uint32_t)((8 * wave + q) * 1024));
-    } else if (q < 16) {
+      dma16(p.a + st * kARow, a_off[q], base + (uint32_t)((8 * wave + q) * 1024));
+    } else if (q < 8 + kBP) {
       const int u = q - 8;
-      const uint32_t dst = base + (uint32_t)(kASlot + (8 * wave + u) * 1024);
-      if constexpr (kTiled) dma16(b_src + st * 8192u, (uint32_t)(u * 1024) + 16u * (uint32_t)lane, dst);
-      else dma16(b_src + st * kTK, b_off[u], dst);
+      const uint32_t dst = base + (uint32_t)(kASlot + (kBP * wave + u) * 1024);
+      if constexpr (kB16) {
+        if constexpr (kTiled) dma16(b_src + (st >> 1) * 8192u, b_off[u] ^ ((st & 1u) << 6), dst);
+        else dma16(b_src + st * kBRow, b_off[u], dst);
+      } else {
+        if constexpr (kTiled) dma16(b_src + st * 8192u, (uint32_t)(u * 1024) + 16u * (uint32_t)lane, dst);
+        else dma16(b_src + st * kBRow, b_off[u], dst);
+      }
     } else if constexpr (kMx) {
       const uint32_t sbase = lds_sf + (uint32_t)(slot * kSfSlot);
-      if (q == 16) dma4(p.a_sf + 4u * st, sf_off[0], sbase + (uint32_t)(256 * wave));
+      if (q == 8 + kBP) dma4(p.a_sf + 4u * st, sf_off[0], sbase + (uint32_t)(256 * wave));
       else dma4(p.w_sf + 4u * st, sf_off[1], sbase + (uint32_t)(4 * kTM + 256 * wave));
     }
   };
 
   // ---- fragments ------------------------------------------------------------
   const int sw = swz(r32);                          // (32i + r32 has the same swizzle)
-  auto read_part = [&](int slot, int h, Frags &f, int part) {
-    const int kind = kPartKind[part], i = kPartFrag[part];
-    const uint8_t *base = s_ring + slot * kSlot +
-                          (kind < 2 ? wm * 128 * kTK : kASlot + wn * 128 * kTK) +
-                          (32 * i + r32) * kTK;
-    const i32x4 v = *reinterpret_cast<const i32x4 *>(
-        base + (((4 * h + g + ((kind & 1) ? 2 : 0)) ^ sw) << 4));
+  const int sw64 = swz64(r32);
+  constexpr int kParts = kB16 ? 12 : 16;            // fragment reads per half-stage
+  constexpr int kMf = kB16 ? 32 : 16;               // MFMA instructions per half-stage
+  auto read_part = [&](int slot, int h, Frags &f, int part) QMOE_INLINE {
+    int kind, i;
+    const uint8_t *p8;
+    if constexpr (kB16) {
+      kind = kPart16Kind[part];
+      i = kPart16Frag[part];
+      if (kind < 2)
+        p8 = s_ring + slot * kSlot + wm * 128 * kARow + (32 * i + r32) * kARow +
+             (((4 * h + 2 * g + kind) ^ sw) << 4);
+      else
+        p8 = s_ring + slot * kSlot + kASlot + wn * 128 * kBRow + (32 * i + r32) * kBRow +
+             (((2 * h + g) ^ sw64) << 4);
+    } else {
+      kind = kPartKind[part];
+      i = kPartFrag[part];
+      p8 = s_ring + slot * kSlot + (kind < 2 ? wm * 128 * kARow : kASlot + wn * 128 * kBRow) +
+           (32 * i + r32) * kARow + (((4 * h + g + ((kind & 1) ? 2 : 0)) ^ sw) << 4);
+    }
+    const i32x4 v = *reinterpret_cast<const i32x4 *>(p8);
     if (kind == 0) f.alo[i] = v;
     else if (kind == 1) f.ahi[i] = v;
     else if (kind == 2) f.blo[i] = v;
@@ -346,7 +426,7 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
   };
   // MXFP8 scales of half h: byte 2h + g of the stage's scale dword (part i:
   // row fragment i, part 4 + j: column fragment j)
-  auto read_scale_part = [&](int slot, int h, Frags &f, int part) {
+  auto read_scale_part = [&](int slot, int h, Frags &f, int part) QMOE_INLINE {
     if constexpr (kMx) {
       const uint8_t *sfs = s_sf + slot * kSfSlot;
       const int sh = 8 * (2 * h + g);
@@ -357,9 +437,24 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
         f.sb[i] = (int)((*reinterpret_cast<const uint32_t *>(sfs + 4 * kTM + 4 * (wn * 128 + 32 * i + r32)) >> sh) & 0xFFu);
     }
   };
+  // the reads that follow MFMA q (of kMf) in a half-stage: fragment parts
+  // (one-byte formats: part q; bf16 activations: part q / 2 after even q)
+  auto reads_after = [&](int q, int slot, int h, Frags &f) QMOE_INLINE {
+    if constexpr (kB16) {
+      if ((q & 1) == 0 && q / 2 < kParts) read_part(slot, h, f, q / 2);
+    } else {
+      read_part(slot, h, f, q);
+      if (kMx && q >= 8) read_scale_part(slot, h, f, q - 8);
+    }
+  };
+  // the DMA piece issued after MFMA q of a second half-stage (-1: none)
+  auto piece_after = [&](int q) QMOE_INLINE -> int {
+    if constexpr (kB16) return (q & 1) && q / 2 < kPieces ? q / 2 : -1;
+    else return q < 16 ? q : -1;
+  };
 
   f32x16 acc[4][4];
-  auto zero_acc = [&]() {
+  auto zero_acc = [&]() QMOE_INLINE {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -367,7 +462,14 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
   };
-  auto mfma_q = [&](const Frags &f, int q) {
+  i32x4 wcv[2];                                     // bf16 weights of the current column fragment
+  auto mfma_q = [&](const Frags &f, int q) QMOE_INLINE {
+    if constexpr (kB16) {
+      const int j = q >> 3, st = (q >> 2) & 1, i = q & 3;
+      if ((q & 7) == 0) dequant16w<kFmt == kFmtF8W16>(f.blo[j], wcv[0], wcv[1]);
+      acc[i][j] = mfma32_bf16(wcv[st], st ? f.ahi[i] : f.alo[i], acc[i][j]);
+      return;
+    }
     const int i = q >> 2, j = q & 3;
     const i32x8 av = __builtin_shufflevector(f.alo[i], f.ahi[i], 0, 1, 2, 3, 4, 5, 6, 7);
     const i32x8 bv = __builtin_shufflevector(f.blo[j], f.bhi[j], 0, 1, 2, 3, 4, 5, 6, 7);
@@ -384,14 +486,14 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
       acc[i][j] = mfma32_fp8(bv, av, acc[i][j]);
     }
   };
-  auto pin_acc = [&]() {     // the accumulators are "used" here: no MFMA sinks past
+  auto pin_acc = [&]() QMOE_INLINE {     // the accumulators are "used" here: no MFMA sinks past
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
   };
 
-  // ---- prologue: routing info of the first tile, then two stages ---------------
+  // ---- prologue: routing info of the first tile, then kRing stages -------------
   // Every stage issues its kPieces DMA instructions (once the last tile's
   // stages are all loaded, the last one again, into the slot just freed).
   if constexpr (kRouted) {
@@ -414,46 +516,49 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
         ++cur_st;
       }
     }
-    // stage 0 has landed here (the loads after it: stage 1's pieces and at
-    // most a few routing loads)
-    if constexpr (kMx) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    // stage 0 has landed here (the loads after it: the later stages' pieces
+    // and at most a few routing loads before them)
+    wait_dma_upto((kRing - 1) * kPieces);
   }
   lds_barrier();
   Frags fa, fb;
 #pragma unroll
-  for (int part = 0; part < 16; ++part) read_part(0, 0, fa, part);
+  for (int part = 0; part < kParts; ++part) read_part(0, 0, fa, part);
 #pragma unroll
   for (int part = 0; part < 8; ++part) read_scale_part(0, 0, fa, part);
   wait_lds();
   zero_acc();
 
-  // One stage (flat index t, ring slot t % 2): half 0 on `fa` while half 1's
-  // fragments are read into `fb`; the wait for stage t + 1 and the barrier;
-  // half 1 on `fb` while stage t + 2 is issued into slot t % 2 and half 0 of
-  // stage t + 1 is read into `fa`.
+  // One stage (flat index t, ring slot t % kRing): half 0 on `fa` while half
+  // 1's fragments are read into `fb`; the wait for stage t + 1 and the
+  // barrier; half 1 on `fb` while stage t + kRing is issued into slot
+  // t % kRing and half 0 of stage t + 1 is read into `fa`.  With three slots
+  // the wait leaves stage t + 2 in flight (vmcnt(kPieces)), except after an
+  // epilogue, whose stores may complete out of order with the loads.
   int t = 0;
-  auto stage = [&]() {
-    const int slot = t & 1;
+  bool after_epi = false;
+  auto stage = [&]() QMOE_INLINE {
+    const int slot = t % kRing, nslot = (t + 1) % kRing;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < kMf; ++q) {
       mfma_q(fa, q);
-      read_part(slot, 1, fb, q);
-      if (kMx && q >= 8) read_scale_part(slot, 1, fb, q - 8);
+      reads_after(q, slot, 1, fb);
       __builtin_amdgcn_sched_barrier(0);
     }
     pin_acc();
     wait_lds();                                     // this wave is done with the slot
-    wait_dma_all();                                 // stage t + 1 has landed here ...
+    if (kRing == 2 || after_epi) wait_dma_all();    // stage t + 1 has landed here ...
+    else wait_dma_upto(kPieces);
+    after_epi = false;
     lds_barrier();                                  // ... everywhere; the slot is free
     advance();
     const uint32_t st = (uint32_t)(cur_live ? cur_st : rl_st);
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < kMf; ++q) {
       mfma_q(fb, q);
-      issue_piece(q, slot, st);
-      read_part(slot ^ 1, 0, fa, q);
-      if (kMx && q >= 8) read_scale_part(slot ^ 1, 0, fa, q - 8);
+      const int pc = piece_after(q);
+      if (pc >= 0) issue_piece(pc, slot, st);
+      reads_after(q, nslot, 0, fa);
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (kMx) {
@@ -471,7 +576,7 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
   };
 
   // ---- epilogue: scale, pack to bf16, store 16-byte pieces -------------------
-  auto epilogue = [&](int k) {
+  auto epilogue = [&](int k) QMOE_INLINE {
     int lane_opaque = lane;
     asm volatile("" : "+v"(lane_opaque));
     const int lane = lane_opaque;
@@ -490,7 +595,7 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
       if constexpr (kRouted) {
         const int slot = s_row[buf][R];
         dst = (R < tl.nb * 128 && slot < S) ? slot : -1;
-        rs = kI8 ? s_ts[buf][R] * s_tw[buf][R] : sc * s_tw[buf][R];
+        rs = kI8 ? s_ts[buf][R] * s_tw[buf][R] : (kB16 ? s_tw[buf][R] : sc * s_tw[buf][R]);
       } else {
         const int row = s_mo[tl.e] + 2 * tl.pr * 128 + R;
         dst = row < s_mo[tl.e + 1] ? row : -1;
@@ -503,9 +608,9 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
           float v[8];
 #pragma unroll
           for (int u = 0; u < 8; ++u) v[u] = acc[i][j][8 * kk + u];
-          if constexpr (kI8) {
-            // int32 -> float times the column scales: accumulator 4k + c is
-            // column 8k + 4g + c of the fragment
+          if constexpr (kCS) {
+            // times the column scales (int8 W8A8: int32 -> float first):
+            // accumulator 4k + c is column 8k + 4g + c of the fragment
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
               const f32x4 cs =
@@ -513,7 +618,7 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
 #pragma unroll
               for (int c = 0; c < 4; ++c) {
                 const float raw = v[4 * h + c];
-                v[4 * h + c] = (float)__builtin_bit_cast(int, raw) * cs[c];
+                v[4 * h + c] = (kI8 ? (float)__builtin_bit_cast(int, raw) : raw) * cs[c];
               }
             }
           }
@@ -545,7 +650,9 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
     for (int s = 0; s < nst; ++s) stage();
     epilogue(k);
     zero_acc();
+    after_epi = true;
   }
+  wait_dma_all();                                   // no copy into LDS outlives the workgroup
 }
 
 }  // namespace
@@ -569,6 +676,14 @@ hipError_t launch_tile_gemm(int fmt, bool tiled, const TileArgs &args, const Wgr
     case kFmtI8:
       if (tiled) hipLaunchKernelGGL((tile_kernel<kFmtI8, true>), gd, bd, 0, s, args, sg);
       else hipLaunchKernelGGL((tile_kernel<kFmtI8, false>), gd, bd, 0, s, args, sg);
+      break;
+    case kFmtInt8:
+      if (tiled) hipLaunchKernelGGL((tile_kernel<kFmtInt8, true>), gd, bd, 0, s, args, sg);
+      else hipLaunchKernelGGL((tile_kernel<kFmtInt8, false>), gd, bd, 0, s, args, sg);
+      break;
+    case kFmtF8W16:
+      if (tiled) hipLaunchKernelGGL((tile_kernel<kFmtF8W16, true>), gd, bd, 0, s, args, sg);
+      else hipLaunchKernelGGL((tile_kernel<kFmtF8W16, false>), gd, bd, 0, s, args, sg);
       break;
     case kFmtMx:
       hipLaunchKernelGGL((tile_kernel<kFmtMx, false>), gd, bd, 0, s, args, sg);

@@ -162,6 +162,13 @@ SMALL = [
     synth.small("fp8wo", 50, 320, 136, 6, 3),
     synth.small("fp8wo", 300, 256, 272, 8, 2, bias_std=1.5),
     synth.small("fp8wo", 40, 128, 48, 1, 1),
+    # bf16 activations with >= 384 routed rows per expert: the tile kernel
+    # (64-k stages; K = 320 ends on half a 128-byte weight block, K = 64 is one
+    # stage per tile)
+    synth.small("int8", 400, 256, 320, 2, 2),
+    synth.small("int8", 500, 320, 200, 2, 2, bias_std=1.5),
+    synth.small("fp8wo", 800, 384, 136, 4, 2, bias_std=1.5),
+    synth.small("fp8wo", 400, 64, 264, 2, 2),
 ]
 
 

@@ -114,6 +114,21 @@ static __device__ __forceinline__ void dequant16w(const i32x4 &w, i32x4 &b0, i32
   else dequant16(w, b0, b1);
 }
 
+// One word of dequant16w's output: bytes 2h and 2h + 1 of weight dword d as a
+// bf16 pair (word 2d' + h of the eight, d' being d's index in the fragment).
+template <bool kFp8W>
+static __device__ __forceinline__ int dequant_pair(uint32_t d, int h) {
+  if constexpr (kFp8W) {
+    const f32x2 v = h ? __builtin_amdgcn_cvt_pk_f32_fp8((int)d, true)
+                      : __builtin_amdgcn_cvt_pk_f32_fp8((int)d, false);
+    return (int)f32x2_to_bf16x2(v[0], v[1]);
+  } else {
+    const float f0 = (float)(int)(int8_t)((d >> (16 * h)) & 0xFFu);
+    const float f1 = (float)((int32_t)(d << (16 - 16 * h)) >> 24);
+    return (int)f32x2_to_bf16x2(f0, f1);
+  }
+}
+
 // grouped-GEMM formats of the tiled kernels
 enum { kFmtFp8 = 0, kFmtInt8 = 1, kFmtMx = 2, kFmtI8 = 3, kFmtF8W16 = 4, kFmtMxW = 5 };
 

@@ -17,12 +17,13 @@
 // fragment as the first operand.
 //
 // Persistent schedule.  One workgroup per CU.  The tiles are ordered expert
-// by expert, column tile by column tile, block pair fastest, and cut into
-// eight contiguous chunks, one per XCD (workgroup b runs on XCD b mod 8, the
-// dispatch order); the workgroups of an XCD take its chunk's tiles round
-// robin, so the tiles in flight on one XCD at a time are neighbours that
-// share activation rows and weight columns in that XCD's L2.  The schedule is
-// static: no device state, no atomics, every launch independent.
+// by expert, then by groups of eight column tiles, then block pair by block
+// pair, columns fastest, and cut into eight contiguous chunks, one per XCD
+// (workgroup b runs on XCD b mod 8, the dispatch order); the workgroups of an
+// XCD take its chunk's tiles round robin, so the 32 tiles in flight on one
+// XCD at a time form a block of at most 4 row pairs x 8 column tiles whose
+// activation rows and weight columns are shared in that XCD's L2.  The
+// schedule is static: no device state, no atomics, every launch independent.
 //
 // Pipeline.  A stage is computed as two halves; the fragment reads of the
 // next half are spread over the MFMAs of the current one.  Between the halves
@@ -64,6 +65,7 @@ constexpr int kARow = 128;                      // activation bytes per row and 
 constexpr int kASlot = kTM * kARow;             // 32 KB of activation rows per stage
 constexpr int kSfSlot = 4 * (kTM + kTN);        // MXFP8: the scale dword of every row and column
 constexpr int kInfo = 4;                        // routing-info buffers (tiles)
+constexpr int kColGroup = 8;                    // column tiles per group of the tile order
 
 // chunk swizzles: 128-byte rows (8 chunks), 64-byte rows (4 chunks)
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
@@ -215,8 +217,13 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
     const int nblk = __builtin_amdgcn_readfirstlane(s_blk_first[e + 1] - s_blk_first[e]);
     const int npair = (nblk + 1) >> 1;
     const int local = L - __builtin_amdgcn_readfirstlane(s_tile_first[e]);
-    const int nt = local / npair;
-    const int pr = local - nt * npair;
+    // column groups of kColGroup tiles, block pairs within a group, columns
+    // fastest: 32 consecutive tiles cover at most 4 block pairs x 8 columns
+    const int grp = local / (npair * kColGroup);
+    const int rem = local - grp * npair * kColGroup;
+    const int gc = min(kColGroup, ntn - grp * kColGroup);   // columns in this group
+    const int pr = rem / gc;
+    const int nt = grp * kColGroup + (rem - pr * gc);
     int nst = K / kTK;
     if constexpr (kW) nst = (seg.po[e + 1] - seg.po[e]) / kTK;
     return {e, nt, pr, min(2, nblk - 2 * pr), nst};
@@ -462,12 +469,24 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
   };
-  i32x4 wcv[2];                                     // bf16 weights of the current column fragment
-  auto mfma_q = [&](const Frags &f, int q) QMOE_INLINE {
+  // bf16 activations: the weights of column fragment j are widened while the
+  // MFMAs of fragment j - 1 run, one bf16 word after each MFMA (the first
+  // fragment of a half during the last group of the half before), so no MFMA
+  // waits for a conversion
+  i32x4 wcv[2], wnx[2];                             // widened weights: current, next fragment
+  auto widen_part = [&](const i32x4 &src, int m) QMOE_INLINE {
+    int *dst = reinterpret_cast<int *>(&wnx[m >> 2]);
+    dst[m & 3] = dequant_pair<kFmt == kFmtF8W16>((uint32_t)src[m >> 1], m & 1);
+  };
+  auto mfma_q = [&](const Frags &f, const Frags &fn, int q) QMOE_INLINE {
     if constexpr (kB16) {
-      const int j = q >> 3, st = (q >> 2) & 1, i = q & 3;
-      if ((q & 7) == 0) dequant16w<kFmt == kFmtF8W16>(f.blo[j], wcv[0], wcv[1]);
+      const int j = q >> 3, m = q & 7, st = m >> 2, i = m & 3;
+      if (m == 0) {
+        wcv[0] = wnx[0];
+        wcv[1] = wnx[1];
+      }
       acc[i][j] = mfma32_bf16(wcv[st], st ? f.ahi[i] : f.alo[i], acc[i][j]);
+      widen_part(j < 3 ? f.blo[j + 1] : fn.blo[0], m);
       return;
     }
     const int i = q >> 2, j = q & 3;
@@ -527,6 +546,10 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
 #pragma unroll
   for (int part = 0; part < 8; ++part) read_scale_part(0, 0, fa, part);
   wait_lds();
+  if constexpr (kB16) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) widen_part(fa.blo[0], m);
+  }
   zero_acc();
 
   // One stage (flat index t, ring slot t % kRing): half 0 on `fa` while half
@@ -541,7 +564,7 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
     const int slot = t % kRing, nslot = (t + 1) % kRing;
 #pragma unroll
     for (int q = 0; q < kMf; ++q) {
-      mfma_q(fa, q);
+      mfma_q(fa, fb, q);
       reads_after(q, slot, 1, fb);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -555,7 +578,7 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
     const uint32_t st = (uint32_t)(cur_live ? cur_st : rl_st);
 #pragma unroll
     for (int q = 0; q < kMf; ++q) {
-      mfma_q(fb, q);
+      mfma_q(fb, fa, q);
       const int pc = piece_after(q);
       if (pc >= 0) issue_piece(pc, slot, st);
       reads_after(q, nslot, 0, fa);

@@ -176,8 +176,10 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
   const int e = blockIdx.x / groups;
   const int grp = blockIdx.x - e * groups;
   const int ntiles = (N + 63) / 64;
-  const int t_begin = grp * tiles_per_group;
-  const int G = min(t_begin + tiles_per_group, ntiles) - t_begin;   // tiles of this workgroup
+  // this workgroup's tiles: grp, grp + groups, grp + 2 groups, ... (strided,
+  // so that each workgroup's weight stream spreads over the expert's columns)
+  const int G = min(tiles_per_group, (ntiles - grp + groups - 1) / groups);
+  auto tile_at = [&](int m) { return grp + groups * m; };
   const int tid = threadIdx.x, lane = tid & 63;
   // the wavefront index, in a scalar register (the compiler cannot tell that
   // tid >> 6 is the same in every lane), so that the per-wavefront group
@@ -194,7 +196,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
   const int ngr = 4 * G;                                    // row groups of the workgroup
 
   // ---- this lane's weight pieces.  Group u of this wavefront is row group
-  // jg = wave + 8u of the workgroup: weight rows 64 (t_begin + jg / 4) +
+  // jg = wave + 8u of the workgroup: weight rows 64 tile_at(jg / 4) +
   // 16 (jg % 4) + 0..15, this lane's row r16 of them.  A wavefront with fewer
   // than four groups repeats the last group's loads (L2 hits) so that every
   // wavefront issues the same number of loads per stage.
@@ -215,7 +217,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
 #pragma unroll
   for (int u = 0; u < kSGroups; ++u) {
     const int jg = min(wave + kSWaves * u, ngr - 1);
-    const int tile = t_begin + (jg >> 2);
+    const int tile = tile_at(jg >> 2);
     const int n = tile * 64 + 16 * (jg & 3) + r16;          // may be >= N in the last tile
     if constexpr (kLayout == MOE_W_ROWMAJOR) {
       const uint32_t row =
@@ -262,7 +264,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
   // the epilogue reads only LDS.
   float cs_pre = 0.0f;
   if (tid < G * 64) {
-    const int col = min(t_begin * 64 + tid, N - 1);
+    const int col = min(tile_at(tid >> 6) * 64 + (tid & 63), N - 1);
     cs_pre = kMode == kSFp8 ? a_scale[0] * w_scale[e] : w_scale[(size_t)e * N + col];
   }
   const int n_sorted_dma = (max_blocks * 16 + 63) / 64;   // 256-byte dword DMAs
@@ -584,7 +586,7 @@ __global__ __launch_bounds__(kSThreads, 1) void stream_kernel(
       for (int q = tid; q < 16 * pieces; q += kSThreads) {
         const int k = q / pieces, c8 = q - k * pieces;
         const int slot = s_slot[16 * i + k];
-        const int col = t_begin * 64 + 8 * c8;
+        const int col = tile_at(c8 >> 3) * 64 + 8 * (c8 & 7);
         if (slot < S && col < N)
           *reinterpret_cast<i32x4 *>(y + (size_t)slot * N + col) =
               *reinterpret_cast<const i32x4 *>(stg + k * wcols + 8 * c8);

@@ -17,13 +17,14 @@
 // fragment as the first operand.
 //
 // Persistent schedule.  One workgroup per CU.  The tiles are ordered expert
-// by expert, then by groups of eight column tiles, then block pair by block
-// pair, columns fastest, and cut into eight contiguous chunks, one per XCD
+// by expert, column tile by column tile, block pair fastest (an expert with
+// more than 8 block pairs: by groups of 8 column tiles, pairs within a
+// group, columns fastest), and cut into eight contiguous chunks, one per XCD
 // (workgroup b runs on XCD b mod 8, the dispatch order); the workgroups of an
 // XCD take its chunk's tiles round robin, so the 32 tiles in flight on one
-// XCD at a time form a block of at most 4 row pairs x 8 column tiles whose
-// activation rows and weight columns are shared in that XCD's L2.  The
-// schedule is static: no device state, no atomics, every launch independent.
+// XCD at a time are neighbours that share weight columns and activation rows
+// in that XCD's L2.  The schedule is static: no device state, no atomics,
+// every launch independent.
 //
 // Pipeline.  A stage is computed as two halves; the fragment reads of the
 // next half are spread over the MFMAs of the current one.  Between the halves
@@ -65,7 +66,8 @@ constexpr int kARow = 128;                      // activation bytes per row and 
 constexpr int kASlot = kTM * kARow;             // 32 KB of activation rows per stage
 constexpr int kSfSlot = 4 * (kTM + kTN);        // MXFP8: the scale dword of every row and column
 constexpr int kInfo = 4;                        // routing-info buffers (tiles)
-constexpr int kColGroup = 8;                    // column tiles per group of the tile order
+constexpr int kMaxPairsTogether = 8;            // tile order: see decode()
+constexpr int kColGroup = 8;
 
 // chunk swizzles: 128-byte rows (8 chunks), 64-byte rows (4 chunks)
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
@@ -217,13 +219,22 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
     const int nblk = __builtin_amdgcn_readfirstlane(s_blk_first[e + 1] - s_blk_first[e]);
     const int npair = (nblk + 1) >> 1;
     const int local = L - __builtin_amdgcn_readfirstlane(s_tile_first[e]);
-    // column groups of kColGroup tiles, block pairs within a group, columns
-    // fastest: 32 consecutive tiles cover at most 4 block pairs x 8 columns
-    const int grp = local / (npair * kColGroup);
-    const int rem = local - grp * npair * kColGroup;
-    const int gc = min(kColGroup, ntn - grp * kColGroup);   // columns in this group
-    const int pr = rem / gc;
-    const int nt = grp * kColGroup + (rem - pr * gc);
+    int nt, pr;
+    if (npair <= kMaxPairsTogether) {
+      // column tile by column tile, block pair fastest: every block pair of a
+      // column tile is in flight at once, so its weights are read once
+      nt = local / npair;
+      pr = local - nt * npair;
+    } else {
+      // many row pairs (MXFP8 segments): groups of kColGroup column tiles,
+      // pairs within a group, columns fastest, so that 32 consecutive tiles
+      // are 4 pairs x 8 columns rather than 2 columns x 16 pairs
+      const int grp = local / (npair * kColGroup);
+      const int rem = local - grp * npair * kColGroup;
+      const int gc = min(kColGroup, ntn - grp * kColGroup);   // columns in this group
+      pr = rem / gc;
+      nt = grp * kColGroup + (rem - pr * gc);
+    }
     int nst = K / kTK;
     if constexpr (kW) nst = (seg.po[e + 1] - seg.po[e]) / kTK;
     return {e, nt, pr, min(2, nblk - 2 * pr), nst};

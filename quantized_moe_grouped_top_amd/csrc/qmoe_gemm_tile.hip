@@ -65,7 +65,6 @@ constexpr int kTN = 256;                        // tile columns
 constexpr int kARow = 128;                      // activation bytes per row and stage
 constexpr int kASlot = kTM * kARow;             // 32 KB of activation rows per stage
 constexpr int kSfSlot = 4 * (kTM + kTN);        // MXFP8: the scale dword of every row and column
-constexpr int kInfo = 4;                        // routing-info buffers (tiles)
 constexpr int kMaxPairsTogether = 8;            // tile order: see decode()
 constexpr int kColGroup = 8;
 
@@ -130,6 +129,13 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
   constexpr int kTK = kB16 ? 64 : 128;               // k per stage
   constexpr int kBRow = kB16 ? 64 : 128;             // weight bytes per row and stage
   constexpr int kRing = kB16 ? 3 : 2;                // stage slots
+  // per-tile routing buffers: with one stage per tile the DMA cursor runs
+  // kRing tiles ahead of the tile being computed (and fetches the sorted
+  // slots of the tile after that one) while the computed tile's epilogue
+  // still needs its own: kRing + 2 buffers of sorted slots, kRing + 1 of the
+  // per-row and per-column scales
+  constexpr int kInfo = kRing + 2;
+  constexpr int kInfoS = kRing + 1;
   constexpr int kSlot = kASlot + kTN * kBRow;        // 48 / 64 KB per stage
   constexpr int kBP = kB16 ? 4 : 8;                  // weight DMA pieces per wavefront and stage
   constexpr int kPieces = 8 + kBP + (kMx ? 2 : 0);   // DMA instructions per wavefront and stage
@@ -138,9 +144,9 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kRing * kSlot];
   __shared__ __attribute__((aligned(16))) uint8_t s_sf[kMx ? kRing * kSfSlot : 16];
   __shared__ __attribute__((aligned(16))) int s_row[kRouted ? kInfo : 1][kTM];    // sorted slots
-  __shared__ __attribute__((aligned(16))) float s_tw[kRouted ? kInfo : 1][kTM];   // router weights
-  __shared__ __attribute__((aligned(16))) float s_ts[kI8 ? kInfo : 1][kTM];       // token scales
-  __shared__ __attribute__((aligned(16))) float s_cs[kCS ? kInfo : 1][kTN];       // column scales
+  __shared__ __attribute__((aligned(16))) float s_tw[kRouted ? kInfoS : 1][kTM];  // router weights
+  __shared__ __attribute__((aligned(16))) float s_ts[kI8 ? kInfoS : 1][kTM];      // token scales
+  __shared__ __attribute__((aligned(16))) float s_cs[kCS ? kInfoS : 1][kTN];      // column scales
   __shared__ int s_blk_first[kMaxExperts + 1];
   __shared__ int s_tile_first[kMaxExperts + 1];
   __shared__ int s_mo[kMx ? kMaxExperts + 1 : 1];     // first row of every segment
@@ -281,7 +287,7 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
     if (t.nst == 0) return;                          // (weight gradient of an empty expert)
     const int n0 = t.nt * kTN;
     if constexpr (kRouted) {
-      const int buf = k % kInfo;
+      const int buf = k % kInfo, bufs = k % kInfoS;
       // this tile's sorted slots have landed (once 64 or more loads follow
       // them they have: at most 63 are outstanding and loads return in order)
       if (k > 0 && issued - info_mark < 64) wait_dma_upto(issued - info_mark);
@@ -298,15 +304,15 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
         const int R = 64 * wave + lane;
         const int slot = s_row[buf][R];
         const int sl = (R < nvalid && slot < S) ? slot : 0;
-        dma4(p.topk_w, (uint32_t)sl * 4u, lds_addr(&s_tw[buf][64 * wave]));
+        dma4(p.topk_w, (uint32_t)sl * 4u, lds_addr(&s_tw[bufs][64 * wave]));
         ++issued;
         if constexpr (kI8) {
-          dma4(p.a_scale, (uint32_t)(sl / top_k) * 4u, lds_addr(&s_ts[buf][64 * wave]));
+          dma4(p.a_scale, (uint32_t)(sl / top_k) * 4u, lds_addr(&s_ts[bufs][64 * wave]));
           ++issued;
         }
         if constexpr (kCS) {
           const int col = min(n0 + 64 * wave + lane, N - 1);
-          dma4(p.w_scale + (size_t)t.e * N, (uint32_t)col * 4u, lds_addr(&s_cs[buf][64 * wave]));
+          dma4(p.w_scale + (size_t)t.e * N, (uint32_t)col * 4u, lds_addr(&s_cs[bufs][64 * wave]));
           ++issued;
         }
       }
@@ -619,7 +625,7 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
     const int n0 = tl.nt * kTN;
     const __amdgpu_buffer_rsrc_t orsrc =
         __builtin_amdgcn_make_buffer_rsrc((void *)p.out, (short)0, (int)p.out_bytes, 0x00020000);
-    const int buf = k % kInfo;
+    const int buf = k % kInfo, bufs = k % kInfoS;
     const float sc = kFmt == kFmtFp8 ? s_wsc[tl.e] : 1.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -629,7 +635,7 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
       if constexpr (kRouted) {
         const int slot = s_row[buf][R];
         dst = (R < tl.nb * 128 && slot < S) ? slot : -1;
-        rs = kI8 ? s_ts[buf][R] * s_tw[buf][R] : (kB16 ? s_tw[buf][R] : sc * s_tw[buf][R]);
+        rs = kI8 ? s_ts[bufs][R] * s_tw[bufs][R] : (kB16 ? s_tw[bufs][R] : sc * s_tw[bufs][R]);
       } else {
         const int row = s_mo[tl.e] + 2 * tl.pr * 128 + R;
         dst = row < s_mo[tl.e + 1] ? row : -1;
@@ -648,7 +654,7 @@ __global__ __launch_bounds__(256, 1) void tile_kernel(const TileArgs p, const Wg
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
               const f32x4 cs =
-                  *reinterpret_cast<const f32x4 *>(&s_cs[buf][cb + 8 * (2 * kk + h) + 4 * g]);
+                  *reinterpret_cast<const f32x4 *>(&s_cs[bufs][cb + 8 * (2 * kk + h) + 4 * g]);
 #pragma unroll
               for (int c = 0; c < 4; ++c) {
                 const float raw = v[4 * h + c];

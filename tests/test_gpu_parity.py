@@ -190,6 +190,21 @@ def test_routed_small(wl, block_m, layout):
     run_routed(wl, block_m=block_m, full=True, layout=layout)
 
 
+# One k-stage per tile (K = 128 for one-byte activations, K = 64 for bf16)
+# with several tiles per workgroup: the tile GEMM's copies then run whole
+# tiles ahead of the tile being computed (its routing-info buffers must not
+# be reused before that tile's epilogue).
+ONE_STAGE = [synth.small("fp8", 4096, 128, 4096, 8, 2), synth.small("int8", 4096, 64, 4096, 8, 2),
+             synth.small("fp8wo", 4096, 64, 2048, 8, 2, bias_std=1.5),
+             synth.small("int8dq", 4096, 128, 2048, 8, 2)]
+
+
+@pytest.mark.parametrize("layout", [qm.MOE_W_ROWMAJOR, qm.MOE_W_TILED], ids=["rowmajor", "tiled"])
+@pytest.mark.parametrize("wl", ONE_STAGE, ids=[w.name for w in ONE_STAGE])
+def test_routed_one_stage_tiles(wl, layout):
+    run_routed(wl, block_m=128, full=False, n_tok=256, n_col=128, layout=layout)
+
+
 # int4 weight-only: the streaming kernel only (block_m 16), plain or packed
 INT4_SMALL = [
     synth.small("int4wo", 50, 384, 136, 6, 3),

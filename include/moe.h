@@ -21,7 +21,8 @@
  *
  * Conventions shared by every entry point
  *   - All array arguments are DEVICE pointers owned by the caller.  The library
- *     never allocates or frees memory and keeps no device state: every launch
+ *     never allocates or frees memory and keeps no device state (the one
+ *     exception, moe_quantize_act_noalloc, says so): every other launch
  *     depends only on its arguments, so calls may run concurrently on
  *     different streams.  On the host it keeps a thread-local record of the
  *     last error and the compute-unit count of the device (which sizes the
@@ -123,6 +124,12 @@ int moe_mx_scale_rows(int rows, int E);
  * ======================================================================== */
 
 /* Top-k routing of every token and grouping of the routed slots by expert.
+ * The grouped GEMM runs as one linear op per expert over that expert's
+ * (unequal) set of routed rows ("Enabling MOE Quantization using linear
+ * decomposition", Summary); this call forms those row sets for the (M, E,
+ * top_k) of the benchmark tables on "Tianxing/moe quantization".  The pages
+ * give no block size: padding each set to a multiple of block_m is the
+ * tiling these kernels use.
  *
  * Routing: for token t the top_k experts with the largest float32 logits are
  * chosen (on equal logits the lower expert index first); router weights are
@@ -455,7 +462,11 @@ int moe_grouped_gemm_mxfp8_wgrad(const uint8_t *dyT_q, const uint8_t *dyT_sf,
  * a6: combine
  * ======================================================================== */
 
-/* Per-token combine: out[t, n] = bf16( y[t*top_k, n] + ... + y[t*top_k+top_k-1, n] )
+/* Per-token combine: the sum over a token's top_k experts of their
+ * router-weighted results (the method statement at the top of this file; the
+ * MoE layer as a sum of per-expert linear outputs, "Enabling MOE Quantization
+ * using linear decomposition", Summary):
+ *     out[t, n] = bf16( y[t*top_k, n] + ... + y[t*top_k+top_k-1, n] )
  * over the bf16 per-slot results, with the adds done in float32 in slot order
  * and the sum rounded to nearest even.  y [M*top_k, N] uint16 bf16, out
  * [M, N] uint16 bf16, both 16-byte aligned.  N must be a multiple of 8. */

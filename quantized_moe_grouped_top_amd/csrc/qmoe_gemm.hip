@@ -28,15 +28,16 @@
 //                   stages ahead), so weight bytes are read once and never
 //                   pass through LDS; the expert's rows arrive in LDS by
 //                   direct-to-LDS DMA.
-//   gemm_big_kernel (routed fp8, block_m = 128, fewer than 384 rows per
+//   gemm_big_kernel (routed fp8, block_m = 128, fewer than 256 rows per
 //                   expert): 256 x 256 tiles on eight wavefronts of 128 x 64,
 //                   operands DMA'd into an LDS ring.
-//   gemm_kernel   (routed int8 W8A16 and fp8 weight-only, block_m = 128):
-//                   128 x 256 tiles on eight wavefronts, weights converted to
-//                   bf16 in registers for the bf16 MFMA.
-// The fp8 W8A8 and int8 W8A8 GEMMs with at least 384 routed rows per expert
-// and the MXFP8 grouped linear (forward and weight gradient) run the 256 x
-// 256 tile kernel of qmoe_gemm_tile.hip.
+//   gemm_kernel   (routed int8 W8A16 and fp8 weight-only, block_m = 128,
+//                   fewer than 256 rows per expert): 128 x 256 tiles on eight
+//                   wavefronts, weights converted to bf16 in registers for
+//                   the bf16 MFMA.
+// The routed GEMMs at block_m 128 with at least 256 routed rows per expert
+// (int8 W8A8: always) and the MXFP8 grouped linear (forward and weight
+// gradient) run the 256 x 256 tile kernel of qmoe_gemm_tile.hip.
 // Routed results are written per slot as bf16; MXFP8 rows as bf16.
 
 #include "qmoe_device.h"
@@ -1284,11 +1285,13 @@ int num_cus() {
 }
 
 // Below this many routed rows per expert (on average) most 256-row tiles
-// hold a single 128-row block; the eight-wavefront kernel then idles the
-// wavefronts of the missing block and gives their SIMD time to the others,
-// where the four-wavefront kernel (one per SIMD) would leave half the MFMA
-// units to a block that does not exist.
-constexpr long long kWideMinRowsPerExpert = 384;
+// hold a single 128-row block; the eight-wavefront kernels then idle the
+// wavefronts of the missing block and give their SIMD time to the others,
+// where the four-wavefront tile kernel (one per SIMD) would leave half the
+// MFMA units to a block that does not exist.  (Measured: fp8 with a biased
+// router at 128 rows per expert runs equally fast on either kernel, at 256
+// rows 6.5% faster on the tile kernel.)
+constexpr long long kWideMinRowsPerExpert = 256;
 
 // persistent decomposition of the weight stream: E * groups workgroups, each
 // with tiles_per_group consecutive 64-column tiles of one expert

@@ -192,7 +192,7 @@ class MxMoE:
 class MxWgrad:
     """Weight gradient of the MXFP8 grouped linear: columnwise quantization
     of the output gradient dy [rows, N] and the input x [rows, K], then one
-    grouped-linear launch per expert into dw [E, N, K] (bf16 bits)."""
+    grouped-GEMM launch over every expert into dw [E, N, K] (bf16 bits)."""
 
     def __init__(self, rows, K, N, E, m_splits, device="cuda"):
         self.rows, self.K, self.N, self.E = rows, K, N, E

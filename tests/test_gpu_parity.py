@@ -147,7 +147,7 @@ SMALL = [
     synth.small("fp8", 1, 128, 64, 8, 2),
     synth.small("int8", 40, 128, 48, 1, 1),
     synth.small("fp8", 33, 256, 96, 4, 4),
-    # >= 384 routed rows per expert: the four-wavefront persistent kernel
+    # >= 256 routed rows per expert: the four-wavefront persistent kernel
     synth.small("fp8", 400, 256, 320, 2, 2),
     synth.small("fp8", 800, 384, 136, 4, 2, bias_std=1.5),
     # int8 W8A8 with per-token activation scales
@@ -162,7 +162,7 @@ SMALL = [
     synth.small("fp8wo", 50, 320, 136, 6, 3),
     synth.small("fp8wo", 300, 256, 272, 8, 2, bias_std=1.5),
     synth.small("fp8wo", 40, 128, 48, 1, 1),
-    # bf16 activations with >= 384 routed rows per expert: the tile kernel
+    # bf16 activations with >= 256 routed rows per expert: the tile kernel
     # (64-k stages; K = 320 ends on half a 128-byte weight block, K = 64 is one
     # stage per tile)
     synth.small("int8", 400, 256, 320, 2, 2),

@@ -75,7 +75,9 @@ def run_routed(wl, block_m=None, variant=0, full=True, n_tok=48, n_col=64, logit
         toks, cols = np.arange(M), np.arange(N)
     else:
         toks = pick(M, n_tok, rng, must=(0, M - 1))
-        cols = pick(N, n_col, rng, must=(0, N - 1, N // 2))
+        # the first and last column, the middle, and both sides of the
+        # 256-column tile edges at the start and the end
+        cols = pick(N, n_col, rng, must=(0, N - 1, N // 2, 255, 256, N - 257, N - 256))
     slots = (toks[:, None] * top_k + np.arange(top_k)[None, :]).reshape(-1)
 
     # ---- weights: bit-exact quantization of the checked rows ----------------
@@ -389,8 +391,9 @@ FULL = [synth.WORKLOADS[n] for n in [
 
 @pytest.mark.parametrize("wl", FULL, ids=[w.name for w in FULL])
 def test_routed_full_size_sampled(wl):
-    """The benchmark's launch configuration: recommended block_m, packed weights."""
-    run_routed(wl, block_m=None, full=False, layout=bench_layout(wl))
+    """The benchmark's launch configuration: recommended block_m, packed weights
+    (128 tokens and 192 columns per case)."""
+    run_routed(wl, block_m=None, full=False, n_tok=128, n_col=192, layout=bench_layout(wl))
     torch.cuda.empty_cache()
 
 

@@ -706,7 +706,10 @@ __global__ __launch_bounds__(kThreads) void act_fp8_kernel(ActRows<kAct> src, in
     out[1] = (int)f32x4_to_e4m3x4(y[4] * inv, y[5] * inv, y[6] * inv, y[7] * inv);
     *reinterpret_cast<i32x2 *>(dst) = out;
   };
-  for (int r = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); r < rows; r += waves) {
+  // rows in the reverse of pass 1's order: the rows pass 1 read last are the
+  // likeliest to be still in the memory-side cache
+  for (int i = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); i < rows; i += waves) {
+    const int r = rows - 1 - i;
     uint8_t *q_row = q + (long long)r * H;
     int c8 = lane;
     for (; c8 + 64 * (U - 1) < n8; c8 += 64 * U) {

@@ -1,7 +1,8 @@
 // Per-token combine of the routed results: out[t, n] = bf16(sum_j y[t*top_k+j, n])
 // over the bf16 per-slot results, with the adds in float32 in slot order and
 // the sum rounded to nearest even.  An HBM stream: each thread handles 8
-// columns (16-byte loads and stores).
+// columns (16-byte loads and stores, with the non-temporal hint: every byte
+// is read or written once).
 #include "qmoe_internal.h"
 
 namespace qmoe {
@@ -28,7 +29,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t *__res
     i32x4 v[kMaxTopK];
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j)
-      if (j < top_k) v[j] = *reinterpret_cast<const i32x4 *>(src + (long long)j * N);
+      if (j < top_k) v[j] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(src + (long long)j * N));
     float acc[8];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -47,7 +48,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t *__res
     i32x4 o;
 #pragma unroll
     for (int q = 0; q < 4; ++q) o[q] = (int)f32x2_to_bf16x2(acc[2 * q], acc[2 * q + 1]);
-    *reinterpret_cast<i32x4 *>(out + t * N + c) = o;
+    __builtin_nontemporal_store(o, reinterpret_cast<i32x4 *>(out + t * N + c));
   }
 }
 

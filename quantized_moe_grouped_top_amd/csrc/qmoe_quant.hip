@@ -448,17 +448,26 @@ __device__ __forceinline__ void act8(const uint16_t *row, int H, int col, float 
   }
 }
 
+// 16-byte load, with the non-temporal hint for data read once
+template <bool kNT>
+__device__ __forceinline__ i32x4 ld16(const uint16_t *p) {
+  if constexpr (kNT) return __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(p));
+  else return *reinterpret_cast<const i32x4 *>(p);
+}
+
 // Sources of the padded-row MXFP8 kernel.  load() fetches the raw bytes of 8
-// consecutive values of row r from column col (col % 8 == 0); values() turns
-// them into the 8 float values.  The kernel issues the loads of kUnroll
+// consecutive values of row r from column col (col % 8 == 0), with the
+// non-temporal hint when kNT (a pass that reads its input once); values()
+// turns them into the 8 float values.  The kernel issues the loads of kUnroll
 // chunks before it converts any, so they are in flight together.
 struct Bf16Rows {
   static constexpr int kUnroll = 2;
   struct Raw { i32x4 a; };
   const uint16_t *x;
   int K;
+  template <bool kNT = false>
   __device__ __forceinline__ Raw load(long long r, int col) const {
-    return {*reinterpret_cast<const i32x4 *>(x + r * K + col)};
+    return {ld16<kNT>(x + r * K + col)};
   }
   __device__ __forceinline__ void values(const Raw &raw, float *v) const { unpack8(raw.a, v); }
 };
@@ -471,14 +480,15 @@ struct ActRows {                   // activation of rows of width 2H (SwiGLU) or
   using Raw = ActRaw<kAct>;
   const uint16_t *x;
   int H;
+  template <bool kNT = false>
   __device__ __forceinline__ Raw load(long long r, int col) const {
     Raw raw;
     if constexpr (kAct == MOE_ACT_SWIGLU) {
       const uint16_t *row = x + r * 2ll * H;
-      raw.a = *reinterpret_cast<const i32x4 *>(row + col);
-      raw.b = *reinterpret_cast<const i32x4 *>(row + H + col);
+      raw.a = ld16<kNT>(row + col);
+      raw.b = ld16<kNT>(row + H + col);
     } else {
-      raw.a = *reinterpret_cast<const i32x4 *>(x + r * (long long)H + col);
+      raw.a = ld16<kNT>(x + r * (long long)H + col);
     }
     return raw;
   }
@@ -529,7 +539,7 @@ __device__ __forceinline__ uint32_t mx_chunk(const float *v, uint8_t *dst) {
   i32x2 o;
   o[0] = (int)f32x4_to_e4m3x4(v[0] * f, v[1] * f, v[2] * f, v[3] * f);
   o[1] = (int)f32x4_to_e4m3x4(v[4] * f, v[5] * f, v[6] * f, v[7] * f);
-  *reinterpret_cast<i32x2 *>(dst) = o;
+  __builtin_nontemporal_store(o, reinterpret_cast<i32x2 *>(dst));
   return b;
 }
 
@@ -595,7 +605,7 @@ __global__ __launch_bounds__(kThreads) void mx_padded_kernel(
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       const int c = c0 + kThreads * j < n8 ? c0 + kThreads * j : c0;
-      raw[j] = src.load(r, 8 * c);
+      raw[j] = src.template load<true>(r, 8 * c);
     }
   };
   auto encode = [&](int c8, const Raw &raw, uint8_t *q_row, uint8_t *sf_row) {
@@ -627,7 +637,7 @@ __global__ __launch_bounds__(kThreads) void mx_padded_kernel(
       for (int j = 0; j < U; ++j)
         if (c0 + kThreads * j < n8) encode(c0 + kThreads * j, cur[j], q_row, sf_row);
       for (int c8 = c0 + kThreads * U; c8 < n8; c8 += kThreads)
-        encode(c8, src.load(r, 8 * c8), q_row, sf_row);
+        encode(c8, src.template load<true>(r, 8 * c8), q_row, sf_row);
     } else {
       for (int c8 = c0; c8 < n8; c8 += kThreads)
         if ((c8 & 3) == 0) sf_row[c8 >> 2] = 0;
@@ -704,7 +714,7 @@ __global__ __launch_bounds__(kThreads) void act_fp8_kernel(ActRows<kAct> src, in
     i32x2 out;
     out[0] = (int)f32x4_to_e4m3x4(y[0] * inv, y[1] * inv, y[2] * inv, y[3] * inv);
     out[1] = (int)f32x4_to_e4m3x4(y[4] * inv, y[5] * inv, y[6] * inv, y[7] * inv);
-    *reinterpret_cast<i32x2 *>(dst) = out;
+    __builtin_nontemporal_store(out, reinterpret_cast<i32x2 *>(dst));
   };
   // rows in the reverse of pass 1's order: the rows pass 1 read last are the
   // likeliest to be still in the memory-side cache
@@ -715,12 +725,12 @@ __global__ __launch_bounds__(kThreads) void act_fp8_kernel(ActRows<kAct> src, in
     for (; c8 + 64 * (U - 1) < n8; c8 += 64 * U) {
       typename ActRows<kAct>::Raw raw[U];
 #pragma unroll
-      for (int j = 0; j < U; ++j) raw[j] = src.load(r, 8 * (c8 + 64 * j));
+      for (int j = 0; j < U; ++j) raw[j] = src.template load<true>(r, 8 * (c8 + 64 * j));
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < U; ++j) encode(raw[j], q_row + 8 * (c8 + 64 * j));
     }
-    for (; c8 < n8; c8 += 64) encode(src.load(r, 8 * c8), q_row + 8 * c8);
+    for (; c8 < n8; c8 += 64) encode(src.template load<true>(r, 8 * c8), q_row + 8 * c8);
   }
 }
 

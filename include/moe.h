@@ -437,7 +437,7 @@ int moe_grouped_gemm_mxfp8(const uint8_t *a_q, const uint8_t *a_sf,
  *   qT  code of row m_offsets[e] + i, column c at byte C*P_e + c*Rp_e + i
  *       (zero for the padding rows)
  *   sfT scale of block j of column c at byte C*P_e/32 + c*Rp_e/32 + j
- * x [rows, C] bf16 (8-byte aligned), m_offsets [E+1] int32 (device), qT at
+ * x [rows, C] bf16 (16-byte aligned), m_offsets [E+1] int32 (device), qT at
  * least C * moe_mx_scale_rows(rows, E) bytes (16-byte aligned), sfT at least
  * C * moe_mx_scale_rows(rows, E) / 32 bytes.  C must be a multiple of 64;
  * rows + 127 E at most 65535 * 128. */

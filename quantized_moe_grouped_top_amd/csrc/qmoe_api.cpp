@@ -486,8 +486,7 @@ int moe_quantize_act_colwise(const uint16_t *x, int rows, int C, const int *m_of
           "%s: the transposed codes must stay below 4 GiB", fn);
   if (rows == 0) return ok();
   REQUIRE(x && m_offsets && qT && sfT, MOE_EINVAL, "%s: null pointer argument", fn);
-  REQUIRE(((uintptr_t)x & 7u) == 0 && aligned16(qT), MOE_EINVAL,
-          "%s: x must be 8-byte and qT 16-byte aligned", fn);
+  REQUIRE(aligned16(x) && aligned16(qT), MOE_EINVAL, "%s: x and qT must be 16-byte aligned", fn);
   return hip_status(qmoe::launch_mx_colwise_bf16(x, rows, C, m_offsets, E, qT, sfT, stream), fn);
 }
 

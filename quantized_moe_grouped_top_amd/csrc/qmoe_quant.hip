@@ -289,8 +289,8 @@ __device__ __forceinline__ uint32_t mx_encode(const float *v, uint8_t *dst) {
     o1[i] = (int)f32x4_to_e4m3x4(v[16 + 4 * i] * f, v[16 + 4 * i + 1] * f, v[16 + 4 * i + 2] * f,
                                  v[16 + 4 * i + 3] * f);
   }
-  *reinterpret_cast<i32x4 *>(dst) = o0;
-  *reinterpret_cast<i32x4 *>(dst + 16) = o1;
+  __builtin_nontemporal_store(o0, reinterpret_cast<i32x4 *>(dst));   // written once
+  __builtin_nontemporal_store(o1, reinterpret_cast<i32x4 *>(dst + 16));
   return (uint32_t)b;
 }
 
@@ -300,7 +300,8 @@ __device__ __forceinline__ uint32_t mx_encode(const float *v, uint8_t *dst) {
 // expert by expert (P_e = sum of Rp of the experts before e): codes at
 // C * P_e + c * Rp_e + row, scale bytes at C * P_e / 32 + c * Rp_e / 32 + j.
 // A workgroup takes one padded 128-row chunk of one expert x 64 columns: the
-// tile is read row by row (16 lanes x 8 or 16 bytes per row, coalesced) into
+// tile is read row by row (16 bytes per lane: 8 lanes per bf16 row, 16 per
+// float row; coalesced) into
 // LDS transposed (a row of LDS per column), then thread (c, j) encodes block
 // j of column c from LDS and four neighbouring threads write the column's
 // 128 codes as one contiguous 128-byte run.
@@ -308,22 +309,15 @@ constexpr int kColwiseCols = 64;                    // columns per workgroup
 
 template <typename Src> struct ColwiseRaw;
 template <> struct ColwiseRaw<uint16_t> {
-  using Vec = i32x2;                                // 4 bf16 of one row
+  static constexpr int kPerLane = 8;                // 8 bf16 of one row per lane
   static constexpr int kPad = 8;                    // row stride 272 bytes (16-byte aligned)
 };
 template <> struct ColwiseRaw<float> {
-  using Vec = f32x4;                                // 4 floats of one row
+  static constexpr int kPerLane = 4;                // 4 floats of one row per lane
   static constexpr int kPad = 4;                    // row stride 528 bytes
 };
-__device__ __forceinline__ void put4(uint16_t (*t)[kMxRowPad + ColwiseRaw<uint16_t>::kPad], int c,
-                                     int r, const i32x2 &v) {
-  t[c][r] = (uint16_t)((uint32_t)v[0] & 0xFFFFu);
-  t[c + 1][r] = (uint16_t)((uint32_t)v[0] >> 16);
-  t[c + 2][r] = (uint16_t)((uint32_t)v[1] & 0xFFFFu);
-  t[c + 3][r] = (uint16_t)((uint32_t)v[1] >> 16);
-}
-__device__ __forceinline__ void put4(float (*t)[kMxRowPad + ColwiseRaw<float>::kPad], int c, int r,
-                                     const f32x4 &v) {
+__device__ __forceinline__ void put_row(float (*t)[kMxRowPad + ColwiseRaw<float>::kPad], int c, int r,
+                                        const f32x4 &v) {
   t[c][r] = v[0];
   t[c + 1][r] = v[1];
   t[c + 2][r] = v[2];
@@ -376,15 +370,42 @@ __global__ __launch_bounds__(kThreads) void mx_colwise_kernel(const Src *__restr
   const int c0 = blockIdx.x * kColwiseCols;
   const long long row0 = s_mo[e] + (pr - s_po[e]);          // first data row of the chunk
   const long long rend = s_mo[e + 1];
-  // load: row r = tid / 16 + 16 i, columns c0 + 4 (tid % 16) .. + 3
-  {
-    const int cg = 4 * (threadIdx.x & 15);
+  // load (16 bytes per lane, the non-temporal hint: the input is read once)
+  if constexpr (R::kPerLane == 8) {
+    // bf16: thread t reads rows rb = 4 (t / 8) .. rb + 3, columns
+    // c0 + 8 (t % 8) .. + 7 (eight lanes cover a row's 128 bytes) and writes
+    // each column's four values as one 8-byte run of its transposed row
+    const int cg = 8 * (int)(threadIdx.x & 7);
+    const int rb = 4 * (int)(threadIdx.x >> 3);
+    i32x4 v4[4];
 #pragma unroll
-    for (int i = 0; i < kMxRowPad / 16; ++i) {
-      const int r = (int)(threadIdx.x >> 4) + 16 * i;
-      typename R::Vec v{};
-      if (row0 + r < rend) v = *reinterpret_cast<const typename R::Vec *>(x + (row0 + r) * C + c0 + cg);
-      put4(s_t, cg, r, v);
+    for (int q = 0; q < 4; ++q) {
+      v4[q] = i32x4{0, 0, 0, 0};
+      if (row0 + rb + q < rend)
+        v4[q] = __builtin_nontemporal_load(
+            reinterpret_cast<const i32x4 *>(x + (row0 + rb + q) * C + c0 + cg));
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      // column cg + k: the low (k even) or high (k odd) half of dword k / 2
+      // of each row, two rows per dword
+      const uint32_t sel = (k & 1) ? 0x07060302u : 0x05040100u;
+      i32x2 w;
+      w[0] = (int)__builtin_amdgcn_perm((uint32_t)v4[1][k >> 1], (uint32_t)v4[0][k >> 1], sel);
+      w[1] = (int)__builtin_amdgcn_perm((uint32_t)v4[3][k >> 1], (uint32_t)v4[2][k >> 1], sel);
+      *reinterpret_cast<i32x2 *>(&s_t[cg + k][rb]) = w;
+    }
+  } else {
+    // float: row r = tid / 16 + 16 i, columns c0 + 4 (tid % 16) .. + 3
+    constexpr int P = R::kPerLane, L = kColwiseCols / P, RS = kThreads / L;
+    const int cg = P * (int)(threadIdx.x % L);
+#pragma unroll
+    for (int i = 0; i < kMxRowPad / RS; ++i) {
+      const int r = (int)(threadIdx.x / L) + RS * i;
+      f32x4 v{};
+      if (row0 + r < rend)
+        v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(x + (row0 + r) * C + c0 + cg));
+      put_row(s_t, cg, r, v);
     }
   }
   __syncthreads();

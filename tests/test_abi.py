@@ -236,6 +236,9 @@ def test_mx_backward_rejects():
     with pytest.raises(qm.MoeError) as ei:
         qm.moe_quantize_act_colwise(FAKE, 100, 128, FAKE, 2, MIS, FAKE, stream=0)
     assert ei.value.code == qm.MOE_EINVAL                       # misaligned codes
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_quantize_act_colwise(FAKE + 8, 100, 128, FAKE, 2, FAKE, FAKE, stream=0)
+    assert ei.value.code == qm.MOE_EINVAL                       # input not 16-byte aligned
     qm.moe_quantize_act_colwise(FAKE, 0, 128, FAKE, 2, FAKE, FAKE, stream=0)   # no rows
     with pytest.raises(qm.MoeError) as ei:
         qm.moe_grouped_gemm_mxfp8_wgrad(FAKE, FAKE, FAKE, FAKE, [10, 20], 2, 100, 128, FAKE,

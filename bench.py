@@ -95,16 +95,42 @@ GEMM_SOURCES = ("qmoe_gemm.hip", "qmoe_gemm_tile.hip", "qmoe_device.h", "qmoe_in
 ACT_SOURCES = ("qmoe_quant.hip", "qmoe_internal.h")
 
 
+def _code_only(text):
+    """C++ source without its comments and with whitespace runs collapsed
+    (string and character literals kept as they are)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash(workload=None):
-    """sha256 over the sources of the workload's timed kernel (the grouped
-    GEMM, or the fused activation quantization): a recorded HBM traffic figure
-    is only valid for the kernel it was counted on."""
+    """sha256 over the code (comments and layout left out) of the sources of
+    the workload's timed kernel (the grouped GEMM, or the fused activation
+    quantization): a recorded HBM traffic figure is only valid for the code
+    it was counted on."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "quantized_moe_grouped_top_amd", "csrc")
     act = workload is not None and workload.startswith(("swiglu_", "srelu_"))
     for name in ACT_SOURCES if act else GEMM_SOURCES:
-        with open(os.path.join(d, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(d, name), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 

@@ -22,7 +22,7 @@
 // Kernels in this file:
 //   stream_kernel (routed, block_m = 16): weight streaming for few rows per
 //                   expert (decode).  One persistent workgroup per CU owns an
-//                   expert and up to 7 consecutive 64-column tiles; each lane
+//                   expert and up to 7 of its 64-column tiles; each lane
 //                   loads exactly the weight pieces of its MFMA operands from
 //                   HBM into registers (buffer loads, up to three 128-k
 //                   stages ahead), so weight bytes are read once and never
@@ -81,8 +81,8 @@ __device__ __forceinline__ i32x4 ld16(const void *p) {
 // block_m = 16: weight streaming
 // =============================================================================
 // One persistent workgroup per CU.  Workgroup b handles expert e = b / groups
-// and a run of G <= 7 consecutive 64-column tiles of that expert (4G groups of
-// 16 weight rows), with up to 64 of the expert's rows per pass.  Wavefront w
+// and G <= 7 of that expert's 64-column tiles (strided, see below; 4G groups
+// of 16 weight rows), with up to 64 of the expert's rows per pass.  Wavefront w
 // owns the row groups w, w + 8, w + 16 and w + 24 (those below 4G): every
 // wavefront owns whole output elements, so no partial sums meet.
 //
@@ -1313,8 +1313,6 @@ int num_cus() {
 // rows 6.5% faster on the tile kernel.)
 constexpr long long kWideMinRowsPerExpert = 256;
 
-// persistent decomposition of the weight stream: E * groups workgroups, each
-// with tiles_per_group consecutive 64-column tiles of one expert
 // bytes of the weight tensor in the layout the call passes (below 4 GiB)
 uint32_t stream_weight_bytes(const RoutedArgs &r) {
   if (r.w_layout == MOE_W_TILED)
@@ -1341,6 +1339,9 @@ decltype(&stream_kernel<kMode, MOE_W_ROWMAJOR, kSMB>) stream_kernel_for(int layo
   return two ? stream_kernel_l<kMode, 2>(layout) : stream_kernel_l<kMode, kSMB>(layout);
 }
 
+// persistent decomposition of the weight stream: E * groups workgroups, each
+// with up to tiles_per_group 64-column tiles of one expert (taken strided:
+// tiles grp, grp + groups, ...)
 void stream_grid(int N, int E, int &groups, int &tiles_per_group) {
   const int ntiles = (N + 63) / 64;
   int tpg = (E * ntiles + num_cus() - 1) / num_cus();

@@ -448,17 +448,21 @@ def main():
         "config": fields["config"],
         "roofline": fields["roofline"],
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, case, args.cpu_seconds)
-    del case
     if args.workload is None:
-        # the HBM-bound decode shape, timed in the same run (no CPU baseline)
+        # the HBM-bound decode shape, timed in the same run (no CPU baseline),
+        # right after the first workload while the GPU is still busy (an idle
+        # GPU, e.g. during the CPU baseline, lowers its clocks first)
         torch.cuda.empty_cache()
-        dfields, _, _ = measure(synth.WORKLOADS[DECODE_WORKLOAD], args)
+        dargs = argparse.Namespace(**vars(args))
+        dargs.warmup = max(args.warmup, 100)
+        dfields, _, _ = measure(synth.WORKLOADS[DECODE_WORKLOAD], dargs)
         line["decode"] = {"workload": DECODE_WORKLOAD, "ms_per_step": dfields["ms_per_step"],
                           "value": dfields["value"], "unit": "GB/s",
                           "gemm_us": dfields["roofline"]["kernel_us"],
                           "roofline": dfields["roofline"]}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, case, args.cpu_seconds)
+    del case
     print(json.dumps(line), flush=True)
 
 

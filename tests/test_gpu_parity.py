@@ -171,6 +171,11 @@ SMALL = [
     synth.small("int8", 500, 320, 200, 2, 2, bias_std=1.5),
     synth.small("fp8wo", 800, 384, 136, 4, 2, bias_std=1.5),
     synth.small("fp8wo", 400, 64, 264, 2, 2),
+    # many experts, most with a few rows or none (the largest E and top_k the
+    # library takes, and two in between)
+    synth.small("fp8", 48, 256, 136, 128, 8),
+    synth.small("int8", 100, 128, 200, 64, 6, bias_std=1.5),
+    synth.small("int8dq", 300, 256, 72, 32, 4),
 ]
 
 

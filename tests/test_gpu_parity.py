@@ -176,6 +176,7 @@ SMALL = [
     synth.small("fp8", 48, 256, 136, 128, 8),
     synth.small("int8", 100, 128, 200, 64, 6, bias_std=1.5),
     synth.small("int8dq", 300, 256, 72, 32, 4),
+    synth.small("fp8wo", 48, 128, 264, 128, 8, bias_std=1.5),
 ]
 
 
@@ -219,6 +220,7 @@ INT4_SMALL = [
     synth.small("int4wo", 40, 128, 48, 1, 1),
     synth.small("int4wo", 1, 128, 64, 8, 2),
     synth.small("int4wo", 60, 256, 136, 8, 2, bias_std=1.5),   # 32 rows per pass, several
+    synth.small("int4wo", 100, 128, 200, 64, 6),                 # many experts
 ]
 
 
@@ -510,6 +512,9 @@ def run_mx(wl, full=True, n_row=64, n_col=64):
 
 
 MX_SMALL = [synth.small("mxfp8", 0, 256, 136, 0, 1, seg=(5, 130, 0, 77)),
+            # many experts, several empty
+            synth.small("mxfp8", 0, 128, 72, 0, 1,
+                        seg=(0, 3, 129, 0, 0, 256, 1, 40, 0, 300, 7, 0, 0, 2, 128, 0)),
             synth.small("mxfp8", 0, 128, 64, 0, 1, seg=(128, 128)),
             synth.small("mxfp8", 0, 384, 16, 0, 1, seg=(1,))]
 

@@ -53,7 +53,8 @@ def _check_out(got_bits, ref32, what):
     assert_bf16_out(got_bits, ref32, F.bf16_round(ref32), what)
 
 
-SEGS = [(64, 64), (37, 0, 200, 5), (1,), (128,), (300, 130)]
+MANY = (0, 3, 129, 0, 0, 256, 1, 40, 0, 300, 7, 0, 0, 2, 128, 0)   # 16 experts, several empty
+SEGS = [(64, 64), (37, 0, 200, 5), (1,), (128,), (300, 130), MANY]
 
 
 @pytest.mark.parametrize("seg", SEGS, ids=["-".join(map(str, s)) for s in SEGS])
@@ -128,7 +129,7 @@ def run_backward(seg, K, N, full=True, n_row=48, n_col=48, seed=7):
 
 
 BWD_SMALL = [((64, 64), 128, 128), ((37, 0, 200, 5), 192, 256), ((1,), 64, 128),
-             ((300, 130, 7), 256, 384)]
+             ((300, 130, 7), 256, 384), (MANY, 128, 128)]
 
 
 @pytest.mark.parametrize("seg,K,N", BWD_SMALL, ids=[f"{len(s)}x{max(s)}-k{k}-n{n}" for s, k, n in BWD_SMALL])

@@ -420,7 +420,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
-              f"(this build runs the hot path on a single MI355X).", file=sys.stderr)
+              f"(the library runs the hot path on one MI355X).", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()

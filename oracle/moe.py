@@ -14,7 +14,7 @@ weight and sum the top_k results of each token.
 Flat slot numbering: the j-th expert choice of token t is slot i = t*top_k + j.
 Per-slot results ``y`` have shape [M*top_k, N] in that order.
 
-Readings taken where the pages are silent (each is restated in the design doc):
+Readings taken where the pages are silent:
 
 * routing selects the top_k experts by float32 logit, larger first, the lower
   expert index first on equal logits; router weights are the softmax over all

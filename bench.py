@@ -20,9 +20,10 @@ step before.
 Prints one JSON line: value = whole-step throughput in algorithmic HBM GB/s
 (the byte count of the "Tianxing/moe quantization" tables: activations +
 expert weights + scales + per-slot bf16 outputs), plus the TFLOPS of the
-step, the roofline of the dominant kernel (the grouped GEMM; each launch in
-the timed region is bracketed by a pair of HIP events on the stream it runs
-on, torch's current stream) and the CPU oracle timed on the host.
+step, the roofline of the dominant kernel (the grouped GEMM: after the timed
+steps, as many back-to-back launches of it on the steps' buffers, weights
+still rotated, bracketed by a pair of HIP events on the stream it runs on,
+torch's current stream) and the CPU oracle timed on the host.
 """
 
 import argparse
@@ -287,6 +288,8 @@ def measure(wl, args):
 
     case = synth.make_case(wl, 0, device="cuda")
     layout = None
+    # step(i): one pass of the whole path; kernel(i): the timed kernel alone,
+    # on the buffers the steps leave behind (inputs rotated the same way)
     if wl.fmt.startswith("act_"):
         # input copies rotate so that no step finds its input in a cache
         copies = args.copies or max(2, -(-(1 << 30) // (2 * case["x"].numel())))
@@ -294,24 +297,21 @@ def measure(wl, args):
         moe = runner.ActQuant(wl.M, wl.N, wl.E, wl.act, wl.fmt[4:])
         mo = case["m_offsets"]
 
-        def step(i, ev):
-            if ev is not None:
-                ev[0].record()
+        def kernel(i):
             moe(xs[i % copies], mo)
-            if ev is not None:
-                ev[1].record()
+
+        step = kernel
     elif wl.fmt == "mxfp8_wgrad":
         copies = 1                             # operands are made from x and dy every step
         moe = runner.MxWgrad(wl.M, wl.K, wl.N, wl.E, wl.seg)
         mo = case["m_offsets"]
 
-        def step(i, ev):
-            moe.quantize(case["dy"], case["x"], mo)
-            if ev is not None:
-                ev[0].record()
+        def kernel(i):
             moe.gemm()
-            if ev is not None:
-                ev[1].record()
+
+        def step(i):
+            moe.quantize(case["dy"], case["x"], mo)
+            moe.gemm()
     else:
         w_q, w_s = runner.quantize_weights(
             case["w"], "mxfp8_colwise" if wl.fmt == "mxfp8_dgrad" else wl.fmt)
@@ -323,58 +323,55 @@ def measure(wl, args):
             w_q = runner.pack_weights(w_q, layout)
         copies = args.copies or max(2, -(-(1 << 30) // w_q.numel()))
         weights = [(w_q, w_s)] + [(w_q.clone(), w_s.clone()) for _ in range(copies - 1)]
-        if wl.fmt == "mxfp8_dgrad":
-            # the output gradient [M, N] against the weights along N: dx [M, K]
-            moe = runner.MxMoE(wl.M, wl.N, wl.K, wl.E)
+        if wl.fmt in ("mxfp8_dgrad", "mxfp8"):
+            # dgrad: the output gradient [M, N] against the weights along N: dx [M, K]
+            if wl.fmt == "mxfp8_dgrad":
+                moe, src = runner.MxMoE(wl.M, wl.N, wl.K, wl.E), case["dy"]
+            else:
+                moe, src = runner.MxMoE(wl.M, wl.K, wl.N, wl.E), case["x"]
             mo = case["m_offsets"]
 
-            def step(i, ev):
+            def kernel(i):
                 q, s = weights[i % copies]
-                moe.quantize(case["dy"], mo)
-                if ev is not None:
-                    ev[0].record()
                 moe.gemm(q, s, mo)
-                if ev is not None:
-                    ev[1].record()
-        elif wl.fmt == "mxfp8":
-            moe = runner.MxMoE(wl.M, wl.K, wl.N, wl.E)
-            mo = case["m_offsets"]
 
-            def step(i, ev):
-                q, s = weights[i % copies]
-                moe.quantize(case["x"], mo)
-                if ev is not None:
-                    ev[0].record()
-                moe.gemm(q, s, mo)
-                if ev is not None:
-                    ev[1].record()
+            def step(i):
+                moe.quantize(src, mo)
+                kernel(i)
         else:
             moe = runner.RoutedMoE(wl.fmt, wl.M, wl.K, wl.N, wl.E, wl.top_k, w_layout=layout)
 
-            def step(i, ev):
+            def kernel(i):
                 q, s = weights[i % copies]
+                moe.gemm(case["x"], q, s)
+
+            def step(i):
                 moe.route(case["logits"])
                 moe.quantize(case["x"])
-                if ev is not None:
-                    ev[0].record()
-                moe.gemm(case["x"], q, s)
-                if ev is not None:
-                    ev[1].record()
+                kernel(i)
                 moe.combine()
 
     for i in range(args.warmup):
-        step(i, None)
-    torch.cuda.synchronize()
-    # the library launches on torch's current stream, which these events mark
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+        step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, events[i])
+        step(args.warmup + i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    gemm_ms = sum(a.elapsed_time(b) for a, b in events) / args.steps
+    # The timed kernel's mean launch duration: HIP events on the stream the
+    # library launches on (torch's current stream) around the same number of
+    # back-to-back launches, with the weights (or inputs) still rotated.
+    # Events around each launch inside the steps would also count the
+    # dispatch after an event marker (~6 us per launch at decode, where
+    # rocprofv3's kernel duration is 76.8 us and such events read 82.8 us).
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(args.steps):
+        kernel(args.warmup + args.steps + i)
+    ev1.record()
+    torch.cuda.synchronize()
+    gemm_ms = ev0.elapsed_time(ev1) / args.steps
 
     active = wl.E
     if wl.fmt in ("fp8", "int8", "int8dq", "fp8wo", "int4wo"):
